@@ -1,0 +1,87 @@
+/*
+ * zno.h -- CPU oracle of the exponent-Huffman float codec.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load liboracle_zno.so.  The GPU library
+ * (libzn.so) never links, loads or includes anything from this directory,
+ * and this directory includes nothing from it: the format constants below
+ * are restated here on purpose.
+ *
+ * What is computed, and where it comes from:
+ *   - field split of each float into its biased exponent and the rest:
+ *     THEORY-599 (nucleation note on ZipNN), "What was actually shown",
+ *     per-field compressibility (ZipNN Table II): the exponent is extracted,
+ *     the sign and fraction bytes are kept as they are;
+ *     FP8: "Lossless Compression of Neural Network Components ... in
+ *     Low-Precision Formats", Abstract: exponent and mantissa are separated
+ *     and entropy-coded independently.
+ *   - order-0 Huffman coding of the exponent per chunk: THEORY-599,
+ *     "Order-0 only (ZipNN section III-A b)".
+ *   - grouped chunks sharing Huffman tables, chosen by a reusable setup:
+ *     "NeuralZip: Reusable Setup for Fast Lossless Compression", Abstract.
+ * Everything the pages leave open (code-length limit, segment size, bit
+ * order, container) is fixed by the format description in this header's
+ * companion zno.c, one reading per comment.
+ */
+#ifndef ZNO_H
+#define ZNO_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ZNO_BF16 = 0, ZNO_FP32 = 1, ZNO_FP8_E4M3 = 2 };
+enum { ZNO_OK = 0, ZNO_ERR_ARG = -1, ZNO_ERR_CORRUPT = -2, ZNO_ERR_CAPACITY = -3,
+       ZNO_ERR_TABLESET = -4, ZNO_ERR_NOMEM = -6 };
+enum { ZNO_RAW = 0, ZNO_CONST = 1, ZNO_HUFF = 2, ZNO_GROUP = 3 };
+
+typedef struct zno_tableset zno_tableset;
+
+/* Per-call diagnostics (not part of the format). */
+typedef struct {
+  uint64_t mode_count[4][4];   /* [coded stream][mode] */
+  uint64_t stream_bytes[4];    /* record bytes per coded stream, headers included */
+  uint64_t payload_bits[4];    /* Huffman/raw payload bits per coded stream */
+  uint64_t raw_plane_bytes;    /* always-raw section bytes */
+  uint64_t escapes;            /* chunks whose group table missed a symbol */
+} zno_stats;
+
+/* ---- single steps, exported so tests can pin each one ---- */
+void zno_split(int dtype, const void *in, uint64_t n, uint8_t *planes /* [n_coded][n] */,
+               uint8_t *rawbits /* [n]: BF16 sign+fraction byte, FP8 sign bit, FP32 unused */);
+void zno_merge(int dtype, const uint8_t *planes, const uint8_t *rawbits, uint64_t n, void *out);
+int  zno_code_lengths(const uint64_t *hist, int alphabet, int max_len, uint8_t *len);
+int  zno_group_lengths(const uint64_t *hist, int alphabet, int max_len, uint8_t *len);
+void zno_canonical_codes(const uint8_t *len, int alphabet, int max_len, uint32_t *code);
+
+/* ---- container ---- */
+int zno_compress_bound(int dtype, const uint64_t *n_elems, int n_tensors, uint32_t chunk_bytes,
+                       uint64_t *bound);
+int zno_compress(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,
+                 uint32_t chunk_bytes, const zno_tableset *ts, void *out, uint64_t cap,
+                 uint64_t *out_bytes, zno_stats *stats);
+int zno_header(const void *in, uint64_t in_bytes, int *dtype, int *n_tensors, uint64_t *n_total,
+               uint32_t *chunk_bytes, uint32_t *n_chunks, uint64_t *total_bytes, uint64_t *ts_hash);
+int zno_decompress(const void *in, uint64_t in_bytes, const zno_tableset *ts, void *const *outs,
+                   const uint64_t *n_elems, int n_tensors);
+
+/* One chunk record alone (for sampled checks of large containers). */
+int zno_encode_chunk(int dtype, const void *chunk, uint64_t n, const uint8_t *group_len /* or NULL */,
+                     int group_id, void *rec, uint64_t cap, uint64_t *rec_bytes, int *escape);
+
+/* ---- NeuralZip-style setup ---- */
+int zno_setup(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,
+              uint32_t chunk_bytes, int n_groups, zno_tableset **out);
+void zno_tableset_free(zno_tableset *ts);
+int zno_tableset_info(const zno_tableset *ts, int *n_groups, uint32_t *n_chunks, uint64_t *hash);
+int zno_tableset_lengths(const zno_tableset *ts, int g, uint8_t *len /* alphabet */);
+int zno_tableset_map(const zno_tableset *ts, uint8_t *map /* n_chunks */);
+int zno_tableset_cost_history(const zno_tableset *ts, uint64_t *cost /* rounds+1 */);
+int zno_tableset_save(const zno_tableset *ts, void *buf, uint64_t cap, uint64_t *len);
+int zno_tableset_load(const void *buf, uint64_t len, zno_tableset **out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,362 @@
+"""Independent pure-Python restatement of the codec, for tiny inputs only.
+
+Test infrastructure: written separately from both the C oracle and the GPU
+library (different data structures, no shared code), so that a slip in either
+shows up as a disagreement on small cases.  Python integers, one bit at a time.
+
+Textbook pieces restated here:
+  * Huffman's algorithm with a binary heap (optimal unlimited code cost);
+  * brute-force search of all length vectors obeying the Kraft-McMillan
+    inequality (optimal length-limited cost);
+  * package-merge as a coin collector whose items carry explicit symbol
+    multisets (Larmore and Hirschberg, 1990);
+  * canonical codes and LSB-first packing (RFC 1951 sections 3.1.1, 3.2.2).
+"""
+from __future__ import annotations
+
+import heapq
+import itertools
+import math
+import struct
+from collections import Counter
+
+MAX_LEN = 11
+RAW, CONST, HUFF, GROUP = 0, 1, 2, 3
+ESIZE = {0: 2, 1: 4, 2: 1}
+NCODED = {0: 1, 1: 4, 2: 2}
+SEG = {0: 512, 1: 1024, 2: 2048}
+
+
+def kbits(dt, p):
+    return (4 if p == 0 else 3) if dt == 2 else 8
+
+
+# ------------------------------------------------------------ code lengths --
+def huffman_cost(weights):
+    """Total coded bits of Huffman's algorithm (sum of all merge weights)."""
+    w = [x for x in weights if x > 0]
+    if len(w) < 2:
+        return 0
+    heapq.heapify(w)
+    cost = 0
+    while len(w) > 1:
+        a, b = heapq.heappop(w), heapq.heappop(w)
+        cost += a + b
+        heapq.heappush(w, a + b)
+    return cost
+
+
+def huffman_depth(weights):
+    """Longest code length of one Huffman tree (ties broken by insertion)."""
+    items = [(x, i, 0) for i, x in enumerate(w for w in weights if w > 0)]
+    if len(items) < 2:
+        return 0
+    heapq.heapify(items)
+    nxt = len(items)
+    while len(items) > 1:
+        a, b = heapq.heappop(items), heapq.heappop(items)
+        heapq.heappush(items, (a[0] + b[0], nxt, max(a[2], b[2]) + 1))
+        nxt += 1
+    return items[0][2]
+
+
+def brute_force_min_cost(weights, max_len):
+    """min sum(w*l) over l in {1..max_len}^d with sum 2^-l <= 1."""
+    w = [x for x in weights if x > 0]
+    d = len(w)
+    if d < 2:
+        return 0
+    best = None
+    for ls in itertools.product(range(1, max_len + 1), repeat=d):
+        if sum(2.0 ** -l for l in ls) <= 1.0 + 1e-12:
+            c = sum(a * b for a, b in zip(w, ls))
+            best = c if best is None or c < best else best
+    return best
+
+
+def package_merge(hist, max_len=MAX_LEN):
+    """Length vector under the codec's tie rule; zeros when < 2 symbols occur."""
+    leaves = sorted((w, s) for s, w in enumerate(hist) if w > 0)
+    d = len(leaves)
+    out = [0] * len(hist)
+    if d < 2:
+        return out
+    leaf_items = [(w, 0, Counter({s: 1})) for w, s in leaves]
+    cur = list(leaf_items)
+    for _ in range(max_len - 1):
+        packages = [(cur[2 * k][0] + cur[2 * k + 1][0], 1, cur[2 * k][2] + cur[2 * k + 1][2])
+                    for k in range(len(cur) // 2)]
+        # stable sort: leaves (kind 0) before packages at equal weight,
+        # each kind keeps its own order
+        cur = sorted(leaf_items + packages, key=lambda it: (it[0], it[1]))
+    total = Counter()
+    for it in cur[:2 * d - 2]:
+        total += it[2]
+    for s in range(len(hist)):
+        out[s] = total[s]
+    return out
+
+
+def group_lengths(hist, max_len=MAX_LEN):
+    h = list(hist)
+    present = [s for s, w in enumerate(h) if w > 0]
+    if not present:
+        return [0] * len(h)
+    if len(present) == 1:
+        partner = 0 if present[0] != 0 else 1
+        # a zero-weight leaf: give it a tiny marker and solve by hand
+        lens = [0] * len(h)
+        lens[present[0]] = 1
+        lens[partner] = 1
+        return lens
+    return package_merge(h, max_len)
+
+
+def canonical(lengths):
+    """RFC 1951 section 3.2.2 code values."""
+    maxl = max(lengths) if lengths else 0
+    bl = [0] * (maxl + 2)
+    for l in lengths:
+        if l:
+            bl[l] += 1
+    code, nxt = 0, [0] * (maxl + 2)
+    for bits in range(1, maxl + 1):
+        code = (code + bl[bits - 1]) << 1
+        nxt[bits] = code
+    out = []
+    for l in lengths:
+        if l:
+            out.append(nxt[l])
+            nxt[l] += 1
+        else:
+            out.append(0)
+    return out
+
+
+def entropy_bits(hist):
+    n = sum(hist)
+    return -sum(w / n * math.log2(w / n) for w in hist if w) if n else 0.0
+
+
+# ----------------------------------------------------------------- fields --
+def split(dt, w):
+    if dt == 0:
+        return [(w >> 7) & 0xFF], ((w >> 8) & 0x80) | (w & 0x7F)
+    if dt == 1:
+        return [(w >> 23) & 0xFF, ((w >> 24) & 0x80) | ((w >> 16) & 0x7F), (w >> 8) & 0xFF,
+                w & 0xFF], 0
+    return [(w >> 3) & 0xF, w & 7], w >> 7
+
+
+def merge(dt, syms, raw):
+    if dt == 0:
+        return ((raw & 0x80) << 8) | (syms[0] << 7) | (raw & 0x7F)
+    if dt == 1:
+        return ((syms[1] & 0x80) << 24) | (syms[0] << 23) | ((syms[1] & 0x7F) << 16) | \
+            (syms[2] << 8) | syms[3]
+    return (raw << 7) | (syms[0] << 3) | syms[1]
+
+
+# ------------------------------------------------------------------- bits --
+class Bits:
+    def __init__(self):
+        self.v = 0
+        self.n = 0
+
+    def put(self, bit):
+        self.v |= (bit & 1) << self.n
+        self.n += 1
+
+    def code(self, c, l):
+        for i in range(l - 1, -1, -1):
+            self.put(c >> i)
+
+    def value(self, v, k):
+        for i in range(k):
+            self.put(v >> i)
+
+    def tobytes(self, nbytes):
+        return self.v.to_bytes(nbytes, "little")
+
+
+def a16(x):
+    return (x + 15) & ~15
+
+
+def section(mode, k, n, nseg, bits):
+    head = 8 + ((1 << k) // 2 if mode == HUFF else 0) + (2 * nseg if mode in (HUFF, GROUP) else 0)
+    pay = 4 * ((bits + 31) // 32) if mode in (HUFF, GROUP) else ((n * k + 7) // 8 if mode == RAW else 0)
+    return a16(head), pay
+
+
+def encode_stream(syms, k, S, group=None):
+    """One stream section; group = (lengths, id) to try GROUP mode."""
+    n = len(syms)
+    A = 1 << k
+    h = [0] * A
+    for s in syms:
+        h[s] += 1
+    nseg = (n + S - 1) // S
+    present = [s for s in range(A) if h[s]]
+    if len(present) == 1:
+        mode, aux, lens = CONST, present[0], None
+    else:
+        rh, rp = section(RAW, k, n, nseg, 0)
+        raw_size = rh + a16(rp)
+        mode, aux, lens = RAW, 0, None
+        tried = False
+        if group is not None:
+            gl, gid = group
+            if all(gl[s] > 0 for s in present):
+                tried = True
+                bits = sum(h[s] * gl[s] for s in range(A))
+                gh, gp = section(GROUP, k, n, nseg, bits)
+                if gh + a16(gp) < raw_size:
+                    mode, aux, lens = GROUP, gid, list(gl)
+        if not tried:
+            ln = package_merge(h)
+            bits = sum(h[s] * ln[s] for s in range(A))
+            hh, hp = section(HUFF, k, n, nseg, bits)
+            if hh + a16(hp) < raw_size:
+                mode, lens = HUFF, ln
+    bits = sum(h[s] * lens[s] for s in range(A)) if lens else 0
+    head, pay = section(mode, k, n, nseg, bits)
+    out = bytearray(head + a16(pay))
+    struct.pack_into("<BBHI", out, 0, mode, aux, nseg, pay)
+    pos = 8
+    if mode == HUFF:
+        for s in range(0, A, 2):
+            out[pos + s // 2] = lens[s] | (lens[s + 1] << 4)
+        pos += A // 2
+    bw = Bits()
+    if mode in (HUFF, GROUP):
+        codes = canonical(lens)
+        for j in range(nseg):
+            b0 = bw.n
+            for s in syms[j * S:(j + 1) * S]:
+                bw.code(codes[s], lens[s])
+            struct.pack_into("<H", out, pos + 2 * j, bw.n - b0)
+    elif mode == RAW:
+        for s in syms:
+            bw.value(s, k)
+    if pay:
+        out[head:head + pay] = bw.tobytes(pay)
+    return bytes(out)
+
+
+def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0):
+    """tensors: lists of ints (bit patterns); groups: (lengths per group, map)."""
+    T = len(tensors)
+    ce = chunk_bytes // ESIZE[dt]
+    nch = [(len(t) + ce - 1) // ce for t in tensors]
+    M = sum(nch)
+    off_dir = 64 + 16 * T
+    cur = a16(off_dir + 8 * (M + 1))
+    raw_off = []
+    raw_size = {0: lambda n: n, 1: lambda n: 0, 2: lambda n: (n + 7) // 8}[dt]
+    for t in tensors:
+        raw_off.append(cur)
+        cur = a16(cur + raw_size(len(t)))
+    off_rec = cur
+    recs, c = [], 0
+    for ti, t in enumerate(tensors):
+        for i0 in range(0, len(t), ce):
+            chunk = t[i0:i0 + ce]
+            planes = [[] for _ in range(NCODED[dt])]
+            for w in chunk:
+                sy, _ = split(dt, w)
+                for p in range(NCODED[dt]):
+                    planes[p].append(sy[p])
+            rec = b""
+            for p in range(NCODED[dt]):
+                grp = None
+                if groups is not None and p == 0:
+                    grp = (groups[0][groups[1][c]], groups[1][c])
+                rec += encode_stream(planes[p], kbits(dt, p), SEG[dt], grp)
+            recs.append(rec)
+            c += 1
+    total = off_rec + sum(len(r) for r in recs) + 16
+    out = bytearray(total)
+    struct.pack_into("<IHBBIIQIHBBQQQQ", out, 0, 0x31464E5A, 1, dt, 1 if groups else 0, T,
+                     chunk_bytes, sum(len(t) for t in tensors), M, SEG[dt], MAX_LEN, NCODED[dt],
+                     ts_hash if groups else 0, off_dir, off_rec, total)
+    for ti, t in enumerate(tensors):
+        struct.pack_into("<QQ", out, 64 + 16 * ti, len(t), raw_off[ti])
+        for i, w in enumerate(t):
+            _, raw = split(dt, w)
+            if dt == 0:
+                out[raw_off[ti] + i] = raw
+            elif dt == 2 and raw:
+                out[raw_off[ti] + i // 8] |= 1 << (i % 8)
+    pos = off_rec
+    for ci, r in enumerate(recs):
+        struct.pack_into("<Q", out, off_dir + 8 * ci, pos)
+        out[pos:pos + len(r)] = r
+        pos += len(r)
+    struct.pack_into("<Q", out, off_dir + 8 * M, pos)
+    return bytes(out)
+
+
+def decode_container(blob, group_lengths_table=None):
+    """Parses and decodes a container; returns the list of tensors (ints)."""
+    (magic, ver, dt, flags, T, cb, ntot, M, S, L, nc, h, off_dir, off_rec,
+     total) = struct.unpack_from("<IHBBIIQIHBBQQQQ", blob, 0)
+    assert magic == 0x31464E5A and ver == 1 and L == MAX_LEN
+    ce = cb // ESIZE[dt]
+    outs, c = [], 0
+    for ti in range(T):
+        n, roff = struct.unpack_from("<QQ", blob, 64 + 16 * ti)
+        vals = []
+        for i0 in range(0, n, ce):
+            m = min(ce, n - i0)
+            pos = struct.unpack_from("<Q", blob, off_dir + 8 * c)[0]
+            planes = []
+            for p in range(nc):
+                k = kbits(dt, p)
+                A = 1 << k
+                mode, aux, nseg, pay = struct.unpack_from("<BBHI", blob, pos)
+                q = pos + 8
+                syms = []
+                if mode == CONST:
+                    syms = [aux] * m
+                    head = 16
+                elif mode == RAW:
+                    head = 16
+                    v = int.from_bytes(blob[pos + head:pos + head + pay], "little")
+                    syms = [(v >> (i * k)) & (A - 1) for i in range(m)]
+                else:
+                    if mode == HUFF:
+                        lens = []
+                        for s in range(0, A, 2):
+                            lens += [blob[q + s // 2] & 15, blob[q + s // 2] >> 4]
+                        q += A // 2
+                    else:
+                        lens = list(group_lengths_table[aux])
+                    seg_bits = [struct.unpack_from("<H", blob, q + 2 * j)[0] for j in range(nseg)]
+                    head = a16(q + 2 * nseg - pos)
+                    codes = canonical(lens)
+                    table = {(lens[s], codes[s]): s for s in range(A) if lens[s]}
+                    v = int.from_bytes(blob[pos + head:pos + head + pay], "little")
+                    bitpos = 0
+                    for j in range(nseg):
+                        end = bitpos + seg_bits[j]
+                        for _ in range(min(S, m - j * S)):
+                            code, l = 0, 0
+                            while True:
+                                code = (code << 1) | ((v >> bitpos) & 1)
+                                bitpos += 1
+                                l += 1
+                                if (l, code) in table:
+                                    syms.append(table[(l, code)])
+                                    break
+                                assert l < MAX_LEN
+                        assert bitpos == end
+                planes.append(syms)
+                pos += head + a16(pay)
+            for i in range(m):
+                e = i0 + i
+                raw = blob[roff + e] if dt == 0 else ((blob[roff + e // 8] >> (e % 8)) & 1 if dt == 2 else 0)
+                vals.append(merge(dt, [planes[p][i] for p in range(nc)], raw))
+            c += 1
+        outs.append(vals)
+    return outs
