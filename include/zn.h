@@ -1,0 +1,154 @@
+/*
+ * zn.h -- C ABI of libzn.so, a lossless codec for floating-point tensors on
+ * AMD MI355X (gfx950): exponent extraction, per-chunk order-0 histograms,
+ * length-limited canonical Huffman codes, chunk-parallel decoding, and
+ * NeuralZip-style grouped code tables built by a reusable setup.
+ *
+ * What each call computes, by source:
+ *   - splitting every float into its exponent and the rest, coding the
+ *     exponent and keeping sign and fraction bytes as they are: THEORY-599
+ *     (nucleation note on "ZipNN: Lossless Compression for AI Models"),
+ *     "What was actually shown", per-field compressibility (ZipNN Table II);
+ *   - an order-0 Huffman code of the exponent per chunk: THEORY-599,
+ *     order-0 only (ZipNN section III-A b);
+ *   - FP8 E4M3: exponent and mantissa separated and entropy-coded
+ *     independently: "Lossless Compression of Neural Network Components:
+ *     Weights, Checkpoints, and K/V Caches in Low-Precision Formats",
+ *     Abstract;
+ *   - grouping chunks with similar exponent distributions, sharing their
+ *     Huffman codes, and choosing these in a setup that later encodings reuse
+ *     while still reading the current values; bit-exact reconstruction:
+ *     "NeuralZip: Reusable Setup for Fast Lossless Compression", Abstract.
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* are device memory owned by the caller (for example
+ *     torch tensors).  h_* are host memory.  The library owns only the opaque
+ *     zn_tableset and the device memory inside it.
+ *   - zn_compress and zn_decompress allocate nothing; they launch on the
+ *     caller's stream in stream order and need d_scratch of at least
+ *     zn_scratch_bytes() bytes (16-byte aligned).  Concurrent calls on one
+ *     tableset need distinct scratch buffers.
+ *   - Inputs are read-only; outputs must not overlap inputs.  Tensor data
+ *     pointers should be 16-byte aligned (unaligned ones take a slow path).
+ *   - Calls return a zn_status and never throw.  HIP failures map to
+ *     ZN_ERR_HIP.  A corrupt container gives ZN_ERR_CORRUPT and leaves the
+ *     outputs unspecified; it never makes the library read or write outside
+ *     the buffers it was given.
+ *   - Bitstreams are bit-identical to the CPU oracle's for the same inputs.
+ */
+#ifndef ZN_H
+#define ZN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ZN_BF16 = 0, ZN_FP32 = 1, ZN_FP8_E4M3 = 2 } zn_dtype;
+
+typedef enum {
+  ZN_OK = 0,
+  ZN_ERR_ARG = -1,       /* bad argument (null pointer, size, dtype, chunk size) */
+  ZN_ERR_CORRUPT = -2,   /* container fails a structural or bitstream check      */
+  ZN_ERR_CAPACITY = -3,  /* output or scratch buffer too small                    */
+  ZN_ERR_TABLESET = -4,  /* container needs another tableset (hash mismatch)     */
+  ZN_ERR_HIP = -5,       /* a HIP runtime call failed                             */
+  ZN_ERR_NOMEM = -6      /* host or setup-time device allocation failed           */
+} zn_status;
+
+/* A plan for a fixed list of tensor sizes: dtype, chunk size, the container
+ * layout, and optionally K grouped code tables.  Library-owned. */
+typedef struct zn_tableset zn_tableset;
+
+/* zn_setup -- the reusable setup ("NeuralZip", Abstract).
+ *   n_elems[n_tensors]: element count of each tensor (host array).
+ *   chunk_bytes: uncompressed bytes per chunk; a multiple of 4096 in
+ *     [4096, 1 MiB].  Chunks never span tensors.
+ *   n_groups == 0: per-chunk code tables only; d_tensors may be NULL and no
+ *     kernel runs.  n_groups in [1, 255]: every chunk of the given tensors is
+ *     histogrammed on the GPU, chunks are grouped by their exponent
+ *     histograms (integer Lloyd rounds) and each group gets one shared code;
+ *     d_tensors (host array of device pointers) must then be valid.
+ * Allocates device memory for the plan (this is the only call that does,
+ * with zn_plan_from_container and zn_tableset_load).  Synchronises stream. */
+zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t *n_elems,
+                   int n_tensors, uint32_t chunk_bytes, int n_groups, hipStream_t stream,
+                   zn_tableset **out);
+
+/* zn_plan_from_container -- a plan (without groups) that matches the layout
+ * of an existing container; reads its header and tensor table with one
+ * synchronous copy.  Containers that use group tables need the tableset they
+ * were compressed with (ZN_ERR_TABLESET here). */
+zn_status zn_plan_from_container(const void *d_in, uint64_t in_bytes, hipStream_t stream,
+                                 zn_tableset **out);
+
+/* Plan facts.  Any output pointer may be NULL; h_n_elems gets n_tensors values. */
+zn_status zn_tableset_info(const zn_tableset *ts, zn_dtype *dtype, int *n_tensors,
+                           uint64_t *h_n_elems, uint32_t *chunk_bytes, uint32_t *n_chunks,
+                           int *n_groups, uint64_t *hash);
+
+/* Worst-case container size for the plan's tensors (host-only arithmetic). */
+zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes);
+
+/* Device scratch needed by zn_compress / zn_decompress for this plan. */
+zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes);
+
+/* zn_compress -- one container holding every tensor of the plan.
+ *   d_in_ptrs: DEVICE array of n_tensors device pointers to the tensors.
+ *   d_out / out_cap: output buffer; out_cap >= zn_compress_bound() always fits.
+ *   out_bytes: host; if non-NULL the call synchronises the stream and returns
+ *     the container size (and ZN_ERR_CAPACITY if it did not fit).  If NULL
+ *     the call is asynchronous; the size is the u64 at d_out + 56 and the
+ *     capacity flag is the u32 at d_scratch once the stream has finished.
+ * Per-chunk tables when the plan has no groups; with groups, chunk c uses
+ * its group's shared code unless the chunk holds a symbol that code lacks
+ * (an escape), which is then coded with its own table. */
+zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void *d_out,
+                      uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
+                      uint64_t scratch_bytes, hipStream_t stream);
+
+/* zn_decompress -- exact reconstruction of every tensor of the container.
+ *   d_out_ptrs: DEVICE array of n_tensors device pointers, each large enough
+ *     for its tensor.
+ *   sync != 0: synchronises and returns ZN_ERR_CORRUPT if any check failed.
+ *   sync == 0: asynchronous; the u32 at d_scratch is non-zero afterwards if
+ *     a check failed.
+ * The plan must match the container's layout; a container built with group
+ * tables needs the same tableset (checked through its hash). */
+zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
+                        void *const *d_out_ptrs, void *d_scratch, uint64_t scratch_bytes,
+                        int sync, hipStream_t stream);
+
+/* Serialisation of a plan, byte-identical to the CPU oracle's; its FNV-1a-64
+ * hash is what containers record. */
+zn_status zn_tableset_save(const zn_tableset *ts, void *h_buf, uint64_t cap, uint64_t *len);
+zn_status zn_tableset_load(const void *h_buf, uint64_t len, zn_tableset **out);
+/* Group g's code lengths (alphabet of the exponent stream) and the chunk map. */
+zn_status zn_tableset_lengths(const zn_tableset *ts, int g, uint8_t *h_len);
+zn_status zn_tableset_map(const zn_tableset *ts, uint8_t *h_map);
+/* Setup objective (total coded exponent bits) before each of the 8 Lloyd
+ * rounds and after the last one: h_cost[9]. */
+zn_status zn_tableset_cost_history(const zn_tableset *ts, uint64_t *h_cost);
+void zn_tableset_free(zn_tableset *ts);
+
+const char *zn_status_str(zn_status s);
+
+/* ---- single steps, for parity tests of each stage (asynchronous) ----
+ * zn_debug_histograms: order-0 histograms of every coded stream of every
+ *   chunk of the plan: d_hist[n_chunks][n_coded][256] u32.
+ * zn_debug_code_lengths: code lengths of n histograms (d_hist[n][256] u64)
+ *   by the device package-merge; group_rule != 0 applies the group-table
+ *   rule for single-symbol histograms; d_len[n][256]. */
+zn_status zn_debug_histograms(const zn_tableset *ts, const void *const *d_in_ptrs,
+                              uint32_t *d_hist, hipStream_t stream);
+zn_status zn_debug_code_lengths(const uint64_t *d_hist, int n, int alphabet, int group_rule,
+                                uint8_t *d_len, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

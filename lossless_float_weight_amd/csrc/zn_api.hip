@@ -1,0 +1,543 @@
+// zn_api.hip -- the C ABI of libzn.so (declared in include/zn.h).
+//
+// Host code: argument checks, the container layout, the tableset (plan plus
+// optional group tables) and the order of launches on the caller's stream.
+// Every step of compression and decompression runs in the kernels of
+// zn_encode.hip / zn_decode.hip; the setup's only host step is sorting the
+// chunk keys once for the initial groups.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/zn.h"
+#include "zn_internal.h"
+
+using namespace zn;
+
+struct zn_tableset {
+  int dtype = 0, T = 0, K = 0;
+  uint32_t chunk_bytes = 0, chunk_elems = 0, n_chunks = 0;
+  uint64_t off_dir = 0, off_records = 0, hash = 0;
+  std::vector<uint64_t> n, raw;
+  std::vector<uint32_t> chunk0;
+  std::vector<uint8_t> hdr;            // header template + tensor table
+  std::vector<uint8_t> len;            // [K][256] group code lengths
+  std::vector<uint8_t> map;            // [n_chunks] group of each chunk
+  std::vector<unsigned long long> cost;  // objective per setup round (diagnostic)
+  // device copies
+  uint64_t *d_n = nullptr, *d_raw = nullptr;
+  uint32_t *d_chunk0 = nullptr;
+  uint8_t *d_hdr = nullptr;
+  uint8_t *d_map = nullptr, *d_len = nullptr;
+  uint32_t *d_enc = nullptr, *d_lut = nullptr;
+  int device = 0;
+};
+
+namespace {
+
+bool valid_dtype(int dt) { return dt == BF16 || dt == FP32 || dt == FP8; }
+bool valid_chunk(uint32_t cb) { return cb >= 4096 && cb <= (1u << 20) && cb % 4096 == 0; }
+
+void put_u16(uint8_t *p, uint32_t v) { p[0] = v & 0xFF; p[1] = (v >> 8) & 0xFF; }
+void put_u32(uint8_t *p, uint32_t v) { for (int i = 0; i < 4; i++) p[i] = (v >> (8 * i)) & 0xFF; }
+void put_u64(uint8_t *p, uint64_t v) { for (int i = 0; i < 8; i++) p[i] = (v >> (8 * i)) & 0xFF; }
+uint32_t get_u16(const uint8_t *p) { return p[0] | (uint32_t(p[1]) << 8); }
+uint32_t get_u32(const uint8_t *p) { return p[0] | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16) | (uint32_t(p[3]) << 24); }
+uint64_t get_u64(const uint8_t *p) { uint64_t v = 0; for (int i = 7; i >= 0; i--) v = (v << 8) | p[i]; return v; }
+
+#define HIPCHK(x)                        \
+  do {                                   \
+    if ((x) != hipSuccess) return ZN_ERR_HIP; \
+  } while (0)
+
+DevLayout dev_layout(const zn_tableset *ts) {
+  DevLayout L;
+  L.t_n = ts->d_n;
+  L.t_raw = ts->d_raw;
+  L.t_chunk0 = ts->d_chunk0;
+  L.T = ts->T;
+  L.n_chunks = ts->n_chunks;
+  L.chunk_elems = ts->chunk_elems;
+  L.off_dir = ts->off_dir;
+  L.off_records = ts->off_records;
+  return L;
+}
+
+int alphabet0(int dt) { return 1 << kbits(dt, 0); }
+
+uint64_t serial_bytes(const zn_tableset *ts) {
+  return 24 + 8ull * ts->T + uint64_t(ts->K) * (alphabet0(ts->dtype) / 2) + ts->n_chunks;
+}
+void serialise(const zn_tableset *ts, uint8_t *b) {
+  const int A = alphabet0(ts->dtype);
+  put_u32(b, kTsMagic);
+  put_u16(b + 4, kVersion);
+  b[6] = uint8_t(ts->dtype);
+  b[7] = uint8_t(ts->K);
+  put_u32(b + 8, ts->chunk_bytes);
+  put_u32(b + 12, uint32_t(ts->T));
+  put_u32(b + 16, ts->n_chunks);
+  put_u32(b + 20, kMaxLen);
+  uint8_t *q = b + 24;
+  for (int t = 0; t < ts->T; t++, q += 8) put_u64(q, ts->n[t]);
+  for (int g = 0; g < ts->K; g++)
+    for (int s = 0; s < A; s += 2) *q++ = uint8_t(ts->len[g * 256 + s] | (ts->len[g * 256 + s + 1] << 4));
+  if (ts->n_chunks) memcpy(q, ts->map.data(), ts->n_chunks);
+}
+uint64_t fnv1a64(const uint8_t *b, uint64_t n) {
+  uint64_t h = 14695981039346656037ull;
+  for (uint64_t i = 0; i < n; i++) {
+    h ^= b[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+void free_device(zn_tableset *ts) {
+  (void)hipFree(ts->d_n);
+  (void)hipFree(ts->d_raw);
+  (void)hipFree(ts->d_chunk0);
+  (void)hipFree(ts->d_hdr);
+  (void)hipFree(ts->d_map);
+  (void)hipFree(ts->d_len);
+  (void)hipFree(ts->d_enc);
+  (void)hipFree(ts->d_lut);
+  ts->d_n = ts->d_raw = nullptr;
+  ts->d_chunk0 = nullptr;
+  ts->d_hdr = ts->d_map = ts->d_len = nullptr;
+  ts->d_enc = ts->d_lut = nullptr;
+}
+
+// Host layout of the container for the plan's tensors.
+zn_status make_plan(zn_tableset *ts, int dt, const uint64_t *n, int T, uint32_t cb) {
+  if (!valid_dtype(dt) || !valid_chunk(cb) || T < 1 || !n) return ZN_ERR_ARG;
+  ts->dtype = dt;
+  ts->T = T;
+  ts->chunk_bytes = cb;
+  ts->chunk_elems = cb / uint32_t(esize(dt));
+  ts->n.assign(n, n + T);
+  ts->raw.assign(T, 0);
+  ts->chunk0.assign(T + 1, 0);
+  uint64_t M = 0;
+  for (int t = 0; t < T; t++) {
+    if (n[t] > (1ull << 40)) return ZN_ERR_ARG;
+    ts->chunk0[t] = uint32_t(M);
+    M += (n[t] + ts->chunk_elems - 1) / ts->chunk_elems;
+    if (M > 0x7FFFFFFFull) return ZN_ERR_ARG;
+  }
+  ts->chunk0[T] = uint32_t(M);
+  ts->n_chunks = uint32_t(M);
+  ts->off_dir = 64 + 16ull * T;
+  uint64_t cur = align16(ts->off_dir + 8 * (M + 1));
+  for (int t = 0; t < T; t++) {
+    ts->raw[t] = cur;
+    cur = align16(cur + rawplane_bytes(dt, n[t]));
+  }
+  ts->off_records = cur;
+  ts->map.assign(M, 0);
+  return ZN_OK;
+}
+
+// Header template (total_bytes left 0), hash, and device copies of the plan.
+zn_status finish_plan(zn_tableset *ts) {
+  std::vector<uint8_t> ser(serial_bytes(ts));
+  serialise(ts, ser.data());
+  ts->hash = fnv1a64(ser.data(), ser.size());
+  uint64_t ntot = 0;
+  for (auto v : ts->n) ntot += v;
+  ts->hdr.assign(64 + 16ull * ts->T, 0);
+  uint8_t *h = ts->hdr.data();
+  put_u32(h, kMagic);
+  put_u16(h + 4, kVersion);
+  h[6] = uint8_t(ts->dtype);
+  h[7] = ts->K ? 1 : 0;
+  put_u32(h + 8, uint32_t(ts->T));
+  put_u32(h + 12, ts->chunk_bytes);
+  put_u64(h + 16, ntot);
+  put_u32(h + 24, ts->n_chunks);
+  put_u16(h + 28, uint32_t(segsyms(ts->dtype)));
+  h[30] = kMaxLen;
+  h[31] = uint8_t(ncoded(ts->dtype));
+  put_u64(h + 32, ts->K ? ts->hash : 0);
+  put_u64(h + 40, ts->off_dir);
+  put_u64(h + 48, ts->off_records);
+  for (int t = 0; t < ts->T; t++) {
+    put_u64(h + 64 + 16 * t, ts->n[t]);
+    put_u64(h + 72 + 16 * t, ts->raw[t]);
+  }
+  if (!ts->d_n) {
+    HIPCHK(hipMalloc(&ts->d_n, 8ull * ts->T));
+    HIPCHK(hipMalloc(&ts->d_raw, 8ull * ts->T));
+    HIPCHK(hipMalloc(&ts->d_chunk0, 4ull * (ts->T + 1)));
+    HIPCHK(hipMalloc(&ts->d_hdr, ts->hdr.size()));
+  }
+  HIPCHK(hipMemcpy(ts->d_n, ts->n.data(), 8ull * ts->T, hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(ts->d_raw, ts->raw.data(), 8ull * ts->T, hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(ts->d_chunk0, ts->chunk0.data(), 4ull * (ts->T + 1), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(ts->d_hdr, ts->hdr.data(), ts->hdr.size(), hipMemcpyHostToDevice));
+  return ZN_OK;
+}
+
+// Device group tables (encode codes, decode tables) from host lengths and map.
+zn_status upload_groups(zn_tableset *ts, hipStream_t s) {
+  const int K = ts->K;
+  if (!K) return ZN_OK;
+  if (!ts->d_map) {
+    HIPCHK(hipMalloc(&ts->d_map, ts->n_chunks ? ts->n_chunks : 1));
+    HIPCHK(hipMalloc(&ts->d_len, 256ull * K));
+    HIPCHK(hipMalloc(&ts->d_enc, 4ull * 256 * K));
+    HIPCHK(hipMalloc(&ts->d_lut, 4ull * kLutSize * K));
+  }
+  if (ts->n_chunks)
+    HIPCHK(hipMemcpyAsync(ts->d_map, ts->map.data(), ts->n_chunks, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(ts->d_len, ts->len.data(), 256ull * K, hipMemcpyHostToDevice, s));
+  uint32_t *ctl = nullptr;
+  HIPCHK(hipMalloc(&ctl, 4));
+  HIPCHK(hipMemsetAsync(ctl, 0, 4, s));
+  hipError_t e = launch_group_tables(ts->d_len, K, alphabet0(ts->dtype), ts->d_enc, ts->d_lut, ctl, s);
+  uint32_t flag = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&flag, ctl, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(ctl);
+  if (e != hipSuccess) return ZN_ERR_HIP;
+  return flag ? ZN_ERR_TABLESET : ZN_OK;
+}
+
+template <class T>
+struct DevBuf {
+  T *p = nullptr;
+  ~DevBuf() { (void)hipFree(p); }
+  hipError_t alloc(size_t n) { return hipMalloc(&p, sizeof(T) * (n ? n : 1)); }
+};
+
+// NeuralZip grouping on the GPU (integer Lloyd rounds); see zn_setup.hip.
+zn_status run_grouping(zn_tableset *ts, const void *const *d_tensors, hipStream_t s) {
+  const int dt = ts->dtype, K = ts->K, NC = ncoded(dt), A = alphabet0(dt);
+  const uint32_t M = ts->n_chunks;
+  const int stride = NC * 256;
+  ts->len.assign(256ull * K, 0);
+  ts->cost.assign(kRounds + 1, 0);
+  DevBuf<const uint8_t *> ptrs;
+  DevBuf<uint32_t> hist;
+  DevBuf<unsigned long long> keys, pooled, cost;
+  DevBuf<uint8_t> map, len;
+  DevBuf<uint32_t> dummy;
+  if (ptrs.alloc(ts->T) || hist.alloc(uint64_t(M) * stride) || keys.alloc(M) ||
+      pooled.alloc(256ull * K) || cost.alloc(1) || map.alloc(M) || len.alloc(256ull * K))
+    return ZN_ERR_NOMEM;
+  HIPCHK(hipMemcpyAsync(ptrs.p, d_tensors, sizeof(void *) * ts->T, hipMemcpyHostToDevice, s));
+  const DevLayout L = dev_layout(ts);
+  HIPCHK(launch_hist_all(dt, L, ptrs.p, hist.p, s));
+  HIPCHK(launch_keys(hist.p, stride, A, L, keys.p, s));
+  std::vector<unsigned long long> hkeys(M);
+  HIPCHK(hipMemcpyAsync(hkeys.data(), keys.p, 8ull * M, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  // initial groups: chunks ordered by (key, chunk), cut into K even runs
+  std::vector<uint32_t> order(M);
+  for (uint32_t c = 0; c < M; c++) order[c] = c;
+  std::sort(order.begin(), order.end(), [&](uint32_t x, uint32_t y) {
+    return hkeys[x] != hkeys[y] ? hkeys[x] < hkeys[y] : x < y;
+  });
+  for (int g = 0; g < K; g++)
+    for (uint64_t i = uint64_t(M) * g / K; i < uint64_t(M) * (g + 1) / K; i++) ts->map[order[i]] = uint8_t(g);
+  HIPCHK(hipMemcpyAsync(map.p, ts->map.data(), M, hipMemcpyHostToDevice, s));
+  for (int r = 0; r <= kRounds; r++) {
+    HIPCHK(hipMemsetAsync(pooled.p, 0, 8 * 256ull * K, s));
+    HIPCHK(launch_pool(hist.p, stride, A, M, map.p, pooled.p, K, s));
+    HIPCHK(launch_lengths(reinterpret_cast<const uint64_t *>(pooled.p), K, A, 1, len.p, s));
+    HIPCHK(hipMemsetAsync(cost.p, 0, 8, s));
+    // the last pass only measures the final assignment
+    HIPCHK(launch_assign(hist.p, stride, A, M, len.p, K, r < kRounds, map.p, cost.p, s));
+    HIPCHK(hipMemcpyAsync(&ts->cost[r], cost.p, 8, hipMemcpyDeviceToHost, s));
+  }
+  HIPCHK(hipMemcpyAsync(ts->len.data(), len.p, 256ull * K, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(ts->map.data(), map.p, M, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  return ZN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *zn_status_str(zn_status s) {
+  switch (s) {
+    case ZN_OK: return "ok";
+    case ZN_ERR_ARG: return "invalid argument";
+    case ZN_ERR_CORRUPT: return "corrupt container";
+    case ZN_ERR_CAPACITY: return "buffer too small";
+    case ZN_ERR_TABLESET: return "tableset mismatch";
+    case ZN_ERR_HIP: return "HIP runtime error";
+    case ZN_ERR_NOMEM: return "out of memory";
+  }
+  return "unknown status";
+}
+
+void zn_tableset_free(zn_tableset *ts) {
+  if (!ts) return;
+  free_device(ts);
+  delete ts;
+}
+
+zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t *n_elems,
+                   int n_tensors, uint32_t chunk_bytes, int n_groups, hipStream_t stream,
+                   zn_tableset **out) {
+  if (!out || n_groups < 0 || n_groups > 255) return ZN_ERR_ARG;
+  *out = nullptr;
+  zn_tableset *ts = new (std::nothrow) zn_tableset;
+  if (!ts) return ZN_ERR_NOMEM;
+  zn_status st = make_plan(ts, dtype, n_elems, n_tensors, chunk_bytes);
+  ts->K = n_groups;
+  if (st == ZN_OK && n_groups > 0) {
+    if (!d_tensors) st = ZN_ERR_ARG;
+    for (int t = 0; st == ZN_OK && t < n_tensors; t++)
+      if (n_elems[t] && !d_tensors[t]) st = ZN_ERR_ARG;
+    if (st == ZN_OK) st = finish_plan(ts);  // device layout is needed by the kernels
+    if (st == ZN_OK) st = run_grouping(ts, d_tensors, stream);
+  }
+  if (st == ZN_OK) st = finish_plan(ts);
+  if (st == ZN_OK) st = upload_groups(ts, stream);
+  if (st != ZN_OK) {
+    zn_tableset_free(ts);
+    return st;
+  }
+  *out = ts;
+  return ZN_OK;
+}
+
+zn_status zn_plan_from_container(const void *d_in, uint64_t in_bytes, hipStream_t stream,
+                                 zn_tableset **out) {
+  if (!d_in || !out || in_bytes < 64) return ZN_ERR_ARG;
+  *out = nullptr;
+  uint8_t h[64];
+  HIPCHK(hipMemcpyAsync(h, d_in, 64, hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  if (get_u32(h) != kMagic || get_u16(h + 4) != kVersion || !valid_dtype(h[6]) || h[7] > 1 ||
+      h[30] != kMaxLen || h[31] != ncoded(h[6]) || get_u16(h + 28) != uint32_t(segsyms(h[6])))
+    return ZN_ERR_CORRUPT;
+  if (h[7] & 1) return ZN_ERR_TABLESET;
+  const uint32_t T = get_u32(h + 8);
+  if (T < 1 || 64 + 16ull * T > in_bytes) return ZN_ERR_CORRUPT;
+  std::vector<uint8_t> tt(16ull * T);
+  HIPCHK(hipMemcpyAsync(tt.data(), static_cast<const uint8_t *>(d_in) + 64, tt.size(),
+                        hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  std::vector<uint64_t> n(T);
+  for (uint32_t t = 0; t < T; t++) n[t] = get_u64(tt.data() + 16 * t);
+  zn_tableset *ts = new (std::nothrow) zn_tableset;
+  if (!ts) return ZN_ERR_NOMEM;
+  zn_status st = make_plan(ts, h[6], n.data(), int(T), get_u32(h + 12));
+  if (st == ZN_ERR_ARG) st = ZN_ERR_CORRUPT;
+  if (st == ZN_OK) st = finish_plan(ts);
+  if (st != ZN_OK) {
+    zn_tableset_free(ts);
+    return st;
+  }
+  *out = ts;
+  return ZN_OK;
+}
+
+zn_status zn_tableset_info(const zn_tableset *ts, zn_dtype *dtype, int *n_tensors, uint64_t *h_n,
+                           uint32_t *chunk_bytes, uint32_t *n_chunks, int *n_groups, uint64_t *hash) {
+  if (!ts) return ZN_ERR_ARG;
+  if (dtype) *dtype = zn_dtype(ts->dtype);
+  if (n_tensors) *n_tensors = ts->T;
+  if (h_n) memcpy(h_n, ts->n.data(), 8ull * ts->T);
+  if (chunk_bytes) *chunk_bytes = ts->chunk_bytes;
+  if (n_chunks) *n_chunks = ts->n_chunks;
+  if (n_groups) *n_groups = ts->K;
+  if (hash) *hash = ts->hash;
+  return ZN_OK;
+}
+
+zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes) {
+  if (!ts || !bytes) return ZN_ERR_ARG;
+  uint64_t b = ts->off_records + 16;
+  for (int t = 0; t < ts->T; t++)
+    for (uint64_t i0 = 0; i0 < ts->n[t]; i0 += ts->chunk_elems) {
+      const uint64_t m = std::min<uint64_t>(ts->chunk_elems, ts->n[t] - i0);
+      for (int p = 0; p < ncoded(ts->dtype); p++) b += section_bytes(RAW, kbits(ts->dtype, p), m, 0, 0);
+    }
+  *bytes = b;
+  return ZN_OK;
+}
+
+zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes) {
+  if (!ts || !bytes) return ZN_ERR_ARG;
+  *bytes = kCtlBytes + 8ull * (ts->n_chunks + 1);
+  return ZN_OK;
+}
+
+zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void *d_out,
+                      uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
+                      uint64_t scratch_bytes, hipStream_t stream) {
+  if (!ts || (!d_in_ptrs && ts->n_chunks) || !d_out || !d_scratch) return ZN_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_scratch) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15))
+    return ZN_ERR_ARG;
+  uint64_t need = 0;
+  zn_scratch_bytes(ts, &need);
+  if (scratch_bytes < need) return ZN_ERR_CAPACITY;
+  if (out_cap < ts->off_records + 16) return ZN_ERR_CAPACITY;
+  uint32_t *ctl = static_cast<uint32_t *>(d_scratch);
+  HIPCHK(launch_zero(ctl, need / 4, stream));
+  EncArgs a;
+  a.L = dev_layout(ts);
+  a.in_ptrs = reinterpret_cast<const uint8_t *const *>(d_in_ptrs);
+  a.group_map = ts->K ? ts->d_map : nullptr;
+  a.group_enc = ts->d_enc;
+  a.group_len = ts->d_len;
+  a.out = static_cast<uint8_t *>(d_out);
+  a.cap = out_cap;
+  a.status = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(d_scratch) + kCtlBytes);
+  a.ctl = ctl;
+  HIPCHK(launch_encode(ts->dtype, a, stream));
+  FinishArgs f;
+  f.L = a.L;
+  f.dtype = ts->dtype;
+  f.hdr = ts->d_hdr;
+  f.hdr_bytes = uint32_t(ts->hdr.size());
+  f.out = a.out;
+  f.cap = out_cap;
+  f.status = a.status;
+  f.ctl = ctl;
+  HIPCHK(launch_finish(f, stream));
+  if (!out_bytes) return ZN_OK;
+  uint32_t flag = 0;
+  uint64_t total = 0;
+  HIPCHK(hipMemcpyAsync(&flag, ctl, 4, hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipMemcpyAsync(&total, a.out + 56, 8, hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  if (flag) return ZN_ERR_CAPACITY;
+  *out_bytes = total;
+  return ZN_OK;
+}
+
+zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
+                        void *const *d_out_ptrs, void *d_scratch, uint64_t scratch_bytes, int sync,
+                        hipStream_t stream) {
+  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks) || !d_scratch) return ZN_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_scratch) & 15) || (reinterpret_cast<uintptr_t>(d_in) & 15))
+    return ZN_ERR_ARG;
+  if (scratch_bytes < kCtlBytes) return ZN_ERR_CAPACITY;
+  if (in_bytes < ts->off_records + 16) return ZN_ERR_CORRUPT;
+  uint32_t *ctl = static_cast<uint32_t *>(d_scratch);
+  HIPCHK(launch_zero(ctl, kCtlBytes / 4, stream));
+  CheckArgs ck;
+  ck.in = static_cast<const uint8_t *>(d_in);
+  ck.in_bytes = in_bytes;
+  ck.hdr = ts->d_hdr;
+  ck.hdr_bytes = uint32_t(ts->hdr.size());
+  ck.hash = ts->hash;
+  ck.K = ts->K;
+  ck.n_chunks = ts->n_chunks;
+  ck.off_dir = ts->off_dir;
+  ck.ctl = ctl;
+  HIPCHK(launch_check(ck, stream));
+  DecArgs a;
+  a.L = dev_layout(ts);
+  a.in = ck.in;
+  a.in_bytes = in_bytes;
+  a.out_ptrs = reinterpret_cast<uint8_t *const *>(d_out_ptrs);
+  a.group_lut = ts->d_lut;
+  a.group_len = ts->d_len;
+  a.K = ts->K;
+  a.ctl = ctl;
+  HIPCHK(launch_decode(ts->dtype, a, stream));
+  if (!sync) return ZN_OK;
+  uint32_t flag = 0;
+  HIPCHK(hipMemcpyAsync(&flag, ctl, 4, hipMemcpyDeviceToHost, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  if (flag & kErrTableset) return ZN_ERR_TABLESET;
+  if (flag) return ZN_ERR_CORRUPT;
+  return ZN_OK;
+}
+
+zn_status zn_tableset_save(const zn_tableset *ts, void *h_buf, uint64_t cap, uint64_t *len) {
+  if (!ts || !len) return ZN_ERR_ARG;
+  *len = serial_bytes(ts);
+  if (!h_buf) return ZN_OK;
+  if (cap < *len) return ZN_ERR_CAPACITY;
+  serialise(ts, static_cast<uint8_t *>(h_buf));
+  return ZN_OK;
+}
+
+zn_status zn_tableset_load(const void *h_buf, uint64_t len, zn_tableset **out) {
+  const uint8_t *b = static_cast<const uint8_t *>(h_buf);
+  if (!b || !out) return ZN_ERR_ARG;
+  *out = nullptr;
+  if (len < 24 || get_u32(b) != kTsMagic || get_u16(b + 4) != kVersion || get_u32(b + 20) != kMaxLen)
+    return ZN_ERR_CORRUPT;
+  const int dt = b[6], K = b[7], T = int(get_u32(b + 12));
+  const uint32_t cb = get_u32(b + 8), M = get_u32(b + 16);
+  if (!valid_dtype(dt) || !valid_chunk(cb) || T < 1 || uint64_t(T) > len / 8) return ZN_ERR_CORRUPT;
+  const int A = alphabet0(dt);
+  if (len != 24 + 8ull * T + uint64_t(K) * (A / 2) + M) return ZN_ERR_CORRUPT;
+  std::vector<uint64_t> n(T);
+  for (int t = 0; t < T; t++) n[t] = get_u64(b + 24 + 8 * t);
+  zn_tableset *ts = new (std::nothrow) zn_tableset;
+  if (!ts) return ZN_ERR_NOMEM;
+  zn_status st = make_plan(ts, dt, n.data(), T, cb);
+  if (st == ZN_OK && ts->n_chunks != M) st = ZN_ERR_CORRUPT;
+  if (st == ZN_OK) {
+    ts->K = K;
+    ts->len.assign(256ull * K, 0);
+    const uint8_t *q = b + 24 + 8ull * T;
+    for (int g = 0; g < K; g++)
+      for (int s = 0; s < A; s += 2, q++) {
+        ts->len[g * 256 + s] = *q & 15;
+        ts->len[g * 256 + s + 1] = *q >> 4;
+        if ((*q & 15) > kMaxLen || (*q >> 4) > kMaxLen) st = ZN_ERR_CORRUPT;
+      }
+    if (M) memcpy(ts->map.data(), q, M);
+    for (uint32_t c = 0; c < M && st == ZN_OK; c++)
+      if (ts->map[c] >= K) st = ZN_ERR_CORRUPT;
+  }
+  if (st == ZN_ERR_ARG) st = ZN_ERR_CORRUPT;
+  if (st == ZN_OK) st = finish_plan(ts);
+  if (st == ZN_OK) st = upload_groups(ts, nullptr);
+  if (st != ZN_OK) {
+    zn_tableset_free(ts);
+    return st;
+  }
+  *out = ts;
+  return ZN_OK;
+}
+
+zn_status zn_tableset_lengths(const zn_tableset *ts, int g, uint8_t *h_len) {
+  if (!ts || !h_len || g < 0 || g >= ts->K) return ZN_ERR_ARG;
+  memcpy(h_len, ts->len.data() + 256ull * g, size_t(alphabet0(ts->dtype)));
+  return ZN_OK;
+}
+
+zn_status zn_tableset_map(const zn_tableset *ts, uint8_t *h_map) {
+  if (!ts || !h_map) return ZN_ERR_ARG;
+  if (ts->n_chunks) memcpy(h_map, ts->map.data(), ts->n_chunks);
+  return ZN_OK;
+}
+
+zn_status zn_tableset_cost_history(const zn_tableset *ts, uint64_t *h_cost) {
+  if (!ts || !h_cost) return ZN_ERR_ARG;
+  for (int r = 0; r <= kRounds; r++) h_cost[r] = r < int(ts->cost.size()) ? ts->cost[r] : 0;
+  return ZN_OK;
+}
+
+zn_status zn_debug_histograms(const zn_tableset *ts, const void *const *d_in_ptrs, uint32_t *d_hist,
+                              hipStream_t stream) {
+  if (!ts || !d_in_ptrs || !d_hist) return ZN_ERR_ARG;
+  HIPCHK(launch_hist_all(ts->dtype, dev_layout(ts), reinterpret_cast<const uint8_t *const *>(d_in_ptrs),
+                         d_hist, stream));
+  return ZN_OK;
+}
+
+zn_status zn_debug_code_lengths(const uint64_t *d_hist, int n, int alphabet, int group_rule,
+                                uint8_t *d_len, hipStream_t stream) {
+  if (!d_hist || !d_len || n < 0 || alphabet < 2 || alphabet > 256 || (alphabet & (alphabet - 1)))
+    return ZN_ERR_ARG;
+  HIPCHK(launch_lengths(d_hist, n, alphabet, group_rule, d_len, stream));
+  return ZN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,335 @@
+// zn_common.h -- format constants and workgroup-level code construction for
+// the gfx950 codec (libzn.so).  Device code is written for 64-lane wavefronts.
+//
+// Format (version 1), shared by every kernel here:
+//   * field split per element (THEORY-599 on ZipNN, per-field compressibility,
+//     ZipNN Table II; FP8: "Lossless Compression of Neural Network Components
+//     ... Low-Precision Formats", Abstract):
+//       BF16  E = (w>>7)&0xFF coded; SF = sign|frac[6:0] kept raw
+//       FP32  P0 = exponent, P1 = sign|frac[22:16], P2, P3 = low fraction
+//             bytes, all coded (raw fallback)
+//       FP8   E4 = (b>>3)&15, M3 = b&7 coded; sign bit kept raw
+//   * per chunk and coded stream: order-0 histogram, optimal prefix code with
+//     lengths <= 11 (package-merge, leaves by (count, symbol), leaves before
+//     packages at equal weight), canonical codes, LSB-first bits with each
+//     code word first-bit-first (THEORY-599, order-0 only);
+//   * streams cut into segments of S symbols (BF16 512, FP32 1024, FP8 2048)
+//     whose bit lengths are stored, so segments decode independently;
+//   * container: 64-byte header, tensor table, chunk directory, raw planes,
+//     16-byte aligned chunk records, 16 zero bytes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zn {
+
+constexpr int kMaxLen = 11;           // longest code word, bits
+constexpr int kLutBits = 11;          // decode window = kMaxLen
+constexpr int kLutSize = 1 << kLutBits;
+constexpr uint32_t kMagic = 0x31464E5Au;     // "ZNF1"
+constexpr uint32_t kTsMagic = 0x53544E5Au;   // "ZNTS"
+constexpr int kVersion = 1;
+constexpr int kRounds = 8;            // Lloyd rounds of the grouped setup
+
+enum Mode { RAW = 0, CONST = 1, HUFF = 2, GROUP = 3 };
+enum DType { BF16 = 0, FP32 = 1, FP8 = 2 };
+
+__host__ __device__ constexpr int esize(int dt) { return dt == BF16 ? 2 : dt == FP32 ? 4 : 1; }
+__host__ __device__ constexpr int ncoded(int dt) { return dt == BF16 ? 1 : dt == FP32 ? 4 : 2; }
+__host__ __device__ constexpr int kbits(int dt, int p) { return dt == FP8 ? (p == 0 ? 4 : 3) : 8; }
+__host__ __device__ constexpr int segsyms(int dt) { return dt == BF16 ? 512 : dt == FP32 ? 1024 : 2048; }
+__host__ __device__ constexpr uint64_t align16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
+__host__ __device__ inline uint64_t rawplane_bytes(int dt, uint64_t n) {
+  return dt == BF16 ? n : dt == FP8 ? (n + 7) / 8 : 0;
+}
+__host__ __device__ inline uint64_t payload_bytes_of(int mode, int k, uint64_t n, uint64_t bits) {
+  if (mode == HUFF || mode == GROUP) return 4 * ((bits + 31) / 32);
+  if (mode == RAW) return (n * uint64_t(k) + 7) / 8;
+  return 0;
+}
+__host__ __device__ inline uint64_t head_bytes_of(int mode, int k, int nseg) {
+  uint64_t h = 8;
+  if (mode == HUFF) h += uint64_t(1 << k) / 2;
+  if (mode == HUFF || mode == GROUP) h += 2 * uint64_t(nseg);
+  return align16(h);
+}
+__host__ __device__ inline uint64_t section_bytes(int mode, int k, uint64_t n, int nseg, uint64_t bits) {
+  return head_bytes_of(mode, k, nseg) + align16(payload_bytes_of(mode, k, n, bits));
+}
+
+// Plan tables that kernels read (device memory owned by the tableset).
+struct DevLayout {
+  const uint64_t *t_n;       // [T] elements per tensor
+  const uint64_t *t_raw;     // [T] offset of the tensor's always-raw section
+  const uint32_t *t_chunk0;  // [T+1] first global chunk of each tensor
+  int T;
+  uint32_t n_chunks;
+  uint32_t chunk_elems;
+  uint64_t off_dir, off_records;
+};
+
+__device__ inline int find_tensor(const DevLayout &L, uint32_t c) {
+  int lo = 0, hi = L.T - 1;  // last t with t_chunk0[t] <= c
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (L.t_chunk0[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- waves ----
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline uint64_t lanemask_lt() {
+  const int ln = threadIdx.x & 63;
+  return ln ? (~0ull >> (64 - ln)) : 0ull;
+}
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ inline uint32_t wave_incl_scan(uint32_t v) {
+  const int ln = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, 64);
+    if (ln >= o) v += t;
+  }
+  return v;
+}
+
+// ------------------------------------------------------- package-merge ----
+// Shared memory of one code construction (about 18 KB).
+struct PMShared {
+  uint64_t w[2][512];               // item weights of the previous/current list
+  uint64_t leaf_w[256];             // leaves sorted by (count, symbol)
+  uint64_t tmp_w[256];              // present symbols in symbol order
+  uint16_t leafpos[kMaxLen][256];   // position of sorted leaf i in list j
+  uint8_t leaf_sym[256];
+  uint8_t tmp_sym[256];
+  int c[kMaxLen];                   // leaves among the selected prefix of list j
+  int d;
+  int wave_cnt[4];
+};
+
+// Optimal code lengths (<= 11) of the weights hw[0..A) by package-merge, for
+// a workgroup of NT >= 256 threads.  List 0 holds the leaves (coins of the
+// smallest denomination); list j merges leaves with packages made of adjacent
+// pairs of list j-1, leaves first at equal weight; the first 2d-2 items of
+// the last list are selected.  Instead of expanding packages, the number of
+// leaves c_j inside the selected prefix of each list is counted backwards
+// (a prefix of p packages is exactly the first 2p items of the list below),
+// and sorted leaf i gets the length #{j : i < c_j}.
+// Returns d, the number of symbols with non-zero weight (after the group
+// rule, which adds the smallest absent symbol with weight 0 when d == 1).
+// len[0..A) is written for every symbol (0 when absent).
+template <int NT>
+__device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rule, uint8_t *len) {
+  static_assert(NT >= 256, "code construction needs at least 256 threads");
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  const bool nz = tid < A && hw[tid] != 0;
+  const uint64_t m = __ballot(nz);
+  if (ln == 0 && wv < 4) S.wave_cnt[wv] = __popcll(m);
+  if (tid < A) len[tid] = 0;
+  __syncthreads();
+  if (nz) {
+    int base = 0;
+    for (int q = 0; q < wv; q++) base += S.wave_cnt[q];
+    const int idx = base + __popcll(m & lanemask_lt());
+    S.tmp_sym[idx] = uint8_t(tid);
+    S.tmp_w[idx] = hw[tid];
+  }
+  if (tid == 0) S.d = S.wave_cnt[0] + S.wave_cnt[1] + S.wave_cnt[2] + S.wave_cnt[3];
+  __syncthreads();
+  int d = S.d;
+  if (group_rule && d == 1) {
+    if (tid == 0) {
+      S.tmp_sym[1] = S.tmp_sym[0] == 0 ? 1 : 0;
+      S.tmp_w[1] = 0;
+      S.d = 2;
+    }
+    __syncthreads();
+    d = 2;
+  }
+  if (d < 2) return d;
+  // rank sort of the leaves by (weight, symbol)
+  if (tid < d) {
+    const uint64_t w = S.tmp_w[tid];
+    const int s = S.tmp_sym[tid];
+    int r = 0;
+    for (int j = 0; j < d; j++) {
+      const uint64_t wj = S.tmp_w[j];
+      r += (wj < w) || (wj == w && S.tmp_sym[j] < s);
+    }
+    S.leaf_w[r] = w;
+    S.leaf_sym[r] = uint8_t(s);
+    S.w[0][r] = w;
+    S.leafpos[0][r] = uint16_t(r);
+  }
+  __syncthreads();
+  int n_prev = d;
+  for (int j = 1; j < kMaxLen; j++) {
+    const uint64_t *prev = S.w[(j - 1) & 1];
+    uint64_t *cur = S.w[j & 1];
+    const int np = n_prev >> 1;
+    for (int q = tid; q < d + np; q += NT) {
+      if (q < d) {  // leaf q: after every package lighter than it
+        const uint64_t wi = S.leaf_w[q];
+        int lo = 0, hi = np;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (prev[2 * mid] + prev[2 * mid + 1] < wi) lo = mid + 1; else hi = mid;
+        }
+        cur[q + lo] = wi;
+        S.leafpos[j][q] = uint16_t(q + lo);
+      } else {      // package k: after every leaf not heavier than it
+        const int k = q - d;
+        const uint64_t p = prev[2 * k] + prev[2 * k + 1];
+        int lo = 0, hi = d;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (S.leaf_w[mid] <= p) lo = mid + 1; else hi = mid;
+        }
+        cur[k + lo] = p;
+      }
+    }
+    __syncthreads();
+    n_prev = d + np;
+  }
+  if (tid < 64) {
+    int msel = 2 * d - 2;
+    for (int j = kMaxLen - 1; j >= 0; j--) {
+      int cnt = 0;
+      for (int i = tid; i < d; i += 64) cnt += S.leafpos[j][i] < msel;
+      cnt = wave_sum(cnt);
+      if (tid == 0) S.c[j] = cnt;
+      msel = 2 * (msel - cnt);
+    }
+  }
+  __syncthreads();
+  if (tid < d) {
+    int l = 0;
+    for (int j = 0; j < kMaxLen; j++) l += tid < S.c[j];
+    len[S.leaf_sym[tid]] = uint8_t(l);
+  }
+  __syncthreads();
+  return d;
+}
+
+// ------------------------------------------------------ canonical codes ----
+// Canonical code values (RFC 1951 section 3.2.2) of lengths len[0..A),
+// stored for LSB-first emission: enc[s] = bit-reversed code | (length << 16).
+// cnt: shared [4][kMaxLen + 1].  Any NT >= 256.
+__device__ inline void canon_encode_table(const uint8_t *len, int A, uint32_t *enc,
+                                          int (*cnt)[kMaxLen + 1]) {
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  const int l = tid < A ? len[tid] : 0;
+  int rank = 0;
+  for (int b = 1; b <= kMaxLen; b++) {
+    const uint64_t m = __ballot(l == b);
+    if (l == b) rank = __popcll(m & lanemask_lt());
+    if (ln == 0 && wv < 4) cnt[wv][b] = __popcll(m);
+  }
+  __syncthreads();
+  if (tid < A) {
+    uint32_t e = 0;
+    if (l) {
+      uint32_t code = 0;
+      for (int b = 1; b <= l; b++) {
+        const int prevc = b > 1 ? cnt[0][b - 1] + cnt[1][b - 1] + cnt[2][b - 1] + cnt[3][b - 1] : 0;
+        code = (code + prevc) << 1;
+      }
+      for (int q = 0; q < wv; q++) code += cnt[q][l];
+      code += rank;
+      e = (__builtin_bitreverse32(code) >> (32 - l)) | (uint32_t(l) << 16);
+    }
+    enc[tid] = e;
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------ decode tables ------
+// Shared memory for one decode table build.
+struct LutShared {
+  int cnt[4][kMaxLen + 1];
+  int first[kMaxLen + 2];     // first canonical code of each length
+  int offs[kMaxLen + 2];      // sorted index of the first symbol of each length
+  int ljend[kMaxLen + 2];     // end of each length's range, left-justified to 11 bits
+  uint8_t sorted[256];        // symbols ordered by (length, symbol)
+  int bad;
+};
+
+// Builds the multi-symbol decode table of a canonical code from its lengths.
+// lut[v] for an 11-bit LSB-first window v holds up to three whole code words:
+// bits 0-7, 8-15, 16-23 the symbols, 24-27 the bits they use, 28-29 their
+// number.  t1 (2048 x u16, scratch) is the single-symbol table indexed by the
+// window read first-bit-as-MSB.  Returns false (for every thread) if the
+// lengths are not a complete prefix code of at least two words with lengths
+// <= 11.  NT >= 256 threads; A <= 256.
+template <int NT>
+__device__ bool build_lut(const uint8_t *len, int A, uint32_t *lut, uint16_t *t1, LutShared &S) {
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  const int l = tid < A ? len[tid] : 0;
+  int rank = 0;
+  for (int b = 1; b <= kMaxLen; b++) {
+    const uint64_t m = __ballot(l == b);
+    if (l == b) rank = __popcll(m & lanemask_lt());
+    if (ln == 0 && wv < 4) S.cnt[wv][b] = __popcll(m);
+  }
+  if (tid == 0) S.bad = 0;
+  __syncthreads();
+  if (tid < A && l > kMaxLen) S.bad = 1;
+  if (tid == 0) {
+    uint32_t code = 0, kraft = 0;
+    int o = 0, d = 0;
+    for (int b = 1; b <= kMaxLen; b++) {
+      const int c = S.cnt[0][b] + S.cnt[1][b] + S.cnt[2][b] + S.cnt[3][b];
+      const int pc = b > 1 ? S.cnt[0][b - 1] + S.cnt[1][b - 1] + S.cnt[2][b - 1] + S.cnt[3][b - 1] : 0;
+      code = (code + pc) << 1;
+      S.first[b] = int(code);
+      S.offs[b] = o;
+      S.ljend[b] = int((code + c) << (kMaxLen - b));
+      o += c;
+      d += c;
+      kraft += uint32_t(c) << (kMaxLen - b);
+    }
+    if (d < 2 || kraft != (1u << kMaxLen)) S.bad = 1;
+  }
+  __syncthreads();
+  if (S.bad) return false;
+  if (tid < A && l) {
+    int pos = S.offs[l] + rank;
+    for (int q = 0; q < wv; q++) pos += S.cnt[q][l];
+    S.sorted[pos] = uint8_t(tid);
+  }
+  __syncthreads();
+  for (int u = tid; u < kLutSize; u += NT) {
+    int b = 1;
+    while (b < kMaxLen && u >= S.ljend[b]) b++;
+    const int idx = (u >> (kMaxLen - b)) - S.first[b];
+    t1[u] = uint16_t(S.sorted[S.offs[b] + idx] | (b << 8));
+  }
+  __syncthreads();
+  for (int v = tid; v < kLutSize; v += NT) {
+    uint32_t w = uint32_t(v);
+    uint32_t e = t1[__builtin_bitreverse32(w) >> (32 - kMaxLen)];
+    int used = int(e >> 8), n = 1;
+    uint32_t syms = e & 0xFF;
+    w >>= used;
+#pragma unroll
+    for (int q = 1; q < 3; q++) {
+      const uint32_t e2 = t1[__builtin_bitreverse32(w) >> (32 - kMaxLen)];
+      const int l2 = int(e2 >> 8);
+      if (used + l2 > kMaxLen || n != q) break;
+      syms |= (e2 & 0xFF) << (8 * q);
+      used += l2;
+      w >>= l2;
+      n++;
+    }
+    lut[v] = syms | (uint32_t(used) << 24) | (uint32_t(n) << 28);
+  }
+  __syncthreads();
+  return true;
+}
+
+}  // namespace zn

@@ -1,0 +1,82 @@
+// zn_internal.h -- launch interface between the C ABI (zn_api.hip) and the
+// kernels (zn_encode.hip, zn_decode.hip, zn_setup.hip).  Not installed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zn_common.h"
+
+namespace zn {
+
+struct EncArgs {
+  DevLayout L;
+  const uint8_t *const *in_ptrs;   // [T] device pointers
+  const uint8_t *group_map;        // [n_chunks] or nullptr
+  const uint32_t *group_enc;       // [K][256] bit-reversed code | len << 16
+  const uint8_t *group_len;        // [K][256]
+  uint8_t *out;
+  uint64_t cap;
+  unsigned long long *status;      // [n_chunks] look-back words
+  uint32_t *ctl;                   // [0] error bits, [1] ticket counter
+};
+
+struct FinishArgs {
+  DevLayout L;
+  int dtype;
+  const uint8_t *hdr;              // header template (64 + 16T bytes, total = 0)
+  uint32_t hdr_bytes;
+  uint8_t *out;
+  uint64_t cap;
+  const unsigned long long *status;
+  uint32_t *ctl;
+};
+
+struct DecArgs {
+  DevLayout L;
+  const uint8_t *in;
+  uint64_t in_bytes;
+  uint8_t *const *out_ptrs;        // [T] device pointers
+  const uint32_t *group_lut;       // [K][2048]
+  const uint8_t *group_len;        // [K][256]
+  int K;
+  uint32_t *ctl;                   // [0] error bits
+};
+
+struct CheckArgs {
+  const uint8_t *in;
+  uint64_t in_bytes;
+  const uint8_t *hdr;              // expected header + tensor table
+  uint32_t hdr_bytes;
+  uint64_t hash;                   // tableset hash (groups) or 0
+  int K;
+  uint32_t n_chunks;
+  uint64_t off_dir;
+  uint32_t *ctl;
+};
+
+// Error bits in ctl[0].
+constexpr uint32_t kErrCapacity = 1, kErrCorrupt = 2, kErrTableset = 4, kErrSpin = 8;
+// Scratch words: ctl[0..63] control, then the look-back status array.
+constexpr uint64_t kCtlBytes = 256;
+
+hipError_t launch_encode(int dtype, const EncArgs &a, hipStream_t s);
+hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
+hipError_t launch_zero(uint32_t *p, uint64_t words, hipStream_t s);
+hipError_t launch_check(const CheckArgs &a, hipStream_t s);
+hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s);
+
+// setup
+hipError_t launch_hist_all(int dtype, const DevLayout &L, const uint8_t *const *in_ptrs,
+                           uint32_t *hist /* [n_chunks][ncoded][256] */, hipStream_t s);
+hipError_t launch_pool(const uint32_t *hist, int stride_words, int A, uint32_t M, const uint8_t *map,
+                       unsigned long long *pooled /* [K][256] */, int K, hipStream_t s);
+hipError_t launch_lengths(const uint64_t *hw, int n, int A, int group_rule, uint8_t *len,
+                          hipStream_t s);
+hipError_t launch_group_tables(const uint8_t *len, int K, int A, uint32_t *enc, uint32_t *lut,
+                               uint32_t *ctl, hipStream_t s);
+hipError_t launch_assign(const uint32_t *hist, int stride_words, int A, uint32_t M, const uint8_t *len,
+                         int K, int reassign, uint8_t *map, unsigned long long *cost, hipStream_t s);
+hipError_t launch_keys(const uint32_t *hist, int stride_words, int A, const DevLayout &L,
+                       unsigned long long *keys, hipStream_t s);
+
+}  // namespace zn

@@ -1,0 +1,256 @@
+"""Python binding of libzn.so (include/zn.h): argument marshalling only.
+
+Every step of setup, compression and decompression runs in the library's HIP
+kernels; this module turns torch tensors into device pointers and streams,
+and raises ZnError on a non-zero status.  There is no fallback: if libzn.so
+is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzn.so")
+
+BF16, FP32, FP8_E4M3 = 0, 1, 2
+TORCH_DTYPE = {BF16: torch.bfloat16, FP32: torch.float32, FP8_E4M3: torch.float8_e4m3fn}
+ZN_DTYPE = {v: k for k, v in TORCH_DTYPE.items()}
+STATUS = {0: "ok", -1: "invalid argument", -2: "corrupt container", -3: "buffer too small",
+          -4: "tableset mismatch", -5: "HIP runtime error", -6: "out of memory"}
+ROUNDS = 8
+
+
+class ZnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(code, 'status %d' % code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Loads libzn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ZnError(-1, f"libzn.so not built at {LIB_PATH} (run __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        P, U64, I, U32 = C.c_void_p, C.c_uint64, C.c_int, C.c_uint32
+        PU64 = C.POINTER(C.c_uint64)
+        L.zn_setup.argtypes = [I, C.POINTER(P), PU64, I, U32, I, P, C.POINTER(P)]
+        L.zn_plan_from_container.argtypes = [P, U64, P, C.POINTER(P)]
+        L.zn_tableset_info.argtypes = [P, C.POINTER(I), C.POINTER(I), PU64, C.POINTER(U32),
+                                       C.POINTER(U32), C.POINTER(I), PU64]
+        L.zn_compress_bound.argtypes = [P, PU64]
+        L.zn_scratch_bytes.argtypes = [P, PU64]
+        L.zn_compress.argtypes = [P, P, P, U64, PU64, P, U64, P]
+        L.zn_decompress.argtypes = [P, P, U64, P, P, U64, I, P]
+        L.zn_tableset_save.argtypes = [P, P, U64, PU64]
+        L.zn_tableset_load.argtypes = [P, U64, C.POINTER(P)]
+        L.zn_tableset_lengths.argtypes = [P, I, P]
+        L.zn_tableset_map.argtypes = [P, P]
+        L.zn_tableset_cost_history.argtypes = [P, PU64]
+        L.zn_tableset_free.argtypes = [P]
+        L.zn_status_str.restype = C.c_char_p
+        L.zn_debug_histograms.argtypes = [P, P, P, P]
+        L.zn_debug_code_lengths.argtypes = [P, I, I, I, P, P]
+        for f in ("zn_setup", "zn_plan_from_container", "zn_tableset_info", "zn_compress_bound",
+                  "zn_scratch_bytes", "zn_compress", "zn_decompress", "zn_tableset_save",
+                  "zn_tableset_load", "zn_tableset_lengths", "zn_tableset_map",
+                  "zn_tableset_cost_history", "zn_debug_histograms", "zn_debug_code_lengths"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise ZnError(rc, where)
+
+
+def _stream(stream) -> C.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr_array(tensors: Sequence[torch.Tensor], device) -> torch.Tensor:
+    """Device array of the tensors' data pointers (the ABI's d_*_ptrs)."""
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def _u64(vals):
+    return (C.c_uint64 * len(vals))(*[int(v) for v in vals])
+
+
+class Tableset:
+    """Owns a zn_tableset handle (the plan and optional group tables)."""
+
+    def __init__(self, handle: C.c_void_p):
+        self.handle = handle
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.zn_tableset_free(h)
+            self.handle = None
+
+    def info(self) -> dict:
+        dt, T, nc, K = C.c_int(), C.c_int(), C.c_uint32(), C.c_int()
+        cb, h = C.c_uint32(), C.c_uint64()
+        _check(lib().zn_tableset_info(self.handle, C.byref(dt), C.byref(T), None, C.byref(cb),
+                                      C.byref(nc), C.byref(K), C.byref(h)), "tableset_info")
+        n = (C.c_uint64 * T.value)()
+        _check(lib().zn_tableset_info(self.handle, None, None, n, None, None, None, None),
+               "tableset_info")
+        return {"dtype": dt.value, "n_tensors": T.value, "n_elems": [int(v) for v in n],
+                "chunk_bytes": cb.value, "n_chunks": nc.value, "n_groups": K.value,
+                "hash": h.value}
+
+    @property
+    def dtype(self) -> int:
+        return self.info()["dtype"]
+
+    @property
+    def n_groups(self) -> int:
+        return self.info()["n_groups"]
+
+    @property
+    def hash(self) -> int:
+        return self.info()["hash"]
+
+    def lengths(self, g: int) -> list:
+        A = 16 if self.dtype == FP8_E4M3 else 256
+        buf = (C.c_uint8 * A)()
+        _check(lib().zn_tableset_lengths(self.handle, g, buf), "tableset_lengths")
+        return list(buf)
+
+    def group_map(self) -> list:
+        buf = (C.c_uint8 * max(1, self.info()["n_chunks"]))()
+        _check(lib().zn_tableset_map(self.handle, buf), "tableset_map")
+        return list(buf)[: self.info()["n_chunks"]]
+
+    def cost_history(self) -> list:
+        buf = (C.c_uint64 * (ROUNDS + 1))()
+        _check(lib().zn_tableset_cost_history(self.handle, buf), "cost_history")
+        return [int(v) for v in buf]
+
+    def save(self) -> bytes:
+        n = C.c_uint64()
+        _check(lib().zn_tableset_save(self.handle, None, 0, C.byref(n)), "tableset_save")
+        buf = (C.c_uint8 * n.value)()
+        _check(lib().zn_tableset_save(self.handle, buf, n.value, C.byref(n)), "tableset_save")
+        return bytes(buf)
+
+    @classmethod
+    def load(cls, data: bytes) -> "Tableset":
+        buf = (C.c_uint8 * len(data)).from_buffer_copy(data)
+        h = C.c_void_p()
+        _check(lib().zn_tableset_load(buf, len(data), C.byref(h)), "tableset_load")
+        return cls(h)
+
+
+def setup(tensors: Sequence[torch.Tensor] | None = None, *, dtype=None, n_elems=None,
+          chunk_bytes: int = 262144, n_groups: int = 0, stream=None) -> Tableset:
+    """zn_setup: a plan for these tensor sizes; with n_groups > 0 the chunks of
+    `tensors` are grouped and share code tables."""
+    if tensors is not None:
+        tensors = [t.contiguous() for t in tensors]
+        dtype = ZN_DTYPE[tensors[0].dtype]
+        n_elems = [t.numel() for t in tensors]
+        ptrs = (C.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    else:
+        ptrs = None
+        dtype = ZN_DTYPE.get(dtype, dtype)
+    h = C.c_void_p()
+    _check(lib().zn_setup(int(dtype), ptrs, _u64(n_elems), len(n_elems), chunk_bytes, n_groups,
+                          _stream(stream), C.byref(h)), "setup")
+    return Tableset(h)
+
+
+def plan_from_container(blob: torch.Tensor, stream=None) -> Tableset:
+    h = C.c_void_p()
+    _check(lib().zn_plan_from_container(C.c_void_p(blob.data_ptr()), blob.numel(), _stream(stream),
+                                        C.byref(h)), "plan_from_container")
+    return Tableset(h)
+
+
+def compress_bound(ts: Tableset) -> int:
+    b = C.c_uint64()
+    _check(lib().zn_compress_bound(ts.handle, C.byref(b)), "compress_bound")
+    return b.value
+
+
+def scratch_bytes(ts: Tableset) -> int:
+    b = C.c_uint64()
+    _check(lib().zn_scratch_bytes(ts.handle, C.byref(b)), "scratch_bytes")
+    return b.value
+
+
+def new_scratch(ts: Tableset, device="cuda") -> torch.Tensor:
+    return torch.empty(scratch_bytes(ts), dtype=torch.uint8, device=device)
+
+
+def compress(ts: Tableset, tensors: Sequence[torch.Tensor], out: torch.Tensor | None = None,
+             scratch: torch.Tensor | None = None, ptrs: torch.Tensor | None = None,
+             sync: bool = True, stream=None):
+    """zn_compress.  Returns the container (a view of `out`) when sync, else
+    `out` itself (size at byte 56 once the stream has run)."""
+    dev = tensors[0].device
+    if out is None:
+        out = torch.empty(compress_bound(ts), dtype=torch.uint8, device=dev)
+    if scratch is None:
+        scratch = new_scratch(ts, dev)
+    if ptrs is None:
+        ptrs = _ptr_array(tensors, dev)
+    nb = C.c_uint64()
+    _check(lib().zn_compress(ts.handle, C.c_void_p(ptrs.data_ptr()), C.c_void_p(out.data_ptr()),
+                             out.numel(), C.byref(nb) if sync else None,
+                             C.c_void_p(scratch.data_ptr()), scratch.numel(), _stream(stream)),
+           "compress")
+    return out[: nb.value] if sync else out
+
+
+def decompress(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Tensor] | None = None,
+               scratch: torch.Tensor | None = None, ptrs: torch.Tensor | None = None,
+               sync: bool = True, stream=None):
+    """zn_decompress into `outs` (allocated from the plan when None)."""
+    if outs is None:
+        info = ts.info()
+        outs = [torch.empty(n, dtype=TORCH_DTYPE[info["dtype"]], device=blob.device)
+                for n in info["n_elems"]]
+    if scratch is None:
+        scratch = torch.empty(256, dtype=torch.uint8, device=blob.device)
+    if ptrs is None:
+        ptrs = _ptr_array(outs, blob.device)
+    _check(lib().zn_decompress(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
+                               C.c_void_p(ptrs.data_ptr()), C.c_void_p(scratch.data_ptr()),
+                               scratch.numel(), 1 if sync else 0, _stream(stream)), "decompress")
+    return outs
+
+
+def debug_histograms(ts: Tableset, tensors: Sequence[torch.Tensor], stream=None) -> torch.Tensor:
+    info = ts.info()
+    nc = {BF16: 1, FP32: 4, FP8_E4M3: 2}[info["dtype"]]
+    hist = torch.zeros((info["n_chunks"], nc, 256), dtype=torch.int32, device=tensors[0].device)
+    ptrs = _ptr_array(tensors, tensors[0].device)
+    _check(lib().zn_debug_histograms(ts.handle, C.c_void_p(ptrs.data_ptr()),
+                                     C.c_void_p(hist.data_ptr()), _stream(stream)), "histograms")
+    torch.cuda.synchronize()
+    return hist
+
+
+def debug_code_lengths(hist: torch.Tensor, alphabet: int = 256, group_rule: bool = False,
+                       stream=None) -> torch.Tensor:
+    """Device package-merge of n histograms (int64 [n, 256] on the GPU)."""
+    hist = hist.to(torch.int64).contiguous()
+    out = torch.zeros(hist.shape, dtype=torch.uint8, device=hist.device)
+    _check(lib().zn_debug_code_lengths(C.c_void_p(hist.data_ptr()), hist.shape[0], alphabet,
+                                       1 if group_rule else 0, C.c_void_p(out.data_ptr()),
+                                       _stream(stream)), "code_lengths")
+    torch.cuda.synchronize()
+    return out

@@ -1,0 +1,51 @@
+"""Helpers shared by the GPU tests: generation, oracle comparison, sampling."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from lossless_float_weight_amd import workloads as W
+from lossless_float_weight_amd import zn
+
+NP_DTYPE = {zn.BF16: np.uint16, zn.FP32: np.uint32, zn.FP8_E4M3: np.uint8}
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return W.bits(t.contiguous()).reshape(-1).cpu().numpy()
+
+
+def gpu_compress(tensors, chunk_bytes=262144, ts=None, n_groups=0):
+    if ts is None:
+        ts = zn.setup(tensors, chunk_bytes=chunk_bytes, n_groups=n_groups)
+    blob = zn.compress(ts, tensors)
+    torch.cuda.synchronize()
+    return ts, blob
+
+
+def assert_roundtrip(ts, blob, tensors):
+    outs = zn.decompress(ts, blob)
+    torch.cuda.synchronize()
+    for a, b in zip(tensors, outs):
+        assert torch.equal(W.bits(a.contiguous()).reshape(-1), W.bits(b).reshape(-1)), "round trip"
+
+
+def first_difference(a: np.ndarray, b: np.ndarray) -> str:
+    n = min(a.size, b.size)
+    idx = np.nonzero(a[:n] != b[:n])[0]
+    where = int(idx[0]) if idx.size else n
+    return f"sizes {a.size} vs {b.size}, first differing byte {where}"
+
+
+def record_bounds(blob: np.ndarray):
+    """Directory of a container: (off_dir, n_chunks, offsets[n_chunks + 1])."""
+    n_chunks = int(np.frombuffer(blob[24:28].tobytes(), np.uint32)[0])
+    off_dir = int(np.frombuffer(blob[40:48].tobytes(), np.uint64)[0])
+    dirv = np.frombuffer(blob[off_dir:off_dir + 8 * (n_chunks + 1)].tobytes(), np.uint64)
+    return off_dir, n_chunks, dirv.astype(np.int64)
+
+
+def sample_chunks(n_chunks: int, k: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    pick = {0, n_chunks - 1}
+    pick |= set(int(x) for x in rng.integers(0, n_chunks, size=min(k, n_chunks)))
+    return sorted(pick)

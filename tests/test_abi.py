@@ -1,0 +1,43 @@
+"""CPU checks of the C-ABI library: it loads without a GPU and exports every
+function that include/zn.h declares (no compute calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zn.h")
+LIB = os.path.join(ROOT, "lossless_float_weight_amd", "libzn.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("zn_setup", "zn_compress", "zn_decompress"):
+        assert required in names
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libzn.so not built")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libzn.so not built")
+def test_status_strings_and_argument_errors_need_no_gpu():
+    lib = ctypes.CDLL(LIB)
+    lib.zn_status_str.restype = ctypes.c_char_p
+    assert lib.zn_status_str(-2) == b"corrupt container"
+    # argument checks return before any HIP call
+    out = ctypes.c_void_p()
+    n = (ctypes.c_uint64 * 1)(1000)
+    assert lib.zn_setup(0, None, n, 1, 1000, 0, None, ctypes.byref(out)) == -1   # bad chunk size
+    assert lib.zn_setup(7, None, n, 1, 262144, 0, None, ctypes.byref(out)) == -1  # bad dtype
+    assert lib.zn_compress(None, None, None, 0, None, None, 0, None) == -1

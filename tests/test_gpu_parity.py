@@ -1,0 +1,248 @@
+"""GPU parity: libzn.so (HIP kernels, through the C ABI) against the CPU oracle.
+
+The bar is bit-exactness: container bytes identical to the oracle's on the
+same seeded inputs, and decompressed tensors identical to the inputs.  Small
+cases compare whole containers; full-size workloads compare sampled chunk
+records one by one (the oracle encodes each sampled chunk alone) plus the
+exact GPU round trip of everything.
+"""
+import numpy as np
+import pytest
+import torch
+
+from lossless_float_weight_amd import workloads as W
+from lossless_float_weight_amd import zn
+from tests.gpu_util import (assert_roundtrip, first_difference, gpu_compress, record_bounds,
+                            sample_chunks, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zn.lib()  # a missing library is an error on a GPU machine, not a skip
+
+
+def _check_equal(oracle, dt, tensors, chunk_bytes, ts=None, ots=None):
+    ts, blob = gpu_compress(tensors, chunk_bytes, ts)
+    g = blob.cpu().numpy()
+    o = oracle.compress(dt, [to_np(t) for t in tensors], chunk_bytes, ots)
+    assert g.size == o.size and np.array_equal(g, o), first_difference(g, o)
+    assert_roundtrip(ts, blob, tensors)
+    return ts, blob
+
+
+# ------------------------------------------------------------ BF16 ---------
+def test_config1_single_bf16(oracle):
+    print("case: single BF16 tensor 2^20, 256 KiB chunks", flush=True)
+    x = W.single_bf16(device="cuda")[0][1]
+    _check_equal(oracle, oracle.BF16, [x], 262144)
+
+
+@pytest.mark.parametrize("n", [1, 7, 511, 512, 513, 2048, 4097, 131071, 131073, 300001])
+@pytest.mark.parametrize("cb", [4096, 262144])
+def test_bf16_ragged(oracle, n, cb):
+    print(f"case: BF16 n={n} chunk={cb}", flush=True)
+    x = W.gaussian(n, 0.0, 0.02, torch.bfloat16, "cuda", seed=n, i=1)
+    _check_equal(oracle, oracle.BF16, [x], cb)
+
+
+def test_bf16_every_pattern_and_modes(oracle):
+    print("case: BF16 all bit patterns, constant, random, single element", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(3)
+    perm = torch.randperm(1 << 16, generator=g)
+    allp = perm.to(torch.int32).to(torch.int16).view(torch.bfloat16).cuda()
+    const = torch.full((70000,), 1.0, dtype=torch.bfloat16, device="cuda")
+    rnd = torch.randint(-32768, 32767, (90000,), generator=g, dtype=torch.int16).view(torch.bfloat16).cuda()
+    one = torch.tensor([-2.5], dtype=torch.bfloat16, device="cuda")
+    norm = W.gaussian(6000, 1.0, 0.05, torch.bfloat16, "cuda", 7, 0)
+    _check_equal(oracle, oracle.BF16, [allp, const, rnd, one, norm], 8192)
+
+
+def test_bf16_block_scaled(oracle):
+    print("case: BF16 transformer block / 4", flush=True)
+    tensors = [t for _, t in W.block_bf16("cuda", seed=2, scale=4)]
+    _check_equal(oracle, oracle.BF16, tensors, 262144)
+
+
+def test_bf16_unaligned_input(oracle):
+    print("case: BF16 unaligned input view", flush=True)
+    base = W.gaussian(40001, 0.0, 0.02, torch.bfloat16, "cuda", 9, 0)
+    x = base[1:]  # 2-byte offset: the scalar path
+    _check_equal(oracle, oracle.BF16, [x], 16384)
+
+
+# ------------------------------------------------------- FP32 and FP8 ------
+def test_fp32_regular_and_clean(oracle):
+    print("case: FP32 regular + clean, 2^19 each", flush=True)
+    tensors = [t for _, t in W.fp32_pair(1 << 19, device="cuda")]
+    _check_equal(oracle, oracle.FP32, tensors, 262144)
+
+
+@pytest.mark.parametrize("n", [1, 1000, 65537])
+def test_fp32_ragged_and_random(oracle, n):
+    print(f"case: FP32 random bits n={n}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(n)
+    x = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), generator=g, dtype=torch.int32).view(torch.float32)
+    y = W.gaussian(n, 0.0, 0.02, torch.float32, "cpu", n, 2)
+    _check_equal(oracle, oracle.FP32, [x.cuda(), y.cuda()], 16384)
+
+
+def test_fp8_blockscaled(oracle):
+    print("case: FP8 E4M3 block-scaled 2^20", flush=True)
+    x = W.fp8_blockscaled(1 << 20, device="cuda")[0][1]
+    _check_equal(oracle, oracle.FP8_E4M3, [x], 262144)
+
+
+@pytest.mark.parametrize("n", [1, 15, 17, 2049, 70001])
+def test_fp8_ragged_every_pattern(oracle, n):
+    print(f"case: FP8 patterns n={n}", flush=True)
+    x = (torch.arange(n, dtype=torch.int64) * 37 % 256).to(torch.uint8).view(torch.float8_e4m3fn)
+    _check_equal(oracle, oracle.FP8_E4M3, [x.cuda()], 4096)
+
+
+# -------------------------------------------------------- single stages ----
+def test_histograms_equal_bincount(oracle):
+    print("case: per-chunk histograms", flush=True)
+    tensors = [t for _, t in W.block_bf16("cuda", seed=2, scale=8)]
+    ts = zn.setup(tensors, chunk_bytes=65536)
+    h = zn.debug_histograms(ts, tensors).cpu().numpy()
+    c = 0
+    for t in tensors:
+        e = ((to_np(t) >> 7) & 0xFF).astype(np.int64)
+        for c0 in range(0, e.size, 32768):
+            assert np.array_equal(h[c, 0], np.bincount(e[c0:c0 + 32768], minlength=256))
+            c += 1
+    assert c == h.shape[0]
+
+
+def test_code_lengths_equal_oracle(oracle):
+    print("case: device package-merge vs oracle", flush=True)
+    rng = np.random.default_rng(11)
+    hs = []
+    for i in range(300):
+        d = int(rng.integers(1, 257))
+        h = np.zeros(256, np.int64)
+        idx = rng.choice(256, d, replace=False)
+        kind = i % 3
+        h[idx] = (rng.integers(1, 5000, d) if kind == 0 else
+                  (2.0 ** rng.uniform(0, 40, d)).astype(np.int64) + 1 if kind == 1 else
+                  rng.integers(1, 3, d))
+        hs.append(h)
+    H = torch.from_numpy(np.stack(hs)).cuda()
+    for group in (False, True):
+        got = zn.debug_code_lengths(H, 256, group).cpu().numpy()
+        for h, g in zip(hs, got):
+            want = oracle.code_lengths(h.astype(np.uint64), group=group)
+            assert np.array_equal(g, want)
+
+
+# ----------------------------------------------------------- grouped setup --
+def _small_model(scale=16, n_layers=2):
+    return [t for _, t in W.model_bf16("cuda", seed=5, n_layers=n_layers, scale=scale)]
+
+
+def test_setup_equals_oracle_and_reuses(oracle):
+    print("case: grouped setup K=16 on a scaled model, reuse on a perturbed copy", flush=True)
+    tensors = _small_model()
+    arrs = [to_np(t) for t in tensors]
+    ts = zn.setup(tensors, chunk_bytes=65536, n_groups=16)
+    ots = oracle.setup(oracle.BF16, arrs, 65536, 16)
+    assert ts.group_map() == ots.group_map().tolist()
+    for g in range(16):
+        assert ts.lengths(g) == ots.lengths(g).tolist()
+    assert ts.hash == ots.hash
+    assert ts.save() == ots.save()
+    assert ts.cost_history() == [int(v) for v in ots.cost_history()]
+    _check_equal(oracle, oracle.BF16, tensors, 65536, ts, ots)
+    names = [f"t{i}" for i in range(len(tensors))]
+    pert = [t for _, t in W.perturbed_model(list(zip(names, tensors)), seed=5)]
+    _check_equal(oracle, oracle.BF16, pert, 65536, ts, ots)
+    # a tableset reloaded from its bytes decodes the same container
+    ts2 = zn.Tableset.load(ts.save())
+    _, blob = gpu_compress(pert, 65536, ts)
+    assert_roundtrip(ts2, blob, pert)
+
+
+def test_escape_chunk(oracle):
+    print("case: escape chunk under a group tableset", flush=True)
+    tensors = _small_model(n_layers=1)
+    ts = zn.setup(tensors, chunk_bytes=65536, n_groups=4)
+    ots = oracle.setup(oracle.BF16, [to_np(t) for t in tensors], 65536, 4)
+    odd = [t.clone() for t in tensors]
+    odd[0].view(-1)[17] = float("inf")
+    _check_equal(oracle, oracle.BF16, odd, 65536, ts, ots)
+
+
+# ------------------------------------------------------- error handling ----
+def test_header_and_table_corruption_rejected(oracle):
+    print("case: corrupt magic and corrupt code lengths", flush=True)
+    x = W.gaussian(20000, 0.0, 0.02, torch.bfloat16, "cuda", 1, 0)
+    ts, blob = gpu_compress([x], 8192)
+    bad = blob.clone()
+    bad[0] ^= 0xFF
+    with pytest.raises(zn.ZnError) as e:
+        zn.decompress(ts, bad)
+    assert e.value.code == -2
+    off_rec = int(np.frombuffer(blob[48:56].cpu().numpy().tobytes(), np.uint64)[0])
+    bad = blob.clone()
+    bad[off_rec + 8:off_rec + 8 + 128] = 0x11   # all lengths 1: not a prefix code
+    with pytest.raises(zn.ZnError) as e:
+        zn.decompress(ts, bad)
+    assert e.value.code == -2
+    other = zn.setup([x], chunk_bytes=8192, n_groups=2)
+    with pytest.raises(zn.ZnError) as e:
+        zn.decompress(other, blob)
+    assert e.value.code in (-2, -4)
+
+
+def test_capacity_reported():
+    print("case: output buffer too small", flush=True)
+    x = W.gaussian(100000, 0.0, 0.02, torch.bfloat16, "cuda", 1, 0)
+    ts = zn.setup([x], chunk_bytes=65536)
+    small = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(zn.ZnError) as e:
+        zn.compress(ts, [x], out=small)
+    assert e.value.code == -3
+
+
+# ------------------------------------------------ full-size workloads ------
+def _sampled_record_parity(oracle, dt, tensors, blob, chunk_bytes, k=12, ts=None):
+    g = blob.cpu().numpy()
+    _, n_chunks, dirv = record_bounds(g)
+    esz = tensors[0].element_size()
+    ce = chunk_bytes // esz
+    starts = np.cumsum([0] + [(t.numel() + ce - 1) // ce for t in tensors])
+    gmap = ts.group_map() if ts is not None and ts.n_groups else None
+    for c in sample_chunks(n_chunks, k):
+        t = int(np.searchsorted(starts, c, side="right") - 1)
+        k0 = (c - starts[t]) * ce
+        chunk = to_np(tensors[t].reshape(-1)[k0:k0 + ce])
+        glen = ts.lengths(gmap[c]) if gmap is not None else None
+        rec, _ = oracle.encode_chunk(dt, chunk, glen, gmap[c] if gmap is not None else 0)
+        got = g[dirv[c]:dirv[c + 1]]
+        assert np.array_equal(got, rec), f"chunk {c}: " + first_difference(got, rec)
+
+
+def test_config2_block_full_size(oracle):
+    print("case: 8B-shaped BF16 block, full size, whole-container parity", flush=True)
+    tensors = [t for _, t in W.block_bf16("cuda", seed=2)]
+    _check_equal(oracle, oracle.BF16, tensors, 262144)
+
+
+def test_config3_fp32_full_size_sampled(oracle):
+    print("case: FP32 regular + clean 2 x 2^27, sampled records", flush=True)
+    tensors = [t for _, t in W.fp32_pair(1 << 27, device="cuda")]
+    ts, blob = gpu_compress(tensors, 262144)
+    _sampled_record_parity(oracle, oracle.FP32, tensors, blob, 262144)
+    assert_roundtrip(ts, blob, tensors)
+
+
+def test_config4_fp8_full_size_sampled(oracle):
+    print("case: FP8 E4M3 2^30, sampled records", flush=True)
+    tensors = [W.fp8_blockscaled(1 << 30, device="cuda")[0][1]]
+    ts, blob = gpu_compress(tensors, 262144)
+    _sampled_record_parity(oracle, oracle.FP8_E4M3, tensors, blob, 262144)
+    assert_roundtrip(ts, blob, tensors)
