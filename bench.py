@@ -1,0 +1,215 @@
+"""Benchmark of the codec's hot path on one MI355X.
+
+One step = one full pass of the path over the workload: zn_compress (field
+split, per-chunk histograms, code construction, look-back, packing) followed
+by zn_decompress (tables, segment-parallel decoding, merge) of every tensor.
+Inputs and buffers are resident in HBM before timing starts; three buffer
+sets rotate so consecutive steps do not hit the 256 MB Infinity Cache with
+the previous step's data.
+
+Prints one JSON line.  `value` is uncompressed GB/s through a whole step
+(compress + decompress); per-direction figures, the compression ratio, the
+roofline of each kernel (algorithmic bytes = container bytes + uncompressed
+bytes per pass, against 8 TB/s HBM) and the CPU oracle's rate on a bounded
+sample of the same workload are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "BF16 decompress/compress GB/s (uncompressed) + % HBM roofline; ratio"
+# Published by the benchmark spec: none, so there is nothing to divide by.
+BASELINE_VALUE = None
+
+WORKLOADS = {
+    "block": "8B-shaped BF16 transformer block: Wq 4096x4096, Wk/Wv 1024x4096, Wo 4096x4096, "
+             "W_gate/W_up 14336x4096, W_down 4096x14336 N(0, sigma~U[0.008,0.03]) + 2 RMSNorm "
+             "vectors N(1, 0.05); 218,112,000 BF16 values, 256 KiB chunks",
+    "single": "single BF16 tensor of 1,048,576 values N(0, 0.02), 256 KiB chunks",
+    "fp32": "FP32 2 x 134,217,728 values N(0, 0.02), regular + clean (low 16 fraction bits zero), "
+            "256 KiB chunks",
+    "fp8": "FP8 E4M3 1,073,741,824 values, N(0,1) scaled per 128-element block to max 448, "
+           "256 KiB chunks",
+}
+
+
+def make_tensors(name: str):
+    from lossless_float_weight_amd import workloads as W
+    if name == "block":
+        return [t for _, t in W.block_bf16("cuda", seed=2)]
+    if name == "single":
+        return [t for _, t in W.single_bf16(device="cuda")]
+    if name == "fp32":
+        return [t for _, t in W.fp32_pair(1 << 27, device="cuda")]
+    if name == "fp8":
+        return [t for _, t in W.fp8_blockscaled(1 << 30, device="cuda")]
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_baseline(tensors, budget_s: float = 20.0):
+    """The CPU oracle as it stands (single thread), compress + decompress of
+    a prefix of the workload's tensors chosen to take about budget_s."""
+    import numpy as np
+
+    from lossless_float_weight_amd import workloads as W
+    from oracle import zno
+    dt = {2: zno.BF16, 4: zno.FP32, 1: zno.FP8_E4M3}[tensors[0].element_size()]
+    arrs = [W.bits(t).reshape(-1).cpu().numpy() for t in tensors]
+    # calibrate on 4 MiB, then take whole tensors (and a slice of the last) up to the budget
+    probe = arrs[0][: (4 << 20) // arrs[0].itemsize] if arrs[0].nbytes > (4 << 20) else arrs[0]
+    t0 = time.perf_counter()
+    b = zno.compress(dt, [probe])
+    zno.decompress(b, [probe.size], dt)
+    rate = probe.nbytes / max(time.perf_counter() - t0, 1e-6)
+    want = rate * budget_s
+    sample, nbytes = [], 0
+    for a in arrs:
+        if nbytes >= want:
+            break
+        take = min(a.size, int((want - nbytes) // a.itemsize))
+        take = max(take, 1)
+        sample.append(np.ascontiguousarray(a[:take]))
+        nbytes += sample[-1].nbytes
+    t0 = time.perf_counter()
+    blob = zno.compress(dt, sample)
+    t1 = time.perf_counter()
+    outs = zno.decompress(blob, [s.size for s in sample], dt)
+    t2 = time.perf_counter()
+    assert all(np.array_equal(x, y) for x, y in zip(sample, outs))
+    return {"value": round(nbytes / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(sample)} leading tensor(s) of the workload, {nbytes} bytes, "
+                      f"compress {nbytes / (t1 - t0) / 1e9:.4f} GB/s + decompress "
+                      f"{nbytes / (t2 - t1) / 1e9:.4f} GB/s, single thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="block", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this codec's path runs on a single MI355X and shards "
+              f"by chunk ranges with no exchange during decode; --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        raise SystemExit(2)
+
+    import torch
+
+    from lossless_float_weight_amd import workloads as W
+    from lossless_float_weight_amd import zn
+
+    torch.cuda.set_device(0)
+    base = make_tensors(args.workload)
+    unc = sum(t.numel() * t.element_size() for t in base)
+    ts = zn.setup(base, chunk_bytes=262144)
+    bound = zn.compress_bound(ts)
+    R = max(1, args.rotate)
+    sets = []
+    for r in range(R):
+        ins = base if r == 0 else [t.clone() for t in base]
+        outs = [torch.empty_like(t).reshape(-1) for t in base]
+        sets.append({
+            "ins": ins, "outs": outs,
+            "in_ptrs": torch.tensor([t.data_ptr() for t in ins], dtype=torch.int64, device="cuda"),
+            "out_ptrs": torch.tensor([t.data_ptr() for t in outs], dtype=torch.int64, device="cuda"),
+            "blob": torch.empty(bound, dtype=torch.uint8, device="cuda"),
+            "cscr": zn.new_scratch(ts), "dscr": torch.empty(256, dtype=torch.uint8, device="cuda"),
+        })
+    # first pass: container size (needed to hand decompress its input length)
+    s0 = sets[0]
+    blob = zn.compress(ts, s0["ins"], out=s0["blob"], scratch=s0["cscr"], ptrs=s0["in_ptrs"])
+    nbytes = blob.numel()
+    for s in sets[1:]:
+        zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"])
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"], sync=False)
+        if ev is not None:
+            ev[1].record()
+        zn.decompress(ts, s["blob"][:nbytes], outs=s["outs"], scratch=s["dscr"], ptrs=s["out_ptrs"],
+                      sync=False)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % R], evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    comp_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+
+    # every buffer set must hold an exact round trip and report no error
+    for s in sets:
+        flags = int(s["cscr"][:4].view(torch.int32).item()) | int(s["dscr"][:4].view(torch.int32).item())
+        assert flags == 0, f"error flags {flags}"
+        total = int(s["blob"][56:64].cpu().numpy().view("<u8")[0])
+        assert total == nbytes
+        for a, b in zip(s["ins"], s["outs"]):
+            assert torch.equal(W.bits(a).reshape(-1), W.bits(b)), "round trip differs"
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2]
+
+    algo = nbytes + unc   # bytes a pass must read and write
+    rl = {}
+    for name, ms in (("decompress", med(dec_ms)), ("compress", med(comp_ms))):
+        gbps = algo / (ms * 1e-3) / 1e9
+        rl[name] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "kernel_ms": round(ms, 4)}
+    dominant = max(rl, key=lambda k: rl[k]["kernel_ms"])
+    ms_step = total_ms / args.steps
+    value = unc / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(value / BASELINE_VALUE, 4) if BASELINE_VALUE else None),
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "uncompressed_bytes": unc,
+                   "container_bytes": nbytes, "chunk_bytes": 262144, "tensors": len(base)},
+        "decompress_GBps": round(unc / (med(dec_ms) * 1e-3) / 1e9, 2),
+        "compress_GBps": round(unc / (med(comp_ms) * 1e-3) / 1e9, 2),
+        "ratio": round(nbytes / unc, 5),
+        "roofline": {k: v for k, v in rl[dominant].items() if k != "kernel_ms"} | {"kernel": dominant},
+        "roofline_decompress": rl["decompress"],
+        "roofline_compress": rl["compress"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(base)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -291,6 +291,7 @@ zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t 
   if (!ts) return ZN_ERR_NOMEM;
   zn_status st = make_plan(ts, dtype, n_elems, n_tensors, chunk_bytes);
   ts->K = n_groups;
+  ts->len.assign(256ull * n_groups, 0);  // group tables are serialised with the plan
   if (st == ZN_OK && n_groups > 0) {
     if (!d_tensors) st = ZN_ERR_ARG;
     for (int t = 0; st == ZN_OK && t < n_tensors; t++)
@@ -424,7 +425,6 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
   if (scratch_bytes < kCtlBytes) return ZN_ERR_CAPACITY;
   if (in_bytes < ts->off_records + 16) return ZN_ERR_CORRUPT;
   uint32_t *ctl = static_cast<uint32_t *>(d_scratch);
-  HIPCHK(launch_zero(ctl, kCtlBytes / 4, stream));
   CheckArgs ck;
   ck.in = static_cast<const uint8_t *>(d_in);
   ck.in_bytes = in_bytes;

@@ -57,6 +57,31 @@ __host__ __device__ inline uint64_t section_bytes(int mode, int k, uint64_t n, i
   return head_bytes_of(mode, k, nseg) + align16(payload_bytes_of(mode, k, n, bits));
 }
 
+// Global-memory pointers.  Pointers read from device arrays are generic to
+// the compiler; casting them to address space 1 gives global_load/store
+// (vector memory only, no LDS counter) and lets loads be scheduled early.
+#define ZN_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const ZN_GLOBAL T *gptr(const T *p) {
+  return (const ZN_GLOBAL T *)(p);
+}
+template <class T>
+__device__ __forceinline__ ZN_GLOBAL T *gptr(T *p) {
+  return (ZN_GLOBAL T *)(p);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 ldg16(const void *p) { return *(const ZN_GLOBAL u32x4 *)(p); }
+__device__ __forceinline__ u32x2 ldg8(const void *p) { return *(const ZN_GLOBAL u32x2 *)(p); }
+__device__ __forceinline__ uint32_t ldg4(const void *p) { return *(const ZN_GLOBAL uint32_t *)(p); }
+__device__ __forceinline__ uint32_t ldg2(const void *p) { return *(const ZN_GLOBAL uint16_t *)(p); }
+__device__ __forceinline__ uint32_t ldg1(const void *p) { return *(const ZN_GLOBAL uint8_t *)(p); }
+__device__ __forceinline__ void stg16(void *p, u32x4 v) { *(ZN_GLOBAL u32x4 *)(p) = v; }
+__device__ __forceinline__ void stg8(void *p, u32x2 v) { *(ZN_GLOBAL u32x2 *)(p) = v; }
+__device__ __forceinline__ void stg4(void *p, uint32_t v) { *(ZN_GLOBAL uint32_t *)(p) = v; }
+__device__ __forceinline__ void stg2(void *p, uint32_t v) { *(ZN_GLOBAL uint16_t *)(p) = uint16_t(v); }
+__device__ __forceinline__ void stg1(void *p, uint32_t v) { *(ZN_GLOBAL uint8_t *)(p) = uint8_t(v); }
+
 // Plan tables that kernels read (device memory owned by the tableset).
 struct DevLayout {
   const uint64_t *t_n;       // [T] elements per tensor

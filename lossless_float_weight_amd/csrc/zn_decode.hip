@@ -37,24 +37,44 @@ struct DecShared {
   int mode[NC], aux[NC];
   unsigned long long pay_off[NC], seg_off[NC];
   uint32_t pay[NC];
-  uint32_t wtot[DEC_NT / 64];
+  uint32_t wtot[DEC_NT / 64][NC];
   int bad;
 };
 
-template <int DT>
-__device__ __forceinline__ uint32_t merge_elem(const uint32_t *sym, uint32_t raw) {
-  if constexpr (DT == BF16) return ((raw & 0x80) << 8) | (sym[0] << 7) | (raw & 0x7F);
-  if constexpr (DT == FP32)
-    return ((sym[1] & 0x80) << 24) | (sym[0] << 23) | ((sym[1] & 0x7F) << 16) | (sym[2] << 8) | sym[3];
-  return ((raw & 1) << 7) | (sym[0] << 3) | sym[1];
+// Orders this wave's LDS writes before its later LDS reads by other lanes:
+// wait for the wave's LDS operations (lgkmcnt 0, vector memory untouched),
+// and keep the compiler from moving memory operations across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint64_t lds8(const uint8_t *p) { return *reinterpret_cast<const uint64_t *>(p); }
+__device__ __forceinline__ uint32_t lds4(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+// 8 BF16 values from 8 exponent bytes and 8 sign|fraction bytes.
+__device__ __forceinline__ u32x4 merge_bf16(uint64_t E, uint64_t SF) {
+  u32x4 o;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const uint32_t e = uint32_t(E >> (32 * h)), s = uint32_t(SF >> (32 * h));
+    const uint32_t x0 = (e & 0xFF) | ((e & 0xFF00) << 8), y0 = (s & 0xFF) | ((s & 0xFF00) << 8);
+    const uint32_t x1 = ((e >> 16) & 0xFF) | ((e >> 8) & 0xFF0000);
+    const uint32_t y1 = ((s >> 16) & 0xFF) | ((s >> 8) & 0xFF0000);
+    o[2 * h] = ((y0 & 0x00800080u) << 8) | (x0 << 7) | (y0 & 0x007F007Fu);
+    o[2 * h + 1] = ((y1 & 0x00800080u) << 8) | (x1 << 7) | (y1 & 0x007F007Fu);
+  }
+  return o;
 }
 
 template <int DT>
 __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
-  constexpr int LPS = DEC_NT / NC;       // lanes per stream
+  constexpr int SPW = 64 / NC;           // segment slots of one stream per wave
+  constexpr int GS = 4 * SPW;            // segment slots per stream per group
   constexpr int VE = 16 / ES;            // elements per 16-byte vector
-  constexpr int VPS = RND * ES / 16;     // vectors per segment per round
+  constexpr int VPS = RND * ES / 16;     // vectors per slot per round
+  constexpr int NVL = SPW * VPS / 64;    // vectors per lane per round
   __shared__ DecShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
   if (a.ctl[0]) return;  // the header check failed
@@ -68,6 +88,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   uint8_t *dst = a.out_ptrs[t] + e0 * ES;
   const bool oaligned = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
   const uint8_t *in = a.in;
+  const uint8_t *rawp = in + a.L.t_raw[t] + (DT == BF16 ? e0 : DT == FP8 ? e0 / 8 : 0);
 
   // ------------------------------------------------- 1. walk the record
   if (tid == 0) {
@@ -110,7 +131,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     const int k = kbits(DT, p), A = 1 << k, mode = sh.mode[p];
     if (mode == HUFF) {
       const uint8_t *nib = in + sh.seg_off[p] - A / 2;
-      if (tid < A) sh.len[p][tid] = (nib[tid >> 1] >> ((tid & 1) * 4)) & 15;
+      if (tid < A) sh.len[p][tid] = (ldg1(nib + (tid >> 1)) >> ((tid & 1) * 4)) & 15;
       __syncthreads();
       if (!build_lut<DEC_NT>(sh.len[p], A, sh.lut[p], sh.u.t1, sh.ls)) {
         if (tid == 0) atomicOr(&a.ctl[0], kErrCorrupt);
@@ -118,182 +139,238 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       }
     } else if (mode == GROUP) {
       const uint32_t *gl = a.group_lut + size_t(sh.aux[p]) * kLutSize;
-      for (int i = tid; i < kLutSize; i += DEC_NT) sh.lut[p][i] = gl[i];
-      if (tid < A) sh.len[p][tid] = a.group_len[sh.aux[p] * 256 + tid];
+      for (int i = tid; i < kLutSize; i += DEC_NT) sh.lut[p][i] = ldg4(gl + i);
+      if (tid < A) sh.len[p][tid] = ldg1(a.group_len + sh.aux[p] * 256 + tid);
     }
   }
   __syncthreads();
 
   // ------------------------------------------------ 3. lanes and rounds
-  const int p = tid / LPS, j = tid % LPS, k = kbits(DT, p);
+  // lane (wave wv, lane ln) decodes stream p, segment slot wv*SPW + ln%SPW
+  const int p = ln / SPW, slot = wv * SPW + ln % SPW, k = kbits(DT, p);
   const int mode = sh.mode[p];
   const bool coded = mode == HUFF || mode == GROUP;
-  const uint4 *P4 = reinterpret_cast<const uint4 *>(in + sh.pay_off[p]);
-  const uint32_t ngroups = (sh.pay[p] + 15) / 16;
+  const uint8_t *pay = in + sh.pay_off[p];
+  const uint32_t paybytes = sh.pay[p];
+  const uint32_t ngroups = (paybytes + 15) / 16;
   const uint32_t *lut = sh.lut[p];
   uint8_t *st = sh.u.stage + tid * STW;
-  uint32_t seg_carry = 0;  // bits of the stream's segments in earlier groups
+  uint8_t *wst = sh.u.stage + wv * 64 * STW;   // this wave's staging
+  uint32_t seg_carry = 0;
   int bad = 0;
-  const int G = (nseg + LPS - 1) / LPS;
+  const int G = (nseg + GS - 1) / GS;
   for (int g = 0; g < G; g++) {
-    const int sj = g * LPS + j;
+    const int sj = g * GS + slot;
     const bool live = sj < nseg;
     const int slen = live ? int(min(uint32_t(S), n - uint32_t(sj) * S)) : 0;
-    // start bit of this lane's segment: scan of the stored segment lengths
+    // start bit of the segment: scan of the stored segment bit lengths
     uint32_t sbits = 0;
-    if (coded && live) sbits = reinterpret_cast<const uint16_t *>(in + sh.seg_off[p])[sj];
+    if (coded && live) sbits = ldg2(in + sh.seg_off[p] + 2 * sj);
     const uint32_t incl = wave_incl_scan(sbits);
-    if (ln == 63) sh.wtot[wv] = incl;
+    const int first = p * SPW;
+    const uint32_t wbase = first > 0 ? __shfl(incl, first - 1, 64) : 0;
+    const uint32_t wlast = __shfl(incl, first + SPW - 1, 64);
+    if (ln == first) sh.wtot[wv][p] = wlast - wbase;
     __syncthreads();
     uint32_t before = 0, gtot = 0;
+#pragma unroll
     for (int q = 0; q < DEC_NT / 64; q++) {
-      if (q * 64 / LPS != p) continue;  // waves of this lane's stream
-      before += q < wv ? sh.wtot[q] : 0;
-      gtot += sh.wtot[q];
+      const uint32_t x = sh.wtot[q][p];
+      before += q < wv ? x : 0;
+      gtot += x;
     }
-    const uint32_t b0 = seg_carry + before + incl - sbits;
+    const uint32_t b0 = seg_carry + before + (incl - sbits - wbase);
     seg_carry += gtot;
     __syncthreads();
 
-    // bit reader state (LSB-first): 64-bit window, 16-byte prefetch queue
-    unsigned long long buf = 0;
+    // bit reader: 64-bit window (LSB-first), current 16-byte group as a
+    // shift register of words, and the next group loaded one group ahead
+    uint64_t buf = 0;
     int nb = 0;
-    uint4 q0 = make_uint4(0, 0, 0, 0), q1 = q0;
-    uint32_t gnext = 0, wtaken = 0;
-    int qi = 0;
-    auto grp = [&](uint32_t gi) { return P4[gi < ngroups ? gi : ngroups - 1]; };
-    auto take = [&]() -> uint32_t {
-      const uint32_t x = qi == 0 ? q0.x : qi == 1 ? q0.y : qi == 2 ? q0.z : q0.w;
-      wtaken++;
-      if (++qi == 4) {
-        q0 = q1;
-        q1 = grp(gnext++);
-        qi = 0;
-      }
-      return x;
-    };
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0, wpos = 0, gn = 0;
+    int cw = 0;
+    u32x4 nx = {0, 0, 0, 0};
+#define ZN_REFILL()                                                   \
+  do {                                                                \
+    buf |= uint64_t(c0) << nb;                                        \
+    nb += 32;                                                         \
+    wpos++;                                                           \
+    c0 = c1;                                                          \
+    c1 = c2;                                                          \
+    c2 = c3;                                                          \
+    if (--cw == 0) {                                                  \
+      c0 = nx[0];                                                     \
+      c1 = nx[1];                                                     \
+      c2 = nx[2];                                                     \
+      c3 = nx[3];                                                     \
+      cw = 4;                                                         \
+      nx = ldg16(pay + 16ull * (gn < ngroups ? gn : ngroups - 1));    \
+      gn++;                                                           \
+    }                                                                 \
+  } while (0)
     if (coded && live) {
-      const uint32_t w0 = b0 >> 5;
-      gnext = (w0 >> 2);
-      q0 = grp(gnext++);
-      q1 = grp(gnext++);
-      qi = int(w0 & 3);
-      wtaken = w0;
-      buf = take();
-      buf |= (unsigned long long)take() << 32;
+      const uint32_t w0 = b0 >> 5, gi = w0 >> 2;
+      const u32x4 q = ldg16(pay + 16ull * (gi < ngroups ? gi : ngroups - 1));
+      nx = ldg16(pay + 16ull * (gi + 1 < ngroups ? gi + 1 : ngroups - 1));
+      gn = gi + 2;
+      c0 = q[0], c1 = q[1], c2 = q[2], c3 = q[3];
+      cw = 4;
+      for (uint32_t s0 = 0; s0 < (w0 & 3); s0++) {
+        c0 = c1, c1 = c2, c2 = c3;
+        cw--;
+      }
+      wpos = w0;
+      ZN_REFILL();
+      ZN_REFILL();
       buf >>= (b0 & 31);
-      nb = 64 - int(b0 & 31);
+      nb -= int(b0 & 31);
     }
-    int ov = 0;          // symbols decoded past the previous round's end
-    uint32_t carry = 0;  // those symbols
-    const int rounds = S / RND;
-    for (int r = 0; r < rounds; r++) {
+    int ov = 0;
+    for (int r = 0; r < S / RND; r++) {
       const int base = r * RND;
       const int lim = slen - base < RND ? (slen - base > 0 ? slen - base : 0) : RND;
-      // prefetch of the raw bits this thread merges after the round
-      constexpr int NVT = (LPS * VPS + DEC_NT - 1) / DEC_NT;
-      unsigned long long rawv[NVT];
-      const int nsg = nseg - g * LPS < LPS ? nseg - g * LPS : LPS;
+      // raw bits merged by this lane after the round, loaded before decoding
+      uint64_t rawv[NVL];
 #pragma unroll
-      for (int i = 0; i < NVT; i++) {
+      for (int i = 0; i < NVL; i++) {
         rawv[i] = 0;
-        const int v = tid + i * DEC_NT;
-        const int sjv = g * LPS + v / VPS;
-        const uint32_t ev = uint32_t(sjv) * S + base + (v % VPS) * VE;
-        if (v / VPS < nsg && ev < n) {
+        const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
+        const int sjv = g * GS + wv * SPW + sl;
+        const uint32_t ev = uint32_t(sjv) * S + base + part * VE;
+        if (sjv < nseg && ev < n) {
           if constexpr (DT == BF16) {
-            const uint8_t *rp = in + a.L.t_raw[t] + e0 + ev;
-            if (ev + VE <= n) rawv[i] = *reinterpret_cast<const unsigned long long *>(rp);
-            else for (uint32_t q = 0; ev + q < n; q++) rawv[i] |= (unsigned long long)rp[q] << (8 * q);
+            if (ev + 8 <= n) {
+              const u32x2 x = ldg8(rawp + ev);
+              rawv[i] = x[0] | (uint64_t(x[1]) << 32);
+            } else {
+              for (uint32_t q = 0; ev + q < n; q++) rawv[i] |= uint64_t(ldg1(rawp + ev + q)) << (8 * q);
+            }
           } else if constexpr (DT == FP8) {
-            const uint8_t *rp = in + a.L.t_raw[t] + (e0 + ev) / 8;
-            rawv[i] = rp[0] | (ev + 8 < n ? uint32_t(rp[1]) << 8 : 0u);
+            if (ev + 16 <= n) rawv[i] = ldg2(rawp + ev / 8);
+            else rawv[i] = ldg1(rawp + ev / 8) | (ev + 8 < n ? ldg1(rawp + ev / 8 + 1) << 8 : 0u);
           }
         }
       }
       if (lim > 0) {
         if (coded) {
+          if (ov > 0) *reinterpret_cast<uint64_t *>(st) = lds8(st + RND);
           int cnt = ov;
-          if (ov > 0) st[0] = uint8_t(carry);
-          if (ov > 1) st[1] = uint8_t(carry >> 8);
-          uint32_t e = 0;
           while (cnt < lim) {
-            if (nb < 32) {
-              buf |= (unsigned long long)take() << nb;
-              nb += 32;
-            }
+            if (nb < 32) ZN_REFILL();
+            uint32_t e = lut[buf & (kLutSize - 1)];
+            st[cnt] = uint8_t(e);
+            st[cnt + 1] = uint8_t(e >> 8);
+            st[cnt + 2] = uint8_t(e >> 16);
+            cnt += int(e >> 28);
+            int bl = int((e >> 24) & 15);
+            buf >>= bl;
+            nb -= bl;
             e = lut[buf & (kLutSize - 1)];
             st[cnt] = uint8_t(e);
             st[cnt + 1] = uint8_t(e >> 8);
             st[cnt + 2] = uint8_t(e >> 16);
             cnt += int(e >> 28);
-            const int bl = int((e >> 24) & 15);
+            bl = int((e >> 24) & 15);
             buf >>= bl;
             nb -= bl;
           }
           ov = cnt - lim;
-          carry = ov > 0 ? (uint32_t(st[lim]) | (uint32_t(st[lim + 1]) << 8)) : 0;
           if (base + lim == slen) {
             // exact end: the segment must use exactly its stored bit length
-            uint64_t pos = uint64_t(wtaken) * 32 - uint32_t(nb);
-            for (int q = 0; q < ov; q++) pos -= sh.len[p][(carry >> (8 * q)) & 0xFF];
+            uint64_t pos = uint64_t(wpos) * 32 - uint32_t(nb);
+            for (int q = 0; q < ov; q++) pos -= sh.len[p][st[lim + q]];
             if (pos != uint64_t(b0) + sbits) bad = 1;
           }
         } else if (mode == RAW) {
-          // k-bit values, value bit 0 first; a round spans whole words
-          const uint64_t i0 = uint64_t(sj) * S + base;
-          const uint32_t *pw = reinterpret_cast<const uint32_t *>(in + sh.pay_off[p]);
-          const uint64_t wbase = i0 * k / 32;
-          const uint32_t maxw = (sh.pay[p] + 15) / 16 * 4;
-          uint32_t wds[8];
+          // k-bit values, value bit 0 first; a round spans k whole words
+          const uint64_t wb = (uint64_t(sj) * S + base) * k / 32;
+          const uint32_t maxw = (paybytes + 15) / 16 * 4;
+          uint32_t wd[8];
+          if (k != 3 && wb + k <= maxw) {
+            const u32x4 q0 = ldg16(pay + 4 * wb);
+            wd[0] = q0[0], wd[1] = q0[1], wd[2] = q0[2], wd[3] = q0[3];
+            if (k == 8) {
+              const u32x4 q1 = ldg16(pay + 4 * wb + 16);
+              wd[4] = q1[0], wd[5] = q1[1], wd[6] = q1[2], wd[7] = q1[3];
+            } else {
+              wd[4] = wd[5] = wd[6] = wd[7] = 0;
+            }
+          } else {
 #pragma unroll
-          for (int q = 0; q < 8; q++)
-            wds[q] = (q < k && wbase + q < maxw) ? pw[wbase + q] : 0u;
+            for (int q = 0; q < 8; q++) wd[q] = (q < k && wb + q < maxw) ? ldg4(pay + 4 * (wb + q)) : 0u;
+          }
+          if (k == 8) {
 #pragma unroll
-          for (int m = 0; m < RND; m++) {
-            const int bit = m * k;
-            const uint32_t lo = wds[bit >> 5] >> (bit & 31);
-            const uint32_t hi = (bit & 31) + k > 32 ? wds[(bit >> 5) + 1] << (32 - (bit & 31)) : 0u;
-            st[m] = uint8_t((lo | hi) & ((1u << k) - 1));
+            for (int q = 0; q < 4; q++)
+              *reinterpret_cast<uint64_t *>(st + 8 * q) = wd[2 * q] | (uint64_t(wd[2 * q + 1]) << 32);
+          } else {
+#pragma unroll
+            for (int m = 0; m < RND; m++) {
+              const int bit = m * k;
+              const uint32_t lo = wd[bit >> 5] >> (bit & 31);
+              const uint32_t hi = (bit & 31) + k > 32 ? wd[(bit >> 5) + 1] << (32 - (bit & 31)) : 0u;
+              st[m] = uint8_t((lo | hi) & ((1u << k) - 1));
+            }
           }
         }
       }
-      __syncthreads();
-      // merge and store: vector v covers VE elements of segment v / VPS
+      wave_lds_sync();
+      // merge and store: vector v of this wave covers VE elements of slot v / VPS
 #pragma unroll
-      for (int i = 0; i < NVT; i++) {
-        const int v = tid + i * DEC_NT;
-        const int js = v / VPS, part = v % VPS;
-        const uint32_t ev = uint32_t(g * LPS + js) * S + base + part * VE;
-        if (js >= nsg || ev >= n) continue;
-        uint32_t outw[4] = {0, 0, 0, 0};
-        const int cnt_e = ev + VE <= n ? VE : int(n - ev);
-        for (int q = 0; q < VE; q++) {
-          uint32_t sym[4] = {0, 0, 0, 0};
+      for (int i = 0; i < NVL; i++) {
+        const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
+        const int sjv = g * GS + wv * SPW + sl;
+        const uint32_t ev = uint32_t(sjv) * S + base + part * VE;
+        if (sjv >= nseg || ev >= n) continue;
+        u32x4 o;
+        if constexpr (DT == BF16) {
+          const uint64_t E = sh.mode[0] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[0])
+                                                 : lds8(wst + sl * STW + part * 8);
+          o = merge_bf16(E, rawv[i]);
+        } else if constexpr (DT == FP32) {
+          uint32_t P[4];
 #pragma unroll
-          for (int pp = 0; pp < NC; pp++) {
-            const int mp = sh.mode[pp];
-            sym[pp] = mp == CONST ? uint32_t(sh.aux[pp])
-                                  : sh.u.stage[(pp * LPS + js) * STW + part * VE + q];
+          for (int pp = 0; pp < 4; pp++)
+            P[pp] = sh.mode[pp] == CONST ? 0x01010101u * uint32_t(sh.aux[pp])
+                                         : lds4(wst + (pp * SPW + sl) * STW + part * 4);
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const uint32_t p0 = (P[0] >> (8 * q)) & 0xFF, p1 = (P[1] >> (8 * q)) & 0xFF;
+            const uint32_t p2 = (P[2] >> (8 * q)) & 0xFF, p3 = (P[3] >> (8 * q)) & 0xFF;
+            o[q] = ((p1 & 0x80) << 24) | (p0 << 23) | ((p1 & 0x7F) << 16) | (p2 << 8) | p3;
           }
-          uint32_t raw = 0;
-          if constexpr (DT == BF16) raw = uint32_t(rawv[i] >> (8 * q)) & 0xFF;
-          if constexpr (DT == FP8) raw = uint32_t(rawv[i] >> q) & 1;
-          const uint32_t w = merge_elem<DT>(sym, raw);
-          outw[(q * ES) >> 2] |= w << (((q * ES) & 3) * 8);
+        } else {
+          uint64_t Ev[2], Mv[2];
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            Ev[h] = sh.mode[0] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[0])
+                                        : lds8(wst + sl * STW + part * 16 + 8 * h);
+            Mv[h] = sh.mode[1] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[1])
+                                        : lds8(wst + (SPW + sl) * STW + part * 16 + 8 * h);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const uint32_t e4 = uint32_t(Ev[q >> 1] >> (32 * (q & 1)));
+            const uint32_t m3 = uint32_t(Mv[q >> 1] >> (32 * (q & 1)));
+            const uint32_t sg = uint32_t(rawv[i] >> (4 * q)) & 15;
+            const uint32_t sb = ((sg & 1) << 7) | ((sg & 2) << 14) | ((sg & 4) << 21) | ((sg & 8) << 28);
+            o[q] = (e4 << 3) | m3 | sb;
+          }
         }
         uint8_t *op = dst + uint64_t(ev) * ES;
-        if (cnt_e == VE && oaligned) {
-          *reinterpret_cast<uint4 *>(op) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+        if (ev + VE <= n && oaligned) {
+          stg16(op, o);
         } else {
-          for (int b = 0; b < cnt_e * ES; b++) op[b] = uint8_t(outw[b >> 2] >> ((b & 3) * 8));
+          const uint32_t cnt_b = (ev + VE <= n ? VE : n - ev) * ES;
+          for (uint32_t b = 0; b < cnt_b; b++) stg1(op + b, o[b >> 2] >> ((b & 3) * 8));
         }
       }
-      __syncthreads();
+      wave_lds_sync();
     }
+#undef ZN_REFILL
   }
   // the stream's segment lengths must add up to its payload
-  if (coded && j == 0 && sh.pay[p] != 4 * ((seg_carry + 31) / 32)) bad = 1;
+  if (coded && ln % SPW == 0 && wv == 0 && paybytes != 4 * ((seg_carry + 31) / 32)) bad = 1;
   if (bad) atomicOr(&a.ctl[0], kErrCorrupt);
 }
 
@@ -302,8 +379,9 @@ __global__ void k_check(CheckArgs a) {
   __shared__ int bad;
   if (tid == 0) bad = 0;
   __syncthreads();
+  // this kernel runs first and owns the error word: it stores, the decode ORs
   if (a.in_bytes < a.hdr_bytes + 8ull * (a.n_chunks + 1)) {
-    if (tid == 0) atomicOr(a.ctl, kErrCorrupt);
+    if (tid == 0) a.ctl[0] = kErrCorrupt;
     return;
   }
   for (uint32_t i = tid; i < a.hdr_bytes; i += blockDim.x) {
@@ -322,7 +400,7 @@ __global__ void k_check(CheckArgs a) {
     if (total > a.in_bytes || (total & 15) || total < 16) err |= kErrCorrupt;
     else if (*reinterpret_cast<const uint64_t *>(a.in + a.off_dir + 8ull * a.n_chunks) != total - 16)
       err |= kErrCorrupt;
-    if (err) atomicOr(a.ctl, err);
+    a.ctl[0] = err;
   }
 }
 

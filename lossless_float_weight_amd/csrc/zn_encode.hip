@@ -67,10 +67,9 @@ __device__ __forceinline__ uint32_t vec_elem(const uint4 &q, int i) {
 
 template <int DT>
 __device__ __forceinline__ uint32_t load_elem(const uint8_t *p) {
-  if constexpr (DT == BF16) return uint32_t(p[0]) | (uint32_t(p[1]) << 8);
-  if constexpr (DT == FP32)
-    return uint32_t(p[0]) | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16) | (uint32_t(p[3]) << 24);
-  return p[0];
+  if constexpr (DT == BF16) return ldg1(p) | (ldg1(p + 1) << 8);
+  if constexpr (DT == FP32) return ldg1(p) | (ldg1(p + 1) << 8) | (ldg1(p + 2) << 16) | (ldg1(p + 3) << 24);
+  return ldg1(p);
 }
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
@@ -168,29 +167,41 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
   for (int i = tid; i < EncShared<DT>::APRIV * COLS; i += ENC_NT) sh.u.priv[i] = 0;
   __syncthreads();
   const int col = ln & (COLS - 1);
-  for (uint32_t v = tid; v < nvec; v += ENC_NT) {
-    const uint4 q = reinterpret_cast<const uint4 *>(src)[v];
+  constexpr int B1 = 4;  // 16-byte loads in flight per thread
+  for (uint32_t v0 = tid; v0 < nvec; v0 += B1 * ENC_NT) {
+    u32x4 qs[B1];
 #pragma unroll
-    for (int i = 0; i < VE; i++) {
-      const uint32_t w = vec_elem<DT>(q, i);
-#pragma unroll
-      for (int p = 0; p < NC; p++)
-        atomicAdd(&sh.u.priv[(priv_base<DT>(p) + field_rt<DT>(w, p)) * COLS + col], 1u);
+    for (int b = 0; b < B1; b++) {
+      const uint32_t v = v0 + b * ENC_NT;
+      if (v < nvec) qs[b] = ldg16(src + 16ull * v);
     }
-    if constexpr (DT == BF16) {
-      uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const uint32_t w0 = vec_elem<DT>(q, i), w1 = vec_elem<DT>(q, i + 4);
-        lo |= (((w0 >> 8) & 0x80) | (w0 & 0x7F)) << (8 * i);
-        hi |= (((w1 >> 8) & 0x80) | (w1 & 0x7F)) << (8 * i);
+    for (int b = 0; b < B1; b++) {
+      const uint32_t v = v0 + b * ENC_NT;
+      if (v >= nvec) break;
+      const uint4 q = make_uint4(qs[b][0], qs[b][1], qs[b][2], qs[b][3]);
+#pragma unroll
+      for (int i = 0; i < VE; i++) {
+        const uint32_t w = vec_elem<DT>(q, i);
+#pragma unroll
+        for (int p = 0; p < NC; p++)
+          atomicAdd(&sh.u.priv[(priv_base<DT>(p) + field_rt<DT>(w, p)) * COLS + col], 1u);
       }
-      *reinterpret_cast<uint2 *>(rawp + e0 + uint64_t(v) * 8) = make_uint2(lo, hi);
-    } else if constexpr (DT == FP8) {
-      uint32_t m = 0;
+      if constexpr (DT == BF16) {
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int i = 0; i < 16; i++) m |= ((vec_elem<DT>(q, i) >> 7) & 1) << i;
-      *reinterpret_cast<uint16_t *>(rawp + e0 / 8 + uint64_t(v) * 2) = uint16_t(m);
+        for (int i = 0; i < 4; i++) {
+          const uint32_t w0 = vec_elem<DT>(q, i), w1 = vec_elem<DT>(q, i + 4);
+          lo |= (((w0 >> 8) & 0x80) | (w0 & 0x7F)) << (8 * i);
+          hi |= (((w1 >> 8) & 0x80) | (w1 & 0x7F)) << (8 * i);
+        }
+        stg8(rawp + e0 + uint64_t(v) * 8, u32x2{lo, hi});
+      } else if constexpr (DT == FP8) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) m |= ((vec_elem<DT>(q, i) >> 7) & 1) << i;
+        stg2(rawp + e0 / 8 + uint64_t(v) * 2, m);
+      }
     }
   }
   for (uint32_t i = nvec * VE + tid; i < n; i += ENC_NT) {  // ragged tail or unaligned input
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
 #pragma unroll
     for (int p = 0; p < NC; p++)
       atomicAdd(&sh.u.priv[(priv_base<DT>(p) + field_rt<DT>(w, p)) * COLS + col], 1u);
-    if constexpr (DT == BF16) rawp[e0 + i] = uint8_t(((w >> 8) & 0x80) | (w & 0x7F));
+    if constexpr (DT == BF16) stg1(rawp + e0 + i, ((w >> 8) & 0x80) | (w & 0x7F));
   }
   if constexpr (DT == FP8) {  // sign bits of the tail, whole bytes by one thread
     if (tid == 0 && nvec * VE < n) {
@@ -356,10 +367,13 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
       const uint32_t eb = tb + uint32_t(tid) * EPT;
       uint32_t w[EPT];
       if (aligned && eb + EPT <= n) {
-        const uint4 *vp = reinterpret_cast<const uint4 *>(src + uint64_t(eb) * ES);
+        const uint8_t *vp = src + uint64_t(eb) * ES;
+        u32x4 qs[NV];
+#pragma unroll
+        for (int j = 0; j < NV; j++) qs[j] = ldg16(vp + 16 * j);
 #pragma unroll
         for (int j = 0; j < NV; j++) {
-          const uint4 q = vp[j];
+          const uint4 q = make_uint4(qs[j][0], qs[j][1], qs[j][2], qs[j][3]);
 #pragma unroll
           for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
         }
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
       const uint32_t endb = uint32_t(tbit & 31) + ttot;
       const uint32_t nfull = endb >> 5;
       const uint64_t w0 = tbit >> 5;
-      for (uint32_t i = tid; i < nfull; i += ENC_NT) pw[w0 + i] = sh.u.pk.stage[i];
+      for (uint32_t i = tid; i < nfull; i += ENC_NT) stg4(pw + w0 + i, sh.u.pk.stage[i]);
       carry = (endb & 31) ? sh.u.pk.stage[nfull] : 0;
       tbit += ttot;
       __syncthreads();

@@ -192,10 +192,22 @@ def test_header_and_table_corruption_rejected(oracle):
     with pytest.raises(zn.ZnError) as e:
         zn.decompress(ts, bad)
     assert e.value.code == -2
-    other = zn.setup([x], chunk_bytes=8192, n_groups=2)
+    # an ungrouped container decodes under any plan of the same layout ...
+    same_layout = zn.setup([x], chunk_bytes=8192, n_groups=2)
+    assert torch.equal(zn.decompress(same_layout, blob)[0].view(torch.int16), x.view(torch.int16))
+    # ... but not under another layout
+    other = zn.setup([x], chunk_bytes=16384)
     with pytest.raises(zn.ZnError) as e:
         zn.decompress(other, blob)
-    assert e.value.code in (-2, -4)
+    assert e.value.code == -2
+    # a grouped container needs the very tableset it was made with
+    _, gblob = gpu_compress([x], 8192, same_layout)
+    third = zn.setup([x * 3], chunk_bytes=8192, n_groups=2)
+    if third.hash != same_layout.hash:
+        with pytest.raises(zn.ZnError) as e:
+            zn.decompress(third, gblob)
+        assert e.value.code == -4
+    assert oracle.decompress_status(gblob.cpu().numpy(), [x.numel()]) == -4
 
 
 def test_capacity_reported():
