@@ -21,8 +21,10 @@
 namespace zn {
 
 constexpr int DEC_NT = 256;
-constexpr int RND = 32;        // symbols per lane per round
-constexpr int STW = RND + 8;   // staging bytes per lane (overflow slack, 8-byte multiple)
+constexpr int RND = 32;        // symbols per lane per round = one strip of its segment
+constexpr int STW = 44;        // staging bytes per lane: a strip + overflow; 11 words
+                               // keep 32 neighbouring lanes on distinct LDS banks
+constexpr int RING = 16;       // words of a lane's payload window in LDS
 
 template <int DT>
 struct DecShared {
@@ -32,6 +34,7 @@ struct DecShared {
     uint16_t t1[kLutSize];
     uint8_t stage[DEC_NT * STW];
   } u;
+  uint32_t ring[DEC_NT * RING];
   uint8_t len[NC][256];
   LutShared ls;
   int mode[NC], aux[NC];
@@ -49,7 +52,10 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ uint64_t lds8(const uint8_t *p) { return *reinterpret_cast<const uint64_t *>(p); }
+__device__ __forceinline__ uint64_t lds8(const uint8_t *p) {  // 4-byte aligned
+  const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+  return q[0] | (uint64_t(q[1]) << 32);
+}
 __device__ __forceinline__ uint32_t lds4(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
 // 8 BF16 values from 8 exponent bytes and 8 sign|fraction bytes.
@@ -146,7 +152,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   __syncthreads();
 
   // ------------------------------------------------ 3. lanes and rounds
-  // lane (wave wv, lane ln) decodes stream p, segment slot wv*SPW + ln%SPW
+  // Lane (wave wv, lane ln) decodes stream p, segment slot wv*SPW + ln%SPW.
+  // Round r decodes strip r*nseg + j of every segment j, so one round of a
+  // wave covers SPW consecutive strips: a contiguous block of the output.
   const int p = ln / SPW, slot = wv * SPW + ln % SPW, k = kbits(DT, p);
   const int mode = sh.mode[p];
   const bool coded = mode == HUFF || mode == GROUP;
@@ -155,14 +163,16 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   const uint32_t ngroups = (paybytes + 15) / 16;
   const uint32_t *lut = sh.lut[p];
   uint8_t *st = sh.u.stage + tid * STW;
-  uint8_t *wst = sh.u.stage + wv * 64 * STW;   // this wave's staging
+  uint32_t *st32 = reinterpret_cast<uint32_t *>(st);
+  const uint8_t *wst = sh.u.stage + wv * 64 * STW;   // this wave's staging
+  uint32_t *ring = sh.ring + tid * RING;
   uint32_t seg_carry = 0;
   int bad = 0;
+  const uint32_t nstrips = (n + RND - 1) / RND;
   const int G = (nseg + GS - 1) / GS;
   for (int g = 0; g < G; g++) {
     const int sj = g * GS + slot;
     const bool live = sj < nseg;
-    const int slen = live ? int(min(uint32_t(S), n - uint32_t(sj) * S)) : 0;
     // start bit of the segment: scan of the stored segment bit lengths
     uint32_t sbits = 0;
     if (coded && live) sbits = ldg2(in + sh.seg_off[p] + 2 * sj);
@@ -183,52 +193,43 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     seg_carry += gtot;
     __syncthreads();
 
-    // bit reader: 64-bit window (LSB-first), current 16-byte group as a
-    // shift register of words, and the next group loaded one group ahead
+    // Bit reader: a 64-bit window (LSB-first) refilled one word at a time
+    // from the lane's ring of payload words in LDS.  Words reach the ring in
+    // 16-byte groups loaded one round before they can be needed.
     uint64_t buf = 0;
     int nb = 0;
-    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0, wpos = 0, gn = 0;
-    int cw = 0;
-    u32x4 nx = {0, 0, 0, 0};
-#define ZN_REFILL()                                                   \
-  do {                                                                \
-    buf |= uint64_t(c0) << nb;                                        \
-    nb += 32;                                                         \
-    wpos++;                                                           \
-    c0 = c1;                                                          \
-    c1 = c2;                                                          \
-    c2 = c3;                                                          \
-    if (--cw == 0) {                                                  \
-      c0 = nx[0];                                                     \
-      c1 = nx[1];                                                     \
-      c2 = nx[2];                                                     \
-      c3 = nx[3];                                                     \
-      cw = 4;                                                         \
-      nx = ldg16(pay + 16ull * (gn < ngroups ? gn : ngroups - 1));    \
-      gn++;                                                           \
-    }                                                                 \
-  } while (0)
+    uint32_t wpos = 0, wf = 0, pre = 0;  // next word to read, first word not fetched
+    u32x4 pq0 = {0, 0, 0, 0}, pq1 = pq0, pq2 = pq0;
+    uint32_t pend_g = 0;
+    int pend_n = 0;
+    auto grp = [&](uint32_t gi) { return ldg16(pay + 16ull * (gi < ngroups ? gi : ngroups - 1)); };
     if (coded && live) {
-      const uint32_t w0 = b0 >> 5, gi = w0 >> 2;
-      const u32x4 q = ldg16(pay + 16ull * (gi < ngroups ? gi : ngroups - 1));
-      nx = ldg16(pay + 16ull * (gi + 1 < ngroups ? gi + 1 : ngroups - 1));
-      gn = gi + 2;
-      c0 = q[0], c1 = q[1], c2 = q[2], c3 = q[3];
-      cw = 4;
-      for (uint32_t s0 = 0; s0 < (w0 & 3); s0++) {
-        c0 = c1, c1 = c2, c2 = c3;
-        cw--;
-      }
-      wpos = w0;
-      ZN_REFILL();
-      ZN_REFILL();
+      const uint32_t w0 = b0 >> 5, g0 = w0 >> 2;
+      const u32x4 a0 = grp(g0), a1 = grp(g0 + 1), a2 = grp(g0 + 2), a3 = grp(g0 + 3);
+      *reinterpret_cast<u32x4 *>(ring + 4 * (g0 & 3)) = a0;
+      *reinterpret_cast<u32x4 *>(ring + 4 * ((g0 + 1) & 3)) = a1;
+      *reinterpret_cast<u32x4 *>(ring + 4 * ((g0 + 2) & 3)) = a2;
+      *reinterpret_cast<u32x4 *>(ring + 4 * ((g0 + 3) & 3)) = a3;
+      wf = 4 * (g0 + 4);
+      buf = ring[w0 & (RING - 1)] | (uint64_t(ring[(w0 + 1) & (RING - 1)]) << 32);
+      wpos = w0 + 2;
       buf >>= (b0 & 31);
-      nb -= int(b0 & 31);
+      nb = 64 - int(b0 & 31);
     }
-    int ov = 0;
+    uint64_t acc = 0;   // decoded symbols not yet written, one per byte
+    int ov = 0;         // symbols of the next strip decoded early
     for (int r = 0; r < S / RND; r++) {
-      const int base = r * RND;
-      const int lim = slen - base < RND ? (slen - base > 0 ? slen - base : 0) : RND;
+      const uint32_t q = uint32_t(r) * nseg + sj;   // this lane's strip
+      const int lim = live && q < nstrips ? int(min(uint32_t(RND), n - q * RND)) : 0;
+      const bool last = live && q < nstrips && q + nseg >= nstrips;
+      // groups fetched last round enter the ring
+      if (pend_n > 0) {
+        *reinterpret_cast<u32x4 *>(ring + 4 * (pend_g & 3)) = pq0;
+        if (pend_n > 1) *reinterpret_cast<u32x4 *>(ring + 4 * ((pend_g + 1) & 3)) = pq1;
+        if (pend_n > 2) *reinterpret_cast<u32x4 *>(ring + 4 * ((pend_g + 2) & 3)) = pq2;
+        wf = 4 * (pend_g + pend_n);
+        pend_n = 0;
+      }
       // raw bits merged by this lane after the round, loaded before decoding
       uint64_t rawv[NVL];
 #pragma unroll
@@ -236,14 +237,15 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         rawv[i] = 0;
         const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
         const int sjv = g * GS + wv * SPW + sl;
-        const uint32_t ev = uint32_t(sjv) * S + base + part * VE;
+        const uint32_t qv = uint32_t(r) * nseg + sjv;
+        const uint32_t ev = qv * RND + part * VE;
         if (sjv < nseg && ev < n) {
           if constexpr (DT == BF16) {
             if (ev + 8 <= n) {
               const u32x2 x = ldg8(rawp + ev);
               rawv[i] = x[0] | (uint64_t(x[1]) << 32);
             } else {
-              for (uint32_t q = 0; ev + q < n; q++) rawv[i] |= uint64_t(ldg1(rawp + ev + q)) << (8 * q);
+              for (uint32_t b = 0; ev + b < n; b++) rawv[i] |= uint64_t(ldg1(rawp + ev + b)) << (8 * b);
             }
           } else if constexpr (DT == FP8) {
             if (ev + 16 <= n) rawv[i] = ldg2(rawp + ev / 8);
@@ -253,37 +255,73 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       }
       if (lim > 0) {
         if (coded) {
-          if (ov > 0) *reinterpret_cast<uint64_t *>(st) = lds8(st + RND);
-          int cnt = ov;
-          while (cnt < lim) {
-            if (nb < 32) ZN_REFILL();
-            uint32_t e = lut[buf & (kLutSize - 1)];
-            st[cnt] = uint8_t(e);
-            st[cnt + 1] = uint8_t(e >> 8);
-            st[cnt + 2] = uint8_t(e >> 16);
-            cnt += int(e >> 28);
-            int bl = int((e >> 24) & 15);
-            buf >>= bl;
-            nb -= bl;
-            e = lut[buf & (kLutSize - 1)];
-            st[cnt] = uint8_t(e);
-            st[cnt + 1] = uint8_t(e >> 8);
-            st[cnt + 2] = uint8_t(e >> 16);
-            cnt += int(e >> 28);
-            bl = int((e >> 24) & 15);
-            buf >>= bl;
-            nb -= bl;
+          int cnt = ov, na = ov, sw = 0;
+          if (na >= 4) {
+            st32[sw++] = uint32_t(acc);
+            acc >>= 32;
+            na -= 4;
           }
+          pre = ring[wpos & (RING - 1)];
+          while (cnt < lim) {
+            if (nb < 32) {
+              buf |= uint64_t(pre) << nb;
+              nb += 32;
+              wpos++;
+              pre = ring[wpos & (RING - 1)];
+            }
+            uint32_t e = lut[buf & (kLutSize - 1)];
+            int m = int(e >> 28), bl = int((e >> 24) & 15);
+            acc |= uint64_t(e & 0xFFFFFF) << (8 * na);
+            na += m;
+            cnt += m;
+            buf >>= bl;
+            nb -= bl;
+            if (na >= 4) {
+              st32[sw++] = uint32_t(acc);
+              acc >>= 32;
+              na -= 4;
+            }
+            if (cnt < lim) {
+              e = lut[buf & (kLutSize - 1)];
+              m = int(e >> 28), bl = int((e >> 24) & 15);
+              acc |= uint64_t(e & 0xFFFFFF) << (8 * na);
+              na += m;
+              cnt += m;
+              buf >>= bl;
+              nb -= bl;
+              if (na >= 4) {
+                st32[sw++] = uint32_t(acc);
+                acc >>= 32;
+                na -= 4;
+              }
+            }
+          }
+          st32[sw] = uint32_t(acc);  // the partial last word
           ov = cnt - lim;
-          if (base + lim == slen) {
+          if (last) {
             // exact end: the segment must use exactly its stored bit length
             uint64_t pos = uint64_t(wpos) * 32 - uint32_t(nb);
-            for (int q = 0; q < ov; q++) pos -= sh.len[p][st[lim + q]];
+            for (int x = 0; x < ov; x++) pos -= sh.len[p][st[lim + x]];
             if (pos != uint64_t(b0) + sbits) bad = 1;
+            ov = 0;
+          } else {
+            // lim == RND here, and at most 2 symbols run over (the second
+            // lookup of an iteration only runs below the limit)
+            acc = ov ? (st32[8] & (0xFFFFFFFFu >> (32 - 8 * ov))) : 0;
+            // fetch the groups the next round may need: words [wpos, wpos + 12)
+            const uint32_t needg = (wpos + 12 + 3) / 4;
+            const uint32_t have = wf / 4;
+            if (needg > have) {
+              pend_g = have;
+              pend_n = int(needg - have);
+              pq0 = grp(pend_g);
+              if (pend_n > 1) pq1 = grp(pend_g + 1);
+              if (pend_n > 2) pq2 = grp(pend_g + 2);
+            }
           }
         } else if (mode == RAW) {
-          // k-bit values, value bit 0 first; a round spans k whole words
-          const uint64_t wb = (uint64_t(sj) * S + base) * k / 32;
+          // k-bit values in element order, value bit 0 first: strip q is k words
+          const uint64_t wb = uint64_t(q) * k;
           const uint32_t maxw = (paybytes + 15) / 16 * 4;
           uint32_t wd[8];
           if (k != 3 && wb + k <= maxw) {
@@ -297,19 +335,23 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             }
           } else {
 #pragma unroll
-            for (int q = 0; q < 8; q++) wd[q] = (q < k && wb + q < maxw) ? ldg4(pay + 4 * (wb + q)) : 0u;
+            for (int x = 0; x < 8; x++) wd[x] = (x < k && wb + x < maxw) ? ldg4(pay + 4 * (wb + x)) : 0u;
           }
           if (k == 8) {
 #pragma unroll
-            for (int q = 0; q < 4; q++)
-              *reinterpret_cast<uint64_t *>(st + 8 * q) = wd[2 * q] | (uint64_t(wd[2 * q + 1]) << 32);
+            for (int x = 0; x < 8; x++) st32[x] = wd[x];
           } else {
 #pragma unroll
-            for (int m = 0; m < RND; m++) {
-              const int bit = m * k;
-              const uint32_t lo = wd[bit >> 5] >> (bit & 31);
-              const uint32_t hi = (bit & 31) + k > 32 ? wd[(bit >> 5) + 1] << (32 - (bit & 31)) : 0u;
-              st[m] = uint8_t((lo | hi) & ((1u << k) - 1));
+            for (int x = 0; x < RND / 4; x++) {
+              uint32_t wv4 = 0;
+#pragma unroll
+              for (int y = 0; y < 4; y++) {
+                const int bit = (4 * x + y) * k;
+                const uint32_t lo = wd[bit >> 5] >> (bit & 31);
+                const uint32_t hi = (bit & 31) + k > 32 ? wd[(bit >> 5) + 1] << (32 - (bit & 31)) : 0u;
+                wv4 |= ((lo | hi) & ((1u << k) - 1)) << (8 * y);
+              }
+              st32[x] = wv4;
             }
           }
         }
@@ -320,7 +362,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       for (int i = 0; i < NVL; i++) {
         const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
         const int sjv = g * GS + wv * SPW + sl;
-        const uint32_t ev = uint32_t(sjv) * S + base + part * VE;
+        const uint32_t qv = uint32_t(r) * nseg + sjv;
+        const uint32_t ev = qv * RND + part * VE;
         if (sjv >= nseg || ev >= n) continue;
         u32x4 o;
         if constexpr (DT == BF16) {
@@ -334,10 +377,10 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             P[pp] = sh.mode[pp] == CONST ? 0x01010101u * uint32_t(sh.aux[pp])
                                          : lds4(wst + (pp * SPW + sl) * STW + part * 4);
 #pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const uint32_t p0 = (P[0] >> (8 * q)) & 0xFF, p1 = (P[1] >> (8 * q)) & 0xFF;
-            const uint32_t p2 = (P[2] >> (8 * q)) & 0xFF, p3 = (P[3] >> (8 * q)) & 0xFF;
-            o[q] = ((p1 & 0x80) << 24) | (p0 << 23) | ((p1 & 0x7F) << 16) | (p2 << 8) | p3;
+          for (int x = 0; x < 4; x++) {
+            const uint32_t p0 = (P[0] >> (8 * x)) & 0xFF, p1 = (P[1] >> (8 * x)) & 0xFF;
+            const uint32_t p2 = (P[2] >> (8 * x)) & 0xFF, p3 = (P[3] >> (8 * x)) & 0xFF;
+            o[x] = ((p1 & 0x80) << 24) | (p0 << 23) | ((p1 & 0x7F) << 16) | (p2 << 8) | p3;
           }
         } else {
           uint64_t Ev[2], Mv[2];
@@ -349,12 +392,12 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
                                         : lds8(wst + (SPW + sl) * STW + part * 16 + 8 * h);
           }
 #pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const uint32_t e4 = uint32_t(Ev[q >> 1] >> (32 * (q & 1)));
-            const uint32_t m3 = uint32_t(Mv[q >> 1] >> (32 * (q & 1)));
-            const uint32_t sg = uint32_t(rawv[i] >> (4 * q)) & 15;
+          for (int x = 0; x < 4; x++) {
+            const uint32_t e4 = uint32_t(Ev[x >> 1] >> (32 * (x & 1)));
+            const uint32_t m3 = uint32_t(Mv[x >> 1] >> (32 * (x & 1)));
+            const uint32_t sg = uint32_t(rawv[i] >> (4 * x)) & 15;
             const uint32_t sb = ((sg & 1) << 7) | ((sg & 2) << 14) | ((sg & 4) << 21) | ((sg & 8) << 28);
-            o[q] = (e4 << 3) | m3 | sb;
+            o[x] = (e4 << 3) | m3 | sb;
           }
         }
         uint8_t *op = dst + uint64_t(ev) * ES;
@@ -367,7 +410,6 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       }
       wave_lds_sync();
     }
-#undef ZN_REFILL
   }
   // the stream's segment lengths must add up to its payload
   if (coded && ln % SPW == 0 && wv == 0 && paybytes != 4 * ((seg_carry + 31) / 32)) bad = 1;

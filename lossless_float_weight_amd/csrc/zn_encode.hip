@@ -362,9 +362,24 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
     const bool with_segs = mode != RAW;
     uint64_t tbit = 0;     // stream bits before this tile
     uint32_t carry = 0;    // partial last word of the previous tile
-    const uint32_t tile_syms = 8u * S;
-    for (uint32_t tb = 0; tb < n; tb += tile_syms) {
-      const uint32_t eb = tb + uint32_t(tid) * EPT;
+    // Huffman-coded streams: wave w of tile T packs segment j = 8T + w, whose
+    // symbols are the 32-symbol strips j, j + nseg, ... of the chunk; lane l
+    // takes symbols [l*EPT, l*EPT + EPT) of the segment, which lie in one
+    // strip.  Raw streams are packed in element order.
+    const int ntiles = (nseg + 7) / 8;
+    for (int T = 0; T < ntiles; T++) {
+      const uint32_t tb = uint32_t(T) * 8u * S;
+      const int jseg = T * 8 + wv;
+      uint32_t eb;
+      bool has = true;
+      if (with_segs) {
+        const uint32_t si = uint32_t(ln) * EPT;
+        eb = 32u * ((si / 32) * uint32_t(nseg) + uint32_t(jseg)) + si % 32;
+        has = jseg < nseg;
+      } else {
+        eb = tb + uint32_t(tid) * EPT;
+      }
+      if (!has) eb = n;  // no symbols in this lane
       uint32_t w[EPT];
       if (aligned && eb + EPT <= n) {
         const uint8_t *vp = src + uint64_t(eb) * ES;
@@ -399,10 +414,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
         woff += q < wv ? x : 0;
         ttot += x;
       }
-      if (with_segs && ln == 0) {
-        const uint32_t seg = tb / S + wv;
-        if (int(seg) < nseg) segt[seg] = uint16_t(sh.u.pk.wtot[wv]);
-      }
+      if (with_segs && ln == 0 && jseg < nseg) stg2(segt + jseg, sh.u.pk.wtot[wv]);
       if (tid == 0 && carry) atomicOr(&sh.u.pk.stage[0], carry);
       const uint32_t start = uint32_t(tbit & 31) + woff + incl - uint32_t(nb);
       uint32_t wi = start >> 5;

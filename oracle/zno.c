@@ -33,9 +33,12 @@
  *                  S = b>>7 (always-raw bit plane).
  *    Every bit pattern is data: NaN, Inf, subnormals and -0 are not special.
  * R2 Chunks: a chunk holds chunk_bytes of uncompressed input of ONE tensor;
- *    the last chunk of a tensor may be short.  Coded streams are cut into
- *    segments of S symbols (BF16 512, FP32 1024, FP8 2048); the last segment
- *    of a short chunk may be short.
+ *    the last chunk of a tensor may be short.  A coded stream of n symbols
+ *    has nseg = ceil(n / S) segments (S = 512 for BF16, 1024 for FP32, 2048
+ *    for FP8).  The stream is cut into strips of W = 32 consecutive symbols
+ *    (the last strip may be short); segment j holds strips j, j + nseg,
+ *    j + 2*nseg, ... in that order.  A full chunk gives every segment S/W
+ *    strips.
  * R3 Code: optimal prefix code with lengths <= L = 11 (package-merge),
  *    leaves ordered by (count, symbol), leaves before packages at equal
  *    weight, packages in creation order.  Canonical code assignment.
@@ -84,6 +87,7 @@
 #define TS_MAGIC 0x53544E5Au
 #define VERSION 1
 #define ROUNDS 8
+#define STRIP 32
 
 /* ------------------------------------------------------------------ */
 /* geometry of each dtype                                              */
@@ -438,7 +442,7 @@ static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8
 }
 
 /* Writes one stream section at out (zeroed); returns its size. */
-static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k, int S,
+static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k,
                              const stream_plan *pl) {
   int A = 1 << k;
   uint64_t head = head_bytes_of(pl->mode, k, pl->nseg);
@@ -458,8 +462,9 @@ static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k
     zno_canonical_codes(pl->len, A, MAXLEN, code);
     for (int j = 0; j < pl->nseg; j++) {
       uint64_t b0 = bw.pos;
-      for (uint64_t i = (uint64_t)j * S; i < n && i < (uint64_t)(j + 1) * S; i++)
-        put_code(&bw, code[sym[i]], pl->len[sym[i]]);
+      for (uint64_t q0 = (uint64_t)j * STRIP; q0 < n; q0 += (uint64_t)pl->nseg * STRIP)
+        for (uint64_t i = q0; i < n && i < q0 + STRIP; i++)
+          put_code(&bw, code[sym[i]], pl->len[sym[i]]);
       put_u16(q + 2 * j, (uint32_t)(bw.pos - b0));
     }
   } else if (pl->mode == ZNO_RAW) {
@@ -500,7 +505,7 @@ static int encode_record(int dt, const uint8_t *chunk, uint64_t n, const uint8_t
   memset(rec, 0, (size_t)total);
   uint64_t off = 0;
   for (int p = 0; p < nc; p++) {
-    uint64_t sz = write_stream(rec + off, sym + (uint64_t)p * n, n, kbits(dt, p), S, &pl[p]);
+    uint64_t sz = write_stream(rec + off, sym + (uint64_t)p * n, n, kbits(dt, p), &pl[p]);
     if (st) {
       st->mode_count[p][pl[p].mode]++;
       st->stream_bytes[p] += sz;
@@ -1034,7 +1039,8 @@ static int64_t decode_stream(const uint8_t *sec, const uint8_t *lim, uint64_t n,
   for (int j = 0; j < nseg; j++) {
     uint64_t sb = get_u16(q + 2 * j);
     bitr br = {payload, seg_start, seg_start + sb};
-    for (uint64_t i = (uint64_t)j * S; i < n && i < (uint64_t)(j + 1) * S; i++) {
+    for (uint64_t i = (uint64_t)j * STRIP; i < n;
+         i = ((i + 1) % STRIP) ? i + 1 : i + 1 + (uint64_t)(nseg - 1) * STRIP) {
       int c = 0, found = -1;
       for (int l = 1; l <= MAXLEN; l++) {
         unsigned bit;

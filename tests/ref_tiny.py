@@ -183,6 +183,19 @@ def a16(x):
     return (x + 15) & ~15
 
 
+STRIP = 32
+
+
+def segment_order(n, nseg, j):
+    """Symbol indices of segment j: strips j, j + nseg, ... of 32 symbols."""
+    out = []
+    q = j
+    while q * STRIP < n:
+        out.extend(range(q * STRIP, min(n, q * STRIP + STRIP)))
+        q += nseg
+    return out
+
+
 def section(mode, k, n, nseg, bits):
     head = 8 + ((1 << k) // 2 if mode == HUFF else 0) + (2 * nseg if mode in (HUFF, GROUP) else 0)
     pay = 4 * ((bits + 31) // 32) if mode in (HUFF, GROUP) else ((n * k + 7) // 8 if mode == RAW else 0)
@@ -233,8 +246,8 @@ def encode_stream(syms, k, S, group=None):
         codes = canonical(lens)
         for j in range(nseg):
             b0 = bw.n
-            for s in syms[j * S:(j + 1) * S]:
-                bw.code(codes[s], lens[s])
+            for i in segment_order(n, nseg, j):
+                bw.code(codes[syms[i]], lens[syms[i]])
             struct.pack_into("<H", out, pos + 2 * j, bw.n - b0)
     elif mode == RAW:
         for s in syms:
@@ -338,16 +351,17 @@ def decode_container(blob, group_lengths_table=None):
                     table = {(lens[s], codes[s]): s for s in range(A) if lens[s]}
                     v = int.from_bytes(blob[pos + head:pos + head + pay], "little")
                     bitpos = 0
+                    syms = [None] * m
                     for j in range(nseg):
                         end = bitpos + seg_bits[j]
-                        for _ in range(min(S, m - j * S)):
+                        for i in segment_order(m, nseg, j):
                             code, l = 0, 0
                             while True:
                                 code = (code << 1) | ((v >> bitpos) & 1)
                                 bitpos += 1
                                 l += 1
                                 if (l, code) in table:
-                                    syms.append(table[(l, code)])
+                                    syms[i] = table[(l, code)]
                                     break
                                 assert l < MAX_LEN
                         assert bitpos == end
