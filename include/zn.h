@@ -94,7 +94,11 @@ zn_status zn_tableset_info(const zn_tableset *ts, zn_dtype *dtype, int *n_tensor
 /* Worst-case container size for the plan's tensors (host-only arithmetic). */
 zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes);
 
-/* Device scratch needed by zn_compress / zn_decompress for this plan. */
+/* Device scratch needed by zn_compress / zn_decompress for this plan: 256
+ * control bytes, 8 bytes per chunk, and one worst-case record slot per chunk
+ * (records are built in their slots, then copied to their final offsets), so
+ * roughly the uncompressed size of the coded fields.  Decompression alone
+ * needs only the first 256 bytes. */
 zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes);
 
 /* zn_compress -- one container holding every tensor of the plan.

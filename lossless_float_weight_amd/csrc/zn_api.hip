@@ -366,9 +366,23 @@ zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes) {
   return ZN_OK;
 }
 
+namespace {
+// A full chunk's record never exceeds its all-raw size (every coded stream
+// takes the smallest of constant, code and raw), so this bounds every record.
+uint64_t slot_bytes(const zn_tableset *ts) {
+  uint64_t b = 0;
+  const uint64_t n = ts->chunk_elems;
+  const int nseg = int((n + segsyms(ts->dtype) - 1) / segsyms(ts->dtype));
+  for (int p = 0; p < ncoded(ts->dtype); p++) b += section_bytes(RAW, kbits(ts->dtype, p), n, nseg, 0);
+  return b;
+}
+uint64_t sizes_offset() { return kCtlBytes; }
+uint64_t slots_offset(const zn_tableset *ts) { return kCtlBytes + (8ull * ts->n_chunks + 255) / 256 * 256; }
+}  // namespace
+
 zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes) {
   if (!ts || !bytes) return ZN_ERR_ARG;
-  *bytes = kCtlBytes + 8ull * (ts->n_chunks + 1);
+  *bytes = slots_offset(ts) + uint64_t(ts->n_chunks) * slot_bytes(ts);
   return ZN_OK;
 }
 
@@ -382,8 +396,9 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   zn_scratch_bytes(ts, &need);
   if (scratch_bytes < need) return ZN_ERR_CAPACITY;
   if (out_cap < ts->off_records + 16) return ZN_ERR_CAPACITY;
-  uint32_t *ctl = static_cast<uint32_t *>(d_scratch);
-  HIPCHK(launch_zero(ctl, need / 4, stream));
+  uint8_t *scr = static_cast<uint8_t *>(d_scratch);
+  uint32_t *ctl = reinterpret_cast<uint32_t *>(scr);
+  HIPCHK(launch_zero(ctl, kCtlBytes / 4, stream));
   EncArgs a;
   a.L = dev_layout(ts);
   a.in_ptrs = reinterpret_cast<const uint8_t *const *>(d_in_ptrs);
@@ -391,9 +406,9 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   a.group_enc = ts->d_enc;
   a.group_len = ts->d_len;
   a.out = static_cast<uint8_t *>(d_out);
-  a.cap = out_cap;
-  a.status = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(d_scratch) + kCtlBytes);
-  a.ctl = ctl;
+  a.slots = scr + slots_offset(ts);
+  a.slot_bytes = slot_bytes(ts);
+  a.sizes = reinterpret_cast<unsigned long long *>(scr + sizes_offset());
   HIPCHK(launch_encode(ts->dtype, a, stream));
   FinishArgs f;
   f.L = a.L;
@@ -402,9 +417,17 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   f.hdr_bytes = uint32_t(ts->hdr.size());
   f.out = a.out;
   f.cap = out_cap;
-  f.status = a.status;
+  f.sizes = a.sizes;
   f.ctl = ctl;
   HIPCHK(launch_finish(f, stream));
+  PlaceArgs pl;
+  pl.n_chunks = ts->n_chunks;
+  pl.off_dir = ts->off_dir;
+  pl.slots = a.slots;
+  pl.slot_bytes = a.slot_bytes;
+  pl.out = a.out;
+  pl.ctl = ctl;
+  HIPCHK(launch_place(pl, stream));
   if (!out_bytes) return ZN_OK;
   uint32_t flag = 0;
   uint64_t total = 0;

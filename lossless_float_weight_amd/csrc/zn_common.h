@@ -112,15 +112,19 @@ __device__ inline uint64_t lanemask_lt() {
   const int ln = threadIdx.x & 63;
   return ln ? (~0ull >> (64 - ln)) : 0ull;
 }
-// inclusive prefix sum over the 64 lanes of a wave
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row_bcast:15 adds
+// row 0's (row 2's) total to row 1 (row 3), and row_bcast:31 adds lane 31's
+// running total to rows 2 and 3.  Lanes without a source receive 0.
 __device__ inline uint32_t wave_incl_scan(uint32_t v) {
-  const int ln = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, 64);
-    if (ln >= o) v += t;
-  }
-  return v;
+  int x = int(v);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return uint32_t(x);
 }
 
 // ------------------------------------------------------- package-merge ----

@@ -11,21 +11,18 @@
 //      raw, by exact section size; the own code is built in LDS by
 //      package-merge (THEORY-599, order-0 only; "NeuralZip: Reusable Setup
 //      for Fast Lossless Compression", Abstract, for group codes);
-//   3. the record size is known from the histogram alone, so the record's
-//      offset comes from a decoupled look-back over the chunks that took
-//      earlier tickets (chunks run in ticket order, so every predecessor is
-//      resident or done);
-//   4. re-read the chunk (it is still in L2 / Infinity Cache) and pack codes:
-//      one wave per segment, a wave scan of bit counts, code words ORed into
-//      an LDS tile, whole 32-bit words stored coalesced.
+//   3. re-read the chunk (it is still in L2) and pack codes into the chunk's
+//      own record slot in scratch: one wave per segment, a wave scan of bit
+//      counts, code words ORed into an LDS tile, whole words stored
+//      coalesced.  The record size is published for the placement pass.
+// Then one workgroup scans the record sizes into the directory (k_finish) and
+// every record is copied from its slot to its place (k_place).  Chunks never
+// wait for each other: a record's offset is only needed by the copy.
 #include "zn_internal.h"
 
 namespace zn {
 
 constexpr int ENC_NT = 512;
-constexpr unsigned long long FLAG_AGG = 1ull << 62, FLAG_INC = 2ull << 62;
-constexpr unsigned long long VALUE_MASK = (1ull << 62) - 1;
-constexpr int SPIN_LIMIT = 1 << 24;
 
 template <int DT, int P>
 __device__ __forceinline__ uint32_t field(uint32_t w) {
@@ -93,8 +90,6 @@ struct EncShared {
   int mode[NC], aux[NC];
   unsigned long long rsum[8];
   int icnt[8];
-  uint32_t chunk;
-  unsigned long long excl;
   int cnt[4][kMaxLen + 1];
   union {
     uint32_t priv[APRIV * COLS];
@@ -149,11 +144,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
   __shared__ EncShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
 
-  // ---------------------------------------------------------------- ticket
-  if (tid == 0) sh.chunk = atomicAdd(&a.ctl[1], 1u);
-  __syncthreads();
-  const uint32_t c = sh.chunk;
-  if (c >= a.L.n_chunks) return;
+  const uint32_t c = blockIdx.x;
   const int t = find_tensor(a.L, c);
   const uint64_t e0 = uint64_t(c - a.L.t_chunk0[t]) * a.L.chunk_elems;
   const uint64_t rem = a.L.t_n[t] - e0;
@@ -291,56 +282,16 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
     __syncthreads();
   }
 
-  // ------------------------------------------------ 3. decoupled look-back
-  if (wv == 0) {
-    unsigned long long excl = 0;
-    if (ln == 0)
-      __hip_atomic_store(&a.status[c], (c == 0 ? FLAG_INC : FLAG_AGG) | rec, __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    if (c > 0) {
-      long long top = (long long)c - 1;
-      int spins = 0;
-      while (true) {
-        const long long idx = top - ln;
-        unsigned long long st = FLAG_INC;
-        if (idx >= 0)
-          st = __hip_atomic_load(&a.status[idx], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long fl = st >> 62;
-        const unsigned long long inc = __ballot(fl == 2), zero = __ballot(fl == 0);
-        const int first = inc ? __ffsll((long long)inc) - 1 : 63;
-        const unsigned long long need = first == 63 ? ~0ull : ((2ull << first) - 1);
-        if (zero & need) {
-          if (++spins > SPIN_LIMIT) {
-            if (ln == 0) atomicOr(&a.ctl[0], kErrSpin);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        excl += wave_sum_u64(ln <= first ? (st & VALUE_MASK) : 0ull);
-        if (inc) break;
-        top -= 64;
-      }
-    }
-    if (ln == 0) {
-      __hip_atomic_store(&a.status[c], FLAG_INC | (excl + rec), __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      sh.excl = excl;
-    }
-  }
-  __syncthreads();
-  const uint64_t roff = a.L.off_records + sh.excl;
-  if (tid == 0) *reinterpret_cast<uint64_t *>(a.out + a.L.off_dir + 8ull * c) = roff;
-  if (roff + rec + 16 > a.cap) {
-    if (tid == 0) atomicOr(&a.ctl[0], kErrCapacity);
-    return;
-  }
+  // the record goes to this chunk's slot; its size to the placement pass
+  if (tid == 0) a.sizes[c] = rec;
+  const uint64_t roff = 0;
+  uint8_t *const recp = a.slots + uint64_t(c) * a.slot_bytes;
 
   // -------------------------------------------------------- 4. the record
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k, mode = sh.mode[p];
     const uint64_t bits = sh.bits[p];
-    uint8_t *sec = a.out + roff + sh.sec_off[p];
+    uint8_t *sec = recp + roff + sh.sec_off[p];
     const uint64_t head = head_bytes_of(mode, k, nseg);
     const uint64_t pay = payload_bytes_of(mode, k, n, bits);
     // stream header, code lengths and the zero pad of the head
@@ -367,28 +318,31 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
     // takes symbols [l*EPT, l*EPT + EPT) of the segment, which lie in one
     // strip.  Raw streams are packed in element order.
     const int ntiles = (nseg + 7) / 8;
-    for (int T = 0; T < ntiles; T++) {
-      const uint32_t tb = uint32_t(T) * 8u * S;
-      const int jseg = T * 8 + wv;
-      uint32_t eb;
-      bool has = true;
+    auto tile_eb = [&](int T) -> uint32_t {  // first element of this lane's run in tile T
       if (with_segs) {
+        const int jseg = T * 8 + wv;
+        if (jseg >= nseg) return n;  // no symbols in this lane
         const uint32_t si = uint32_t(ln) * EPT;
-        eb = 32u * ((si / 32) * uint32_t(nseg) + uint32_t(jseg)) + si % 32;
-        has = jseg < nseg;
-      } else {
-        eb = tb + uint32_t(tid) * EPT;
+        return 32u * ((si / 32) * uint32_t(nseg) + uint32_t(jseg)) + si % 32;
       }
-      if (!has) eb = n;  // no symbols in this lane
-      uint32_t w[EPT];
-      if (aligned && eb + EPT <= n) {
-        const uint8_t *vp = src + uint64_t(eb) * ES;
-        u32x4 qs[NV];
+      return uint32_t(T) * 8u * S + uint32_t(tid) * EPT;
+    };
+    // the next tile's 16-byte vectors are loaded one tile ahead
+    u32x4 nq[NV];
+    uint32_t neb = tile_eb(0);
+    if (aligned && neb + EPT <= n) {
 #pragma unroll
-        for (int j = 0; j < NV; j++) qs[j] = ldg16(vp + 16 * j);
+      for (int j = 0; j < NV; j++) nq[j] = ldg16(src + uint64_t(neb) * ES + 16 * j);
+    }
+    for (int T = 0; T < ntiles; T++) {
+      const int jseg = T * 8 + wv;
+      const uint32_t eb = neb;
+      const bool vec = aligned && eb + EPT <= n;
+      uint32_t w[EPT];
+      if (vec) {
 #pragma unroll
         for (int j = 0; j < NV; j++) {
-          const uint4 q = make_uint4(qs[j][0], qs[j][1], qs[j][2], qs[j][3]);
+          const uint4 q = make_uint4(nq[j][0], nq[j][1], nq[j][2], nq[j][3]);
 #pragma unroll
           for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
         }
@@ -397,12 +351,43 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
         for (int i = 0; i < EPT; i++)
           w[i] = eb + i < n ? load_elem<DT>(src + uint64_t(eb + i) * ES) : 0;
       }
-      uint32_t code[EPT];
+      // Concatenate the thread's codes 8 at a time without branches: pairs
+      // fit 22 bits, quads 44 bits (one u64), two quads 88 bits (lo | hi<<64).
+      constexpr int NG = EPT / 8;
+      uint64_t glo[NG];
+      uint32_t ghi[NG];
+      int gb[NG];
       int nb = 0;
 #pragma unroll
-      for (int i = 0; i < EPT; i++) {
-        code[i] = eb + i < n ? sh.enc[p][field_rt<DT>(w[i], p)] : 0;
-        nb += int(code[i] >> 16);
+      for (int g8 = 0; g8 < NG; g8++) {
+        uint32_t v[8], l[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int e = g8 * 8 + i;
+          const uint32_t c = eb + e < n ? sh.enc[p][field_rt<DT>(w[e], p)] : 0u;
+          v[i] = c & 0xFFFF;
+          l[i] = c >> 16;
+        }
+        const uint32_t c01 = v[0] | (v[1] << l[0]), l01 = l[0] + l[1];
+        const uint32_t c23 = v[2] | (v[3] << l[2]), l23 = l[2] + l[3];
+        const uint32_t c45 = v[4] | (v[5] << l[4]), l45 = l[4] + l[5];
+        const uint32_t c67 = v[6] | (v[7] << l[6]), l67 = l[6] + l[7];
+        const uint64_t q0 = uint64_t(c01) | (uint64_t(c23) << l01);
+        const uint64_t q1 = uint64_t(c45) | (uint64_t(c67) << l45);
+        const uint32_t L0 = l01 + l23, L1 = l45 + l67;
+        glo[g8] = q0 | (q1 << L0);
+        ghi[g8] = L0 ? uint32_t(q1 >> (64 - L0)) : 0u;
+        gb[g8] = int(L0 + L1);
+        nb += gb[g8];
+      }
+      // issued once this tile's codes are computed, so no later wait for this
+      // tile's data also waits for the next tile's loads
+      if (T + 1 < ntiles) {
+        neb = tile_eb(T + 1);
+        if (aligned && neb + EPT <= n) {
+#pragma unroll
+          for (int j = 0; j < NV; j++) nq[j] = ldg16(src + uint64_t(neb) * ES + 16 * j);
+        }
       }
       const uint32_t incl = wave_incl_scan(uint32_t(nb));
       if (ln == 63) sh.u.pk.wtot[wv] = incl;
@@ -416,23 +401,22 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
       }
       if (with_segs && ln == 0 && jseg < nseg) stg2(segt + jseg, sh.u.pk.wtot[wv]);
       if (tid == 0 && carry) atomicOr(&sh.u.pk.stage[0], carry);
-      const uint32_t start = uint32_t(tbit & 31) + woff + incl - uint32_t(nb);
-      uint32_t wi = start >> 5;
-      int ab = int(start & 31);
-      unsigned long long acc = 0;
+      uint32_t start = uint32_t(tbit & 31) + woff + incl - uint32_t(nb);
 #pragma unroll
-      for (int i = 0; i < EPT; i++) {
-        const int l = int(code[i] >> 16);
-        acc |= (unsigned long long)(code[i] & 0xFFFF) << ab;
-        ab += l;
-        if (ab >= 32) {
-          atomicOr(&sh.u.pk.stage[wi], uint32_t(acc));
-          wi++;
-          acc >>= 32;
-          ab -= 32;
+      for (int g8 = 0; g8 < NG; g8++) {
+        // the 88-bit group shifted to its bit offset covers at most 4 words
+        const uint32_t sft = start & 31, wi = start >> 5;
+        const uint64_t t0 = glo[g8] << sft;
+        const uint64_t t1 = (uint64_t(ghi[g8]) << sft) | (sft ? glo[g8] >> (64 - sft) : 0ull);
+        if (gb[g8]) {
+          atomicOr(&sh.u.pk.stage[wi], uint32_t(t0));
+          const uint32_t x1 = uint32_t(t0 >> 32), x2 = uint32_t(t1), x3 = uint32_t(t1 >> 32);
+          if (x1) atomicOr(&sh.u.pk.stage[wi + 1], x1);
+          if (x2) atomicOr(&sh.u.pk.stage[wi + 2], x2);
+          if (x3) atomicOr(&sh.u.pk.stage[wi + 3], x3);
         }
+        start += uint32_t(gb[g8]);
       }
-      if (ab > 0 && acc) atomicOr(&sh.u.pk.stage[wi], uint32_t(acc));
       __syncthreads();
       const uint32_t endb = uint32_t(tbit & 31) + ttot;
       const uint32_t nfull = endb >> 5;
@@ -450,32 +434,68 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
   }
 }
 
-__global__ void k_finish(FinishArgs a) {
+// One workgroup: exclusive scan of the record sizes into the directory, then
+// the header, the alignment gaps and the 16-byte zero tail.
+__global__ __launch_bounds__(1024) void k_finish(FinishArgs a) {
+  __shared__ unsigned long long wsum[16];
   const int tid = threadIdx.x;
+  const uint32_t M = a.L.n_chunks;
+  const uint32_t per = (M + 1023) / 1024;
+  const uint32_t c0 = tid * per, c1 = c0 + per < M ? c0 + per : M;
+  unsigned long long s = 0;
+  for (uint32_t c = c0; c < c1; c++) s += a.sizes[c];
+  // block exclusive scan of the per-thread sums
+  unsigned long long incl = s;
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long t = __shfl_up(incl, o, 64);
+    if ((tid & 63) >= o) incl += t;
+  }
+  if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+  __syncthreads();
+  unsigned long long before = 0, total = 0;
+  for (int w = 0; w < 16; w++) {
+    before += w < (tid >> 6) ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  unsigned long long off = a.L.off_records + before + incl - s;
+  uint64_t *dir = reinterpret_cast<uint64_t *>(a.out + a.L.off_dir);
+  const uint64_t end = a.L.off_records + total;
+  const bool fits = end + 16 <= a.cap;
+  for (uint32_t c = c0; c < c1; c++) {
+    stg8(dir + c, u32x2{uint32_t(off), uint32_t(off >> 32)});
+    off += a.sizes[c];
+  }
   for (uint32_t i = tid; i < a.hdr_bytes; i += blockDim.x)
-    if (i < 56 || i >= 64) a.out[i] = a.hdr[i];
-  uint64_t end = a.L.off_records;
-  if (a.L.n_chunks)
-    end += a.status[a.L.n_chunks - 1] & VALUE_MASK;
-  // zero the alignment gaps around the directory and raw planes
-  const uint64_t dir_end = a.L.off_dir + 8ull * (a.L.n_chunks + 1);
+    if (i < 56 || i >= 64) stg1(a.out + i, a.hdr[i]);
+  const uint64_t dir_end = a.L.off_dir + 8ull * (M + 1);
   const uint64_t raw0 = a.L.T ? a.L.t_raw[0] : a.L.off_records;
-  for (uint64_t i = dir_end + tid; i < raw0; i += blockDim.x) a.out[i] = 0;
+  for (uint64_t i = dir_end + tid; i < raw0; i += blockDim.x) stg1(a.out + i, 0);
   for (int t = tid; t < a.L.T; t += blockDim.x) {
     const uint64_t b = a.L.t_raw[t] + rawplane_bytes(a.dtype, a.L.t_n[t]);
     const uint64_t e = t + 1 < a.L.T ? a.L.t_raw[t + 1] : a.L.off_records;
-    for (uint64_t i = b; i < e; i++) a.out[i] = 0;
+    for (uint64_t i = b; i < e; i++) stg1(a.out + i, 0);
   }
   if (tid == 0) {
-    if (end + 16 > a.cap || (a.ctl[0] & (kErrCapacity | kErrSpin))) {
+    if (!fits) {
       atomicOr(&a.ctl[0], kErrCapacity);
     } else {
-      *reinterpret_cast<uint64_t *>(a.out + a.L.off_dir + 8ull * a.L.n_chunks) = end;
-      *reinterpret_cast<uint64_t *>(a.out + 56) = end + 16;
+      stg8(dir + M, u32x2{uint32_t(end), uint32_t(end >> 32)});
+      const uint64_t tot = end + 16;
+      stg8(a.out + 56, u32x2{uint32_t(tot), uint32_t(tot >> 32)});
     }
   }
-  if (end + 16 <= a.cap)
-    for (int i = tid; i < 16; i += blockDim.x) a.out[end + i] = 0;
+  if (fits && tid < 4) stg4(a.out + end + 4 * tid, 0);
+}
+
+// One workgroup per record: copy it from its slot to the directory offset.
+__global__ __launch_bounds__(256) void k_place(PlaceArgs a) {
+  if (a.ctl[0]) return;  // the container did not fit
+  const uint32_t c = blockIdx.x;
+  const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.off_dir);
+  const uint64_t d0 = dir[c], n16 = (dir[c + 1] - d0) / 16;
+  const uint8_t *src = a.slots + uint64_t(c) * a.slot_bytes;
+  uint8_t *dst = a.out + d0;
+  for (uint64_t i = threadIdx.x; i < n16; i += 256) stg16(dst + 16 * i, ldg16(src + 16 * i));
 }
 
 __global__ void k_zero(uint32_t *p, uint64_t words) {
@@ -494,7 +514,13 @@ hipError_t launch_encode(int dtype, const EncArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_finish, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_place(const PlaceArgs &a, hipStream_t s) {
+  if (a.n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_place, dim3(a.n_chunks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -14,12 +14,14 @@ struct EncArgs {
   const uint8_t *group_map;        // [n_chunks] or nullptr
   const uint32_t *group_enc;       // [K][256] bit-reversed code | len << 16
   const uint8_t *group_len;        // [K][256]
-  uint8_t *out;
-  uint64_t cap;
-  unsigned long long *status;      // [n_chunks] look-back words
-  uint32_t *ctl;                   // [0] error bits, [1] ticket counter
+  uint8_t *out;                    // container (the raw planes are written here)
+  uint8_t *slots;                  // [n_chunks][slot_bytes] records before placement
+  uint64_t slot_bytes;
+  unsigned long long *sizes;       // [n_chunks] record bytes
 };
 
+// Offsets of the records (exclusive scan of their sizes), the directory, the
+// header and the alignment gaps; one workgroup.
 struct FinishArgs {
   DevLayout L;
   int dtype;
@@ -27,8 +29,18 @@ struct FinishArgs {
   uint32_t hdr_bytes;
   uint8_t *out;
   uint64_t cap;
-  const unsigned long long *status;
-  uint32_t *ctl;
+  const unsigned long long *sizes;
+  uint32_t *ctl;                   // [0] error bits
+};
+
+// Copies every record from its slot to its place in the container.
+struct PlaceArgs {
+  uint32_t n_chunks;
+  uint64_t off_dir;
+  const uint8_t *slots;
+  uint64_t slot_bytes;
+  uint8_t *out;
+  const uint32_t *ctl;
 };
 
 struct DecArgs {
@@ -55,12 +67,13 @@ struct CheckArgs {
 };
 
 // Error bits in ctl[0].
-constexpr uint32_t kErrCapacity = 1, kErrCorrupt = 2, kErrTableset = 4, kErrSpin = 8;
-// Scratch words: ctl[0..63] control, then the look-back status array.
+constexpr uint32_t kErrCapacity = 1, kErrCorrupt = 2, kErrTableset = 4;
+// Compress scratch: ctl[0..63] control, record sizes, then one slot per chunk.
 constexpr uint64_t kCtlBytes = 256;
 
 hipError_t launch_encode(int dtype, const EncArgs &a, hipStream_t s);
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
+hipError_t launch_place(const PlaceArgs &a, hipStream_t s);
 hipError_t launch_zero(uint32_t *p, uint64_t words, hipStream_t s);
 hipError_t launch_check(const CheckArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s);
