@@ -132,14 +132,16 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v) {
 struct PMShared {
   uint64_t w[2][512];               // item weights of the previous/current list
   uint64_t leaf_w[256];             // leaves sorted by (count, symbol)
-  uint64_t tmp_w[256];              // present symbols in symbol order
-  uint16_t leafpos[kMaxLen][256];   // position of sorted leaf i in list j
+  uint8_t leafcl[kMaxLen][256];     // packages ahead of sorted leaf i in list j
   uint8_t leaf_sym[256];
   uint8_t tmp_sym[256];
   int c[kMaxLen];                   // leaves among the selected prefix of list j
   int d;
   int wave_cnt[4];
 };
+// present symbols in symbol order, before sorting (shares w[1], which is
+// written only from the first merge on)
+#define PM_TMP_W(S) ((S).w[1])
 
 // Optimal code lengths (<= 11) of the weights hw[0..A) by package-merge, for
 // a workgroup of NT >= 256 threads.  List 0 holds the leaves (coins of the
@@ -166,7 +168,7 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
     for (int q = 0; q < wv; q++) base += S.wave_cnt[q];
     const int idx = base + __popcll(m & lanemask_lt());
     S.tmp_sym[idx] = uint8_t(tid);
-    S.tmp_w[idx] = hw[tid];
+    PM_TMP_W(S)[idx] = hw[tid];
   }
   if (tid == 0) S.d = S.wave_cnt[0] + S.wave_cnt[1] + S.wave_cnt[2] + S.wave_cnt[3];
   __syncthreads();
@@ -174,7 +176,7 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
   if (group_rule && d == 1) {
     if (tid == 0) {
       S.tmp_sym[1] = S.tmp_sym[0] == 0 ? 1 : 0;
-      S.tmp_w[1] = 0;
+      PM_TMP_W(S)[1] = 0;
       S.d = 2;
     }
     __syncthreads();
@@ -183,17 +185,17 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
   if (d < 2) return d;
   // rank sort of the leaves by (weight, symbol)
   if (tid < d) {
-    const uint64_t w = S.tmp_w[tid];
+    const uint64_t w = PM_TMP_W(S)[tid];
     const int s = S.tmp_sym[tid];
     int r = 0;
     for (int j = 0; j < d; j++) {
-      const uint64_t wj = S.tmp_w[j];
+      const uint64_t wj = PM_TMP_W(S)[j];
       r += (wj < w) || (wj == w && S.tmp_sym[j] < s);
     }
     S.leaf_w[r] = w;
     S.leaf_sym[r] = uint8_t(s);
     S.w[0][r] = w;
-    S.leafpos[0][r] = uint16_t(r);
+    S.leafcl[0][r] = 0;
   }
   __syncthreads();
   int n_prev = d;
@@ -210,7 +212,7 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
           if (prev[2 * mid] + prev[2 * mid + 1] < wi) lo = mid + 1; else hi = mid;
         }
         cur[q + lo] = wi;
-        S.leafpos[j][q] = uint16_t(q + lo);
+        S.leafcl[j][q] = uint8_t(lo);
       } else {      // package k: after every leaf not heavier than it
         const int k = q - d;
         const uint64_t p = prev[2 * k] + prev[2 * k + 1];
@@ -229,7 +231,7 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
     int msel = 2 * d - 2;
     for (int j = kMaxLen - 1; j >= 0; j--) {
       int cnt = 0;
-      for (int i = tid; i < d; i += 64) cnt += S.leafpos[j][i] < msel;
+      for (int i = tid; i < d; i += 64) cnt += i + S.leafcl[j][i] < msel;
       cnt = wave_sum(cnt);
       if (tid == 0) S.c[j] = cnt;
       msel = 2 * (msel - cnt);
@@ -243,6 +245,163 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
   }
   __syncthreads();
   return d;
+}
+
+// ------------------------------------------- one-wave code construction ----
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), lane));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), lane));
+  return lo | (uint64_t(hi) << 32);
+}
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Orders this wave's LDS writes before its later LDS reads by other lanes:
+// wait for the wave's LDS operations (lgkmcnt 0, vector memory untouched),
+// and keep the compiler from moving memory operations across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Wave-private LDS of the one-wave package-merge.
+struct WaveCB {
+  uint64_t lst[128];   // the current merged list
+  uint64_t srt[64];    // leaves sorted by (count, symbol)
+  uint8_t sym[64], ssym[64];
+};
+
+// The package-merge of pm_lengths (same lists, same tie rule, same result)
+// run by one wave when at most 64 symbols are present: leaf i lives in lane
+// i, list item j in lane j (j < 64) or lane j-64, and the rank of each item
+// in the merged list is counted against the other list's items read one by
+// one from lane registers, so no workgroup barrier is needed.
+// Returns d (after the group rule), or -1 when more than 64 symbols are
+// present (the workgroup version must run).  Every lane of the wave calls it.
+template <class WT>
+__device__ int wave_pm_lengths(const WT *hist, int A, bool group_rule, uint8_t *len, WaveCB &W) {
+  const int ln = threadIdx.x & 63;
+  uint64_t x[4], m[4];
+  int d = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int s = ln + 64 * q;
+    x[q] = s < A ? uint64_t(hist[s]) : 0;
+    m[q] = __ballot(x[q] != 0);
+    d += __popcll(m[q]);
+    if (s < A) len[s] = 0;
+  }
+  if (d > 64) return -1;
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if (x[q]) {
+      const int idx = base + __popcll(m[q] & lanemask_lt());
+      W.srt[idx] = x[q];
+      W.sym[idx] = uint8_t(ln + 64 * q);
+    }
+    base += __popcll(m[q]);
+  }
+  wave_lds_sync();
+  if (group_rule && d == 1) {
+    if (ln == 0) {
+      W.sym[1] = W.sym[0] == 0 ? 1 : 0;
+      W.srt[1] = 0;
+    }
+    wave_lds_sync();
+    d = 2;
+  }
+  if (d < 2) return d;
+  // rank sort of the leaves by (weight, symbol)
+  const uint64_t w = ln < d ? W.srt[ln] : ~0ull;
+  const int sy = ln < d ? W.sym[ln] : 255;
+  int r = 0;
+  for (int j = 0; j < d; j++) {
+    const uint64_t wj = readlane64(w, j);
+    const int sj = __builtin_amdgcn_readlane(sy, j);
+    r += (wj < w) || (wj == w && sj < sy);
+  }
+  wave_lds_sync();
+  if (ln < d) {
+    W.lst[r] = w;
+    W.ssym[r] = uint8_t(sy);
+  }
+  wave_lds_sync();
+  const uint64_t lw = ln < d ? W.lst[ln] : ~0ull;
+  const int lsym = ln < d ? W.ssym[ln] : 0;
+  uint64_t c0 = lw, c1 = 0;
+  int ncur = d;
+  int lp[kMaxLen];
+  lp[0] = ln;
+#pragma unroll
+  for (int j = 1; j < kMaxLen; j++) {
+    const int np = ncur >> 1;
+    const int i0 = 2 * ln, i1 = 2 * ln + 1;
+    const uint64_t a0 = __shfl(c0, i0 & 63, 64), a1 = __shfl(c1, i0 & 63, 64);
+    const uint64_t b0 = __shfl(c0, i1 & 63, 64), b1 = __shfl(c1, i1 & 63, 64);
+    const uint64_t P = (i0 < 64 ? a0 : a1) + (i1 < 64 ? b0 : b1);
+    int cl = 0, cp = 0;
+    for (int k = 0; k < np; k++) cl += readlane64(P, k) < lw;   // packages lighter
+    for (int i = 0; i < d; i++) cp += readlane64(lw, i) <= P;   // leaves not heavier
+    wave_lds_sync();
+    if (ln < d) W.lst[ln + cl] = lw;
+    if (ln < np) W.lst[ln + cp] = P;
+    lp[j] = ln + cl;
+    wave_lds_sync();
+    ncur = d + np;
+    c0 = ln < ncur ? W.lst[ln] : 0;
+    c1 = ln + 64 < ncur ? W.lst[ln + 64] : 0;
+  }
+  int msel = 2 * d - 2, l = 0;
+#pragma unroll
+  for (int j = kMaxLen - 1; j >= 0; j--) {
+    const int cnt = __popcll(__ballot(ln < d && lp[j] < msel));
+    l += ln < cnt;
+    msel = 2 * (msel - cnt);
+  }
+  if (ln < d) len[lsym] = uint8_t(l);
+  wave_lds_sync();
+  return d;
+}
+
+// Canonical codes (RFC 1951 section 3.2.2) by one wave: enc[s] = bit-reversed
+// code | (length << 16), for A <= 256 symbols.
+__device__ inline void wave_canon(const uint8_t *len, int A, uint32_t *enc) {
+  const int ln = threadIdx.x & 63;
+  int l[4], rank[4] = {0, 0, 0, 0};
+  uint32_t bl[kMaxLen + 1];
+  bl[0] = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) l[q] = ln + 64 * q < A ? len[ln + 64 * q] : 0;
+#pragma unroll
+  for (int b = 1; b <= kMaxLen; b++) {
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint64_t mm = __ballot(l[q] == b);
+      if (l[q] == b) rank[q] = base + __popcll(mm & lanemask_lt());
+      base += __popcll(mm);
+    }
+    bl[b] = uint32_t(base);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int s = ln + 64 * q;
+    if (s >= A) continue;
+    uint32_t e = 0;
+    if (l[q]) {
+      uint32_t code = 0;
+#pragma unroll
+      for (int b = 1; b <= kMaxLen; b++)
+        if (b <= l[q]) code = (code + bl[b - 1]) << 1;
+      code += uint32_t(rank[q]);
+      e = (__builtin_bitreverse32(code) >> (32 - l[q])) | (uint32_t(l[q]) << 16);
+    }
+    enc[s] = e;
+  }
+  wave_lds_sync();
 }
 
 // ------------------------------------------------------ canonical codes ----

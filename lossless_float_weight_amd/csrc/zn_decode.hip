@@ -44,14 +44,6 @@ struct DecShared {
   int bad;
 };
 
-// Orders this wave's LDS writes before its later LDS reads by other lanes:
-// wait for the wave's LDS operations (lgkmcnt 0, vector memory untouched),
-// and keep the compiler from moving memory operations across.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_wave_barrier();
-}
-
 __device__ __forceinline__ uint64_t lds8(const uint8_t *p) {  // 4-byte aligned
   const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
   return q[0] | (uint64_t(q[1]) << 32);

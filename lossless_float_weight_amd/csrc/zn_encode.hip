@@ -1,6 +1,6 @@
 // zn_encode.hip -- the compression pass for gfx950.
 //
-// One workgroup of 512 threads (8 wave64s) per chunk, in one launch:
+// One workgroup per chunk (4 wave64s for BF16, 8 otherwise), in one launch:
 //   1. read the chunk once with 16-byte loads, split every element into its
 //      coded fields and its always-raw bits (THEORY-599 on ZipNN, per-field
 //      compressibility, ZipNN Table II), store the raw bits straight to their
@@ -22,7 +22,9 @@
 
 namespace zn {
 
-constexpr int ENC_NT = 512;
+// threads per chunk: BF16 chunks use 256 so that every chunk of a large
+// workload is resident at once (8 workgroups of under 20 KB LDS per CU)
+constexpr int enc_nt(int dt) { return dt == BF16 ? 256 : 512; }
 
 template <int DT, int P>
 __device__ __forceinline__ uint32_t field(uint32_t w) {
@@ -79,28 +81,36 @@ template <int DT>
 struct EncShared {
   static constexpr int NC = ncoded(DT);
   static constexpr int S = segsyms(DT);
+  static constexpr int NT = enc_nt(DT);
+  static constexpr int NW = NT / 64;                              // waves = segments per pack tile
   static constexpr int COLS = DT == FP32 ? 16 : 32;
   static constexpr int APRIV = DT == FP8 ? (16 + 8) : 256 * NC;   // total bins
-  static constexpr int STAGE = (8 * S * kMaxLen + 31) / 32 + 4;   // words of one pack tile
+  // BF16 counts two bins per word (a column sees at most 1/32 of a chunk,
+  // 16384 values at the largest chunk size, so 16 bits cannot overflow)
+  static constexpr bool PACK16 = DT == BF16;
+  static constexpr int PRIVW = PACK16 ? APRIV * COLS / 2 : APRIV * COLS;
+  static constexpr int STAGE = (NW * S * kMaxLen + 31) / 32 + 4;  // words of one pack tile
   uint32_t hist[NC][256];
   uint32_t enc[NC][256];
   uint8_t len[NC][256];
   unsigned long long bits[NC];
   unsigned long long sec_off[NC + 1];
   int mode[NC], aux[NC];
-  unsigned long long rsum[8];
-  int icnt[8];
+  unsigned long long rsum[NW];
+  int icnt[NW];
   int cnt[4][kMaxLen + 1];
+  int need_block;
   union {
-    uint32_t priv[APRIV * COLS];
+    uint32_t priv[PRIVW];
     struct {
       PMShared pm;
       uint64_t hw[256];
     } cb;
     struct {
       uint32_t stage[STAGE];
-      uint32_t wtot[8];
+      uint32_t wtot[NW];
     } pk;
+    WaveCB wcb;
   } u;
 };
 
@@ -119,7 +129,7 @@ __device__ unsigned long long block_sum(EncShared<DT> &sh, unsigned long long v)
   if ((tid & 63) == 0) sh.rsum[tid >> 6] = v;
   __syncthreads();
   unsigned long long t = 0;
-  for (int w = 0; w < ENC_NT / 64; w++) t += sh.rsum[w];
+  for (int w = 0; w < EncShared<DT>::NW; w++) t += sh.rsum[w];
   return t;
 }
 template <int DT>
@@ -130,17 +140,29 @@ __device__ int block_count(EncShared<DT> &sh, bool pred) {
   if ((tid & 63) == 0) sh.icnt[tid >> 6] = c;
   __syncthreads();
   int t = 0;
-  for (int w = 0; w < ENC_NT / 64; w++) t += sh.icnt[w];
+  for (int w = 0; w < EncShared<DT>::NW; w++) t += sh.icnt[w];
   return t;
 }
 
+// one histogram count of field value b of stream p, in column col
 template <int DT>
-__global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
+__device__ __forceinline__ void count(EncShared<DT> &sh, int p, uint32_t b, int col) {
+  constexpr int COLS = EncShared<DT>::COLS;
+  const uint32_t bin = priv_base<DT>(p) + b;
+  if constexpr (EncShared<DT>::PACK16)
+    atomicAdd(&sh.u.priv[(bin >> 1) * COLS + col], 1u << (16 * (bin & 1)));
+  else
+    atomicAdd(&sh.u.priv[bin * COLS + col], 1u);
+}
+
+template <int DT>
+__global__ __launch_bounds__(enc_nt(DT)) void k_encode(EncArgs a) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per pack tile (a wave = a segment)
   constexpr int NV = EPT / VE;         // vectors per thread per pack tile
   constexpr int COLS = EncShared<DT>::COLS;
+  constexpr int ENC_NT = EncShared<DT>::NT, NW = EncShared<DT>::NW;
   __shared__ EncShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
 
@@ -155,7 +177,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
   uint8_t *rawp = a.out + a.L.t_raw[t];
 
   // ------------------------------------------- 1. split, raw planes, counts
-  for (int i = tid; i < EncShared<DT>::APRIV * COLS; i += ENC_NT) sh.u.priv[i] = 0;
+  for (int i = tid; i < EncShared<DT>::PRIVW; i += ENC_NT) sh.u.priv[i] = 0;
   __syncthreads();
   const int col = ln & (COLS - 1);
   constexpr int B1 = 4;  // 16-byte loads in flight per thread
@@ -175,8 +197,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
       for (int i = 0; i < VE; i++) {
         const uint32_t w = vec_elem<DT>(q, i);
 #pragma unroll
-        for (int p = 0; p < NC; p++)
-          atomicAdd(&sh.u.priv[(priv_base<DT>(p) + field_rt<DT>(w, p)) * COLS + col], 1u);
+        for (int p = 0; p < NC; p++) count<DT>(sh, p, field_rt<DT>(w, p), col);
       }
       if constexpr (DT == BF16) {
         uint32_t lo = 0, hi = 0;
@@ -198,8 +219,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
   for (uint32_t i = nvec * VE + tid; i < n; i += ENC_NT) {  // ragged tail or unaligned input
     const uint32_t w = load_elem<DT>(src + uint64_t(i) * ES);
 #pragma unroll
-    for (int p = 0; p < NC; p++)
-      atomicAdd(&sh.u.priv[(priv_base<DT>(p) + field_rt<DT>(w, p)) * COLS + col], 1u);
+    for (int p = 0; p < NC; p++) count<DT>(sh, p, field_rt<DT>(w, p), col);
     if constexpr (DT == BF16) stg1(rawp + e0 + i, ((w >> 8) & 0x80) | (w & 0x7F));
   }
   if constexpr (DT == FP8) {  // sign bits of the tail, whole bytes by one thread
@@ -215,7 +235,13 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
   __syncthreads();
   for (int i = tid; i < EncShared<DT>::APRIV; i += ENC_NT) {
     uint32_t s = 0;
-    for (int j = 0; j < COLS; j++) s += sh.u.priv[i * COLS + ((j + i) & (COLS - 1))];
+    if constexpr (EncShared<DT>::PACK16) {
+      const int sh16 = 16 * (i & 1);
+      for (int j = 0; j < COLS; j++)
+        s += (sh.u.priv[(i >> 1) * COLS + ((j + (i >> 1)) & (COLS - 1))] >> sh16) & 0xFFFF;
+    } else {
+      for (int j = 0; j < COLS; j++) s += sh.u.priv[i * COLS + ((j + i) & (COLS - 1))];
+    }
     int p = 0, sym = i;
     if constexpr (DT == FP8) { p = i >= 16; sym = i - (p ? 16 : 0); }
     else { p = i >> 8; sym = i & 255; }
@@ -228,57 +254,106 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
   unsigned long long rec = 0;
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k;
-    const uint32_t h = tid < A ? sh.hist[p][tid] : 0;
-    const int d = block_count<DT>(sh, h != 0);
-    int mode;
-    unsigned long long bits = 0;
-    if (d == 1) {
-      mode = CONST;
-      if (h) sh.aux[p] = tid;
-    } else {
-      const unsigned long long raw = section_bytes(RAW, k, n, nseg, 0);
-      bool escape = true;
-      mode = RAW;
-      if (p == 0 && a.group_map) {
-        const int g = a.group_map[c];
-        const uint8_t gl = tid < A ? a.group_len[g * 256 + tid] : 0;
-        const int miss = block_count<DT>(sh, h != 0 && gl == 0);
-        if (miss == 0) {
-          escape = false;
-          bits = block_sum<DT>(sh, (unsigned long long)h * gl);
-          if (section_bytes(GROUP, k, n, nseg, bits) < raw) {
-            mode = GROUP;
-            if (tid < A) {
-              sh.len[p][tid] = gl;
-              sh.enc[p][tid] = a.group_enc[g * 256 + tid];
+    const unsigned long long raw = section_bytes(RAW, k, n, nseg, 0);
+    // wave 0 decides the mode and builds the code; the workgroup helps only
+    // when more than 64 symbols are present
+    if (wv == 0) {
+      uint32_t hq[4];
+      uint64_t mq[4];
+      int d = 0;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int s2 = ln + 64 * q;
+        hq[q] = s2 < A ? sh.hist[p][s2] : 0u;
+        mq[q] = __ballot(hq[q] != 0);
+        d += __popcll(mq[q]);
+      }
+      int mode = RAW, aux = 0, need_block = 0;
+      uint64_t bits = 0;
+      if (d == 1) {
+        mode = CONST;
+#pragma unroll
+        for (int q = 3; q >= 0; q--)
+          if (mq[q]) aux = 64 * q + __ffsll((long long)mq[q]) - 1;
+      } else {
+        bool escape = true;
+        if (p == 0 && a.group_map) {
+          const int g = ldg1(a.group_map + c);
+          uint32_t gl[4];
+          bool miss = false;
+          uint64_t part = 0;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int s2 = ln + 64 * q;
+            gl[q] = s2 < A ? ldg1(a.group_len + g * 256 + s2) : 0u;
+            miss |= hq[q] && !gl[q];
+            part += uint64_t(hq[q]) * gl[q];
+          }
+          if (!__ballot(miss)) {
+            escape = false;
+            bits = wave_sum64(part);
+            if (section_bytes(GROUP, k, n, nseg, bits) < raw) {
+              mode = GROUP;
+              aux = g;
+#pragma unroll
+              for (int q = 0; q < 4; q++) {
+                const int s2 = ln + 64 * q;
+                if (s2 < A) {
+                  sh.len[p][s2] = uint8_t(gl[q]);
+                  sh.enc[p][s2] = ldg4(a.group_enc + g * 256 + s2);
+                }
+              }
             }
-            if (tid == 0) sh.aux[p] = g;
+          }
+        }
+        if (escape) {
+          if (wave_pm_lengths<uint32_t>(sh.hist[p], A, false, sh.len[p], sh.u.wcb) < 0) {
+            need_block = 1;
+          } else {
+            uint64_t part = 0;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const int s2 = ln + 64 * q;
+              if (s2 < A) part += uint64_t(hq[q]) * sh.len[p][s2];
+            }
+            bits = wave_sum64(part);
+            if (section_bytes(HUFF, k, n, nseg, bits) < raw) {
+              mode = HUFF;
+              wave_canon(sh.len[p], A, sh.enc[p]);
+            }
           }
         }
       }
-      if (escape) {
-        if (tid < A) sh.u.cb.hw[tid] = h;
-        __syncthreads();
-        pm_lengths<ENC_NT>(sh.u.cb.pm, sh.u.cb.hw, A, false, sh.len[p]);
-        const uint8_t l = tid < A ? sh.len[p][tid] : 0;
-        bits = block_sum<DT>(sh, (unsigned long long)h * l);
-        if (section_bytes(HUFF, k, n, nseg, bits) < raw) {
-          mode = HUFF;
-          canon_encode_table(sh.len[p], A, sh.enc[p], sh.cnt);
-        }
+      if (ln == 0) {
+        sh.mode[p] = mode;
+        sh.aux[p] = aux;
+        sh.bits[p] = bits;
+        sh.need_block = need_block;
       }
-      if (mode == RAW) {
-        if (tid < A) sh.enc[p][tid] = uint32_t(tid) | (uint32_t(k) << 16);
-        bits = uint64_t(n) * k;
-      }
-      if (tid == 0 && mode != GROUP) sh.aux[p] = 0;
     }
+    __syncthreads();
+    if (sh.need_block) {
+      const uint32_t h = tid < A ? sh.hist[p][tid] : 0;
+      if (tid < A) sh.u.cb.hw[tid] = h;
+      __syncthreads();
+      pm_lengths<ENC_NT>(sh.u.cb.pm, sh.u.cb.hw, A, false, sh.len[p]);
+      const uint8_t l = tid < A ? sh.len[p][tid] : 0;
+      const unsigned long long bits = block_sum<DT>(sh, (unsigned long long)h * l);
+      const bool huff = section_bytes(HUFF, k, n, nseg, bits) < raw;
+      if (huff) canon_encode_table(sh.len[p], A, sh.enc[p], sh.cnt);
+      if (tid == 0) {
+        sh.mode[p] = huff ? HUFF : RAW;
+        sh.bits[p] = bits;
+      }
+      __syncthreads();
+    }
+    const int mode = sh.mode[p];
+    if (mode == RAW && tid < A) sh.enc[p][tid] = uint32_t(tid) | (uint32_t(k) << 16);
     if (tid == 0) {
-      sh.mode[p] = mode;
-      sh.bits[p] = bits;
+      if (mode == RAW) sh.bits[p] = uint64_t(n) * k;
       sh.sec_off[p] = rec;
     }
-    rec += section_bytes(mode, k, n, nseg, mode == RAW ? 0 : bits);
+    rec += section_bytes(mode, k, n, nseg, mode == RAW ? 0 : sh.bits[p]);
     __syncthreads();
   }
 
@@ -313,19 +388,19 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
     const bool with_segs = mode != RAW;
     uint64_t tbit = 0;     // stream bits before this tile
     uint32_t carry = 0;    // partial last word of the previous tile
-    // Huffman-coded streams: wave w of tile T packs segment j = 8T + w, whose
+    // Huffman-coded streams: wave w of tile T packs segment j = NW*T + w, whose
     // symbols are the 32-symbol strips j, j + nseg, ... of the chunk; lane l
     // takes symbols [l*EPT, l*EPT + EPT) of the segment, which lie in one
     // strip.  Raw streams are packed in element order.
-    const int ntiles = (nseg + 7) / 8;
+    const int ntiles = (nseg + NW - 1) / NW;
     auto tile_eb = [&](int T) -> uint32_t {  // first element of this lane's run in tile T
       if (with_segs) {
-        const int jseg = T * 8 + wv;
+        const int jseg = T * NW + wv;
         if (jseg >= nseg) return n;  // no symbols in this lane
         const uint32_t si = uint32_t(ln) * EPT;
         return 32u * ((si / 32) * uint32_t(nseg) + uint32_t(jseg)) + si % 32;
       }
-      return uint32_t(T) * 8u * S + uint32_t(tid) * EPT;
+      return uint32_t(T) * uint32_t(NW * S) + uint32_t(tid) * EPT;
     };
     // the next tile's 16-byte vectors are loaded one tile ahead
     u32x4 nq[NV];
@@ -335,7 +410,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
       for (int j = 0; j < NV; j++) nq[j] = ldg16(src + uint64_t(neb) * ES + 16 * j);
     }
     for (int T = 0; T < ntiles; T++) {
-      const int jseg = T * 8 + wv;
+      const int jseg = T * NW + wv;
       const uint32_t eb = neb;
       const bool vec = aligned && eb + EPT <= n;
       uint32_t w[EPT];
@@ -394,7 +469,7 @@ __global__ __launch_bounds__(ENC_NT) void k_encode(EncArgs a) {
       for (int i = tid; i < EncShared<DT>::STAGE; i += ENC_NT) sh.u.pk.stage[i] = 0;
       __syncthreads();
       uint32_t woff = 0, ttot = 0;
-      for (int q = 0; q < 8; q++) {
+      for (int q = 0; q < NW; q++) {
         const uint32_t x = sh.u.pk.wtot[q];
         woff += q < wv ? x : 0;
         ttot += x;
@@ -506,7 +581,7 @@ __global__ void k_zero(uint32_t *p, uint64_t words) {
 
 hipError_t launch_encode(int dtype, const EncArgs &a, hipStream_t s) {
   if (a.L.n_chunks == 0) return hipSuccess;
-  const dim3 grid(a.L.n_chunks), block(ENC_NT);
+  const dim3 grid(a.L.n_chunks), block(enc_nt(dtype));
   if (dtype == BF16) hipLaunchKernelGGL(k_encode<BF16>, grid, block, 0, s, a);
   else if (dtype == FP32) hipLaunchKernelGGL(k_encode<FP32>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(k_encode<FP8>, grid, block, 0, s, a);

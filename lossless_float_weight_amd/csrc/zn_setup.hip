@@ -94,15 +94,25 @@ __global__ __launch_bounds__(256) void k_pool(const uint32_t *hist, int stride, 
   if (tid < A && acc) atomicAdd(&pooled[g * 256 + tid], acc);
 }
 
+// One histogram per workgroup: the one-wave package-merge when at most 64
+// symbols are present, the workgroup version otherwise (same result).
 __global__ __launch_bounds__(256) void k_lengths(const uint64_t *hw, int A, int group_rule,
                                                  uint8_t *len) {
   __shared__ PMShared pm;
+  __shared__ WaveCB wcb;
   __shared__ uint64_t w[256];
   __shared__ uint8_t l[256];
+  __shared__ int big;
   const int tid = threadIdx.x, h = blockIdx.x;
   w[tid] = tid < A ? hw[uint64_t(h) * 256 + tid] : 0;
   __syncthreads();
-  pm_lengths<256>(pm, w, A, group_rule != 0, l);
+  if (tid < 64) {
+    const int d = wave_pm_lengths<uint64_t>(w, A, group_rule != 0, l, wcb);
+    if (tid == 0) big = d < 0;
+  }
+  __syncthreads();
+  if (big) pm_lengths<256>(pm, w, A, group_rule != 0, l);
+  __syncthreads();
   len[uint64_t(h) * 256 + tid] = tid < A ? l[tid] : 0;
 }
 
