@@ -95,10 +95,10 @@ zn_status zn_tableset_info(const zn_tableset *ts, zn_dtype *dtype, int *n_tensor
 zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes);
 
 /* Device scratch needed by zn_compress / zn_decompress for this plan: 256
- * control bytes, 8 bytes per chunk, and one worst-case record slot per chunk
- * (records are built in their slots, then copied to their final offsets), so
- * roughly the uncompressed size of the coded fields.  Decompression alone
- * needs only the first 256 bytes. */
+ * control bytes, 8 bytes per chunk (record sizes) and a code plan of
+ * 64 + 1024 bytes per coded field per chunk (the code chosen for each
+ * stream): at 256 KiB chunks 1/240 of the input for BF16, 1/63 for FP32.
+ * Decompression alone needs only the first 256 bytes. */
 zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes);
 
 /* zn_compress -- one container holding every tensor of the plan.

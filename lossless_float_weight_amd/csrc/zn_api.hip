@@ -367,22 +367,13 @@ zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes) {
 }
 
 namespace {
-// A full chunk's record never exceeds its all-raw size (every coded stream
-// takes the smallest of constant, code and raw), so this bounds every record.
-uint64_t slot_bytes(const zn_tableset *ts) {
-  uint64_t b = 0;
-  const uint64_t n = ts->chunk_elems;
-  const int nseg = int((n + segsyms(ts->dtype) - 1) / segsyms(ts->dtype));
-  for (int p = 0; p < ncoded(ts->dtype); p++) b += section_bytes(RAW, kbits(ts->dtype, p), n, nseg, 0);
-  return b;
-}
 uint64_t sizes_offset() { return kCtlBytes; }
-uint64_t slots_offset(const zn_tableset *ts) { return kCtlBytes + (8ull * ts->n_chunks + 255) / 256 * 256; }
+uint64_t plans_offset(const zn_tableset *ts) { return kCtlBytes + (8ull * ts->n_chunks + 255) / 256 * 256; }
 }  // namespace
 
 zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes) {
   if (!ts || !bytes) return ZN_ERR_ARG;
-  *bytes = slots_offset(ts) + uint64_t(ts->n_chunks) * slot_bytes(ts);
+  *bytes = plans_offset(ts) + uint64_t(ts->n_chunks) * plan_bytes(ts->dtype);
   return ZN_OK;
 }
 
@@ -406,10 +397,9 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   a.group_enc = ts->d_enc;
   a.group_len = ts->d_len;
   a.out = static_cast<uint8_t *>(d_out);
-  a.slots = scr + slots_offset(ts);
-  a.slot_bytes = slot_bytes(ts);
+  a.plans = scr + plans_offset(ts);
   a.sizes = reinterpret_cast<unsigned long long *>(scr + sizes_offset());
-  HIPCHK(launch_encode(ts->dtype, a, stream));
+  HIPCHK(launch_analyze(ts->dtype, a, stream));
   FinishArgs f;
   f.L = a.L;
   f.dtype = ts->dtype;
@@ -420,14 +410,13 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   f.sizes = a.sizes;
   f.ctl = ctl;
   HIPCHK(launch_finish(f, stream));
-  PlaceArgs pl;
-  pl.n_chunks = ts->n_chunks;
-  pl.off_dir = ts->off_dir;
-  pl.slots = a.slots;
-  pl.slot_bytes = a.slot_bytes;
-  pl.out = a.out;
-  pl.ctl = ctl;
-  HIPCHK(launch_place(pl, stream));
+  PackArgs pk;
+  pk.L = a.L;
+  pk.in_ptrs = a.in_ptrs;
+  pk.plans = a.plans;
+  pk.out = a.out;
+  pk.ctl = ctl;
+  HIPCHK(launch_pack(ts->dtype, pk, stream));
   if (!out_bytes) return ZN_OK;
   uint32_t flag = 0;
   uint64_t total = 0;

@@ -258,12 +258,15 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-// Orders this wave's LDS writes before its later LDS reads by other lanes:
-// wait for the wave's LDS operations (lgkmcnt 0, vector memory untouched),
-// and keep the compiler from moving memory operations across.
+// Orders this wave's LDS writes before its later LDS reads by other lanes of
+// the same wave.  The hardware already runs a wave's LDS instructions in
+// order; the wavefront-scope release/acquire fences are what stop the
+// compiler from moving the memory operations of one lane across the point
+// (the wave barrier alone does not: it is not a memory operation).
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Wave-private LDS of the one-wave package-merge.

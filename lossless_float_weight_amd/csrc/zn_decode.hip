@@ -22,9 +22,11 @@ namespace zn {
 
 constexpr int DEC_NT = 256;
 constexpr int RND = 32;        // symbols per lane per round = one strip of its segment
-constexpr int STW = 44;        // staging bytes per lane: a strip + overflow; 11 words
-                               // keep 32 neighbouring lanes on distinct LDS banks
+constexpr int STWW = 10;       // staging words per lane: a strip and up to 5 symbols more
 constexpr int RING = 16;       // words of a lane's payload window in LDS
+// Staging and ring are lane-interleaved (word w of thread t at w * DEC_NT + t),
+// so lanes that touch different words of their own areas still hit
+// different LDS banks.
 
 template <int DT>
 struct DecShared {
@@ -32,9 +34,9 @@ struct DecShared {
   uint32_t lut[NC][kLutSize];
   union {
     uint16_t t1[kLutSize];
-    uint8_t stage[DEC_NT * STW];
+    uint32_t stage[STWW * DEC_NT];
   } u;
-  uint32_t ring[DEC_NT * RING];
+  uint32_t ring[RING * DEC_NT];
   uint8_t len[NC][256];
   LutShared ls;
   int mode[NC], aux[NC];
@@ -44,23 +46,26 @@ struct DecShared {
   int bad;
 };
 
-__device__ __forceinline__ uint64_t lds8(const uint8_t *p) {  // 4-byte aligned
-  const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-  return q[0] | (uint64_t(q[1]) << 32);
+// Staged words w and w + 1 of thread t.
+__device__ __forceinline__ uint64_t stg_pair(const uint32_t *stage, int w, int t) {
+  return stage[w * DEC_NT + t] | (uint64_t(stage[(w + 1) * DEC_NT + t]) << 32);
 }
-__device__ __forceinline__ uint32_t lds4(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
-// 8 BF16 values from 8 exponent bytes and 8 sign|fraction bytes.
+// 8 BF16 values from 8 exponent bytes and 8 sign|fraction bytes: a byte
+// permute pairs each value's bytes as [sign|fraction, exponent], then the
+// exponent moves down one bit and the sign up to bit 15 of each half.
 __device__ __forceinline__ u32x4 merge_bf16(uint64_t E, uint64_t SF) {
   u32x4 o;
 #pragma unroll
   for (int h = 0; h < 2; h++) {
     const uint32_t e = uint32_t(E >> (32 * h)), s = uint32_t(SF >> (32 * h));
-    const uint32_t x0 = (e & 0xFF) | ((e & 0xFF00) << 8), y0 = (s & 0xFF) | ((s & 0xFF00) << 8);
-    const uint32_t x1 = ((e >> 16) & 0xFF) | ((e >> 8) & 0xFF0000);
-    const uint32_t y1 = ((s >> 16) & 0xFF) | ((s >> 8) & 0xFF0000);
-    o[2 * h] = ((y0 & 0x00800080u) << 8) | (x0 << 7) | (y0 & 0x007F007Fu);
-    o[2 * h + 1] = ((y1 & 0x00800080u) << 8) | (x1 << 7) | (y1 & 0x007F007Fu);
+#pragma unroll
+    for (int x = 0; x < 2; x++) {
+      // bytes [s(2x), e(2x), s(2x+1), e(2x+1)]; e is bytes 4..7 of the pair
+      const uint32_t w = __builtin_amdgcn_perm(e, s, x ? 0x07030602u : 0x05010400u);
+      const uint32_t t = (w & 0x007F007Fu) | ((w >> 1) & ~0x007F007Fu);
+      o[2 * h + x] = ((w << 8) & 0x80008000u) | (t & ~0x80008000u);
+    }
   }
   return o;
 }
@@ -86,6 +91,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   uint8_t *dst = a.out_ptrs[t] + e0 * ES;
   const bool oaligned = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
   const uint8_t *in = a.in;
+  uint8_t *const sink = reinterpret_cast<uint8_t *>(a.ctl) + kSinkOff;
   const uint8_t *rawp = in + a.L.t_raw[t] + (DT == BF16 ? e0 : DT == FP8 ? e0 / 8 : 0);
 
   // ------------------------------------------------- 1. walk the record
@@ -154,10 +160,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   const uint32_t paybytes = sh.pay[p];
   const uint32_t ngroups = (paybytes + 15) / 16;
   const uint32_t *lut = sh.lut[p];
-  uint8_t *st = sh.u.stage + tid * STW;
-  uint32_t *st32 = reinterpret_cast<uint32_t *>(st);
-  const uint8_t *wst = sh.u.stage + wv * 64 * STW;   // this wave's staging
-  uint32_t *ring = sh.ring + tid * RING;
+  uint32_t *sp = sh.u.stage + tid;    // staged word w of this lane: sp[w * DEC_NT]
+  uint32_t *rp = sh.ring + tid;       // ring word w of this lane: rp[w * DEC_NT]
+  const int t0 = wv * 64;             // first thread of this wave
   uint32_t seg_carry = 0;
   int bad = 0;
   const uint32_t nstrips = (n + RND - 1) / RND;
@@ -195,120 +200,143 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     uint32_t pend_g = 0;
     int pend_n = 0;
     auto grp = [&](uint32_t gi) { return ldg16(pay + 16ull * (gi < ngroups ? gi : ngroups - 1)); };
+    auto put_group = [&](uint32_t gi, const u32x4 &x) {  // payload group gi into its ring slot
+      uint32_t *q = rp + 4 * (gi & 3) * DEC_NT;
+      q[0] = x[0];
+      q[DEC_NT] = x[1];
+      q[2 * DEC_NT] = x[2];
+      q[3 * DEC_NT] = x[3];
+    };
     if (coded && live) {
       const uint32_t w0 = b0 >> 5, g0 = w0 >> 2;
       const u32x4 a0 = grp(g0), a1 = grp(g0 + 1), a2 = grp(g0 + 2), a3 = grp(g0 + 3);
-      *reinterpret_cast<u32x4 *>(ring + 4 * (g0 & 3)) = a0;
-      *reinterpret_cast<u32x4 *>(ring + 4 * ((g0 + 1) & 3)) = a1;
-      *reinterpret_cast<u32x4 *>(ring + 4 * ((g0 + 2) & 3)) = a2;
-      *reinterpret_cast<u32x4 *>(ring + 4 * ((g0 + 3) & 3)) = a3;
+      put_group(g0, a0);
+      put_group(g0 + 1, a1);
+      put_group(g0 + 2, a2);
+      put_group(g0 + 3, a3);
       wf = 4 * (g0 + 4);
-      buf = ring[w0 & (RING - 1)] | (uint64_t(ring[(w0 + 1) & (RING - 1)]) << 32);
+      buf = rp[(w0 & (RING - 1)) * DEC_NT] | (uint64_t(rp[((w0 + 1) & (RING - 1)) * DEC_NT]) << 32);
       wpos = w0 + 2;
       buf >>= (b0 & 31);
       nb = 64 - int(b0 & 31);
     }
-    uint64_t acc = 0;   // decoded symbols not yet written, one per byte
-    int ov = 0;         // symbols of the next strip decoded early
-    for (int r = 0; r < S / RND; r++) {
+    int ov = 0;         // symbols of the next strip decoded early (staged words 8, 9)
+    // Raw bits merged by this lane in round r: one load per vector, always
+    // issued (an empty vector reads the plane's first bytes and is ignored),
+    // so every round issues the same loads and no wait has to drain the
+    // stores in flight.  A partial last vector stays inside the plane, whose
+    // size is padded to 16 bytes: BF16 vectors start at multiples of 8
+    // bytes, FP8 sign words at multiples of 2.
+    auto load_raw = [&](int r, uint64_t (&rv)[NVL]) {
+#pragma unroll
+      for (int i = 0; i < NVL; i++) {
+        const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
+        const int sjv = g * GS + wv * SPW + sl;
+        const uint32_t ev = (uint32_t(r) * nseg + sjv) * RND + part * VE;
+        const bool ok = sjv < nseg && ev < n;
+        if constexpr (DT == BF16) {
+          const u32x2 x = ldg8(rawp + (ok ? ev : 0));
+          rv[i] = x[0] | (uint64_t(x[1]) << 32);
+        } else if constexpr (DT == FP8) {
+          rv[i] = ldg2(rawp + (ok ? ev / 8 : 0));
+        } else {
+          rv[i] = 0;
+        }
+      }
+    };
+    constexpr int NR = S / RND;   // rounds, an even number
+    static_assert(NR % 2 == 0, "rounds come in pairs");
+    uint64_t rawA[NVL], rawB[NVL];
+    load_raw(0, rawA);
+    // One round; the raw bits of the next round load into nxt while this one
+    // decodes (the loop below alternates two register sets, so no copy makes
+    // the compiler wait for loads in flight).
+    auto round = [&](int r, const uint64_t (&rawv)[NVL], uint64_t (&nxt)[NVL]) {
+      load_raw(r + 1 < NR ? r + 1 : r, nxt);  // the last round reloads its own: same count
       const uint32_t q = uint32_t(r) * nseg + sj;   // this lane's strip
       const int lim = live && q < nstrips ? int(min(uint32_t(RND), n - q * RND)) : 0;
       const bool last = live && q < nstrips && q + nseg >= nstrips;
       // groups fetched last round enter the ring
       if (pend_n > 0) {
-        *reinterpret_cast<u32x4 *>(ring + 4 * (pend_g & 3)) = pq0;
-        if (pend_n > 1) *reinterpret_cast<u32x4 *>(ring + 4 * ((pend_g + 1) & 3)) = pq1;
-        if (pend_n > 2) *reinterpret_cast<u32x4 *>(ring + 4 * ((pend_g + 2) & 3)) = pq2;
+        put_group(pend_g, pq0);
+        if (pend_n > 1) put_group(pend_g + 1, pq1);
+        if (pend_n > 2) put_group(pend_g + 2, pq2);
         wf = 4 * (pend_g + pend_n);
         pend_n = 0;
       }
-      // raw bits merged by this lane after the round, loaded before decoding
-      uint64_t rawv[NVL];
-#pragma unroll
-      for (int i = 0; i < NVL; i++) {
-        rawv[i] = 0;
-        const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
-        const int sjv = g * GS + wv * SPW + sl;
-        const uint32_t qv = uint32_t(r) * nseg + sjv;
-        const uint32_t ev = qv * RND + part * VE;
-        if (sjv < nseg && ev < n) {
-          if constexpr (DT == BF16) {
-            if (ev + 8 <= n) {
-              const u32x2 x = ldg8(rawp + ev);
-              rawv[i] = x[0] | (uint64_t(x[1]) << 32);
-            } else {
-              for (uint32_t b = 0; ev + b < n; b++) rawv[i] |= uint64_t(ldg1(rawp + ev + b)) << (8 * b);
-            }
-          } else if constexpr (DT == FP8) {
-            if (ev + 16 <= n) rawv[i] = ldg2(rawp + ev / 8);
-            else rawv[i] = ldg1(rawp + ev / 8) | (ev + 8 < n ? ldg1(rawp + ev / 8 + 1) << 8 : 0u);
-          }
-        }
-      }
       if (lim > 0) {
         if (coded) {
-          int cnt = ov, na = ov, sw = 0;
-          if (na >= 4) {
-            st32[sw++] = uint32_t(acc);
-            acc >>= 32;
-            na -= 4;
+          // Symbols are staged four to a word.  cur holds the bytes of the
+          // word being filled; each lookup writes that word and the next
+          // (aligned stores; the next word holds what spilled over) and
+          // moves on when the word is complete -- no branch per lookup.
+          // The window is refilled, also without branches, with 32 bits
+          // whenever fewer than 32 remain: enough for the two lookups of
+          // an iteration (at most 22 bits).
+          uint32_t cur = 0;
+          uint32_t *wp = sp;        // the word being filled
+          if (ov) {  // symbols of this strip decoded last round: words 8, 9 -> 0, 1
+            const uint32_t c8 = sp[8 * DEC_NT], c9 = sp[9 * DEC_NT];
+            sp[0] = c8;
+            sp[DEC_NT] = c9;
+            cur = ov >= 4 ? c9 : c8;
+            wp = ov >= 4 ? sp + DEC_NT : sp;
           }
-          pre = ring[wpos & (RING - 1)];
-          while (cnt < lim) {
-            if (nb < 32) {
-              buf |= uint64_t(pre) << nb;
-              nb += 32;
-              wpos++;
-              pre = ring[wpos & (RING - 1)];
-            }
-            uint32_t e = lut[buf & (kLutSize - 1)];
-            int m = int(e >> 28), bl = int((e >> 24) & 15);
-            acc |= uint64_t(e & 0xFFFFFF) << (8 * na);
+          int pos = ov;             // symbols of this strip decoded so far
+          uint32_t na = ov & 3;     // bytes in cur
+          pre = rp[(wpos & (RING - 1)) * DEC_NT];
+          auto emit = [&](uint32_t e) {
+            const uint64_t t = uint64_t(e & 0xFFFFFF) << (8 * na);
+            const uint32_t lo = cur | uint32_t(t), hi = uint32_t(t >> 32);
+            wp[0] = lo;
+            wp[DEC_NT] = hi;
+            const uint32_t m = e >> 28;
+            pos += int(m);
             na += m;
-            cnt += m;
+            const bool full = na >= 4;
+            cur = full ? hi : lo;
+            wp += full ? DEC_NT : 0;
+            na &= 3;
+          };
+          while (pos < lim) {
+            const bool need = nb < 32;
+            buf |= uint64_t(need ? pre : 0u) << nb;
+            nb += need ? 32 : 0;
+            wpos += need ? 1u : 0u;
+            pre = rp[(wpos & (RING - 1)) * DEC_NT];
+            uint32_t e = lut[buf & (kLutSize - 1)];
+            emit(e);
+            uint32_t bl = (e >> 24) & 15;
             buf >>= bl;
-            nb -= bl;
-            if (na >= 4) {
-              st32[sw++] = uint32_t(acc);
-              acc >>= 32;
-              na -= 4;
-            }
-            if (cnt < lim) {
-              e = lut[buf & (kLutSize - 1)];
-              m = int(e >> 28), bl = int((e >> 24) & 15);
-              acc |= uint64_t(e & 0xFFFFFF) << (8 * na);
-              na += m;
-              cnt += m;
-              buf >>= bl;
-              nb -= bl;
-              if (na >= 4) {
-                st32[sw++] = uint32_t(acc);
-                acc >>= 32;
-                na -= 4;
-              }
-            }
+            nb -= int(bl);
+            e = lut[buf & (kLutSize - 1)];
+            emit(e);
+            bl = (e >> 24) & 15;
+            buf >>= bl;
+            nb -= int(bl);
           }
-          st32[sw] = uint32_t(acc);  // the partial last word
-          ov = cnt - lim;
+          ov = pos - lim;   // at most 5: the loop stops 2 lookups of 3 symbols past lim - 1
           if (last) {
             // exact end: the segment must use exactly its stored bit length
-            uint64_t pos = uint64_t(wpos) * 32 - uint32_t(nb);
-            for (int x = 0; x < ov; x++) pos -= sh.len[p][st[lim + x]];
-            if (pos != uint64_t(b0) + sbits) bad = 1;
+            uint64_t bpos = uint64_t(wpos) * 32 - uint32_t(nb);
+            for (int x = 0; x < ov; x++) {
+              const int b = lim + x;
+              bpos -= sh.len[p][(sp[(b >> 2) * DEC_NT] >> (8 * (b & 3))) & 0xFF];
+            }
+            if (bpos != uint64_t(b0) + sbits) bad = 1;
             ov = 0;
           } else {
-            // lim == RND here, and at most 2 symbols run over (the second
-            // lookup of an iteration only runs below the limit)
-            acc = ov ? (st32[8] & (0xFFFFFFFFu >> (32 - 8 * ov))) : 0;
-            // fetch the groups the next round may need: words [wpos, wpos + 12)
+            // lim == RND here.  Fetch the groups the next round may need: a
+            // round reads at most 32 lookups (352 bits) with at least 10
+            // bits left in the window, so words [wpos, wpos + 12).
             const uint32_t needg = (wpos + 12 + 3) / 4;
             const uint32_t have = wf / 4;
             if (needg > have) {
               pend_g = have;
               pend_n = int(needg - have);
               pq0 = grp(pend_g);
-              if (pend_n > 1) pq1 = grp(pend_g + 1);
-              if (pend_n > 2) pq2 = grp(pend_g + 2);
+              pq1 = grp(pend_g + 1);   // loaded even when unused: see load_raw
+              pq2 = grp(pend_g + 2);
             }
           }
         } else if (mode == RAW) {
@@ -331,7 +359,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           }
           if (k == 8) {
 #pragma unroll
-            for (int x = 0; x < 8; x++) st32[x] = wd[x];
+            for (int x = 0; x < 8; x++) sp[x * DEC_NT] = wd[x];
           } else {
 #pragma unroll
             for (int x = 0; x < RND / 4; x++) {
@@ -343,7 +371,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
                 const uint32_t hi = (bit & 31) + k > 32 ? wd[(bit >> 5) + 1] << (32 - (bit & 31)) : 0u;
                 wv4 |= ((lo | hi) & ((1u << k) - 1)) << (8 * y);
               }
-              st32[x] = wv4;
+              sp[x * DEC_NT] = wv4;
             }
           }
         }
@@ -356,18 +384,18 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         const int sjv = g * GS + wv * SPW + sl;
         const uint32_t qv = uint32_t(r) * nseg + sjv;
         const uint32_t ev = qv * RND + part * VE;
-        if (sjv >= nseg || ev >= n) continue;
+        const bool valid = sjv < nseg && ev < n;
         u32x4 o;
         if constexpr (DT == BF16) {
           const uint64_t E = sh.mode[0] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[0])
-                                                 : lds8(wst + sl * STW + part * 8);
+                                                 : stg_pair(sh.u.stage, 2 * part, t0 + sl);
           o = merge_bf16(E, rawv[i]);
         } else if constexpr (DT == FP32) {
           uint32_t P[4];
 #pragma unroll
           for (int pp = 0; pp < 4; pp++)
             P[pp] = sh.mode[pp] == CONST ? 0x01010101u * uint32_t(sh.aux[pp])
-                                         : lds4(wst + (pp * SPW + sl) * STW + part * 4);
+                                         : sh.u.stage[part * DEC_NT + t0 + pp * SPW + sl];
 #pragma unroll
           for (int x = 0; x < 4; x++) {
             const uint32_t p0 = (P[0] >> (8 * x)) & 0xFF, p1 = (P[1] >> (8 * x)) & 0xFF;
@@ -379,9 +407,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; h++) {
             Ev[h] = sh.mode[0] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[0])
-                                        : lds8(wst + sl * STW + part * 16 + 8 * h);
+                                        : stg_pair(sh.u.stage, 4 * part + 2 * h, t0 + sl);
             Mv[h] = sh.mode[1] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[1])
-                                        : lds8(wst + (SPW + sl) * STW + part * 16 + 8 * h);
+                                        : stg_pair(sh.u.stage, 4 * part + 2 * h, t0 + SPW + sl);
           }
 #pragma unroll
           for (int x = 0; x < 4; x++) {
@@ -392,15 +420,27 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             o[x] = (e4 << 3) | m3 | sb;
           }
         }
+        // Every lane stores one vector per iteration -- lanes without a
+        // whole aligned vector store into the scratch sink -- so each round
+        // issues the same stores and the compiler's waits for older loads
+        // never have to drain them.
         uint8_t *op = dst + uint64_t(ev) * ES;
-        if (ev + VE <= n && oaligned) {
-          stg16(op, o);
-        } else {
+        const bool whole = valid && ev + VE <= n && oaligned;
+        stg16(whole ? op : sink, o);
+        if (valid && !whole) {  // a partial last vector or an unaligned output
           const uint32_t cnt_b = (ev + VE <= n ? VE : n - ev) * ES;
           for (uint32_t b = 0; b < cnt_b; b++) stg1(op + b, o[b >> 2] >> ((b & 3) * 8));
         }
       }
       wave_lds_sync();
+    };
+    // the first pair is peeled so that the loop is entered with the memory
+    // operations of a whole round in flight, as on every later pass
+    round(0, rawA, rawB);
+    round(1, rawB, rawA);
+    for (int r = 2; r < NR; r += 2) {
+      round(r, rawA, rawB);
+      round(r + 1, rawB, rawA);
     }
   }
   // the stream's segment lengths must add up to its payload

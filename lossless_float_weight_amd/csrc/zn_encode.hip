@@ -1,30 +1,41 @@
 // zn_encode.hip -- the compression pass for gfx950.
 //
-// One workgroup per chunk (4 wave64s for BF16, 8 otherwise), in one launch:
-//   1. read the chunk once with 16-byte loads, split every element into its
+// Three launches, each chunk-parallel or tiny:
+//   k_analyze (one workgroup per chunk; 4 wave64s for BF16, 8 otherwise)
+//   1. reads the chunk once with 16-byte loads, splits every element into its
 //      coded fields and its always-raw bits (THEORY-599 on ZipNN, per-field
-//      compressibility, ZipNN Table II), store the raw bits straight to their
-//      final place, and count each coded field in LDS histograms privatised
+//      compressibility, ZipNN Table II), stores the raw bits straight to their
+//      final place, and counts each coded field in LDS histograms privatised
 //      per lane column (the exponent histogram is very skewed: a handful of
 //      bins take most hits, so lanes must not share counters);
-//   2. per coded stream: constant / shared group code / own optimal code /
-//      raw, by exact section size; the own code is built in LDS by
+//   2. per coded stream chooses constant / shared group code / own optimal
+//      code / raw by exact section size; the own code is built in LDS by
 //      package-merge (THEORY-599, order-0 only; "NeuralZip: Reusable Setup
-//      for Fast Lossless Compression", Abstract, for group codes);
-//   3. re-read the chunk (it is still in L2) and pack codes into the chunk's
-//      own record slot in scratch: one wave per segment, a wave scan of bit
-//      counts, code words ORed into an LDS tile, whole words stored
-//      coalesced.  The record size is published for the placement pass.
-// Then one workgroup scans the record sizes into the directory (k_finish) and
-// every record is copied from its slot to its place (k_place).  Chunks never
-// wait for each other: a record's offset is only needed by the copy.
+//      for Fast Lossless Compression", Abstract, for group codes).  The
+//      choice, the code words and the record size go to a per-chunk plan.
+//   k_finish (one workgroup) scans the record sizes into the directory and
+//   writes the header and the alignment gaps.
+//   k_pack (one workgroup of 4 wave64s per chunk) writes the chunk's record
+//   at its directory offset: stream heads, then the payload packed one wave
+//   per segment -- a wave scan of bit counts, code words ORed into an LDS
+//   tile, whole words stored coalesced.
+// No chunk ever waits for another, and no record is copied after packing.
 #include "zn_internal.h"
 
 namespace zn {
 
-// threads per chunk: BF16 chunks use 256 so that every chunk of a large
-// workload is resident at once (8 workgroups of under 20 KB LDS per CU)
+// threads per chunk in k_analyze: BF16 chunks use 256 so that every chunk of
+// a large workload is resident at once (7 workgroups of under 20 KB LDS per
+// CU); k_pack always uses 256.
 constexpr int enc_nt(int dt) { return dt == BF16 ? 256 : 512; }
+constexpr int PACK_NT = 256, PACK_NW = PACK_NT / 64;
+
+// Per-chunk plan, written by k_analyze and read by k_pack:
+//   u64 bits[4] (payload bits per coded stream), u32 sec_off[4] (offset of
+//   each stream's section in the record), u8 mode[4], u8 aux[4], pad to 64,
+//   then u32 enc[ncoded][256] (bit-reversed code | length << 16) for the
+//   streams coded with a Huffman or group code.
+__host__ __device__ constexpr uint64_t plan_stride(int dt) { return 64 + 1024ull * ncoded(dt); }
 
 template <int DT, int P>
 __device__ __forceinline__ uint32_t field(uint32_t w) {
@@ -89,7 +100,6 @@ struct EncShared {
   // 16384 values at the largest chunk size, so 16 bits cannot overflow)
   static constexpr bool PACK16 = DT == BF16;
   static constexpr int PRIVW = PACK16 ? APRIV * COLS / 2 : APRIV * COLS;
-  static constexpr int STAGE = (NW * S * kMaxLen + 31) / 32 + 4;  // words of one pack tile
   uint32_t hist[NC][256];
   uint32_t enc[NC][256];
   uint8_t len[NC][256];
@@ -106,12 +116,17 @@ struct EncShared {
       PMShared pm;
       uint64_t hw[256];
     } cb;
-    struct {
-      uint32_t stage[STAGE];
-      uint32_t wtot[NW];
-    } pk;
     WaveCB wcb;
   } u;
+};
+
+template <int DT>
+struct PackShared {
+  static constexpr int NC = ncoded(DT);
+  static constexpr int STAGE = (PACK_NW * segsyms(DT) * kMaxLen + 31) / 32 + 4;  // words of a tile
+  uint32_t enc[NC][256];
+  uint32_t stage[STAGE];
+  uint32_t wtot[PACK_NW];
 };
 
 template <int DT>
@@ -156,13 +171,11 @@ __device__ __forceinline__ void count(EncShared<DT> &sh, int p, uint32_t b, int 
 }
 
 template <int DT>
-__global__ __launch_bounds__(enc_nt(DT)) void k_encode(EncArgs a) {
+__global__ __launch_bounds__(enc_nt(DT)) void k_analyze(EncArgs a) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
-  constexpr int EPT = S / 64;          // elements per thread per pack tile (a wave = a segment)
-  constexpr int NV = EPT / VE;         // vectors per thread per pack tile
   constexpr int COLS = EncShared<DT>::COLS;
-  constexpr int ENC_NT = EncShared<DT>::NT, NW = EncShared<DT>::NW;
+  constexpr int ENC_NT = EncShared<DT>::NT;
   __shared__ EncShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
 
@@ -357,27 +370,69 @@ __global__ __launch_bounds__(enc_nt(DT)) void k_encode(EncArgs a) {
     __syncthreads();
   }
 
-  // the record goes to this chunk's slot; its size to the placement pass
+  // the plan: sizes and offsets, then the code words of coded streams
+  uint8_t *plan = a.plans + uint64_t(c) * plan_stride(DT);
   if (tid == 0) a.sizes[c] = rec;
-  const uint64_t roff = 0;
-  uint8_t *const recp = a.slots + uint64_t(c) * a.slot_bytes;
-
-  // -------------------------------------------------------- 4. the record
+  if (tid < NC) {
+    stg8(plan + 8 * tid, u32x2{uint32_t(sh.bits[tid]), uint32_t(sh.bits[tid] >> 32)});
+    stg4(plan + 32 + 4 * tid, uint32_t(sh.sec_off[tid]));
+    stg1(plan + 48 + tid, uint32_t(sh.mode[tid]));
+    stg1(plan + 52 + tid, uint32_t(sh.aux[tid]));
+  }
   for (int p = 0; p < NC; p++) {
-    const int k = kbits(DT, p), A = 1 << k, mode = sh.mode[p];
-    const uint64_t bits = sh.bits[p];
-    uint8_t *sec = recp + roff + sh.sec_off[p];
+    const int A = 1 << kbits(DT, p), mode = sh.mode[p];
+    if ((mode == HUFF || mode == GROUP) && tid < A) stg4(plan + 64 + 1024 * p + 4 * tid, sh.enc[p][tid]);
+  }
+}
+
+// One workgroup per chunk: the record at its directory offset.
+template <int DT>
+__global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
+  constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
+  constexpr int VE = 16 / ES;          // elements per 16-byte vector
+  constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
+  constexpr int NV = EPT / VE;         // vectors per thread per tile
+  constexpr int NW = PACK_NW, ENC_NT = PACK_NT;
+  constexpr int STAGE = PackShared<DT>::STAGE;
+  __shared__ PackShared<DT> sh;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  if (a.ctl[0]) return;  // the container did not fit
+
+  const uint32_t c = blockIdx.x;
+  const int t = find_tensor(a.L, c);
+  const uint64_t e0 = uint64_t(c - a.L.t_chunk0[t]) * a.L.chunk_elems;
+  const uint64_t rem = a.L.t_n[t] - e0;
+  const uint32_t n = uint32_t(rem < a.L.chunk_elems ? rem : a.L.chunk_elems);
+  const uint8_t *src = a.in_ptrs[t] + e0 * ES;
+  const bool aligned = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  const int nseg = int((n + S - 1) / S);
+  const uint8_t *plan = a.plans + uint64_t(c) * plan_stride(DT);
+  const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
+  uint8_t *const recp = a.out + dir[c];
+  for (int p = 0; p < NC; p++) {
+    const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
+    if (tid < A)
+      sh.enc[p][tid] = mode == RAW ? uint32_t(tid) | (uint32_t(k) << 16)
+                     : (mode == HUFF || mode == GROUP) ? ldg4(plan + 64 + 1024 * p + 4 * tid) : 0u;
+  }
+  __syncthreads();
+
+  // -------------------------------------------------------- the record
+  for (int p = 0; p < NC; p++) {
+    const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
+    const uint64_t bits = *reinterpret_cast<const uint64_t *>(plan + 8 * p);
+    uint8_t *sec = recp + *reinterpret_cast<const uint32_t *>(plan + 32 + 4 * p);
     const uint64_t head = head_bytes_of(mode, k, nseg);
     const uint64_t pay = payload_bytes_of(mode, k, n, bits);
     // stream header, code lengths and the zero pad of the head
     if (tid == 0) {
       *reinterpret_cast<uint32_t *>(sec) =
-          uint32_t(mode) | (uint32_t(sh.aux[p]) << 8) | (uint32_t(nseg) << 16);
+          uint32_t(mode) | (uint32_t(plan[52 + p]) << 8) | (uint32_t(nseg) << 16);
       *reinterpret_cast<uint32_t *>(sec + 4) = uint32_t(pay);
     }
     uint64_t used = 8;
     if (mode == HUFF) {
-      if (tid < A / 2) sec[8 + tid] = uint8_t(sh.len[p][2 * tid] | (sh.len[p][2 * tid + 1] << 4));
+      if (tid < A / 2) sec[8 + tid] = uint8_t((sh.enc[p][2 * tid] >> 16) | ((sh.enc[p][2 * tid + 1] >> 16) << 4));
       used += A / 2;
     }
     if (mode == HUFF || mode == GROUP) used += 2ull * nseg;
@@ -465,17 +520,17 @@ __global__ __launch_bounds__(enc_nt(DT)) void k_encode(EncArgs a) {
         }
       }
       const uint32_t incl = wave_incl_scan(uint32_t(nb));
-      if (ln == 63) sh.u.pk.wtot[wv] = incl;
-      for (int i = tid; i < EncShared<DT>::STAGE; i += ENC_NT) sh.u.pk.stage[i] = 0;
+      if (ln == 63) sh.wtot[wv] = incl;
+      for (int i = tid; i < STAGE; i += ENC_NT) sh.stage[i] = 0;
       __syncthreads();
       uint32_t woff = 0, ttot = 0;
       for (int q = 0; q < NW; q++) {
-        const uint32_t x = sh.u.pk.wtot[q];
+        const uint32_t x = sh.wtot[q];
         woff += q < wv ? x : 0;
         ttot += x;
       }
-      if (with_segs && ln == 0 && jseg < nseg) stg2(segt + jseg, sh.u.pk.wtot[wv]);
-      if (tid == 0 && carry) atomicOr(&sh.u.pk.stage[0], carry);
+      if (with_segs && ln == 0 && jseg < nseg) stg2(segt + jseg, sh.wtot[wv]);
+      if (tid == 0 && carry) atomicOr(&sh.stage[0], carry);
       uint32_t start = uint32_t(tbit & 31) + woff + incl - uint32_t(nb);
 #pragma unroll
       for (int g8 = 0; g8 < NG; g8++) {
@@ -484,11 +539,11 @@ __global__ __launch_bounds__(enc_nt(DT)) void k_encode(EncArgs a) {
         const uint64_t t0 = glo[g8] << sft;
         const uint64_t t1 = (uint64_t(ghi[g8]) << sft) | (sft ? glo[g8] >> (64 - sft) : 0ull);
         if (gb[g8]) {
-          atomicOr(&sh.u.pk.stage[wi], uint32_t(t0));
+          atomicOr(&sh.stage[wi], uint32_t(t0));
           const uint32_t x1 = uint32_t(t0 >> 32), x2 = uint32_t(t1), x3 = uint32_t(t1 >> 32);
-          if (x1) atomicOr(&sh.u.pk.stage[wi + 1], x1);
-          if (x2) atomicOr(&sh.u.pk.stage[wi + 2], x2);
-          if (x3) atomicOr(&sh.u.pk.stage[wi + 3], x3);
+          if (x1) atomicOr(&sh.stage[wi + 1], x1);
+          if (x2) atomicOr(&sh.stage[wi + 2], x2);
+          if (x3) atomicOr(&sh.stage[wi + 3], x3);
         }
         start += uint32_t(gb[g8]);
       }
@@ -496,8 +551,8 @@ __global__ __launch_bounds__(enc_nt(DT)) void k_encode(EncArgs a) {
       const uint32_t endb = uint32_t(tbit & 31) + ttot;
       const uint32_t nfull = endb >> 5;
       const uint64_t w0 = tbit >> 5;
-      for (uint32_t i = tid; i < nfull; i += ENC_NT) stg4(pw + w0 + i, sh.u.pk.stage[i]);
-      carry = (endb & 31) ? sh.u.pk.stage[nfull] : 0;
+      for (uint32_t i = tid; i < nfull; i += ENC_NT) stg4(pw + w0 + i, sh.stage[i]);
+      carry = (endb & 31) ? sh.stage[nfull] : 0;
       tbit += ttot;
       __syncthreads();
     }
@@ -562,40 +617,34 @@ __global__ __launch_bounds__(1024) void k_finish(FinishArgs a) {
   if (fits && tid < 4) stg4(a.out + end + 4 * tid, 0);
 }
 
-// One workgroup per record: copy it from its slot to the directory offset.
-__global__ __launch_bounds__(256) void k_place(PlaceArgs a) {
-  if (a.ctl[0]) return;  // the container did not fit
-  const uint32_t c = blockIdx.x;
-  const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.off_dir);
-  const uint64_t d0 = dir[c], n16 = (dir[c + 1] - d0) / 16;
-  const uint8_t *src = a.slots + uint64_t(c) * a.slot_bytes;
-  uint8_t *dst = a.out + d0;
-  for (uint64_t i = threadIdx.x; i < n16; i += 256) stg16(dst + 16 * i, ldg16(src + 16 * i));
-}
-
 __global__ void k_zero(uint32_t *p, uint64_t words) {
   for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < words;
        i += uint64_t(gridDim.x) * blockDim.x)
     p[i] = 0;
 }
 
-hipError_t launch_encode(int dtype, const EncArgs &a, hipStream_t s) {
+uint64_t plan_bytes(int dtype) { return plan_stride(dtype); }
+
+hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s) {
   if (a.L.n_chunks == 0) return hipSuccess;
   const dim3 grid(a.L.n_chunks), block(enc_nt(dtype));
-  if (dtype == BF16) hipLaunchKernelGGL(k_encode<BF16>, grid, block, 0, s, a);
-  else if (dtype == FP32) hipLaunchKernelGGL(k_encode<FP32>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_encode<FP8>, grid, block, 0, s, a);
+  if (dtype == BF16) hipLaunchKernelGGL(k_analyze<BF16>, grid, block, 0, s, a);
+  else if (dtype == FP32) hipLaunchKernelGGL(k_analyze<FP32>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_analyze<FP8>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s) {
+  if (a.L.n_chunks == 0) return hipSuccess;
+  const dim3 grid(a.L.n_chunks), block(PACK_NT);
+  if (dtype == BF16) hipLaunchKernelGGL(k_pack<BF16>, grid, block, 0, s, a);
+  else if (dtype == FP32) hipLaunchKernelGGL(k_pack<FP32>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_pack<FP8>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_place(const PlaceArgs &a, hipStream_t s) {
-  if (a.n_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_place, dim3(a.n_chunks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -15,9 +15,16 @@ struct EncArgs {
   const uint32_t *group_enc;       // [K][256] bit-reversed code | len << 16
   const uint8_t *group_len;        // [K][256]
   uint8_t *out;                    // container (the raw planes are written here)
-  uint8_t *slots;                  // [n_chunks][slot_bytes] records before placement
-  uint64_t slot_bytes;
+  uint8_t *plans;                  // [n_chunks][plan_bytes(dtype)] code choice and code words
   unsigned long long *sizes;       // [n_chunks] record bytes
+};
+// Packs every record at its directory offset (after k_finish).
+struct PackArgs {
+  DevLayout L;
+  const uint8_t *const *in_ptrs;
+  const uint8_t *plans;
+  uint8_t *out;
+  const uint32_t *ctl;             // [0] non-zero: the container did not fit, write nothing
 };
 
 // Offsets of the records (exclusive scan of their sizes), the directory, the
@@ -31,16 +38,6 @@ struct FinishArgs {
   uint64_t cap;
   const unsigned long long *sizes;
   uint32_t *ctl;                   // [0] error bits
-};
-
-// Copies every record from its slot to its place in the container.
-struct PlaceArgs {
-  uint32_t n_chunks;
-  uint64_t off_dir;
-  const uint8_t *slots;
-  uint64_t slot_bytes;
-  uint8_t *out;
-  const uint32_t *ctl;
 };
 
 struct DecArgs {
@@ -68,12 +65,16 @@ struct CheckArgs {
 
 // Error bits in ctl[0].
 constexpr uint32_t kErrCapacity = 1, kErrCorrupt = 2, kErrTableset = 4;
-// Compress scratch: ctl[0..63] control, record sizes, then one slot per chunk.
+// Compress scratch: ctl[0..63] control, record sizes, then one plan per chunk.
 constexpr uint64_t kCtlBytes = 256;
+// Bytes [128, 144) of the decompress scratch take the stores of lanes that
+// have nothing to store (their content is meaningless).
+constexpr uint64_t kSinkOff = 128;
 
-hipError_t launch_encode(int dtype, const EncArgs &a, hipStream_t s);
+uint64_t plan_bytes(int dtype);
+hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s);
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
-hipError_t launch_place(const PlaceArgs &a, hipStream_t s);
+hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s);
 hipError_t launch_zero(uint32_t *p, uint64_t words, hipStream_t s);
 hipError_t launch_check(const CheckArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s);
