@@ -1,23 +1,32 @@
 """Benchmark of the codec's hot path on one MI355X.
 
 One step = one full pass of the path over the workload: zn_compress (field
-split, per-chunk histograms, code construction, look-back, packing) followed
-by zn_decompress (tables, segment-parallel decoding, merge) of every tensor.
-Inputs and buffers are resident in HBM before timing starts; three buffer
-sets rotate so consecutive steps do not hit the 256 MB Infinity Cache with
-the previous step's data.
+split, per-chunk histograms, code construction, packing at the final record
+offsets) followed by zn_decompress (tables, segment-parallel decoding,
+merge) of every tensor.  Inputs and buffers are resident in HBM before timing
+starts; three buffer sets rotate so consecutive steps do not hit the 256 MB
+Infinity Cache with the previous step's data.
 
 Prints one JSON line.  `value` is uncompressed GB/s through a whole step
-(compress + decompress); per-direction figures, the compression ratio, the
-roofline of each kernel (algorithmic bytes = container bytes + uncompressed
-bytes per pass, against 8 TB/s HBM) and the CPU oracle's rate on a bounded
-sample of the same workload are reported beside it.
+(compress + decompress).  `roofline` is for the dominant kernel: its
+algorithmic bytes per launch (container bytes + uncompressed bytes for the
+decoder) over its average launch duration, timed with HIP events that the
+library records on the call's stream around that kernel only; `traffic` is
+the HBM bytes per launch from committed rocprofv3 counter runs
+(profiles/traffic_*.txt), reported only while the kernel sources are the
+ones those counters were taken on.  The CPU oracle's rate on a bounded
+sample of the same workload is reported beside it.
+
+--copy-calibration runs a plain device-to-device copy of the workload's
+size instead (the calibration kernel for the HBM byte counters).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,8 +35,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "BF16 decompress/compress GB/s (uncompressed) + % HBM roofline; ratio"
-# Published by the benchmark spec: none, so there is nothing to divide by.
+# BASELINE publishes no figure for this metric on any hardware.
 BASELINE_VALUE = None
+CHUNK_BYTES = 262144
 
 WORKLOADS = {
     "block": "8B-shaped BF16 transformer block: Wq 4096x4096, Wk/Wv 1024x4096, Wo 4096x4096, "
@@ -39,6 +49,35 @@ WORKLOADS = {
     "fp8": "FP8 E4M3 1,073,741,824 values, N(0,1) scaled per 128-element block to max 448, "
            "256 KiB chunks",
 }
+
+# kernel -> sources whose text decides its code (for the counter files' hash)
+KERNEL_SOURCES = {
+    "decode": ["zn_decode.hip", "zn_common.h", "zn_internal.h"],
+    "analyze": ["zn_encode.hip", "zn_common.h", "zn_internal.h"],
+    "pack": ["zn_encode.hip", "zn_common.h", "zn_internal.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "lossless_float_weight_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt, if
+    that file was measured on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    mh = re.search(r"^source_hash:\s*(\w+)", text, re.M)
+    mt = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    if not mh or not mt or mh.group(1) != source_hash(kernel):
+        return None
+    return int(mt.group(1))
 
 
 def make_tensors(name: str):
@@ -91,6 +130,27 @@ def cpu_baseline(tensors, budget_s: float = 20.0):
                       f"{nbytes / (t2 - t1) / 1e9:.4f} GB/s, single thread"}
 
 
+def copy_calibration(args) -> None:
+    """Plain device-to-device copies of the workload's byte count (the
+    reference kernel for the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    base = make_tensors(args.workload)
+    nbytes = sum(t.numel() * t.element_size() for t in base)
+    del base
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes": nbytes, "steps": args.steps, "ms_per_copy": round(dt * 1e3, 4),
+                      "GBps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,12 +159,16 @@ def main():
     ap.add_argument("--workload", default="block", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this codec's path runs on a single MI355X and shards "
               f"by chunk ranges with no exchange during decode; --gpus {args.gpus} is not run.",
               file=sys.stderr)
         raise SystemExit(2)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
 
     import torch
 
@@ -114,7 +178,7 @@ def main():
     torch.cuda.set_device(0)
     base = make_tensors(args.workload)
     unc = sum(t.numel() * t.element_size() for t in base)
-    ts = zn.setup(base, chunk_bytes=262144)
+    ts = zn.setup(base, chunk_bytes=CHUNK_BYTES)
     bound = zn.compress_bound(ts)
     R = max(1, args.rotate)
     sets = []
@@ -135,7 +199,12 @@ def main():
     for s in sets[1:]:
         zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"])
 
-    def step(s, ev=None):
+    kernels = ("analyze", "pack", "decode")
+
+    def step(s, ev=None, kev=None):
+        if kev is not None:
+            for k in kernels:
+                zn.debug_kernel_events(k, *kev[k])
         if ev is not None:
             ev[0].record()
         zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"], sync=False)
@@ -149,17 +218,25 @@ def main():
     for i in range(args.warmup):
         step(sets[i % R])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    kevs = [{k: (ev(), ev()) for k in kernels} for _ in range(args.steps)]
+    start, end = ev(), ev()
+    for e in [start, end] + [x for row in evs for x in row] + \
+             [x for d in kevs for pair in d.values() for x in pair]:
+        e.record()   # create every event before the timed region
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(sets[i % R], evs[i])
+        step(sets[i % R], evs[i], kevs[i])
     end.record()
     torch.cuda.synchronize()
+    for k in kernels:
+        zn.debug_kernel_events(k, None, None)
     total_ms = start.elapsed_time(end)
     comp_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    kern_ms = {k: [d[k][0].elapsed_time(d[k][1]) for d in kevs] for k in kernels}
 
     # every buffer set must hold an exact round trip and report no error
     for s in sets:
@@ -174,14 +251,19 @@ def main():
         v = sorted(v)
         return v[len(v) // 2]
 
-    algo = nbytes + unc   # bytes a pass must read and write
+    raw_planes = unc // 2 if base[0].element_size() == 2 else (unc // 8 if base[0].element_size() == 1 else 0)
+    # algorithmic bytes per launch: what each kernel must read and write
+    algo = {"decode": nbytes + unc,                       # container in, tensors out
+            "analyze": unc + raw_planes,                  # tensors in, always-raw planes out
+            "pack": unc + (nbytes - raw_planes)}          # tensors in, coded records out
     rl = {}
-    for name, ms in (("decompress", med(dec_ms)), ("compress", med(comp_ms))):
-        gbps = algo / (ms * 1e-3) / 1e9
-        rl[name] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                    "kernel_ms": round(ms, 4)}
-    dominant = max(rl, key=lambda k: rl[k]["kernel_ms"])
+    for k in kernels:
+        avg = sum(kern_ms[k]) / len(kern_ms[k])
+        gbps = algo[k] / (avg * 1e-3) / 1e9
+        rl[k] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(k, args.workload),
+                 "kernel": f"k_{k}", "avg_ms": round(avg, 4), "algorithmic_bytes": algo[k]}
+    dominant = max(rl, key=lambda k: rl[k]["avg_ms"])
     ms_step = total_ms / args.steps
     value = unc / (ms_step * 1e-3) / 1e9
     line = {
@@ -198,13 +280,12 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "uncompressed_bytes": unc,
-                   "container_bytes": nbytes, "chunk_bytes": 262144, "tensors": len(base)},
+                   "container_bytes": nbytes, "chunk_bytes": CHUNK_BYTES, "tensors": len(base)},
         "decompress_GBps": round(unc / (med(dec_ms) * 1e-3) / 1e9, 2),
         "compress_GBps": round(unc / (med(comp_ms) * 1e-3) / 1e9, 2),
         "ratio": round(nbytes / unc, 5),
-        "roofline": {k: v for k, v in rl[dominant].items() if k != "kernel_ms"} | {"kernel": dominant},
-        "roofline_decompress": rl["decompress"],
-        "roofline_compress": rl["compress"],
+        "roofline": {k: v for k, v in rl[dominant].items() if k not in ("avg_ms", "algorithmic_bytes")},
+        "kernels": rl,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(base)

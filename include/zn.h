@@ -152,6 +152,15 @@ zn_status zn_debug_histograms(const zn_tableset *ts, const void *const *d_in_ptr
 zn_status zn_debug_code_lengths(const uint64_t *d_hist, int n, int alphabet, int group_rule,
                                 uint8_t *d_len, hipStream_t stream);
 
+/* ---- kernel timing, for measurement tools ----
+ * zn_debug_kernel_events: from now on, record the HIP events `before` and
+ *   `after` (hipEvent_t, owned by the caller) on the call's stream right
+ *   before and right after every launch of the named kernel: "analyze",
+ *   "finish", "pack" (compression), "check", "decode" (decompression).
+ *   NULL events stop the recording for that kernel.  Process-wide, not
+ *   thread-safe; ZN_ERR_ARG for an unknown name. */
+zn_status zn_debug_kernel_events(const char *kernel, void *before, void *after);
+
 #ifdef __cplusplus
 }
 #endif

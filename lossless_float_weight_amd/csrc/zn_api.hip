@@ -17,6 +17,25 @@
 
 using namespace zn;
 
+// Events recorded around kernel launches (zn_debug_kernel_events).
+namespace {
+const char *const kKernelNames[] = {"analyze", "finish", "pack", "check", "decode"};
+enum { KAnalyze, KFinish, KPack, KCheck, KDecode, KCount };
+hipEvent_t g_ev_before[KCount], g_ev_after[KCount];
+
+// Runs one launch between the events registered for it, if any.
+template <class F>
+hipError_t timed(int k, hipStream_t s, F launch) {
+  if (g_ev_before[k]) {
+    const hipError_t e = hipEventRecord(g_ev_before[k], s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch();
+  if (e != hipSuccess || !g_ev_after[k]) return e;
+  return hipEventRecord(g_ev_after[k], s);
+}
+}  // namespace
+
 struct zn_tableset {
   int dtype = 0, T = 0, K = 0;
   uint32_t chunk_bytes = 0, chunk_elems = 0, n_chunks = 0;
@@ -399,7 +418,7 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   a.out = static_cast<uint8_t *>(d_out);
   a.plans = scr + plans_offset(ts);
   a.sizes = reinterpret_cast<unsigned long long *>(scr + sizes_offset());
-  HIPCHK(launch_analyze(ts->dtype, a, stream));
+  HIPCHK(timed(KAnalyze, stream, [&] { return launch_analyze(ts->dtype, a, stream); }));
   FinishArgs f;
   f.L = a.L;
   f.dtype = ts->dtype;
@@ -409,14 +428,14 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   f.cap = out_cap;
   f.sizes = a.sizes;
   f.ctl = ctl;
-  HIPCHK(launch_finish(f, stream));
+  HIPCHK(timed(KFinish, stream, [&] { return launch_finish(f, stream); }));
   PackArgs pk;
   pk.L = a.L;
   pk.in_ptrs = a.in_ptrs;
   pk.plans = a.plans;
   pk.out = a.out;
   pk.ctl = ctl;
-  HIPCHK(launch_pack(ts->dtype, pk, stream));
+  HIPCHK(timed(KPack, stream, [&] { return launch_pack(ts->dtype, pk, stream); }));
   if (!out_bytes) return ZN_OK;
   uint32_t flag = 0;
   uint64_t total = 0;
@@ -447,7 +466,7 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
   ck.n_chunks = ts->n_chunks;
   ck.off_dir = ts->off_dir;
   ck.ctl = ctl;
-  HIPCHK(launch_check(ck, stream));
+  HIPCHK(timed(KCheck, stream, [&] { return launch_check(ck, stream); }));
   DecArgs a;
   a.L = dev_layout(ts);
   a.in = ck.in;
@@ -457,7 +476,7 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
   a.group_len = ts->d_len;
   a.K = ts->K;
   a.ctl = ctl;
-  HIPCHK(launch_decode(ts->dtype, a, stream));
+  HIPCHK(timed(KDecode, stream, [&] { return launch_decode(ts->dtype, a, stream); }));
   if (!sync) return ZN_OK;
   uint32_t flag = 0;
   HIPCHK(hipMemcpyAsync(&flag, ctl, 4, hipMemcpyDeviceToHost, stream));
@@ -550,6 +569,18 @@ zn_status zn_debug_code_lengths(const uint64_t *d_hist, int n, int alphabet, int
     return ZN_ERR_ARG;
   HIPCHK(launch_lengths(d_hist, n, alphabet, group_rule, d_len, stream));
   return ZN_OK;
+}
+
+zn_status zn_debug_kernel_events(const char *kernel, void *before, void *after) {
+  if (!kernel) return ZN_ERR_ARG;
+  for (int k = 0; k < KCount; k++) {
+    if (strcmp(kernel, kKernelNames[k]) == 0) {
+      g_ev_before[k] = static_cast<hipEvent_t>(before);
+      g_ev_after[k] = static_cast<hipEvent_t>(after);
+      return ZN_OK;
+    }
+  }
+  return ZN_ERR_ARG;
 }
 
 }  // extern "C"

@@ -59,10 +59,12 @@ def lib() -> C.CDLL:
         L.zn_status_str.restype = C.c_char_p
         L.zn_debug_histograms.argtypes = [P, P, P, P]
         L.zn_debug_code_lengths.argtypes = [P, I, I, I, P, P]
+        L.zn_debug_kernel_events.argtypes = [C.c_char_p, P, P]
         for f in ("zn_setup", "zn_plan_from_container", "zn_tableset_info", "zn_compress_bound",
                   "zn_scratch_bytes", "zn_compress", "zn_decompress", "zn_tableset_save",
                   "zn_tableset_load", "zn_tableset_lengths", "zn_tableset_map",
-                  "zn_tableset_cost_history", "zn_debug_histograms", "zn_debug_code_lengths"):
+                  "zn_tableset_cost_history", "zn_debug_histograms", "zn_debug_code_lengths",
+                  "zn_debug_kernel_events"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -254,3 +256,16 @@ def debug_code_lengths(hist: torch.Tensor, alphabet: int = 256, group_rule: bool
                                        _stream(stream)), "code_lengths")
     torch.cuda.synchronize()
     return out
+
+
+def debug_kernel_events(kernel: str, before=None, after=None) -> None:
+    """zn_debug_kernel_events with torch.cuda.Event objects (None stops the
+    recording for that kernel).  Events not yet created are created here."""
+    def handle(e):
+        if e is None:
+            return None
+        if not e.cuda_event:
+            e.record()
+        return C.c_void_p(e.cuda_event)
+    _check(lib().zn_debug_kernel_events(kernel.encode(), handle(before), handle(after)),
+           "kernel_events")

@@ -41,3 +41,13 @@ def test_status_strings_and_argument_errors_need_no_gpu():
     assert lib.zn_setup(0, None, n, 1, 1000, 0, None, ctypes.byref(out)) == -1   # bad chunk size
     assert lib.zn_setup(7, None, n, 1, 262144, 0, None, ctypes.byref(out)) == -1  # bad dtype
     assert lib.zn_compress(None, None, None, 0, None, None, 0, None) == -1
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libzn.so not built")
+def test_kernel_event_names_need_no_gpu():
+    lib = ctypes.CDLL(LIB)
+    lib.zn_debug_kernel_events.argtypes = [ctypes.c_char_p, ctypes.c_void_p, ctypes.c_void_p]
+    for name in (b"analyze", b"finish", b"pack", b"check", b"decode"):
+        assert lib.zn_debug_kernel_events(name, None, None) == 0
+    assert lib.zn_debug_kernel_events(b"encode", None, None) == -1
+    assert lib.zn_debug_kernel_events(None, None, None) == -1
