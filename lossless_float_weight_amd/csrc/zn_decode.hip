@@ -23,7 +23,7 @@ namespace zn {
 constexpr int DEC_NT = 256;
 constexpr int RND = 32;        // symbols per lane per round = one strip of its segment
 constexpr int STWW = 10;       // staging words per lane: a strip and up to 5 symbols more
-constexpr int RING = 16;       // words of a lane's payload window in LDS
+constexpr int RING = 32;       // words of a lane's payload window in LDS: two 64-byte sectors
 // Staging and ring are lane-interleaved (word w of thread t at w * DEC_NT + t),
 // so lanes that touch different words of their own areas still hit
 // different LDS banks.
@@ -191,30 +191,39 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     __syncthreads();
 
     // Bit reader: a 64-bit window (LSB-first) refilled one word at a time
-    // from the lane's ring of payload words in LDS.  Words reach the ring in
-    // 16-byte groups loaded one round before they can be needed.
+    // from the lane's ring of payload words in LDS.  The ring holds two
+    // 64-byte sectors of the payload, aligned in memory so that every sector
+    // is one HBM burst read once; a sector is loaded one round before it can
+    // be needed.  Word positions count from the aligned base pay64.
     uint64_t buf = 0;
     int nb = 0;
-    uint32_t wpos = 0, wf = 0, pre = 0;  // next word to read, first word not fetched
-    u32x4 pq0 = {0, 0, 0, 0}, pq1 = pq0, pq2 = pq0;
-    uint32_t pend_g = 0;
-    int pend_n = 0;
-    auto grp = [&](uint32_t gi) { return ldg16(pay + 16ull * (gi < ngroups ? gi : ngroups - 1)); };
-    auto put_group = [&](uint32_t gi, const u32x4 &x) {  // payload group gi into its ring slot
-      uint32_t *q = rp + 4 * (gi & 3) * DEC_NT;
-      q[0] = x[0];
-      q[DEC_NT] = x[1];
-      q[2 * DEC_NT] = x[2];
-      q[3 * DEC_NT] = x[3];
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(pay);
+    const uint8_t *pay64 = pay - (pa & 63);       // inside the container: pay is past the header
+    const uint32_t adj = uint32_t(pa & 63) / 4;   // payload word 0 is window word adj
+    const uint32_t glast = adj / 4 + ngroups - 1; // last 16-byte group holding payload
+    uint32_t wpos = 0, nsec = 0, pre = 0;         // next word to read, next sector to fetch
+    u32x4 ps0 = {0, 0, 0, 0}, ps1 = ps0, ps2 = ps0, ps3 = ps0;
+    bool pend = false;
+    // 16-byte group gi of the window; groups past the payload read its last one
+    auto grp = [&](uint32_t gi) { return ldg16(pay64 + 16ull * (gi < glast ? gi : glast)); };
+    auto put_sector = [&](uint32_t sc, const u32x4 &x0, const u32x4 &x1, const u32x4 &x2,
+                          const u32x4 &x3) {
+      uint32_t *q = rp + (sc & 1) * 16 * DEC_NT;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        q[k * DEC_NT] = x0[k];
+        q[(4 + k) * DEC_NT] = x1[k];
+        q[(8 + k) * DEC_NT] = x2[k];
+        q[(12 + k) * DEC_NT] = x3[k];
+      }
     };
     if (coded && live) {
-      const uint32_t w0 = b0 >> 5, g0 = w0 >> 2;
-      const u32x4 a0 = grp(g0), a1 = grp(g0 + 1), a2 = grp(g0 + 2), a3 = grp(g0 + 3);
-      put_group(g0, a0);
-      put_group(g0 + 1, a1);
-      put_group(g0 + 2, a2);
-      put_group(g0 + 3, a3);
-      wf = 4 * (g0 + 4);
+      const uint32_t w0 = (b0 >> 5) + adj, s0 = w0 >> 4;
+      const u32x4 a0 = grp(4 * s0), a1 = grp(4 * s0 + 1), a2 = grp(4 * s0 + 2), a3 = grp(4 * s0 + 3);
+      const u32x4 a4 = grp(4 * s0 + 4), a5 = grp(4 * s0 + 5), a6 = grp(4 * s0 + 6), a7 = grp(4 * s0 + 7);
+      put_sector(s0, a0, a1, a2, a3);
+      put_sector(s0 + 1, a4, a5, a6, a7);
+      nsec = s0 + 2;
       buf = rp[(w0 & (RING - 1)) * DEC_NT] | (uint64_t(rp[((w0 + 1) & (RING - 1)) * DEC_NT]) << 32);
       wpos = w0 + 2;
       buf >>= (b0 & 31);
@@ -257,12 +266,10 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       const int lim = live && q < nstrips ? int(min(uint32_t(RND), n - q * RND)) : 0;
       const bool last = live && q < nstrips && q + nseg >= nstrips;
       // groups fetched last round enter the ring
-      if (pend_n > 0) {
-        put_group(pend_g, pq0);
-        if (pend_n > 1) put_group(pend_g + 1, pq1);
-        if (pend_n > 2) put_group(pend_g + 2, pq2);
-        wf = 4 * (pend_g + pend_n);
-        pend_n = 0;
+      if (pend) {
+        put_sector(nsec, ps0, ps1, ps2, ps3);
+        nsec++;
+        pend = false;
       }
       if (lim > 0) {
         if (coded) {
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           ov = pos - lim;   // at most 5: the loop stops 2 lookups of 3 symbols past lim - 1
           if (last) {
             // exact end: the segment must use exactly its stored bit length
-            uint64_t bpos = uint64_t(wpos) * 32 - uint32_t(nb);
+            uint64_t bpos = uint64_t(wpos - adj) * 32 - uint32_t(nb);
             for (int x = 0; x < ov; x++) {
               const int b = lim + x;
               bpos -= sh.len[p][(sp[(b >> 2) * DEC_NT] >> (8 * (b & 3))) & 0xFF];
@@ -326,17 +333,16 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             if (bpos != uint64_t(b0) + sbits) bad = 1;
             ov = 0;
           } else {
-            // lim == RND here.  Fetch the groups the next round may need: a
-            // round reads at most 32 lookups (352 bits) with at least 10
-            // bits left in the window, so words [wpos, wpos + 12).
-            const uint32_t needg = (wpos + 12 + 3) / 4;
-            const uint32_t have = wf / 4;
-            if (needg > have) {
-              pend_g = have;
-              pend_n = int(needg - have);
-              pq0 = grp(pend_g);
-              pq1 = grp(pend_g + 1);   // loaded even when unused: see load_raw
-              pq2 = grp(pend_g + 2);
+            // lim == RND here.  The next round reads at most 32 lookups
+            // (352 bits) with at least 10 bits left in the window, so words
+            // [wpos, wpos + 12): at most one sector past those in the ring,
+            // whose slot held a sector before wpos's.
+            if (((wpos + 11) >> 4) >= nsec) {
+              ps0 = grp(4 * nsec);
+              ps1 = grp(4 * nsec + 1);
+              ps2 = grp(4 * nsec + 2);
+              ps3 = grp(4 * nsec + 3);
+              pend = true;
             }
           }
         } else if (mode == RAW) {
