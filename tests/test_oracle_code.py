@@ -159,3 +159,18 @@ def test_canonical_prefix_free_and_ordered(oracle):
         for l in set(ln.tolist()) - {0}:
             cs = [int(codes[s]) for s in range(len(ln)) if ln[s] == l]
             assert cs == list(range(cs[0], cs[0] + len(cs)))
+
+
+def test_length_limit_costs_little_on_weight_exponents(oracle):
+    # exponents of N(0, sigma) BF16 chunks: the 11-bit limit binds (unlimited
+    # Huffman trees are 14-16 deep) but adds under 0.2% to the coded bits
+    import torch
+    for sigma in (0.008, 0.02, 0.03):
+        g = torch.Generator().manual_seed(int(sigma * 1e4))
+        x = (torch.randn(131072, dtype=torch.float64, generator=g) * sigma).to(torch.bfloat16)
+        e = ((x.view(torch.int16).numpy().astype(np.uint16) >> 7) & 0xFF).astype(np.int64)
+        h = np.bincount(e, minlength=256).astype(np.uint64)
+        ln = oracle.code_lengths(h, max_len=11)
+        free = ref_tiny.huffman_cost([int(v) for v in h if v])
+        assert ln.max() <= 11 and ref_tiny.huffman_depth([int(v) for v in h if v]) > 11
+        assert free <= _cost(h, ln) <= free * 1.002
