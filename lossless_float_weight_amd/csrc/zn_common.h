@@ -76,6 +76,14 @@ __device__ __forceinline__ u32x2 ldg8(const void *p) { return *(const ZN_GLOBAL 
 __device__ __forceinline__ uint32_t ldg4(const void *p) { return *(const ZN_GLOBAL uint32_t *)(p); }
 __device__ __forceinline__ uint32_t ldg2(const void *p) { return *(const ZN_GLOBAL uint16_t *)(p); }
 __device__ __forceinline__ uint32_t ldg1(const void *p) { return *(const ZN_GLOBAL uint8_t *)(p); }
+// Streaming loads of data read once: the non-temporal hint keeps them from
+// displacing reused lines in the caches.
+__device__ __forceinline__ u32x4 ldg16s(const void *p) {
+  return __builtin_nontemporal_load((const ZN_GLOBAL u32x4 *)(p));
+}
+__device__ __forceinline__ u32x2 ldg8s(const void *p) {
+  return __builtin_nontemporal_load((const ZN_GLOBAL u32x2 *)(p));
+}
 __device__ __forceinline__ void stg16(void *p, u32x4 v) { *(ZN_GLOBAL u32x4 *)(p) = v; }
 __device__ __forceinline__ void stg8(void *p, u32x2 v) { *(ZN_GLOBAL u32x2 *)(p) = v; }
 __device__ __forceinline__ void stg4(void *p, uint32_t v) { *(ZN_GLOBAL uint32_t *)(p) = v; }

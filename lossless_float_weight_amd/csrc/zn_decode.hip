@@ -244,7 +244,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         const uint32_t ev = (uint32_t(r) * nseg + sjv) * RND + part * VE;
         const bool ok = sjv < nseg && ev < n;
         if constexpr (DT == BF16) {
-          const u32x2 x = ldg8(rawp + (ok ? ev : 0));
+          const u32x2 x = ldg8s(rawp + (ok ? ev : 0));
           rv[i] = x[0] | (uint64_t(x[1]) << 32);
         } else if constexpr (DT == FP8) {
           rv[i] = ldg2(rawp + (ok ? ev / 8 : 0));

@@ -258,3 +258,37 @@ def test_config4_fp8_full_size_sampled(oracle):
     ts, blob = gpu_compress(tensors, 262144)
     _sampled_record_parity(oracle, oracle.FP8_E4M3, tensors, blob, 262144)
     assert_roundtrip(ts, blob, tensors)
+
+
+@pytest.mark.slow
+def test_config5_full_model_grouped(oracle):
+    """Full 8B-shaped model + KV cache (290 tensors, 9.65e9 BF16 values):
+    the K = 16 setup on the GPU equals the oracle's on the same data; the
+    perturbed copy compressed with that setup unchanged matches the oracle's
+    records on sampled chunks and round-trips exactly."""
+    import time
+    t0 = time.time()
+    print("case: full model 290 tensors, K=16 setup, perturbed reuse", flush=True)
+    named = W.model_bf16("cuda", seed=5)
+    tensors = [t for _, t in named]
+    print(f"  generated {sum(t.numel() for t in tensors)} values in {time.time() - t0:.0f} s", flush=True)
+    ts = zn.setup(tensors, chunk_bytes=262144, n_groups=16)
+    torch.cuda.synchronize()
+    print(f"  GPU setup done at {time.time() - t0:.0f} s", flush=True)
+    arrs = [to_np(t) for t in tensors]
+    ots = oracle.setup(oracle.BF16, arrs, 262144, 16)
+    print(f"  oracle setup done at {time.time() - t0:.0f} s", flush=True)
+    assert ts.group_map() == ots.group_map().tolist()
+    for g in range(16):
+        assert ts.lengths(g) == ots.lengths(g).tolist()
+    assert ts.hash == ots.hash and ts.save() == ots.save()
+    assert ts.cost_history() == [int(v) for v in ots.cost_history()]
+    del arrs
+    pert = [t for _, t in W.perturbed_model(named, seed=5)]
+    del named, tensors
+    _, blob = gpu_compress(pert, 262144, ts)
+    print(f"  perturbed copy compressed at {time.time() - t0:.0f} s, ratio "
+          f"{blob.numel() / (2 * sum(t.numel() for t in pert)):.5f}", flush=True)
+    _sampled_record_parity(oracle, oracle.BF16, pert, blob, 262144, k=24, ts=ts)
+    assert_roundtrip(ts, blob, pert)
+    print(f"  done at {time.time() - t0:.0f} s", flush=True)
