@@ -48,6 +48,9 @@ WORKLOADS = {
             "256 KiB chunks",
     "fp8": "FP8 E4M3 1,073,741,824 values, N(0,1) scaled per 128-element block to max 448, "
            "256 KiB chunks",
+    "model": "8B-shaped BF16 model: 32 blocks as in 'block' + embedding 128256x4096 N(0, 0.02) + KV cache "
+             "[32,2,8,32768,128] N(0,1) = 9,652,404,224 values; setup with 16 shared-table groups on it, "
+             "steps on a perturbed copy (weights + N(0, 1e-4)) with that setup unchanged; 256 KiB chunks",
 }
 
 # kernel -> sources whose text decides its code (for the counter files' hash)
@@ -90,6 +93,8 @@ def make_tensors(name: str):
         return [t for _, t in W.fp32_pair(1 << 27, device="cuda")]
     if name == "fp8":
         return [t for _, t in W.fp8_blockscaled(1 << 30, device="cuda")]
+    if name == "model":
+        return [t for _, t in W.model_bf16("cuda", seed=5)]
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -101,21 +106,21 @@ def cpu_baseline(tensors, budget_s: float = 20.0):
     from lossless_float_weight_amd import workloads as W
     from oracle import zno
     dt = {2: zno.BF16, 4: zno.FP32, 1: zno.FP8_E4M3}[tensors[0].element_size()]
-    arrs = [W.bits(t).reshape(-1).cpu().numpy() for t in tensors]
+    esz = tensors[0].element_size()
     # calibrate on 4 MiB, then take whole tensors (and a slice of the last) up to the budget
-    probe = arrs[0][: (4 << 20) // arrs[0].itemsize] if arrs[0].nbytes > (4 << 20) else arrs[0]
+    first = W.bits(tensors[0]).reshape(-1)
+    probe = first[: (4 << 20) // esz].cpu().numpy()
     t0 = time.perf_counter()
     b = zno.compress(dt, [probe])
     zno.decompress(b, [probe.size], dt)
     rate = probe.nbytes / max(time.perf_counter() - t0, 1e-6)
     want = rate * budget_s
     sample, nbytes = [], 0
-    for a in arrs:
+    for t in tensors:
         if nbytes >= want:
             break
-        take = min(a.size, int((want - nbytes) // a.itemsize))
-        take = max(take, 1)
-        sample.append(np.ascontiguousarray(a[:take]))
+        take = max(1, min(t.numel(), int((want - nbytes) // esz)))
+        sample.append(np.ascontiguousarray(W.bits(t).reshape(-1)[:take].cpu().numpy()))
         nbytes += sample[-1].nbytes
     t0 = time.perf_counter()
     blob = zno.compress(dt, sample)
@@ -178,9 +183,22 @@ def main():
     torch.cuda.set_device(0)
     base = make_tensors(args.workload)
     unc = sum(t.numel() * t.element_size() for t in base)
-    ts = zn.setup(base, chunk_bytes=CHUNK_BYTES)
+    extra = {}
+    if args.workload == "model":
+        # the reusable setup: groups and shared tables from the model, then
+        # every step compresses a perturbed copy with that setup unchanged
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ts = zn.setup(base, chunk_bytes=CHUNK_BYTES, n_groups=16)
+        torch.cuda.synchronize()
+        extra["setup_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        names = [f"t{i}" for i in range(len(base))]
+        base = [t for _, t in W.perturbed_model(list(zip(names, base)), seed=5)]
+        torch.cuda.synchronize()
+    else:
+        ts = zn.setup(base, chunk_bytes=CHUNK_BYTES)
     bound = zn.compress_bound(ts)
-    R = max(1, args.rotate)
+    R = max(1, args.rotate if args.workload != "model" else 1)
     sets = []
     for r in range(R):
         ins = base if r == 0 else [t.clone() for t in base]
@@ -287,6 +305,29 @@ def main():
         "roofline": {k: v for k, v in rl[dominant].items() if k not in ("avg_ms", "algorithmic_bytes")},
         "kernels": rl,
     }
+    if args.workload == "model":
+        # the same compression with per-chunk tables (no setup), for the
+        # post-setup speed-up the reusable setup is about
+        plain = zn.setup(base, chunk_bytes=CHUNK_BYTES)
+        pscr = zn.new_scratch(plain)
+        pblob = torch.empty(zn.compress_bound(plain), dtype=torch.uint8, device="cuda")
+        ptrs = sets[0]["in_ptrs"]
+        for _ in range(2):
+            zn.compress(plain, base, out=pblob, scratch=pscr, ptrs=ptrs, sync=False)
+        pe = [[ev(), ev()] for _ in range(5)]
+        for a, b in pe:
+            a.record()
+            zn.compress(plain, base, out=pblob, scratch=pscr, ptrs=ptrs, sync=False)
+            b.record()
+        torch.cuda.synchronize()
+        per_chunk_ms = med([a.elapsed_time(b) for a, b in pe])
+        pbytes = int(pblob[56:64].cpu().numpy().view("<u8")[0])
+        extra.update({"post_setup_compress_ms": round(med(comp_ms), 3),
+                      "per_chunk_table_compress_ms": round(per_chunk_ms, 3),
+                      "post_setup_speedup": round(per_chunk_ms / med(comp_ms), 3),
+                      "per_chunk_table_ratio": round(pbytes / unc, 5)})
+        del pblob, pscr
+    line.update(extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(base)
     print(json.dumps(line), flush=True)
