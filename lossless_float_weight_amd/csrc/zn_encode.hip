@@ -120,13 +120,19 @@ struct EncShared {
   } u;
 };
 
+// Segments per wave in one pack tile: 16 symbols per lane per tile (more
+// per tile holds fewer workgroups per CU than the chunks need).
+constexpr int pack_g(int dt) { return segsyms(dt) / 64 >= 16 ? 1 : 16 / (segsyms(dt) / 64); }
+
 template <int DT>
 struct PackShared {
   static constexpr int NC = ncoded(DT);
-  static constexpr int STAGE = (PACK_NW * segsyms(DT) * kMaxLen + 31) / 32 + 4;  // words of a tile
+  static constexpr int G = pack_g(DT);
+  // words of one tile at the longest codes, plus slack for the group ORs
+  static constexpr int STAGE = (PACK_NW * G * segsyms(DT) * kMaxLen + 31) / 32 + 4;
   uint32_t enc[NC][256];
-  uint32_t stage[STAGE];
-  uint32_t wtot[PACK_NW];
+  uint32_t stage[2][STAGE];      // alternate tiles use alternate buffers
+  uint32_t wtot[2][PACK_NW];
 };
 
 template <int DT>
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
   constexpr int NV = EPT / VE;         // vectors per thread per tile
-  constexpr int NW = PACK_NW, ENC_NT = PACK_NT;
+  constexpr int NW = PACK_NW, ENC_NT = PACK_NT, G = PackShared<DT>::G;
   constexpr int STAGE = PackShared<DT>::STAGE;
   __shared__ PackShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
@@ -415,6 +421,7 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
       sh.enc[p][tid] = mode == RAW ? uint32_t(tid) | (uint32_t(k) << 16)
                      : (mode == HUFF || mode == GROUP) ? ldg4(plan + 64 + 1024 * p + 4 * tid) : 0u;
   }
+  for (int i = tid; i < 2 * STAGE; i += ENC_NT) sh.stage[i / STAGE][i % STAGE] = 0;
   __syncthreads();
 
   // -------------------------------------------------------- the record
@@ -442,119 +449,144 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     uint16_t *segt = reinterpret_cast<uint16_t *>(sec + 8 + (mode == HUFF ? A / 2 : 0));
     const bool with_segs = mode != RAW;
     uint64_t tbit = 0;     // stream bits before this tile
-    uint32_t carry = 0;    // partial last word of the previous tile
-    // Huffman-coded streams: wave w of tile T packs segment j = NW*T + w, whose
-    // symbols are the 32-symbol strips j, j + nseg, ... of the chunk; lane l
-    // takes symbols [l*EPT, l*EPT + EPT) of the segment, which lie in one
-    // strip.  Raw streams are packed in element order.
-    const int ntiles = (nseg + NW - 1) / NW;
-    auto tile_eb = [&](int T) -> uint32_t {  // first element of this lane's run in tile T
+    // Huffman-coded streams: tile T holds NW*G consecutive segments; wave w
+    // packs segments J = (T*NW + w)*G + g, g < G, whose symbols are the
+    // 32-symbol strips J, J + nseg, ... of the chunk; lane l takes symbols
+    // [l*EPT, l*EPT + EPT) of each, which lie in one strip.  Raw streams are
+    // packed in element order as if cut into segments of S elements.
+    const int ntiles = (nseg + NW * G - 1) / (NW * G);
+    auto seg_eb = [&](int J) -> uint32_t {  // first element of this lane's run in segment J
       if (with_segs) {
-        const int jseg = T * NW + wv;
-        if (jseg >= nseg) return n;  // no symbols in this lane
+        if (J >= nseg) return n;  // no symbols in this lane
         const uint32_t si = uint32_t(ln) * EPT;
-        return 32u * ((si / 32) * uint32_t(nseg) + uint32_t(jseg)) + si % 32;
+        return 32u * ((si / 32) * uint32_t(nseg) + uint32_t(J)) + si % 32;
       }
-      return uint32_t(T) * uint32_t(NW * S) + uint32_t(tid) * EPT;
+      return uint32_t(J) * uint32_t(S) + uint32_t(ln) * EPT;
     };
     // the next tile's 16-byte vectors are loaded one tile ahead
-    u32x4 nq[NV];
-    uint32_t neb = tile_eb(0);
-    if (aligned && neb + EPT <= n) {
+    u32x4 nq[G][NV];
+    uint32_t neb[G];
+    auto issue = [&](int T) {
 #pragma unroll
-      for (int j = 0; j < NV; j++) nq[j] = ldg16(src + uint64_t(neb) * ES + 16 * j);
-    }
-    for (int T = 0; T < ntiles; T++) {
-      const int jseg = T * NW + wv;
-      const uint32_t eb = neb;
-      const bool vec = aligned && eb + EPT <= n;
-      uint32_t w[EPT];
-      if (vec) {
+      for (int g = 0; g < G; g++) {
+        neb[g] = seg_eb((T * NW + wv) * G + g);
+        if (aligned && neb[g] + EPT <= n) {
 #pragma unroll
-        for (int j = 0; j < NV; j++) {
-          const uint4 q = make_uint4(nq[j][0], nq[j][1], nq[j][2], nq[j][3]);
-#pragma unroll
-          for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
+          for (int j = 0; j < NV; j++) nq[g][j] = ldg16(src + uint64_t(neb[g]) * ES + 16 * j);
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < EPT; i++)
-          w[i] = eb + i < n ? load_elem<DT>(src + uint64_t(eb + i) * ES) : 0;
       }
-      // Concatenate the thread's codes 8 at a time without branches: pairs
-      // fit 22 bits, quads 44 bits (one u64), two quads 88 bits (lo | hi<<64).
+    };
+    issue(0);
+    for (int T = 0; T < ntiles; T++) {
+      const int buf = T & 1;
+      uint32_t *stage = sh.stage[buf];
+      // Concatenate each run's codes 8 at a time without branches: pairs fit
+      // 22 bits, quads 44 bits (one u64), two quads 88 bits (lo | hi<<64).
       constexpr int NG = EPT / 8;
-      uint64_t glo[NG];
-      uint32_t ghi[NG];
-      int gb[NG];
-      int nb = 0;
+      uint64_t glo[G][NG];
+      uint32_t ghi[G][NG];
+      uint32_t gb[G][NG], nb[G];
 #pragma unroll
-      for (int g8 = 0; g8 < NG; g8++) {
-        uint32_t v[8], l[8];
+      for (int g = 0; g < G; g++) {
+        const uint32_t eb = neb[g];
+        const bool vec = aligned && eb + EPT <= n;
+        uint32_t w[EPT];
+        if (vec) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const int e = g8 * 8 + i;
-          const uint32_t c = eb + e < n ? sh.enc[p][field_rt<DT>(w[e], p)] : 0u;
-          v[i] = c & 0xFFFF;
-          l[i] = c >> 16;
+          for (int j = 0; j < NV; j++) {
+            const uint4 q = make_uint4(nq[g][j][0], nq[g][j][1], nq[g][j][2], nq[g][j][3]);
+#pragma unroll
+            for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPT; i++)
+            w[i] = eb + i < n ? load_elem<DT>(src + uint64_t(eb + i) * ES) : 0;
         }
-        const uint32_t c01 = v[0] | (v[1] << l[0]), l01 = l[0] + l[1];
-        const uint32_t c23 = v[2] | (v[3] << l[2]), l23 = l[2] + l[3];
-        const uint32_t c45 = v[4] | (v[5] << l[4]), l45 = l[4] + l[5];
-        const uint32_t c67 = v[6] | (v[7] << l[6]), l67 = l[6] + l[7];
-        const uint64_t q0 = uint64_t(c01) | (uint64_t(c23) << l01);
-        const uint64_t q1 = uint64_t(c45) | (uint64_t(c67) << l45);
-        const uint32_t L0 = l01 + l23, L1 = l45 + l67;
-        glo[g8] = q0 | (q1 << L0);
-        ghi[g8] = L0 ? uint32_t(q1 >> (64 - L0)) : 0u;
-        gb[g8] = int(L0 + L1);
-        nb += gb[g8];
+        nb[g] = 0;
+#pragma unroll
+        for (int g8 = 0; g8 < NG; g8++) {
+          uint32_t v[8], l[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            const int e = g8 * 8 + i;
+            const uint32_t c = eb + e < n ? sh.enc[p][field_rt<DT>(w[e], p)] : 0u;
+            v[i] = c & 0xFFFF;
+            l[i] = c >> 16;
+          }
+          const uint32_t c01 = v[0] | (v[1] << l[0]), l01 = l[0] + l[1];
+          const uint32_t c23 = v[2] | (v[3] << l[2]), l23 = l[2] + l[3];
+          const uint32_t c45 = v[4] | (v[5] << l[4]), l45 = l[4] + l[5];
+          const uint32_t c67 = v[6] | (v[7] << l[6]), l67 = l[6] + l[7];
+          const uint64_t q0 = uint64_t(c01) | (uint64_t(c23) << l01);
+          const uint64_t q1 = uint64_t(c45) | (uint64_t(c67) << l45);
+          const uint32_t L0 = l01 + l23, L1 = l45 + l67;
+          glo[g][g8] = q0 | (q1 << L0);
+          ghi[g][g8] = L0 ? uint32_t(q1 >> (64 - L0)) : 0u;
+          gb[g][g8] = L0 + L1;
+          nb[g] += gb[g][g8];
+        }
       }
       // issued once this tile's codes are computed, so no later wait for this
       // tile's data also waits for the next tile's loads
-      if (T + 1 < ntiles) {
-        neb = tile_eb(T + 1);
-        if (aligned && neb + EPT <= n) {
+      if (T + 1 < ntiles) issue(T + 1);
+      // bit offsets: a wave scan per segment; segments follow each other
+      uint32_t incl[G], segtot[G], wsum = 0;
 #pragma unroll
-          for (int j = 0; j < NV; j++) nq[j] = ldg16(src + uint64_t(neb) * ES + 16 * j);
-        }
+      for (int g = 0; g < G; g++) {
+        incl[g] = wave_incl_scan(nb[g]);
+        segtot[g] = uint32_t(__builtin_amdgcn_readlane(int(incl[g]), 63));
+        wsum += segtot[g];
       }
-      const uint32_t incl = wave_incl_scan(uint32_t(nb));
-      if (ln == 63) sh.wtot[wv] = incl;
-      for (int i = tid; i < STAGE; i += ENC_NT) sh.stage[i] = 0;
+      if (ln == 0) sh.wtot[buf][wv] = wsum;
       __syncthreads();
       uint32_t woff = 0, ttot = 0;
       for (int q = 0; q < NW; q++) {
-        const uint32_t x = sh.wtot[q];
+        const uint32_t x = sh.wtot[buf][q];
         woff += q < wv ? x : 0;
         ttot += x;
       }
-      if (with_segs && ln == 0 && jseg < nseg) stg2(segt + jseg, sh.wtot[wv]);
-      if (tid == 0 && carry) atomicOr(&sh.stage[0], carry);
-      uint32_t start = uint32_t(tbit & 31) + woff + incl - uint32_t(nb);
+      uint32_t base = uint32_t(tbit & 31) + woff;
 #pragma unroll
-      for (int g8 = 0; g8 < NG; g8++) {
-        // the 88-bit group shifted to its bit offset covers at most 4 words
-        const uint32_t sft = start & 31, wi = start >> 5;
-        const uint64_t t0 = glo[g8] << sft;
-        const uint64_t t1 = (uint64_t(ghi[g8]) << sft) | (sft ? glo[g8] >> (64 - sft) : 0ull);
-        if (gb[g8]) {
-          atomicOr(&sh.stage[wi], uint32_t(t0));
-          const uint32_t x1 = uint32_t(t0 >> 32), x2 = uint32_t(t1), x3 = uint32_t(t1 >> 32);
-          if (x1) atomicOr(&sh.stage[wi + 1], x1);
-          if (x2) atomicOr(&sh.stage[wi + 2], x2);
-          if (x3) atomicOr(&sh.stage[wi + 3], x3);
+      for (int g = 0; g < G; g++) {
+        const int J = (T * NW + wv) * G + g;
+        if (with_segs && ln == 0 && J < nseg) stg2(segt + J, segtot[g]);
+        uint32_t start = base + incl[g] - nb[g];
+#pragma unroll
+        for (int g8 = 0; g8 < NG; g8++) {
+          // the 88-bit group shifted to its bit offset covers at most 4 words;
+          // ORing zero words is harmless, so no lane branches
+          const uint32_t sft = start & 31, wi = start >> 5;
+          const uint64_t t0 = glo[g][g8] << sft;
+          const uint64_t t1 = (uint64_t(ghi[g][g8]) << sft) | (sft ? glo[g][g8] >> (64 - sft) : 0ull);
+          atomicOr(&stage[wi], uint32_t(t0));
+          atomicOr(&stage[wi + 1], uint32_t(t0 >> 32));
+          atomicOr(&stage[wi + 2], uint32_t(t1));
+          atomicOr(&stage[wi + 3], uint32_t(t1 >> 32));
+          start += gb[g][g8];
         }
-        start += uint32_t(gb[g8]);
+        base += segtot[g];
       }
       __syncthreads();
+      // store the whole words and clear them for the tile after next; the
+      // partial last word moves to word 0 of the next tile's (clear) buffer
       const uint32_t endb = uint32_t(tbit & 31) + ttot;
       const uint32_t nfull = endb >> 5;
       const uint64_t w0 = tbit >> 5;
-      for (uint32_t i = tid; i < nfull; i += ENC_NT) stg4(pw + w0 + i, sh.stage[i]);
-      carry = (endb & 31) ? sh.stage[nfull] : 0;
+      for (uint32_t i = tid; i < nfull; i += ENC_NT) {
+        stg4(pw + w0 + i, stage[i]);
+        stage[i] = 0;
+      }
+      if (tid == 0) {
+        sh.stage[buf ^ 1][0] = stage[nfull];
+        stage[nfull] = 0;
+      }
       tbit += ttot;
-      __syncthreads();
+    }
+    uint32_t carry = 0;   // the partial last word (thread 0 moved it and reads it back)
+    if (tid == 0) {
+      carry = sh.stage[ntiles & 1][0];
+      sh.stage[ntiles & 1][0] = 0;
     }
     // last partial word and the zero pad of the payload
     const uint64_t words = (tbit + 31) >> 5;
