@@ -280,15 +280,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Wave-private LDS of the one-wave package-merge.
 struct WaveCB {
   uint64_t lst[128];   // the current merged list
-  uint64_t srt[64];    // leaves sorted by (count, symbol)
+  uint64_t srt[64];    // present symbols' counts, in symbol order
+  uint64_t leaf[64];   // leaf weights sorted by (count, symbol)
+  uint64_t pk[64];     // the packages of the list being built
   uint8_t sym[64], ssym[64];
 };
 
 // The package-merge of pm_lengths (same lists, same tie rule, same result)
 // run by one wave when at most 64 symbols are present: leaf i lives in lane
-// i, list item j in lane j (j < 64) or lane j-64, and the rank of each item
-// in the merged list is counted against the other list's items read one by
-// one from lane registers, so no workgroup barrier is needed.
+// i, list item j in lane j (j < 64) or lane j-64.  Both inputs of each merge
+// are sorted, so each item's rank in the merged list comes from a binary
+// search of the other input in LDS; no workgroup barrier is needed.
 // Returns d (after the group rule), or -1 when more than 64 symbols are
 // present (the workgroup version must run).  Every lane of the wave calls it.
 template <class WT>
@@ -342,6 +344,7 @@ __device__ int wave_pm_lengths(const WT *hist, int A, bool group_rule, uint8_t *
   wave_lds_sync();
   const uint64_t lw = ln < d ? W.lst[ln] : ~0ull;
   const int lsym = ln < d ? W.ssym[ln] : 0;
+  if (ln < d) W.leaf[ln] = lw;
   uint64_t c0 = lw, c1 = 0;
   int ncur = d;
   int lp[kMaxLen];
@@ -353,9 +356,18 @@ __device__ int wave_pm_lengths(const WT *hist, int A, bool group_rule, uint8_t *
     const uint64_t a0 = __shfl(c0, i0 & 63, 64), a1 = __shfl(c1, i0 & 63, 64);
     const uint64_t b0 = __shfl(c0, i1 & 63, 64), b1 = __shfl(c1, i1 & 63, 64);
     const uint64_t P = (i0 < 64 ? a0 : a1) + (i1 < 64 ? b0 : b1);
+    if (ln < np) W.pk[ln] = P;
+    wave_lds_sync();
+    // cl = packages lighter than the leaf, cp = leaves not heavier than the
+    // package (leaves go first at equal weight): binary lifting over <= 64
     int cl = 0, cp = 0;
-    for (int k = 0; k < np; k++) cl += readlane64(P, k) < lw;   // packages lighter
-    for (int i = 0; i < d; i++) cp += readlane64(lw, i) <= P;   // leaves not heavier
+#pragma unroll
+    for (int step = 64; step; step >>= 1) {
+      const int a = cl + step, b = cp + step;
+      const uint64_t pa = W.pk[(a <= np ? a : 1) - 1], lb = W.leaf[(b <= d ? b : 1) - 1];
+      cl = a <= np && pa < lw ? a : cl;
+      cp = b <= d && lb <= P ? b : cp;
+    }
     wave_lds_sync();
     if (ln < d) W.lst[ln + cl] = lw;
     if (ln < np) W.lst[ln + cp] = P;

@@ -177,7 +177,11 @@ __device__ __forceinline__ void count(EncShared<DT> &sh, int p, uint32_t b, int 
 }
 
 template <int DT>
-__global__ __launch_bounds__(enc_nt(DT)) void k_analyze(EncArgs a) {
+// BF16: at most 7 waves' worth of registers per SIMD, so that every chunk of a
+// large workload is resident at once (the scalar registers would otherwise
+// allow 6 workgroups per CU; the extra ones spill to vector-register lanes,
+// not to memory).
+__global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT == BF16 ? 7 : 1))) void k_analyze(EncArgs a) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int COLS = EncShared<DT>::COLS;
