@@ -37,7 +37,8 @@ enum DType { BF16 = 0, FP32 = 1, FP8 = 2 };
 __host__ __device__ constexpr int esize(int dt) { return dt == BF16 ? 2 : dt == FP32 ? 4 : 1; }
 __host__ __device__ constexpr int ncoded(int dt) { return dt == BF16 ? 1 : dt == FP32 ? 4 : 2; }
 __host__ __device__ constexpr int kbits(int dt, int p) { return dt == FP8 ? (p == 0 ? 4 : 3) : 8; }
-__host__ __device__ constexpr int segsyms(int dt) { return dt == BF16 ? 512 : dt == FP32 ? 1024 : 2048; }
+// symbols per segment: a full 256 KiB chunk gives 256 segments per coded stream
+__host__ __device__ constexpr int segsyms(int dt) { return dt == BF16 ? 512 : dt == FP32 ? 256 : 1024; }
 __host__ __device__ constexpr uint64_t align16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
 __host__ __device__ inline uint64_t rawplane_bytes(int dt, uint64_t n) {
   return dt == BF16 ? n : dt == FP8 ? (n + 7) / 8 : 0;

@@ -16,6 +16,8 @@
 //      workgroup merges the fields staged in LDS with the raw bits and
 //      stores whole 16-byte vectors, so stores stay coalesced although every
 //      lane works on a different segment.
+#include <type_traits>
+
 #include "zn_internal.h"
 
 namespace zn {
@@ -42,7 +44,7 @@ struct DecShared {
   int mode[NC], aux[NC];
   unsigned long long pay_off[NC], seg_off[NC];
   uint32_t pay[NC];
-  uint32_t wtot[DEC_NT / 64][NC];
+  uint32_t wtot[DEC_NT / 64][NC];   // [wave][coded stream index]
   int bad;
 };
 
@@ -73,11 +75,7 @@ __device__ __forceinline__ u32x4 merge_bf16(uint64_t E, uint64_t SF) {
 template <int DT>
 __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
-  constexpr int SPW = 64 / NC;           // segment slots of one stream per wave
-  constexpr int GS = 4 * SPW;            // segment slots per stream per group
   constexpr int VE = 16 / ES;            // elements per 16-byte vector
-  constexpr int VPS = RND * ES / 16;     // vectors per slot per round
-  constexpr int NVL = SPW * VPS / 64;    // vectors per lane per round
   __shared__ DecShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
   if (a.ctl[0]) return;  // the header check failed
@@ -150,136 +148,182 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   __syncthreads();
 
   // ------------------------------------------------ 3. lanes and rounds
-  // Lane (wave wv, lane ln) decodes stream p, segment slot wv*SPW + ln%SPW.
-  // Round r decodes strip r*nseg + j of every segment j, so one round of a
-  // wave covers SPW consecutive strips: a contiguous block of the output.
-  const int p = ln / SPW, slot = wv * SPW + ln % SPW, k = kbits(DT, p);
-  const int mode = sh.mode[p];
-  const bool coded = mode == HUFF || mode == GROUP;
-  const uint8_t *pay = in + sh.pay_off[p];
-  const uint32_t paybytes = sh.pay[p];
-  const uint32_t ngroups = (paybytes + 15) / 16;
-  const uint32_t *lut = sh.lut[p];
-  uint32_t *sp = sh.u.stage + tid;    // staged word w of this lane: sp[w * DEC_NT]
-  uint32_t *rp = sh.ring + tid;       // ring word w of this lane: rp[w * DEC_NT]
-  const int t0 = wv * 64;             // first thread of this wave
-  uint32_t seg_carry = 0;
-  int bad = 0;
-  const uint32_t nstrips = (n + RND - 1) / RND;
-  const int G = (nseg + GS - 1) / GS;
-  for (int g = 0; g < G; g++) {
-    const int sj = g * GS + slot;
-    const bool live = sj < nseg;
-    // start bit of the segment: scan of the stored segment bit lengths
-    uint32_t sbits = 0;
-    if (coded && live) sbits = ldg2(in + sh.seg_off[p] + 2 * sj);
-    const uint32_t incl = wave_incl_scan(sbits);
-    const int first = p * SPW;
-    const uint32_t wbase = first > 0 ? __shfl(incl, first - 1, 64) : 0;
-    const uint32_t wlast = __shfl(incl, first + SPW - 1, 64);
-    if (ln == first) sh.wtot[wv][p] = wlast - wbase;
-    __syncthreads();
-    uint32_t before = 0, gtot = 0;
+  // Lanes decode only the Huffman- or group-coded streams; raw and constant
+  // streams need no decoding and the merge reads them straight from the
+  // record.  With ncc coded streams, SPW = 64, 32 or 16 lanes of each wave
+  // take one coded stream each (a template per SPW; the branch below is
+  // uniform per workgroup).
+  int ncc = 0, cs[NC], cidx[NC];
 #pragma unroll
-    for (int q = 0; q < DEC_NT / 64; q++) {
-      const uint32_t x = sh.wtot[q][p];
-      before += q < wv ? x : 0;
-      gtot += x;
+  for (int p = 0; p < NC; p++) {
+    cidx[p] = -1;
+    if (sh.mode[p] == HUFF || sh.mode[p] == GROUP) { cs[ncc] = p; cidx[p] = ncc; ncc++; }
+  }
+  // Fields of the raw streams for one 16-byte output vector of VE elements
+  // starting at element ev (< n): k = 8 gives VE bytes, k = 4 VE nibbles,
+  // k = 3 a 3*VE-bit run.  Every read stays inside the stream's payload, or
+  // at most 4 bytes past it where the record or the container tail follows
+  // (the record walk checked that the container holds them).
+  auto raw_field = [&](int p, uint32_t ev) -> uint64_t {
+    const uint8_t *pay = in + sh.pay_off[p];
+    const int k = kbits(DT, p);
+    if (k == 8) {
+      if constexpr (VE == 8) { const u32x2 x = ldg8(pay + ev); return x[0] | (uint64_t(x[1]) << 32); }
+      else if constexpr (VE == 4) return ldg4(pay + ev);
+      else return 0;
     }
-    const uint32_t b0 = seg_carry + before + (incl - sbits - wbase);
-    seg_carry += gtot;
-    __syncthreads();
+    if (k == 4) { const u32x2 x = ldg8(pay + ev / 2); return x[0] | (uint64_t(x[1]) << 32); }
+    const uint32_t b = ev * 3, w0 = b >> 5;   // ev is a multiple of 16: b & 31 is 0 or 16
+    const uint64_t x = ldg4(pay + 4 * w0) | (uint64_t(ldg4(pay + 4 * w0 + 4)) << 32);
+    return x >> (b & 31);
+  };
+  // a constant stream's byte in every byte lane
+  auto cfield = [&](int p) -> uint64_t { return 0x0101010101010101ull * uint64_t(sh.aux[p]); };
 
-    // Bit reader: a 64-bit window (LSB-first) refilled one word at a time
-    // from the lane's ring of payload words in LDS.  The ring holds two
-    // 64-byte sectors of the payload, aligned in memory so that every sector
-    // is one HBM burst read once; a sector is loaded one round before it can
-    // be needed.  Word positions count from the aligned base pay64.
-    uint64_t buf = 0;
-    int nb = 0;
-    const uintptr_t pa = reinterpret_cast<uintptr_t>(pay);
-    const uint8_t *pay64 = pay - (pa & 63);       // inside the container: pay is past the header
-    const uint32_t adj = uint32_t(pa & 63) / 4;   // payload word 0 is window word adj
-    const uint32_t glast = adj / 4 + ngroups - 1; // last 16-byte group holding payload
-    uint32_t wpos = 0, nsec = 0, pre = 0;         // next word to read, next sector to fetch
-    u32x4 ps0 = {0, 0, 0, 0}, ps1 = ps0, ps2 = ps0, ps3 = ps0;
-    bool pend = false;
-    // 16-byte group gi of the window; groups past the payload read its last one
-    auto grp = [&](uint32_t gi) { return ldg16(pay64 + 16ull * (gi < glast ? gi : glast)); };
-    auto put_sector = [&](uint32_t sc, const u32x4 &x0, const u32x4 &x1, const u32x4 &x2,
-                          const u32x4 &x3) {
-      uint32_t *q = rp + (sc & 1) * 16 * DEC_NT;
+  int bad = 0;
+  auto path = [&](auto spw_c, auto rawf_c) {
+    constexpr int SPW = decltype(spw_c)::value;   // lanes per coded stream per wave
+    constexpr bool RAWF = decltype(rawf_c)::value; // some stream is stored raw
+    constexpr int GS = 4 * SPW;                   // segments per coded stream per group
+    constexpr int VPS = RND * ES / 16;            // output vectors per strip
+    constexpr int NVL = SPW * VPS / 64;           // output vectors per lane per round
+    // Lane (wave wv, lane ln) decodes coded stream ci = ln / SPW, segment slot
+    // wv*SPW + ln%SPW.  Round r decodes strip r*nseg + j of every segment j,
+    // so one round of a wave covers SPW consecutive strips: a contiguous
+    // block of the output.
+    const int ci = ln / SPW, slot = wv * SPW + ln % SPW;
+    const bool coded = ci < ncc;
+    const int p = coded ? cs[ci] : 0;
+    const uint8_t *pay = in + sh.pay_off[p];
+    const uint32_t paybytes = sh.pay[p];
+    const uint32_t ngroups = (paybytes + 15) / 16;
+    const uint32_t *lut = sh.lut[p];
+    uint32_t *sp = sh.u.stage + tid;    // staged word w of this lane: sp[w * DEC_NT]
+    uint32_t *rp = sh.ring + tid;       // ring word w of this lane: rp[w * DEC_NT]
+    const int t0 = wv * 64;             // first thread of this wave
+    uint32_t seg_carry = 0;
+    const uint32_t nstrips = (n + RND - 1) / RND;
+    const int G = (nseg + GS - 1) / GS;
+    for (int g = 0; g < G; g++) {
+      const int sj = g * GS + slot;
+      const bool live = sj < nseg;
+      // start bit of the segment: scan of the stored segment bit lengths
+      uint32_t sbits = 0;
+      if (coded && live) sbits = ldg2(in + sh.seg_off[p] + 2 * sj);
+      const uint32_t incl = wave_incl_scan(sbits);
+      const int first = ci * SPW;
+      const uint32_t wbase = first > 0 ? __shfl(incl, first - 1, 64) : 0;
+      const uint32_t wlast = __shfl(incl, (first + SPW - 1) & 63, 64);
+      if (coded && ln == first) sh.wtot[wv][ci] = wlast - wbase;
+      __syncthreads();
+      uint32_t before = 0, gtot = 0;
+      if (coded) {
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        q[k * DEC_NT] = x0[k];
-        q[(4 + k) * DEC_NT] = x1[k];
-        q[(8 + k) * DEC_NT] = x2[k];
-        q[(12 + k) * DEC_NT] = x3[k];
-      }
-    };
-    if (coded && live) {
-      const uint32_t w0 = (b0 >> 5) + adj, s0 = w0 >> 4;
-      const u32x4 a0 = grp(4 * s0), a1 = grp(4 * s0 + 1), a2 = grp(4 * s0 + 2), a3 = grp(4 * s0 + 3);
-      const u32x4 a4 = grp(4 * s0 + 4), a5 = grp(4 * s0 + 5), a6 = grp(4 * s0 + 6), a7 = grp(4 * s0 + 7);
-      put_sector(s0, a0, a1, a2, a3);
-      put_sector(s0 + 1, a4, a5, a6, a7);
-      nsec = s0 + 2;
-      buf = rp[(w0 & (RING - 1)) * DEC_NT] | (uint64_t(rp[((w0 + 1) & (RING - 1)) * DEC_NT]) << 32);
-      wpos = w0 + 2;
-      buf >>= (b0 & 31);
-      nb = 64 - int(b0 & 31);
-    }
-    int ov = 0;         // symbols of the next strip decoded early (staged words 8, 9)
-    // Raw bits merged by this lane in round r: one load per vector, always
-    // issued (an empty vector reads the plane's first bytes and is ignored),
-    // so every round issues the same loads and no wait has to drain the
-    // stores in flight.  A partial last vector stays inside the plane, whose
-    // size is padded to 16 bytes: BF16 vectors start at multiples of 8
-    // bytes, FP8 sign words at multiples of 2.
-    auto load_raw = [&](int r, uint64_t (&rv)[NVL]) {
-#pragma unroll
-      for (int i = 0; i < NVL; i++) {
-        const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
-        const int sjv = g * GS + wv * SPW + sl;
-        const uint32_t ev = (uint32_t(r) * nseg + sjv) * RND + part * VE;
-        const bool ok = sjv < nseg && ev < n;
-        if constexpr (DT == BF16) {
-          const u32x2 x = ldg8s(rawp + (ok ? ev : 0));
-          rv[i] = x[0] | (uint64_t(x[1]) << 32);
-        } else if constexpr (DT == FP8) {
-          rv[i] = ldg2(rawp + (ok ? ev / 8 : 0));
-        } else {
-          rv[i] = 0;
+        for (int q = 0; q < DEC_NT / 64; q++) {
+          const uint32_t x = sh.wtot[q][ci];
+          before += q < wv ? x : 0;
+          gtot += x;
         }
       }
-    };
-    constexpr int NR = S / RND;   // rounds, an even number
-    static_assert(NR % 2 == 0, "rounds come in pairs");
-    uint64_t rawA[NVL], rawB[NVL];
-    load_raw(0, rawA);
-    // One round; the raw bits of the next round load into nxt while this one
-    // decodes (the loop below alternates two register sets, so no copy makes
-    // the compiler wait for loads in flight).
-    auto round = [&](int r, const uint64_t (&rawv)[NVL], uint64_t (&nxt)[NVL]) {
-      load_raw(r + 1 < NR ? r + 1 : r, nxt);  // the last round reloads its own: same count
-      const uint32_t q = uint32_t(r) * nseg + sj;   // this lane's strip
-      const int lim = live && q < nstrips ? int(min(uint32_t(RND), n - q * RND)) : 0;
-      const bool last = live && q < nstrips && q + nseg >= nstrips;
-      // groups fetched last round enter the ring
-      if (pend) {
-        put_sector(nsec, ps0, ps1, ps2, ps3);
-        nsec++;
-        pend = false;
+      const uint32_t b0 = seg_carry + before + (incl - sbits - wbase);
+      seg_carry += gtot;
+      __syncthreads();
+
+      // Bit reader: a 64-bit window (LSB-first) refilled one word at a time
+      // from the lane's ring of payload words in LDS.  The ring holds two
+      // 64-byte sectors of the payload, aligned in memory so that every
+      // sector is one HBM burst read once; a sector is loaded one round
+      // before it can be needed.  Word positions count from the aligned base.
+      uint64_t buf = 0;
+      int nb = 0;
+      const uintptr_t pa = reinterpret_cast<uintptr_t>(pay);
+      const uint8_t *pay64 = pay - (pa & 63);       // inside the container: pay is past the header
+      const uint32_t adj = uint32_t(pa & 63) / 4;   // payload word 0 is window word adj
+      const uint32_t glast = adj / 4 + ngroups - 1; // last 16-byte group holding payload
+      uint32_t wpos = 0, nsec = 0, pre = 0;         // next word to read, next sector to fetch
+      u32x4 ps0 = {0, 0, 0, 0}, ps1 = ps0, ps2 = ps0, ps3 = ps0;
+      bool pend = false;
+      // 16-byte group gi of the window; groups past the payload read its last one
+      auto grp = [&](uint32_t gi) { return ldg16(pay64 + 16ull * (gi < glast ? gi : glast)); };
+      auto put_sector = [&](uint32_t sc, const u32x4 &x0, const u32x4 &x1, const u32x4 &x2,
+                            const u32x4 &x3) {
+        uint32_t *q = rp + (sc & 1) * 16 * DEC_NT;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+          q[kk * DEC_NT] = x0[kk];
+          q[(4 + kk) * DEC_NT] = x1[kk];
+          q[(8 + kk) * DEC_NT] = x2[kk];
+          q[(12 + kk) * DEC_NT] = x3[kk];
+        }
+      };
+      if (coded && live) {
+        const uint32_t w0 = (b0 >> 5) + adj, s0 = w0 >> 4;
+        const u32x4 a0 = grp(4 * s0), a1 = grp(4 * s0 + 1), a2 = grp(4 * s0 + 2), a3 = grp(4 * s0 + 3);
+        const u32x4 a4 = grp(4 * s0 + 4), a5 = grp(4 * s0 + 5), a6 = grp(4 * s0 + 6), a7 = grp(4 * s0 + 7);
+        put_sector(s0, a0, a1, a2, a3);
+        put_sector(s0 + 1, a4, a5, a6, a7);
+        nsec = s0 + 2;
+        buf = rp[(w0 & (RING - 1)) * DEC_NT] | (uint64_t(rp[((w0 + 1) & (RING - 1)) * DEC_NT]) << 32);
+        wpos = w0 + 2;
+        buf >>= (b0 & 31);
+        nb = 64 - int(b0 & 31);
       }
-      if (lim > 0) {
-        if (coded) {
+      int ov = 0;         // symbols of the next strip decoded early (staged words 8, 9)
+      // Raw bits and raw-stream fields merged by this lane in round r: the
+      // same loads every round (an empty vector reads element 0 and is
+      // ignored), so no wait has to drain the stores in flight.  A partial
+      // last vector stays inside the always-raw plane, whose size is padded
+      // to 16 bytes: BF16 vectors start at multiples of 8 bytes, FP8 sign
+      // words at multiples of 2.
+      using FT = std::conditional_t<ES == 4, uint32_t, uint64_t>;  // VE raw-stream fields
+      struct RawIn { uint64_t plane[NVL]; FT f[NC][NVL]; };
+      auto load_raw = [&](int r, RawIn &rv) {
+#pragma unroll
+        for (int i = 0; i < NVL; i++) {
+          const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
+          const int sjv = g * GS + wv * SPW + sl;
+          const uint32_t ev0 = (uint32_t(r) * nseg + sjv) * RND + part * VE;
+          const uint32_t ev = sjv < nseg && ev0 < n ? ev0 : 0;
+          if constexpr (DT == BF16) {
+            const u32x2 x = ldg8s(rawp + ev);
+            rv.plane[i] = x[0] | (uint64_t(x[1]) << 32);
+          } else if constexpr (DT == FP8) {
+            rv.plane[i] = ldg2(rawp + ev / 8);
+          } else {
+            rv.plane[i] = 0;
+          }
+          if constexpr (RAWF) {
+#pragma unroll
+            for (int q = 0; q < NC; q++) rv.f[q][i] = sh.mode[q] == RAW ? FT(raw_field(q, ev)) : FT(0);
+          }
+        }
+      };
+      constexpr int NR = S / RND;   // rounds, an even number
+      static_assert(NR % 2 == 0, "rounds come in pairs");
+      RawIn rawA, rawB;
+      load_raw(0, rawA);
+      // One round; the raw inputs of the next round load into nxt while this
+      // one decodes (the loop below alternates two register sets, so no copy
+      // makes the compiler wait for loads in flight).
+      auto round = [&](int r, const RawIn &rawv, RawIn &nxt) {
+        load_raw(r + 1 < NR ? r + 1 : r, nxt);  // the last round reloads its own: same count
+        const uint32_t q = uint32_t(r) * nseg + sj;   // this lane's strip
+        const int lim = coded && live && q < nstrips ? int(min(uint32_t(RND), n - q * RND)) : 0;
+        const bool last = live && q < nstrips && q + nseg >= nstrips;
+        // the sector fetched last round enters the ring
+        if (pend) {
+          put_sector(nsec, ps0, ps1, ps2, ps3);
+          nsec++;
+          pend = false;
+        }
+        if (lim > 0) {
           // Symbols are staged four to a word.  cur holds the bytes of the
           // word being filled; each lookup writes that word and the next
           // (aligned stores; the next word holds what spilled over) and
           // moves on when the word is complete -- no branch per lookup.
           // The window is refilled, also without branches, with 32 bits
-          // whenever fewer than 32 remain: enough for the two lookups of
-          // an iteration (at most 22 bits).
+          // whenever fewer than 32 remain: enough for the two lookups of an
+          // iteration (at most 22 bits).
           uint32_t cur = 0;
           uint32_t *wp = sp;        // the word being filled
           if (ov) {  // symbols of this strip decoded last round: words 8, 9 -> 0, 1
@@ -293,8 +337,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           uint32_t na = ov & 3;     // bytes in cur
           pre = rp[(wpos & (RING - 1)) * DEC_NT];
           auto emit = [&](uint32_t e) {
-            const uint64_t t = uint64_t(e & 0xFFFFFF) << (8 * na);
-            const uint32_t lo = cur | uint32_t(t), hi = uint32_t(t >> 32);
+            const uint64_t tt = uint64_t(e & 0xFFFFFF) << (8 * na);
+            const uint32_t lo = cur | uint32_t(tt), hi = uint32_t(tt >> 32);
             wp[0] = lo;
             wp[DEC_NT] = hi;
             const uint32_t m = e >> 28;
@@ -327,130 +371,135 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             // exact end: the segment must use exactly its stored bit length
             uint64_t bpos = uint64_t(wpos - adj) * 32 - uint32_t(nb);
             for (int x = 0; x < ov; x++) {
-              const int b = lim + x;
-              bpos -= sh.len[p][(sp[(b >> 2) * DEC_NT] >> (8 * (b & 3))) & 0xFF];
+              const int bb = lim + x;
+              bpos -= sh.len[p][(sp[(bb >> 2) * DEC_NT] >> (8 * (bb & 3))) & 0xFF];
             }
             if (bpos != uint64_t(b0) + sbits) bad = 1;
             ov = 0;
-          } else {
-            // lim == RND here.  The next round reads at most 32 lookups
-            // (352 bits) with at least 10 bits left in the window, so words
+          } else if (((wpos + 11) >> 4) >= nsec) {
+            // lim == RND here.  The next round reads at most 32 lookups (352
+            // bits) with at least 10 bits left in the window, so words
             // [wpos, wpos + 12): at most one sector past those in the ring,
             // whose slot held a sector before wpos's.
-            if (((wpos + 11) >> 4) >= nsec) {
-              ps0 = grp(4 * nsec);
-              ps1 = grp(4 * nsec + 1);
-              ps2 = grp(4 * nsec + 2);
-              ps3 = grp(4 * nsec + 3);
-              pend = true;
-            }
+            ps0 = grp(4 * nsec);
+            ps1 = grp(4 * nsec + 1);
+            ps2 = grp(4 * nsec + 2);
+            ps3 = grp(4 * nsec + 3);
+            pend = true;
           }
-        } else if (mode == RAW) {
-          // k-bit values in element order, value bit 0 first: strip q is k words
-          const uint64_t wb = uint64_t(q) * k;
-          const uint32_t maxw = (paybytes + 15) / 16 * 4;
-          uint32_t wd[8];
-          if (k != 3 && wb + k <= maxw) {
-            const u32x4 q0 = ldg16(pay + 4 * wb);
-            wd[0] = q0[0], wd[1] = q0[1], wd[2] = q0[2], wd[3] = q0[3];
-            if (k == 8) {
-              const u32x4 q1 = ldg16(pay + 4 * wb + 16);
-              wd[4] = q1[0], wd[5] = q1[1], wd[6] = q1[2], wd[7] = q1[3];
-            } else {
-              wd[4] = wd[5] = wd[6] = wd[7] = 0;
+        }
+        wave_lds_sync();
+        // merge and store: vector v of this wave covers VE elements of slot v / VPS
+#pragma unroll
+        for (int i = 0; i < NVL; i++) {
+          const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
+          const int sjv = g * GS + wv * SPW + sl;
+          const uint32_t qv = uint32_t(r) * nseg + sjv;
+          const uint32_t ev = qv * RND + part * VE;
+          const bool valid = sjv < nseg && ev < n;
+          // staged bytes of coded stream pp for this vector (VE bytes)
+          auto staged = [&](int pp, int h) -> uint64_t {
+            const int th = t0 + cidx[pp] * SPW + sl;
+            if constexpr (ES == 2) return stg_pair(sh.u.stage, 2 * part, th);
+            else if constexpr (ES == 4) return sh.u.stage[part * DEC_NT + th];
+            else return stg_pair(sh.u.stage, 4 * part + 2 * h, th);
+          };
+          auto fieldv = [&](int pp, int h) -> uint64_t {   // h: 8-byte half (FP8)
+            const int md = sh.mode[pp];
+            if (md == CONST) return cfield(pp);
+            if (md != RAW || !RAWF) return staged(pp, h);
+            return rawv.f[pp][i];
+          };
+          u32x4 o;
+          if constexpr (DT == BF16) {
+            o = merge_bf16(fieldv(0, 0), rawv.plane[i]);
+          } else if constexpr (DT == FP32) {
+            uint32_t P[4];
+#pragma unroll
+            for (int pp = 0; pp < 4; pp++) P[pp] = uint32_t(fieldv(pp, 0));
+#pragma unroll
+            for (int x = 0; x < 4; x++) {
+              const uint32_t p0 = (P[0] >> (8 * x)) & 0xFF, p1 = (P[1] >> (8 * x)) & 0xFF;
+              const uint32_t p2 = (P[2] >> (8 * x)) & 0xFF, p3 = (P[3] >> (8 * x)) & 0xFF;
+              o[x] = ((p1 & 0x80) << 24) | (p0 << 23) | ((p1 & 0x7F) << 16) | (p2 << 8) | p3;
             }
           } else {
+            // E4 and M3 of the 16 elements as bytes, from whichever source
+            uint64_t Ev[2], Mv[2];
+            const int m0 = sh.mode[0], m1 = sh.mode[1];
 #pragma unroll
-            for (int x = 0; x < 8; x++) wd[x] = (x < k && wb + x < maxw) ? ldg4(pay + 4 * (wb + x)) : 0u;
-          }
-          if (k == 8) {
+            for (int h = 0; h < 2; h++) {
+              if (m0 == RAW) {
+                const uint64_t x = rawv.f[0][i] >> (32 * h);   // 8 nibbles
+                uint64_t y = 0;
 #pragma unroll
-            for (int x = 0; x < 8; x++) sp[x * DEC_NT] = wd[x];
-          } else {
-#pragma unroll
-            for (int x = 0; x < RND / 4; x++) {
-              uint32_t wv4 = 0;
-#pragma unroll
-              for (int y = 0; y < 4; y++) {
-                const int bit = (4 * x + y) * k;
-                const uint32_t lo = wd[bit >> 5] >> (bit & 31);
-                const uint32_t hi = (bit & 31) + k > 32 ? wd[(bit >> 5) + 1] << (32 - (bit & 31)) : 0u;
-                wv4 |= ((lo | hi) & ((1u << k) - 1)) << (8 * y);
+                for (int j = 0; j < 8; j++) y |= ((x >> (4 * j)) & 15) << (8 * j);
+                Ev[h] = y;
+              } else {
+                Ev[h] = fieldv(0, h);
               }
-              sp[x * DEC_NT] = wv4;
+              if (m1 == RAW) {
+                const uint64_t x = rawv.f[1][i] >> (24 * h);   // 8 values of 3 bits
+                uint64_t y = 0;
+#pragma unroll
+                for (int j = 0; j < 8; j++) y |= ((x >> (3 * j)) & 7) << (8 * j);
+                Mv[h] = y;
+              } else {
+                Mv[h] = fieldv(1, h);
+              }
+            }
+#pragma unroll
+            for (int x = 0; x < 4; x++) {
+              const uint32_t e4 = uint32_t(Ev[x >> 1] >> (32 * (x & 1)));
+              const uint32_t m3 = uint32_t(Mv[x >> 1] >> (32 * (x & 1)));
+              const uint32_t sg = uint32_t(rawv.plane[i] >> (4 * x)) & 15;
+              const uint32_t sb = ((sg & 1) << 7) | ((sg & 2) << 14) | ((sg & 4) << 21) | ((sg & 8) << 28);
+              o[x] = (e4 << 3) | m3 | sb;
             }
           }
+          // Every lane stores one vector per iteration -- lanes without a
+          // whole aligned vector store into the scratch sink -- so each round
+          // issues the same stores and the compiler's waits for older loads
+          // never have to drain them.
+          uint8_t *op = dst + uint64_t(ev) * ES;
+          const bool whole = valid && ev + VE <= n && oaligned;
+          stg16(whole ? op : sink, o);
+          if (valid && !whole) {  // a partial last vector or an unaligned output
+            const uint32_t cnt_b = (ev + VE <= n ? VE : n - ev) * ES;
+            for (uint32_t b = 0; b < cnt_b; b++) stg1(op + b, o[b >> 2] >> ((b & 3) * 8));
+          }
         }
+        wave_lds_sync();
+      };
+      // the first pair is peeled so that the loop is entered with the memory
+      // operations of a whole round in flight, as on every later pass
+      round(0, rawA, rawB);
+      round(1, rawB, rawA);
+      for (int r = 2; r < NR; r += 2) {
+        round(r, rawA, rawB);
+        round(r + 1, rawB, rawA);
       }
-      wave_lds_sync();
-      // merge and store: vector v of this wave covers VE elements of slot v / VPS
+    }
+    // each coded stream's segment lengths must add up to its payload
+    if (coded && ln % SPW == 0 && wv == 0 && paybytes != 4 * ((seg_carry + 31) / 32)) bad = 1;
+  };
+  bool anyraw = false;
 #pragma unroll
-      for (int i = 0; i < NVL; i++) {
-        const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
-        const int sjv = g * GS + wv * SPW + sl;
-        const uint32_t qv = uint32_t(r) * nseg + sjv;
-        const uint32_t ev = qv * RND + part * VE;
-        const bool valid = sjv < nseg && ev < n;
-        u32x4 o;
-        if constexpr (DT == BF16) {
-          const uint64_t E = sh.mode[0] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[0])
-                                                 : stg_pair(sh.u.stage, 2 * part, t0 + sl);
-          o = merge_bf16(E, rawv[i]);
-        } else if constexpr (DT == FP32) {
-          uint32_t P[4];
-#pragma unroll
-          for (int pp = 0; pp < 4; pp++)
-            P[pp] = sh.mode[pp] == CONST ? 0x01010101u * uint32_t(sh.aux[pp])
-                                         : sh.u.stage[part * DEC_NT + t0 + pp * SPW + sl];
-#pragma unroll
-          for (int x = 0; x < 4; x++) {
-            const uint32_t p0 = (P[0] >> (8 * x)) & 0xFF, p1 = (P[1] >> (8 * x)) & 0xFF;
-            const uint32_t p2 = (P[2] >> (8 * x)) & 0xFF, p3 = (P[3] >> (8 * x)) & 0xFF;
-            o[x] = ((p1 & 0x80) << 24) | (p0 << 23) | ((p1 & 0x7F) << 16) | (p2 << 8) | p3;
-          }
-        } else {
-          uint64_t Ev[2], Mv[2];
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            Ev[h] = sh.mode[0] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[0])
-                                        : stg_pair(sh.u.stage, 4 * part + 2 * h, t0 + sl);
-            Mv[h] = sh.mode[1] == CONST ? 0x0101010101010101ull * uint64_t(sh.aux[1])
-                                        : stg_pair(sh.u.stage, 4 * part + 2 * h, t0 + SPW + sl);
-          }
-#pragma unroll
-          for (int x = 0; x < 4; x++) {
-            const uint32_t e4 = uint32_t(Ev[x >> 1] >> (32 * (x & 1)));
-            const uint32_t m3 = uint32_t(Mv[x >> 1] >> (32 * (x & 1)));
-            const uint32_t sg = uint32_t(rawv[i] >> (4 * x)) & 15;
-            const uint32_t sb = ((sg & 1) << 7) | ((sg & 2) << 14) | ((sg & 4) << 21) | ((sg & 8) << 28);
-            o[x] = (e4 << 3) | m3 | sb;
-          }
-        }
-        // Every lane stores one vector per iteration -- lanes without a
-        // whole aligned vector store into the scratch sink -- so each round
-        // issues the same stores and the compiler's waits for older loads
-        // never have to drain them.
-        uint8_t *op = dst + uint64_t(ev) * ES;
-        const bool whole = valid && ev + VE <= n && oaligned;
-        stg16(whole ? op : sink, o);
-        if (valid && !whole) {  // a partial last vector or an unaligned output
-          const uint32_t cnt_b = (ev + VE <= n ? VE : n - ev) * ES;
-          for (uint32_t b = 0; b < cnt_b; b++) stg1(op + b, o[b >> 2] >> ((b & 3) * 8));
-        }
-      }
-      wave_lds_sync();
-    };
-    // the first pair is peeled so that the loop is entered with the memory
-    // operations of a whole round in flight, as on every later pass
-    round(0, rawA, rawB);
-    round(1, rawB, rawA);
-    for (int r = 2; r < NR; r += 2) {
-      round(r, rawA, rawB);
-      round(r + 1, rawB, rawA);
+  for (int p = 0; p < NC; p++) anyraw |= sh.mode[p] == RAW;
+  using I16 = std::integral_constant<int, 16>;
+  using I32 = std::integral_constant<int, 32>;
+  using I64 = std::integral_constant<int, 64>;
+  using T = std::true_type;
+  using F = std::false_type;
+  if (ncc <= 1) {
+    if (anyraw) path(I64{}, T{}); else path(I64{}, F{});
+  } else if constexpr (NC >= 2) {
+    if (ncc == 2) {
+      if (anyraw) path(I32{}, T{}); else path(I32{}, F{});
+    } else if constexpr (NC == 4) {
+      if (anyraw) path(I16{}, T{}); else path(I16{}, F{});
     }
   }
-  // the stream's segment lengths must add up to its payload
-  if (coded && ln % SPW == 0 && wv == 0 && paybytes != 4 * ((seg_carry + 31) / 32)) bad = 1;
   if (bad) atomicOr(&a.ctl[0], kErrCorrupt);
 }
 

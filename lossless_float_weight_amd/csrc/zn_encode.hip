@@ -329,7 +329,23 @@ __global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT =
             }
           }
         }
+        // Any prefix code spends at least n*H bits (Shannon's bound from the
+        // Kraft inequality), so when even that cannot beat the raw section the
+        // optimal code need not be built: the choice is RAW either way.  The
+        // bound is taken 64 bits and a relative 1e-9 below the double-precision
+        // sum, far more than its rounding error.
+        bool raw_sure = false;
         if (escape) {
+          double hb = 0.0;
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            if (hq[q]) hb += double(hq[q]) * log2(double(n) / double(hq[q]));
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) hb += __shfl_xor(hb, o, 64);
+          const double lb = hb * (1.0 - 1e-9) - 64.0;
+          raw_sure = lb > 0.0 && section_bytes(HUFF, k, n, nseg, uint64_t(lb)) >= raw;
+        }
+        if (escape && !raw_sure) {
           if (wave_pm_lengths<uint32_t>(sh.hist[p], A, false, sh.len[p], sh.u.wcb) < 0) {
             need_block = 1;
           } else {
@@ -484,9 +500,11 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     for (int T = 0; T < ntiles; T++) {
       const int buf = T & 1;
       uint32_t *stage = sh.stage[buf];
-      // Concatenate each run's codes 8 at a time without branches: pairs fit
-      // 22 bits, quads 44 bits (one u64), two quads 88 bits (lo | hi<<64).
-      constexpr int NG = EPT / 8;
+      // Concatenate each run's codes 8 (or, for 4-element runs, 4) at a time
+      // without branches: pairs fit 22 bits, quads 44 bits (one u64), two
+      // quads 88 bits (lo | hi<<64).
+      constexpr int GE = EPT < 8 ? EPT : 8;   // codes per group
+      constexpr int NG = EPT / GE;
       uint64_t glo[G][NG];
       uint32_t ghi[G][NG];
       uint32_t gb[G][NG], nb[G];
@@ -510,10 +528,10 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
         nb[g] = 0;
 #pragma unroll
         for (int g8 = 0; g8 < NG; g8++) {
-          uint32_t v[8], l[8];
+          uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-          for (int i = 0; i < 8; i++) {
-            const int e = g8 * 8 + i;
+          for (int i = 0; i < GE; i++) {
+            const int e = g8 * GE + i;
             const uint32_t c = eb + e < n ? sh.enc[p][field_rt<DT>(w[e], p)] : 0u;
             v[i] = c & 0xFFFF;
             l[i] = c >> 16;

@@ -34,8 +34,8 @@
  *    Every bit pattern is data: NaN, Inf, subnormals and -0 are not special.
  * R2 Chunks: a chunk holds chunk_bytes of uncompressed input of ONE tensor;
  *    the last chunk of a tensor may be short.  A coded stream of n symbols
- *    has nseg = ceil(n / S) segments (S = 512 for BF16, 1024 for FP32, 2048
- *    for FP8).  The stream is cut into strips of W = 32 consecutive symbols
+ *    has nseg = ceil(n / S) segments (S = 512 for BF16, 256 for FP32, 1024
+ *    for FP8: a full 256 KiB chunk gives 256 segments per coded stream).  The stream is cut into strips of W = 32 consecutive symbols
  *    (the last strip may be short); segment j holds strips j, j + nseg,
  *    j + 2*nseg, ... in that order.  A full chunk gives every segment S/W
  *    strips.
@@ -95,7 +95,7 @@
 static int esize(int dt) { return dt == ZNO_BF16 ? 2 : dt == ZNO_FP32 ? 4 : 1; }
 static int ncoded(int dt) { return dt == ZNO_BF16 ? 1 : dt == ZNO_FP32 ? 4 : 2; }
 static int kbits(int dt, int p) { return dt == ZNO_FP8_E4M3 ? (p == 0 ? 4 : 3) : 8; }
-static int segsyms(int dt) { return dt == ZNO_BF16 ? 512 : dt == ZNO_FP32 ? 1024 : 2048; }
+static int segsyms(int dt) { return dt == ZNO_BF16 ? 512 : dt == ZNO_FP32 ? 256 : 1024; }
 static uint64_t rawplane_bytes(int dt, uint64_t n) {
   return dt == ZNO_BF16 ? n : dt == ZNO_FP8_E4M3 ? (n + 7) / 8 : 0;
 }

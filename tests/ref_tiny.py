@@ -24,7 +24,7 @@ MAX_LEN = 11
 RAW, CONST, HUFF, GROUP = 0, 1, 2, 3
 ESIZE = {0: 2, 1: 4, 2: 1}
 NCODED = {0: 1, 1: 4, 2: 2}
-SEG = {0: 512, 1: 1024, 2: 2048}
+SEG = {0: 512, 1: 256, 2: 1024}
 
 
 def kbits(dt, p):
