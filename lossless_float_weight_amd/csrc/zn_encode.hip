@@ -444,6 +444,70 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   for (int i = tid; i < 2 * STAGE; i += ENC_NT) sh.stage[i / STAGE][i % STAGE] = 0;
   __syncthreads();
 
+  // ------------------------------------------- raw streams, in one pass
+  // Fixed-width values in element order, value bit 0 first.  A lane takes LE
+  // consecutive elements per step, LE*k a multiple of 32 for every field
+  // width of the dtype, so it writes whole words of every raw stream with no
+  // scan; the next step's elements are loaded while this step packs.  Bits
+  // past the last element are zero.
+  {
+    constexpr int LE = DT == FP8 ? 32 : VE;      // FP8: k = 3 needs 32 elements per 3 words
+    constexpr int NQ = LE / VE;                  // 16-byte loads per lane per step
+    uint32_t rawmask = 0;
+    uint8_t *pw[NC];
+#pragma unroll
+    for (int p = 0; p < NC; p++) {
+      const int k = kbits(DT, p), mode = plan[48 + p];
+      rawmask |= uint32_t(mode == RAW) << p;
+      pw[p] = recp + *reinterpret_cast<const uint32_t *>(plan + 32 + 4 * p) + head_bytes_of(mode, k, nseg);
+    }
+    if (rawmask) {
+      u32x4 nx[NQ];
+      auto fetch = [&](uint32_t e) {
+        if (aligned && e + LE <= n) {
+#pragma unroll
+          for (int j = 0; j < NQ; j++) nx[j] = ldg16(src + uint64_t(e + j * VE) * ES);
+        }
+      };
+      fetch(uint32_t(tid) * LE);
+      for (uint32_t e = uint32_t(tid) * LE; e < n; e += uint32_t(ENC_NT) * LE) {
+        uint32_t w[LE];
+        if (aligned && e + LE <= n) {
+#pragma unroll
+          for (int j = 0; j < NQ; j++) {
+            const uint4 xq = make_uint4(nx[j][0], nx[j][1], nx[j][2], nx[j][3]);
+#pragma unroll
+            for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(xq, i);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < LE; i++) w[i] = e + i < n ? load_elem<DT>(src + uint64_t(e + i) * ES) : 0u;
+        }
+        fetch(e + uint32_t(ENC_NT) * LE);
+#pragma unroll
+        for (int p = 0; p < NC; p++) {
+          if (!((rawmask >> p) & 1)) continue;
+          constexpr int MAXW = LE * 8 / 32;
+          const int k = kbits(DT, p);
+          uint32_t wd[MAXW];
+#pragma unroll
+          for (int x = 0; x < MAXW; x++) wd[x] = 0;
+#pragma unroll
+          for (int i = 0; i < LE; i++) {
+            const uint32_t f = e + i < n ? field_rt<DT>(w[i], p) : 0u;
+            const int b = i * k;
+            wd[b >> 5] |= f << (b & 31);
+            if ((b & 31) + k > 32) wd[(b >> 5) + 1] |= f >> (32 - (b & 31));
+          }
+          const uint32_t nw = uint32_t((uint64_t(n) * k + 31) / 32), w0 = e / 32 * k + (e % 32) * k / 32;
+#pragma unroll
+          for (int x = 0; x < MAXW; x++)
+            if (x * 32 < LE * k && w0 + x < nw) stg4(pw[p] + 4ull * (w0 + x), wd[x]);
+        }
+      }
+    }
+  }
+
   // -------------------------------------------------------- the record
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
@@ -466,6 +530,11 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     for (uint64_t i = used + tid; i < head; i += ENC_NT) sec[i] = 0;
     if (mode == CONST) continue;
     uint32_t *pw = reinterpret_cast<uint32_t *>(sec + head);
+    if (mode == RAW) {   // packed by the pass above; zero the section's pad
+      const uint64_t nw = (uint64_t(n) * k + 31) / 32, padw = align16(pay) / 4;
+      for (uint64_t i = nw + tid; i < padw; i += ENC_NT) pw[i] = 0;
+      continue;
+    }
     uint16_t *segt = reinterpret_cast<uint16_t *>(sec + 8 + (mode == HUFF ? A / 2 : 0));
     const bool with_segs = mode != RAW;
     uint64_t tbit = 0;     // stream bits before this tile
