@@ -473,8 +473,8 @@ struct LutShared {
 
 // Builds the multi-symbol decode table of a canonical code from its lengths.
 // lut[v] for an 11-bit LSB-first window v holds up to three whole code words:
-// bits 0-7, 8-15, 16-23 the symbols, 24-27 the bits they use, 28-29 their
-// number.  t1 (2048 x u16, scratch) is the single-symbol table indexed by the
+// bits 0-5 the bits they use (so the entry itself can serve as a shift
+// amount), 6-7 their number, 8-15, 16-23, 24-31 the symbols.  t1 (2048 x u16, scratch) is the single-symbol table indexed by the
 // window read first-bit-as-MSB.  Returns false (for every thread) if the
 // lengths are not a complete prefix code of at least two words with lengths
 // <= 11.  NT >= 256 threads; A <= 256.
@@ -538,7 +538,7 @@ __device__ bool build_lut(const uint8_t *len, int A, uint32_t *lut, uint16_t *t1
       w >>= l2;
       n++;
     }
-    lut[v] = syms | (uint32_t(used) << 24) | (uint32_t(n) << 28);
+    lut[v] = uint32_t(used) | (uint32_t(n) << 6) | (syms << 8);
   }
   __syncthreads();
   return true;

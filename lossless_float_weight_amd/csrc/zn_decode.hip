@@ -24,11 +24,12 @@ namespace zn {
 
 constexpr int DEC_NT = 256;
 constexpr int RND = 32;        // symbols per lane per round = one strip of its segment
-constexpr int STWW = 10;       // staging words per lane: a strip and up to 5 symbols more
+constexpr int STB = 40;        // staging bytes per lane: a strip and up to 5 symbols more
 constexpr int RING = 32;       // words of a lane's payload window in LDS: two 64-byte sectors
-// Staging and ring are lane-interleaved (word w of thread t at w * DEC_NT + t),
-// so lanes that touch different words of their own areas still hit
-// different LDS banks.
+// The ring is lane-interleaved (word w of thread t at w * DEC_NT + t), so
+// lanes that touch different words of their own rings still hit different
+// LDS banks.  Staging is STB contiguous bytes per lane: each lookup stores
+// its symbols as single bytes at the lane's running position.
 
 template <int DT>
 struct DecShared {
@@ -36,7 +37,7 @@ struct DecShared {
   uint32_t lut[NC][kLutSize];
   union {
     uint16_t t1[kLutSize];
-    uint32_t stage[STWW * DEC_NT];
+    uint8_t stage[DEC_NT * STB];
   } u;
   uint32_t ring[RING * DEC_NT];
   uint8_t len[NC][256];
@@ -48,9 +49,17 @@ struct DecShared {
   int bad;
 };
 
-// Staged words w and w + 1 of thread t.
-__device__ __forceinline__ uint64_t stg_pair(const uint32_t *stage, int w, int t) {
-  return stage[w * DEC_NT + t] | (uint64_t(stage[(w + 1) * DEC_NT + t]) << 32);
+// Staged bytes [b, b + 8) of thread t (b a multiple of 8).
+__device__ __forceinline__ uint64_t stg8(const uint8_t *stage, int b, int t) {
+  return *reinterpret_cast<const uint64_t *>(stage + t * STB + b);
+}
+
+// (a & m) | (b & ~m) in one instruction (v_bfi_b32); the compiler tends to
+// split the two-operand form into three ANDs and an OR.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(m), "v"(a), "v"(b));
+  return d;
 }
 
 // 8 BF16 values from 8 exponent bytes and 8 sign|fraction bytes: a byte
@@ -65,11 +74,45 @@ __device__ __forceinline__ u32x4 merge_bf16(uint64_t E, uint64_t SF) {
     for (int x = 0; x < 2; x++) {
       // bytes [s(2x), e(2x), s(2x+1), e(2x+1)]; e is bytes 4..7 of the pair
       const uint32_t w = __builtin_amdgcn_perm(e, s, x ? 0x07030602u : 0x05010400u);
-      const uint32_t t = (w & 0x007F007Fu) | ((w >> 1) & ~0x007F007Fu);
-      o[2 * h + x] = ((w << 8) & 0x80008000u) | (t & ~0x80008000u);
+      o[2 * h + x] = bfi(0x80008000u, w << 8, bfi(0x007F007Fu, w, w >> 1));
     }
   }
   return o;
+}
+
+// 4 FP32 values from their four field bytes (exponent; sign and fraction
+// bits 22..16; fraction 15..8; fraction 7..0), each field one byte per value:
+// a 4x4 byte transpose by permutes gives [f3, f2, f1, f0] per value, then the
+// exponent moves down one bit and the sign up to bit 31.
+__device__ __forceinline__ u32x4 merge_fp32(uint32_t P0, uint32_t P1, uint32_t P2, uint32_t P3) {
+  const uint32_t al = __builtin_amdgcn_perm(P2, P3, 0x05010400u), ah = __builtin_amdgcn_perm(P2, P3, 0x07030602u);
+  const uint32_t bl = __builtin_amdgcn_perm(P0, P1, 0x05010400u), bh = __builtin_amdgcn_perm(P0, P1, 0x07030602u);
+  const uint32_t X[4] = {__builtin_amdgcn_perm(bl, al, 0x05040100u), __builtin_amdgcn_perm(bl, al, 0x07060302u),
+                         __builtin_amdgcn_perm(bh, ah, 0x05040100u), __builtin_amdgcn_perm(bh, ah, 0x07060302u)};
+  u32x4 o;
+#pragma unroll
+  for (int x = 0; x < 4; x++) o[x] = bfi(0x80000000u, X[x] << 8, bfi(0x007FFFFFu, X[x], X[x] >> 1));
+  return o;
+}
+
+// 8 nibbles (32 bits) -> 8 bytes: a permute spreads the nibble pairs to
+// every other byte, then each pair splits across its byte and the next.
+__device__ __forceinline__ uint64_t nib_bytes(uint32_t x) {
+  const uint32_t lo = __builtin_amdgcn_perm(0u, x, 0x0C010C00u), hi = __builtin_amdgcn_perm(0u, x, 0x0C030C02u);
+  return uint64_t((lo | (lo << 4)) & 0x0F0F0F0Fu) | (uint64_t((hi | (hi << 4)) & 0x0F0F0F0Fu) << 32);
+}
+
+// 8 values of 3 bits (bits 0..23) -> 8 bytes: pairs of values to bits 0..5
+// and 16..21, then each pair splits across its byte and the next.
+__device__ __forceinline__ uint64_t tri_bytes(uint32_t x) {
+  uint64_t r = 0;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const uint32_t y = x >> (12 * h);
+    const uint32_t a = (y & 0x3Fu) | ((y << 10) & 0x3F0000u);
+    r |= uint64_t((a | (a << 5)) & 0x07070707u) << (32 * h);
+  }
+  return r;
 }
 
 template <int DT>
@@ -164,8 +207,17 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   // k = 3 a 3*VE-bit run.  Every read stays inside the stream's payload, or
   // at most 4 bytes past it where the record or the container tail follows
   // (the record walk checked that the container holds them).
+  // payload bases as wave-uniform values, so loads take a scalar base and a
+  // 32-bit lane offset
+  const uint8_t *payu[NC];
+#pragma unroll
+  for (int p = 0; p < NC; p++) {
+    const uint64_t po = sh.pay_off[p];
+    payu[p] = in + ((uint64_t(__builtin_amdgcn_readfirstlane(uint32_t(po >> 32))) << 32) |
+                    __builtin_amdgcn_readfirstlane(uint32_t(po)));
+  }
   auto raw_field = [&](int p, uint32_t ev) -> uint64_t {
-    const uint8_t *pay = in + sh.pay_off[p];
+    const uint8_t *pay = payu[p];
     const int k = kbits(DT, p);
     if (k == 8) {
       if constexpr (VE == 8) { const u32x2 x = ldg8(pay + ev); return x[0] | (uint64_t(x[1]) << 32); }
@@ -181,9 +233,13 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   auto cfield = [&](int p) -> uint64_t { return 0x0101010101010101ull * uint64_t(sh.aux[p]); };
 
   int bad = 0;
-  auto path = [&](auto spw_c, auto rawf_c) {
+  auto path = [&](auto spw_c, auto rawf_c, auto allc_c, auto rawm_c) {
     constexpr int SPW = decltype(spw_c)::value;   // lanes per coded stream per wave
     constexpr bool RAWF = decltype(rawf_c)::value; // some stream is stored raw
+    constexpr bool ALLC = decltype(allc_c)::value; // every stream is coded
+    // RAWM != 0: stream p is raw if bit p is set and coded otherwise, known
+    // here, so only the raw streams' fields are loaded and held
+    constexpr int RAWM = decltype(rawm_c)::value;
     constexpr int GS = 4 * SPW;                   // segments per coded stream per group
     constexpr int VPS = RND * ES / 16;            // output vectors per strip
     constexpr int NVL = SPW * VPS / 64;           // output vectors per lane per round
@@ -198,7 +254,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     const uint32_t paybytes = sh.pay[p];
     const uint32_t ngroups = (paybytes + 15) / 16;
     const uint32_t *lut = sh.lut[p];
-    uint32_t *sp = sh.u.stage + tid;    // staged word w of this lane: sp[w * DEC_NT]
+    uint8_t *sb = sh.u.stage + tid * STB;   // this lane's staged symbols
     uint32_t *rp = sh.ring + tid;       // ring word w of this lane: rp[w * DEC_NT]
     const int t0 = wv * 64;             // first thread of this wave
     uint32_t seg_carry = 0;
@@ -229,12 +285,14 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       seg_carry += gtot;
       __syncthreads();
 
-      // Bit reader: a 64-bit window (LSB-first) refilled one word at a time
-      // from the lane's ring of payload words in LDS.  The ring holds two
-      // 64-byte sectors of the payload, aligned in memory so that every
-      // sector is one HBM burst read once; a sector is loaded one round
-      // before it can be needed.  Word positions count from the aligned base.
-      uint64_t buf = 0;
+      // Bit reader: a window of nb bits (LSB-first) refilled one word at a
+      // time from the lane's ring of payload words in LDS, kept shifted up
+      // by two (W = window << 2) so that W & 0x1FFC is the byte offset of
+      // the table entry of its next 11 bits.  The ring holds two 64-byte
+      // sectors of the payload, aligned in memory so that every sector is
+      // one HBM burst read once; a sector is loaded one round before it can
+      // be needed.  Word positions count from the aligned base.
+      uint64_t W = 0;
       int nb = 0;
       const uintptr_t pa = reinterpret_cast<uintptr_t>(pay);
       const uint8_t *pay64 = pay - (pa & 63);       // inside the container: pay is past the header
@@ -263,10 +321,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         put_sector(s0, a0, a1, a2, a3);
         put_sector(s0 + 1, a4, a5, a6, a7);
         nsec = s0 + 2;
-        buf = rp[(w0 & (RING - 1)) * DEC_NT] | (uint64_t(rp[((w0 + 1) & (RING - 1)) * DEC_NT]) << 32);
-        wpos = w0 + 2;
-        buf >>= (b0 & 31);
-        nb = 64 - int(b0 & 31);
+        W = uint64_t(rp[(w0 & (RING - 1)) * DEC_NT] >> (b0 & 31)) << 2;
+        wpos = w0 + 1;
+        nb = 32 - int(b0 & 31);
       }
       int ov = 0;         // symbols of the next strip decoded early (staged words 8, 9)
       // Raw bits and raw-stream fields merged by this lane in round r: the
@@ -292,10 +349,15 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           } else {
             rv.plane[i] = 0;
           }
-          if constexpr (RAWF) {
+          if constexpr (RAWM != 0) {
+#pragma unroll
+            for (int q = 0; q < NC; q++)
+              if ((RAWM >> q) & 1) rv.f[q][i] = FT(raw_field(q, ev));
+          } else if constexpr (RAWF) {
 #pragma unroll
             for (int q = 0; q < NC; q++) rv.f[q][i] = sh.mode[q] == RAW ? FT(raw_field(q, ev)) : FT(0);
           }
+          if constexpr (NVL > 4) __builtin_amdgcn_sched_barrier(0);   // addresses of one vector live at a time
         }
       };
       constexpr int NR = S / RND;   // rounds, an even number
@@ -317,68 +379,64 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           pend = false;
         }
         if (lim > 0) {
-          // Symbols are staged four to a word.  cur holds the bytes of the
-          // word being filled; each lookup writes that word and the next
-          // (aligned stores; the next word holds what spilled over) and
-          // moves on when the word is complete -- no branch per lookup.
-          // The window is refilled, also without branches, with 32 bits
-          // whenever fewer than 32 remain: enough for the two lookups of an
-          // iteration (at most 22 bits).
-          uint32_t cur = 0;
-          uint32_t *wp = sp;        // the word being filled
-          if (ov) {  // symbols of this strip decoded last round: words 8, 9 -> 0, 1
-            const uint32_t c8 = sp[8 * DEC_NT], c9 = sp[9 * DEC_NT];
-            sp[0] = c8;
-            sp[DEC_NT] = c9;
-            cur = ov >= 4 ? c9 : c8;
-            wp = ov >= 4 ? sp + DEC_NT : sp;
+          // Each lookup stores its (up to three) symbols as bytes at pos and
+          // moves pos on by their number; bytes past the valid ones are
+          // overwritten by the next lookup.  The window is refilled, without
+          // branches, with 32 bits whenever fewer than 30 remain: enough for
+          // the two lookups of an iteration (at most 22 bits), and the word
+          // lands at bit nb + 2 <= 31 of W, so nothing falls off its top.
+          if (ov) {  // symbols of this strip decoded last round: bytes 32.. -> 0..
+            uint32_t *sw = reinterpret_cast<uint32_t *>(sb);
+            const uint32_t c8 = sw[8], c9 = sw[9];
+            sw[0] = c8;
+            sw[1] = c9;
           }
-          int pos = ov;             // symbols of this strip decoded so far
-          uint32_t na = ov & 3;     // bytes in cur
-          pre = rp[(wpos & (RING - 1)) * DEC_NT];
-          auto emit = [&](uint32_t e) {
-            const uint64_t tt = uint64_t(e & 0xFFFFFF) << (8 * na);
-            const uint32_t lo = cur | uint32_t(tt), hi = uint32_t(tt >> 32);
-            wp[0] = lo;
-            wp[DEC_NT] = hi;
-            const uint32_t m = e >> 28;
-            pos += int(m);
-            na += m;
-            const bool full = na >= 4;
-            cur = full ? hi : lo;
-            wp += full ? DEC_NT : 0;
-            na &= 3;
+          // a: stage byte of the next symbol; nbk + 64 a == nb + 2 at all
+          // times, so a lookup updates both with its low byte (bits used +
+          // 64 x symbols) and the refill test needs one multiply-add.
+          const uint32_t abase = uint32_t(tid * STB);
+          uint32_t a = abase + uint32_t(ov);
+          const uint32_t alim = abase + uint32_t(lim);
+          uint32_t nbk = uint32_t(nb + 2) - (a << 6);
+          pre = rp[__builtin_amdgcn_ubfe(wpos, 0, 5) * DEC_NT];
+          const uint8_t *lutb = reinterpret_cast<const uint8_t *>(lut);
+          uint8_t *const st = sh.u.stage;
+          auto step = [&]() {
+            const uint32_t e = *reinterpret_cast<const uint32_t *>(lutb + (uint32_t(W) & 0x1FFCu));
+            const uint32_t x = __builtin_amdgcn_alignbyte(e, e, 1);   // symbols 0 and 2 in bytes 0 and 2
+            st[a] = uint8_t(x);
+            st[a + 1] = uint8_t(e >> 16);
+            st[a + 2] = uint8_t(x >> 16);
+            a += (e >> 6) & 3;
+            W >>= (e & 63);
+            nbk -= e & 0xFF;
           };
-          while (pos < lim) {
-            const bool need = nb < 32;
-            buf |= uint64_t(need ? pre : 0u) << nb;
-            nb += need ? 32 : 0;
+          while (a < alim) {
+            const uint32_t t = nbk + (a << 6);   // nb + 2
+            const bool need = t < 32;
+            W |= uint64_t(need ? pre : 0u) << t;
+            nbk += need ? 32u : 0u;
             wpos += need ? 1u : 0u;
-            pre = rp[(wpos & (RING - 1)) * DEC_NT];
-            uint32_t e = lut[buf & (kLutSize - 1)];
-            emit(e);
-            uint32_t bl = (e >> 24) & 15;
-            buf >>= bl;
-            nb -= int(bl);
-            e = lut[buf & (kLutSize - 1)];
-            emit(e);
-            bl = (e >> 24) & 15;
-            buf >>= bl;
-            nb -= int(bl);
+            pre = rp[__builtin_amdgcn_ubfe(wpos, 0, 5) * DEC_NT];
+            step();
+            step();
           }
+          const int pos = int(a - abase);
+          nb = int(nbk + (a << 6)) - 2;
           ov = pos - lim;   // at most 5: the loop stops 2 lookups of 3 symbols past lim - 1
           if (last) {
             // exact end: the segment must use exactly its stored bit length
             uint64_t bpos = uint64_t(wpos - adj) * 32 - uint32_t(nb);
             for (int x = 0; x < ov; x++) {
               const int bb = lim + x;
-              bpos -= sh.len[p][(sp[(bb >> 2) * DEC_NT] >> (8 * (bb & 3))) & 0xFF];
+              bpos -= sh.len[p][sb[bb]];
             }
             if (bpos != uint64_t(b0) + sbits) bad = 1;
             ov = 0;
           } else if (((wpos + 11) >> 4) >= nsec) {
             // lim == RND here.  The next round reads at most 32 lookups (352
-            // bits) with at least 10 bits left in the window, so words
+            // bits); the window now holds at least 8 bits and takes a word
+            // only while it holds fewer than 30, so at most 12 words
             // [wpos, wpos + 12): at most one sector past those in the ring,
             // whose slot held a sector before wpos's.
             ps0 = grp(4 * nsec);
@@ -389,84 +447,86 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           }
         }
         wave_lds_sync();
-        // merge and store: vector v of this wave covers VE elements of slot v / VPS
-#pragma unroll
-        for (int i = 0; i < NVL; i++) {
+        // merge: vector v of this wave covers VE elements of slot v / VPS
+        auto vec = [&](int i, uint32_t &ev, bool &valid) -> u32x4 {
           const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
           const int sjv = g * GS + wv * SPW + sl;
-          const uint32_t qv = uint32_t(r) * nseg + sjv;
-          const uint32_t ev = qv * RND + part * VE;
-          const bool valid = sjv < nseg && ev < n;
+          ev = (uint32_t(r) * nseg + sjv) * RND + part * VE;
+          valid = sjv < nseg && ev < n;
           // staged bytes of coded stream pp for this vector (VE bytes)
           auto staged = [&](int pp, int h) -> uint64_t {
             const int th = t0 + cidx[pp] * SPW + sl;
-            if constexpr (ES == 2) return stg_pair(sh.u.stage, 2 * part, th);
-            else if constexpr (ES == 4) return sh.u.stage[part * DEC_NT + th];
-            else return stg_pair(sh.u.stage, 4 * part + 2 * h, th);
+            if constexpr (ES == 2) return stg8(sh.u.stage, 8 * part, th);
+            else if constexpr (ES == 4) return *reinterpret_cast<const uint32_t *>(sh.u.stage + th * STB + 4 * part);
+            else return stg8(sh.u.stage, 16 * part + 8 * h, th);
           };
           auto fieldv = [&](int pp, int h) -> uint64_t {   // h: 8-byte half (FP8)
-            const int md = sh.mode[pp];
-            if (md == CONST) return cfield(pp);
-            if (md != RAW || !RAWF) return staged(pp, h);
-            return rawv.f[pp][i];
+            if constexpr (ALLC) {
+              return staged(pp, h);
+            } else if constexpr (RAWM != 0) {
+              return ((RAWM >> pp) & 1) ? uint64_t(rawv.f[pp][i]) : staged(pp, h);
+            } else {
+              const int md = sh.mode[pp];
+              if (md == CONST) return cfield(pp);
+              if (md != RAW || !RAWF) return staged(pp, h);
+              return rawv.f[pp][i];
+            }
           };
           u32x4 o;
           if constexpr (DT == BF16) {
             o = merge_bf16(fieldv(0, 0), rawv.plane[i]);
           } else if constexpr (DT == FP32) {
-            uint32_t P[4];
-#pragma unroll
-            for (int pp = 0; pp < 4; pp++) P[pp] = uint32_t(fieldv(pp, 0));
-#pragma unroll
-            for (int x = 0; x < 4; x++) {
-              const uint32_t p0 = (P[0] >> (8 * x)) & 0xFF, p1 = (P[1] >> (8 * x)) & 0xFF;
-              const uint32_t p2 = (P[2] >> (8 * x)) & 0xFF, p3 = (P[3] >> (8 * x)) & 0xFF;
-              o[x] = ((p1 & 0x80) << 24) | (p0 << 23) | ((p1 & 0x7F) << 16) | (p2 << 8) | p3;
-            }
+            o = merge_fp32(uint32_t(fieldv(0, 0)), uint32_t(fieldv(1, 0)), uint32_t(fieldv(2, 0)),
+                           uint32_t(fieldv(3, 0)));
           } else {
             // E4 and M3 of the 16 elements as bytes, from whichever source
             uint64_t Ev[2], Mv[2];
-            const int m0 = sh.mode[0], m1 = sh.mode[1];
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-              if (m0 == RAW) {
-                const uint64_t x = rawv.f[0][i] >> (32 * h);   // 8 nibbles
-                uint64_t y = 0;
-#pragma unroll
-                for (int j = 0; j < 8; j++) y |= ((x >> (4 * j)) & 15) << (8 * j);
-                Ev[h] = y;
-              } else {
-                Ev[h] = fieldv(0, h);
-              }
-              if (m1 == RAW) {
-                const uint64_t x = rawv.f[1][i] >> (24 * h);   // 8 values of 3 bits
-                uint64_t y = 0;
-#pragma unroll
-                for (int j = 0; j < 8; j++) y |= ((x >> (3 * j)) & 7) << (8 * j);
-                Mv[h] = y;
-              } else {
-                Mv[h] = fieldv(1, h);
-              }
+              const bool r0 = RAWM != 0 ? (RAWM & 1) != 0 : !ALLC && RAWF && sh.mode[0] == RAW;
+              const bool r1 = RAWM != 0 ? (RAWM & 2) != 0 : !ALLC && RAWF && sh.mode[1] == RAW;
+              if (r0) Ev[h] = nib_bytes(uint32_t(rawv.f[0][i] >> (32 * h)));
+              else Ev[h] = fieldv(0, h);
+              if (r1) Mv[h] = tri_bytes(uint32_t(rawv.f[1][i] >> (24 * h)));
+              else Mv[h] = fieldv(1, h);
             }
 #pragma unroll
             for (int x = 0; x < 4; x++) {
               const uint32_t e4 = uint32_t(Ev[x >> 1] >> (32 * (x & 1)));
               const uint32_t m3 = uint32_t(Mv[x >> 1] >> (32 * (x & 1)));
               const uint32_t sg = uint32_t(rawv.plane[i] >> (4 * x)) & 15;
-              const uint32_t sb = ((sg & 1) << 7) | ((sg & 2) << 14) | ((sg & 4) << 21) | ((sg & 8) << 28);
-              o[x] = (e4 << 3) | m3 | sb;
+              // sign bits 0..3 to bits 7, 15, 23, 31
+              o[x] = (e4 << 3) | m3 | (((sg * 0x204081u) << 7) & 0x80808080u);
             }
           }
-          // Every lane stores one vector per iteration -- lanes without a
-          // whole aligned vector store into the scratch sink -- so each round
-          // issues the same stores and the compiler's waits for older loads
-          // never have to drain them.
-          uint8_t *op = dst + uint64_t(ev) * ES;
+          return o;
+        };
+        // Every lane stores one vector per iteration -- lanes without a
+        // whole aligned vector store into the scratch sink -- so each round
+        // issues the same stores and the compiler's waits for older loads
+        // never have to drain them.
+        bool partial = false;
+#pragma unroll
+        for (int i = 0; i < NVL; i++) {
+          uint32_t ev;
+          bool valid;
+          const u32x4 o = vec(i, ev, valid);
           const bool whole = valid && ev + VE <= n && oaligned;
-          stg16(whole ? op : sink, o);
-          if (valid && !whole) {  // a partial last vector or an unaligned output
-            const uint32_t cnt_b = (ev + VE <= n ? VE : n - ev) * ES;
-            for (uint32_t b = 0; b < cnt_b; b++) stg1(op + b, o[b >> 2] >> ((b & 3) * 8));
+          stg16(whole ? dst + uint64_t(ev) * ES : sink, o);
+          partial |= valid && !whole;
+          __builtin_amdgcn_sched_barrier(0);   // one vector at a time: fewer registers live
+        }
+        if (__ballot(partial)) {  // the last vectors of a tensor, or an unaligned output
+#pragma unroll
+          for (int i = 0; i < NVL; i++) {
+            uint32_t ev;
+            bool valid;
+            const u32x4 o = vec(i, ev, valid);
+            if (valid && !(ev + VE <= n && oaligned)) {
+              uint8_t *op = dst + uint64_t(ev) * ES;
+              const uint32_t cnt_b = (ev + VE <= n ? VE : n - ev) * ES;
+              for (uint32_t b = 0; b < cnt_b; b++) stg1(op + b, o[b >> 2] >> ((b & 3) * 8));
+            }
           }
         }
         wave_lds_sync();
@@ -491,14 +551,28 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   using I64 = std::integral_constant<int, 64>;
   using T = std::true_type;
   using F = std::false_type;
-  if (ncc <= 1) {
-    if (anyraw) path(I64{}, T{}); else path(I64{}, F{});
-  } else if constexpr (NC >= 2) {
-    if (ncc == 2) {
-      if (anyraw) path(I32{}, T{}); else path(I32{}, F{});
-    } else if constexpr (NC == 4) {
-      if (anyraw) path(I16{}, T{}); else path(I16{}, F{});
-    }
+  using I0 = std::integral_constant<int, 0>;
+  using I2 = std::integral_constant<int, 2>;
+  using I14 = std::integral_constant<int, 14>;
+  if (ncc == NC) {
+    if constexpr (NC == 1) path(I64{}, F{}, T{}, I0{});
+    else if constexpr (NC == 2) path(I32{}, F{}, T{}, I0{});
+    else path(I16{}, F{}, T{}, I0{});
+  } else if constexpr (NC == 1) {
+    if (anyraw) path(I64{}, T{}, F{}, I0{}); else path(I64{}, F{}, F{}, I0{});
+  } else if constexpr (NC == 2) {
+    // usual FP8 weights: E4 coded, M3 raw
+    if (ncc == 1 && cs[0] == 0 && sh.mode[1] == RAW) path(I64{}, T{}, F{}, I2{});
+    else if (anyraw) path(I64{}, T{}, F{}, I0{});
+    else path(I64{}, F{}, F{}, I0{});
+  } else {
+    // usual FP32 weights: exponent coded, the three fraction bytes raw.
+    // Any other mix takes 16 lanes per stream, whatever ncc is: few
+    // vectors per lane keep the registers of this rare case small.
+    if (ncc == 1 && cs[0] == 0 && sh.mode[1] == RAW && sh.mode[2] == RAW && sh.mode[3] == RAW)
+      path(I64{}, T{}, F{}, I14{});
+    else if (anyraw) path(I16{}, T{}, F{}, I0{});
+    else path(I16{}, F{}, F{}, I0{});
   }
   if (bad) atomicOr(&a.ctl[0], kErrCorrupt);
 }
