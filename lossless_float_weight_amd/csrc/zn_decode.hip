@@ -233,13 +233,15 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   auto cfield = [&](int p) -> uint64_t { return 0x0101010101010101ull * uint64_t(sh.aux[p]); };
 
   int bad = 0;
-  auto path = [&](auto spw_c, auto rawf_c, auto allc_c, auto rawm_c) {
+  auto path = [&](auto spw_c, auto rawf_c, auto allc_c, auto rawm_c, auto constm_c) {
     constexpr int SPW = decltype(spw_c)::value;   // lanes per coded stream per wave
     constexpr bool RAWF = decltype(rawf_c)::value; // some stream is stored raw
     constexpr bool ALLC = decltype(allc_c)::value; // every stream is coded
-    // RAWM != 0: stream p is raw if bit p is set and coded otherwise, known
-    // here, so only the raw streams' fields are loaded and held
+    // RAWM != 0: stream p is raw if bit p of RAWM is set, constant if bit p
+    // of CONSTM is, coded otherwise -- known here, so only the raw streams'
+    // fields are loaded and held and no mode is tested per vector
     constexpr int RAWM = decltype(rawm_c)::value;
+    constexpr int CONSTM = decltype(constm_c)::value;
     constexpr int GS = 4 * SPW;                   // segments per coded stream per group
     constexpr int VPS = RND * ES / 16;            // output vectors per strip
     constexpr int NVL = SPW * VPS / 64;           // output vectors per lane per round
@@ -268,7 +270,10 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       if (coded && live) sbits = ldg2(in + sh.seg_off[p] + 2 * sj);
       const uint32_t incl = wave_incl_scan(sbits);
       const int first = ci * SPW;
-      const uint32_t wbase = first > 0 ? __shfl(incl, first - 1, 64) : 0;
+      // every lane takes part in the shuffle: a lane left out of it by a
+      // branch returns 0 to the lanes reading from it
+      const uint32_t wprev = __shfl(incl, (first + 63) & 63, 64);
+      const uint32_t wbase = first > 0 ? wprev : 0;
       const uint32_t wlast = __shfl(incl, (first + SPW - 1) & 63, 64);
       if (coded && ln == first) sh.wtot[wv][ci] = wlast - wbase;
       __syncthreads();
@@ -464,6 +469,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             if constexpr (ALLC) {
               return staged(pp, h);
             } else if constexpr (RAWM != 0) {
+              if ((CONSTM >> pp) & 1) return cfield(pp);
               return ((RAWM >> pp) & 1) ? uint64_t(rawv.f[pp][i]) : staged(pp, h);
             } else {
               const int md = sh.mode[pp];
@@ -553,26 +559,34 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   using F = std::false_type;
   using I0 = std::integral_constant<int, 0>;
   using I2 = std::integral_constant<int, 2>;
+  using I12 = std::integral_constant<int, 12>;
   using I14 = std::integral_constant<int, 14>;
+  int rawm = 0, constm = 0;
+#pragma unroll
+  for (int p = 0; p < NC; p++) {
+    rawm |= int(sh.mode[p] == RAW) << p;
+    constm |= int(sh.mode[p] == CONST) << p;
+  }
   if (ncc == NC) {
-    if constexpr (NC == 1) path(I64{}, F{}, T{}, I0{});
-    else if constexpr (NC == 2) path(I32{}, F{}, T{}, I0{});
-    else path(I16{}, F{}, T{}, I0{});
+    if constexpr (NC == 1) path(I64{}, F{}, T{}, I0{}, I0{});
+    else if constexpr (NC == 2) path(I32{}, F{}, T{}, I0{}, I0{});
+    else path(I16{}, F{}, T{}, I0{}, I0{});
   } else if constexpr (NC == 1) {
-    if (anyraw) path(I64{}, T{}, F{}, I0{}); else path(I64{}, F{}, F{}, I0{});
+    if (anyraw) path(I64{}, T{}, F{}, I0{}, I0{}); else path(I64{}, F{}, F{}, I0{}, I0{});
   } else if constexpr (NC == 2) {
     // usual FP8 weights: E4 coded, M3 raw
-    if (ncc == 1 && cs[0] == 0 && sh.mode[1] == RAW) path(I64{}, T{}, F{}, I2{});
-    else if (anyraw) path(I64{}, T{}, F{}, I0{});
-    else path(I64{}, F{}, F{}, I0{});
+    if (ncc == 1 && rawm == 2) path(I64{}, T{}, F{}, I2{}, I0{});
+    else if (anyraw) path(I64{}, T{}, F{}, I0{}, I0{});
+    else path(I64{}, F{}, F{}, I0{}, I0{});
   } else {
-    // usual FP32 weights: exponent coded, the three fraction bytes raw.
-    // Any other mix takes 16 lanes per stream, whatever ncc is: few
-    // vectors per lane keep the registers of this rare case small.
-    if (ncc == 1 && cs[0] == 0 && sh.mode[1] == RAW && sh.mode[2] == RAW && sh.mode[3] == RAW)
-      path(I64{}, T{}, F{}, I14{});
-    else if (anyraw) path(I16{}, T{}, F{}, I0{});
-    else path(I16{}, F{}, F{}, I0{});
+    // usual FP32 weights: exponent coded, the three fraction bytes raw, or
+    // the low two constant (values that are rounded BF16).  Any other mix
+    // takes 16 lanes per stream, whatever ncc is: few vectors per lane keep
+    // the registers of this rare case small.
+    if (ncc == 1 && rawm == 14) path(I64{}, T{}, F{}, I14{}, I0{});
+    else if (ncc == 1 && rawm == 2 && constm == 12) path(I64{}, T{}, F{}, I2{}, I12{});
+    else if (anyraw) path(I16{}, T{}, F{}, I0{}, I0{});
+    else path(I16{}, F{}, F{}, I0{}, I0{});
   }
   if (bad) atomicOr(&a.ctl[0], kErrCorrupt);
 }

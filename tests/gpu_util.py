@@ -44,6 +44,26 @@ def record_bounds(blob: np.ndarray):
     return off_dir, n_chunks, dirv.astype(np.int64)
 
 
+def field_modes(blob: np.ndarray, n_fields: int, kbits):
+    """Per chunk, the tuple of its streams' modes (0 raw, 1 constant, 2 Huffman,
+    3 group) read from the records (format: 8-byte stream head, code lengths
+    as nibbles when Huffman, u16 segment bit lengths when coded, then the
+    16-byte aligned payload)."""
+    _, n_chunks, dirv = record_bounds(blob)
+    out = []
+    for c in range(n_chunks):
+        pos, modes = int(dirv[c]), []
+        for p in range(n_fields):
+            h0 = int(np.frombuffer(blob[pos:pos + 4].tobytes(), np.uint32)[0])
+            pay = int(np.frombuffer(blob[pos + 4:pos + 8].tobytes(), np.uint32)[0])
+            mode, nseg = h0 & 0xFF, h0 >> 16
+            head = 8 + ((1 << kbits[p]) // 2 if mode == 2 else 0) + (2 * nseg if mode in (2, 3) else 0)
+            pos += ((head + 15) & ~15) + ((pay + 15) & ~15)
+            modes.append(mode)
+        out.append(tuple(modes))
+    return out
+
+
 def sample_chunks(n_chunks: int, k: int, seed: int = 0):
     rng = np.random.default_rng(seed)
     pick = {0, n_chunks - 1}

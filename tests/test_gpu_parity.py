@@ -12,7 +12,7 @@ import torch
 
 from lossless_float_weight_amd import workloads as W
 from lossless_float_weight_amd import zn
-from tests.gpu_util import (assert_roundtrip, first_difference, gpu_compress, record_bounds,
+from tests.gpu_util import (assert_roundtrip, field_modes, first_difference, gpu_compress, record_bounds,
                             sample_chunks, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +88,44 @@ def test_fp32_ragged_and_random(oracle, n):
     x = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), generator=g, dtype=torch.int32).view(torch.float32)
     y = W.gaussian(n, 0.0, 0.02, torch.float32, "cpu", n, 2)
     _check_equal(oracle, oracle.FP32, [x.cuda(), y.cuda()], 16384)
+
+
+def _fp32_mixes():
+    """One FP32 tensor per chunk (16 KiB chunks of 4096 values), each with
+    another mix of coded, raw and constant field bytes."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    n = 4096
+    small = torch.randint(0, 16, (n,), generator=g).to(torch.float32)          # 2 coded, 2 constant
+    pick = torch.randn(23, generator=g)[torch.randint(0, 23, (n,), generator=g)]  # all 4 coded
+    top = (torch.randint(0, 8, (n,), generator=g) << 16) | torch.randint(0, 1 << 16, (n,), generator=g)
+    mixed = ((torch.randint(120, 124, (n,), generator=g) << 23) | top).to(torch.int32).view(torch.float32)
+    sparse = torch.randint(0, 1 << 16, (n,), generator=g).to(torch.int32).view(torch.float32)  # 2 raw, 2 const
+    return [small, pick, mixed, sparse]
+
+
+def test_fp32_every_decode_path(oracle):
+    # all coded; coded exponent + raw fraction; coded + raw + constant;
+    # several coded streams with raw ones; raw and constant only
+    print("case: FP32 field-mode mixes", flush=True)
+    ts = [t.cuda() for t in _fp32_mixes()] + [W.gaussian(4096, 0.0, 0.02, torch.float32, "cuda", 9, 0)]
+    _, blob = _check_equal(oracle, oracle.FP32, ts, 16384)
+    modes = set(field_modes(blob.cpu().numpy(), 4, [8, 8, 8, 8]))
+    assert (2, 2, 2, 2) in modes and (2, 0, 0, 0) in modes
+    assert any(m.count(2) in (2, 3) and 0 in m for m in modes)
+    assert any(1 in m and 2 in m for m in modes) and any(2 not in m for m in modes)
+
+
+def test_fp8_every_decode_path(oracle):
+    print("case: FP8 field-mode mixes", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(8)
+    n = 4096
+    both = torch.randint(0, 6, (n,), generator=g).to(torch.uint8) * 9          # E4 and M3 skewed: both coded
+    m3 = (torch.randint(0, 16, (n,), generator=g) << 3 | torch.randint(0, 2, (n,), generator=g)).to(torch.uint8)
+    e4 = W.fp8_blockscaled(n, device="cpu")[0][1].view(torch.uint8)             # E4 coded, M3 raw
+    ts = [x.view(torch.float8_e4m3fn).cuda() for x in (both, m3, e4)]
+    _, blob = _check_equal(oracle, oracle.FP8_E4M3, ts, 4096)
+    modes = set(field_modes(blob.cpu().numpy(), 2, [4, 3]))
+    assert (2, 2) in modes and (2, 0) in modes and (0, 2) in modes
 
 
 def test_fp8_blockscaled(oracle):
