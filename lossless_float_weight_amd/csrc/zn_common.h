@@ -474,12 +474,14 @@ struct LutShared {
 // Builds the multi-symbol decode table of a canonical code from its lengths.
 // lut[v] for an 11-bit LSB-first window v holds up to three whole code words:
 // bits 0-5 the bits they use (so the entry itself can serve as a shift
-// amount), 6-7 their number, 8-15, 16-23, 24-31 the symbols.  t1 (2048 x u16, scratch) is the single-symbol table indexed by the
-// window read first-bit-as-MSB.  Returns false (for every thread) if the
+// amount), 6-7 their number, 8-15, 16-23, 24-31 the symbols.  t1 (2048 x
+// u16, scratch) is the single-symbol table, indexed like lut by the LSB-first
+// window: symbol | length << 8.  Returns false (for every thread) if the
 // lengths are not a complete prefix code of at least two words with lengths
 // <= 11.  NT >= 256 threads; A <= 256.
 template <int NT>
-__device__ bool build_lut(const uint8_t *len, int A, uint32_t *lut, uint16_t *t1, LutShared &S) {
+__device__ __attribute__((always_inline)) bool build_lut(const uint8_t *len, int A, uint32_t *lut, uint16_t *t1,
+                                                     LutShared &S) {
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
   const int l = tid < A ? len[tid] : 0;
   int rank = 0;
@@ -491,21 +493,29 @@ __device__ bool build_lut(const uint8_t *len, int A, uint32_t *lut, uint16_t *t1
   if (tid == 0) S.bad = 0;
   __syncthreads();
   if (tid < A && l > kMaxLen) S.bad = 1;
-  if (tid == 0) {
-    uint32_t code = 0, kraft = 0;
-    int o = 0, d = 0;
-    for (int b = 1; b <= kMaxLen; b++) {
-      const int c = S.cnt[0][b] + S.cnt[1][b] + S.cnt[2][b] + S.cnt[3][b];
-      const int pc = b > 1 ? S.cnt[0][b - 1] + S.cnt[1][b - 1] + S.cnt[2][b - 1] + S.cnt[3][b - 1] : 0;
-      code = (code + pc) << 1;
-      S.first[b] = int(code);
-      S.offs[b] = o;
-      S.ljend[b] = int((code + c) << (kMaxLen - b));
-      o += c;
-      d += c;
-      kraft += uint32_t(c) << (kMaxLen - b);
+  if (wv == 0) {
+    // lane b (1..11): the number of codes of length b, the sorted index of
+    // the first of them, the first canonical code of length b (the sum of
+    // c_j << (b - j) over j < b) and the end of its range left-justified
+    const int b = ln;
+    const bool isb = b >= 1 && b <= kMaxLen;
+    const int c = isb ? S.cnt[0][b] + S.cnt[1][b] + S.cnt[2][b] + S.cnt[3][b] : 0;
+    const uint32_t incl = wave_incl_scan(uint32_t(c));
+    uint32_t first = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxLen; j++) {
+      const uint32_t cj = uint32_t(__builtin_amdgcn_readlane(c, j));
+      first += j < b ? cj << (b - j) : 0u;
     }
-    if (d < 2 || kraft != (1u << kMaxLen)) S.bad = 1;
+    const uint32_t kr = wave_incl_scan(isb ? uint32_t(c) << (kMaxLen - (isb ? b : 1)) : 0u);
+    const uint32_t kraft = uint32_t(__builtin_amdgcn_readlane(int(kr), 63));
+    const uint32_t d = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+    if (isb) {
+      S.first[b] = int(first);
+      S.offs[b] = int(incl) - c;
+      S.ljend[b] = int((first + uint32_t(c)) << (kMaxLen - b));
+    }
+    if (ln == 0 && (d < 2 || kraft != (1u << kMaxLen))) S.bad = 1;
   }
   __syncthreads();
   if (S.bad) return false;
@@ -515,31 +525,73 @@ __device__ bool build_lut(const uint8_t *len, int A, uint32_t *lut, uint16_t *t1
     S.sorted[pos] = uint8_t(tid);
   }
   __syncthreads();
-  for (int u = tid; u < kLutSize; u += NT) {
-    int b = 1;
-    while (b < kMaxLen && u >= S.ljend[b]) b++;
-    const int idx = (u >> (kMaxLen - b)) - S.first[b];
-    t1[u] = uint16_t(S.sorted[S.offs[b] + idx] | (b << 8));
-  }
-  __syncthreads();
-  for (int v = tid; v < kLutSize; v += NT) {
-    uint32_t w = uint32_t(v);
-    uint32_t e = t1[__builtin_bitreverse32(w) >> (32 - kMaxLen)];
-    int used = int(e >> 8), n = 1;
-    uint32_t syms = e & 0xFF;
-    w >>= used;
+  // single-symbol table: the length of the code starting a window is one
+  // more than the number of lengths whose range ends at or below it.
+  // Counted with subtract-and-shift in inline asm: as compares they would
+  // all write one condition register and serialise the entries of a thread.
+  // All lengths first, then all table reads, then all writes, so that the
+  // reads of the eight entries of a thread overlap.
+  static_assert(kLutSize % NT == 0, "whole passes");
+  constexpr int PER = kLutSize / NT;
+  int ljm[kMaxLen];
 #pragma unroll
-    for (int q = 1; q < 3; q++) {
-      const uint32_t e2 = t1[__builtin_bitreverse32(w) >> (32 - kMaxLen)];
-      const int l2 = int(e2 >> 8);
-      if (used + l2 > kMaxLen || n != q) break;
-      syms |= (e2 & 0xFF) << (8 * q);
-      used += l2;
-      w >>= l2;
-      n++;
+  for (int j = 1; j < kMaxLen; j++) ljm[j] = S.ljend[j] - 1;
+  // Entry v of t1 is the code starting the LSB-first window v, whose
+  // first-bit-as-MSB reading u = reverse(v) is what the ranges compare.
+  // Threads take consecutive v, so both the stores here and the first
+  // lookups below fall in distinct LDS banks.
+  auto rev11 = [](int v) { return int(__builtin_bitreverse32(uint32_t(v)) >> (32 - kMaxLen)); };
+  int bl[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int u = rev11(tid + i * NT);
+    int b = 1;
+#pragma unroll
+    for (int j = 1; j < kMaxLen; j++) {
+      int ge;   // 1 if u >= ljend[j]
+      asm("v_sub_u32 %0, %1, %2\n\tv_lshrrev_b32 %0, 31, %0" : "=&v"(ge) : "v"(ljm[j]), "v"(u));
+      b += ge;
     }
-    lut[v] = uint32_t(used) | (uint32_t(n) << 6) | (syms << 8);
+    bl[i] = b;
   }
+  int fo[PER], of[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    fo[i] = S.first[bl[i]];
+    of[i] = S.offs[bl[i]];
+  }
+  uint32_t tv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int u = rev11(tid + i * NT);
+    tv[i] = uint32_t(S.sorted[of[i] + (u >> (kMaxLen - bl[i])) - fo[i]]) | uint32_t(bl[i] << 8);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; i++) t1[tid + i * NT] = uint16_t(tv[i]);
+  __syncthreads();
+  // up to three whole code words per 11-bit window, without branches; the
+  // three lookups of the eight entries of a thread go in three passes
+  auto t1at = [&](uint32_t w) { return uint32_t(t1[w]); };
+  uint32_t e1[PER], e2[PER], e3[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) e1[i] = t1at(uint32_t(tid + i * NT));
+#pragma unroll
+  for (int i = 0; i < PER; i++) e2[i] = t1at(uint32_t(tid + i * NT) >> (e1[i] >> 8));
+#pragma unroll
+  for (int i = 0; i < PER; i++) e3[i] = t1at((uint32_t(tid + i * NT) >> (e1[i] >> 8)) >> (e2[i] >> 8));
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const uint32_t l1 = e1[i] >> 8, l2 = e2[i] >> 8, l3 = e3[i] >> 8;
+    // all-ones masks: the second (third) word fits in the window
+    const uint32_t m2 = uint32_t(int(l1 + l2 - kMaxLen - 1) >> 31);
+    const uint32_t m3 = m2 & uint32_t(int(l1 + l2 + l3 - kMaxLen - 1) >> 31);
+    const uint32_t used = l1 + (l2 & m2) + (l3 & m3);
+    const uint32_t n = 1 + (m2 & 1) + (m3 & 1);
+    const uint32_t syms = (e1[i] & 0xFF) | (((e2[i] & 0xFF) << 8) & m2) | (((e3[i] & 0xFF) << 16) & m3);
+    tv[i] = used | (n << 6) | (syms << 8);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; i++) lut[tid + i * NT] = tv[i];
   __syncthreads();
   return true;
 }

@@ -171,6 +171,34 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     return;
   }
 
+  // ------------------------------------------------ 3. lanes and rounds
+  // Lanes decode only the Huffman- or group-coded streams; raw and constant
+  // streams need no decoding and the merge reads them straight from the
+  // record.  With ncc coded streams, SPW = 64, 32 or 16 lanes of each wave
+  // take one coded stream each (a template per SPW; the branch below is
+  // uniform per workgroup).
+  int ncc = 0, cs[NC], cidx[NC], rawm = 0, constm = 0;
+#pragma unroll
+  for (int p = 0; p < NC; p++) {
+    cidx[p] = -1;
+    if (sh.mode[p] == HUFF || sh.mode[p] == GROUP) { cs[ncc] = p; cidx[p] = ncc; ncc++; }
+    rawm |= int(sh.mode[p] == RAW) << p;
+    constm |= int(sh.mode[p] == CONST) << p;
+  }
+  // Lanes per coded stream, as the dispatch at the end chooses it: all
+  // coded streams share each wave; FP32 with a coded exponent and raw or
+  // constant fraction bytes gives the exponent every lane; any other FP32
+  // mix takes 16 lanes per stream.
+  const int spw = ncc == NC ? 64 / NC
+                  : NC <= 2 ? 64
+                  : ncc == 1 && (rawm == 14 || (rawm == 2 && constm == 12)) ? 64 : 16;
+  // The first segment length of this lane, loaded before the tables are
+  // built so that its latency overlaps the build.
+  uint32_t sbits0 = 0;
+  {
+    const int ci = ln / spw, sj = wv * spw + ln % spw;
+    if (ci < ncc && sj < nseg) sbits0 = ldg2(in + sh.seg_off[cs[ci]] + 2 * sj);
+  }
   // ---------------------------------------------------------- 2. tables
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k, mode = sh.mode[p];
@@ -190,18 +218,6 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   }
   __syncthreads();
 
-  // ------------------------------------------------ 3. lanes and rounds
-  // Lanes decode only the Huffman- or group-coded streams; raw and constant
-  // streams need no decoding and the merge reads them straight from the
-  // record.  With ncc coded streams, SPW = 64, 32 or 16 lanes of each wave
-  // take one coded stream each (a template per SPW; the branch below is
-  // uniform per workgroup).
-  int ncc = 0, cs[NC], cidx[NC];
-#pragma unroll
-  for (int p = 0; p < NC; p++) {
-    cidx[p] = -1;
-    if (sh.mode[p] == HUFF || sh.mode[p] == GROUP) { cs[ncc] = p; cidx[p] = ncc; ncc++; }
-  }
   // Fields of the raw streams for one 16-byte output vector of VE elements
   // starting at element ev (< n): k = 8 gives VE bytes, k = 4 VE nibbles,
   // k = 3 a 3*VE-bit run.  Every read stays inside the stream's payload, or
@@ -242,6 +258,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     // fields are loaded and held and no mode is tested per vector
     constexpr int RAWM = decltype(rawm_c)::value;
     constexpr int CONSTM = decltype(constm_c)::value;
+    if (spw != SPW) { bad = 1; return; }   // the layout sbits0 was loaded for
     constexpr int GS = 4 * SPW;                   // segments per coded stream per group
     constexpr int VPS = RND * ES / 16;            // output vectors per strip
     constexpr int NVL = SPW * VPS / 64;           // output vectors per lane per round
@@ -266,8 +283,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       const int sj = g * GS + slot;
       const bool live = sj < nseg;
       // start bit of the segment: scan of the stored segment bit lengths
-      uint32_t sbits = 0;
-      if (coded && live) sbits = ldg2(in + sh.seg_off[p] + 2 * sj);
+      uint32_t sbits = sbits0;
+      if (g > 0 && coded && live) sbits = ldg2(in + sh.seg_off[p] + 2 * sj);
       const uint32_t incl = wave_incl_scan(sbits);
       const int first = ci * SPW;
       // every lane takes part in the shuffle: a lane left out of it by a
@@ -561,12 +578,6 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   using I2 = std::integral_constant<int, 2>;
   using I12 = std::integral_constant<int, 12>;
   using I14 = std::integral_constant<int, 14>;
-  int rawm = 0, constm = 0;
-#pragma unroll
-  for (int p = 0; p < NC; p++) {
-    rawm |= int(sh.mode[p] == RAW) << p;
-    constm |= int(sh.mode[p] == CONST) << p;
-  }
   if (ncc == NC) {
     if constexpr (NC == 1) path(I64{}, F{}, T{}, I0{}, I0{});
     else if constexpr (NC == 2) path(I32{}, F{}, T{}, I0{}, I0{});
