@@ -86,6 +86,9 @@ __device__ __forceinline__ u32x2 ldg8s(const void *p) {
   return __builtin_nontemporal_load((const ZN_GLOBAL u32x2 *)(p));
 }
 __device__ __forceinline__ void stg16(void *p, u32x4 v) { *(ZN_GLOBAL u32x4 *)(p) = v; }
+// Streaming store of output read by nothing here: the non-temporal hint
+// writes it through instead of leaving dirty lines for later kernels to evict.
+__device__ __forceinline__ void stg16s(void *p, u32x4 v) { __builtin_nontemporal_store(v, (ZN_GLOBAL u32x4 *)(p)); }
 __device__ __forceinline__ void stg8(void *p, u32x2 v) { *(ZN_GLOBAL u32x2 *)(p) = v; }
 __device__ __forceinline__ void stg4(void *p, uint32_t v) { *(ZN_GLOBAL uint32_t *)(p) = v; }
 __device__ __forceinline__ void stg2(void *p, uint32_t v) { *(ZN_GLOBAL uint16_t *)(p) = uint16_t(v); }

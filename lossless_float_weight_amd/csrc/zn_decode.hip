@@ -321,6 +321,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       const uint32_t adj = uint32_t(pa & 63) / 4;   // payload word 0 is window word adj
       const uint32_t glast = adj / 4 + ngroups - 1; // last 16-byte group holding payload
       uint32_t wpos = 0, nsec = 0, pre = 0;         // next word to read, next sector to fetch
+      uint32_t slast = 0;                           // last sector holding bits of the segment
       u32x4 ps0 = {0, 0, 0, 0}, ps1 = ps0, ps2 = ps0, ps3 = ps0;
       bool pend = false;
       // 16-byte group gi of the window; groups past the payload read its last one
@@ -338,8 +339,12 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       };
       if (coded && live) {
         const uint32_t w0 = (b0 >> 5) + adj, s0 = w0 >> 4;
+        // No sector past the one holding the segment's last bit is loaded:
+        // it belongs to the next segment, whose lane read it long ago.
+        slast = (((b0 + sbits - 1) >> 5) + adj) >> 4;
+        const uint32_t s1 = s0 + 1 <= slast ? s0 + 1 : s0;
         const u32x4 a0 = grp(4 * s0), a1 = grp(4 * s0 + 1), a2 = grp(4 * s0 + 2), a3 = grp(4 * s0 + 3);
-        const u32x4 a4 = grp(4 * s0 + 4), a5 = grp(4 * s0 + 5), a6 = grp(4 * s0 + 6), a7 = grp(4 * s0 + 7);
+        const u32x4 a4 = grp(4 * s1), a5 = grp(4 * s1 + 1), a6 = grp(4 * s1 + 2), a7 = grp(4 * s1 + 3);
         put_sector(s0, a0, a1, a2, a3);
         put_sector(s0 + 1, a4, a5, a6, a7);
         nsec = s0 + 2;
@@ -350,7 +355,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       int ov = 0;         // symbols of the next strip decoded early (staged words 8, 9)
       // Raw bits and raw-stream fields merged by this lane in round r: the
       // same loads every round (an empty vector reads element 0 and is
-      // ignored), so no wait has to drain the stores in flight.  A partial
+      // ignored; r = -1, after the last round, reads element 0 everywhere),
+      // so no wait has to drain the stores in flight.  A partial
       // last vector stays inside the always-raw plane, whose size is padded
       // to 16 bytes: BF16 vectors start at multiples of 8 bytes, FP8 sign
       // words at multiples of 2.
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           const int v = ln + 64 * i, sl = v / VPS, part = v % VPS;
           const int sjv = g * GS + wv * SPW + sl;
           const uint32_t ev0 = (uint32_t(r) * nseg + sjv) * RND + part * VE;
-          const uint32_t ev = sjv < nseg && ev0 < n ? ev0 : 0;
+          const uint32_t ev = r >= 0 && sjv < nseg && ev0 < n ? ev0 : 0;
           if constexpr (DT == BF16) {
             const u32x2 x = ldg8s(rawp + ev);
             rv.plane[i] = x[0] | (uint64_t(x[1]) << 32);
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       // one decodes (the loop below alternates two register sets, so no copy
       // makes the compiler wait for loads in flight).
       auto round = [&](int r, const RawIn &rawv, RawIn &nxt) {
-        load_raw(r + 1 < NR ? r + 1 : r, nxt);  // the last round reloads its own: same count
+        load_raw(r + 1 < NR ? r + 1 : -1, nxt);  // the last round loads one line: same count
         const uint32_t q = uint32_t(r) * nseg + sj;   // this lane's strip
         const int lim = coded && live && q < nstrips ? int(min(uint32_t(RND), n - q * RND)) : 0;
         const bool last = live && q < nstrips && q + nseg >= nstrips;
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             }
             if (bpos != uint64_t(b0) + sbits) bad = 1;
             ov = 0;
-          } else if (((wpos + 11) >> 4) >= nsec) {
+          } else if (((wpos + 11) >> 4) >= nsec && nsec <= slast) {
             // lim == RND here.  The next round reads at most 32 lookups (352
             // bits); the window now holds at least 8 bits and takes a word
             // only while it holds fewer than 30, so at most 12 words
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           bool valid;
           const u32x4 o = vec(i, ev, valid);
           const bool whole = valid && ev + VE <= n && oaligned;
-          stg16(whole ? dst + uint64_t(ev) * ES : sink, o);
+          stg16s(whole ? dst + uint64_t(ev) * ES : sink, o);
           partial |= valid && !whole;
           __builtin_amdgcn_sched_barrier(0);   // one vector at a time: fewer registers live
         }
