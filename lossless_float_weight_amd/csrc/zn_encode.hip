@@ -88,6 +88,23 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   return v;
 }
 
+// Segments per wave in one pack tile: 16 symbols per lane per tile (more
+// per tile holds fewer workgroups per CU than the chunks need).
+constexpr int pack_g(int dt) { return segsyms(dt) / 64 >= 16 ? 1 : 16 / (segsyms(dt) / 64); }
+
+template <int DT>
+struct PackShared {
+  static constexpr int NC = ncoded(DT);
+  static constexpr int G = pack_g(DT);
+  // words of one tile at the longest codes, plus slack for the group ORs
+  static constexpr int STAGE = (PACK_NW * G * segsyms(DT) * kMaxLen + 31) / 32 + 4;
+  uint32_t enc[NC][256];
+  uint32_t stage[2][STAGE];      // alternate tiles use alternate buffers
+  uint32_t wtot[2][PACK_NW];
+  unsigned long long bits[NC], sec_off[NC];
+  int mode[NC], aux[NC];
+};
+
 template <int DT>
 struct EncShared {
   static constexpr int NC = ncoded(DT);
@@ -118,21 +135,6 @@ struct EncShared {
     } cb;
     WaveCB wcb;
   } u;
-};
-
-// Segments per wave in one pack tile: 16 symbols per lane per tile (more
-// per tile holds fewer workgroups per CU than the chunks need).
-constexpr int pack_g(int dt) { return segsyms(dt) / 64 >= 16 ? 1 : 16 / (segsyms(dt) / 64); }
-
-template <int DT>
-struct PackShared {
-  static constexpr int NC = ncoded(DT);
-  static constexpr int G = pack_g(DT);
-  // words of one tile at the longest codes, plus slack for the group ORs
-  static constexpr int STAGE = (PACK_NW * G * segsyms(DT) * kMaxLen + 31) / 32 + 4;
-  uint32_t enc[NC][256];
-  uint32_t stage[2][STAGE];      // alternate tiles use alternate buffers
-  uint32_t wtot[2][PACK_NW];
 };
 
 template <int DT>
@@ -176,20 +178,16 @@ __device__ __forceinline__ void count(EncShared<DT> &sh, int p, uint32_t b, int 
     atomicAdd(&sh.u.priv[bin * COLS + col], 1u);
 }
 
+// Steps 1 and 2 for chunk c: raw planes stored, histograms, and per coded
+// stream the mode, code and section offset in sh.  Returns the record size.
 template <int DT>
-// BF16: at most 7 waves' worth of registers per SIMD, so that every chunk of a
-// large workload is resident at once (the scalar registers would otherwise
-// allow 6 workgroups per CU; the extra ones spill to vector-register lanes,
-// not to memory).
-__global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT == BF16 ? 7 : 1))) void k_analyze(EncArgs a) {
+__device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT> &sh, uint32_t c) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int COLS = EncShared<DT>::COLS;
   constexpr int ENC_NT = EncShared<DT>::NT;
-  __shared__ EncShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
 
-  const uint32_t c = blockIdx.x;
   const int t = find_tensor(a.L, c);
   const uint64_t e0 = uint64_t(c - a.L.t_chunk0[t]) * a.L.chunk_elems;
   const uint64_t rem = a.L.t_n[t] - e0;
@@ -395,6 +393,20 @@ __global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT =
     rec += section_bytes(mode, k, n, nseg, mode == RAW ? 0 : sh.bits[p]);
     __syncthreads();
   }
+  return rec;
+}
+
+template <int DT>
+// BF16: at most 7 waves' worth of registers per SIMD, so that every chunk of a
+// large workload is resident at once (the scalar registers would otherwise
+// allow 6 workgroups per CU; the extra ones spill to vector-register lanes,
+// not to memory).
+__global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT == BF16 ? 7 : 1))) void k_analyze(EncArgs a) {
+  constexpr int NC = ncoded(DT);
+  __shared__ EncShared<DT> sh;
+  const int tid = threadIdx.x;
+  const uint32_t c = blockIdx.x;
+  const uint64_t rec = analyze_chunk<DT>(a, sh, c);
 
   // the plan: sizes and offsets, then the code words of coded streams
   uint8_t *plan = a.plans + uint64_t(c) * plan_stride(DT);
@@ -411,37 +423,32 @@ __global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT =
   }
 }
 
-// One workgroup per chunk: the record at its directory offset.
+// The record of chunk c at recp: stream heads, raw streams, coded payloads.
+// The choice per stream (mode, aux, payload bits, section offset) and the
+// code words come from LDS; stage and wtot are LDS scratch of this function.
 template <int DT>
-__global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
+__device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *const *in_ptrs, uint32_t c,
+                                           uint8_t *const recp, const uint32_t (*enc)[256], const int *pmode,
+                                           const int *paux, const unsigned long long *pbits,
+                                           const unsigned long long *psec,
+                                           uint32_t (*stage_all)[PackShared<DT>::STAGE],
+                                           uint32_t (*wtot)[PACK_NW]) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
   constexpr int NV = EPT / VE;         // vectors per thread per tile
   constexpr int NW = PACK_NW, ENC_NT = PACK_NT, G = PackShared<DT>::G;
   constexpr int STAGE = PackShared<DT>::STAGE;
-  __shared__ PackShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
-  if (a.ctl[0]) return;  // the container did not fit
 
-  const uint32_t c = blockIdx.x;
-  const int t = find_tensor(a.L, c);
-  const uint64_t e0 = uint64_t(c - a.L.t_chunk0[t]) * a.L.chunk_elems;
-  const uint64_t rem = a.L.t_n[t] - e0;
-  const uint32_t n = uint32_t(rem < a.L.chunk_elems ? rem : a.L.chunk_elems);
-  const uint8_t *src = a.in_ptrs[t] + e0 * ES;
+  const int t = find_tensor(L, c);
+  const uint64_t e0 = uint64_t(c - L.t_chunk0[t]) * L.chunk_elems;
+  const uint64_t rem = L.t_n[t] - e0;
+  const uint32_t n = uint32_t(rem < L.chunk_elems ? rem : L.chunk_elems);
+  const uint8_t *src = in_ptrs[t] + e0 * ES;
   const bool aligned = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
   const int nseg = int((n + S - 1) / S);
-  const uint8_t *plan = a.plans + uint64_t(c) * plan_stride(DT);
-  const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
-  uint8_t *const recp = a.out + dir[c];
-  for (int p = 0; p < NC; p++) {
-    const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
-    if (tid < A)
-      sh.enc[p][tid] = mode == RAW ? uint32_t(tid) | (uint32_t(k) << 16)
-                     : (mode == HUFF || mode == GROUP) ? ldg4(plan + 64 + 1024 * p + 4 * tid) : 0u;
-  }
-  for (int i = tid; i < 2 * STAGE; i += ENC_NT) sh.stage[i / STAGE][i % STAGE] = 0;
+  for (int i = tid; i < 2 * STAGE; i += ENC_NT) stage_all[i / STAGE][i % STAGE] = 0;
   __syncthreads();
 
   // ------------------------------------------- raw streams, in one pass
@@ -457,9 +464,9 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     uint8_t *pw[NC];
 #pragma unroll
     for (int p = 0; p < NC; p++) {
-      const int k = kbits(DT, p), mode = plan[48 + p];
+      const int k = kbits(DT, p), mode = pmode[p];
       rawmask |= uint32_t(mode == RAW) << p;
-      pw[p] = recp + *reinterpret_cast<const uint32_t *>(plan + 32 + 4 * p) + head_bytes_of(mode, k, nseg);
+      pw[p] = recp + psec[p] + head_bytes_of(mode, k, nseg);
     }
     if (rawmask) {
       u32x4 nx[NQ];
@@ -510,20 +517,20 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
 
   // -------------------------------------------------------- the record
   for (int p = 0; p < NC; p++) {
-    const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
-    const uint64_t bits = *reinterpret_cast<const uint64_t *>(plan + 8 * p);
-    uint8_t *sec = recp + *reinterpret_cast<const uint32_t *>(plan + 32 + 4 * p);
+    const int k = kbits(DT, p), A = 1 << k, mode = pmode[p];
+    const uint64_t bits = pbits[p];
+    uint8_t *sec = recp + psec[p];
     const uint64_t head = head_bytes_of(mode, k, nseg);
     const uint64_t pay = payload_bytes_of(mode, k, n, bits);
     // stream header, code lengths and the zero pad of the head
     if (tid == 0) {
       *reinterpret_cast<uint32_t *>(sec) =
-          uint32_t(mode) | (uint32_t(plan[52 + p]) << 8) | (uint32_t(nseg) << 16);
+          uint32_t(mode) | (uint32_t(paux[p]) << 8) | (uint32_t(nseg) << 16);
       *reinterpret_cast<uint32_t *>(sec + 4) = uint32_t(pay);
     }
     uint64_t used = 8;
     if (mode == HUFF) {
-      if (tid < A / 2) sec[8 + tid] = uint8_t((sh.enc[p][2 * tid] >> 16) | ((sh.enc[p][2 * tid + 1] >> 16) << 4));
+      if (tid < A / 2) sec[8 + tid] = uint8_t((enc[p][2 * tid] >> 16) | ((enc[p][2 * tid + 1] >> 16) << 4));
       used += A / 2;
     }
     if (mode == HUFF || mode == GROUP) used += 2ull * nseg;
@@ -568,7 +575,7 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     issue(0);
     for (int T = 0; T < ntiles; T++) {
       const int buf = T & 1;
-      uint32_t *stage = sh.stage[buf];
+      uint32_t *stage = stage_all[buf];
       // Concatenate each run's codes 8 (or, for 4-element runs, 4) at a time
       // without branches: pairs fit 22 bits, quads 44 bits (one u64), two
       // quads 88 bits (lo | hi<<64).
@@ -601,7 +608,7 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
 #pragma unroll
           for (int i = 0; i < GE; i++) {
             const int e = g8 * GE + i;
-            const uint32_t c = eb + e < n ? sh.enc[p][field_rt<DT>(w[e], p)] : 0u;
+            const uint32_t c = eb + e < n ? enc[p][field_rt<DT>(w[e], p)] : 0u;
             v[i] = c & 0xFFFF;
             l[i] = c >> 16;
           }
@@ -629,11 +636,11 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
         segtot[g] = uint32_t(__builtin_amdgcn_readlane(int(incl[g]), 63));
         wsum += segtot[g];
       }
-      if (ln == 0) sh.wtot[buf][wv] = wsum;
+      if (ln == 0) wtot[buf][wv] = wsum;
       __syncthreads();
       uint32_t woff = 0, ttot = 0;
       for (int q = 0; q < NW; q++) {
-        const uint32_t x = sh.wtot[buf][q];
+        const uint32_t x = wtot[buf][q];
         woff += q < wv ? x : 0;
         ttot += x;
       }
@@ -669,15 +676,15 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
         stage[i] = 0;
       }
       if (tid == 0) {
-        sh.stage[buf ^ 1][0] = stage[nfull];
+        stage_all[buf ^ 1][0] = stage[nfull];
         stage[nfull] = 0;
       }
       tbit += ttot;
     }
     uint32_t carry = 0;   // the partial last word (thread 0 moved it and reads it back)
     if (tid == 0) {
-      carry = sh.stage[ntiles & 1][0];
-      sh.stage[ntiles & 1][0] = 0;
+      carry = stage_all[ntiles & 1][0];
+      stage_all[ntiles & 1][0] = 0;
     }
     // last partial word and the zero pad of the payload
     const uint64_t words = (tbit + 31) >> 5;
@@ -685,6 +692,33 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     const uint64_t padw = align16(pay) / 4;
     for (uint64_t i = words + tid; i < padw; i += ENC_NT) pw[i] = 0;
   }
+}
+
+
+// One workgroup per chunk: the record at its directory offset.
+template <int DT>
+__global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
+  constexpr int NC = ncoded(DT);
+  __shared__ PackShared<DT> sh;
+  const int tid = threadIdx.x;
+  if (a.ctl[0]) return;  // the container did not fit
+  const uint32_t c = blockIdx.x;
+  const uint8_t *plan = a.plans + uint64_t(c) * plan_stride(DT);
+  for (int p = 0; p < NC; p++) {
+    const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
+    if (tid < A)
+      sh.enc[p][tid] = mode == RAW ? uint32_t(tid) | (uint32_t(k) << 16)
+                     : (mode == HUFF || mode == GROUP) ? ldg4(plan + 64 + 1024 * p + 4 * tid) : 0u;
+  }
+  if (tid < NC) {
+    sh.mode[tid] = plan[48 + tid];
+    sh.aux[tid] = plan[52 + tid];
+    sh.bits[tid] = *reinterpret_cast<const uint64_t *>(plan + 8 * tid);
+    sh.sec_off[tid] = *reinterpret_cast<const uint32_t *>(plan + 32 + 4 * tid);
+  }
+  const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
+  pack_chunk<DT>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off, sh.stage,
+                 sh.wtot);
 }
 
 // One workgroup: exclusive scan of the record sizes into the directory, then
