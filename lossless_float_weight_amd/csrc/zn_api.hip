@@ -408,7 +408,6 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   if (out_cap < ts->off_records + 16) return ZN_ERR_CAPACITY;
   uint8_t *scr = static_cast<uint8_t *>(d_scratch);
   uint32_t *ctl = reinterpret_cast<uint32_t *>(scr);
-  HIPCHK(launch_zero(ctl, kCtlBytes / 4, stream));
   EncArgs a;
   a.L = dev_layout(ts);
   a.in_ptrs = reinterpret_cast<const uint8_t *const *>(d_in_ptrs);

@@ -763,21 +763,16 @@ __global__ __launch_bounds__(1024) void k_finish(FinishArgs a) {
     for (uint64_t i = b; i < e; i++) stg1(a.out + i, 0);
   }
   if (tid == 0) {
-    if (!fits) {
-      atomicOr(&a.ctl[0], kErrCapacity);
-    } else {
+    // the only writer of the error word during compression: a store, so the
+    // scratch needs no clearing beforehand
+    stg4(a.ctl, fits ? 0u : kErrCapacity);
+    if (fits) {
       stg8(dir + M, u32x2{uint32_t(end), uint32_t(end >> 32)});
       const uint64_t tot = end + 16;
       stg8(a.out + 56, u32x2{uint32_t(tot), uint32_t(tot >> 32)});
     }
   }
   if (fits && tid < 4) stg4(a.out + end + 4 * tid, 0);
-}
-
-__global__ void k_zero(uint32_t *p, uint64_t words) {
-  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < words;
-       i += uint64_t(gridDim.x) * blockDim.x)
-    p[i] = 0;
 }
 
 uint64_t plan_bytes(int dtype) { return plan_stride(dtype); }
@@ -802,13 +797,6 @@ hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s) {
 
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero(uint32_t *p, uint64_t words, hipStream_t s) {
-  if (!words) return hipSuccess;
-  const uint64_t blocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
-  hipLaunchKernelGGL(k_zero, dim3(uint32_t(blocks)), dim3(256), 0, s, p, words);
   return hipGetLastError();
 }
 

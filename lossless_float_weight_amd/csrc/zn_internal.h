@@ -75,7 +75,6 @@ uint64_t plan_bytes(int dtype);
 hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s);
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
 hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s);
-hipError_t launch_zero(uint32_t *p, uint64_t words, hipStream_t s);
 hipError_t launch_check(const CheckArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s);
 
