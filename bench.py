@@ -10,8 +10,11 @@ Infinity Cache with the previous step's data.
 Prints one JSON line.  `value` is uncompressed GB/s through a whole step
 (compress + decompress).  `roofline` is for the dominant kernel: its
 algorithmic bytes per launch (container bytes + uncompressed bytes for the
-decoder) over its average launch duration, timed with HIP events that the
-library records on the call's stream around that kernel only; `traffic` is
+decoder) over its average launch duration, timed in the timed region with
+HIP events that the library attaches to that kernel's dispatches only (each
+timed launch costs the stream a few microseconds, so the other kernels are
+timed in a separate pass before it, which also picks the dominant one and
+gives the compress / decompress split); `traffic` is
 the HBM bytes per launch from committed rocprofv3 counter runs
 (profiles/traffic_*.txt), reported only while the kernel sources are the
 ones those counters were taken on.  The CPU oracle's rate on a bounded
@@ -274,43 +277,58 @@ def main():
         zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"])
 
     kernels = ("analyze", "pack", "decode")
+    everything = ("analyze", "finish", "pack", "check", "decode")
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(s, ev=None, kev=None):
+    def new_events(n, names):
+        out = [{k: (ev(), ev()) for k in names} for _ in range(n)]
+        for d in out:
+            for pair in d.values():
+                for e in pair:
+                    e.record()   # created before any timed launch
+        return out
+
+    def step(s, kev=None):
         if kev is not None:
-            for k in kernels:
-                zn.debug_kernel_events(k, *kev[k])
-        if ev is not None:
-            ev[0].record()
+            for k, pair in kev.items():
+                zn.debug_kernel_events(k, *pair)
         zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"], sync=False)
-        if ev is not None:
-            ev[1].record()
         zn.decompress(ts, s["blob"][:nbytes], outs=s["outs"], scratch=s["dscr"], ptrs=s["out_ptrs"],
                       sync=False)
-        if ev is not None:
-            ev[2].record()
+
+    def stop_timing():
+        for k in everything:
+            zn.debug_kernel_events(k, None, None)
 
     for i in range(args.warmup):
         step(sets[i % R])
     torch.cuda.synchronize()
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    evs = [[ev() for _ in range(3)] for _ in range(args.steps)]
-    kevs = [{k: (ev(), ev()) for k in kernels} for _ in range(args.steps)]
+    # breakdown pass: every kernel timed (start and end of its dispatch)
+    nb_steps = max(3, min(args.steps, 10))
+    bev = new_events(nb_steps, everything)
+    torch.cuda.synchronize()
+    for i in range(nb_steps):
+        step(sets[i % R], bev[i])
+    torch.cuda.synchronize()
+    stop_timing()
+    kern_ms = {k: [d[k][0].elapsed_time(d[k][1]) for d in bev] for k in kernels}
+    comp_ms = [d["analyze"][0].elapsed_time(d["pack"][1]) for d in bev]
+    dec_ms = [d["check"][0].elapsed_time(d["decode"][1]) for d in bev]
+    dominant = max(kernels, key=lambda k: sum(kern_ms[k]))
+    # timed region: only the dominant kernel's launches carry events
+    kevs = new_events(args.steps, (dominant,))
     start, end = ev(), ev()
-    for e in [start, end] + [x for row in evs for x in row] + \
-             [x for d in kevs for pair in d.values() for x in pair]:
-        e.record()   # create every event before the timed region
+    start.record()
+    end.record()
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(sets[i % R], evs[i], kevs[i])
+        step(sets[i % R], kevs[i])
     end.record()
     torch.cuda.synchronize()
-    for k in kernels:
-        zn.debug_kernel_events(k, None, None)
+    stop_timing()
     total_ms = start.elapsed_time(end)
-    comp_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    kern_ms = {k: [d[k][0].elapsed_time(d[k][1]) for d in kevs] for k in kernels}
+    kern_ms[dominant] = [d[dominant][0].elapsed_time(d[dominant][1]) for d in kevs]
 
     # every buffer set must hold an exact round trip and report no error
     for s in sets:
@@ -336,8 +354,8 @@ def main():
         gbps = algo[k] / (avg * 1e-3) / 1e9
         rl[k] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                  "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(k, args.workload),
-                 "kernel": f"k_{k}", "avg_ms": round(avg, 4), "algorithmic_bytes": algo[k]}
-    dominant = max(rl, key=lambda k: rl[k]["avg_ms"])
+                 "kernel": f"k_{k}", "avg_ms": round(avg, 4), "algorithmic_bytes": algo[k],
+                 "timed_in": "timed region" if k == dominant else f"breakdown pass ({nb_steps} steps)"}
     ms_step = total_ms / args.steps
     value = unc / (ms_step * 1e-3) / 1e9
     line = {
@@ -358,7 +376,8 @@ def main():
         "decompress_GBps": round(unc / (med(dec_ms) * 1e-3) / 1e9, 2),
         "compress_GBps": round(unc / (med(comp_ms) * 1e-3) / 1e9, 2),
         "ratio": round(nbytes / unc, 5),
-        "roofline": {k: v for k, v in rl[dominant].items() if k not in ("avg_ms", "algorithmic_bytes")},
+        "roofline": {k: v for k, v in rl[dominant].items()
+                     if k not in ("avg_ms", "algorithmic_bytes", "timed_in")},
         "kernels": rl,
     }
     if args.workload == "model":
@@ -370,13 +389,15 @@ def main():
         ptrs = sets[0]["in_ptrs"]
         for _ in range(2):
             zn.compress(plain, base, out=pblob, scratch=pscr, ptrs=ptrs, sync=False)
-        pe = [[ev(), ev()] for _ in range(5)]
-        for a, b in pe:
-            a.record()
-            zn.compress(plain, base, out=pblob, scratch=pscr, ptrs=ptrs, sync=False)
-            b.record()
+        pe = new_events(5, ("analyze", "pack"))
         torch.cuda.synchronize()
-        per_chunk_ms = med([a.elapsed_time(b) for a, b in pe])
+        for d in pe:
+            for k, pair in d.items():
+                zn.debug_kernel_events(k, *pair)
+            zn.compress(plain, base, out=pblob, scratch=pscr, ptrs=ptrs, sync=False)
+        torch.cuda.synchronize()
+        stop_timing()
+        per_chunk_ms = med([d["analyze"][0].elapsed_time(d["pack"][1]) for d in pe])
         pbytes = int(pblob[56:64].cpu().numpy().view("<u8")[0])
         extra.update({"post_setup_compress_ms": round(med(comp_ms), 3),
                       "per_chunk_table_compress_ms": round(per_chunk_ms, 3),

@@ -153,12 +153,14 @@ zn_status zn_debug_code_lengths(const uint64_t *d_hist, int n, int alphabet, int
                                 uint8_t *d_len, hipStream_t stream);
 
 /* ---- kernel timing, for measurement tools ----
- * zn_debug_kernel_events: from now on, record the HIP events `before` and
- *   `after` (hipEvent_t, owned by the caller) on the call's stream right
- *   before and right after every launch of the named kernel: "analyze",
- *   "finish", "pack" (compression), "check", "decode" (decompression).
- *   NULL events stop the recording for that kernel.  Process-wide, not
- *   thread-safe; ZN_ERR_ARG for an unknown name. */
+ * zn_debug_kernel_events: from now on, every launch of the named kernel
+ *   ("analyze", "finish", "pack" (compression), "check", "decode"
+ *   (decompression)) sets the HIP events `before` and `after` (hipEvent_t,
+ *   created with timing by the caller, who owns them) to its start and end
+ *   times.  The events ride on the kernel's own dispatch, so no marker is
+ *   added to the stream between launches; a call that launches nothing (no
+ *   chunks) leaves them as they were.  NULL events stop the timing of that
+ *   kernel.  Process-wide, not thread-safe; ZN_ERR_ARG for an unknown name. */
 zn_status zn_debug_kernel_events(const char *kernel, void *before, void *after);
 
 #ifdef __cplusplus

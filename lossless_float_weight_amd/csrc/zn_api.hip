@@ -17,23 +17,12 @@
 
 using namespace zn;
 
-// Events recorded around kernel launches (zn_debug_kernel_events).
+// Events that take the start and end times of kernel launches
+// (zn_debug_kernel_events); the launches attach them to their dispatches.
 namespace {
 const char *const kKernelNames[] = {"analyze", "finish", "pack", "check", "decode"};
 enum { KAnalyze, KFinish, KPack, KCheck, KDecode, KCount };
 hipEvent_t g_ev_before[KCount], g_ev_after[KCount];
-
-// Runs one launch between the events registered for it, if any.
-template <class F>
-hipError_t timed(int k, hipStream_t s, F launch) {
-  if (g_ev_before[k]) {
-    const hipError_t e = hipEventRecord(g_ev_before[k], s);
-    if (e != hipSuccess) return e;
-  }
-  const hipError_t e = launch();
-  if (e != hipSuccess || !g_ev_after[k]) return e;
-  return hipEventRecord(g_ev_after[k], s);
-}
 }  // namespace
 
 struct zn_tableset {
@@ -417,7 +406,7 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   a.out = static_cast<uint8_t *>(d_out);
   a.plans = scr + plans_offset(ts);
   a.sizes = reinterpret_cast<unsigned long long *>(scr + sizes_offset());
-  HIPCHK(timed(KAnalyze, stream, [&] { return launch_analyze(ts->dtype, a, stream); }));
+  HIPCHK(launch_analyze(ts->dtype, a, stream, g_ev_before[KAnalyze], g_ev_after[KAnalyze]));
   FinishArgs f;
   f.L = a.L;
   f.dtype = ts->dtype;
@@ -427,14 +416,14 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   f.cap = out_cap;
   f.sizes = a.sizes;
   f.ctl = ctl;
-  HIPCHK(timed(KFinish, stream, [&] { return launch_finish(f, stream); }));
+  HIPCHK(launch_finish(f, stream, g_ev_before[KFinish], g_ev_after[KFinish]));
   PackArgs pk;
   pk.L = a.L;
   pk.in_ptrs = a.in_ptrs;
   pk.plans = a.plans;
   pk.out = a.out;
   pk.ctl = ctl;
-  HIPCHK(timed(KPack, stream, [&] { return launch_pack(ts->dtype, pk, stream); }));
+  HIPCHK(launch_pack(ts->dtype, pk, stream, g_ev_before[KPack], g_ev_after[KPack]));
   if (!out_bytes) return ZN_OK;
   uint32_t flag = 0;
   uint64_t total = 0;
@@ -465,7 +454,7 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
   ck.n_chunks = ts->n_chunks;
   ck.off_dir = ts->off_dir;
   ck.ctl = ctl;
-  HIPCHK(timed(KCheck, stream, [&] { return launch_check(ck, stream); }));
+  HIPCHK(launch_check(ck, stream, g_ev_before[KCheck], g_ev_after[KCheck]));
   DecArgs a;
   a.L = dev_layout(ts);
   a.in = ck.in;
@@ -475,7 +464,7 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
   a.group_len = ts->d_len;
   a.K = ts->K;
   a.ctl = ctl;
-  HIPCHK(timed(KDecode, stream, [&] { return launch_decode(ts->dtype, a, stream); }));
+  HIPCHK(launch_decode(ts->dtype, a, stream, g_ev_before[KDecode], g_ev_after[KDecode]));
   if (!sync) return ZN_OK;
   uint32_t flag = 0;
   HIPCHK(hipMemcpyAsync(&flag, ctl, 4, hipMemcpyDeviceToHost, stream));

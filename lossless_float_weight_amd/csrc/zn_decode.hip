@@ -121,9 +121,14 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   constexpr int VE = 16 / ES;            // elements per 16-byte vector
   __shared__ DecShared<DT> sh;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
-  if (a.ctl[0]) return;  // the header check failed
-
   const uint32_t c = blockIdx.x;
+  // the error word and the chunk's directory entries in one round trip (the
+  // directory lies below the records, which the host checked the input holds)
+  const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.in + a.L.off_dir);
+  const uint32_t ctl0 = a.ctl[0];
+  const uint64_t r0 = dir[c], r1 = dir[c + 1];
+  if (ctl0) return;  // the header check failed
+
   const int t = find_tensor(a.L, c);
   const uint64_t e0 = uint64_t(c - a.L.t_chunk0[t]) * a.L.chunk_elems;
   const uint64_t rem = a.L.t_n[t] - e0;
@@ -135,11 +140,25 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   uint8_t *const sink = reinterpret_cast<uint8_t *>(a.ctl) + kSinkOff;
   const uint8_t *rawp = in + a.L.t_raw[t] + (DT == BF16 ? e0 : DT == FP8 ? e0 / 8 : 0);
 
+  // The first stream of the record is usually Huffman- or group-coded:
+  // its code lengths (Huffman) and segment lengths (at either offset) are
+  // loaded with its header, before the walk has read the mode, wherever the
+  // record lies inside the input.
+  constexpr int A0 = 1 << kbits(DT, 0);
+  const bool spec = r0 >= a.L.off_records && (r0 & 15) == 0 &&
+                    r0 + 8 + A0 / 2 + 2ull * uint64_t(nseg) <= a.in_bytes;
+  uint32_t nib0 = 0, sbh0 = 0, sbg0 = 0;
+  if (spec) {
+    if (tid < A0) nib0 = ldg1(in + r0 + 8 + (tid >> 1));
+    if (tid < nseg) {
+      sbh0 = ldg2(in + r0 + 8 + A0 / 2 + 2 * tid);
+      sbg0 = ldg2(in + r0 + 8 + 2 * tid);
+    }
+  }
+
   // ------------------------------------------------- 1. walk the record
   if (tid == 0) {
     int bad = 0;
-    const uint64_t *dir = reinterpret_cast<const uint64_t *>(in + a.L.off_dir);
-    const uint64_t r0 = dir[c], r1 = dir[c + 1];
     if (r0 < a.L.off_records || r1 < r0 || r1 + 16 > a.in_bytes || (r0 & 15)) bad = 1;
     uint64_t pos = r0;
     for (int p = 0; p < NC && !bad; p++) {
@@ -197,14 +216,20 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   uint32_t sbits0 = 0;
   {
     const int ci = ln / spw, sj = wv * spw + ln % spw;
-    if (ci < ncc && sj < nseg) sbits0 = ldg2(in + sh.seg_off[cs[ci]] + 2 * sj);
+    if (ci < ncc && sj < nseg) {
+      if (spec && cs[ci] == 0 && sj == tid) sbits0 = sh.mode[0] == HUFF ? sbh0 : sbg0;
+      else sbits0 = ldg2(in + sh.seg_off[cs[ci]] + 2 * sj);
+    }
   }
   // ---------------------------------------------------------- 2. tables
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k, mode = sh.mode[p];
     if (mode == HUFF) {
       const uint8_t *nib = in + sh.seg_off[p] - A / 2;
-      if (tid < A) sh.len[p][tid] = (ldg1(nib + (tid >> 1)) >> ((tid & 1) * 4)) & 15;
+      if (tid < A) {
+        const uint32_t x = p == 0 && spec ? nib0 : ldg1(nib + (tid >> 1));
+        sh.len[p][tid] = (x >> ((tid & 1) * 4)) & 15;
+      }
       __syncthreads();
       if (!build_lut<DEC_NT>(sh.len[p], A, sh.lut[p], sh.u.t1, sh.ls)) {
         if (tid == 0) atomicOr(&a.ctl[0], kErrCorrupt);
@@ -353,6 +378,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         nb = 32 - int(b0 & 31);
       }
       int ov = 0;         // symbols of the next strip decoded early (staged words 8, 9)
+      uint64_t cur = 0;   // staged bytes not yet stored whole: those of the word at a, then the next
       // Raw bits and raw-stream fields merged by this lane in round r: the
       // same loads every round (an empty vector reads element 0 and is
       // ignored; r = -1, after the last round, reads element 0 everywhere),
@@ -407,9 +433,11 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           pend = false;
         }
         if (lim > 0) {
-          // Each lookup stores its (up to three) symbols as bytes at pos and
-          // moves pos on by their number; bytes past the valid ones are
-          // overwritten by the next lookup.  The window is refilled, without
+          // Each lookup appends its (up to three) symbols, one byte each, to
+          // the lane's staged bytes: they join the pending bytes of the
+          // current word in cur, which is stored whole and aligned (single
+          // bytes would each cost the LDS a partial-word write); a word that
+          // fills moves the rest of cur down.  The window is refilled, without
           // branches, with 32 bits whenever fewer than 30 remain: enough for
           // the two lookups of an iteration (at most 22 bits), and the word
           // lands at bit nb + 2 <= 31 of W, so nothing falls off its top.
@@ -428,14 +456,14 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           uint32_t nbk = uint32_t(nb + 2) - (a << 6);
           pre = rp[__builtin_amdgcn_ubfe(wpos, 0, 5) * DEC_NT];
           const uint8_t *lutb = reinterpret_cast<const uint8_t *>(lut);
-          uint8_t *const st = sh.u.stage;
+          uint32_t *const stw = reinterpret_cast<uint32_t *>(sh.u.stage);   // abase is a multiple of 8
           auto step = [&]() {
             const uint32_t e = *reinterpret_cast<const uint32_t *>(lutb + (uint32_t(W) & 0x1FFCu));
-            const uint32_t x = __builtin_amdgcn_alignbyte(e, e, 1);   // symbols 0 and 2 in bytes 0 and 2
-            st[a] = uint8_t(x);
-            st[a + 1] = uint8_t(e >> 16);
-            st[a + 2] = uint8_t(x >> 16);
-            a += (e >> 6) & 3;
+            cur |= uint64_t(e >> 8) << ((a & 3) * 8);   // unused symbol bytes of an entry are zero
+            stw[a >> 2] = uint32_t(cur);
+            const uint32_t an = a + ((e >> 6) & 3);
+            cur = (an ^ a) > 3 ? cur >> 32 : cur;
+            a = an;
             W >>= (e & 63);
             nbk -= e & 0xFF;
           };
@@ -449,6 +477,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             step();
             step();
           }
+          stw[a >> 2] = uint32_t(cur);   // the last, partial word
           const int pos = int(a - abase);
           nb = int(nbk + (a << 6)) - 2;
           ov = pos - lim;   // at most 5: the loop stops 2 lookups of 3 symbols past lim - 1
@@ -461,6 +490,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             }
             if (bpos != uint64_t(b0) + sbits) bad = 1;
             ov = 0;
+            cur = 0;
           } else if (((wpos + 11) >> 4) >= nsec && nsec <= slast) {
             // lim == RND here.  The next round reads at most 32 lookups (352
             // bits); the window now holds at least 8 bits and takes a word
@@ -638,17 +668,17 @@ __global__ void k_check(CheckArgs a) {
   }
 }
 
-hipError_t launch_check(const CheckArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_check, dim3(1), dim3(256), 0, s, a);
+hipError_t launch_check(const CheckArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL(k_check, dim3(1), dim3(256), 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s) {
+hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.L.n_chunks == 0) return hipSuccess;
   const dim3 grid(a.L.n_chunks), block(DEC_NT);
-  if (dtype == BF16) hipLaunchKernelGGL(k_decode<BF16>, grid, block, 0, s, a);
-  else if (dtype == FP32) hipLaunchKernelGGL(k_decode<FP32>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_decode<FP8>, grid, block, 0, s, a);
+  if (dtype == BF16) hipExtLaunchKernelGGL(k_decode<BF16>, grid, block, 0, s, e0, e1, 0, a);
+  else if (dtype == FP32) hipExtLaunchKernelGGL(k_decode<FP32>, grid, block, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL(k_decode<FP8>, grid, block, 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 

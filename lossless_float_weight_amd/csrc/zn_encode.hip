@@ -777,26 +777,26 @@ __global__ __launch_bounds__(1024) void k_finish(FinishArgs a) {
 
 uint64_t plan_bytes(int dtype) { return plan_stride(dtype); }
 
-hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s) {
+hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.L.n_chunks == 0) return hipSuccess;
   const dim3 grid(a.L.n_chunks), block(enc_nt(dtype));
-  if (dtype == BF16) hipLaunchKernelGGL(k_analyze<BF16>, grid, block, 0, s, a);
-  else if (dtype == FP32) hipLaunchKernelGGL(k_analyze<FP32>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_analyze<FP8>, grid, block, 0, s, a);
+  if (dtype == BF16) hipExtLaunchKernelGGL(k_analyze<BF16>, grid, block, 0, s, e0, e1, 0, a);
+  else if (dtype == FP32) hipExtLaunchKernelGGL(k_analyze<FP32>, grid, block, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL(k_analyze<FP8>, grid, block, 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s) {
+hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.L.n_chunks == 0) return hipSuccess;
   const dim3 grid(a.L.n_chunks), block(PACK_NT);
-  if (dtype == BF16) hipLaunchKernelGGL(k_pack<BF16>, grid, block, 0, s, a);
-  else if (dtype == FP32) hipLaunchKernelGGL(k_pack<FP32>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_pack<FP8>, grid, block, 0, s, a);
+  if (dtype == BF16) hipExtLaunchKernelGGL(k_pack<BF16>, grid, block, 0, s, e0, e1, 0, a);
+  else if (dtype == FP32) hipExtLaunchKernelGGL(k_pack<FP32>, grid, block, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL(k_pack<FP8>, grid, block, 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, s, a);
+hipError_t launch_finish(const FinishArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL(k_finish, dim3(1), dim3(1024), 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 

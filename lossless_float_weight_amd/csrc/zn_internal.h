@@ -1,6 +1,7 @@
 // zn_internal.h -- launch interface between the C ABI (zn_api.hip) and the
 // kernels (zn_encode.hip, zn_decode.hip, zn_setup.hip).  Not installed.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,11 +73,17 @@ constexpr uint64_t kCtlBytes = 256;
 constexpr uint64_t kSinkOff = 128;
 
 uint64_t plan_bytes(int dtype);
-hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s);
-hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
-hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s);
-hipError_t launch_check(const CheckArgs &a, hipStream_t s);
-hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s);
+// e0, e1 (optional): events that take the start and end times of the
+// launch, attached to its dispatch (no marker joins the stream); left as they
+// were when there is nothing to launch.
+hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s, hipEvent_t e0 = nullptr,
+                          hipEvent_t e1 = nullptr);
+hipError_t launch_finish(const FinishArgs &a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s, hipEvent_t e0 = nullptr,
+                       hipEvent_t e1 = nullptr);
+hipError_t launch_check(const CheckArgs &a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s, hipEvent_t e0 = nullptr,
+                         hipEvent_t e1 = nullptr);
 
 // setup
 hipError_t launch_hist_all(int dtype, const DevLayout &L, const uint8_t *const *in_ptrs,
