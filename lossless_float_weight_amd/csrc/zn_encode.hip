@@ -436,6 +436,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
+  static_assert(64 * EPT * kMaxLen < 65536, "two segments' bit counts share one 32-bit scan");
   constexpr int NV = EPT / VE;         // vectors per thread per tile
   constexpr int NW = PACK_NW, ENC_NT = PACK_NT, G = PackShared<DT>::G;
   constexpr int STAGE = PackShared<DT>::STAGE;
@@ -602,13 +603,18 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
             w[i] = eb + i < n ? load_elem<DT>(src + uint64_t(eb + i) * ES) : 0;
         }
         nb[g] = 0;
+        // elements of this lane's run inside the chunk: the code of every
+        // element is read, and those past the end are dropped by a select
+        // (no branch per element; their w is 0, a valid table index)
+        const uint32_t lim = eb < n ? n - eb : 0u;
 #pragma unroll
         for (int g8 = 0; g8 < NG; g8++) {
           uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
           for (int i = 0; i < GE; i++) {
             const int e = g8 * GE + i;
-            const uint32_t c = eb + e < n ? enc[p][field_rt<DT>(w[e], p)] : 0u;
+            const uint32_t ce = enc[p][field_rt<DT>(w[e], p)];
+            const uint32_t c = uint32_t(e) < lim ? ce : 0u;
             v[i] = c & 0xFFFF;
             l[i] = c >> 16;
           }
@@ -628,11 +634,22 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
       // issued once this tile's codes are computed, so no later wait for this
       // tile's data also waits for the next tile's loads
       if (T + 1 < ntiles) issue(T + 1);
-      // bit offsets: a wave scan per segment; segments follow each other
+      // bit offsets: a wave scan per segment, two segments per scan in 16-bit
+      // halves (a lane's run codes to at most 16 x 11 bits, a wave's to at
+      // most 11264 < 2^16); segments follow each other
       uint32_t incl[G], segtot[G], wsum = 0;
 #pragma unroll
+      for (int g = 0; g < G; g += 2) {
+        if (g + 1 < G) {
+          const uint32_t x = wave_incl_scan(nb[g] | (nb[g + 1] << 16));
+          incl[g] = x & 0xFFFFu;
+          incl[g + 1] = x >> 16;
+        } else {
+          incl[g] = wave_incl_scan(nb[g]);
+        }
+      }
+#pragma unroll
       for (int g = 0; g < G; g++) {
-        incl[g] = wave_incl_scan(nb[g]);
         segtot[g] = uint32_t(__builtin_amdgcn_readlane(int(incl[g]), 63));
         wsum += segtot[g];
       }
