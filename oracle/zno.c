@@ -640,6 +640,28 @@ static uint64_t total_cost(const uint32_t *hist, uint32_t M, int A, const uint8_
   return t;
 }
 
+/* Exponent-stream (stream 0) histogram of every chunk of every tensor, in
+ * tensor order then chunk order; cn[c] = the chunk's element count. */
+static void chunk_histograms(int dt, const void *const *tensors, const uint64_t *n_elems, int T,
+                             uint32_t cb, uint32_t *hist, uint64_t *cn) {
+  const int A = 1 << kbits(dt, 0);
+  const uint64_t ce = chunk_elems(dt, cb);
+  uint32_t c = 0;
+  for (int t = 0; t < T; t++) {
+    const uint8_t *b = (const uint8_t *)tensors[t];
+    for (uint64_t i0 = 0; i0 < n_elems[t]; i0 += ce, c++) {
+      uint64_t n = n_elems[t] - i0 < ce ? n_elems[t] - i0 : ce;
+      cn[c] = n;
+      for (uint64_t i = 0; i < n; i++) {
+        uint8_t s4[4];
+        uint32_t raw;
+        split_one(dt, load_elem(dt, b, i0 + i), s4, &raw);
+        hist[(uint64_t)c * A + s4[0]]++;
+      }
+    }
+  }
+}
+
 typedef struct {
   uint64_t key;
   uint32_t c;
@@ -672,7 +694,6 @@ int zno_setup(int dt, const void *const *tensors, const uint64_t *n_elems, int T
     return ZNO_ERR_ARG;
   }
   int A = 1 << kbits(dt, 0);
-  uint64_t ce = chunk_elems(dt, cb);
   uint32_t *hist = (uint32_t *)calloc((size_t)M * A + 1, 4);
   uint64_t *cn = (uint64_t *)calloc((size_t)M + 1, 8);
   keyed *keys = (keyed *)calloc((size_t)M + 1, sizeof(keyed));
@@ -681,20 +702,8 @@ int zno_setup(int dt, const void *const *tensors, const uint64_t *n_elems, int T
     return ZNO_ERR_NOMEM;
   }
   /* (1) exponent-stream histogram of every chunk of every tensor */
-  uint32_t c = 0;
-  for (int t = 0; t < T; t++) {
-    const uint8_t *b = (const uint8_t *)tensors[t];
-    for (uint64_t i0 = 0; i0 < n_elems[t]; i0 += ce, c++) {
-      uint64_t n = n_elems[t] - i0 < ce ? n_elems[t] - i0 : ce;
-      cn[c] = n;
-      for (uint64_t i = 0; i < n; i++) {
-        uint8_t s4[4];
-        uint32_t raw;
-        split_one(dt, load_elem(dt, b, i0 + i), s4, &raw);
-        hist[(uint64_t)c * A + s4[0]]++;
-      }
-    }
-  }
+  chunk_histograms(dt, tensors, n_elems, T, cb, hist, cn);
+  uint32_t c;
   /* (2) initial groups: chunks ordered by their mean exponent, cut evenly */
   for (c = 0; c < M; c++) {
     uint64_t sum = 0;
@@ -731,6 +740,62 @@ int zno_setup(int dt, const void *const *tensors, const uint64_t *n_elems, int T
   if (rc == ZNO_OK) ts->cost[ROUNDS] = total_cost(hist, M, A, ts->map, ts->len);
   free(hist), free(cn), free(keys);
   if (rc == ZNO_OK) rc = ts_rehash(ts);
+  if (rc < 0) {
+    zno_tableset_free(ts);
+    return rc;
+  }
+  *out = ts;
+  return ZNO_OK;
+}
+
+/* Transfer of a setup to other tensors of the same dtype ("another
+ * compatible architecture"  [NZ Abstract]): the source's K group codes are
+ * kept as they are; every chunk of the new tensors goes to the group code
+ * that codes its exponent histogram in the fewest bits, ties to the smaller
+ * group id; a chunk that every group code lacks a symbol for goes to group 0
+ * (compression then codes it with its own table).  The assignment depends on
+ * the chunk's content only, not on its position.  The cost history is the
+ * source's (the tables were fit there). */
+int zno_setup_transfer(const zno_tableset *src, const void *const *tensors, const uint64_t *n_elems,
+                       int T, zno_tableset **out) {
+  if (!out) return ZNO_ERR_ARG;
+  *out = NULL;
+  if (!src || src->K < 1 || !tensors || !n_elems || T < 1) return ZNO_ERR_ARG;
+  const int dt = src->dtype, K = src->K, A = 1 << kbits(dt, 0);
+  const uint32_t cb = src->chunk_bytes;
+  uint64_t M64 = 0;
+  for (int t = 0; t < T; t++) {
+    if (n_elems[t] && !tensors[t]) return ZNO_ERR_ARG;
+    M64 += nchunks_of(dt, n_elems[t], cb);
+  }
+  if (M64 > 0xFFFFFFFFull) return ZNO_ERR_ARG;
+  const uint32_t M = (uint32_t)M64;
+  zno_tableset *ts = ts_alloc(dt, K, cb, T, M);
+  if (!ts) return ZNO_ERR_NOMEM;
+  memcpy(ts->n_elems, n_elems, 8 * (size_t)T);
+  memcpy(ts->len, src->len, (size_t)K * 256);
+  memcpy(ts->cost, src->cost, sizeof ts->cost);
+  uint32_t *hist = (uint32_t *)calloc((size_t)M * A + 1, 4);
+  uint64_t *cn = (uint64_t *)calloc((size_t)M + 1, 8);
+  if (!hist || !cn) {
+    free(hist), free(cn), zno_tableset_free(ts);
+    return ZNO_ERR_NOMEM;
+  }
+  chunk_histograms(dt, tensors, n_elems, T, cb, hist, cn);
+  for (uint32_t c = 0; c < M; c++) {
+    uint64_t best = UINT64_MAX;
+    int bg = 0;
+    for (int g = 0; g < K; g++) {
+      uint64_t x = chunk_cost(hist + (uint64_t)c * A, ts->len[g], A);
+      if (x < best) { /* strict: ties keep the smaller group id */
+        best = x;
+        bg = g;
+      }
+    }
+    ts->map[c] = (uint8_t)bg;
+  }
+  free(hist), free(cn);
+  int rc = ts_rehash(ts);
   if (rc < 0) {
     zno_tableset_free(ts);
     return rc;

@@ -73,6 +73,10 @@ int zno_encode_chunk(int dtype, const void *chunk, uint64_t n, const uint8_t *gr
 /* ---- NeuralZip-style setup ---- */
 int zno_setup(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,
               uint32_t chunk_bytes, int n_groups, zno_tableset **out);
+/* The source's group codes for other tensors of its dtype and chunk size;
+ * each chunk to the group code of least coded size (content, not position). */
+int zno_setup_transfer(const zno_tableset *src, const void *const *tensors, const uint64_t *n_elems,
+                       int n_tensors, zno_tableset **out);
 void zno_tableset_free(zno_tableset *ts);
 int zno_tableset_info(const zno_tableset *ts, int *n_groups, uint32_t *n_chunks, uint64_t *hash);
 int zno_tableset_lengths(const zno_tableset *ts, int g, uint8_t *len /* alphabet */);

@@ -73,6 +73,7 @@ def lib():
         L.zno_decompress.argtypes = [P, U64, P, C.POINTER(P), PU64, I]
         L.zno_encode_chunk.argtypes = [I, P, U64, P, I, P, U64, PU64, C.POINTER(I)]
         L.zno_setup.argtypes = [I, C.POINTER(P), PU64, I, U32, I, C.POINTER(P)]
+        L.zno_setup_transfer.argtypes = [P, C.POINTER(P), PU64, I, C.POINTER(P)]
         L.zno_tableset_free.argtypes = [P]
         L.zno_tableset_info.argtypes = [P, C.POINTER(I), C.POINTER(U32), PU64]
         L.zno_tableset_lengths.argtypes = [P, I, P]
@@ -284,3 +285,16 @@ def setup(dtype: int, tensors, chunk_bytes: int = 262144, n_groups: int = 16) ->
     _check(lib().zno_setup(dtype, ptrs, _u64arr([a.size for a in arrs]), len(arrs), chunk_bytes,
                            n_groups, C.byref(h)), "setup")
     return Tableset(h, dtype)
+
+
+def setup_transfer(src: Tableset, tensors) -> Tableset:
+    """The source's group codes for other tensors of its dtype and chunk size,
+    each chunk assigned by content to the group code of least coded size."""
+    if isinstance(tensors, np.ndarray):
+        tensors = [tensors]
+    arrs = [np.ascontiguousarray(t, ELEM_DTYPE[src.dtype]).ravel() for t in tensors]
+    ptrs = (C.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    h = C.c_void_p()
+    _check(lib().zno_setup_transfer(src.handle, ptrs, _u64arr([a.size for a in arrs]), len(arrs),
+                                    C.byref(h)), "setup_transfer")
+    return Tableset(h, src.dtype)

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("zn_setup", "zn_compress", "zn_decompress"):
+    for required in ("zn_setup", "zn_setup_transfer", "zn_compress", "zn_decompress"):
         assert required in names
 
 
@@ -41,6 +41,7 @@ def test_status_strings_and_argument_errors_need_no_gpu():
     assert lib.zn_setup(0, None, n, 1, 1000, 0, None, ctypes.byref(out)) == -1   # bad chunk size
     assert lib.zn_setup(7, None, n, 1, 262144, 0, None, ctypes.byref(out)) == -1  # bad dtype
     assert lib.zn_compress(None, None, None, 0, None, None, 0, None) == -1
+    assert lib.zn_setup_transfer(None, None, n, 1, None, ctypes.byref(out)) == -1      # no source
 
 
 @pytest.mark.skipif(not os.path.exists(LIB), reason="libzn.so not built")
