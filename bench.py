@@ -51,6 +51,11 @@ WORKLOADS = {
             "256 KiB chunks",
     "fp8": "FP8 E4M3 1,073,741,824 values, N(0,1) scaled per 128-element block to max 448, "
            "256 KiB chunks",
+    "transfer": "setup with 16 shared-table groups on the 8B-shaped BF16 block above, transferred to another "
+                "architecture: 2 3B-shaped BF16 blocks (Wq/Wo 3072x3072, Wk/Wv 1024x3072, W_gate/W_up 8192x3072, "
+                "W_down 3072x8192 N(0, sigma~U[0.01,0.04]) + 2 RMSNorm vectors N(1, 0.05) each; 201,338,880 "
+                "values), each chunk assigned by content to its cheapest group code; steps on the 3B-shaped "
+                "blocks with that tableset; 256 KiB chunks",
     "model": "8B-shaped BF16 model: 32 blocks as in 'block' + embedding 128256x4096 N(0, 0.02) + KV cache "
              "[32,2,8,32768,128] N(0,1) = 9,652,404,224 values; setup with 16 shared-table groups on it, "
              "steps on a perturbed copy (weights + N(0, 1e-4)) with that setup unchanged; 256 KiB chunks",
@@ -98,6 +103,8 @@ def make_tensors(name: str):
         return [t for _, t in W.fp8_blockscaled(1 << 30, device="cuda")]
     if name == "model":
         return [t for _, t in W.model_bf16("cuda", seed=5)]
+    if name == "transfer":
+        return [t for i in range(2) for _, t in W.other_block_bf16("cuda", seed=7, first_index=9 * i)]
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -254,6 +261,18 @@ def main():
         names = [f"t{i}" for i in range(len(base))]
         base = [t for _, t in W.perturbed_model(list(zip(names, base)), seed=5)]
         torch.cuda.synchronize()
+    elif args.workload == "transfer":
+        # the source setup on one architecture, reused on another by content
+        src_tensors = make_tensors("block")
+        src = zn.setup(src_tensors, chunk_bytes=CHUNK_BYTES, n_groups=16)
+        del src_tensors
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ts = zn.setup_transfer(src, base)
+        torch.cuda.synchronize()
+        extra["transfer_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        gm = ts.group_map()
+        extra["groups_used"] = len(set(gm))
     else:
         ts = zn.setup(base, chunk_bytes=CHUNK_BYTES)
     bound = zn.compress_bound(ts)
@@ -380,7 +399,7 @@ def main():
                      if k not in ("avg_ms", "algorithmic_bytes", "timed_in")},
         "kernels": rl,
     }
-    if args.workload == "model":
+    if args.workload in ("model", "transfer"):
         # the same compression with per-chunk tables (no setup), for the
         # post-setup speed-up the reusable setup is about
         plain = zn.setup(base, chunk_bytes=CHUNK_BYTES)

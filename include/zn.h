@@ -74,10 +74,26 @@ typedef struct zn_tableset zn_tableset;
  *     histograms (integer Lloyd rounds) and each group gets one shared code;
  *     d_tensors (host array of device pointers) must then be valid.
  * Allocates device memory for the plan (this is the only call that does,
- * with zn_plan_from_container and zn_tableset_load).  Synchronises stream. */
+ * with zn_setup_transfer, zn_plan_from_container and zn_tableset_load).
+ * Synchronises stream. */
 zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t *n_elems,
                    int n_tensors, uint32_t chunk_bytes, int n_groups, hipStream_t stream,
                    zn_tableset **out);
+
+/* zn_setup_transfer -- a setup reused on other tensors of the same dtype and
+ * chunk size, such as another compatible architecture ("NeuralZip: Reusable
+ * Setup for Fast Lossless Compression", Abstract).  The new plan keeps src's
+ * K group codes unchanged; every chunk of the new tensors (d_tensors: host
+ * array of device pointers; n_elems[n_tensors] host) is histogrammed on the
+ * GPU and assigned by its content to the group code that codes its exponent
+ * stream in the fewest bits, ties to the smaller group id; a chunk that every
+ * group code lacks a symbol for goes to group 0 and is coded with its own
+ * table when compressed.  The cost history is src's.  src must have groups
+ * (ZN_ERR_ARG otherwise) and stays valid.  Allocates device memory for the
+ * plan; synchronises stream. */
+zn_status zn_setup_transfer(const zn_tableset *src, const void *const *d_tensors,
+                            const uint64_t *n_elems, int n_tensors, hipStream_t stream,
+                            zn_tableset **out);
 
 /* zn_plan_from_container -- a plan (without groups) that matches the layout
  * of an existing container; reads its header and tensor table with one

@@ -267,6 +267,32 @@ zn_status run_grouping(zn_tableset *ts, const void *const *d_tensors, hipStream_
   return ZN_OK;
 }
 
+// Content-based assignment of a transferred setup: every chunk of the new
+// tensors to the group code of least coded size (ties to the smaller id; a
+// chunk that every code lacks a symbol for stays in group 0).
+zn_status run_transfer(zn_tableset *ts, const void *const *d_tensors, hipStream_t s) {
+  const int dt = ts->dtype, K = ts->K, NC = ncoded(dt), A = alphabet0(dt);
+  const uint32_t M = ts->n_chunks;
+  const int stride = NC * 256;
+  DevBuf<const uint8_t *> ptrs;
+  DevBuf<uint32_t> hist;
+  DevBuf<unsigned long long> cost;
+  DevBuf<uint8_t> map, len;
+  if (ptrs.alloc(ts->T) || hist.alloc(uint64_t(M) * stride) || cost.alloc(1) || map.alloc(M) ||
+      len.alloc(256ull * K))
+    return ZN_ERR_NOMEM;
+  HIPCHK(hipMemcpyAsync(ptrs.p, d_tensors, sizeof(void *) * ts->T, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(len.p, ts->len.data(), 256ull * K, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemsetAsync(map.p, 0, M ? M : 1, s));
+  HIPCHK(hipMemsetAsync(cost.p, 0, 8, s));
+  const DevLayout L = dev_layout(ts);
+  HIPCHK(launch_hist_all(dt, L, ptrs.p, hist.p, s));
+  HIPCHK(launch_assign(hist.p, stride, A, M, len.p, K, 1, map.p, cost.p, s));
+  if (M) HIPCHK(hipMemcpyAsync(ts->map.data(), map.p, M, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  return ZN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,6 +334,34 @@ zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t 
     if (st == ZN_OK) st = run_grouping(ts, d_tensors, stream);
   }
   if (st == ZN_OK) st = finish_plan(ts);
+  if (st == ZN_OK) st = upload_groups(ts, stream);
+  if (st != ZN_OK) {
+    zn_tableset_free(ts);
+    return st;
+  }
+  *out = ts;
+  return ZN_OK;
+}
+
+zn_status zn_setup_transfer(const zn_tableset *src, const void *const *d_tensors,
+                            const uint64_t *n_elems, int n_tensors, hipStream_t stream,
+                            zn_tableset **out) {
+  if (!out) return ZN_ERR_ARG;
+  *out = nullptr;
+  if (!src || src->K < 1 || !d_tensors || !n_elems || n_tensors < 1) return ZN_ERR_ARG;
+  zn_tableset *ts = new (std::nothrow) zn_tableset;
+  if (!ts) return ZN_ERR_NOMEM;
+  zn_status st = make_plan(ts, src->dtype, n_elems, n_tensors, src->chunk_bytes);
+  if (st == ZN_OK) {
+    ts->K = src->K;
+    ts->len = src->len;    // the source's codes, unchanged
+    ts->cost = src->cost;  // and the history of their fit
+    for (int t = 0; t < n_tensors; t++)
+      if (n_elems[t] && !d_tensors[t]) st = ZN_ERR_ARG;
+  }
+  if (st == ZN_OK) st = finish_plan(ts);  // device layout for the kernels
+  if (st == ZN_OK) st = run_transfer(ts, d_tensors, stream);
+  if (st == ZN_OK) st = finish_plan(ts);  // hash of the new map
   if (st == ZN_OK) st = upload_groups(ts, stream);
   if (st != ZN_OK) {
     zn_tableset_free(ts);

@@ -82,6 +82,24 @@ def block_bf16(device="cpu", seed=2, scale=1, first_index=0, prefix=""):
     return out
 
 
+def other_block_bf16(device="cpu", seed=7, scale=1, first_index=0, prefix=""):
+    """Another architecture's BF16 block (3B-shaped: hidden 3072, kv 1024, ffn
+    8192): matrices N(0, sigma), sigma ~ U[0.01, 0.04] per matrix; RMSNorm
+    vectors N(1, 0.05).  scale > 1 divides every dimension (tests)."""
+    out = []
+    for j, (name, shape) in enumerate(block_shapes(3072 // scale, 1024 // scale, 8192 // scale)):
+        i = first_index + j
+        n = 1
+        for d in shape:
+            n *= d
+        if name.endswith("norm"):
+            t = gaussian(n, 1.0, 0.05, torch.bfloat16, device, seed, i)
+        else:
+            t = gaussian(n, 0.0, uniform_sigma(0.01, 0.04, seed, i), torch.bfloat16, device, seed, i)
+        out.append((prefix + name, t.view(shape)))
+    return out
+
+
 def fp32_pair(n=1 << 27, device="cpu", seed=3):
     """FP32 N(0, 0.02): a regular copy and a clean copy (low 16 fraction bits zero)."""
     reg = gaussian(n, 0.0, 0.02, torch.float32, device, seed, 0)

@@ -43,6 +43,7 @@ def lib() -> C.CDLL:
         P, U64, I, U32 = C.c_void_p, C.c_uint64, C.c_int, C.c_uint32
         PU64 = C.POINTER(C.c_uint64)
         L.zn_setup.argtypes = [I, C.POINTER(P), PU64, I, U32, I, P, C.POINTER(P)]
+        L.zn_setup_transfer.argtypes = [P, C.POINTER(P), PU64, I, P, C.POINTER(P)]
         L.zn_plan_from_container.argtypes = [P, U64, P, C.POINTER(P)]
         L.zn_tableset_info.argtypes = [P, C.POINTER(I), C.POINTER(I), PU64, C.POINTER(U32),
                                        C.POINTER(U32), C.POINTER(I), PU64]
@@ -60,7 +61,7 @@ def lib() -> C.CDLL:
         L.zn_debug_histograms.argtypes = [P, P, P, P]
         L.zn_debug_code_lengths.argtypes = [P, I, I, I, P, P]
         L.zn_debug_kernel_events.argtypes = [C.c_char_p, P, P]
-        for f in ("zn_setup", "zn_plan_from_container", "zn_tableset_info", "zn_compress_bound",
+        for f in ("zn_setup", "zn_setup_transfer", "zn_plan_from_container", "zn_tableset_info", "zn_compress_bound",
                   "zn_scratch_bytes", "zn_compress", "zn_decompress", "zn_tableset_save",
                   "zn_tableset_load", "zn_tableset_lengths", "zn_tableset_map",
                   "zn_tableset_cost_history", "zn_debug_histograms", "zn_debug_code_lengths",
@@ -171,6 +172,17 @@ def setup(tensors: Sequence[torch.Tensor] | None = None, *, dtype=None, n_elems=
     h = C.c_void_p()
     _check(lib().zn_setup(int(dtype), ptrs, _u64(n_elems), len(n_elems), chunk_bytes, n_groups,
                           _stream(stream), C.byref(h)), "setup")
+    return Tableset(h)
+
+
+def setup_transfer(src: Tableset, tensors: Sequence[torch.Tensor], stream=None) -> Tableset:
+    """zn_setup_transfer: src's group codes for these tensors (same dtype and
+    chunk size), each chunk assigned by content to its cheapest group code."""
+    tensors = [t.contiguous() for t in tensors]
+    ptrs = (C.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    h = C.c_void_p()
+    _check(lib().zn_setup_transfer(src.handle, ptrs, _u64([t.numel() for t in tensors]), len(tensors),
+                                   _stream(stream), C.byref(h)), "setup_transfer")
     return Tableset(h)
 
 

@@ -204,6 +204,26 @@ def test_setup_equals_oracle_and_reuses(oracle):
     assert_roundtrip(ts2, blob, pert)
 
 
+def test_transfer_equals_oracle(oracle):
+    print("case: grouped setup K=8 on a scaled model, transferred to another architecture", flush=True)
+    tensors = _small_model()
+    ts = zn.setup(tensors, chunk_bytes=65536, n_groups=8)
+    ots = oracle.setup(oracle.BF16, [to_np(t) for t in tensors], 65536, 8)
+    other = [t for _, t in W.other_block_bf16("cuda", seed=7, scale=8)]
+    other[1].view(-1)[5] = float("inf")    # a chunk no group code can code
+    tr = zn.setup_transfer(ts, other)
+    otr = oracle.setup_transfer(ots, [to_np(t) for t in other])
+    assert tr.group_map() == otr.group_map().tolist()
+    assert tr.save() == otr.save() and tr.hash == otr.hash
+    assert tr.cost_history() == ts.cost_history()
+    _check_equal(oracle, oracle.BF16, other, 65536, tr, otr)
+    # and back onto the set-up tensors themselves
+    tr2 = zn.setup_transfer(ts, tensors)
+    otr2 = oracle.setup_transfer(ots, [to_np(t) for t in tensors])
+    assert tr2.save() == otr2.save()
+    _check_equal(oracle, oracle.BF16, tensors, 65536, tr2, otr2)
+
+
 def test_escape_chunk(oracle):
     print("case: escape chunk under a group tableset", flush=True)
     tensors = _small_model(n_layers=1)
