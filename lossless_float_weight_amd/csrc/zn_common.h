@@ -13,7 +13,7 @@
 //     lengths <= 11 (package-merge, leaves by (count, symbol), leaves before
 //     packages at equal weight), canonical codes, LSB-first bits with each
 //     code word first-bit-first (THEORY-599, order-0 only);
-//   * streams cut into segments of S symbols (BF16 512, FP32 1024, FP8 2048)
+//   * streams cut into segments of S symbols (BF16 512, FP32 256, FP8 1024)
 //     whose bit lengths are stored, so segments decode independently;
 //   * container: 64-byte header, tensor table, chunk directory, raw planes,
 //     16-byte aligned chunk records, 16 zero bytes.

@@ -14,6 +14,9 @@ Recipe (every tensor has its own torch.Generator seeded with seed*1000 + i):
   * FP32 "clean": the regular float32 with its low 16 fraction bits cleared;
   * FP8 E4M3: per 128-element block scaled so max|z| maps to 448, clamped to
     +-448 and cast to float8_e4m3fn (round-to-nearest-even, no NaN produced);
+  * FP4 E2M1 pairs: per 32-value block scaled so max|z| maps to 6 (the
+    largest E2M1 magnitude), rounded to the nearest E2M1 value (ties to the
+    even code), two values per byte, the first in the low nibble;
   * perturbed copy of a BF16 weight: bf16(fp32(w) + N(0, 1e-4)).
 Host (cpu) and device (cuda) generators produce different streams; tests that
 compare the two sides always generate once and copy.
@@ -123,6 +126,39 @@ def fp8_blockscaled(n=1 << 30, block=128, device="cpu", seed=4):
         y = (zb * (448.0 / amax)).clamp(-448.0, 448.0).reshape(-1)[:m]
         out[s:s + m] = y.to(torch.float8_e4m3fn)
     return [("w_fp8", out)]
+
+
+# E2M1 magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); the midpoints
+# between neighbours decide the rounding
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def fp4_blockscaled(n_bytes=1 << 29, block=32, device="cpu", seed=8):
+    """FP4 E2M1 pairs (uint8, two values per byte, the first in the low
+    nibble): N(0,1) scaled per 32-value block to max |z| = 6, rounded to the
+    nearest E2M1 value, ties to the even code."""
+    g = _gen(device, seed, 0)
+    n = 2 * n_bytes
+    out = torch.empty(n_bytes, dtype=torch.uint8, device=device)
+    mids = torch.tensor(_E2M1_MIDS, dtype=torch.float64, device=device)
+    step = (GEN_BLOCK // (2 * block)) * 2 * block
+    for s in range(0, n, step):
+        m = min(step, n - s)
+        z = torch.randn(m, dtype=torch.float64, device=device, generator=g)
+        nb = (m + block - 1) // block
+        zp = torch.zeros(nb * block, dtype=torch.float64, device=device)
+        zp[:m] = z
+        zb = zp.view(nb, block)
+        amax = zb.abs().amax(dim=1, keepdim=True).clamp_min(1e-300)
+        y = (zb * (6.0 / amax)).reshape(-1)[:m]
+        a = y.abs()
+        code = torch.bucketize(a, mids)               # mids below a, a tie counted as below
+        tie = (code < 7) & (a == mids[code.clamp(max=6)])
+        code = code + (tie & (code % 2 == 1)).to(code.dtype)   # a tie goes to the even code
+        nib = (code + 8 * (y < 0).to(code.dtype)).to(torch.uint8)
+        pair = nib.view(-1, 2)
+        out[s // 2:(s + m) // 2] = pair[:, 0] | (pair[:, 1] << 4)
+    return [("w_fp4", out)]
 
 
 def model_bf16(device="cpu", seed=5, n_layers=32, scale=1, with_kv=True, kv_tokens=32768):

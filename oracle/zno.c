@@ -31,6 +31,14 @@
  *                  P2 = (w>>8)&0xFF, P3 = w&0xFF         coded streams 2, 3
  *    FP8 byte b:   E4 = (b>>3)&0xF (stream 0), M3 = b&7 (stream 1),
  *                  S = b>>7 (always-raw bit plane).
+ *    FP4 (E2M1, the FP8 page's other low-precision format), stored two
+ *    values to a byte, the first in the low nibble; a nibble is
+ *    sign(bit 3) | exponent(bits 2..1) | mantissa(bit 0).  One element is
+ *    one byte (two values): E = e_lo | e_hi<<2 (stream 0, 4 bits),
+ *    M = m_lo | m_hi<<1 (stream 1, 2 bits), S = s_lo | s_hi<<1 (always-raw,
+ *    2 bits per element).  Reading: the pages name FP4 but not its layout;
+ *    this is its usual packed storage, with each field of the byte's two
+ *    values kept together as one symbol.
  *    Every bit pattern is data: NaN, Inf, subnormals and -0 are not special.
  * R2 Chunks: a chunk holds chunk_bytes of uncompressed input of ONE tensor;
  *    the last chunk of a tensor may be short.  A coded stream of n symbols
@@ -94,13 +102,17 @@
 /* ------------------------------------------------------------------ */
 static int esize(int dt) { return dt == ZNO_BF16 ? 2 : dt == ZNO_FP32 ? 4 : 1; }
 static int ncoded(int dt) { return dt == ZNO_BF16 ? 1 : dt == ZNO_FP32 ? 4 : 2; }
-static int kbits(int dt, int p) { return dt == ZNO_FP8_E4M3 ? (p == 0 ? 4 : 3) : 8; }
+static int kbits(int dt, int p) {
+  return dt == ZNO_FP8_E4M3 ? (p == 0 ? 4 : 3) : dt == ZNO_FP4X2_E2M1 ? (p == 0 ? 4 : 2) : 8;
+}
 static int segsyms(int dt) { return dt == ZNO_BF16 ? 512 : dt == ZNO_FP32 ? 256 : 1024; }
 static uint64_t rawplane_bytes(int dt, uint64_t n) {
-  return dt == ZNO_BF16 ? n : dt == ZNO_FP8_E4M3 ? (n + 7) / 8 : 0;
+  return dt == ZNO_BF16 ? n : dt == ZNO_FP8_E4M3 ? (n + 7) / 8 : dt == ZNO_FP4X2_E2M1 ? (n + 3) / 4 : 0;
 }
 static uint64_t align16(uint64_t x) { return (x + 15) & ~(uint64_t)15; }
-static int valid_dtype(int dt) { return dt == ZNO_BF16 || dt == ZNO_FP32 || dt == ZNO_FP8_E4M3; }
+static int valid_dtype(int dt) {
+  return dt == ZNO_BF16 || dt == ZNO_FP32 || dt == ZNO_FP8_E4M3 || dt == ZNO_FP4X2_E2M1;
+}
 static int valid_chunk(uint32_t cb) { return cb >= 4096 && cb <= (1u << 20) && cb % 4096 == 0; }
 
 static void put_u16(uint8_t *p, uint32_t v) { p[0] = v & 0xFF; p[1] = (v >> 8) & 0xFF; }
@@ -143,10 +155,15 @@ static void split_one(int dt, uint32_t w, uint8_t *sym, uint32_t *raw) {
     sym[2] = (w >> 8) & 0xFF;                       /* fraction[15:8]            */
     sym[3] = w & 0xFF;                              /* fraction[7:0]             */
     *raw = 0;
-  } else {
+  } else if (dt == ZNO_FP8_E4M3) {
     sym[0] = (w >> 3) & 0xF;                        /* E4M3 exponent             */
     sym[1] = w & 7;                                 /* E4M3 mantissa             */
     *raw = (w >> 7) & 1;                            /* sign                      */
+  } else {                                          /* two E2M1 values, low first */
+    const uint32_t lo = w & 0xF, hi = (w >> 4) & 0xF;
+    sym[0] = (uint8_t)(((lo >> 1) & 3) | (((hi >> 1) & 3) << 2));  /* exponents   */
+    sym[1] = (uint8_t)((lo & 1) | ((hi & 1) << 1));                /* mantissas   */
+    *raw = ((lo >> 3) & 1) | (((hi >> 3) & 1) << 1);               /* signs       */
   }
 }
 static uint32_t merge_one(int dt, const uint8_t *sym, uint32_t raw) {
@@ -155,7 +172,10 @@ static uint32_t merge_one(int dt, const uint8_t *sym, uint32_t raw) {
   if (dt == ZNO_FP32)
     return ((uint32_t)(sym[1] & 0x80) << 24) | ((uint32_t)sym[0] << 23) |
            ((uint32_t)(sym[1] & 0x7F) << 16) | ((uint32_t)sym[2] << 8) | sym[3];
-  return ((raw & 1) << 7) | ((uint32_t)(sym[0] & 0xF) << 3) | (sym[1] & 7);
+  if (dt == ZNO_FP8_E4M3) return ((raw & 1) << 7) | ((uint32_t)(sym[0] & 0xF) << 3) | (sym[1] & 7);
+  const uint32_t lo = ((raw & 1) << 3) | ((uint32_t)(sym[0] & 3) << 1) | (sym[1] & 1);
+  const uint32_t hi = (((raw >> 1) & 1) << 3) | ((uint32_t)((sym[0] >> 2) & 3) << 1) | ((sym[1] >> 1) & 1);
+  return lo | (hi << 4);
 }
 
 void zno_split(int dt, const void *in, uint64_t n, uint8_t *planes, uint8_t *rawbits) {
@@ -967,6 +987,7 @@ int zno_compress(int dt, const void *const *tensors, const uint64_t *n, int T, u
       split_one(dt, load_elem(dt, b, i), s4, &raw);
       if (dt == ZNO_BF16) out[raw_off[t] + i] = (uint8_t)raw;
       if (dt == ZNO_FP8_E4M3 && raw) out[raw_off[t] + i / 8] |= (uint8_t)(1u << (i % 8));
+      if (dt == ZNO_FP4X2_E2M1 && raw) out[raw_off[t] + i / 4] |= (uint8_t)(raw << (2 * (i % 4)));
     }
     if (st) st->raw_plane_bytes += rawplane_bytes(dt, n[t]);
   }
@@ -1195,6 +1216,7 @@ int zno_decompress(const void *inv, uint64_t in_bytes, const zno_tableset *ts, v
         uint64_t e = i0 + i;
         if (dt == ZNO_BF16) raw = in[raw_off[t] + e];
         if (dt == ZNO_FP8_E4M3) raw = (in[raw_off[t] + e / 8] >> (e % 8)) & 1;
+        if (dt == ZNO_FP4X2_E2M1) raw = (in[raw_off[t] + e / 4] >> (2 * (e % 4))) & 3;
         store_elem(dt, o, e, merge_one(dt, s4, raw));
       }
     }

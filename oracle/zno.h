@@ -31,7 +31,9 @@
 extern "C" {
 #endif
 
-enum { ZNO_BF16 = 0, ZNO_FP32 = 1, ZNO_FP8_E4M3 = 2 };
+/* ZNO_FP4X2_E2M1: one element is a byte holding two FP4 E2M1 values, the
+ * first in the low nibble; element counts are bytes. */
+enum { ZNO_BF16 = 0, ZNO_FP32 = 1, ZNO_FP8_E4M3 = 2, ZNO_FP4X2_E2M1 = 3 };
 enum { ZNO_OK = 0, ZNO_ERR_ARG = -1, ZNO_ERR_CORRUPT = -2, ZNO_ERR_CAPACITY = -3,
        ZNO_ERR_TABLESET = -4, ZNO_ERR_NOMEM = -6 };
 enum { ZNO_RAW = 0, ZNO_CONST = 1, ZNO_HUFF = 2, ZNO_GROUP = 3 };

@@ -5,7 +5,7 @@ CPU-baseline leg are the only callers.  The GPU library and its Python binding
 never import this module; the two share no code.
 
 Elements are passed as their raw bit patterns: numpy uint16 for BF16, uint32
-for FP32 and uint8 for FP8 E4M3.
+for FP32, uint8 for FP8 E4M3 and for FP4 E2M1 pairs (two values per byte).
 """
 from __future__ import annotations
 
@@ -19,12 +19,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle_zno.so")
 SRC = os.path.join(HERE, "zno.c")
 
-BF16, FP32, FP8_E4M3 = 0, 1, 2
+BF16, FP32, FP8_E4M3, FP4X2_E2M1 = 0, 1, 2, 3
 RAW, CONST, HUFF, GROUP = 0, 1, 2, 3
 MAX_LEN = 11
-ELEM_DTYPE = {BF16: np.uint16, FP32: np.uint32, FP8_E4M3: np.uint8}
-N_CODED = {BF16: 1, FP32: 4, FP8_E4M3: 2}
-ALPHABET0 = {BF16: 256, FP32: 256, FP8_E4M3: 16}
+ELEM_DTYPE = {BF16: np.uint16, FP32: np.uint32, FP8_E4M3: np.uint8, FP4X2_E2M1: np.uint8}
+N_CODED = {BF16: 1, FP32: 4, FP8_E4M3: 2, FP4X2_E2M1: 2}
+ALPHABET0 = {BF16: 256, FP32: 256, FP8_E4M3: 16, FP4X2_E2M1: 16}
 STATUS = {0: "ok", -1: "argument", -2: "corrupt", -3: "capacity", -4: "tableset", -6: "nomem"}
 
 

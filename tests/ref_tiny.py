@@ -22,13 +22,17 @@ from collections import Counter
 
 MAX_LEN = 11
 RAW, CONST, HUFF, GROUP = 0, 1, 2, 3
-ESIZE = {0: 2, 1: 4, 2: 1}
-NCODED = {0: 1, 1: 4, 2: 2}
-SEG = {0: 512, 1: 256, 2: 1024}
+ESIZE = {0: 2, 1: 4, 2: 1, 3: 1}
+NCODED = {0: 1, 1: 4, 2: 2, 3: 2}
+SEG = {0: 512, 1: 256, 2: 1024, 3: 1024}
 
 
 def kbits(dt, p):
-    return (4 if p == 0 else 3) if dt == 2 else 8
+    if dt == 2:
+        return 4 if p == 0 else 3
+    if dt == 3:
+        return 4 if p == 0 else 2
+    return 8
 
 
 # ------------------------------------------------------------ code lengths --
@@ -145,6 +149,14 @@ def split(dt, w):
     if dt == 1:
         return [(w >> 23) & 0xFF, ((w >> 24) & 0x80) | ((w >> 16) & 0x7F), (w >> 8) & 0xFF,
                 w & 0xFF], 0
+    if dt == 3:
+        # two FP4 E2M1 values, the first in the low nibble; a nibble reads
+        # 8*sign + 2*exponent + mantissa
+        lo, hi = w % 16, w // 16
+        e = [(v // 2) % 4 for v in (lo, hi)]
+        m = [v % 2 for v in (lo, hi)]
+        sg = [v // 8 for v in (lo, hi)]
+        return [e[0] + 4 * e[1], m[0] + 2 * m[1]], sg[0] + 2 * sg[1]
     return [(w >> 3) & 0xF, w & 7], w >> 7
 
 
@@ -154,6 +166,10 @@ def merge(dt, syms, raw):
     if dt == 1:
         return ((syms[1] & 0x80) << 24) | (syms[0] << 23) | ((syms[1] & 0x7F) << 16) | \
             (syms[2] << 8) | syms[3]
+    if dt == 3:
+        nib = [8 * (raw % 2) + 2 * (syms[0] % 4) + syms[1] % 2,
+               8 * (raw // 2) + 2 * (syms[0] // 4) + syms[1] // 2]
+        return nib[0] + 16 * nib[1]
     return (raw << 7) | (syms[0] << 3) | syms[1]
 
 
@@ -266,7 +282,7 @@ def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0):
     off_dir = 64 + 16 * T
     cur = a16(off_dir + 8 * (M + 1))
     raw_off = []
-    raw_size = {0: lambda n: n, 1: lambda n: 0, 2: lambda n: (n + 7) // 8}[dt]
+    raw_size = {0: lambda n: n, 1: lambda n: 0, 2: lambda n: (n + 7) // 8, 3: lambda n: (n + 3) // 4}[dt]
     for t in tensors:
         raw_off.append(cur)
         cur = a16(cur + raw_size(len(t)))
@@ -301,6 +317,8 @@ def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0):
                 out[raw_off[ti] + i] = raw
             elif dt == 2 and raw:
                 out[raw_off[ti] + i // 8] |= 1 << (i % 8)
+            elif dt == 3 and raw:
+                out[raw_off[ti] + i // 4] |= raw << (2 * (i % 4))
     pos = off_rec
     for ci, r in enumerate(recs):
         struct.pack_into("<Q", out, off_dir + 8 * ci, pos)
@@ -369,7 +387,14 @@ def decode_container(blob, group_lengths_table=None):
                 pos += head + a16(pay)
             for i in range(m):
                 e = i0 + i
-                raw = blob[roff + e] if dt == 0 else ((blob[roff + e // 8] >> (e % 8)) & 1 if dt == 2 else 0)
+                if dt == 0:
+                    raw = blob[roff + e]
+                elif dt == 2:
+                    raw = (blob[roff + e // 8] >> (e % 8)) & 1
+                elif dt == 3:
+                    raw = (blob[roff + e // 4] >> (2 * (e % 4))) & 3
+                else:
+                    raw = 0
                 vals.append(merge(dt, [planes[p][i] for p in range(nc)], raw))
             c += 1
         outs.append(vals)

@@ -45,12 +45,12 @@ def test_roundtrip_bf16_ragged(oracle, n):
     _roundtrip(oracle, oracle.BF16, [_bf16(n, seed=n)], cb=4096)
 
 
-@pytest.mark.parametrize("dt", [0, 1, 2])
+@pytest.mark.parametrize("dt", [0, 1, 2, 3])
 def test_roundtrip_every_bit_pattern(oracle, dt):
     rng = np.random.default_rng(dt)
     if dt == 0:
         x = rng.permutation(np.arange(1 << 16, dtype=np.uint16))
-    elif dt == 2:
+    elif dt in (2, 3):
         x = np.tile(np.arange(256, dtype=np.uint8), 64)
     else:
         x = rng.integers(0, 1 << 32, 70000, dtype=np.uint64).astype(np.uint32)
@@ -79,10 +79,19 @@ def test_roundtrip_fp8_and_fp32_configs_small(oracle):
     _roundtrip(oracle, oracle.FP8_E4M3, [x8])
     pair = W.fp32_pair(150000, device="cpu", seed=3)
     _roundtrip(oracle, oracle.FP32, [_bits_np(t) for _, t in pair])
+    x4 = W.fp4_blockscaled(300001, device="cpu", seed=8)[0][1].numpy()
+    blob, st = oracle.compress(oracle.FP4X2_E2M1, [x4], 262144, with_stats=True)
+    (y4,) = oracle.decompress(blob, [x4.size], oracle.FP4X2_E2M1)
+    assert np.array_equal(x4, y4)
+    # block-scaled values use every exponent, but not evenly: the exponent
+    # pairs are coded below their 4 raw bits, the near-uniform mantissa bits
+    # stay raw (the whole container is then about as large as the input)
+    assert st["mode_count"][0][oracle.HUFF] > 0 and st["mode_count"][1][oracle.RAW] > 0
+    assert st["payload_bits"][0] < 4 * x4.size
 
 
 # -------------------------------------------------- independent restatement --
-@pytest.mark.parametrize("dt,n", [(0, 3000), (0, 1), (1, 2500), (2, 5000)])
+@pytest.mark.parametrize("dt,n", [(0, 3000), (0, 1), (1, 2500), (2, 5000), (3, 5001), (3, 3)])
 def test_bytes_equal_independent_python_encoder(oracle, dt, n):
     rng = np.random.default_rng(n)
     if dt == 0:
@@ -90,8 +99,10 @@ def test_bytes_equal_independent_python_encoder(oracle, dt, n):
     elif dt == 1:
         f = (rng.standard_normal(n) * 0.02).astype(np.float32).view(np.uint32)
         tensors = [f, f & np.uint32(0xFFFF0000)]
-    else:
+    elif dt == 2:
         tensors = [_bits_np(W.fp8_blockscaled(n, device="cpu", seed=6)[0][1])]
+    else:
+        tensors = [W.fp4_blockscaled(n, device="cpu", seed=9)[0][1].numpy(), np.full(77, 0x22, np.uint8)]
     blob = oracle.compress(dt, tensors, 4096)
     ref = ref_tiny.encode_container(dt, [[int(v) for v in t] for t in tensors], 4096)
     assert blob.tobytes() == ref

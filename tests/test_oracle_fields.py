@@ -4,9 +4,13 @@ The split follows THEORY-599 (nucleation note on ZipNN), per-field
 compressibility (ZipNN Table II): the exponent is taken out, the sign and
 fraction bytes stay as they are; FP8 follows "Lossless Compression of Neural
 Network Components ... Low-Precision Formats", Abstract (exponent and
-mantissa separated).  Pins: merge(split(x)) == x on every BF16 and FP8 bit
-pattern; the extracted field equals the IEEE-754 biased exponent that numpy /
-torch report for normal numbers (frexp); hand-checked bit patterns.
+mantissa separated), and so does FP4 (E2M1, the same page's other format),
+stored two values to a byte.  Pins: merge(split(x)) == x on every BF16, FP8
+and FP4-pair bit pattern; the extracted field equals the IEEE-754 biased
+exponent that numpy / torch report for normal numbers (frexp), and for FP4
+the exponent and mantissa of each value of the E2M1 magnitude list (0, 0.5,
+1, 1.5, 2, 3, 4, 6: bias 1, one mantissa bit, subnormals below 1);
+hand-checked bit patterns.
 """
 import numpy as np
 import pytest
@@ -29,6 +33,47 @@ def test_fp8_exhaustive_identity(oracle):
     planes, raw = oracle.split(oracle.FP8_E4M3, x)
     assert np.array_equal(oracle.merge(oracle.FP8_E4M3, planes, raw), x)
     assert planes[0].max() == 15 and planes[1].max() == 7 and raw.max() == 1
+
+
+def test_fp4_exhaustive_identity(oracle):
+    x = np.arange(256, dtype=np.uint8)
+    planes, raw = oracle.split(oracle.FP4X2_E2M1, x)
+    assert np.array_equal(oracle.merge(oracle.FP4X2_E2M1, planes, raw), x)
+    assert planes[0].max() == 15 and planes[1].max() == 3 and raw.max() == 3
+    key = (planes[0].astype(np.int64) * 4 + planes[1]) * 4 + raw
+    assert np.unique(key).size == 256          # a bijection
+
+
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_fp4_fields_against_e2m1_values(oracle):
+    # Each byte holds two values, the first in its low nibble; a nibble is a
+    # sign bit over a 3-bit magnitude code.  From each value's magnitude
+    # alone: exponent = 0 below 1 (subnormal), else floor(log2 |v|) + 1 (bias
+    # 1); mantissa = the fraction's one bit (0.5 steps for subnormals).
+    x = np.arange(256, dtype=np.uint8)
+    planes, raw = oracle.split(oracle.FP4X2_E2M1, x)
+    for half, shift in ((0, 0), (1, 4)):
+        nib = (x >> shift) & 15
+        mag = np.array([E2M1_MAGNITUDES[v & 7] for v in nib])
+        neg = nib >= 8
+        sub = mag < 1.0
+        e = np.where(sub, 0, _frexp_exponent(np.where(sub, 1.0, mag)))
+        m = np.where(sub, mag / 0.5, (mag / 2.0 ** (e - 1) - 1.0) * 2.0)
+        assert np.array_equal((planes[0] >> (2 * half)) & 3, e.astype(np.uint8))
+        assert np.array_equal((planes[1] >> half) & 1, m.astype(np.uint8))
+        assert np.array_equal((raw >> half) & 1, neg.astype(np.uint8))
+
+
+@pytest.mark.parametrize("value,e,m,s", [(0x21, 4, 1, 0), (0xF7, 15, 3, 2), (0x00, 0, 0, 0),
+                                          (0x8A, 1, 0, 3), (0x1C, 2, 2, 1)])
+def test_fp4_hand_checked(oracle, value, e, m, s):
+    # 0x21: 0.5 then 1.0; 0xF7: 6.0 then -6.0; 0x8A: -1.0 then -0.0;
+    # 0x1C: -2.0 then 0.5
+    planes, raw = oracle.split(oracle.FP4X2_E2M1, np.array([value], np.uint8))
+    assert (planes[0][0], planes[1][0], raw[0]) == (e, m, s)
+    assert ref_tiny.split(3, value) == ([e, m], s)
 
 
 def test_fp32_random_and_special_identity(oracle):
