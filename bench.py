@@ -51,6 +51,8 @@ WORKLOADS = {
             "256 KiB chunks",
     "fp8": "FP8 E4M3 1,073,741,824 values, N(0,1) scaled per 128-element block to max 448, "
            "256 KiB chunks",
+    "fp4": "FP4 E2M1 pairs, 536,870,912 bytes = 2^30 values, N(0,1) scaled per 32-value block to max 6, "
+           "rounded to E2M1 (ties to even), two values per byte; 256 KiB chunks",
     "transfer": "setup with 16 shared-table groups on the 8B-shaped BF16 block above, transferred to another "
                 "architecture: 2 3B-shaped BF16 blocks (Wq/Wo 3072x3072, Wk/Wv 1024x3072, W_gate/W_up 8192x3072, "
                 "W_down 3072x8192 N(0, sigma~U[0.01,0.04]) + 2 RMSNorm vectors N(1, 0.05) each; 201,338,880 "
@@ -101,6 +103,8 @@ def make_tensors(name: str):
         return [t for _, t in W.fp32_pair(1 << 27, device="cuda")]
     if name == "fp8":
         return [t for _, t in W.fp8_blockscaled(1 << 30, device="cuda")]
+    if name == "fp4":
+        return [t for _, t in W.fp4_blockscaled(1 << 29, device="cuda")]
     if name == "model":
         return [t for _, t in W.model_bf16("cuda", seed=5)]
     if name == "transfer":
@@ -137,6 +141,8 @@ def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16):
     from lossless_float_weight_amd import workloads as W
     from oracle import zno
     dt = {2: zno.BF16, 4: zno.FP32, 1: zno.FP8_E4M3}[tensors[0].element_size()]
+    if str(tensors[0].dtype) == "torch.uint8":   # FP4 E2M1 pairs travel as bytes
+        dt = zno.FP4X2_E2M1
     esz = tensors[0].element_size()
     # calibrate on 4 MiB, then take whole tensors (and a slice of the last) up to the budget
     first = W.bits(tensors[0]).reshape(-1)
@@ -362,7 +368,9 @@ def main():
         v = sorted(v)
         return v[len(v) // 2]
 
-    raw_planes = unc // 2 if base[0].element_size() == 2 else (unc // 8 if base[0].element_size() == 1 else 0)
+    raw_planes = {2: unc // 2, 4: 0, 1: unc // 8}[base[0].element_size()]
+    if base[0].dtype == torch.uint8:     # FP4 pairs: two sign bits per byte
+        raw_planes = unc // 4
     # algorithmic bytes per launch: what each kernel must read and write
     algo = {"decode": nbytes + unc,                       # container in, tensors out
             "analyze": unc + raw_planes,                  # tensors in, always-raw planes out

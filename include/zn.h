@@ -48,7 +48,12 @@
 extern "C" {
 #endif
 
-typedef enum { ZN_BF16 = 0, ZN_FP32 = 1, ZN_FP8_E4M3 = 2 } zn_dtype;
+/* ZN_FP4X2_E2M1: every element is one byte holding two FP4 E2M1 values, the
+ * first in the low nibble (a nibble is sign | 2 exponent bits | 1 mantissa
+ * bit); element counts are bytes.  The byte's two exponents form one coded
+ * 4-bit field and its two mantissas one coded 2-bit field; its two sign bits
+ * are kept raw. */
+typedef enum { ZN_BF16 = 0, ZN_FP32 = 1, ZN_FP8_E4M3 = 2, ZN_FP4X2_E2M1 = 3 } zn_dtype;
 
 typedef enum {
   ZN_OK = 0,

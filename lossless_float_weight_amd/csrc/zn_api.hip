@@ -46,7 +46,7 @@ struct zn_tableset {
 
 namespace {
 
-bool valid_dtype(int dt) { return dt == BF16 || dt == FP32 || dt == FP8; }
+bool valid_dtype(int dt) { return dt == BF16 || dt == FP32 || dt == FP8 || dt == FP4X2; }
 bool valid_chunk(uint32_t cb) { return cb >= 4096 && cb <= (1u << 20) && cb % 4096 == 0; }
 
 void put_u16(uint8_t *p, uint32_t v) { p[0] = v & 0xFF; p[1] = (v >> 8) & 0xFF; }

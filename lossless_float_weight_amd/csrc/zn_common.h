@@ -9,6 +9,10 @@
 //       FP32  P0 = exponent, P1 = sign|frac[22:16], P2, P3 = low fraction
 //             bytes, all coded (raw fallback)
 //       FP8   E4 = (b>>3)&15, M3 = b&7 coded; sign bit kept raw
+//       FP4 pairs (E2M1, two values per byte, the first in the low nibble;
+//             a nibble is sign(3) | exponent(2..1) | mantissa(0)):
+//             E = e_lo | e_hi<<2 and M = m_lo | m_hi<<1 coded; the two sign
+//             bits kept raw
 //   * per chunk and coded stream: order-0 histogram, optimal prefix code with
 //     lengths <= 11 (package-merge, leaves by (count, symbol), leaves before
 //     packages at equal weight), canonical codes, LSB-first bits with each
@@ -32,16 +36,18 @@ constexpr int kVersion = 1;
 constexpr int kRounds = 8;            // Lloyd rounds of the grouped setup
 
 enum Mode { RAW = 0, CONST = 1, HUFF = 2, GROUP = 3 };
-enum DType { BF16 = 0, FP32 = 1, FP8 = 2 };
+enum DType { BF16 = 0, FP32 = 1, FP8 = 2, FP4X2 = 3 };
 
 __host__ __device__ constexpr int esize(int dt) { return dt == BF16 ? 2 : dt == FP32 ? 4 : 1; }
 __host__ __device__ constexpr int ncoded(int dt) { return dt == BF16 ? 1 : dt == FP32 ? 4 : 2; }
-__host__ __device__ constexpr int kbits(int dt, int p) { return dt == FP8 ? (p == 0 ? 4 : 3) : 8; }
+__host__ __device__ constexpr int kbits(int dt, int p) {
+  return dt == FP8 ? (p == 0 ? 4 : 3) : dt == FP4X2 ? (p == 0 ? 4 : 2) : 8;
+}
 // symbols per segment: a full 256 KiB chunk gives 256 segments per coded stream
 __host__ __device__ constexpr int segsyms(int dt) { return dt == BF16 ? 512 : dt == FP32 ? 256 : 1024; }
 __host__ __device__ constexpr uint64_t align16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
 __host__ __device__ inline uint64_t rawplane_bytes(int dt, uint64_t n) {
-  return dt == BF16 ? n : dt == FP8 ? (n + 7) / 8 : 0;
+  return dt == BF16 ? n : dt == FP8 ? (n + 7) / 8 : dt == FP4X2 ? (n + 3) / 4 : 0;
 }
 __host__ __device__ inline uint64_t payload_bytes_of(int mode, int k, uint64_t n, uint64_t bits) {
   if (mode == HUFF || mode == GROUP) return 4 * ((bits + 31) / 32);

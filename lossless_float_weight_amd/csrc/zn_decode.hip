@@ -115,6 +115,26 @@ __device__ __forceinline__ uint64_t tri_bytes(uint32_t x) {
   return r;
 }
 
+// 8 values of 2 bits (bits 0..15) -> 8 bytes: the usual bit spread puts each
+// value in a nibble of its own, then nib_bytes spreads the nibbles.
+__device__ __forceinline__ uint64_t duo_bytes(uint32_t x) {
+  x &= 0xFFFFu;
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return nib_bytes(x);
+}
+
+// 4 bytes of FP4 pairs from their exponent pairs (e, a byte each), mantissa
+// pairs (m, a byte each) and the 8 sign bits sg (two per byte): each byte is
+// m_lo | e_lo << 1 | s_lo << 3 | m_hi << 4 | e_hi << 5 | s_hi << 7.
+__device__ __forceinline__ uint32_t merge_fp4x2(uint32_t e, uint32_t m, uint32_t sg) {
+  uint32_t t = (sg | (sg << 12)) & 0x000F000Fu;   // sign pairs to their bytes
+  t = (t | (t << 6)) & 0x03030303u;
+  return (m & 0x01010101u) | ((e & 0x03030303u) << 1) | ((t & 0x01010101u) << 3) |
+         ((m & 0x02020202u) << 3) | ((e & 0x0C0C0C0Cu) << 3) | ((t & 0x02020202u) << 6);
+}
+
 template <int DT>
 __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
@@ -138,7 +158,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   const bool oaligned = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
   const uint8_t *in = a.in;
   uint8_t *const sink = reinterpret_cast<uint8_t *>(a.ctl) + kSinkOff;
-  const uint8_t *rawp = in + a.L.t_raw[t] + (DT == BF16 ? e0 : DT == FP8 ? e0 / 8 : 0);
+  const uint8_t *rawp = in + a.L.t_raw[t] + (DT == BF16 ? e0 : DT == FP8 ? e0 / 8 : DT == FP4X2 ? e0 / 4 : 0);
 
   // The first stream of the record is usually Huffman- or group-coded:
   // its code lengths (Huffman) and segment lengths (at either offset) are
@@ -245,7 +265,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
 
   // Fields of the raw streams for one 16-byte output vector of VE elements
   // starting at element ev (< n): k = 8 gives VE bytes, k = 4 VE nibbles,
-  // k = 3 a 3*VE-bit run.  Every read stays inside the stream's payload, or
+  // k = 3 a 3*VE-bit run, k = 2 a 2*VE-bit word.  Every read stays inside the stream's payload, or
   // at most 4 bytes past it where the record or the container tail follows
   // (the record walk checked that the container holds them).
   // payload bases as wave-uniform values, so loads take a scalar base and a
@@ -266,6 +286,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       else return 0;
     }
     if (k == 4) { const u32x2 x = ldg8(pay + ev / 2); return x[0] | (uint64_t(x[1]) << 32); }
+    if (k == 2) return ldg4(pay + ev / 4);   // ev is a multiple of 16: a whole word
     const uint32_t b = ev * 3, w0 = b >> 5;   // ev is a multiple of 16: b & 31 is 0 or 16
     const uint64_t x = ldg4(pay + 4 * w0) | (uint64_t(ldg4(pay + 4 * w0 + 4)) << 32);
     return x >> (b & 31);
@@ -385,7 +406,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       // so no wait has to drain the stores in flight.  A partial
       // last vector stays inside the always-raw plane, whose size is padded
       // to 16 bytes: BF16 vectors start at multiples of 8 bytes, FP8 sign
-      // words at multiples of 2.
+      // words at multiples of 2, FP4 sign words at multiples of 4.
       using FT = std::conditional_t<ES == 4, uint32_t, uint64_t>;  // VE raw-stream fields
       struct RawIn { uint64_t plane[NVL]; FT f[NC][NVL]; };
       auto load_raw = [&](int r, RawIn &rv) {
@@ -400,6 +421,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             rv.plane[i] = x[0] | (uint64_t(x[1]) << 32);
           } else if constexpr (DT == FP8) {
             rv.plane[i] = ldg2(rawp + ev / 8);
+          } else if constexpr (DT == FP4X2) {
+            rv.plane[i] = ldg4(rawp + ev / 4);    // two sign bits per element
           } else {
             rv.plane[i] = 0;
           }
@@ -537,6 +560,22 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           } else if constexpr (DT == FP32) {
             o = merge_fp32(uint32_t(fieldv(0, 0)), uint32_t(fieldv(1, 0)), uint32_t(fieldv(2, 0)),
                            uint32_t(fieldv(3, 0)));
+          } else if constexpr (DT == FP4X2) {
+            // exponent pairs and mantissa pairs of the 16 elements as bytes
+            uint64_t Ev[2], Mv[2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+              const bool r0 = RAWM != 0 ? (RAWM & 1) != 0 : !ALLC && RAWF && sh.mode[0] == RAW;
+              const bool r1 = RAWM != 0 ? (RAWM & 2) != 0 : !ALLC && RAWF && sh.mode[1] == RAW;
+              if (r0) Ev[h] = nib_bytes(uint32_t(rawv.f[0][i] >> (32 * h)));
+              else Ev[h] = fieldv(0, h);
+              if (r1) Mv[h] = duo_bytes(uint32_t(rawv.f[1][i] >> (16 * h)));
+              else Mv[h] = fieldv(1, h);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; x++)
+              o[x] = merge_fp4x2(uint32_t(Ev[x >> 1] >> (32 * (x & 1))), uint32_t(Mv[x >> 1] >> (32 * (x & 1))),
+                                 uint32_t(rawv.plane[i] >> (8 * x)) & 0xFFu);
           } else {
             // E4 and M3 of the 16 elements as bytes, from whichever source
             uint64_t Ev[2], Mv[2];
@@ -678,7 +717,8 @@ hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s, hipEvent_t 
   const dim3 grid(a.L.n_chunks), block(DEC_NT);
   if (dtype == BF16) hipExtLaunchKernelGGL(k_decode<BF16>, grid, block, 0, s, e0, e1, 0, a);
   else if (dtype == FP32) hipExtLaunchKernelGGL(k_decode<FP32>, grid, block, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL(k_decode<FP8>, grid, block, 0, s, e0, e1, 0, a);
+  else if (dtype == FP8) hipExtLaunchKernelGGL(k_decode<FP8>, grid, block, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL(k_decode<FP4X2>, grid, block, 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 

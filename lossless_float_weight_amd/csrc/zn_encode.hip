@@ -46,6 +46,10 @@ __device__ __forceinline__ uint32_t field(uint32_t w) {
     if constexpr (P == 2) return (w >> 8) & 0xFF;
     return w & 0xFF;
   }
+  if constexpr (DT == FP4X2) {   // the byte's two exponents, then its two mantissas
+    if constexpr (P == 0) return ((w >> 1) & 3) | ((w >> 3) & 0xC);
+    return (w & 1) | ((w >> 3) & 2);
+  }
   if constexpr (P == 0) return (w >> 3) & 0xF;
   return w & 7;
 }
@@ -112,7 +116,7 @@ struct EncShared {
   static constexpr int NT = enc_nt(DT);
   static constexpr int NW = NT / 64;                              // waves = segments per pack tile
   static constexpr int COLS = DT == FP32 ? 16 : 32;
-  static constexpr int APRIV = DT == FP8 ? (16 + 8) : 256 * NC;   // total bins
+  static constexpr int APRIV = DT == FP8 ? (16 + 8) : DT == FP4X2 ? (16 + 4) : 256 * NC;   // total bins
   // BF16 counts two bins per word (a column sees at most 1/32 of a chunk,
   // 16384 values at the largest chunk size, so 16 bits cannot overflow)
   static constexpr bool PACK16 = DT == BF16;
@@ -139,7 +143,7 @@ struct EncShared {
 
 template <int DT>
 __device__ __forceinline__ int priv_base(int p) {
-  if constexpr (DT == FP8) return p == 0 ? 0 : 16;
+  if constexpr (DT == FP8 || DT == FP4X2) return p == 0 ? 0 : 16;
   return p * 256;
 }
 
@@ -234,6 +238,14 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
 #pragma unroll
         for (int i = 0; i < 16; i++) m |= ((vec_elem<DT>(q, i) >> 7) & 1) << i;
         stg2(rawp + e0 / 8 + uint64_t(v) * 2, m);
+      } else if constexpr (DT == FP4X2) {   // the two sign bits of each byte
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const uint32_t w = vec_elem<DT>(q, i);
+          m |= (((w >> 3) & 1) | ((w >> 6) & 2)) << (2 * i);
+        }
+        stg4(rawp + e0 / 4 + uint64_t(v) * 4, m);
       }
     }
   }
@@ -253,6 +265,18 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
       }
     }
   }
+  if constexpr (DT == FP4X2) {  // sign pairs of the tail, whole bytes by one thread
+    if (tid == 0 && nvec * VE < n) {
+      for (uint32_t b = nvec * VE / 4; b < (n + 3) / 4; b++) {
+        uint32_t m = 0;
+        for (uint32_t i = b * 4; i < b * 4 + 4 && i < n; i++) {
+          const uint32_t w = src[i];
+          m |= (((w >> 3) & 1) | ((w >> 6) & 2)) << (2 * (i - b * 4));
+        }
+        rawp[e0 / 4 + b] = uint8_t(m);
+      }
+    }
+  }
   __syncthreads();
   for (int i = tid; i < EncShared<DT>::APRIV; i += ENC_NT) {
     uint32_t s = 0;
@@ -264,7 +288,7 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
       for (int j = 0; j < COLS; j++) s += sh.u.priv[i * COLS + ((j + i) & (COLS - 1))];
     }
     int p = 0, sym = i;
-    if constexpr (DT == FP8) { p = i >= 16; sym = i - (p ? 16 : 0); }
+    if constexpr (DT == FP8 || DT == FP4X2) { p = i >= 16; sym = i - (p ? 16 : 0); }
     else { p = i >> 8; sym = i & 255; }
     sh.hist[p][sym] = s;
   }
@@ -459,7 +483,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   // scan; the next step's elements are loaded while this step packs.  Bits
   // past the last element are zero.
   {
-    constexpr int LE = DT == FP8 ? 32 : VE;      // FP8: k = 3 needs 32 elements per 3 words
+    constexpr int LE = DT == FP8 || DT == FP4X2 ? 32 : VE;   // FP8: k = 3 needs 32 elements per 3 words
     constexpr int NQ = LE / VE;                  // 16-byte loads per lane per step
     uint32_t rawmask = 0;
     uint8_t *pw[NC];
@@ -799,7 +823,8 @@ hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s, hipEvent_t
   const dim3 grid(a.L.n_chunks), block(enc_nt(dtype));
   if (dtype == BF16) hipExtLaunchKernelGGL(k_analyze<BF16>, grid, block, 0, s, e0, e1, 0, a);
   else if (dtype == FP32) hipExtLaunchKernelGGL(k_analyze<FP32>, grid, block, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL(k_analyze<FP8>, grid, block, 0, s, e0, e1, 0, a);
+  else if (dtype == FP8) hipExtLaunchKernelGGL(k_analyze<FP8>, grid, block, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL(k_analyze<FP4X2>, grid, block, 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
@@ -808,7 +833,8 @@ hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s, hipEvent_t e
   const dim3 grid(a.L.n_chunks), block(PACK_NT);
   if (dtype == BF16) hipExtLaunchKernelGGL(k_pack<BF16>, grid, block, 0, s, e0, e1, 0, a);
   else if (dtype == FP32) hipExtLaunchKernelGGL(k_pack<FP32>, grid, block, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL(k_pack<FP8>, grid, block, 0, s, e0, e1, 0, a);
+  else if (dtype == FP8) hipExtLaunchKernelGGL(k_pack<FP8>, grid, block, 0, s, e0, e1, 0, a);
+  else hipExtLaunchKernelGGL(k_pack<FP4X2>, grid, block, 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 

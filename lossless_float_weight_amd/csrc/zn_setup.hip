@@ -24,6 +24,10 @@ __device__ __forceinline__ uint32_t sfield(uint32_t w) {
     if constexpr (P == 2) return (w >> 8) & 0xFF;
     return w & 0xFF;
   }
+  if constexpr (DT == FP4X2) {
+    if constexpr (P == 0) return ((w >> 1) & 3) | ((w >> 3) & 0xC);
+    return (w & 1) | ((w >> 3) & 2);
+  }
   if constexpr (P == 0) return (w >> 3) & 0xF;
   return w & 7;
 }
@@ -192,7 +196,8 @@ hipError_t launch_hist_all(int dtype, const DevLayout &L, const uint8_t *const *
   const dim3 grid(L.n_chunks), block(HIST_NT);
   if (dtype == BF16) hipLaunchKernelGGL(k_hist_all<BF16>, grid, block, 0, s, L, in_ptrs, hist);
   else if (dtype == FP32) hipLaunchKernelGGL(k_hist_all<FP32>, grid, block, 0, s, L, in_ptrs, hist);
-  else hipLaunchKernelGGL(k_hist_all<FP8>, grid, block, 0, s, L, in_ptrs, hist);
+  else if (dtype == FP8) hipLaunchKernelGGL(k_hist_all<FP8>, grid, block, 0, s, L, in_ptrs, hist);
+  else hipLaunchKernelGGL(k_hist_all<FP4X2>, grid, block, 0, s, L, in_ptrs, hist);
   return hipGetLastError();
 }
 

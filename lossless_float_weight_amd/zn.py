@@ -16,8 +16,10 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzn.so")
 
-BF16, FP32, FP8_E4M3 = 0, 1, 2
-TORCH_DTYPE = {BF16: torch.bfloat16, FP32: torch.float32, FP8_E4M3: torch.float8_e4m3fn}
+BF16, FP32, FP8_E4M3, FP4X2_E2M1 = 0, 1, 2, 3
+# FP4 E2M1 pairs travel as uint8 tensors (two values per byte, low nibble first)
+TORCH_DTYPE = {BF16: torch.bfloat16, FP32: torch.float32, FP8_E4M3: torch.float8_e4m3fn,
+               FP4X2_E2M1: torch.uint8}
 ZN_DTYPE = {v: k for k, v in TORCH_DTYPE.items()}
 STATUS = {0: "ok", -1: "invalid argument", -2: "corrupt container", -3: "buffer too small",
           -4: "tableset mismatch", -5: "HIP runtime error", -6: "out of memory"}
@@ -127,7 +129,7 @@ class Tableset:
         return self.info()["hash"]
 
     def lengths(self, g: int) -> list:
-        A = 16 if self.dtype == FP8_E4M3 else 256
+        A = 16 if self.dtype in (FP8_E4M3, FP4X2_E2M1) else 256
         buf = (C.c_uint8 * A)()
         _check(lib().zn_tableset_lengths(self.handle, g, buf), "tableset_lengths")
         return list(buf)
@@ -249,7 +251,7 @@ def decompress(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Tensor] | 
 
 def debug_histograms(ts: Tableset, tensors: Sequence[torch.Tensor], stream=None) -> torch.Tensor:
     info = ts.info()
-    nc = {BF16: 1, FP32: 4, FP8_E4M3: 2}[info["dtype"]]
+    nc = {BF16: 1, FP32: 4, FP8_E4M3: 2, FP4X2_E2M1: 2}[info["dtype"]]
     hist = torch.zeros((info["n_chunks"], nc, 256), dtype=torch.int32, device=tensors[0].device)
     ptrs = _ptr_array(tensors, tensors[0].device)
     _check(lib().zn_debug_histograms(ts.handle, C.c_void_p(ptrs.data_ptr()),

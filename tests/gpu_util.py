@@ -7,7 +7,7 @@ import torch
 from lossless_float_weight_amd import workloads as W
 from lossless_float_weight_amd import zn
 
-NP_DTYPE = {zn.BF16: np.uint16, zn.FP32: np.uint32, zn.FP8_E4M3: np.uint8}
+NP_DTYPE = {zn.BF16: np.uint16, zn.FP32: np.uint32, zn.FP8_E4M3: np.uint8, zn.FP4X2_E2M1: np.uint8}
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

@@ -141,6 +141,53 @@ def test_fp8_ragged_every_pattern(oracle, n):
     _check_equal(oracle, oracle.FP8_E4M3, [x.cuda()], 4096)
 
 
+# ------------------------------------------------------------- FP4 pairs ----
+def _fp4_bytes(lo, hi):
+    return (lo.to(torch.int64) | (hi.to(torch.int64) << 4)).to(torch.uint8)
+
+
+def test_fp4_every_decode_path(oracle):
+    print("case: FP4 pair field-mode mixes", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(12)
+    n = 8192
+    # nibble = 8 sign + 2 exponent + mantissa
+    def nib(e, m, s):
+        return 8 * s + 2 * e + m
+    sk = lambda: torch.randint(0, 8, (n,), generator=g).clamp(max=4) // 2           # skewed 0..2
+    bit = lambda: torch.randint(0, 2, (n,), generator=g)
+    few = lambda: (torch.randint(0, 8, (n,), generator=g) == 0).to(torch.int64)      # mostly 0
+    both = _fp4_bytes(nib(sk(), few(), bit()), nib(sk(), few(), bit()))            # E and M coded
+    mraw = _fp4_bytes(nib(sk(), bit(), bit()), nib(sk(), bit(), bit()))            # E coded, M raw
+    eraw = _fp4_bytes(nib(torch.randint(0, 4, (n,), generator=g), few(), bit()),
+                      nib(torch.randint(0, 4, (n,), generator=g), few(), bit()))   # E raw, M coded
+    const = torch.full((n,), 0x22, dtype=torch.uint8)                              # both constant
+    ts = [x.cuda() for x in (both, mraw, eraw, const)]
+    _, blob = _check_equal(oracle, oracle.FP4X2_E2M1, ts, 4096)
+    modes = set(field_modes(blob.cpu().numpy(), 2, [4, 2]))
+    assert {(2, 2), (2, 0), (0, 2), (1, 1)} <= modes, modes
+
+
+def test_fp4_blockscaled(oracle):
+    print("case: FP4 E2M1 pairs block-scaled 2^20 bytes", flush=True)
+    x = W.fp4_blockscaled(1 << 20, device="cuda")[0][1]
+    _check_equal(oracle, oracle.FP4X2_E2M1, [x], 262144)
+
+
+@pytest.mark.parametrize("n", [1, 3, 15, 17, 2049, 70001])
+def test_fp4_ragged_every_pattern(oracle, n):
+    print(f"case: FP4 pair patterns n={n}", flush=True)
+    x = (torch.arange(n, dtype=torch.int64) * 37 % 256).to(torch.uint8)
+    _check_equal(oracle, oracle.FP4X2_E2M1, [x.cuda()], 4096)
+
+
+def test_fp4_full_size_sampled(oracle):
+    print("case: FP4 E2M1 pairs 2^29 bytes, sampled records", flush=True)
+    tensors = [W.fp4_blockscaled(1 << 29, device="cuda")[0][1]]
+    ts, blob = gpu_compress(tensors, 262144)
+    _sampled_record_parity(oracle, oracle.FP4X2_E2M1, tensors, blob, 262144)
+    assert_roundtrip(ts, blob, tensors)
+
+
 # -------------------------------------------------------- single stages ----
 def test_histograms_equal_bincount(oracle):
     print("case: per-chunk histograms", flush=True)
