@@ -476,24 +476,37 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   for (int i = tid; i < 2 * STAGE; i += ENC_NT) stage_all[i / STAGE][i % STAGE] = 0;
   __syncthreads();
 
-  // ------------------------------------------- raw streams, in one pass
-  // Fixed-width values in element order, value bit 0 first.  A lane takes LE
-  // consecutive elements per step, LE*k a multiple of 32 for every field
-  // width of the dtype, so it writes whole words of every raw stream with no
-  // scan; the next step's elements are loaded while this step packs.  Bits
-  // past the last element are zero.
+  // ------------------------------------------- raw streams
+  // Fixed-width values in element order, value bit 0 first; bits past the
+  // last element are zero.  A raw stream whose values fill whole words in a
+  // run of EPT elements (EPT*k a multiple of 32) is written from the tiles of
+  // the first coded stream, which read every element anyway; the others, and
+  // all of them when no stream is coded, take one pass of their own here.
+  uint32_t rawmask = 0, tilemask = 0;
+  int firstcoded = -1;
+  uint8_t *pwr[NC];
+#pragma unroll
+  for (int p = 0; p < NC; p++) {
+    const int k = kbits(DT, p), mode = pmode[p];
+    rawmask |= uint32_t(mode == RAW) << p;
+    pwr[p] = recp + psec[p] + head_bytes_of(mode, k, nseg);
+    if (firstcoded < 0 && (mode == HUFF || mode == GROUP)) firstcoded = p;
+  }
+  if (firstcoded >= 0) {
+#pragma unroll
+    for (int p = 0; p < NC; p++)
+      if (((rawmask >> p) & 1) && (EPT * kbits(DT, p)) % 32 == 0) tilemask |= 1u << p;
+  }
+  // The pass: a lane takes LE consecutive elements per step, LE*k a multiple
+  // of 32 for every field width of the dtype, so it writes whole words of
+  // every raw stream with no scan; the next step's elements are loaded while
+  // this step packs.
   {
     constexpr int LE = DT == FP8 || DT == FP4X2 ? 32 : VE;   // FP8: k = 3 needs 32 elements per 3 words
     constexpr int NQ = LE / VE;                  // 16-byte loads per lane per step
-    uint32_t rawmask = 0;
-    uint8_t *pw[NC];
-#pragma unroll
-    for (int p = 0; p < NC; p++) {
-      const int k = kbits(DT, p), mode = pmode[p];
-      rawmask |= uint32_t(mode == RAW) << p;
-      pw[p] = recp + psec[p] + head_bytes_of(mode, k, nseg);
-    }
-    if (rawmask) {
+    const uint32_t passmask = rawmask & ~tilemask;
+    uint8_t *const *pw = pwr;
+    if (passmask) {
       u32x4 nx[NQ];
       auto fetch = [&](uint32_t e) {
         if (aligned && e + LE <= n) {
@@ -518,7 +531,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         fetch(e + uint32_t(ENC_NT) * LE);
 #pragma unroll
         for (int p = 0; p < NC; p++) {
-          if (!((rawmask >> p) & 1)) continue;
+          if (!((passmask >> p) & 1)) continue;
           constexpr int MAXW = LE * 8 / 32;
           const int k = kbits(DT, p);
           uint32_t wd[MAXW];
@@ -562,7 +575,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
     for (uint64_t i = used + tid; i < head; i += ENC_NT) sec[i] = 0;
     if (mode == CONST) continue;
     uint32_t *pw = reinterpret_cast<uint32_t *>(sec + head);
-    if (mode == RAW) {   // packed by the pass above; zero the section's pad
+    if (mode == RAW) {   // packed above or by the coded stream's tiles; zero the section's pad
       const uint64_t nw = (uint64_t(n) * k + 31) / 32, padw = align16(pay) / 4;
       for (uint64_t i = nw + tid; i < padw; i += ENC_NT) pw[i] = 0;
       continue;
@@ -631,6 +644,28 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         // element is read, and those past the end are dropped by a select
         // (no branch per element; their w is 0, a valid table index)
         const uint32_t lim = eb < n ? n - eb : 0u;
+        // the raw streams written from these tiles: the run's EPT values are
+        // whole words at element eb of each (eb*k is a multiple of 32)
+        if (p == firstcoded && tilemask && lim > 0) {
+#pragma unroll
+          for (int q = 0; q < NC; q++) {
+            if (!((tilemask >> q) & 1)) continue;
+            const int kq = kbits(DT, q);
+            constexpr int MAXW = EPT * 8 / 32;
+            uint32_t wd[MAXW];
+#pragma unroll
+            for (int x = 0; x < MAXW; x++) wd[x] = 0;
+#pragma unroll
+            for (int e = 0; e < EPT; e++) {
+              const uint32_t f = uint32_t(e) < lim ? field_rt<DT>(w[e], q) : 0u;
+              wd[(e * kq) >> 5] |= f << ((e * kq) & 31);
+            }
+            const uint32_t nwq = uint32_t((uint64_t(n) * kq + 31) / 32), w0 = eb * kq / 32;
+#pragma unroll
+            for (int x = 0; x < MAXW; x++)
+              if (x * 32 < EPT * kq && w0 + x < nwq) stg4(pwr[q] + 4ull * (w0 + x), wd[x]);
+          }
+        }
 #pragma unroll
         for (int g8 = 0; g8 < NG; g8++) {
           uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l[8] = {0, 0, 0, 0, 0, 0, 0, 0};
