@@ -478,10 +478,12 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
 
   // ------------------------------------------- raw streams
   // Fixed-width values in element order, value bit 0 first; bits past the
-  // last element are zero.  A raw stream whose values fill whole words in a
-  // run of EPT elements (EPT*k a multiple of 32) is written from the tiles of
-  // the first coded stream, which read every element anyway; the others, and
-  // all of them when no stream is coded, take one pass of their own here.
+  // last element are zero.  For FP32, whose raw streams take whole words in a
+  // lane's run of EPT elements (EPT*k = 32), they are written from the tiles
+  // of the first coded stream, which read every element anyway: the input is
+  // read once.  Otherwise (and when no stream is coded) they take one pass of
+  // their own here, in element order: for 1-byte elements the short stores
+  // scattered over the tiles cost more than reading the chunk again.
   uint32_t rawmask = 0, tilemask = 0;
   int firstcoded = -1;
   uint8_t *pwr[NC];
@@ -495,7 +497,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   if (firstcoded >= 0) {
 #pragma unroll
     for (int p = 0; p < NC; p++)
-      if (((rawmask >> p) & 1) && (EPT * kbits(DT, p)) % 32 == 0) tilemask |= 1u << p;
+      if (DT == FP32 && ((rawmask >> p) & 1) && (EPT * kbits(DT, p)) % 32 == 0) tilemask |= 1u << p;
   }
   // The pass: a lane takes LE consecutive elements per step, LE*k a multiple
   // of 32 for every field width of the dtype, so it writes whole words of
@@ -646,24 +648,21 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         const uint32_t lim = eb < n ? n - eb : 0u;
         // the raw streams written from these tiles: the run's EPT values are
         // whole words at element eb of each (eb*k is a multiple of 32)
-        if (p == firstcoded && tilemask && lim > 0) {
+        if (p == firstcoded && tilemask) {
 #pragma unroll
           for (int q = 0; q < NC; q++) {
             if (!((tilemask >> q) & 1)) continue;
             const int kq = kbits(DT, q);
-            constexpr int MAXW = EPT * 8 / 32;
-            uint32_t wd[MAXW];
-#pragma unroll
-            for (int x = 0; x < MAXW; x++) wd[x] = 0;
+            uint64_t bq = 0;   // the run's values, kq bits each (EPT*kq <= 64)
 #pragma unroll
             for (int e = 0; e < EPT; e++) {
               const uint32_t f = uint32_t(e) < lim ? field_rt<DT>(w[e], q) : 0u;
-              wd[(e * kq) >> 5] |= f << ((e * kq) & 31);
+              bq |= uint64_t(f) << ((e * kq) & 63);
             }
             const uint32_t nwq = uint32_t((uint64_t(n) * kq + 31) / 32), w0 = eb * kq / 32;
 #pragma unroll
-            for (int x = 0; x < MAXW; x++)
-              if (x * 32 < EPT * kq && w0 + x < nwq) stg4(pwr[q] + 4ull * (w0 + x), wd[x]);
+            for (int x = 0; x < 2; x++)
+              if (x * 32 < EPT * kq && lim > 0 && w0 + x < nwq) stg4(pwr[q] + 4ull * (w0 + x), uint32_t(bq >> (32 * x)));
           }
         }
 #pragma unroll
