@@ -180,6 +180,10 @@ def setup(tensors: Sequence[torch.Tensor] | None = None, *, dtype=None, n_elems=
 def setup_transfer(src: Tableset, tensors: Sequence[torch.Tensor], stream=None) -> Tableset:
     """zn_setup_transfer: src's group codes for these tensors (same dtype and
     chunk size), each chunk assigned by content to its cheapest group code."""
+    want = TORCH_DTYPE[src.info()["dtype"]]
+    if any(t.dtype != want for t in tensors):
+        raise ZnError(-1, f"setup_transfer: the source tableset codes {want}, got "
+                          f"{sorted(set(str(t.dtype) for t in tensors))}")
     tensors = [t.contiguous() for t in tensors]
     ptrs = (C.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
     h = C.c_void_p()

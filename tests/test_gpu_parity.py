@@ -264,6 +264,9 @@ def test_transfer_equals_oracle(oracle):
     assert tr.save() == otr.save() and tr.hash == otr.hash
     assert tr.cost_history() == ts.cost_history()
     _check_equal(oracle, oracle.BF16, other, 65536, tr, otr)
+    # tensors of another dtype are refused
+    with pytest.raises(zn.ZnError):
+        zn.setup_transfer(ts, [other[1].float()])
     # and back onto the set-up tensors themselves
     tr2 = zn.setup_transfer(ts, tensors)
     otr2 = oracle.setup_transfer(ots, [to_np(t) for t in tensors])
