@@ -86,7 +86,7 @@ zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t 
                    zn_tableset **out);
 
 /* zn_setup_transfer -- a setup reused on other tensors of the same dtype and
- * chunk size, such as another compatible architecture ("NeuralZip: Reusable
+ * chunk size, such as another architecture of the same kind ("NeuralZip: Reusable
  * Setup for Fast Lossless Compression", Abstract).  The new plan keeps src's
  * K group codes unchanged; every chunk of the new tensors (d_tensors: host
  * array of device pointers; n_elems[n_tensors] host) is histogrammed on the

@@ -768,8 +768,8 @@ int zno_setup(int dt, const void *const *tensors, const uint64_t *n_elems, int T
   return ZNO_OK;
 }
 
-/* Transfer of a setup to other tensors of the same dtype ("another
- * compatible architecture"  [NZ Abstract]): the source's K group codes are
+/* Transfer of a setup to other tensors of the same dtype (another model
+ * architecture of the same kind  [NZ Abstract]): the source's K group codes are
  * kept as they are; every chunk of the new tensors goes to the group code
  * that codes its exponent histogram in the fewest bits, ties to the smaller
  * group id; a chunk that every group code lacks a symbol for goes to group 0
