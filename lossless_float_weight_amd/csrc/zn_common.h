@@ -481,16 +481,19 @@ struct LutShared {
 };
 
 // Builds the multi-symbol decode table of a canonical code from its lengths.
-// lut[v] for an 11-bit LSB-first window v holds up to three whole code words:
-// bits 0-5 the bits they use (so the entry itself can serve as a shift
-// amount), 6-7 their number, 8-15, 16-23, 24-31 the symbols.  t1 (2048 x
-// u16, scratch) is the single-symbol table, indexed like lut by the LSB-first
-// window: symbol | length << 8.  Returns false (for every thread) if the
-// lengths are not a complete prefix code of at least two words with lengths
-// <= 11.  NT >= 256 threads; A <= 256.
-template <int NT>
+// lut[v] for a WB-bit LSB-first window v (2^WB entries) holds up to three
+// whole code words: bits 0-5 the bits they use (so the entry itself can serve
+// as a shift amount), 6-7 their number, 8-15, 16-23, 24-31 the symbols.  t1
+// (2^WB x u16, scratch) is the single-symbol table, indexed like lut by the
+// LSB-first window: symbol | length << 8.  Returns false (for every thread) if
+// the lengths are not a complete prefix code of at least two words with
+// lengths <= min(11, WB).  A window narrower than 11 bits serves small
+// alphabets: a complete code over d symbols has no word longer than d - 1
+// bits.  NT >= 256 threads; A <= 256.
+template <int NT, int WB = kLutBits>
 __device__ __attribute__((always_inline)) bool build_lut(const uint8_t *len, int A, uint32_t *lut, uint16_t *t1,
                                                      LutShared &S) {
+  static_assert(WB >= 2 && WB <= kLutBits, "window of 2..11 bits");
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
   const int l = tid < A ? len[tid] : 0;
   int rank = 0;
@@ -501,7 +504,7 @@ __device__ __attribute__((always_inline)) bool build_lut(const uint8_t *len, int
   }
   if (tid == 0) S.bad = 0;
   __syncthreads();
-  if (tid < A && l > kMaxLen) S.bad = 1;
+  if (tid < A && l > (WB < kMaxLen ? WB : kMaxLen)) S.bad = 1;
   if (wv == 0) {
     // lane b (1..11): the number of codes of length b, the sorted index of
     // the first of them, the first canonical code of length b (the sum of
@@ -540,8 +543,10 @@ __device__ __attribute__((always_inline)) bool build_lut(const uint8_t *len, int
   // all write one condition register and serialise the entries of a thread.
   // All lengths first, then all table reads, then all writes, so that the
   // reads of the eight entries of a thread overlap.
-  static_assert(kLutSize % NT == 0, "whole passes");
-  constexpr int PER = kLutSize / NT;
+  constexpr int TS = 1 << WB;                  // table entries
+  static_assert(TS % NT == 0 || TS < NT, "whole passes");
+  constexpr int PER = TS >= NT ? TS / NT : 1;  // entries per thread (threads past TS idle)
+  const bool own = tid < TS;
   int ljm[kMaxLen];
 #pragma unroll
   for (int j = 1; j < kMaxLen; j++) ljm[j] = S.ljend[j] - 1;
@@ -549,11 +554,15 @@ __device__ __attribute__((always_inline)) bool build_lut(const uint8_t *len, int
   // first-bit-as-MSB reading u = reverse(v) is what the ranges compare.
   // Threads take consecutive v, so both the stores here and the first
   // lookups below fall in distinct LDS banks.
-  auto rev11 = [](int v) { return int(__builtin_bitreverse32(uint32_t(v)) >> (32 - kMaxLen)); };
+  // (reading the window's WB bits as the top bits of an 11-bit code)
+  auto rev11 = [](int v) {
+    return int(__builtin_bitreverse32(uint32_t(v)) >> (32 - WB)) << (kMaxLen - WB);
+  };
+  auto win = [&](int i) { return (tid + i * NT) & (TS - 1); };   // this thread's i-th window
   int bl[PER];
 #pragma unroll
   for (int i = 0; i < PER; i++) {
-    const int u = rev11(tid + i * NT);
+    const int u = rev11(win(i));
     int b = 1;
 #pragma unroll
     for (int j = 1; j < kMaxLen; j++) {
@@ -572,35 +581,37 @@ __device__ __attribute__((always_inline)) bool build_lut(const uint8_t *len, int
   uint32_t tv[PER];
 #pragma unroll
   for (int i = 0; i < PER; i++) {
-    const int u = rev11(tid + i * NT);
+    const int u = rev11(win(i));
     tv[i] = uint32_t(S.sorted[of[i] + (u >> (kMaxLen - bl[i])) - fo[i]]) | uint32_t(bl[i] << 8);
   }
 #pragma unroll
-  for (int i = 0; i < PER; i++) t1[tid + i * NT] = uint16_t(tv[i]);
+  for (int i = 0; i < PER; i++)
+    if (own) t1[win(i)] = uint16_t(tv[i]);
   __syncthreads();
-  // up to three whole code words per 11-bit window, without branches; the
-  // three lookups of the eight entries of a thread go in three passes
+  // up to three whole code words per window, without branches; the three
+  // lookups of the entries of a thread go in three passes
   auto t1at = [&](uint32_t w) { return uint32_t(t1[w]); };
   uint32_t e1[PER], e2[PER], e3[PER];
 #pragma unroll
-  for (int i = 0; i < PER; i++) e1[i] = t1at(uint32_t(tid + i * NT));
+  for (int i = 0; i < PER; i++) e1[i] = t1at(uint32_t(win(i)));
 #pragma unroll
-  for (int i = 0; i < PER; i++) e2[i] = t1at(uint32_t(tid + i * NT) >> (e1[i] >> 8));
+  for (int i = 0; i < PER; i++) e2[i] = t1at(uint32_t(win(i)) >> (e1[i] >> 8));
 #pragma unroll
-  for (int i = 0; i < PER; i++) e3[i] = t1at((uint32_t(tid + i * NT) >> (e1[i] >> 8)) >> (e2[i] >> 8));
+  for (int i = 0; i < PER; i++) e3[i] = t1at((uint32_t(win(i)) >> (e1[i] >> 8)) >> (e2[i] >> 8));
 #pragma unroll
   for (int i = 0; i < PER; i++) {
     const uint32_t l1 = e1[i] >> 8, l2 = e2[i] >> 8, l3 = e3[i] >> 8;
     // all-ones masks: the second (third) word fits in the window
-    const uint32_t m2 = uint32_t(int(l1 + l2 - kMaxLen - 1) >> 31);
-    const uint32_t m3 = m2 & uint32_t(int(l1 + l2 + l3 - kMaxLen - 1) >> 31);
+    const uint32_t m2 = uint32_t(int(l1 + l2 - WB - 1) >> 31);
+    const uint32_t m3 = m2 & uint32_t(int(l1 + l2 + l3 - WB - 1) >> 31);
     const uint32_t used = l1 + (l2 & m2) + (l3 & m3);
     const uint32_t n = 1 + (m2 & 1) + (m3 & 1);
     const uint32_t syms = (e1[i] & 0xFF) | (((e2[i] & 0xFF) << 8) & m2) | (((e3[i] & 0xFF) << 16) & m3);
     tv[i] = used | (n << 6) | (syms << 8);
   }
 #pragma unroll
-  for (int i = 0; i < PER; i++) lut[tid + i * NT] = tv[i];
+  for (int i = 0; i < PER; i++)
+    if (own) lut[win(i)] = tv[i];
   __syncthreads();
   return true;
 }

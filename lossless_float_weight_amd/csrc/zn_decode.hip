@@ -31,15 +31,26 @@ constexpr int RING = 32;       // words of a lane's payload window in LDS: two 6
 // LDS banks.  Staging is STB contiguous bytes per lane: each lookup stores
 // its symbols as single bytes at the lane's running position.
 
+// The second stream of FP8 (3-bit mantissas) and FP4 pairs (2-bit mantissa
+// pairs) has at most 8 symbols, so no code word is longer than 7 bits and a
+// 128-entry table decodes it: with one full table and this one, the LDS of a
+// workgroup fits three workgroups per CU.
+constexpr int kSmallBits = 7;
+
 template <int DT>
 struct DecShared {
   static constexpr int NC = ncoded(DT);
-  uint32_t lut[NC][kLutSize];
-  union {
+  static constexpr bool SMALL1 = NC == 2;          // stream 1 takes the small table
+  static constexpr int NL = SMALL1 ? 1 : NC;       // full tables
+  uint32_t lut[NL][kLutSize];
+  // 16-byte aligned: the merge reads staged bytes 8 at a time (an unaligned
+  // LDS access costs extra cycles)
+  alignas(16) union {
     uint16_t t1[kLutSize];
     uint8_t stage[DEC_NT * STB];
   } u;
-  uint32_t ring[RING * DEC_NT];
+  alignas(16) uint32_t ring[RING * DEC_NT];
+  uint32_t lutm[SMALL1 ? (1 << kSmallBits) : 1];
   uint8_t len[NC][256];
   LutShared ls;
   int mode[NC], aux[NC];
@@ -251,13 +262,20 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         sh.len[p][tid] = (x >> ((tid & 1) * 4)) & 15;
       }
       __syncthreads();
-      if (!build_lut<DEC_NT>(sh.len[p], A, sh.lut[p], sh.u.t1, sh.ls)) {
+      bool ok;
+      if constexpr (DecShared<DT>::SMALL1) {
+        ok = p == 1 ? build_lut<DEC_NT, kSmallBits>(sh.len[p], A, sh.lutm, sh.u.t1, sh.ls)
+                    : build_lut<DEC_NT>(sh.len[p], A, sh.lut[0], sh.u.t1, sh.ls);
+      } else {
+        ok = build_lut<DEC_NT>(sh.len[p], A, sh.lut[p], sh.u.t1, sh.ls);
+      }
+      if (!ok) {
         if (tid == 0) atomicOr(&a.ctl[0], kErrCorrupt);
         return;
       }
     } else if (mode == GROUP) {
       const uint32_t *gl = a.group_lut + size_t(sh.aux[p]) * kLutSize;
-      for (int i = tid; i < kLutSize; i += DEC_NT) sh.lut[p][i] = ldg4(gl + i);
+      for (int i = tid; i < kLutSize; i += DEC_NT) sh.lut[DecShared<DT>::SMALL1 ? 0 : p][i] = ldg4(gl + i);
       if (tid < A) sh.len[p][tid] = ldg1(a.group_len + sh.aux[p] * 256 + tid);
     }
   }
@@ -318,7 +336,11 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     const uint8_t *pay = in + sh.pay_off[p];
     const uint32_t paybytes = sh.pay[p];
     const uint32_t ngroups = (paybytes + 15) / 16;
-    const uint32_t *lut = sh.lut[p];
+    constexpr bool SMALL1 = DecShared<DT>::SMALL1;
+    const bool small = SMALL1 && p == 1;
+    const uint32_t *lut = small ? sh.lutm : sh.lut[SMALL1 ? 0 : p];
+    // byte offset of the entry of the window's next bits (W = window << 2)
+    const uint32_t wmask = small ? ((1u << kSmallBits) - 1) << 2 : uint32_t(kLutSize - 1) << 2;
     uint8_t *sb = sh.u.stage + tid * STB;   // this lane's staged symbols
     uint32_t *rp = sh.ring + tid;       // ring word w of this lane: rp[w * DEC_NT]
     const int t0 = wv * 64;             // first thread of this wave
@@ -355,8 +377,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
 
       // Bit reader: a window of nb bits (LSB-first) refilled one word at a
       // time from the lane's ring of payload words in LDS, kept shifted up
-      // by two (W = window << 2) so that W & 0x1FFC is the byte offset of
-      // the table entry of its next 11 bits.  The ring holds two 64-byte
+      // by two (W = window << 2) so that W & wmask is the byte offset of
+      // the table entry of its next 11 bits (7 for the small table).  The ring holds two 64-byte
       // sectors of the payload, aligned in memory so that every sector is
       // one HBM burst read once; a sector is loaded one round before it can
       // be needed.  Word positions count from the aligned base.
@@ -481,7 +503,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           const uint8_t *lutb = reinterpret_cast<const uint8_t *>(lut);
           uint32_t *const stw = reinterpret_cast<uint32_t *>(sh.u.stage);   // abase is a multiple of 8
           auto step = [&]() {
-            const uint32_t e = *reinterpret_cast<const uint32_t *>(lutb + (uint32_t(W) & 0x1FFCu));
+            const uint32_t e = *reinterpret_cast<const uint32_t *>(lutb + (uint32_t(W) & wmask));
             cur |= uint64_t(e >> 8) << ((a & 3) * 8);   // unused symbol bytes of an entry are zero
             stw[a >> 2] = uint32_t(cur);
             const uint32_t an = a + ((e >> 6) & 3);
