@@ -116,10 +116,14 @@ struct EncShared {
   static constexpr int NT = enc_nt(DT);
   static constexpr int NW = NT / 64;                              // waves = segments per pack tile
   static constexpr int COLS = DT == FP32 ? 16 : 32;
-  static constexpr int APRIV = DT == FP8 ? (16 + 8) : DT == FP4X2 ? (16 + 4) : 256 * NC;   // total bins
-  // BF16 counts two bins per word (a column sees at most 1/32 of a chunk,
-  // 16384 values at the largest chunk size, so 16 bits cannot overflow)
-  static constexpr bool PACK16 = DT == BF16;
+  // 1-byte elements count whole bytes (one bin of 256 per element) and take
+  // their two fields' histograms from that; the others count each field
+  static constexpr bool BYTEHIST = DT == FP8 || DT == FP4X2;
+  static constexpr int APRIV = BYTEHIST ? 256 : 256 * NC;   // total bins
+  // BF16 and 1-byte elements count two bins per word (a column sees at most
+  // 1/32 of a chunk, 32768 values at the largest chunk size, so 16 bits
+  // cannot overflow)
+  static constexpr bool PACK16 = DT == BF16 || BYTEHIST;
   static constexpr int PRIVW = PACK16 ? APRIV * COLS / 2 : APRIV * COLS;
   uint32_t hist[NC][256];
   uint32_t enc[NC][256];
@@ -143,7 +147,6 @@ struct EncShared {
 
 template <int DT>
 __device__ __forceinline__ int priv_base(int p) {
-  if constexpr (DT == FP8 || DT == FP4X2) return p == 0 ? 0 : 16;
   return p * 256;
 }
 
@@ -203,6 +206,9 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
 
   // ------------------------------------------- 1. split, raw planes, counts
   for (int i = tid; i < EncShared<DT>::PRIVW; i += ENC_NT) sh.u.priv[i] = 0;
+  if constexpr (EncShared<DT>::BYTEHIST) {   // the field histograms are summed into
+    for (int i = tid; i < NC * 256; i += ENC_NT) sh.hist[i >> 8][i & 255] = 0;
+  }
   __syncthreads();
   const int col = ln & (COLS - 1);
   constexpr int B1 = 4;  // 16-byte loads in flight per thread
@@ -221,8 +227,12 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
 #pragma unroll
       for (int i = 0; i < VE; i++) {
         const uint32_t w = vec_elem<DT>(q, i);
+        if constexpr (EncShared<DT>::BYTEHIST) {
+          count<DT>(sh, 0, w, col);
+        } else {
 #pragma unroll
-        for (int p = 0; p < NC; p++) count<DT>(sh, p, field_rt<DT>(w, p), col);
+          for (int p = 0; p < NC; p++) count<DT>(sh, p, field_rt<DT>(w, p), col);
+        }
       }
       if constexpr (DT == BF16) {
         uint32_t lo = 0, hi = 0;
@@ -251,8 +261,12 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
   }
   for (uint32_t i = nvec * VE + tid; i < n; i += ENC_NT) {  // ragged tail or unaligned input
     const uint32_t w = load_elem<DT>(src + uint64_t(i) * ES);
+    if constexpr (EncShared<DT>::BYTEHIST) {
+      count<DT>(sh, 0, w, col);
+    } else {
 #pragma unroll
-    for (int p = 0; p < NC; p++) count<DT>(sh, p, field_rt<DT>(w, p), col);
+      for (int p = 0; p < NC; p++) count<DT>(sh, p, field_rt<DT>(w, p), col);
+    }
     if constexpr (DT == BF16) stg1(rawp + e0 + i, ((w >> 8) & 0x80) | (w & 0x7F));
   }
   if constexpr (DT == FP8) {  // sign bits of the tail, whole bytes by one thread
@@ -287,10 +301,13 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
     } else {
       for (int j = 0; j < COLS; j++) s += sh.u.priv[i * COLS + ((j + i) & (COLS - 1))];
     }
-    int p = 0, sym = i;
-    if constexpr (DT == FP8 || DT == FP4X2) { p = i >= 16; sym = i - (p ? 16 : 0); }
-    else { p = i >> 8; sym = i & 255; }
-    sh.hist[p][sym] = s;
+    if constexpr (EncShared<DT>::BYTEHIST) {
+      // byte i's count goes to its value of each field
+      atomicAdd(&sh.hist[0][field_rt<DT>(uint32_t(i), 0)], s);
+      atomicAdd(&sh.hist[1][field_rt<DT>(uint32_t(i), 1)], s);
+    } else {
+      sh.hist[i >> 8][i & 255] = s;
+    }
   }
   __syncthreads();
 
