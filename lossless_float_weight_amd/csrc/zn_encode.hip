@@ -105,6 +105,10 @@ struct PackShared {
   uint32_t enc[NC][256];
   uint32_t stage[2][STAGE];      // alternate tiles use alternate buffers
   uint32_t wtot[2][PACK_NW];
+  // 1-byte elements: one tile's words of a raw stream (32 strips per segment,
+  // up to 4 words per strip), written from the coded stream's tiles
+  static constexpr bool RSTAGE = DT == FP8 || DT == FP4X2;
+  uint32_t rawt[RSTAGE ? 32 * PACK_NW * G * 4 : 1];
   unsigned long long bits[NC], sec_off[NC];
   int mode[NC], aux[NC];
 };
@@ -473,7 +477,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
                                            const int *paux, const unsigned long long *pbits,
                                            const unsigned long long *psec,
                                            uint32_t (*stage_all)[PackShared<DT>::STAGE],
-                                           uint32_t (*wtot)[PACK_NW]) {
+                                           uint32_t (*wtot)[PACK_NW], uint32_t *rawt) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
@@ -498,10 +502,15 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   // last element are zero.  For FP32, whose raw streams take whole words in a
   // lane's run of EPT elements (EPT*k = 32), they are written from the tiles
   // of the first coded stream, which read every element anyway: the input is
-  // read once.  Otherwise (and when no stream is coded) they take one pass of
-  // their own here, in element order: for 1-byte elements the short stores
-  // scattered over the tiles cost more than reading the chunk again.
-  uint32_t rawmask = 0, tilemask = 0;
+  // read once.  For 1-byte elements in chunks of whole segments with the
+  // exponent coded and the mantissa raw, the exponent's tiles put each strip's
+  // mantissa words in LDS and the tile's words go out as rows of 16-byte
+  // stores (one row per strip row of the tile's segments).
+  // Otherwise (and when no stream is coded) they take one pass of their own
+  // here, in element order.
+  constexpr bool RSTAGE = PackShared<DT>::RSTAGE;
+  constexpr int NWG = NW * G;            // segments per tile
+  uint32_t rawmask = 0, tilemask = 0, lmask = 0;
   int firstcoded = -1;
   uint8_t *pwr[NC];
 #pragma unroll
@@ -515,7 +524,9 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
 #pragma unroll
     for (int p = 0; p < NC; p++)
       if (DT == FP32 && ((rawmask >> p) & 1) && (EPT * kbits(DT, p)) % 32 == 0) tilemask |= 1u << p;
+    if (RSTAGE && n % S == 0 && firstcoded == 0 && rawmask == 2u) lmask = 2u;
   }
+  static_assert(!RSTAGE || (EPT == 16 && G == 1), "a lane's run is half a strip; one segment per wave");
   // The pass: a lane takes LE consecutive elements per step, LE*k a multiple
   // of 32 for every field width of the dtype, so it writes whole words of
   // every raw stream with no scan; the next step's elements are loaded while
@@ -523,7 +534,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   {
     constexpr int LE = DT == FP8 || DT == FP4X2 ? 32 : VE;   // FP8: k = 3 needs 32 elements per 3 words
     constexpr int NQ = LE / VE;                  // 16-byte loads per lane per step
-    const uint32_t passmask = rawmask & ~tilemask;
+    const uint32_t passmask = rawmask & ~tilemask & ~lmask;
     uint8_t *const *pw = pwr;
     if (passmask) {
       u32x4 nx[NQ];
@@ -682,6 +693,18 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
               if (x * 32 < EPT * kq && lim > 0 && w0 + x < nwq) stg4(pwr[q] + 4ull * (w0 + x), uint32_t(bq >> (32 * x)));
           }
         }
+        if (RSTAGE && p == 0 && lmask && lim > 0) {
+          // strip ln/2 of this segment, half ln&1: 16 mantissas, 16*KM bits,
+          // at 16-bit word KM*(ln&1) of the strip's KM words; every strip is full
+          constexpr int KM = kbits(DT, 1);
+          uint16_t *rt = reinterpret_cast<uint16_t *>(rawt);
+          uint64_t bq = 0;
+#pragma unroll
+          for (int e = 0; e < EPT; e++) bq |= uint64_t(field_rt<DT>(w[e], 1)) << (e * KM);
+          const int at = ((ln >> 1) * NWG + wv * G + g) * 2 * KM + (ln & 1) * KM;
+#pragma unroll
+          for (int x = 0; x < KM; x++) rt[at + x] = uint16_t(bq >> (16 * x));
+        }
 #pragma unroll
         for (int g8 = 0; g8 < NG; g8++) {
           uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -735,6 +758,30 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         const uint32_t x = wtot[buf][q];
         woff += q < wv ? x : 0;
         ttot += x;
+      }
+      if (RSTAGE && p == 0 && lmask) {
+        // the tile's mantissa words: strip row r holds kq words of each of the
+        // tile's segments, at word kq*(r*nseg + T*NWG) of the stream
+        {
+          constexpr int q = 1, kq = kbits(DT, 1);
+          const int segs = nseg - T * NWG < NWG ? nseg - T * NWG : NWG;   // segments in this tile
+          const uint32_t rw = uint32_t(segs) * kq;                        // words per row
+          uint32_t *const dst = reinterpret_cast<uint32_t *>(pwr[q]) + uint32_t(kq * NWG) * uint32_t(T);
+          if (segs == NWG && (nseg * kq) % 4 == 0 && (reinterpret_cast<uintptr_t>(pwr[q]) & 15) == 0) {
+            // NWG*kq words per row, a multiple of 4, 16-byte aligned
+            const int per = NWG * kq / 4;
+            for (int i = tid; i < 32 * per; i += ENC_NT) {
+              const int r = i / per, v = i % per;
+              const uint32_t *sv = rawt + r * NWG * kq + 4 * v;
+              stg16(dst + uint64_t(kq) * uint32_t(r) * uint32_t(nseg) + 4 * v, u32x4{sv[0], sv[1], sv[2], sv[3]});
+            }
+          } else {
+            for (uint32_t i = tid; i < 32 * rw; i += ENC_NT) {
+              const uint32_t r = i / rw, v = i % rw;
+              stg4(dst + uint64_t(kq) * r * uint32_t(nseg) + v, rawt[r * NWG * kq + v]);
+            }
+          }
+        }
       }
       uint32_t base = uint32_t(tbit & 31) + woff;
 #pragma unroll
@@ -810,7 +857,7 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   }
   const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
   pack_chunk<DT>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off, sh.stage,
-                 sh.wtot);
+                 sh.wtot, sh.rawt);
 }
 
 // One workgroup: exclusive scan of the record sizes into the directory, then

@@ -141,6 +141,23 @@ def test_fp8_ragged_every_pattern(oracle, n):
     _check_equal(oracle, oracle.FP8_E4M3, [x.cuda()], 4096)
 
 
+@pytest.mark.parametrize("dt", ["fp8", "fp4"])
+def test_1byte_mantissa_raw_whole_segments(oracle, dt):
+    # chunks of whole 1024-element segments, exponent coded and mantissa raw:
+    # the mantissa words are written from the exponent's tiles, as 16-byte
+    # rows (segment count a multiple of 4) or word by word (the rest)
+    print(f"case: {dt} whole segments, mantissa raw", flush=True)
+    odt = oracle.FP8_E4M3 if dt == "fp8" else oracle.FP4X2_E2M1
+    seen = set()
+    for k in (1, 3, 5, 6, 259):
+        x = (W.fp8_blockscaled(1024 * k, device="cuda")[0][1] if dt == "fp8"
+             else W.fp4_blockscaled(1024 * k, device="cuda")[0][1])
+        for cb in (4096, 262144):
+            _, blob = _check_equal(oracle, odt, [x], cb)
+            seen |= set(field_modes(blob.cpu().numpy(), 2, [4, 3] if dt == "fp8" else [4, 2]))
+    assert (2, 0) in seen, seen
+
+
 # ------------------------------------------------------------- FP4 pairs ----
 def _fp4_bytes(lo, hi):
     return (lo.to(torch.int64) | (hi.to(torch.int64) << 4)).to(torch.uint8)
