@@ -96,6 +96,19 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 // per tile holds fewer workgroups per CU than the chunks need).
 constexpr int pack_g(int dt) { return segsyms(dt) / 64 >= 16 ? 1 : 16 / (segsyms(dt) / 64); }
 
+// The mantissa fields of a word's four 1-byte elements, element 0 in the low
+// bits (FP8: 3 bits each; FP4 pairs: the byte's two mantissa bits, low nibble's first).
+template <int DT>
+__device__ __forceinline__ uint32_t mant4(uint32_t x) {
+  if constexpr (DT == FP8) {
+    const uint32_t m = x & 0x07070707u, t = m | (m >> 5);
+    return (t & 0x3Fu) | ((t >> 10) & 0xFC0u);
+  } else {
+    const uint32_t m = (x & 0x01010101u) | ((x >> 3) & 0x02020202u), t = m | (m >> 6);
+    return (t & 0xFu) | ((t >> 12) & 0xF0u);
+  }
+}
+
 template <int DT>
 struct PackShared {
   static constexpr int NC = ncoded(DT);
@@ -693,17 +706,29 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
               if (x * 32 < EPT * kq && lim > 0 && w0 + x < nwq) stg4(pwr[q] + 4ull * (w0 + x), uint32_t(bq >> (32 * x)));
           }
         }
-        if (RSTAGE && p == 0 && lmask && lim > 0) {
+        if constexpr (RSTAGE) if (p == 0 && lmask && lim > 0) {
           // strip ln/2 of this segment, half ln&1: 16 mantissas, 16*KM bits,
           // at 16-bit word KM*(ln&1) of the strip's KM words; every strip is full
           constexpr int KM = kbits(DT, 1);
-          uint16_t *rt = reinterpret_cast<uint16_t *>(rawt);
+          static_assert(KM == 2 || KM == 3, "mantissa widths of the 1-byte types");
           uint64_t bq = 0;
 #pragma unroll
-          for (int e = 0; e < EPT; e++) bq |= uint64_t(field_rt<DT>(w[e], 1)) << (e * KM);
-          const int at = ((ln >> 1) * NWG + wv * G + g) * 2 * KM + (ln & 1) * KM;
-#pragma unroll
-          for (int x = 0; x < KM; x++) rt[at + x] = uint16_t(bq >> (16 * x));
+          for (int j = 0; j < 4; j++) {
+            const uint32_t x = vec ? nq[g][0][j]
+                                   : w[4 * j] | (w[4 * j + 1] << 8) | (w[4 * j + 2] << 16) | (w[4 * j + 3] << 24);
+            bq |= uint64_t(mant4<DT>(x)) << (4 * KM * j);
+          }
+          const int at = ((ln >> 1) * NWG + wv * G + g) * 2 * KM + (ln & 1) * KM;   // 16-bit words
+          uint16_t *rt = reinterpret_cast<uint16_t *>(rawt);
+          if constexpr (KM == 2) {
+            rawt[at >> 1] = uint32_t(bq);
+          } else if (ln & 1) {   // odd half: a 16-bit word, then an aligned 32-bit one
+            rt[at] = uint16_t(bq);
+            rawt[(at + 1) >> 1] = uint32_t(bq >> 16);
+          } else {
+            rawt[at >> 1] = uint32_t(bq);
+            rt[at + 2] = uint16_t(bq >> 32);
+          }
         }
 #pragma unroll
         for (int g8 = 0; g8 < NG; g8++) {
@@ -759,6 +784,27 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         woff += q < wv ? x : 0;
         ttot += x;
       }
+      uint32_t base = uint32_t(tbit & 31) + woff;
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        const int J = (T * NW + wv) * G + g;
+        if (with_segs && ln == 0 && J < nseg) stg2(segt + J, segtot[g]);
+        uint32_t start = base + incl[g] - nb[g];
+#pragma unroll
+        for (int g8 = 0; g8 < NG; g8++) {
+          // the 88-bit group shifted to its bit offset covers at most 4 words;
+          // ORing zero words is harmless, so no lane branches
+          const uint32_t sft = start & 31, wi = start >> 5;
+          const uint64_t t0 = glo[g][g8] << sft;
+          const uint64_t t1 = (uint64_t(ghi[g][g8]) << sft) | (sft ? glo[g][g8] >> (64 - sft) : 0ull);
+          atomicOr(&stage[wi], uint32_t(t0));
+          atomicOr(&stage[wi + 1], uint32_t(t0 >> 32));
+          atomicOr(&stage[wi + 2], uint32_t(t1));
+          atomicOr(&stage[wi + 3], uint32_t(t1 >> 32));
+          start += gb[g][g8];
+        }
+        base += segtot[g];
+      }
       if (RSTAGE && p == 0 && lmask) {
         // the tile's mantissa words: strip row r holds kq words of each of the
         // tile's segments, at word kq*(r*nseg + T*NWG) of the stream
@@ -782,27 +828,6 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
             }
           }
         }
-      }
-      uint32_t base = uint32_t(tbit & 31) + woff;
-#pragma unroll
-      for (int g = 0; g < G; g++) {
-        const int J = (T * NW + wv) * G + g;
-        if (with_segs && ln == 0 && J < nseg) stg2(segt + J, segtot[g]);
-        uint32_t start = base + incl[g] - nb[g];
-#pragma unroll
-        for (int g8 = 0; g8 < NG; g8++) {
-          // the 88-bit group shifted to its bit offset covers at most 4 words;
-          // ORing zero words is harmless, so no lane branches
-          const uint32_t sft = start & 31, wi = start >> 5;
-          const uint64_t t0 = glo[g][g8] << sft;
-          const uint64_t t1 = (uint64_t(ghi[g][g8]) << sft) | (sft ? glo[g][g8] >> (64 - sft) : 0ull);
-          atomicOr(&stage[wi], uint32_t(t0));
-          atomicOr(&stage[wi + 1], uint32_t(t0 >> 32));
-          atomicOr(&stage[wi + 2], uint32_t(t1));
-          atomicOr(&stage[wi + 3], uint32_t(t1 >> 32));
-          start += gb[g][g8];
-        }
-        base += segtot[g];
       }
       __syncthreads();
       // store the whole words and clear them for the tile after next; the
