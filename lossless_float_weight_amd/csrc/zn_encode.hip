@@ -93,8 +93,10 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 }
 
 // Segments per wave in one pack tile: 16 symbols per lane per tile (more
-// per tile holds fewer workgroups per CU than the chunks need).
-constexpr int pack_g(int dt) { return segsyms(dt) / 64 >= 16 ? 1 : 16 / (segsyms(dt) / 64); }
+// per tile holds fewer workgroups per CU than the chunks need); FP32, whose
+// tiles also carry three raw streams, takes 8 (80 VGPRs: 6 workgroups per CU
+// instead of 4 at 16).
+constexpr int pack_g(int dt) { return dt == FP32 ? 2 : segsyms(dt) / 64 >= 16 ? 1 : 16 / (segsyms(dt) / 64); }
 
 // The mantissa fields of a word's four 1-byte elements, element 0 in the low
 // bits (FP8: 3 bits each; FP4 pairs: the byte's two mantissa bits, low nibble's first).
