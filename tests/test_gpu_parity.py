@@ -150,11 +150,13 @@ def test_1byte_mantissa_raw_whole_segments(oracle, dt):
     odt = oracle.FP8_E4M3 if dt == "fp8" else oracle.FP4X2_E2M1
     seen = set()
     for k in (1, 3, 5, 6, 259):
-        x = (W.fp8_blockscaled(1024 * k, device="cuda")[0][1] if dt == "fp8"
-             else W.fp4_blockscaled(1024 * k, device="cuda")[0][1])
-        for cb in (4096, 262144):
-            _, blob = _check_equal(oracle, odt, [x], cb)
-            seen |= set(field_modes(blob.cpu().numpy(), 2, [4, 3] if dt == "fp8" else [4, 2]))
+        x = (W.fp8_blockscaled(1024 * k + 1, device="cuda")[0][1] if dt == "fp8"
+             else W.fp4_blockscaled(1024 * k + 1, device="cuda")[0][1])
+        # aligned, and one byte off 16-byte alignment (the tiles then load bytes)
+        for t in (x[: 1024 * k], x[1:]):
+            for cb in (4096, 262144):
+                _, blob = _check_equal(oracle, odt, [t], cb)
+                seen |= set(field_modes(blob.cpu().numpy(), 2, [4, 3] if dt == "fp8" else [4, 2]))
     assert (2, 0) in seen, seen
 
 
