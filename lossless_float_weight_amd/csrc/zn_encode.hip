@@ -139,10 +139,12 @@ struct EncShared {
   // their two fields' histograms from that; the others count each field
   static constexpr bool BYTEHIST = DT == FP8 || DT == FP4X2;
   static constexpr int APRIV = BYTEHIST ? 256 : 256 * NC;   // total bins
-  // BF16 and 1-byte elements count two bins per word (a column sees at most
-  // 1/32 of a chunk, 32768 values at the largest chunk size, so 16 bits
-  // cannot overflow)
-  static constexpr bool PACK16 = DT == BF16 || BYTEHIST;
+  // BF16 counts two bins per word (a column sees at most 1/32 of a chunk,
+  // 16384 values at the largest chunk size, so 16 bits cannot overflow), to
+  // keep every chunk of a block resident at once; the others count one bin
+  // per word (for 1-byte elements the bin's address is then two instructions
+  // from the byte, and the histogram 32 KB)
+  static constexpr bool PACK16 = DT == BF16;
   static constexpr int PRIVW = PACK16 ? APRIV * COLS / 2 : APRIV * COLS;
   uint32_t hist[NC][256];
   uint32_t enc[NC][256];
