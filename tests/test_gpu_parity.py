@@ -160,6 +160,22 @@ def test_1byte_mantissa_raw_whole_segments(oracle, dt):
     assert (2, 0) in seen, seen
 
 
+@pytest.mark.parametrize("cb", [1 << 20, 12288])
+def test_largest_and_odd_chunk_sizes(oracle, cb):
+    # the largest chunk (1 MiB: 1024 BF16 segments, 16-bit histogram bins at
+    # their limit) and a chunk of three 4 KiB pages, every dtype, 2.5 chunks
+    print(f"case: every dtype at {cb}-byte chunks", flush=True)
+    nb = cb * 5 // 2
+    cases = [
+        (oracle.BF16, [t for _, t in W.single_bf16(nb // 2, device="cuda")]),
+        (oracle.FP32, [t for _, t in W.fp32_pair(nb // 4, device="cuda")]),
+        (oracle.FP8_E4M3, [W.fp8_blockscaled(nb, device="cuda")[0][1]]),
+        (oracle.FP4X2_E2M1, [W.fp4_blockscaled(nb, device="cuda")[0][1]]),
+    ]
+    for odt, tensors in cases:
+        _check_equal(oracle, odt, tensors, cb)
+
+
 # ------------------------------------------------------------- FP4 pairs ----
 def _fp4_bytes(lo, hi):
     return (lo.to(torch.int64) | (hi.to(torch.int64) << 4)).to(torch.uint8)
