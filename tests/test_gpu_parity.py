@@ -160,6 +160,18 @@ def test_1byte_mantissa_raw_whole_segments(oracle, dt):
     assert (2, 0) in seen, seen
 
 
+def test_empty_tensors(oracle):
+    # zero-element tensors among others, and a container of one empty tensor
+    # (no chunks: the chunk kernels are not launched)
+    print("case: empty tensors", flush=True)
+    x = W.single_bf16(1000, device="cuda")[0][1]
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    _check_equal(oracle, oracle.BF16, [e, x, e], 4096)
+    _check_equal(oracle, oracle.BF16, [e], 4096)
+    f = torch.empty(0, dtype=torch.float8_e4m3fn, device="cuda")
+    _check_equal(oracle, oracle.FP8_E4M3, [f, W.fp8_blockscaled(3000, device="cuda")[0][1]], 4096)
+
+
 @pytest.mark.parametrize("cb", [1 << 20, 12288])
 def test_largest_and_odd_chunk_sizes(oracle, cb):
     # the largest chunk (1 MiB: 1024 BF16 segments, 16-bit histogram bins at
