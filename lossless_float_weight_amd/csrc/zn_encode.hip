@@ -16,9 +16,11 @@
 //   k_finish (one workgroup) scans the record sizes into the directory and
 //   writes the header and the alignment gaps.
 //   k_pack (one workgroup of 4 wave64s per chunk) writes the chunk's record
-//   at its directory offset: stream heads, then the payload packed one wave
-//   per segment -- a wave scan of bit counts, code words ORed into an LDS
-//   tile, whole words stored coalesced.
+//   at its directory offset: stream heads, then each coded payload in tiles
+//   of whole segments (one or two per wave) -- a wave scan of bit counts, code
+//   words ORed into an LDS tile, whole words stored coalesced -- and the raw
+//   streams, from those tiles where their words allow, else in a pass of
+//   their own.
 // No chunk ever waits for another, and no record is copied after packing.
 #include "zn_internal.h"
 
