@@ -52,3 +52,21 @@ def test_kernel_event_names_need_no_gpu():
         assert lib.zn_debug_kernel_events(name, None, None) == 0
     assert lib.zn_debug_kernel_events(b"encode", None, None) == -1
     assert lib.zn_debug_kernel_events(None, None, None) == -1
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libzn.so not built")
+def test_bad_tableset_bytes_and_null_plans_need_no_gpu():
+    # a saved plan is parsed and checked before any device memory is taken
+    lib = ctypes.CDLL(LIB)
+    out = ctypes.c_void_p()
+    assert lib.zn_tableset_load(None, 0, ctypes.byref(out)) == -1 and out.value is None
+    rng = __import__("random").Random(1)
+    for buf in (bytes(64), bytes(rng.randrange(256) for _ in range(4096))):
+        b = ctypes.create_string_buffer(buf, len(buf))
+        assert lib.zn_tableset_load(b, len(buf), ctypes.byref(out)) == -2     # corrupt
+        assert out.value is None
+    v = ctypes.c_uint64()
+    assert lib.zn_compress_bound(None, ctypes.byref(v)) == -1
+    assert lib.zn_scratch_bytes(None, ctypes.byref(v)) == -1
+    assert lib.zn_tableset_info(None, None, None, None, None, None, None, None) == -1
+    assert lib.zn_decompress(None, None, 0, None, None, 0, 1, None) == -1
