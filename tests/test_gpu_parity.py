@@ -298,6 +298,28 @@ def test_setup_equals_oracle_and_reuses(oracle):
     assert_roundtrip(ts2, blob, pert)
 
 
+@pytest.mark.parametrize("dt", ["fp32", "fp8", "fp4"])
+def test_setup_other_dtypes_equals_oracle(oracle, dt):
+    # grouped setup (K = 4) on the exponent stream of the other dtypes: map,
+    # group lengths, hash, saved bytes, cost history and containers
+    print(f"case: grouped setup K=4, {dt}", flush=True)
+    if dt == "fp32":
+        odt, tensors = oracle.FP32, [t for _, t in W.fp32_pair(1 << 18, device="cuda")]
+    elif dt == "fp8":
+        odt, tensors = oracle.FP8_E4M3, [W.fp8_blockscaled(1 << 20, device="cuda")[0][1]]
+    else:
+        odt, tensors = oracle.FP4X2_E2M1, [W.fp4_blockscaled(1 << 20, device="cuda")[0][1]]
+    arrs = [to_np(t) for t in tensors]
+    ts = zn.setup(tensors, chunk_bytes=65536, n_groups=4)
+    ots = oracle.setup(odt, arrs, 65536, 4)
+    assert ts.group_map() == ots.group_map().tolist()
+    for g in range(4):
+        assert ts.lengths(g) == ots.lengths(g).tolist()
+    assert ts.hash == ots.hash and ts.save() == ots.save()
+    assert ts.cost_history() == [int(v) for v in ots.cost_history()]
+    _check_equal(oracle, odt, tensors, 65536, ts, ots)
+
+
 def test_transfer_equals_oracle(oracle):
     print("case: grouped setup K=8 on a scaled model, transferred to another architecture", flush=True)
     tensors = _small_model()
