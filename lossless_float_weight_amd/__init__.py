@@ -5,5 +5,5 @@ The GPU path is libzn.so (HIP kernels for gfx950, C ABI in include/zn.h);
 """
 from . import workloads  # noqa: F401
 from . import zn  # noqa: F401
-from .zn import (BF16, FP32, FP8_E4M3, Tableset, ZnError, compress, compress_bound,  # noqa: F401
-                 decompress, plan_from_container, scratch_bytes, setup)
+from .zn import (BF16, FP32, FP8_E4M3, FP4X2_E2M1, Tableset, ZnError, compress,  # noqa: F401
+                 compress_bound, decompress, plan_from_container, scratch_bytes, setup, setup_transfer)
