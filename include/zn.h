@@ -100,10 +100,30 @@ zn_status zn_setup_transfer(const zn_tableset *src, const void *const *d_tensors
                             const uint64_t *n_elems, int n_tensors, hipStream_t stream,
                             zn_tableset **out);
 
+/* zn_header_info -- the facts a container's 64-byte header records, read
+ * from host memory (h_hdr, hdr_bytes >= 64; nothing past byte 64 is read):
+ * dtype, tensor count, total element count, chunk size, chunk count, total
+ * container bytes and the tableset hash (0 unless the container was made with
+ * group tables).  Host-only: no HIP call, usable without a GPU.  A decoder
+ * learns from it which plan and tableset it needs before any device work
+ * ("NeuralZip: Reusable Setup for Fast Lossless Compression", Abstract: the
+ * representations chosen by the setup are what later encodings use, so a
+ * container must name the setup it depends on).  ZN_ERR_ARG for a null or
+ * short buffer; ZN_ERR_CORRUPT when the magic, version, dtype, flags, chunk
+ * size, segment size, code-length limit, coded-stream count or tensor count
+ * is not one this library writes, or the hash is set without the group flag.
+ * Any output pointer may be NULL. */
+zn_status zn_header_info(const void *h_hdr, uint64_t hdr_bytes, zn_dtype *dtype, int *n_tensors,
+                         uint64_t *n_elems, uint32_t *chunk_bytes, uint32_t *n_chunks,
+                         uint64_t *total_bytes, uint64_t *ts_hash);
+
 /* zn_plan_from_container -- a plan (without groups) that matches the layout
- * of an existing container; reads its header and tensor table with one
- * synchronous copy.  Containers that use group tables need the tableset they
- * were compressed with (ZN_ERR_TABLESET here). */
+ * of an existing container; reads its header and tensor table with two
+ * synchronous copies and checks that the header's layout fields (element
+ * total, chunk count, directory, record and raw-plane offsets) are the ones
+ * that plan gives (ZN_ERR_CORRUPT otherwise).  Containers that use group
+ * tables need the tableset they were compressed with (ZN_ERR_TABLESET here).
+ * ZN_ERR_ARG for null pointers or in_bytes < 64. */
 zn_status zn_plan_from_container(const void *d_in, uint64_t in_bytes, hipStream_t stream,
                                  zn_tableset **out);
 
@@ -122,7 +142,13 @@ zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes);
  * Decompression alone needs only the first 256 bytes. */
 zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes);
 
-/* zn_compress -- one container holding every tensor of the plan.
+/* zn_compress -- one container holding every tensor of the plan.  Per chunk
+ * and coded field: the order-0 histogram, an optimal prefix code of the field
+ * (THEORY-599, nucleation note on ZipNN, "What was actually shown": the
+ * exponent is extracted and Huffman-coded order-0 while sign and fraction
+ * bytes stay as they are, ZipNN Table II and section III-A b), or the group's
+ * shared code chosen by the setup ("NeuralZip: Reusable Setup for Fast
+ * Lossless Compression", Abstract), then the packed bits.
  *   d_in_ptrs: DEVICE array of n_tensors device pointers to the tensors.
  *   d_out / out_cap: output buffer; out_cap >= zn_compress_bound() always fits.
  *   out_bytes: host; if non-NULL the call synchronises the stream and returns
@@ -136,7 +162,11 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
                       uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
                       uint64_t scratch_bytes, hipStream_t stream);
 
-/* zn_decompress -- exact reconstruction of every tensor of the container.
+/* zn_decompress -- exact reconstruction of every tensor of the container
+ * (bit-to-bit: "NeuralZip: Reusable Setup for Fast Lossless Compression",
+ * Abstract; lossless: "Lossless Compression of Neural Network Components ...
+ * in Low-Precision Formats", Abstract): chunks and their segments decode in
+ * parallel and the coded fields are merged back with the stored bits.
  *   d_out_ptrs: DEVICE array of n_tensors device pointers, each large enough
  *     for its tensor.
  *   sync != 0: synchronises and returns ZN_ERR_CORRUPT if any check failed.

@@ -371,6 +371,25 @@ zn_status zn_setup_transfer(const zn_tableset *src, const void *const *d_tensors
   return ZN_OK;
 }
 
+zn_status zn_header_info(const void *h_hdr, uint64_t hdr_bytes, zn_dtype *dtype, int *n_tensors,
+                         uint64_t *n_elems, uint32_t *chunk_bytes, uint32_t *n_chunks,
+                         uint64_t *total_bytes, uint64_t *ts_hash) {
+  const uint8_t *h = static_cast<const uint8_t *>(h_hdr);
+  if (!h || hdr_bytes < 64) return ZN_ERR_ARG;
+  if (get_u32(h) != kMagic || get_u16(h + 4) != kVersion || !valid_dtype(h[6]) || h[7] > 1 ||
+      h[30] != kMaxLen || h[31] != ncoded(h[6]) || get_u16(h + 28) != uint32_t(segsyms(h[6])) ||
+      !valid_chunk(get_u32(h + 12)) || get_u32(h + 8) < 1 || (h[7] == 0 && get_u64(h + 32) != 0))
+    return ZN_ERR_CORRUPT;
+  if (dtype) *dtype = zn_dtype(h[6]);
+  if (n_tensors) *n_tensors = int(get_u32(h + 8));
+  if (n_elems) *n_elems = get_u64(h + 16);
+  if (chunk_bytes) *chunk_bytes = get_u32(h + 12);
+  if (n_chunks) *n_chunks = get_u32(h + 24);
+  if (total_bytes) *total_bytes = get_u64(h + 56);
+  if (ts_hash) *ts_hash = get_u64(h + 32);
+  return ZN_OK;
+}
+
 zn_status zn_plan_from_container(const void *d_in, uint64_t in_bytes, hipStream_t stream,
                                  zn_tableset **out) {
   if (!d_in || !out || in_bytes < 64) return ZN_ERR_ARG;
@@ -378,12 +397,11 @@ zn_status zn_plan_from_container(const void *d_in, uint64_t in_bytes, hipStream_
   uint8_t h[64];
   HIPCHK(hipMemcpyAsync(h, d_in, 64, hipMemcpyDeviceToHost, stream));
   HIPCHK(hipStreamSynchronize(stream));
-  if (get_u32(h) != kMagic || get_u16(h + 4) != kVersion || !valid_dtype(h[6]) || h[7] > 1 ||
-      h[30] != kMaxLen || h[31] != ncoded(h[6]) || get_u16(h + 28) != uint32_t(segsyms(h[6])))
+  if (zn_header_info(h, 64, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) != ZN_OK)
     return ZN_ERR_CORRUPT;
   if (h[7] & 1) return ZN_ERR_TABLESET;
   const uint32_t T = get_u32(h + 8);
-  if (T < 1 || 64 + 16ull * T > in_bytes) return ZN_ERR_CORRUPT;
+  if (64 + 16ull * T > in_bytes) return ZN_ERR_CORRUPT;
   std::vector<uint8_t> tt(16ull * T);
   HIPCHK(hipMemcpyAsync(tt.data(), static_cast<const uint8_t *>(d_in) + 64, tt.size(),
                         hipMemcpyDeviceToHost, stream));
@@ -394,6 +412,14 @@ zn_status zn_plan_from_container(const void *d_in, uint64_t in_bytes, hipStream_
   if (!ts) return ZN_ERR_NOMEM;
   zn_status st = make_plan(ts, h[6], n.data(), int(T), get_u32(h + 12));
   if (st == ZN_ERR_ARG) st = ZN_ERR_CORRUPT;
+  // the header's layout fields must be the ones this plan gives
+  uint64_t ntot = 0;
+  for (uint32_t t = 0; t < T; t++) ntot += n[t];
+  if (st == ZN_OK && (get_u64(h + 16) != ntot || get_u32(h + 24) != ts->n_chunks || get_u64(h + 40) != ts->off_dir ||
+                      get_u64(h + 48) != ts->off_records))
+    st = ZN_ERR_CORRUPT;
+  for (uint32_t t = 0; st == ZN_OK && t < T; t++)
+    if (get_u64(tt.data() + 16 * t + 8) != ts->raw[t]) st = ZN_ERR_CORRUPT;
   if (st == ZN_OK) st = finish_plan(ts);
   if (st != ZN_OK) {
     zn_tableset_free(ts);
@@ -565,8 +591,10 @@ zn_status zn_tableset_load(const void *h_buf, uint64_t len, zn_tableset **out) {
         if ((*q & 15) > kMaxLen || (*q >> 4) > kMaxLen) st = ZN_ERR_CORRUPT;
       }
     if (M) memcpy(ts->map.data(), q, M);
+    // a plan without groups stores its map as zero bytes; with groups each
+    // byte names one of the K groups
     for (uint32_t c = 0; c < M && st == ZN_OK; c++)
-      if (ts->map[c] >= K) st = ZN_ERR_CORRUPT;
+      if (K ? ts->map[c] >= K : ts->map[c] != 0) st = ZN_ERR_CORRUPT;
   }
   if (st == ZN_ERR_ARG) st = ZN_ERR_CORRUPT;
   if (st == ZN_OK) st = finish_plan(ts);

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   // the error word and the chunk's directory entries in one round trip (the
   // directory lies below the records, which the host checked the input holds)
   const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.in + a.L.off_dir);
-  const uint32_t ctl0 = a.ctl[0];
+  const uint32_t ctl0 = a.ctl[0], grouped = a.ctl[1];
   const uint64_t r0 = dir[c], r1 = dir[c + 1];
   if (ctl0) return;  // the header check failed
 
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
 
   // ------------------------------------------------- 1. walk the record
   if (tid == 0) {
-    int bad = 0;
+    int bad = 0, tsbad = 0;
     if (r0 < a.L.off_records || r1 < r0 || r1 + 16 > a.in_bytes || (r0 & 15)) bad = 1;
     uint64_t pos = r0;
     for (int p = 0; p < NC && !bad; p++) {
@@ -204,7 +204,13 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       if (mode == CONST && (aux >= A || pay != 0)) bad = 1;
       if (mode == RAW && (aux != 0 || pay != (uint64_t(n) * k + 7) / 8)) bad = 1;
       if (mode == HUFF && (aux != 0 || pay == 0 || (pay & 3))) bad = 1;
-      if (mode == GROUP && (p != 0 || aux >= a.K || pay == 0 || (pay & 3))) bad = 1;
+      // a group code only for the first stream of a container made with
+      // groups; a group id the tableset lacks is a tableset mismatch, and an
+      // empty group (its decode table is all zero) has no code at all
+      if (mode == GROUP && (p != 0 || !grouped || pay == 0 || (pay & 3))) bad = 1;
+      if (mode == GROUP && !bad && aux >= a.K) tsbad = 1;
+      if (mode == GROUP && !bad && !tsbad && ldg4(a.group_lut + size_t(aux) * kLutSize) == 0) bad = 1;
+      if (tsbad) break;
       sh.mode[p] = mode;
       sh.aux[p] = aux;
       sh.pay[p] = pay;
@@ -212,12 +218,12 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       sh.seg_off[p] = pos + 8 + (mode == HUFF ? A / 2 : 0);
       pos += head + align16(pay);
     }
-    if (!bad && pos != r1) bad = 1;
-    sh.bad = bad;
+    if (!bad && !tsbad && pos != r1) bad = 1;
+    sh.bad = bad ? int(kErrCorrupt) : tsbad ? int(kErrTableset) : 0;
   }
   __syncthreads();
   if (sh.bad) {
-    if (tid == 0) atomicOr(&a.ctl[0], kErrCorrupt);
+    if (tid == 0) atomicOr(&a.ctl[0], uint32_t(sh.bad));
     return;
   }
 
@@ -704,9 +710,13 @@ __global__ void k_check(CheckArgs a) {
   __shared__ int bad;
   if (tid == 0) bad = 0;
   __syncthreads();
-  // this kernel runs first and owns the error word: it stores, the decode ORs
+  // this kernel runs first and owns the error word (ctl[0]) and the
+  // container's group flag (ctl[1]): it stores, the decode reads and ORs
   if (a.in_bytes < a.hdr_bytes + 8ull * (a.n_chunks + 1)) {
-    if (tid == 0) a.ctl[0] = kErrCorrupt;
+    if (tid == 0) {
+      a.ctl[0] = kErrCorrupt;
+      a.ctl[1] = 0;
+    }
     return;
   }
   for (uint32_t i = tid; i < a.hdr_bytes; i += blockDim.x) {
@@ -726,6 +736,7 @@ __global__ void k_check(CheckArgs a) {
     else if (*reinterpret_cast<const uint64_t *>(a.in + a.off_dir + 8ull * a.n_chunks) != total - 16)
       err |= kErrCorrupt;
     a.ctl[0] = err;
+    a.ctl[1] = flags == 1 ? 1u : 0u;
   }
 }
 

@@ -203,6 +203,7 @@ hipError_t launch_hist_all(int dtype, const DevLayout &L, const uint8_t *const *
 
 hipError_t launch_keys(const uint32_t *hist, int stride, int A, const DevLayout &L,
                        unsigned long long *keys, hipStream_t s) {
+  if (!L.n_chunks) return hipSuccess;
   hipLaunchKernelGGL(k_keys, dim3((L.n_chunks + 255) / 256), dim3(256), 0, s, hist, stride, A, L, keys);
   return hipGetLastError();
 }

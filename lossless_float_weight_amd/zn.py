@@ -47,6 +47,8 @@ def lib() -> C.CDLL:
         L.zn_setup.argtypes = [I, C.POINTER(P), PU64, I, U32, I, P, C.POINTER(P)]
         L.zn_setup_transfer.argtypes = [P, C.POINTER(P), PU64, I, P, C.POINTER(P)]
         L.zn_plan_from_container.argtypes = [P, U64, P, C.POINTER(P)]
+        L.zn_header_info.argtypes = [P, U64, C.POINTER(I), C.POINTER(I), PU64, C.POINTER(U32),
+                                     C.POINTER(U32), PU64, PU64]
         L.zn_tableset_info.argtypes = [P, C.POINTER(I), C.POINTER(I), PU64, C.POINTER(U32),
                                        C.POINTER(U32), C.POINTER(I), PU64]
         L.zn_compress_bound.argtypes = [P, PU64]
@@ -63,7 +65,8 @@ def lib() -> C.CDLL:
         L.zn_debug_histograms.argtypes = [P, P, P, P]
         L.zn_debug_code_lengths.argtypes = [P, I, I, I, P, P]
         L.zn_debug_kernel_events.argtypes = [C.c_char_p, P, P]
-        for f in ("zn_setup", "zn_setup_transfer", "zn_plan_from_container", "zn_tableset_info", "zn_compress_bound",
+        for f in ("zn_setup", "zn_setup_transfer", "zn_plan_from_container", "zn_header_info",
+                  "zn_tableset_info", "zn_compress_bound",
                   "zn_scratch_bytes", "zn_compress", "zn_decompress", "zn_tableset_save",
                   "zn_tableset_load", "zn_tableset_lengths", "zn_tableset_map",
                   "zn_tableset_cost_history", "zn_debug_histograms", "zn_debug_code_lengths",
@@ -105,6 +108,12 @@ class Tableset:
             self.handle = None
 
     def info(self) -> dict:
+        """Plan facts (fixed for the handle's lifetime, so read once)."""
+        if getattr(self, "_info", None) is None:
+            self._info = self._read_info()
+        return dict(self._info)
+
+    def _read_info(self) -> dict:
         dt, T, nc, K = C.c_int(), C.c_int(), C.c_uint32(), C.c_int()
         cb, h = C.c_uint32(), C.c_uint64()
         _check(lib().zn_tableset_info(self.handle, C.byref(dt), C.byref(T), None, C.byref(cb),
@@ -199,6 +208,54 @@ def plan_from_container(blob: torch.Tensor, stream=None) -> Tableset:
     return Tableset(h)
 
 
+def header_info(hdr) -> dict:
+    """zn_header_info on the first 64 bytes of a container (host bytes, a
+    numpy array or a tensor on any device)."""
+    if isinstance(hdr, torch.Tensor):
+        hdr = hdr[:64].cpu().numpy().tobytes()
+    elif not isinstance(hdr, (bytes, bytearray)):
+        hdr = bytes(memoryview(hdr)[:64])
+    buf = (C.c_uint8 * max(1, len(hdr))).from_buffer_copy(bytes(hdr) or b"\0")
+    dt, T = C.c_int(), C.c_int()
+    n, tot, h = C.c_uint64(), C.c_uint64(), C.c_uint64()
+    cb, nc = C.c_uint32(), C.c_uint32()
+    _check(lib().zn_header_info(buf, len(hdr), C.byref(dt), C.byref(T), C.byref(n), C.byref(cb),
+                                C.byref(nc), C.byref(tot), C.byref(h)), "header_info")
+    return {"dtype": dt.value, "n_tensors": T.value, "n_elems": n.value, "chunk_bytes": cb.value,
+            "n_chunks": nc.value, "total_bytes": tot.value, "tableset_hash": h.value}
+
+
+def _check_tensors(ts: Tableset, tensors, where: str, exact: bool) -> None:
+    """The tensors must be the plan's: count, dtype, one CUDA device,
+    contiguous storage, and exactly (inputs) or at least (outputs) the
+    plan's element counts.  Raises ZnError(-1) before any launch."""
+    info = ts.info()
+    want = TORCH_DTYPE[info["dtype"]]
+    if len(tensors) != info["n_tensors"]:
+        raise ZnError(-1, f"{where}: plan has {info['n_tensors']} tensors, got {len(tensors)}")
+    dev = None
+    for i, (t, n) in enumerate(zip(tensors, info["n_elems"])):
+        if t.dtype != want:
+            raise ZnError(-1, f"{where}: tensor {i} is {t.dtype}, the plan codes {want}")
+        if not t.is_cuda or (dev is not None and t.device != dev):
+            raise ZnError(-1, f"{where}: tensor {i} is not on the plan's CUDA device")
+        dev = t.device
+        if not t.is_contiguous():
+            raise ZnError(-1, f"{where}: tensor {i} is not contiguous (pass .contiguous())")
+        if (t.numel() != n) if exact else (t.numel() < n):
+            raise ZnError(-1, f"{where}: tensor {i} has {t.numel()} elements, the plan {n}")
+
+
+def _keep_alive(stream, *tensors) -> None:
+    """Temporaries of an asynchronous call on a stream other than the current
+    one stay allocated until that stream's work is done."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def compress_bound(ts: Tableset) -> int:
     b = C.c_uint64()
     _check(lib().zn_compress_bound(ts.handle, C.byref(b)), "compress_bound")
@@ -220,13 +277,22 @@ def compress(ts: Tableset, tensors: Sequence[torch.Tensor], out: torch.Tensor | 
              sync: bool = True, stream=None):
     """zn_compress.  Returns the container (a view of `out`) when sync, else
     `out` itself (size at byte 56 once the stream has run)."""
+    _check_tensors(ts, tensors, "compress", exact=True)
     dev = tensors[0].device
+    tmp = []
     if out is None:
         out = torch.empty(compress_bound(ts), dtype=torch.uint8, device=dev)
     if scratch is None:
         scratch = new_scratch(ts, dev)
+        tmp.append(scratch)
     if ptrs is None:
         ptrs = _ptr_array(tensors, dev)
+        tmp.append(ptrs)
+    for name, b in (("out", out), ("scratch", scratch)):
+        if b.device != dev or not b.is_contiguous() or b.dtype != torch.uint8:
+            raise ZnError(-1, f"compress: {name} must be a contiguous uint8 tensor on {dev}")
+    if not sync:
+        _keep_alive(stream, *tmp)
     nb = C.c_uint64()
     _check(lib().zn_compress(ts.handle, C.c_void_p(ptrs.data_ptr()), C.c_void_p(out.data_ptr()),
                              out.numel(), C.byref(nb) if sync else None,
@@ -239,14 +305,24 @@ def decompress(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Tensor] | 
                scratch: torch.Tensor | None = None, ptrs: torch.Tensor | None = None,
                sync: bool = True, stream=None):
     """zn_decompress into `outs` (allocated from the plan when None)."""
+    if not blob.is_cuda or not blob.is_contiguous() or blob.dtype != torch.uint8:
+        raise ZnError(-1, "decompress: the container must be a contiguous uint8 CUDA tensor")
     if outs is None:
         info = ts.info()
         outs = [torch.empty(n, dtype=TORCH_DTYPE[info["dtype"]], device=blob.device)
                 for n in info["n_elems"]]
+    _check_tensors(ts, outs, "decompress", exact=False)
+    if outs and outs[0].device != blob.device:
+        raise ZnError(-1, "decompress: outputs and container on different devices")
+    tmp = []
     if scratch is None:
         scratch = torch.empty(256, dtype=torch.uint8, device=blob.device)
+        tmp.append(scratch)
     if ptrs is None:
         ptrs = _ptr_array(outs, blob.device)
+        tmp.append(ptrs)
+    if not sync:
+        _keep_alive(stream, *tmp)
     _check(lib().zn_decompress(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
                                C.c_void_p(ptrs.data_ptr()), C.c_void_p(scratch.data_ptr()),
                                scratch.numel(), 1 if sync else 0, _stream(stream)), "decompress")

@@ -879,7 +879,9 @@ int zno_tableset_load(const void *buf, uint64_t len, zno_tableset **out) {
     }
   memcpy(ts->map, q, M);
   int bad = msum != M;
-  for (uint32_t c = 0; c < M && !bad; c++) bad = ts->map[c] >= K;
+  /* a plan without groups stores its map as zero bytes; with groups each
+     byte names one of the K groups */
+  for (uint32_t c = 0; c < M && !bad; c++) bad = K ? ts->map[c] >= K : ts->map[c] != 0;
   for (int g = 0; g < K && !bad; g++)
     for (int s = 0; s < A; s++) bad |= ts->len[g][s] > MAXLEN;
   if (bad || ts_rehash(ts) < 0) {
@@ -1033,6 +1035,9 @@ int zno_header(const void *inv, uint64_t in_bytes, int *dt, int *T, uint64_t *nt
   if (!valid_dtype(in[6]) || (in[7] & ~1u) || in[30] != MAXLEN || in[31] != ncoded(in[6]) ||
       get_u16(in + 28) != (uint32_t)segsyms(in[6]) || !valid_chunk(get_u32(in + 12)))
     return ZNO_ERR_CORRUPT;
+  /* R6: a container holds at least one tensor, and its hash field is zero
+     unless the group bit is set */
+  if (get_u32(in + 8) < 1 || (!(in[7] & 1) && get_u64(in + 32) != 0)) return ZNO_ERR_CORRUPT;
   if (dt) *dt = in[6];
   if (T) *T = (int)get_u32(in + 8);
   if (ntot) *ntot = get_u64(in + 16);

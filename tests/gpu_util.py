@@ -64,8 +64,12 @@ def field_modes(blob: np.ndarray, n_fields: int, kbits):
     return out
 
 
-def sample_chunks(n_chunks: int, k: int, seed: int = 0):
-    rng = np.random.default_rng(seed)
-    pick = {0, n_chunks - 1}
-    pick |= set(int(x) for x in rng.integers(0, n_chunks, size=min(k, n_chunks)))
-    return sorted(pick)
+def oracle_compress_async(oracle, dt, arrs, chunk_bytes, ots=None):
+    """The oracle's container of arrs, computed in a host thread (the oracle's
+    C code runs with the interpreter lock released, so the GPU side of a test
+    proceeds meanwhile).  Returns a future."""
+    import concurrent.futures as cf
+    ex = cf.ThreadPoolExecutor(1)
+    fut = ex.submit(oracle.compress, dt, arrs, chunk_bytes, ots)
+    ex.shutdown(wait=False)
+    return fut

@@ -27,6 +27,17 @@ NCODED = {0: 1, 1: 4, 2: 2, 3: 2}
 SEG = {0: 512, 1: 256, 2: 1024, 3: 1024}
 
 
+def fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64-bit (Fowler, Noll and Vo): start from the offset basis, then
+    per byte XOR it into the low bits and multiply by the 64-bit FNV prime
+    2^40 + 2^8 + 0xB3, modulo 2^64."""
+    prime = (1 << 40) + (1 << 8) + 0xB3
+    h = 0xCBF29CE484222325
+    for b in data:
+        h = ((h ^ b) * prime) % (1 << 64)
+    return h
+
+
 def kbits(dt, p):
     if dt == 2:
         return 4 if p == 0 else 3

@@ -70,3 +70,62 @@ def test_bad_tableset_bytes_and_null_plans_need_no_gpu():
     assert lib.zn_scratch_bytes(None, ctypes.byref(v)) == -1
     assert lib.zn_tableset_info(None, None, None, None, None, None, None, None) == -1
     assert lib.zn_decompress(None, None, 0, None, None, 0, 1, None) == -1
+
+
+def _header_info(lib, buf: bytes):
+    I, U32, U64 = ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64
+    P = ctypes.POINTER
+    lib.zn_header_info.argtypes = [ctypes.c_void_p, U64, P(I), P(I), P(U64), P(U32), P(U32), P(U64), P(U64)]
+    dt, T = I(-1), I(-1)
+    n, tot, h = U64(), U64(), U64()
+    cb, nc = U32(), U32()
+    b = ctypes.create_string_buffer(buf, max(1, len(buf)))
+    rc = lib.zn_header_info(b, len(buf), ctypes.byref(dt), ctypes.byref(T), ctypes.byref(n), ctypes.byref(cb),
+                            ctypes.byref(nc), ctypes.byref(tot), ctypes.byref(h))
+    return rc, {"dtype": dt.value, "n_tensors": T.value, "n_elems": n.value, "chunk_bytes": cb.value,
+                "n_chunks": nc.value, "total_bytes": tot.value, "tableset_hash": h.value}
+
+
+def _oracle_status(oracle, buf: bytes):
+    import numpy as np
+    try:
+        return 0, oracle.header(np.frombuffer(buf, np.uint8))
+    except oracle.OracleError as e:
+        return e.code, None
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libzn.so not built")
+def test_header_info_equals_oracle_header_needs_no_gpu(oracle):
+    # zn_header_info is host-only; on containers of every dtype (grouped and
+    # not) and on every single-byte corruption of their headers it returns
+    # the oracle's status and, when it accepts, the oracle's fields
+    import numpy as np
+    lib = ctypes.CDLL(LIB)
+    rng = np.random.default_rng(4)
+    blobs = []
+    for dt, n in ((oracle.BF16, 70000), (oracle.FP32, 20000), (oracle.FP8_E4M3, 90000),
+                  (oracle.FP4X2_E2M1, 50000)):
+        x = rng.integers(0, 1 << (8 * oracle.ELEM_DTYPE[dt]().itemsize), n, dtype=np.uint64)
+        x = x.astype(oracle.ELEM_DTYPE[dt])
+        blobs.append(oracle.compress(dt, [x, x[: n // 3]], 16384))
+    g = rng.normal(0, 0.02, 200000).astype(np.float32).view(np.uint32)
+    bf = ((g + 0x8000) >> 16).astype(np.uint16)
+    ts = oracle.setup(oracle.BF16, [bf], 65536, 2)
+    blobs.append(oracle.compress(oracle.BF16, [bf], 65536, ts))
+    for blob in blobs:
+        hdr = blob[:64].tobytes()
+        rc, got = _header_info(lib, hdr)
+        orc, want = _oracle_status(oracle, hdr)
+        assert rc == orc == 0 and got == want
+        for pos in range(64):
+            for v in (hdr[pos] ^ 1, hdr[pos] ^ 0x80, 0, 255):
+                bad = bytearray(hdr)
+                bad[pos] = v
+                rc, got = _header_info(lib, bytes(bad))
+                orc, want = _oracle_status(oracle, bytes(bad))
+                assert rc == orc, (pos, v, rc, orc)
+                if rc == 0:
+                    assert got == want
+    assert _header_info(lib, blobs[0][:63].tobytes())[0] == -1      # too short: argument error
+    lib.zn_header_info.argtypes = [ctypes.c_void_p, ctypes.c_uint64] + [ctypes.c_void_p] * 7
+    assert lib.zn_header_info(None, 64, *([None] * 7)) == -1

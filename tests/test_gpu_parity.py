@@ -1,10 +1,8 @@
 """GPU parity: libzn.so (HIP kernels, through the C ABI) against the CPU oracle.
 
 The bar is bit-exactness: container bytes identical to the oracle's on the
-same seeded inputs, and decompressed tensors identical to the inputs.  Small
-cases compare whole containers; full-size workloads compare sampled chunk
-records one by one (the oracle encodes each sampled chunk alone) plus the
-exact GPU round trip of everything.
+same seeded inputs, and decompressed tensors identical to the inputs.  Every
+case, the full-size workloads included, compares whole containers.
 """
 import numpy as np
 import pytest
@@ -12,8 +10,8 @@ import torch
 
 from lossless_float_weight_amd import workloads as W
 from lossless_float_weight_amd import zn
-from tests.gpu_util import (assert_roundtrip, field_modes, first_difference, gpu_compress, record_bounds,
-                            sample_chunks, to_np)
+from tests.gpu_util import (assert_roundtrip, field_modes, first_difference, gpu_compress,
+                            oracle_compress_async, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -227,14 +225,6 @@ def test_fp4_ragged_every_pattern(oracle, n):
     _check_equal(oracle, oracle.FP4X2_E2M1, [x.cuda()], 4096)
 
 
-def test_fp4_full_size_sampled(oracle):
-    print("case: FP4 E2M1 pairs 2^29 bytes, sampled records", flush=True)
-    tensors = [W.fp4_blockscaled(1 << 29, device="cuda")[0][1]]
-    ts, blob = gpu_compress(tensors, 262144)
-    _sampled_record_parity(oracle, oracle.FP4X2_E2M1, tensors, blob, 262144)
-    assert_roundtrip(ts, blob, tensors)
-
-
 # -------------------------------------------------------- single stages ----
 def test_histograms_equal_bincount(oracle):
     print("case: per-chunk histograms", flush=True)
@@ -398,51 +388,56 @@ def test_capacity_reported():
 
 
 # ------------------------------------------------ full-size workloads ------
-def _sampled_record_parity(oracle, dt, tensors, blob, chunk_bytes, k=12, ts=None):
+# Every full-size workload is compared as a whole container: the oracle
+# compresses the same bits on the host (in a thread, while the GPU works) and
+# the two containers must be equal byte for byte -- header, tensor table,
+# directory, always-raw planes, every record and the zero tail.
+def _whole_container_parity(oracle, dt, tensors, chunk_bytes, ts=None, ots=None, label=""):
+    import time
+    t0 = time.time()
+    arrs = [to_np(t) for t in tensors]
+    fut = oracle_compress_async(oracle, dt, arrs, chunk_bytes, ots)
+    ts, blob = gpu_compress(tensors, chunk_bytes, ts)
     g = blob.cpu().numpy()
-    _, n_chunks, dirv = record_bounds(g)
-    esz = tensors[0].element_size()
-    ce = chunk_bytes // esz
-    starts = np.cumsum([0] + [(t.numel() + ce - 1) // ce for t in tensors])
-    gmap = ts.group_map() if ts is not None and ts.n_groups else None
-    for c in sample_chunks(n_chunks, k):
-        t = int(np.searchsorted(starts, c, side="right") - 1)
-        k0 = (c - starts[t]) * ce
-        chunk = to_np(tensors[t].reshape(-1)[k0:k0 + ce])
-        glen = ts.lengths(gmap[c]) if gmap is not None else None
-        rec, _ = oracle.encode_chunk(dt, chunk, glen, gmap[c] if gmap is not None else 0)
-        got = g[dirv[c]:dirv[c + 1]]
-        assert np.array_equal(got, rec), f"chunk {c}: " + first_difference(got, rec)
+    print(f"  {label}: GPU container {g.size} bytes at {time.time() - t0:.0f} s", flush=True)
+    assert_roundtrip(ts, blob, tensors)
+    del blob
+    o = fut.result()
+    print(f"  {label}: oracle container {o.size} bytes at {time.time() - t0:.0f} s", flush=True)
+    assert g.size == o.size and np.array_equal(g, o), first_difference(g, o)
+    return ts
 
 
 def test_config2_block_full_size(oracle):
     print("case: 8B-shaped BF16 block, full size, whole-container parity", flush=True)
     tensors = [t for _, t in W.block_bf16("cuda", seed=2)]
-    _check_equal(oracle, oracle.BF16, tensors, 262144)
+    _whole_container_parity(oracle, oracle.BF16, tensors, 262144, label="block")
 
 
-def test_config3_fp32_full_size_sampled(oracle):
-    print("case: FP32 regular + clean 2 x 2^27, sampled records", flush=True)
+def test_config3_fp32_full_size(oracle):
+    print("case: FP32 regular + clean 2 x 2^27, whole-container parity", flush=True)
     tensors = [t for _, t in W.fp32_pair(1 << 27, device="cuda")]
-    ts, blob = gpu_compress(tensors, 262144)
-    _sampled_record_parity(oracle, oracle.FP32, tensors, blob, 262144)
-    assert_roundtrip(ts, blob, tensors)
+    _whole_container_parity(oracle, oracle.FP32, tensors, 262144, label="fp32 pair")
 
 
-def test_config4_fp8_full_size_sampled(oracle):
-    print("case: FP8 E4M3 2^30, sampled records", flush=True)
+def test_config4_fp8_full_size(oracle):
+    print("case: FP8 E4M3 2^30, whole-container parity", flush=True)
     tensors = [W.fp8_blockscaled(1 << 30, device="cuda")[0][1]]
-    ts, blob = gpu_compress(tensors, 262144)
-    _sampled_record_parity(oracle, oracle.FP8_E4M3, tensors, blob, 262144)
-    assert_roundtrip(ts, blob, tensors)
+    _whole_container_parity(oracle, oracle.FP8_E4M3, tensors, 262144, label="fp8")
+
+
+def test_fp4_full_size(oracle):
+    print("case: FP4 E2M1 pairs 2^29 bytes, whole-container parity", flush=True)
+    tensors = [W.fp4_blockscaled(1 << 29, device="cuda")[0][1]]
+    _whole_container_parity(oracle, oracle.FP4X2_E2M1, tensors, 262144, label="fp4")
 
 
 @pytest.mark.slow
 def test_config5_full_model_grouped(oracle):
     """Full 8B-shaped model + KV cache (290 tensors, 9.65e9 BF16 values):
     the K = 16 setup on the GPU equals the oracle's on the same data; the
-    perturbed copy compressed with that setup unchanged matches the oracle's
-    records on sampled chunks and round-trips exactly."""
+    perturbed copy compressed with that setup unchanged is byte-identical to
+    the oracle's container and round-trips exactly."""
     import time
     t0 = time.time()
     print("case: full model 290 tensors, K=16 setup, perturbed reuse", flush=True)
@@ -463,9 +458,5 @@ def test_config5_full_model_grouped(oracle):
     del arrs
     pert = [t for _, t in W.perturbed_model(named, seed=5)]
     del named, tensors
-    _, blob = gpu_compress(pert, 262144, ts)
-    print(f"  perturbed copy compressed at {time.time() - t0:.0f} s, ratio "
-          f"{blob.numel() / (2 * sum(t.numel() for t in pert)):.5f}", flush=True)
-    _sampled_record_parity(oracle, oracle.BF16, pert, blob, 262144, k=24, ts=ts)
-    assert_roundtrip(ts, blob, pert)
+    _whole_container_parity(oracle, oracle.BF16, pert, 262144, ts, ots, label="perturbed model")
     print(f"  done at {time.time() - t0:.0f} s", flush=True)

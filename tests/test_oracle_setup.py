@@ -156,3 +156,58 @@ def test_grouping_matches_independent_restatement(oracle):
     assert ts.group_map().tolist() == grp
     for g in range(K):
         assert ts.lengths(g).tolist() == tab[g]
+
+
+# ------------------------------------------------------------- tableset hash
+def _fnv_vectors():
+    import ast
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "fnv1a64_vectors.txt")
+    out = []
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            lit, hx = line.rstrip("\n").split("\t")
+            out.append((ast.literal_eval(lit), int(hx, 16)))
+    return out
+
+
+def test_fnv1a64_restatement_matches_published_vectors():
+    vecs = _fnv_vectors()
+    assert len(vecs) >= 3
+    for data, want in vecs:
+        assert ref_tiny.fnv1a64(data) == want, data
+
+
+@pytest.mark.parametrize("K", [0, 1, 4])
+def test_tableset_hash_is_fnv1a64_of_saved_bytes(oracle, K):
+    # the hash a grouped container records is FNV-1a-64 over the saved
+    # tableset; the restatement above is pinned to the published vectors
+    arrs = _np(_model(n_layers=1))
+    ts = oracle.setup(oracle.BF16, arrs, 65536, K)
+    assert ts.hash == ref_tiny.fnv1a64(ts.save())
+    blob = oracle.compress(oracle.BF16, arrs, 65536, ts)
+    h = oracle.header(blob)
+    assert h["tableset_hash"] == (ref_tiny.fnv1a64(ts.save()) if K else 0)
+
+
+def test_transferred_tableset_hash_is_fnv1a64(oracle):
+    arrs = _np(_model(n_layers=1))
+    ts = oracle.setup(oracle.BF16, arrs, 65536, 4)
+    other = [W.bits(t).numpy().ravel() for _, t in W.other_block_bf16("cpu", seed=7, scale=16)]
+    tr = oracle.setup_transfer(ts, other)
+    assert tr.hash == ref_tiny.fnv1a64(tr.save()) and tr.hash != ts.hash
+
+
+def test_plan_without_groups_saves_and_loads(oracle):
+    # a plan with no groups stores its chunk map as zero bytes and loads back
+    arrs = _np(_model(n_layers=1))
+    ts = oracle.setup(oracle.BF16, arrs, 65536, 0)
+    saved = ts.save()
+    assert ts.n_groups == 0 and ts.group_map().size > 0 and not np.any(ts.group_map())
+    back = oracle.Tableset.load(saved)
+    assert back.save() == saved and back.hash == ts.hash
+    # a non-zero map byte in such a plan is corrupt
+    bad = bytearray(saved)
+    bad[-1] = 1
+    with pytest.raises(oracle.OracleError):
+        oracle.Tableset.load(bytes(bad))
