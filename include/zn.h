@@ -178,6 +178,27 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
                         void *const *d_out_ptrs, void *d_scratch, uint64_t scratch_bytes,
                         int sync, hipStream_t stream);
 
+/* zn_decompress_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): zn_decompress with the same kernels and checks, its 256-byte
+ * control area (error word, group flag, sink of lanes without a whole
+ * vector) in a static device array owned by the library instead of caller
+ * scratch.  Allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Each GPU holds its own copy of the array until the process ends;
+ * every call on a GPU shares that GPU's copy, which keeps the last call's
+ * contents (the first kernel of each call overwrites what it needs), so
+ * calls that overlap on one GPU (several streams or host threads) race and
+ * must be ordered by the caller.  The area's size does not depend on the
+ * container, so no container is refused for its size.
+ *   d_status: NULL, or a caller-owned device u32 that receives the error word
+ *     (0 ok, 2 corrupt, 4 tableset mismatch) by a device-to-device copy
+ *     ordered after the kernels, for callers that do not synchronise.
+ *   sync: as for zn_decompress.  Other arguments and statuses as for
+ *     zn_decompress. */
+zn_status zn_decompress_noalloc(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
+                                void *const *d_out_ptrs, uint32_t *d_status, int sync,
+                                hipStream_t stream);
+
 /* Serialisation of a plan, byte-identical to the CPU oracle's; its FNV-1a-64
  * hash is what containers record. */
 zn_status zn_tableset_save(const zn_tableset *ts, void *h_buf, uint64_t cap, uint64_t *len);

@@ -9,6 +9,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -515,15 +517,21 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   return ZN_OK;
 }
 
-zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
-                        void *const *d_out_ptrs, void *d_scratch, uint64_t scratch_bytes, int sync,
-                        hipStream_t stream) {
-  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks) || !d_scratch) return ZN_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(d_scratch) & 15) || (reinterpret_cast<uintptr_t>(d_in) & 15))
-    return ZN_ERR_ARG;
-  if (scratch_bytes < kCtlBytes) return ZN_ERR_CAPACITY;
+}  // extern "C"
+
+// Control area of zn_decompress_noalloc: device memory the library owns, one
+// copy per GPU (each GPU holds its own copy at its own address), kept until
+// the process ends.  Its need does not grow with the container: 256 bytes.
+constexpr uint64_t kNoAllocScratchBytes = 256;
+static_assert(kNoAllocScratchBytes >= kCtlBytes, "the decoder's control area fits");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+// The decompression launches on a caller's stream with the control area ctl
+// (256 bytes: error word, group flag, sink of lanes without a whole vector).
+zn_status decompress_with(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
+                          void *const *d_out_ptrs, uint32_t *ctl, int sync, hipStream_t stream) {
   if (in_bytes < ts->off_records + 16) return ZN_ERR_CORRUPT;
-  uint32_t *ctl = static_cast<uint32_t *>(d_scratch);
   CheckArgs ck;
   ck.in = static_cast<const uint8_t *>(d_in);
   ck.in_bytes = in_bytes;
@@ -552,6 +560,59 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
   if (flag & kErrTableset) return ZN_ERR_TABLESET;
   if (flag) return ZN_ERR_CORRUPT;
   return ZN_OK;
+}
+
+// Device address of `scratch` on each GPU, looked up once per device with
+// that device current (in host code the array's name is only a stand-in).
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+zn_status noalloc_scratch(void **out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return ZN_ERR_ARG;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ZN_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ZN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
+                        void *const *d_out_ptrs, void *d_scratch, uint64_t scratch_bytes, int sync,
+                        hipStream_t stream) {
+  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks) || !d_scratch) return ZN_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_scratch) & 15) || (reinterpret_cast<uintptr_t>(d_in) & 15))
+    return ZN_ERR_ARG;
+  if (scratch_bytes < kCtlBytes) return ZN_ERR_CAPACITY;
+  return decompress_with(ts, d_in, in_bytes, d_out_ptrs, static_cast<uint32_t *>(d_scratch), sync, stream);
+}
+
+zn_status zn_decompress_noalloc(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
+                                void *const *d_out_ptrs, uint32_t *d_status, int sync,
+                                hipStream_t stream) {
+  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks)) return ZN_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(d_in) & 15) return ZN_ERR_ARG;
+  void *ctl = nullptr;
+  zn_status st = noalloc_scratch(&ctl);
+  if (st != ZN_OK) return st;
+  st = decompress_with(ts, d_in, in_bytes, d_out_ptrs, static_cast<uint32_t *>(ctl), sync, stream);
+  // the error word, for callers that do not synchronise (a device-to-device
+  // copy, stream-ordered after the kernels)
+  if (d_status && (st == ZN_OK || st == ZN_ERR_CORRUPT || st == ZN_ERR_TABLESET) &&
+      in_bytes >= ts->off_records + 16)
+    HIPCHK(hipMemcpyAsync(d_status, ctl, 4, hipMemcpyDeviceToDevice, stream));
+  return st;
 }
 
 zn_status zn_tableset_save(const zn_tableset *ts, void *h_buf, uint64_t cap, uint64_t *len) {

@@ -55,6 +55,7 @@ def lib() -> C.CDLL:
         L.zn_scratch_bytes.argtypes = [P, PU64]
         L.zn_compress.argtypes = [P, P, P, U64, PU64, P, U64, P]
         L.zn_decompress.argtypes = [P, P, U64, P, P, U64, I, P]
+        L.zn_decompress_noalloc.argtypes = [P, P, U64, P, P, I, P]
         L.zn_tableset_save.argtypes = [P, P, U64, PU64]
         L.zn_tableset_load.argtypes = [P, U64, C.POINTER(P)]
         L.zn_tableset_lengths.argtypes = [P, I, P]
@@ -67,7 +68,8 @@ def lib() -> C.CDLL:
         L.zn_debug_kernel_events.argtypes = [C.c_char_p, P, P]
         for f in ("zn_setup", "zn_setup_transfer", "zn_plan_from_container", "zn_header_info",
                   "zn_tableset_info", "zn_compress_bound",
-                  "zn_scratch_bytes", "zn_compress", "zn_decompress", "zn_tableset_save",
+                  "zn_scratch_bytes", "zn_compress", "zn_decompress", "zn_decompress_noalloc",
+                  "zn_tableset_save",
                   "zn_tableset_load", "zn_tableset_lengths", "zn_tableset_map",
                   "zn_tableset_cost_history", "zn_debug_histograms", "zn_debug_code_lengths",
                   "zn_debug_kernel_events"):
@@ -326,6 +328,26 @@ def decompress(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Tensor] | 
     _check(lib().zn_decompress(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
                                C.c_void_p(ptrs.data_ptr()), C.c_void_p(scratch.data_ptr()),
                                scratch.numel(), 1 if sync else 0, _stream(stream)), "decompress")
+    return outs
+
+
+def decompress_noalloc(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Tensor],
+                       ptrs: torch.Tensor, status: torch.Tensor | None = None, sync: bool = True,
+                       stream=None):
+    """zn_decompress_noalloc: the library allocates nothing; the caller
+    passes the outputs, their device pointer array and optionally a device
+    int32 `status` that receives the error word."""
+    if not blob.is_cuda or not blob.is_contiguous() or blob.dtype != torch.uint8:
+        raise ZnError(-1, "decompress_noalloc: the container must be a contiguous uint8 CUDA tensor")
+    _check_tensors(ts, outs, "decompress_noalloc", exact=False)
+    if ptrs.device != blob.device or ptrs.dtype != torch.int64 or ptrs.numel() != len(outs):
+        raise ZnError(-1, "decompress_noalloc: ptrs must be the outputs' int64 device pointers")
+    if status is not None and (status.device != blob.device or status.dtype != torch.int32):
+        raise ZnError(-1, "decompress_noalloc: status must be an int32 tensor on the container's device")
+    _check(lib().zn_decompress_noalloc(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
+                                       C.c_void_p(ptrs.data_ptr()),
+                                       C.c_void_p(status.data_ptr()) if status is not None else None,
+                                       1 if sync else 0, _stream(stream)), "decompress_noalloc")
     return outs
 
 
