@@ -259,11 +259,18 @@ def main():
     if args.workload == "model":
         # the reusable setup: groups and shared tables from the model, then
         # every step compresses a perturbed copy with that setup unchanged
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ts = zn.setup(base, chunk_bytes=CHUNK_BYTES, n_groups=16)
-        torch.cuda.synchronize()
-        extra["setup_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        # the first call also loads the setup kernels and allocates; the setup
+        # time is that of the calls after it (a new checkpoint set up again)
+        times = []
+        for _ in range(4):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ts = zn.setup(base, chunk_bytes=CHUNK_BYTES, n_groups=16)
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t0) * 1e3)
+        extra["setup_first_ms"] = round(times[0], 2)
+        extra["setup_ms"] = round(sorted(times[1:])[1], 2)
+        extra["setup_GBps"] = round(unc / (extra["setup_ms"] * 1e-3) / 1e9, 1)
         names = [f"t{i}" for i in range(len(base))]
         base = [t for _, t in W.perturbed_model(list(zip(names, base)), seed=5)]
         torch.cuda.synchronize()

@@ -225,44 +225,52 @@ struct DevBuf {
 
 // NeuralZip grouping on the GPU (integer Lloyd rounds); see zn_setup.hip.
 zn_status run_grouping(zn_tableset *ts, const void *const *d_tensors, hipStream_t s) {
-  const int dt = ts->dtype, K = ts->K, NC = ncoded(dt), A = alphabet0(dt);
+  const int dt = ts->dtype, K = ts->K, A = alphabet0(dt);
   const uint32_t M = ts->n_chunks;
-  const int stride = NC * 256;
+  const int stride = 256;   // the exponent stream's histogram only
   ts->len.assign(256ull * K, 0);
   ts->cost.assign(kRounds + 1, 0);
   DevBuf<const uint8_t *> ptrs;
   DevBuf<uint32_t> hist;
   DevBuf<unsigned long long> keys, pooled, cost;
   DevBuf<uint8_t> map, len;
-  DevBuf<uint32_t> dummy;
   if (ptrs.alloc(ts->T) || hist.alloc(uint64_t(M) * stride) || keys.alloc(M) ||
-      pooled.alloc(256ull * K) || cost.alloc(1) || map.alloc(M) || len.alloc(256ull * K))
+      pooled.alloc(256ull * K) || cost.alloc(kRounds + 1) || map.alloc(M) || len.alloc(256ull * K))
     return ZN_ERR_NOMEM;
   HIPCHK(hipMemcpyAsync(ptrs.p, d_tensors, sizeof(void *) * ts->T, hipMemcpyHostToDevice, s));
   const DevLayout L = dev_layout(ts);
-  HIPCHK(launch_hist_all(dt, L, ptrs.p, hist.p, s));
+  HIPCHK(launch_hist0(dt, L, ptrs.p, hist.p, s));
   HIPCHK(launch_keys(hist.p, stride, A, L, keys.p, s));
   std::vector<unsigned long long> hkeys(M);
   HIPCHK(hipMemcpyAsync(hkeys.data(), keys.p, 8ull * M, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
-  // initial groups: chunks ordered by (key, chunk), cut into K even runs
-  std::vector<uint32_t> order(M);
+  // initial groups: chunks ordered by (key, chunk), cut into K even runs.
+  // A key is below 256 * 2^16 = 2^24: three stable counting passes over its
+  // bytes (least significant first) starting from chunk order give exactly
+  // that order.
+  std::vector<uint32_t> order(M), tmp(M);
   for (uint32_t c = 0; c < M; c++) order[c] = c;
-  std::sort(order.begin(), order.end(), [&](uint32_t x, uint32_t y) {
-    return hkeys[x] != hkeys[y] ? hkeys[x] < hkeys[y] : x < y;
-  });
+  for (int pass = 0; pass < 3; pass++) {
+    uint32_t cnt[257] = {0};
+    const int sh = 8 * pass;
+    for (uint32_t i = 0; i < M; i++) cnt[((hkeys[order[i]] >> sh) & 0xFF) + 1]++;
+    for (int b = 0; b < 256; b++) cnt[b + 1] += cnt[b];
+    for (uint32_t i = 0; i < M; i++) tmp[cnt[(hkeys[order[i]] >> sh) & 0xFF]++] = order[i];
+    order.swap(tmp);
+  }
   for (int g = 0; g < K; g++)
     for (uint64_t i = uint64_t(M) * g / K; i < uint64_t(M) * (g + 1) / K; i++) ts->map[order[i]] = uint8_t(g);
   HIPCHK(hipMemcpyAsync(map.p, ts->map.data(), M, hipMemcpyHostToDevice, s));
+  // every round's cost goes to its own word, read back once at the end
+  HIPCHK(hipMemsetAsync(cost.p, 0, 8ull * (kRounds + 1), s));
   for (int r = 0; r <= kRounds; r++) {
     HIPCHK(hipMemsetAsync(pooled.p, 0, 8 * 256ull * K, s));
     HIPCHK(launch_pool(hist.p, stride, A, M, map.p, pooled.p, K, s));
     HIPCHK(launch_lengths(reinterpret_cast<const uint64_t *>(pooled.p), K, A, 1, len.p, s));
-    HIPCHK(hipMemsetAsync(cost.p, 0, 8, s));
     // the last pass only measures the final assignment
-    HIPCHK(launch_assign(hist.p, stride, A, M, len.p, K, r < kRounds, map.p, cost.p, s));
-    HIPCHK(hipMemcpyAsync(&ts->cost[r], cost.p, 8, hipMemcpyDeviceToHost, s));
+    HIPCHK(launch_assign(hist.p, stride, A, M, len.p, K, r < kRounds, map.p, cost.p + r, s));
   }
+  HIPCHK(hipMemcpyAsync(ts->cost.data(), cost.p, 8ull * (kRounds + 1), hipMemcpyDeviceToHost, s));
   HIPCHK(hipMemcpyAsync(ts->len.data(), len.p, 256ull * K, hipMemcpyDeviceToHost, s));
   HIPCHK(hipMemcpyAsync(ts->map.data(), map.p, M, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
@@ -273,9 +281,9 @@ zn_status run_grouping(zn_tableset *ts, const void *const *d_tensors, hipStream_
 // tensors to the group code of least coded size (ties to the smaller id; a
 // chunk that every code lacks a symbol for stays in group 0).
 zn_status run_transfer(zn_tableset *ts, const void *const *d_tensors, hipStream_t s) {
-  const int dt = ts->dtype, K = ts->K, NC = ncoded(dt), A = alphabet0(dt);
+  const int dt = ts->dtype, K = ts->K, A = alphabet0(dt);
   const uint32_t M = ts->n_chunks;
-  const int stride = NC * 256;
+  const int stride = 256;   // the exponent stream's histogram only
   DevBuf<const uint8_t *> ptrs;
   DevBuf<uint32_t> hist;
   DevBuf<unsigned long long> cost;
@@ -288,7 +296,7 @@ zn_status run_transfer(zn_tableset *ts, const void *const *d_tensors, hipStream_
   HIPCHK(hipMemsetAsync(map.p, 0, M ? M : 1, s));
   HIPCHK(hipMemsetAsync(cost.p, 0, 8, s));
   const DevLayout L = dev_layout(ts);
-  HIPCHK(launch_hist_all(dt, L, ptrs.p, hist.p, s));
+  HIPCHK(launch_hist0(dt, L, ptrs.p, hist.p, s));
   HIPCHK(launch_assign(hist.p, stride, A, M, len.p, K, 1, map.p, cost.p, s));
   if (M) HIPCHK(hipMemcpyAsync(ts->map.data(), map.p, M, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));

@@ -233,14 +233,30 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   // record.  With ncc coded streams, SPW = 64, 32 or 16 lanes of each wave
   // take one coded stream each (a template per SPW; the branch below is
   // uniform per workgroup).
-  int ncc = 0, cs[NC], cidx[NC], rawm = 0, constm = 0;
+  // The coded streams as a bit mask (no array indexed by a lane-dependent
+  // value, which the compiler would place in scratch memory): the ci-th coded
+  // stream is the ci-th set bit, and stream p is coded stream number
+  // popcount(codedm below p).
+  int ncc = 0, codedm = 0, rawm = 0, constm = 0;
 #pragma unroll
   for (int p = 0; p < NC; p++) {
-    cidx[p] = -1;
-    if (sh.mode[p] == HUFF || sh.mode[p] == GROUP) { cs[ncc] = p; cidx[p] = ncc; ncc++; }
+    const bool cod = sh.mode[p] == HUFF || sh.mode[p] == GROUP;
+    codedm |= int(cod) << p;
+    ncc += int(cod);
     rawm |= int(sh.mode[p] == RAW) << p;
     constm |= int(sh.mode[p] == CONST) << p;
   }
+  auto nth_coded = [&](int k) {   // the stream of coded-stream number k (0 if none)
+    int r = 0, cnt = 0;
+#pragma unroll
+    for (int q = 0; q < NC; q++) {
+      const bool isc = (codedm >> q) & 1;
+      r = isc && cnt == k ? q : r;
+      cnt += int(isc);
+    }
+    return r;
+  };
+  auto cidx = [&](int p) { return __popc(uint32_t(codedm) & ((1u << p) - 1u)); };
   // Lanes per coded stream, as the dispatch at the end chooses it: all
   // coded streams share each wave; FP32 with a coded exponent and raw or
   // constant fraction bytes gives the exponent every lane; any other FP32
@@ -254,8 +270,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   {
     const int ci = ln / spw, sj = wv * spw + ln % spw;
     if (ci < ncc && sj < nseg) {
-      if (spec && cs[ci] == 0 && sj == tid) sbits0 = sh.mode[0] == HUFF ? sbh0 : sbg0;
-      else sbits0 = ldg2(in + sh.seg_off[cs[ci]] + 2 * sj);
+      const int pc = nth_coded(ci);
+      if (spec && pc == 0 && sj == tid) sbits0 = sh.mode[0] == HUFF ? sbh0 : sbg0;
+      else sbits0 = ldg2(in + sh.seg_off[pc] + 2 * sj);
     }
   }
   // ---------------------------------------------------------- 2. tables
@@ -338,7 +355,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     // block of the output.
     const int ci = ln / SPW, slot = wv * SPW + ln % SPW;
     const bool coded = ci < ncc;
-    const int p = coded ? cs[ci] : 0;
+    const int p = coded ? nth_coded(ci) : 0;
     const uint8_t *pay = in + sh.pay_off[p];
     const uint32_t paybytes = sh.pay[p];
     const uint32_t ngroups = (paybytes + 15) / 16;
@@ -564,7 +581,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           valid = sjv < nseg && ev < n;
           // staged bytes of coded stream pp for this vector (VE bytes)
           auto staged = [&](int pp, int h) -> uint64_t {
-            const int th = t0 + cidx[pp] * SPW + sl;
+            const int th = t0 + cidx(pp) * SPW + sl;
             if constexpr (ES == 2) return stg8(sh.u.stage, 8 * part, th);
             else if constexpr (ES == 4) return *reinterpret_cast<const uint32_t *>(sh.u.stage + th * STB + 4 * part);
             else return stg8(sh.u.stage, 16 * part + 8 * h, th);

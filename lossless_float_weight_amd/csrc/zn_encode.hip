@@ -227,6 +227,86 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
   const uint32_t nvec = aligned ? n / VE : 0;
   uint8_t *rawp = a.out + a.L.t_raw[t];
 
+  // ------------------------- 0. BF16 with a group code: no histogram needed
+  // The setup chose the chunk's code; what the mode choice needs is the
+  // coded size under it (the sum of the code lengths of the chunk's
+  // exponents), whether every exponent present has a code word, and whether
+  // only one exponent value occurs (constant).  All three come from one
+  // 64-bit LDS table entry per exponent value, summed per thread: the code
+  // length (bits 0-15), 1 if it has no code word (bits 16-31), 1 if it equals
+  // the chunk's first exponent (bits 32-47); a thread sums at most 2048
+  // entries of at most 11, so no field overflows.  A chunk with an exponent
+  // its group lacks (an escape) is counted below like any other.
+  if constexpr (DT == BF16) {
+    if (a.group_map) {
+      const int g = ldg1(a.group_map + c);
+      const uint32_t ef = (load_elem<DT>(src) >> 7) & 0xFF;   // the chunk's first exponent
+      unsigned long long *tbl = reinterpret_cast<unsigned long long *>(sh.u.priv);
+      if (tid < 256) {
+        const uint32_t l = ldg1(a.group_len + g * 256 + tid);
+        tbl[tid] = l | (uint64_t(l == 0) << 16) | (uint64_t(uint32_t(tid) == ef) << 32);
+      }
+      __syncthreads();
+      unsigned long long acc = 0;
+      constexpr int B0 = 4;  // 16-byte loads in flight per thread
+      for (uint32_t v0 = tid; v0 < nvec; v0 += B0 * ENC_NT) {
+        u32x4 qs[B0];
+#pragma unroll
+        for (int b = 0; b < B0; b++) {
+          const uint32_t v = v0 + b * ENC_NT;
+          if (v < nvec) qs[b] = ldg16(src + 16ull * v);
+        }
+#pragma unroll
+        for (int b = 0; b < B0; b++) {
+          const uint32_t v = v0 + b * ENC_NT;
+          if (v >= nvec) break;
+          const uint4 q = make_uint4(qs[b][0], qs[b][1], qs[b][2], qs[b][3]);
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const uint32_t w0 = vec_elem<DT>(q, i), w1 = vec_elem<DT>(q, i + 4);
+            acc += tbl[(w0 >> 7) & 0xFF] + tbl[(w1 >> 7) & 0xFF];
+            lo |= (((w0 >> 8) & 0x80) | (w0 & 0x7F)) << (8 * i);
+            hi |= (((w1 >> 8) & 0x80) | (w1 & 0x7F)) << (8 * i);
+          }
+          stg8(rawp + e0 + uint64_t(v) * 8, u32x2{lo, hi});
+        }
+      }
+      for (uint32_t i = nvec * VE + tid; i < n; i += ENC_NT) {  // ragged tail or unaligned input
+        const uint32_t w = load_elem<DT>(src + uint64_t(i) * ES);
+        acc += tbl[(w >> 7) & 0xFF];
+        stg1(rawp + e0 + i, ((w >> 8) & 0x80) | (w & 0x7F));
+      }
+      const unsigned long long bits = block_sum<DT>(sh, acc & 0xFFFFu);
+      const unsigned long long nmiss = block_sum<DT>(sh, (acc >> 16) & 0xFFFFu);
+      const unsigned long long nfirst = block_sum<DT>(sh, (acc >> 32) & 0xFFFFu);
+      const int nseg = int((n + S - 1) / S);
+      const unsigned long long raw = section_bytes(RAW, 8, n, nseg, 0);
+      if (nfirst == n || nmiss == 0) {
+        int mode = RAW, aux = 0;
+        if (nfirst == n) {
+          mode = CONST;
+          aux = int(ef);
+        } else if (section_bytes(GROUP, 8, n, nseg, bits) < raw) {
+          mode = GROUP;
+          aux = g;
+        }
+        if (tid < 256)
+          sh.enc[0][tid] = mode == GROUP ? ldg4(a.group_enc + g * 256 + tid)
+                                         : uint32_t(tid) | (8u << 16);
+        if (tid == 0) {
+          sh.mode[0] = mode;
+          sh.aux[0] = aux;
+          sh.bits[0] = mode == GROUP ? bits : mode == RAW ? uint64_t(n) * 8 : 0;
+          sh.sec_off[0] = 0;
+        }
+        __syncthreads();
+        return section_bytes(mode, 8, n, nseg, mode == GROUP ? bits : 0);
+      }
+      __syncthreads();   // an escape: the histogram below decides
+    }
+  }
+
   // ------------------------------------------- 1. split, raw planes, counts
   for (int i = tid; i < EncShared<DT>::PRIVW; i += ENC_NT) sh.u.priv[i] = 0;
   if constexpr (EncShared<DT>::BYTEHIST) {   // the field histograms are summed into

@@ -88,6 +88,8 @@ hipError_t launch_decode(int dtype, const DecArgs &a, hipStream_t s, hipEvent_t 
 // setup
 hipError_t launch_hist_all(int dtype, const DevLayout &L, const uint8_t *const *in_ptrs,
                            uint32_t *hist /* [n_chunks][ncoded][256] */, hipStream_t s);
+hipError_t launch_hist0(int dtype, const DevLayout &L, const uint8_t *const *in_ptrs,
+                        uint32_t *hist /* [n_chunks][256], the first coded stream */, hipStream_t s);
 hipError_t launch_pool(const uint32_t *hist, int stride_words, int A, uint32_t M, const uint8_t *map,
                        unsigned long long *pooled /* [K][256] */, int K, hipStream_t s);
 hipError_t launch_lengths(const uint64_t *hw, int n, int A, int group_rule, uint8_t *len,
