@@ -83,6 +83,33 @@
  *    from the final assignment.  A pooled histogram with one symbol gets the
  *    smallest absent symbol as a zero-weight second leaf.  The chunk->group
  *    map is positional (tensor order, chunk order).
+ * R8 tANS coder of the exponent stream (the alternative entropy stage of
+ *    THEORY-599's order-0 discussion, ZipNN Fig. 4: FSE, a tabled
+ *    asymmetric-numeral-system coder, codes exponents 0-2% smaller than
+ *    Huffman).  Chosen per compression call, for chunks coded with their own
+ *    table (no group tables).  Ours, after Duda's tabled ANS:
+ *    - 2^11 states.  Normalised counts q: q[s] = max(1, floor(h[s]*2^11/n))
+ *      for present symbols (0 otherwise); if they sum below 2^11 the
+ *      shortfall goes one each to the present symbols of largest remainder
+ *      h[s]*2^11 mod n (ties to the smaller symbol); if above, one is taken
+ *      repeatedly from the symbol of largest q (ties to the smaller symbol).
+ *    - Spread: symbols in increasing order, q[s] states each, visit states
+ *      0, 1283, 2*1283, ... modulo 2^11 (1283 is odd, so every state once).
+ *    - A symbol s seen at state x in [0, 2^11) has rank r = number of states
+ *      below x that hold s; decoding at X = 2^11 + x outputs s, forms
+ *      y = q[s] + r, reads nb = 11 - floor(log2 y) bits v (value bit 0 first)
+ *      and moves to X = y*2^nb + v.  Encoding runs the segment backwards from
+ *      X = 2^11: for s it emits the nb low bits of X with X >> nb in
+ *      [q[s], 2q[s]) and moves to 2^11 + (the (X>>nb) - q[s])-th state of s.
+ *      A segment's bits are its final state minus 2^11 (11 bits), then the
+ *      emitted bits in decoding order (the first symbol's first), so it
+ *      decodes forward from that state and must end at 2^11 having read
+ *      exactly its bit length.
+ *    - Mode TANS (4) when its section is smaller than the raw one (ties to
+ *      RAW); one distinct symbol is CONST as always.  Section: head, a
+ *      presence mask of A bits (bit s of byte s/8), u16 q[s] of each present
+ *      symbol in increasing order, u16 bit length per segment, pad 16,
+ *      payload (4*ceil(bits/32) bytes, segments bit-contiguous), pad 16.
  * ---------------------------------------------------------------------------
  */
 #include "zno.h"
@@ -375,21 +402,194 @@ static int get_bit(bitr *r, unsigned *bit) {
 }
 
 /* ------------------------------------------------------------------ */
+/* R8: tabled asymmetric numeral systems                               */
+/* ------------------------------------------------------------------ */
+#define TL (1u << ZNO_TANS_LOG)
+#define TSTEP 1283u
+
+int zno_tans_normalize(const uint64_t *h, int A, uint32_t *q) {
+  uint64_t n = 0;
+  int d = 0;
+  if (A < 1 || A > 256) return ZNO_ERR_ARG;
+  for (int s = 0; s < A; s++) {
+    n += h[s];
+    d += h[s] != 0;
+  }
+  if (n == 0) return ZNO_ERR_ARG;
+  int64_t sum = 0;
+  for (int s = 0; s < A; s++) {
+    q[s] = 0;
+    if (!h[s]) continue;
+    uint64_t f = h[s] * TL / n;
+    q[s] = f ? (uint32_t)f : 1u;
+    sum += q[s];
+  }
+  /* shortfall: one each to the largest remainders (at most d of them) */
+  if (sum < (int64_t)TL) {
+    /* the floors lose less than one per present symbol, so the shortfall is
+       at most d: one pass over the d largest remainders covers it */
+    uint8_t given[256] = {0};
+    int64_t need = (int64_t)TL - sum;
+    for (int64_t k = 0; k < need; k++) {
+      int best = -1;
+      uint64_t br = 0;
+      for (int s = 0; s < A; s++) {
+        if (!h[s] || given[s]) continue;
+        uint64_t r = (h[s] * TL) % n;
+        if (best < 0 || r > br) {
+          best = s;
+          br = r;
+        }
+      }
+      if (best < 0) return ZNO_ERR_ARG;
+      given[best] = 1;
+      q[best]++;
+      sum++;
+    }
+  }
+  /* excess (from the symbols raised to 1): one at a time from the largest */
+  while (sum > (int64_t)TL) {
+    int best = -1;
+    for (int s = 0; s < A; s++)
+      if (q[s] > 1 && (best < 0 || q[s] > q[best])) best = s;
+    if (best < 0) return ZNO_ERR_ARG;
+    q[best]--;
+    sum--;
+  }
+  return d;
+}
+
+void zno_tans_spread(const uint32_t *q, int A, uint8_t *sym_of_state) {
+  uint32_t pos = 0;
+  for (int s = 0; s < A; s++)
+    for (uint32_t i = 0; i < q[s]; i++) {
+      sym_of_state[pos] = (uint8_t)s;
+      pos = (pos + TSTEP) & (TL - 1);
+    }
+}
+
+static int floor_log2(uint32_t y) {
+  int b = -1;
+  while (y) {
+    y >>= 1;
+    b++;
+  }
+  return b;
+}
+
+int64_t zno_tans_encode(const uint32_t *q, int A, const uint8_t *sym, uint64_t n, uint8_t *out,
+                        uint32_t *final_state) {
+  uint8_t spread[TL];
+  uint32_t first[257], cnt[256];
+  uint32_t *state_of = (uint32_t *)malloc(sizeof(uint32_t) * TL); /* [first[s] + k] = k-th state of s */
+  uint32_t *cval = (uint32_t *)malloc(sizeof(uint32_t) * (n ? n : 1));
+  uint8_t *cbits = (uint8_t *)malloc(n ? n : 1);
+  if (!state_of || !cval || !cbits) {
+    free(state_of), free(cval), free(cbits);
+    return ZNO_ERR_NOMEM;
+  }
+  zno_tans_spread(q, A, spread);
+  first[0] = 0;
+  for (int s = 0; s < A; s++) {
+    first[s + 1] = first[s] + q[s];
+    cnt[s] = 0;
+  }
+  for (uint32_t x = 0; x < TL; x++) {
+    int s = spread[x];
+    state_of[first[s] + cnt[s]++] = x;
+  }
+  /* backwards over the symbols, from the initial state 2^11 */
+  uint32_t X = TL;
+  int64_t total = 0;
+  for (uint64_t i = n; i-- > 0;) {
+    int s = sym[i];
+    if (s >= A || q[s] == 0) {
+      free(state_of), free(cval), free(cbits);
+      return ZNO_ERR_ARG;
+    }
+    int nb = 0;
+    while ((X >> nb) >= 2 * q[s]) nb++;
+    cval[i] = X & ((1u << nb) - 1u);
+    cbits[i] = (uint8_t)nb;
+    total += nb;
+    X = TL + state_of[first[s] + ((X >> nb) - q[s])];
+  }
+  *final_state = X - TL;
+  /* the bits in decoding order: the first symbol's first, value bit 0 first */
+  if (out) {
+    bitw bw = {out, 0};
+    for (uint64_t i = 0; i < n; i++) put_value(&bw, cval[i], cbits[i]);
+  }
+  free(state_of), free(cval), free(cbits);
+  return total;
+}
+
+/* Decodes n symbols of one segment from the bit reader br (positioned at the
+ * segment's first bit, ending at its last); spread and rank describe the
+ * states (rank[x]: states below x holding the same symbol). */
+static int tans_decode_segment(const uint32_t *q, const uint8_t *spread, const uint32_t *rank, bitr *br,
+                               uint32_t final_state, uint64_t n, uint8_t *sym, uint64_t stride_fn_unused) {
+  (void)stride_fn_unused;
+  uint32_t X = TL + final_state;
+  for (uint64_t i = 0; i < n; i++) {
+    uint32_t x = X - TL;
+    int s = spread[x];
+    uint32_t y = q[s] + rank[x];
+    int nb = ZNO_TANS_LOG - floor_log2(y);
+    uint32_t v = 0;
+    for (int k = 0; k < nb; k++) {
+      unsigned bit;
+      if (get_bit(br, &bit)) return ZNO_ERR_CORRUPT;
+      v |= (uint32_t)bit << k;
+    }
+    sym[i] = (uint8_t)s;
+    X = (y << nb) + v;
+  }
+  /* a valid segment ends where it began, having read exactly its bits */
+  if (X != TL || br->pos != br->end) return ZNO_ERR_CORRUPT;
+  return ZNO_OK;
+}
+
+/* The states' ranks of a spread table. */
+static void tans_ranks(const uint8_t *spread, uint32_t *rank) {
+  uint32_t seen[256] = {0};
+  for (uint32_t x = 0; x < TL; x++) rank[x] = seen[spread[x]]++;
+}
+
+int zno_tans_decode(const uint32_t *q, int A, const uint8_t *bits, uint64_t nbits,
+                    uint32_t final_state, uint64_t n, uint8_t *sym) {
+  uint8_t spread[TL];
+  uint32_t rank[TL];
+  uint64_t sum = 0;
+  for (int s = 0; s < A; s++) sum += q[s];
+  if (sum != TL || final_state >= TL) return ZNO_ERR_CORRUPT;
+  zno_tans_spread(q, A, spread);
+  tans_ranks(spread, rank);
+  bitr br = {bits, 0, nbits};
+  return tans_decode_segment(q, spread, rank, &br, final_state, n, sym, 0);
+}
+
+/* ------------------------------------------------------------------ */
 /* R5/R6: stream sections and chunk records                           */
 /* ------------------------------------------------------------------ */
 static uint64_t payload_bytes_of(int mode, int k, uint64_t n, uint64_t bits) {
-  if (mode == ZNO_HUFF || mode == ZNO_GROUP) return 4 * ((bits + 31) / 32);
+  if (mode == ZNO_HUFF || mode == ZNO_GROUP || mode == ZNO_TANS) return 4 * ((bits + 31) / 32);
   if (mode == ZNO_RAW) return (n * (uint64_t)k + 7) / 8;
   return 0;
 }
-static uint64_t head_bytes_of(int mode, int k, int nseg) {
+/* d: present symbols (used by TANS only) */
+static uint64_t head_bytes_d(int mode, int k, int nseg, int d) {
   uint64_t h = 8;
   if (mode == ZNO_HUFF) h += (uint64_t)(1 << k) / 2;
   if (mode == ZNO_HUFF || mode == ZNO_GROUP) h += 2 * (uint64_t)nseg;
+  if (mode == ZNO_TANS) h += (uint64_t)(1 << k) / 8 + 2 * (uint64_t)d + 2 * (uint64_t)nseg;
   return align16(h);
 }
+static uint64_t section_bytes_d(int mode, int k, uint64_t n, int nseg, uint64_t bits, int d) {
+  return head_bytes_d(mode, k, nseg, d) + align16(payload_bytes_of(mode, k, n, bits));
+}
 static uint64_t section_bytes(int mode, int k, uint64_t n, int nseg, uint64_t bits) {
-  return head_bytes_of(mode, k, nseg) + align16(payload_bytes_of(mode, k, n, bits));
+  return section_bytes_d(mode, k, n, nseg, bits, 0);
 }
 static uint64_t chunk_elems(int dt, uint32_t cb) { return cb / (uint32_t)esize(dt); }
 static uint64_t nchunks_of(int dt, uint64_t n, uint32_t cb) {
@@ -399,13 +599,23 @@ static uint64_t nchunks_of(int dt, uint64_t n, uint32_t cb) {
 
 /* Plans one coded stream of one chunk: histogram, mode and code lengths. */
 typedef struct {
-  int mode, aux, nseg;
+  int mode, aux, nseg, d;
   uint8_t len[256];
+  uint32_t q[256];  /* TANS: normalised counts */
   uint64_t bits;
 } stream_plan;
 
+/* The symbols of segment j of a stream of n symbols, in decoding order
+ * (strips j, j + nseg, ...); returns their number. */
+static uint64_t segment_symbols(const uint8_t *sym, uint64_t n, int nseg, int j, uint8_t *dst) {
+  uint64_t m = 0;
+  for (uint64_t q0 = (uint64_t)j * STRIP; q0 < n; q0 += (uint64_t)nseg * STRIP)
+    for (uint64_t i = q0; i < n && i < q0 + STRIP; i++) dst[m++] = sym[i];
+  return m;
+}
+
 static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8_t *group_len,
-                       int group_id, stream_plan *pl, int *escape) {
+                       int group_id, int coder, stream_plan *pl, int *escape) {
   uint64_t h[256] = {0};
   int A = 1 << k, d = 0, last = 0;
   for (uint64_t i = 0; i < n; i++) h[sym[i]]++;
@@ -415,6 +625,7 @@ static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8
       last = s;
     }
   memset(pl->len, 0, sizeof pl->len);
+  pl->d = d;
   pl->nseg = (int)((n + (uint64_t)S - 1) / (uint64_t)S);
   pl->bits = 0;
   pl->aux = 0;
@@ -445,6 +656,32 @@ static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8
     }
     if (escape) *escape = 1;
   }
+  if (coder == ZNO_CODER_TANS) {
+    /* tANS: exact size from encoding every segment (R8) */
+    int rc = zno_tans_normalize(h, A, pl->q);
+    if (rc < 0) return rc;
+    uint8_t *seg = (uint8_t *)malloc((size_t)n);
+    if (!seg) return ZNO_ERR_NOMEM;
+    uint64_t bits = 0;
+    for (int j = 0; j < pl->nseg; j++) {
+      uint64_t m = segment_symbols(sym, n, pl->nseg, j, seg);
+      uint32_t st;
+      int64_t b = zno_tans_encode(pl->q, A, seg, m, NULL, &st);
+      if (b < 0) {
+        free(seg);
+        return (int)b;
+      }
+      bits += ZNO_TANS_LOG + (uint64_t)b;   /* the state, then the emitted bits */
+    }
+    free(seg);
+    if (section_bytes_d(ZNO_TANS, k, n, pl->nseg, bits, d) < raw) {
+      pl->mode = ZNO_TANS;
+      pl->bits = bits;
+    } else {
+      pl->mode = ZNO_RAW;
+    }
+    return ZNO_OK;
+  }
   uint8_t len[256];
   int rc = zno_code_lengths(h, A, MAXLEN, len);
   if (rc < 0) return rc;
@@ -465,7 +702,7 @@ static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8
 static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k,
                              const stream_plan *pl) {
   int A = 1 << k;
-  uint64_t head = head_bytes_of(pl->mode, k, pl->nseg);
+  uint64_t head = head_bytes_d(pl->mode, k, pl->nseg, pl->d);
   uint64_t pay = payload_bytes_of(pl->mode, k, n, pl->bits);
   out[0] = (uint8_t)pl->mode;
   out[1] = (uint8_t)pl->aux;
@@ -487,6 +724,27 @@ static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k
           put_code(&bw, code[sym[i]], pl->len[sym[i]]);
       put_u16(q + 2 * j, (uint32_t)(bw.pos - b0));
     }
+  } else if (pl->mode == ZNO_TANS) {
+    for (int s = 0; s < A; s++)
+      if (pl->q[s]) q[s / 8] |= (uint8_t)(1u << (s % 8));
+    q += A / 8;
+    for (int s = 0; s < A; s++)
+      if (pl->q[s]) {
+        put_u16(q, pl->q[s]);
+        q += 2;
+      }
+    uint8_t *seg = (uint8_t *)malloc((size_t)n), *tmp = (uint8_t *)calloc((size_t)n * 2 + 8, 1);
+    for (int j = 0; j < pl->nseg && seg && tmp; j++) {
+      uint64_t m = segment_symbols(sym, n, pl->nseg, j, seg);
+      uint32_t st;
+      memset(tmp, 0, (size_t)n * 2 + 8);
+      int64_t b = zno_tans_encode(pl->q, A, seg, m, tmp, &st);
+      put_value(&bw, st, ZNO_TANS_LOG);
+      for (int64_t i = 0; i < b; i++) put_bit(&bw, (tmp[i >> 3] >> (i & 7)) & 1);
+      put_u16(q + 2 * j, (uint32_t)(ZNO_TANS_LOG + b));
+    }
+    free(seg);
+    free(tmp);
   } else if (pl->mode == ZNO_RAW) {
     for (uint64_t i = 0; i < n; i++) put_value(&bw, sym[i], k);
   }
@@ -495,7 +753,7 @@ static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k
 
 /* Encodes the record of one chunk of n elements; the record is zero-padded. */
 static int encode_record(int dt, const uint8_t *chunk, uint64_t n, const uint8_t *group_len,
-                         int group_id, uint8_t *rec, uint64_t cap, uint64_t *rec_bytes,
+                         int group_id, int coder, uint8_t *rec, uint64_t cap, uint64_t *rec_bytes,
                          int *escape, zno_stats *st) {
   int nc = ncoded(dt), S = segsyms(dt);
   uint8_t *sym = (uint8_t *)malloc((size_t)n * 4 + 1);
@@ -511,12 +769,12 @@ static int encode_record(int dt, const uint8_t *chunk, uint64_t n, const uint8_t
   if (escape) *escape = 0;
   for (int p = 0; p < nc; p++) {
     int rc = plan_stream(sym + (uint64_t)p * n, n, kbits(dt, p), S, p == 0 ? group_len : NULL,
-                         group_id, &pl[p], escape);
+                         group_id, p == 0 ? coder : ZNO_CODER_HUFFMAN, &pl[p], escape);
     if (rc < 0) {
       free(sym);
       return rc;
     }
-    total += section_bytes(pl[p].mode, kbits(dt, p), n, pl[p].nseg, pl[p].bits);
+    total += section_bytes_d(pl[p].mode, kbits(dt, p), n, pl[p].nseg, pl[p].bits, pl[p].d);
   }
   if (total > cap) {
     free(sym);
@@ -538,11 +796,17 @@ static int encode_record(int dt, const uint8_t *chunk, uint64_t n, const uint8_t
   return ZNO_OK;
 }
 
+int zno_encode_chunk2(int dt, const void *chunk, uint64_t n, const uint8_t *group_len, int group_id,
+                      int coder, void *rec, uint64_t cap, uint64_t *rec_bytes, int *escape) {
+  if (!valid_dtype(dt) || !rec_bytes || n == 0) return ZNO_ERR_ARG;
+  if (coder != ZNO_CODER_HUFFMAN && (coder != ZNO_CODER_TANS || group_len)) return ZNO_ERR_ARG;
+  return encode_record(dt, (const uint8_t *)chunk, n, group_len, group_id, coder, (uint8_t *)rec, cap,
+                       rec_bytes, escape, NULL);
+}
 int zno_encode_chunk(int dt, const void *chunk, uint64_t n, const uint8_t *group_len, int group_id,
                      void *rec, uint64_t cap, uint64_t *rec_bytes, int *escape) {
-  if (!valid_dtype(dt) || !rec_bytes || n == 0) return ZNO_ERR_ARG;
-  return encode_record(dt, (const uint8_t *)chunk, n, group_len, group_id, (uint8_t *)rec, cap,
-                       rec_bytes, escape, NULL);
+  return zno_encode_chunk2(dt, chunk, n, group_len, group_id, ZNO_CODER_HUFFMAN, rec, cap, rec_bytes,
+                           escape);
 }
 
 /* ------------------------------------------------------------------ */
@@ -941,7 +1205,14 @@ static int ts_matches(const zno_tableset *ts, int dt, const uint64_t *n, int T, 
 int zno_compress(int dt, const void *const *tensors, const uint64_t *n, int T, uint32_t cb,
                  const zno_tableset *ts, void *outv, uint64_t cap, uint64_t *out_bytes,
                  zno_stats *st) {
+  return zno_compress2(dt, tensors, n, T, cb, ts, ZNO_CODER_HUFFMAN, outv, cap, out_bytes, st);
+}
+
+int zno_compress2(int dt, const void *const *tensors, const uint64_t *n, int T, uint32_t cb,
+                  const zno_tableset *ts, int coder, void *outv, uint64_t cap, uint64_t *out_bytes,
+                  zno_stats *st) {
   if (!valid_dtype(dt) || !valid_chunk(cb) || T < 1 || !n || !outv || !out_bytes) return ZNO_ERR_ARG;
+  if (coder != ZNO_CODER_HUFFMAN && (coder != ZNO_CODER_TANS || (ts && ts->K > 0))) return ZNO_ERR_ARG;
   for (int t = 0; t < T; t++)
     if (n[t] && (!tensors || !tensors[t])) return ZNO_ERR_ARG;
   int grouped = ts && ts->K > 0;
@@ -1007,7 +1278,7 @@ int zno_compress(int dt, const void *const *tensors, const uint64_t *n, int T, u
         rc = ZNO_ERR_CAPACITY;
         break;
       }
-      rc = encode_record(dt, b + i0 * (uint64_t)esize(dt), m, grouped ? ts->len[g] : NULL, g,
+      rc = encode_record(dt, b + i0 * (uint64_t)esize(dt), m, grouped ? ts->len[g] : NULL, g, coder,
                          out + pos, cap - pos, &sz, &esc, st);
       if (rc < 0) break;
       if (st) st->escapes += (uint64_t)esc;
@@ -1057,10 +1328,71 @@ static int64_t decode_stream(const uint8_t *sec, const uint8_t *lim, uint64_t n,
   int mode = sec[0], aux = sec[1], nseg = (int)get_u16(sec + 2);
   uint64_t pay = get_u32(sec + 4);
   int want_seg = (int)((n + (uint64_t)S - 1) / (uint64_t)S);
-  if (mode > ZNO_GROUP || nseg != want_seg) return ZNO_ERR_CORRUPT;
-  uint64_t head = head_bytes_of(mode, k, nseg);
+  if (mode > ZNO_TANS || nseg != want_seg) return ZNO_ERR_CORRUPT;
+  int dpresent = 0;
+  if (mode == ZNO_TANS) {
+    if (lim - sec < 8 + A / 8) return ZNO_ERR_CORRUPT;
+    for (int s = 0; s < A; s++) dpresent += (sec[8 + s / 8] >> (s % 8)) & 1;
+  }
+  uint64_t head = head_bytes_d(mode, k, nseg, dpresent);
   if ((uint64_t)(lim - sec) < head + align16(pay)) return ZNO_ERR_CORRUPT;
   const uint8_t *payload = sec + head;
+  if (mode == ZNO_TANS) {
+    /* R8: counts of the present symbols summing to 2^11, each at least 1,
+       then each segment from its final state */
+    if (aux != 0) return ZNO_ERR_CORRUPT;
+    uint32_t q[256];
+    uint64_t sum = 0;
+    const uint8_t *qp = sec + 8 + A / 8;
+    for (int s = 0; s < A; s++) {
+      q[s] = 0;
+      if ((sec[8 + s / 8] >> (s % 8)) & 1) {
+        q[s] = get_u16(qp);
+        qp += 2;
+        if (q[s] == 0) return ZNO_ERR_CORRUPT;
+      }
+      sum += q[s];
+    }
+    if (sum != TL) return ZNO_ERR_CORRUPT;
+    const uint8_t *sbits = qp;
+    uint64_t total_bits = 0;
+    for (int j = 0; j < nseg; j++) total_bits += get_u16(sbits + 2 * j);
+    if (pay != 4 * ((total_bits + 31) / 32)) return ZNO_ERR_CORRUPT;
+    uint8_t spread[TL];
+    uint32_t rank[TL];
+    zno_tans_spread(q, A, spread);
+    tans_ranks(spread, rank);
+    uint8_t *seg = (uint8_t *)malloc((size_t)n);
+    if (!seg) return ZNO_ERR_NOMEM;
+    uint64_t seg_start = 0;
+    for (int j = 0; j < nseg; j++) {
+      uint64_t sb = get_u16(sbits + 2 * j);
+      bitr br = {payload, seg_start, seg_start + sb};
+      uint32_t st = 0;
+      for (int b = 0; b < ZNO_TANS_LOG; b++) {
+        unsigned bit;
+        if (get_bit(&br, &bit)) {
+          free(seg);
+          return ZNO_ERR_CORRUPT;
+        }
+        st |= (uint32_t)bit << b;
+      }
+      /* the segment's symbols: strips j, j + nseg, ... */
+      uint64_t m = 0;
+      for (uint64_t q0 = (uint64_t)j * STRIP; q0 < n; q0 += (uint64_t)nseg * STRIP)
+        for (uint64_t i = q0; i < n && i < q0 + STRIP; i++) m++;
+      if (tans_decode_segment(q, spread, rank, &br, st, m, seg, 0) < 0) {
+        free(seg);
+        return ZNO_ERR_CORRUPT;
+      }
+      m = 0;
+      for (uint64_t q0 = (uint64_t)j * STRIP; q0 < n; q0 += (uint64_t)nseg * STRIP)
+        for (uint64_t i = q0; i < n && i < q0 + STRIP; i++) sym[i] = seg[m++];
+      seg_start += sb;
+    }
+    free(seg);
+    return (int64_t)(head + align16(pay));
+  }
   if (mode == ZNO_CONST) {
     if (aux >= A || pay != 0) return ZNO_ERR_CORRUPT;
     for (uint64_t i = 0; i < n; i++) sym[i] = (uint8_t)aux;

@@ -36,13 +36,18 @@ extern "C" {
 enum { ZNO_BF16 = 0, ZNO_FP32 = 1, ZNO_FP8_E4M3 = 2, ZNO_FP4X2_E2M1 = 3 };
 enum { ZNO_OK = 0, ZNO_ERR_ARG = -1, ZNO_ERR_CORRUPT = -2, ZNO_ERR_CAPACITY = -3,
        ZNO_ERR_TABLESET = -4, ZNO_ERR_NOMEM = -6 };
-enum { ZNO_RAW = 0, ZNO_CONST = 1, ZNO_HUFF = 2, ZNO_GROUP = 3 };
+enum { ZNO_RAW = 0, ZNO_CONST = 1, ZNO_HUFF = 2, ZNO_GROUP = 3, ZNO_TANS = 4 };
+/* Coder of the exponent stream (stream 0) of chunks coded with their own
+ * table: canonical Huffman (the default) or tabled asymmetric numeral
+ * systems (tANS) with 2^11 states. */
+enum { ZNO_CODER_HUFFMAN = 0, ZNO_CODER_TANS = 1 };
+#define ZNO_TANS_LOG 11
 
 typedef struct zno_tableset zno_tableset;
 
 /* Per-call diagnostics (not part of the format). */
 typedef struct {
-  uint64_t mode_count[4][4];   /* [coded stream][mode] */
+  uint64_t mode_count[4][5];   /* [coded stream][mode] */
   uint64_t stream_bytes[4];    /* record bytes per coded stream, headers included */
   uint64_t payload_bits[4];    /* Huffman/raw payload bits per coded stream */
   uint64_t raw_plane_bytes;    /* always-raw section bytes */
@@ -57,12 +62,28 @@ int  zno_code_lengths(const uint64_t *hist, int alphabet, int max_len, uint8_t *
 int  zno_group_lengths(const uint64_t *hist, int alphabet, int max_len, uint8_t *len);
 void zno_canonical_codes(const uint8_t *len, int alphabet, int max_len, uint32_t *code);
 
+/* tANS steps: normalised counts (sum 2^11, at least 1 for every present
+ * symbol), the spread of symbols over the 2^11 states, and one segment's
+ * encoding (symbols in decoding order; returns its bit count, writes the
+ * final state minus 2^11, and the bits LSB-first to out when non-NULL). */
+int  zno_tans_normalize(const uint64_t *hist, int alphabet, uint32_t *q);
+void zno_tans_spread(const uint32_t *q, int alphabet, uint8_t *sym_of_state);
+int64_t zno_tans_encode(const uint32_t *q, int alphabet, const uint8_t *sym, uint64_t n,
+                        uint8_t *out, uint32_t *final_state);
+int  zno_tans_decode(const uint32_t *q, int alphabet, const uint8_t *bits, uint64_t nbits,
+                     uint32_t final_state, uint64_t n, uint8_t *sym);
+
 /* ---- container ---- */
 int zno_compress_bound(int dtype, const uint64_t *n_elems, int n_tensors, uint32_t chunk_bytes,
                        uint64_t *bound);
 int zno_compress(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,
                  uint32_t chunk_bytes, const zno_tableset *ts, void *out, uint64_t cap,
                  uint64_t *out_bytes, zno_stats *stats);
+/* zno_compress with a coder for the exponent stream (ZNO_CODER_*); tANS only
+ * without group tables (ZNO_ERR_ARG otherwise). */
+int zno_compress2(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,
+                  uint32_t chunk_bytes, const zno_tableset *ts, int coder, void *out, uint64_t cap,
+                  uint64_t *out_bytes, zno_stats *stats);
 int zno_header(const void *in, uint64_t in_bytes, int *dtype, int *n_tensors, uint64_t *n_total,
                uint32_t *chunk_bytes, uint32_t *n_chunks, uint64_t *total_bytes, uint64_t *ts_hash);
 int zno_decompress(const void *in, uint64_t in_bytes, const zno_tableset *ts, void *const *outs,
@@ -71,6 +92,8 @@ int zno_decompress(const void *in, uint64_t in_bytes, const zno_tableset *ts, vo
 /* One chunk record alone (for sampled checks of large containers). */
 int zno_encode_chunk(int dtype, const void *chunk, uint64_t n, const uint8_t *group_len /* or NULL */,
                      int group_id, void *rec, uint64_t cap, uint64_t *rec_bytes, int *escape);
+int zno_encode_chunk2(int dtype, const void *chunk, uint64_t n, const uint8_t *group_len, int group_id,
+                      int coder, void *rec, uint64_t cap, uint64_t *rec_bytes, int *escape);
 
 /* ---- NeuralZip-style setup ---- */
 int zno_setup(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,

@@ -20,7 +20,9 @@ LIB = os.path.join(HERE, "liboracle_zno.so")
 SRC = os.path.join(HERE, "zno.c")
 
 BF16, FP32, FP8_E4M3, FP4X2_E2M1 = 0, 1, 2, 3
-RAW, CONST, HUFF, GROUP = 0, 1, 2, 3
+RAW, CONST, HUFF, GROUP, TANS = 0, 1, 2, 3, 4
+CODER_HUFFMAN, CODER_TANS = 0, 1
+TANS_LOG = 11
 MAX_LEN = 11
 ELEM_DTYPE = {BF16: np.uint16, FP32: np.uint32, FP8_E4M3: np.uint8, FP4X2_E2M1: np.uint8}
 N_CODED = {BF16: 1, FP32: 4, FP8_E4M3: 2, FP4X2_E2M1: 2}
@@ -45,7 +47,7 @@ def build(force: bool = True) -> str:
 
 
 class _Stats(C.Structure):
-    _fields_ = [("mode_count", (C.c_uint64 * 4) * 4), ("stream_bytes", C.c_uint64 * 4),
+    _fields_ = [("mode_count", (C.c_uint64 * 5) * 4), ("stream_bytes", C.c_uint64 * 4),
                 ("payload_bits", C.c_uint64 * 4), ("raw_plane_bytes", C.c_uint64),
                 ("escapes", C.c_uint64)]
 
@@ -68,6 +70,13 @@ def lib():
         L.zno_canonical_codes.argtypes = [P, I, I, P]
         L.zno_compress_bound.argtypes = [I, PU64, I, U32, PU64]
         L.zno_compress.argtypes = [I, C.POINTER(P), PU64, I, U32, P, P, U64, PU64, C.POINTER(_Stats)]
+        L.zno_compress2.argtypes = [I, C.POINTER(P), PU64, I, U32, P, I, P, U64, PU64, C.POINTER(_Stats)]
+        L.zno_encode_chunk2.argtypes = [I, P, U64, P, I, I, P, U64, PU64, C.POINTER(I)]
+        L.zno_tans_normalize.argtypes = [PU64, I, P]
+        L.zno_tans_spread.argtypes = [P, I, P]
+        L.zno_tans_encode.argtypes = [P, I, P, U64, P, C.POINTER(U32)]
+        L.zno_tans_encode.restype = C.c_int64
+        L.zno_tans_decode.argtypes = [P, I, P, U64, U32, U64, P]
         L.zno_header.argtypes = [P, U64, C.POINTER(I), C.POINTER(I), PU64, C.POINTER(U32),
                                  C.POINTER(U32), PU64, PU64]
         L.zno_decompress.argtypes = [P, U64, P, C.POINTER(P), PU64, I]
@@ -142,9 +151,44 @@ def compress_bound(dtype: int, n_elems, chunk_bytes: int) -> int:
     return b.value
 
 
+def tans_normalize(hist) -> np.ndarray:
+    h = np.ascontiguousarray(np.asarray(hist, dtype=np.uint64))
+    q = np.zeros(h.size, np.uint32)
+    _check(lib().zno_tans_normalize(h.ctypes.data_as(C.POINTER(C.c_uint64)), h.size, _ptr(q)), "tans_normalize")
+    return q
+
+
+def tans_spread(q) -> np.ndarray:
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.uint32))
+    out = np.zeros(1 << TANS_LOG, np.uint8)
+    lib().zno_tans_spread(_ptr(q), q.size, _ptr(out))
+    return out
+
+
+def tans_encode(q, syms):
+    """One segment: (bits as a uint8 array, LSB-first; bit count; final state - 2^11)."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.uint32))
+    x = np.ascontiguousarray(np.asarray(syms, dtype=np.uint8))
+    out = np.zeros(2 * x.size + 8, np.uint8)
+    st = C.c_uint32()
+    nb = lib().zno_tans_encode(_ptr(q), q.size, _ptr(x), x.size, _ptr(out), C.byref(st))
+    _check(int(nb) if nb < 0 else 0, "tans_encode")
+    return out, int(nb), st.value
+
+
+def tans_decode(q, bits, nbits: int, state: int, n: int):
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.uint32))
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint8))
+    out = np.zeros(max(1, n), np.uint8)
+    rc = lib().zno_tans_decode(_ptr(q), q.size, _ptr(b), nbits, state, n, _ptr(out))
+    _check(rc, "tans_decode")
+    return out[:n]
+
+
 def compress(dtype: int, tensors, chunk_bytes: int = 262144, ts: "Tableset | None" = None,
-             with_stats: bool = False):
-    """Compresses a list of tensors (bit-pattern arrays) into one container."""
+             with_stats: bool = False, coder: int = CODER_HUFFMAN):
+    """Compresses a list of tensors (bit-pattern arrays) into one container;
+    coder selects Huffman or tANS for the exponent stream."""
     if isinstance(tensors, np.ndarray):
         tensors = [tensors]
     arrs = [np.ascontiguousarray(t, dtype=ELEM_DTYPE[dtype]).ravel() for t in tensors]
@@ -154,15 +198,15 @@ def compress(dtype: int, tensors, chunk_bytes: int = 262144, ts: "Tableset | Non
     ptrs = (C.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
     nb = C.c_uint64()
     st = _Stats()
-    rc = lib().zno_compress(dtype, ptrs, _u64arr(n), len(arrs), chunk_bytes,
-                            ts.handle if ts is not None else None, _ptr(out), cap, C.byref(nb),
-                            C.byref(st))
+    rc = lib().zno_compress2(dtype, ptrs, _u64arr(n), len(arrs), chunk_bytes,
+                             ts.handle if ts is not None else None, coder, _ptr(out), cap, C.byref(nb),
+                             C.byref(st))
     _check(rc, "compress")
     blob = out[: nb.value].copy()
     if not with_stats:
         return blob
     stats = {
-        "mode_count": [[int(st.mode_count[p][m]) for m in range(4)] for p in range(4)],
+        "mode_count": [[int(st.mode_count[p][m]) for m in range(5)] for p in range(4)],
         "stream_bytes": [int(v) for v in st.stream_bytes],
         "payload_bits": [int(v) for v in st.payload_bits],
         "raw_plane_bytes": int(st.raw_plane_bytes),
@@ -206,7 +250,8 @@ def decompress_status(blob: np.ndarray, n_elems, ts: "Tableset | None" = None) -
                                 _u64arr(n_elems), len(outs))
 
 
-def encode_chunk(dtype: int, chunk: np.ndarray, group_len=None, group_id: int = 0):
+def encode_chunk(dtype: int, chunk: np.ndarray, group_len=None, group_id: int = 0,
+                 coder: int = CODER_HUFFMAN):
     """Record bytes of one chunk (the container's record for it) and its escape flag."""
     x = np.ascontiguousarray(chunk, ELEM_DTYPE[dtype]).ravel()
     cap = 64 + 4 * (x.size * 4 + 4096)
@@ -217,8 +262,8 @@ def encode_chunk(dtype: int, chunk: np.ndarray, group_len=None, group_id: int = 
     if group_len is not None:
         gl_arr = np.ascontiguousarray(np.asarray(group_len, np.uint8))
         gl = _ptr(gl_arr)
-    _check(lib().zno_encode_chunk(dtype, _ptr(x), x.size, gl, group_id, _ptr(rec), cap,
-                                  C.byref(nb), C.byref(esc)), "encode_chunk")
+    _check(lib().zno_encode_chunk2(dtype, _ptr(x), x.size, gl, group_id, coder, _ptr(rec), cap,
+                                   C.byref(nb), C.byref(esc)), "encode_chunk")
     return rec[: nb.value].copy(), bool(esc.value)
 
 

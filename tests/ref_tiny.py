@@ -223,13 +223,147 @@ def segment_order(n, nseg, j):
     return out
 
 
-def section(mode, k, n, nseg, bits):
+TANS = 4
+TANS_LOG = 11
+TANS_STEP = 1283
+
+
+def section(mode, k, n, nseg, bits, d=0):
     head = 8 + ((1 << k) // 2 if mode == HUFF else 0) + (2 * nseg if mode in (HUFF, GROUP) else 0)
-    pay = 4 * ((bits + 31) // 32) if mode in (HUFF, GROUP) else ((n * k + 7) // 8 if mode == RAW else 0)
+    if mode == TANS:
+        head = 8 + (1 << k) // 8 + 2 * d + 2 * nseg
+    pay = 4 * ((bits + 31) // 32) if mode in (HUFF, GROUP, TANS) else ((n * k + 7) // 8 if mode == RAW else 0)
     return a16(head), pay
 
 
-def encode_stream(syms, k, S, group=None):
+# ----------------------------------------------------------------- tANS ----
+# Restated from the description of tabled asymmetric numeral systems (Duda):
+# a table of L = 2^11 states in which symbol s owns q[s] states; decoding a
+# state yields its symbol and, with the state's rank among that symbol's
+# states, the next state after reading a few bits; encoding runs backwards.
+def tans_normalize(h):
+    """Counts q with sum L, q >= 1 for present symbols (largest remainders
+    fill a shortfall, ties to the smaller symbol; an excess is taken one at a
+    time from the largest count, ties to the smaller symbol)."""
+    L = 1 << TANS_LOG
+    n = sum(h)
+    q = [0] * len(h)
+    for s, c in enumerate(h):
+        if c:
+            q[s] = max(1, c * L // n)
+    short = L - sum(q)
+    if short > 0:
+        ranked = sorted((s for s, c in enumerate(h) if c), key=lambda s: (-((h[s] * L) % n), s))
+        for s in ranked[:short]:
+            q[s] += 1
+    heap = [(-v, s) for s, v in enumerate(q) if v > 1]
+    heapq.heapify(heap)
+    while sum(q) > L:
+        v, s = heapq.heappop(heap)
+        q[s] -= 1
+        if q[s] > 1:
+            heapq.heappush(heap, (-q[s], s))
+    return q
+
+
+def tans_spread(q):
+    """State of the k-th visit is k*1283 mod L; visits go to symbols in
+    increasing order, q[s] each."""
+    L = 1 << TANS_LOG
+    owner = []
+    for s, v in enumerate(q):
+        owner.extend([s] * v)
+    spread = [0] * L
+    for k in range(L):
+        spread[(k * TANS_STEP) % L] = owner[k]
+    return spread
+
+
+def tans_encode_segment(q, syms):
+    """Returns (list of bits, decoding order, the 11 state bits first)."""
+    L = 1 << TANS_LOG
+    spread = tans_spread(q)
+    states = {}
+    for x in range(L):
+        states.setdefault(spread[x], []).append(x)
+    X = L
+    chunks = []
+    for s in reversed(syms):
+        nb = 0
+        while (X >> nb) >= 2 * q[s]:
+            nb += 1
+        chunks.append([(X >> i) & 1 for i in range(nb)])
+        X = L + states[s][(X >> nb) - q[s]]
+    bits = [((X - L) >> i) & 1 for i in range(TANS_LOG)]
+    for c in reversed(chunks):
+        bits.extend(c)
+    return bits
+
+
+def tans_decode_segment(q, bits, n):
+    L = 1 << TANS_LOG
+    spread = tans_spread(q)
+    rank, seen = [0] * L, {}
+    for x in range(L):
+        rank[x] = seen.get(spread[x], 0)
+        seen[spread[x]] = rank[x] + 1
+    pos = TANS_LOG
+    X = L + sum(b << i for i, b in enumerate(bits[:TANS_LOG]))
+    out = []
+    for _ in range(n):
+        x = X - L
+        s = spread[x]
+        y = q[s] + rank[x]
+        nb = TANS_LOG - (y.bit_length() - 1)
+        v = sum(b << i for i, b in enumerate(bits[pos:pos + nb]))
+        if len(bits[pos:pos + nb]) < nb:
+            raise ValueError("segment too short")
+        pos += nb
+        out.append(s)
+        X = (y << nb) + v
+    if X != L or pos != len(bits):
+        raise ValueError("segment does not end in the initial state")
+    return out
+
+
+def encode_stream_tans(syms, k, S):
+    """One stream section with the tANS coder (no group tables)."""
+    n = len(syms)
+    A = 1 << k
+    h = [0] * A
+    for s in syms:
+        h[s] += 1
+    nseg = (n + S - 1) // S
+    present = [s for s in range(A) if h[s]]
+    if len(present) == 1:
+        return encode_stream(syms, k, S)   # constant
+    q = tans_normalize(h)
+    segbits = [tans_encode_segment(q, [syms[i] for i in segment_order(n, nseg, j)]) for j in range(nseg)]
+    bits = sum(len(b) for b in segbits)
+    rh, rp = section(RAW, k, n, nseg, 0)
+    th, tp = section(TANS, k, n, nseg, bits, len(present))
+    if th + a16(tp) >= rh + a16(rp):
+        return encode_stream(syms, k, S, force_raw=True)
+    out = bytearray(th + a16(tp))
+    struct.pack_into("<BBHI", out, 0, TANS, 0, nseg, tp)
+    pos = 8
+    for s in present:
+        out[pos + s // 8] |= 1 << (s % 8)
+    pos += A // 8
+    for s in present:
+        struct.pack_into("<H", out, pos, q[s])
+        pos += 2
+    bw = Bits()
+    for j, b in enumerate(segbits):
+        struct.pack_into("<H", out, pos + 2 * j, len(b))
+        for bit in b:
+            bw.put(bit)
+    if tp:
+        out[th:th + tp] = bw.tobytes(tp)
+    return bytes(out)
+
+
+def encode_stream(syms, k, S, group=None, force_raw=False):
     """One stream section; group = (lengths, id) to try GROUP mode."""
     n = len(syms)
     A = 1 << k
@@ -253,7 +387,7 @@ def encode_stream(syms, k, S, group=None):
                 gh, gp = section(GROUP, k, n, nseg, bits)
                 if gh + a16(gp) < raw_size:
                     mode, aux, lens = GROUP, gid, list(gl)
-        if not tried:
+        if not tried and not force_raw:
             ln = package_merge(h)
             bits = sum(h[s] * ln[s] for s in range(A))
             hh, hp = section(HUFF, k, n, nseg, bits)
@@ -284,8 +418,9 @@ def encode_stream(syms, k, S, group=None):
     return bytes(out)
 
 
-def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0):
-    """tensors: lists of ints (bit patterns); groups: (lengths per group, map)."""
+def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0, tans=False):
+    """tensors: lists of ints (bit patterns); groups: (lengths per group, map);
+    tans: the exponent stream with the tANS coder."""
     T = len(tensors)
     ce = chunk_bytes // ESIZE[dt]
     nch = [(len(t) + ce - 1) // ce for t in tensors]
@@ -312,7 +447,10 @@ def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0):
                 grp = None
                 if groups is not None and p == 0:
                     grp = (groups[0][groups[1][c]], groups[1][c])
-                rec += encode_stream(planes[p], kbits(dt, p), SEG[dt], grp)
+                if tans and p == 0:
+                    rec += encode_stream_tans(planes[p], kbits(dt, p), SEG[dt])
+                else:
+                    rec += encode_stream(planes[p], kbits(dt, p), SEG[dt], grp)
             recs.append(rec)
             c += 1
     total = off_rec + sum(len(r) for r in recs) + 16

@@ -1,0 +1,173 @@
+"""Oracle pins for the tANS coder of the exponent stream.
+
+THEORY-599 (nucleation note on ZipNN), order-0 only / ZipNN Fig. 4: a
+finite-state-entropy (tabled asymmetric numeral systems) coder codes the
+exponents 0-2% smaller than Huffman.  The coder follows Duda's tabled ANS:
+what is pinned here is what the mathematics fixes --
+  * normalised counts sum to the table size, every present symbol keeps at
+    least one state, and (no clamping) each count is within one of h*L/n;
+  * the spread is a permutation giving each symbol exactly its count;
+  * decoding inverts encoding: exhaustively on tiny alphabets and strings,
+    and on random segments; a segment decodes back to the initial state;
+  * the coded size is the ideal sum of log2(L/q) over the symbols plus at
+    most a small per-symbol term, and at or below the Huffman size on
+    weight exponents by 0-2% (the note's band);
+  * the container bytes equal an independent Python restatement.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from lossless_float_weight_amd import workloads as W
+from tests import ref_tiny
+
+L = 1 << 11
+
+
+def _exponents(n, std=0.02, seed=0):
+    x = W.gaussian(n, 0.0, std, __import__("torch").bfloat16, "cpu", seed, 0)
+    return ((W.bits(x).numpy().astype(np.int64) >> 7) & 0xFF)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_normalised_counts(oracle, case):
+    rng = np.random.default_rng(case)
+    A = 256 if case % 2 == 0 else 16
+    d = int(rng.integers(1, A + 1))
+    h = np.zeros(A, np.uint64)
+    idx = rng.choice(A, d, replace=False)
+    if case % 3 == 0:        # many rare symbols next to dominant ones: the excess path
+        h[idx] = rng.integers(1, 3, d)
+        h[idx[0]] = 10 ** 7
+    else:
+        h[idx] = rng.integers(1, 100000, d)
+    q = oracle.tans_normalize(h).astype(np.int64)
+    assert q.sum() == L
+    assert np.all((q >= 1) == (h > 0))
+    assert q.tolist() == ref_tiny.tans_normalize([int(v) for v in h])
+    n = int(h.sum())
+    if np.all(h[h > 0].astype(np.float64) * L >= n):   # nothing clamped up to 1
+        ideal = h.astype(np.float64) * L / n
+        assert np.all(np.abs(q - ideal) < 1.0 + 1e-9)
+
+
+def test_spread_is_a_permutation(oracle):
+    rng = np.random.default_rng(5)
+    for A in (2, 16, 256):
+        h = rng.integers(0, 50, A).astype(np.uint64)
+        h[0] += 1
+        q = oracle.tans_normalize(h)
+        sp = oracle.tans_spread(q)
+        assert np.array_equal(np.bincount(sp, minlength=A)[:A], q)
+        assert sp.tolist() == ref_tiny.tans_spread([int(v) for v in q])
+    # the step is odd, so it visits every one of the 2^11 states
+    assert math.gcd(1283, L) == 1
+
+
+def test_exhaustive_round_trip_tiny(oracle):
+    # every string up to length 6 over 3 symbols, under two count vectors
+    for q3 in ([1024, 1023, 1], [683, 683, 682]):
+        q = np.array(q3, np.uint32)
+        for m in range(1, 7):
+            for syms in itertools.product(range(3), repeat=m):
+                bits, nb, st = oracle.tans_encode(q, syms)
+                assert st < L
+                back = oracle.tans_decode(q, bits, nb, st, m)
+                assert back.tolist() == list(syms)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_round_trip_and_cost_random_segments(oracle, seed):
+    rng = np.random.default_rng(seed)
+    e = _exponents(4096, seed=seed)
+    h = np.bincount(e, minlength=256).astype(np.uint64)
+    q = oracle.tans_normalize(h)
+    for n in (1, 7, 512, 4096):
+        seg = rng.permutation(e)[:n].astype(np.uint8)
+        bits, nb, st = oracle.tans_encode(q, seg)
+        assert np.array_equal(oracle.tans_decode(q, bits, nb, st, n), seg)
+        # ANS cost: each symbol costs log2(L/q) bits up to the state's
+        # fraction, so the total stays within a bit per symbol of the ideal
+        # and, over a long segment, within 0.5% of it
+        ideal = float(np.sum(np.log2(L / q[seg].astype(np.float64))))
+        assert abs(nb - ideal) <= 11 + 0.005 * ideal + (n if n < 100 else 0)
+        # the independent restatement emits the same bits
+        ref = ref_tiny.tans_encode_segment([int(v) for v in q], [int(v) for v in seg])
+        got = [int((bits[i >> 3] >> (i & 7)) & 1) for i in range(nb)]
+        assert ref[11:] == got and sum(b << i for i, b in enumerate(ref[:11])) == st
+
+
+def test_corrupt_segment_is_refused(oracle):
+    e = _exponents(2048, seed=9).astype(np.uint8)
+    h = np.bincount(e, minlength=256).astype(np.uint64)
+    q = oracle.tans_normalize(h)
+    bits, nb, st = oracle.tans_encode(q, e[:512])
+    with pytest.raises(oracle.OracleError):
+        oracle.tans_decode(q, bits, nb - 1, st, 512)      # one bit short
+    bad = bits.copy()
+    bad[0] ^= 1
+    try:
+        out = oracle.tans_decode(q, bad, nb, st, 512)
+        assert not np.array_equal(out, e[:512])
+    except oracle.OracleError:
+        pass
+
+
+def test_tans_beats_huffman_on_weight_exponents_by_the_pages_band(oracle):
+    # THEORY-599 / ZipNN Fig. 4: FSE 0-2% smaller than Huffman on exponents
+    x = W.single_bf16(1 << 20, device="cpu")[0][1]
+    arr = W.bits(x).numpy()
+    _, sh = oracle.compress(oracle.BF16, [arr], 262144, with_stats=True)
+    _, st = oracle.compress(oracle.BF16, [arr], 262144, with_stats=True, coder=oracle.CODER_TANS)
+    nch = -(-arr.nbytes // 262144)
+    assert st["mode_count"][0][oracle.TANS] == nch and sh["mode_count"][0][oracle.HUFF] == nch
+    gain = 1.0 - st["payload_bits"][0] / sh["payload_bits"][0]
+    assert 0.0 <= gain <= 0.02, gain
+
+
+@pytest.mark.parametrize("dt,n", [(0, 1), (0, 513), (0, 70001), (1, 4097), (2, 9000), (3, 5001)])
+def test_tans_containers_equal_restatement_and_round_trip(oracle, dt, n):
+    rng = np.random.default_rng(n)
+    if dt == 0:
+        x = W.bits(W.gaussian(n, 0.0, 0.02, __import__("torch").bfloat16, "cpu", n, 1)).numpy()
+    elif dt == 1:
+        x = rng.normal(0, 0.02, n).astype(np.float32).view(np.uint32)
+    else:
+        x = (rng.integers(0, 256, n).astype(np.uint8) & np.uint8(0x9F))
+    blob = oracle.compress(dt, [x], 16384, coder=oracle.CODER_TANS)
+    assert np.array_equal(oracle.decompress(blob, [n])[0], x)
+    if n <= 10000:
+        ref = ref_tiny.encode_container(dt, [[int(v) for v in x]], 16384, tans=True)
+        assert bytes(blob) == ref
+
+
+def test_tans_mode_rule(oracle):
+    # a near-uniform exponent stream codes no smaller than raw: RAW, ties
+    # included; a constant stream is CONST; a grouped plan refuses tANS
+    rng = np.random.default_rng(2)
+    e = rng.permutation(np.repeat(np.arange(256), 32)).astype(np.uint16)
+    x = (e << 7) | rng.integers(0, 128, e.size).astype(np.uint16)
+    _, st = oracle.compress(oracle.BF16, [x], 16384, with_stats=True, coder=oracle.CODER_TANS)
+    assert st["mode_count"][0][oracle.RAW] == 1
+    c = np.full(5000, 0x3F80, np.uint16)
+    _, st = oracle.compress(oracle.BF16, [c], 16384, with_stats=True, coder=oracle.CODER_TANS)
+    assert st["mode_count"][0][oracle.CONST] == 1
+    ts = oracle.setup(oracle.BF16, [x], 16384, 2)
+    with pytest.raises(oracle.OracleError):
+        oracle.compress(oracle.BF16, [x], 16384, ts, coder=oracle.CODER_TANS)
+
+
+def test_tans_container_corruption_never_crashes(oracle):
+    x = W.bits(W.single_bf16(40000, device="cpu")[0][1]).numpy()
+    blob = oracle.compress(oracle.BF16, [x], 16384, coder=oracle.CODER_TANS)
+    rng = np.random.default_rng(8)
+    refused = 0
+    for _ in range(200):
+        b = blob.copy()
+        b[int(rng.integers(0, b.size))] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        st = oracle.decompress_status(b, [x.size])
+        assert st in (0, -1, -2)
+        refused += st != 0
+    assert refused > 0
