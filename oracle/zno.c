@@ -1322,13 +1322,15 @@ int zno_header(const void *inv, uint64_t in_bytes, int *dt, int *T, uint64_t *nt
 /* Decodes one stream section of n symbols at sec (within [sec, lim)).
  * Returns the section size, or a negative status. */
 static int64_t decode_stream(const uint8_t *sec, const uint8_t *lim, uint64_t n, int k, int S,
-                             const zno_tableset *ts, int allow_group, uint8_t *sym) {
+                             const zno_tableset *ts, int allow_group, int allow_tans, uint8_t *sym) {
   int A = 1 << k;
   if (lim - sec < 16) return ZNO_ERR_CORRUPT;
   int mode = sec[0], aux = sec[1], nseg = (int)get_u16(sec + 2);
   uint64_t pay = get_u32(sec + 4);
   int want_seg = (int)((n + (uint64_t)S - 1) / (uint64_t)S);
   if (mode > ZNO_TANS || nseg != want_seg) return ZNO_ERR_CORRUPT;
+  /* R8: tANS codes the exponent stream (the first coded stream) only */
+  if (mode == ZNO_TANS && !allow_tans) return ZNO_ERR_CORRUPT;
   int dpresent = 0;
   if (mode == ZNO_TANS) {
     if (lim - sec < 8 + A / 8) return ZNO_ERR_CORRUPT;
@@ -1537,7 +1539,7 @@ int zno_decompress(const void *inv, uint64_t in_bytes, const zno_tableset *ts, v
       }
       const uint8_t *sec = in + r0;
       for (int p = 0; p < nc; p++) {
-        int64_t sz = decode_stream(sec, in + r1, m, kbits(dt, p), S, ts, grouped && p == 0,
+        int64_t sz = decode_stream(sec, in + r1, m, kbits(dt, p), S, ts, grouped && p == 0, p == 0,
                                    sym + (uint64_t)p * m);
         if (sz < 0) {
           rc = (int)sz;

@@ -504,6 +504,25 @@ def decode_container(blob, group_lengths_table=None):
                     head = 16
                     v = int.from_bytes(blob[pos + head:pos + head + pay], "little")
                     syms = [(v >> (i * k)) & (A - 1) for i in range(m)]
+                elif mode == TANS:
+                    assert p == 0
+                    present = [s for s in range(A) if (blob[q + s // 8] >> (s % 8)) & 1]
+                    q += A // 8
+                    cnt = [0] * A
+                    for s in present:
+                        cnt[s] = struct.unpack_from("<H", blob, q)[0]
+                        q += 2
+                    seg_bits = [struct.unpack_from("<H", blob, q + 2 * j)[0] for j in range(nseg)]
+                    head = a16(q + 2 * nseg - pos)
+                    v = int.from_bytes(blob[pos + head:pos + head + pay], "little")
+                    bitpos = 0
+                    syms = [None] * m
+                    for j in range(nseg):
+                        seg = [(v >> (bitpos + i)) & 1 for i in range(seg_bits[j])]
+                        bitpos += seg_bits[j]
+                        order = list(segment_order(m, nseg, j))
+                        for i, sy in zip(order, tans_decode_segment(cnt, seg, len(order))):
+                            syms[i] = sy
                 else:
                     if mode == HUFF:
                         lens = []

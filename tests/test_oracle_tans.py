@@ -171,3 +171,37 @@ def test_tans_container_corruption_never_crashes(oracle):
         assert st in (0, -1, -2)
         refused += st != 0
     assert refused > 0
+
+
+def test_restatement_decodes_the_oracles_tans_containers(oracle):
+    rng = np.random.default_rng(4)
+    for dt, n in ((0, 2500), (2, 3000), (3, 2049), (1, 700)):
+        if dt == 0:
+            x = W.bits(W.gaussian(n, 0.0, 0.02, __import__("torch").bfloat16, "cpu", dt, 2)).numpy()
+        elif dt == 1:
+            x = rng.normal(0, 0.02, n).astype(np.float32).view(np.uint32)
+        else:
+            x = rng.integers(0, 256, n).astype(np.uint8) & np.uint8(0x9F)
+        blob = oracle.compress(dt, [x], 4096, coder=oracle.CODER_TANS)
+        assert ref_tiny.decode_container(bytes(blob))[0] == [int(v) for v in x]
+
+
+def test_tans_outside_the_exponent_stream_is_refused(oracle):
+    # R8 gives tANS to the exponent stream only: a second stream marked TANS
+    # is refused even where its bytes would parse
+    import struct
+    rng = np.random.default_rng(6)
+    x = (rng.integers(0, 4, 8192).astype(np.uint8) << 3) | rng.integers(0, 2, 8192).astype(np.uint8)
+    blob = oracle.compress(oracle.FP8_E4M3, [x], 8192, coder=oracle.CODER_TANS)
+    off_dir = struct.unpack_from("<Q", blob, 40)[0]
+    r0 = struct.unpack_from("<Q", blob, off_dir)[0]
+    mode, aux, nseg, pay = struct.unpack_from("<BBHI", blob, r0)
+    assert mode == oracle.TANS
+    d = sum(bin(int(v)).count("1") for v in blob[r0 + 8:r0 + 10])
+    head, _ = ref_tiny.section(mode, 4, 8192, nseg, 0, d)
+    s1 = r0 + head + ((pay + 15) & ~15)
+    assert blob[s1] == oracle.HUFF
+    assert oracle.decompress_status(blob, [x.size]) == 0
+    bad = blob.copy()
+    bad[s1] = oracle.TANS
+    assert oracle.decompress_status(bad, [x.size]) == -2
