@@ -112,7 +112,7 @@ def make_tensors(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def _oracle_worker(path, lo, hi, dt, reps, barrier, q):
+def _oracle_worker(path, lo, hi, dt, reps, barrier, q, coder=0):
     """One process of the multi-core CPU baseline: compress + decompress of
     elements [lo, hi) of the sample, reps times, after all processes are ready."""
     import numpy as np
@@ -123,12 +123,12 @@ def _oracle_worker(path, lo, hi, dt, reps, barrier, q):
     barrier.wait()
     t0 = time.perf_counter()
     for _ in range(reps):
-        b = zno.compress(dt, [x])
+        b = zno.compress(dt, [x], coder=coder)
         ok &= bool(np.array_equal(zno.decompress(b, [x.size], dt)[0], x))
     q.put((time.perf_counter() - t0, ok))
 
 
-def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16):
+def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16, coder: int = 0):
     """The CPU oracle as it stands, compress + decompress of a prefix of the
     workload's tensors chosen to take about budget_s on one thread: first on
     one thread, then split by whole chunks over one process per host core (at
@@ -148,7 +148,7 @@ def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16):
     first = W.bits(tensors[0]).reshape(-1)
     probe = first[: (4 << 20) // esz].cpu().numpy()
     t0 = time.perf_counter()
-    b = zno.compress(dt, [probe])
+    b = zno.compress(dt, [probe], coder=coder)
     zno.decompress(b, [probe.size], dt)
     rate = probe.nbytes / max(time.perf_counter() - t0, 1e-6)
     want = rate * budget_s
@@ -160,7 +160,7 @@ def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16):
         sample.append(np.ascontiguousarray(W.bits(t).reshape(-1)[:take].cpu().numpy()))
         nbytes += sample[-1].nbytes
     t0 = time.perf_counter()
-    blob = zno.compress(dt, sample)
+    blob = zno.compress(dt, sample, coder=coder)
     t1 = time.perf_counter()
     outs = zno.decompress(blob, [s.size for s in sample], dt)
     t2 = time.perf_counter()
@@ -181,7 +181,7 @@ def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16):
         np.save(path, flat)
         ctx = mp.get_context("spawn")
         barrier, q = ctx.Barrier(len(spans)), ctx.Queue()
-        procs = [ctx.Process(target=_oracle_worker, args=(path, lo, hi, dt, reps, barrier, q))
+        procs = [ctx.Process(target=_oracle_worker, args=(path, lo, hi, dt, reps, barrier, q, coder))
                  for lo, hi in spans]
         for pr in procs:
             pr.start()
@@ -237,7 +237,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--coder", default="huffman", choices=("huffman", "tans"),
+                    help="exponent coder (tans: tabled ANS, plans without groups)")
     args = ap.parse_args()
+    if args.coder == "tans" and args.workload in ("model", "transfer"):
+        raise SystemExit("--coder tans takes a workload without group tables")
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this codec's path runs on a single MI355X and shards "
               f"by chunk ranges with no exchange during decode; --gpus {args.gpus} is not run.",
@@ -253,6 +257,7 @@ def main():
     from lossless_float_weight_amd import zn
 
     torch.cuda.set_device(0)
+    coder = zn.CODER_TANS if args.coder == "tans" else zn.CODER_HUFFMAN
     base = make_tensors(args.workload)
     unc = sum(t.numel() * t.element_size() for t in base)
     extra = {}
@@ -303,10 +308,10 @@ def main():
         })
     # first pass: container size (needed to hand decompress its input length)
     s0 = sets[0]
-    blob = zn.compress(ts, s0["ins"], out=s0["blob"], scratch=s0["cscr"], ptrs=s0["in_ptrs"])
+    blob = zn.compress2(ts, coder, s0["ins"], out=s0["blob"], scratch=s0["cscr"], ptrs=s0["in_ptrs"])
     nbytes = blob.numel()
     for s in sets[1:]:
-        zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"])
+        zn.compress2(ts, coder, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"])
 
     kernels = ("analyze", "pack", "decode")
     everything = ("analyze", "finish", "pack", "check", "decode")
@@ -325,7 +330,7 @@ def main():
         if kev is not None:
             for k, pair in kev.items():
                 zn.debug_kernel_events(k, *pair)
-        zn.compress(ts, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"], sync=False)
+        zn.compress2(ts, coder, s["ins"], out=s["blob"], scratch=s["cscr"], ptrs=s["in_ptrs"], sync=False)
         zn.decompress(ts, s["blob"][:nbytes], outs=s["outs"], scratch=s["dscr"], ptrs=s["out_ptrs"],
                       sync=False)
 
@@ -392,7 +397,7 @@ def main():
         avg = sum(kern_ms[k]) / len(kern_ms[k])
         gbps = algo[k] / (avg * 1e-3) / 1e9
         rl[k] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(k, args.workload),
+                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(k, args.workload + ("" if args.coder == "huffman" else "_tans")),
                  "kernel": f"k_{k}", "avg_ms": round(avg, 4), "algorithmic_bytes": algo[k],
                  "timed_in": "timed region" if k == dominant else f"breakdown pass ({nb_steps} steps)"}
     ms_step = total_ms / args.steps
@@ -410,7 +415,7 @@ def main():
         "vs_baseline": (round(value / BASELINE_VALUE, 4) if BASELINE_VALUE else None),
         "dtype": "u32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload], "uncompressed_bytes": unc,
+        "config": {"workload": WORKLOADS[args.workload], "coder": args.coder, "uncompressed_bytes": unc,
                    "container_bytes": nbytes, "chunk_bytes": CHUNK_BYTES, "tensors": len(base)},
         "decompress_GBps": round(unc / (med(dec_ms) * 1e-3) / 1e9, 2),
         "compress_GBps": round(unc / (med(comp_ms) * 1e-3) / 1e9, 2),
@@ -449,7 +454,7 @@ def main():
         del pblob, pscr
     line.update(extra)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(base)
+        line["cpu_baseline"] = cpu_baseline(base, coder=coder)
     print(json.dumps(line), flush=True)
 
 

@@ -67,6 +67,13 @@ typedef enum {
 
 /* A plan for a fixed list of tensor sizes: dtype, chunk size, the container
  * layout, and optionally K grouped code tables.  Library-owned. */
+/* Entropy coder of the exponent stream (zn_compress2).  ZN_CODER_TANS is the
+ * tabled asymmetric-numeral-system coder (FSE) that THEORY-599's order-0
+ * discussion reports, after ZipNN Fig. 4, as coding exponents 0-2% smaller
+ * than Huffman; it serves chunks coded with their own table (plans without
+ * groups).  The other coded fields keep their Huffman codes. */
+typedef enum { ZN_CODER_HUFFMAN = 0, ZN_CODER_TANS = 1 } zn_coder;
+
 typedef struct zn_tableset zn_tableset;
 
 /* zn_setup -- the reusable setup ("NeuralZip", Abstract).
@@ -136,9 +143,10 @@ zn_status zn_tableset_info(const zn_tableset *ts, zn_dtype *dtype, int *n_tensor
 zn_status zn_compress_bound(const zn_tableset *ts, uint64_t *bytes);
 
 /* Device scratch needed by zn_compress / zn_decompress for this plan: 256
- * control bytes, 8 bytes per chunk (record sizes) and a code plan of
- * 64 + 1024 bytes per coded field per chunk (the code chosen for each
- * stream): at 256 KiB chunks 1/240 of the input for BF16, 1/63 for FP32.
+ * control bytes, 8 bytes per chunk (record sizes) and a code plan per chunk
+ * of 64 + 1024 bytes per coded field (the code chosen for each stream) plus
+ * 2 bytes per segment of the exponent stream (tANS segment lengths): at
+ * 256 KiB chunks 1/163 of the input for BF16, 1/56 for FP32.
  * Decompression alone needs only the first 256 bytes. */
 zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes);
 
@@ -161,6 +169,21 @@ zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes);
 zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void *d_out,
                       uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
                       uint64_t scratch_bytes, hipStream_t stream);
+
+/* zn_compress2 -- zn_compress with the exponent stream's coder chosen
+ * (zn_coder; zn_compress is ZN_CODER_HUFFMAN).  With ZN_CODER_TANS each
+ * chunk's exponent stream gets normalised counts summing to 2^11 and is
+ * coded with tabled ANS (THEORY-599, order-0 discussion; ZipNN Fig. 4), when
+ * that section is smaller than the raw one; a constant stream stays constant.
+ * Every segment is encoded twice (once to size it, once to write it) and
+ * decoding takes one table step per symbol, so tANS trades speed for the
+ * pages' 0-2%.  Arguments, ownership, synchronisation and errors as
+ * zn_compress; ZN_ERR_ARG for an unknown coder or for ZN_CODER_TANS with a
+ * plan that has groups (group codes are Huffman codes).  zn_decompress reads
+ * either coder's containers. */
+zn_status zn_compress2(const zn_tableset *ts, int coder, const void *const *d_in_ptrs, void *d_out,
+                       uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
+                       uint64_t scratch_bytes, hipStream_t stream);
 
 /* zn_decompress -- exact reconstruction of every tensor of the container
  * (bit-to-bit: "NeuralZip: Reusable Setup for Fast Lossless Compression",

@@ -471,14 +471,22 @@ uint64_t plans_offset(const zn_tableset *ts) { return kCtlBytes + (8ull * ts->n_
 
 zn_status zn_scratch_bytes(const zn_tableset *ts, uint64_t *bytes) {
   if (!ts || !bytes) return ZN_ERR_ARG;
-  *bytes = plans_offset(ts) + uint64_t(ts->n_chunks) * plan_bytes(ts->dtype);
+  *bytes = plans_offset(ts) + uint64_t(ts->n_chunks) * plan_bytes(ts->dtype, ts->chunk_elems);
   return ZN_OK;
 }
 
 zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void *d_out,
                       uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
                       uint64_t scratch_bytes, hipStream_t stream) {
+  return zn_compress2(ts, ZN_CODER_HUFFMAN, d_in_ptrs, d_out, out_cap, out_bytes, d_scratch, scratch_bytes,
+                      stream);
+}
+
+zn_status zn_compress2(const zn_tableset *ts, int coder, const void *const *d_in_ptrs, void *d_out,
+                       uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
+                       uint64_t scratch_bytes, hipStream_t stream) {
   if (!ts || (!d_in_ptrs && ts->n_chunks) || !d_out || !d_scratch) return ZN_ERR_ARG;
+  if (coder != ZN_CODER_HUFFMAN && (coder != ZN_CODER_TANS || ts->K > 0)) return ZN_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_scratch) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15))
     return ZN_ERR_ARG;
   uint64_t need = 0;
@@ -495,7 +503,9 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   a.group_len = ts->d_len;
   a.out = static_cast<uint8_t *>(d_out);
   a.plans = scr + plans_offset(ts);
+  a.plan_stride = plan_bytes(ts->dtype, ts->chunk_elems);
   a.sizes = reinterpret_cast<unsigned long long *>(scr + sizes_offset());
+  a.coder = coder;
   HIPCHK(launch_analyze(ts->dtype, a, stream, g_ev_before[KAnalyze], g_ev_after[KAnalyze]));
   FinishArgs f;
   f.L = a.L;
@@ -511,8 +521,10 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
   pk.L = a.L;
   pk.in_ptrs = a.in_ptrs;
   pk.plans = a.plans;
+  pk.plan_stride = a.plan_stride;
   pk.out = a.out;
   pk.ctl = ctl;
+  pk.coder = coder;
   HIPCHK(launch_pack(ts->dtype, pk, stream, g_ev_before[KPack], g_ev_after[KPack]));
   if (!out_bytes) return ZN_OK;
   uint32_t flag = 0;

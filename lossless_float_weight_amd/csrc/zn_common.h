@@ -35,7 +35,13 @@ constexpr uint32_t kTsMagic = 0x53544E5Au;   // "ZNTS"
 constexpr int kVersion = 1;
 constexpr int kRounds = 8;            // Lloyd rounds of the grouped setup
 
-enum Mode { RAW = 0, CONST = 1, HUFF = 2, GROUP = 3 };
+enum Mode { RAW = 0, CONST = 1, HUFF = 2, GROUP = 3, TANS = 4 };
+// coder of the exponent stream, chosen per compression call
+enum Coder { CODER_HUFFMAN = 0, CODER_TANS = 1 };
+// tabled ANS (Duda): 2^11 states, spread with an odd step (every state once)
+constexpr int kTansLog = 11;
+constexpr uint32_t kTansStates = 1u << kTansLog;
+constexpr uint32_t kTansStep = 1283;
 enum DType { BF16 = 0, FP32 = 1, FP8 = 2, FP4X2 = 3 };
 
 __host__ __device__ constexpr int esize(int dt) { return dt == BF16 ? 2 : dt == FP32 ? 4 : 1; }
@@ -50,18 +56,22 @@ __host__ __device__ inline uint64_t rawplane_bytes(int dt, uint64_t n) {
   return dt == BF16 ? n : dt == FP8 ? (n + 7) / 8 : dt == FP4X2 ? (n + 3) / 4 : 0;
 }
 __host__ __device__ inline uint64_t payload_bytes_of(int mode, int k, uint64_t n, uint64_t bits) {
-  if (mode == HUFF || mode == GROUP) return 4 * ((bits + 31) / 32);
+  if (mode == HUFF || mode == GROUP || mode == TANS) return 4 * ((bits + 31) / 32);
   if (mode == RAW) return (n * uint64_t(k) + 7) / 8;
   return 0;
 }
-__host__ __device__ inline uint64_t head_bytes_of(int mode, int k, int nseg) {
+// d: symbols present (a TANS head stores a presence mask of 2^k bits and the
+// count of each present symbol)
+__host__ __device__ inline uint64_t head_bytes_of(int mode, int k, int nseg, int d = 0) {
   uint64_t h = 8;
   if (mode == HUFF) h += uint64_t(1 << k) / 2;
   if (mode == HUFF || mode == GROUP) h += 2 * uint64_t(nseg);
+  if (mode == TANS) h += uint64_t(1 << k) / 8 + 2 * uint64_t(d) + 2 * uint64_t(nseg);
   return align16(h);
 }
-__host__ __device__ inline uint64_t section_bytes(int mode, int k, uint64_t n, int nseg, uint64_t bits) {
-  return head_bytes_of(mode, k, nseg) + align16(payload_bytes_of(mode, k, n, bits));
+__host__ __device__ inline uint64_t section_bytes(int mode, int k, uint64_t n, int nseg, uint64_t bits,
+                                                 int d = 0) {
+  return head_bytes_of(mode, k, nseg, d) + align16(payload_bytes_of(mode, k, n, bits));
 }
 
 // Global-memory pointers.  Pointers read from device arrays are generic to
@@ -614,6 +624,217 @@ __device__ __attribute__((always_inline)) bool build_lut(const uint8_t *len, int
     if (own) lut[win(i)] = tv[i];
   __syncthreads();
   return true;
+}
+
+// ------------------------------------------------------------- tANS ----
+// The exponent coder of THEORY-599's order-0 discussion (ZipNN Fig. 4: a
+// finite-state-entropy coder, i.e. tabled asymmetric numeral systems, codes
+// exponents 0-2% smaller than Huffman), after Duda's tabled ANS:
+//   * counts q[s] normalised to sum 2^11: floor(h*2^11/n), at least 1 for a
+//     present symbol; a shortfall goes one each to the present symbols of
+//     largest remainder h*2^11 mod n (ties to the smaller symbol), an excess
+//     is taken one at a time from the largest count (ties to the smaller);
+//   * the i-th state handed out (symbols in increasing order, q[s] each) is
+//     state i*1283 mod 2^11;
+//   * a state x holding s has rank r among the states of s below it; decoding
+//     x outputs s, forms y = q[s] + r, reads nb = 11 - floor(log2 y) bits v
+//     (value bit 0 first) and goes to state (y << nb) + v - 2^11; encoding,
+//     backwards from state 2^11 (x = 0), emits the nb low bits of X = 2^11 + x
+//     with X >> nb in [q, 2q) and goes to the (X >> nb) - q -th state of s.
+
+// Workgroup LDS of the table construction.
+template <int NT>
+struct TansBuild {
+  uint8_t spread[kTansStates];      // symbol of each state
+  uint16_t cnt[NT / 64][256];       // states of each symbol met by each wave
+  uint16_t cum[260];                // first assignment index of each symbol
+  int ok;
+};
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t t = uint32_t(__shfl_xor(int(v), o, 64));
+    v = t > v ? t : v;
+  }
+  return v;
+}
+
+// Normalised counts q[0..A) of the histogram hist[0..A) of n > 0 symbols
+// (n <= 2^20, so h * 2^11 fits 32 bits), by one whole wave.  Returns the
+// number of present symbols.
+__device__ inline int wave_tans_normalize(const uint32_t *hist, int A, uint32_t n, uint32_t *q) {
+  const int ln = threadIdx.x & 63;
+  uint32_t h[4], c[4], rem[4];
+  bool given[4];
+  uint32_t part = 0;
+  int dl = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int s = ln + 64 * j;
+    h[j] = s < A ? hist[s] : 0u;
+    const uint32_t x = h[j] * kTansStates;
+    const uint32_t f = x / n;
+    c[j] = h[j] ? (f ? f : 1u) : 0u;
+    rem[j] = h[j] ? x - f * n : 0u;
+    given[j] = false;
+    part += c[j];
+    dl += h[j] != 0;
+  }
+  int sum = wave_sum(int(part));
+  const int d = wave_sum(dl);
+  // shortfall: the present symbols of largest remainder, one each (a key is
+  // remainder << 8 | (255 - s), plus one so that 0 means none)
+  while (sum < int(kTansStates)) {
+    uint32_t key = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t kj = (h[j] && !given[j]) ? ((rem[j] << 8) | uint32_t(255 - (ln + 64 * j))) + 1u : 0u;
+      key = kj > key ? kj : key;
+    }
+    key = wave_max_u32(key);
+    if (!key) break;   // no symbol left: cannot happen, the floors lose less than one each
+    const int s = 255 - int((key - 1u) & 255u);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      if (s == ln + 64 * j) {
+        c[j]++;
+        given[j] = true;
+      }
+    sum++;
+  }
+  // excess (symbols raised to 1): one at a time from the largest count
+  while (sum > int(kTansStates)) {
+    uint32_t key = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t kj = c[j] > 1 ? (c[j] << 8) | uint32_t(255 - (ln + 64 * j)) : 0u;
+      key = kj > key ? kj : key;
+    }
+    key = wave_max_u32(key);
+    if (!key) break;   // cannot happen: the excess is at most the symbols raised to 1
+    const int s = 255 - int(key & 255u);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      if (s == ln + 64 * j) c[j]--;
+    sum--;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    if (ln + 64 * j < A) q[ln + 64 * j] = c[j];
+  return d;
+}
+
+// The state tables of the counts q[0..A) (in LDS), by the whole workgroup of
+// NT threads.  Writes, where the pointer is not null:
+//   dec[x]   = s | nb << 8 | ((y << nb) - 2^11) << 12 for each state x (decoding);
+//   est[cum[s] + r] = x, the r-th state of s in increasing order (encoding);
+//   esym[s]  = q | nb0 << 12 | (cum - q + 2^11) << 16, nb0 = 11 - floor(log2 q)
+//              (0 for an absent symbol).
+// Returns false (uniformly) unless the counts sum to 2^11.
+template <int NT>
+__device__ bool tans_tables(const uint32_t *q, int A, TansBuild<NT> &B, uint32_t *dec, uint16_t *est,
+                            uint32_t *esym) {
+  constexpr int NW = NT / 64, SPW = int(kTansStates) / NW, PER = int(kTansStates) / NT;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  if (wv == 0) {
+    // cumulative counts: lane ln sums symbols 4 ln .. 4 ln + 3
+    uint32_t c4[4], part = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int s = 4 * ln + j;
+      c4[j] = s < A ? q[s] : 0u;
+      part += c4[j];
+    }
+    const uint32_t incl = wave_incl_scan(part);
+    uint32_t run = incl - part;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int s = 4 * ln + j;
+      if (s < A) B.cum[s] = uint16_t(run > 0xFFFFu ? 0xFFFFu : run);
+      run += c4[j];
+    }
+    const uint32_t total = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+    if (ln == 0) {
+      B.cum[A] = uint16_t(total > 0xFFFFu ? 0xFFFFu : total);
+      B.ok = total == kTansStates;
+    }
+  }
+  for (int i = tid; i < NW * 256; i += NT) (&B.cnt[0][0])[i] = 0;
+  __syncthreads();
+  if (!B.ok) return false;
+  // spread: assignment index i goes to state i*1283 mod 2^11
+  {
+    const int i0 = tid * PER;
+    int lo = 0, hi = A - 1;   // last s with cum[s] <= i0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (B.cum[mid] <= i0) lo = mid; else hi = mid - 1;
+    }
+    int s = lo;
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int i = i0 + k;
+      while (B.cum[s + 1] <= i) s++;
+      B.spread[(uint32_t(i) * kTansStep) & (kTansStates - 1)] = uint8_t(s);
+    }
+  }
+  __syncthreads();
+  // ranks: wave wv takes states [wv*SPW, (wv+1)*SPW) in batches of 64; a
+  // lane's rank within the wave is the wave's running count of its symbol
+  // plus the lanes below it holding the same symbol
+  constexpr int NB = SPW / 64;
+  uint32_t rl[NB], sy[NB];
+#pragma unroll
+  for (int b = 0; b < NB; b++) {
+    const int x = wv * SPW + b * 64 + ln;
+    const uint32_t s = B.spread[x];
+    uint64_t eq = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 8; bit++) {
+      const uint64_t m = __ballot((s >> bit) & 1);
+      eq &= ((s >> bit) & 1) ? m : ~m;
+    }
+    const uint32_t below = uint32_t(__popcll(eq & lanemask_lt()));
+    sy[b] = s;
+    rl[b] = B.cnt[wv][s] + below;
+    wave_lds_sync();
+    if (below == 0) B.cnt[wv][s] = uint16_t(B.cnt[wv][s] + __popcll(eq));
+    wave_lds_sync();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NB; b++) {
+    const int x = wv * SPW + b * 64 + ln;
+    const uint32_t s = sy[b];
+    uint32_t r = rl[b];
+    for (int w = 0; w < wv; w++) r += B.cnt[w][s];
+    const uint32_t qs = q[s];
+    if (dec) {
+      const uint32_t y = qs + r;                       // in [q, 2q)
+      const uint32_t nb = uint32_t(kTansLog) - (31u - uint32_t(__clz(int(y))));
+      dec[x] = s | (nb << 8) | (((y << nb) - kTansStates) << 12);
+    }
+    if (est) est[B.cum[s] + r] = uint16_t(x);
+  }
+  if (esym && tid < A) {
+    const uint32_t qs = q[tid];
+    const uint32_t nb0 = qs ? uint32_t(kTansLog) - (31u - uint32_t(__clz(int(qs)))) : 0u;
+    esym[tid] = qs ? qs | (nb0 << 12) | ((uint32_t(B.cum[tid]) - qs + kTansStates) << 16) : 0u;
+  }
+  __syncthreads();
+  return true;
+}
+
+// One encoding step from state X in [2^11, 2^12) for the symbol whose esym
+// entry is info: emits the nb low bits of X (returned: nb, and the bits in v)
+// and moves X on.
+__device__ __forceinline__ uint32_t tans_enc_step(uint32_t &X, uint32_t info, const uint16_t *est, uint32_t &v) {
+  const uint32_t qs = info & 0xFFFu, nb0 = (info >> 12) & 15u;
+  const uint32_t nb = nb0 - (X < (qs << nb0) ? 1u : 0u);
+  v = X & ((1u << nb) - 1u);
+  X = kTansStates + est[(X >> nb) + (info >> 16) - kTansStates];
+  return nb;
 }
 
 }  // namespace zn

@@ -48,6 +48,11 @@ struct DecShared {
   alignas(16) union {
     uint16_t t1[kLutSize];
     uint8_t stage[DEC_NT * STB];
+    struct {                 // a tANS stream's counts and table construction
+      uint32_t q[256];
+      int wc[DEC_NT / 64];
+      TansBuild<DEC_NT> tb;
+    } tq;
   } u;
   alignas(16) uint32_t ring[RING * DEC_NT];
   uint32_t lutm[SMALL1 ? (1 << kSmallBits) : 1];
@@ -55,6 +60,7 @@ struct DecShared {
   LutShared ls;
   int mode[NC], aux[NC];
   unsigned long long pay_off[NC], seg_off[NC];
+  unsigned long long tq_off;      // a tANS first stream: its presence mask
   uint32_t pay[NC];
   uint32_t wtot[DEC_NT / 64][NC];   // [wave][coded stream index]
   int bad;
@@ -198,9 +204,16 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       const uint32_t h0 = *reinterpret_cast<const uint32_t *>(in + pos);
       const uint32_t pay = *reinterpret_cast<const uint32_t *>(in + pos + 4);
       const int mode = h0 & 0xFF, aux = (h0 >> 8) & 0xFF, ns = h0 >> 16;
-      if (mode > GROUP || ns != nseg) { bad = 1; break; }
-      const uint64_t head = head_bytes_of(mode, k, nseg);
+      // tANS codes the exponent stream (the first) only
+      if (mode > TANS || ns != nseg || (mode == TANS && p != 0)) { bad = 1; break; }
+      int dp = 0;   // tANS: symbols present, from the mask of A bits
+      if (mode == TANS) {
+        if (pos + 8 + A / 8 > r1) { bad = 1; break; }
+        for (int b = 0; b < A / 8; b++) dp += __popc(in[pos + 8 + b]);
+      }
+      const uint64_t head = head_bytes_of(mode, k, nseg, dp);
       if (pos + head + align16(pay) > r1) { bad = 1; break; }
+      if (mode == TANS && (aux != 0 || pay == 0 || (pay & 3))) bad = 1;
       if (mode == CONST && (aux >= A || pay != 0)) bad = 1;
       if (mode == RAW && (aux != 0 || pay != (uint64_t(n) * k + 7) / 8)) bad = 1;
       if (mode == HUFF && (aux != 0 || pay == 0 || (pay & 3))) bad = 1;
@@ -215,7 +228,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       sh.aux[p] = aux;
       sh.pay[p] = pay;
       sh.pay_off[p] = pos + head;
-      sh.seg_off[p] = pos + 8 + (mode == HUFF ? A / 2 : 0);
+      sh.seg_off[p] = pos + 8 + (mode == HUFF ? A / 2 : 0) + (mode == TANS ? A / 8 + 2 * dp : 0);
+      if (mode == TANS) sh.tq_off = pos + 8;
       pos += head + align16(pay);
     }
     if (!bad && !tsbad && pos != r1) bad = 1;
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   int ncc = 0, codedm = 0, rawm = 0, constm = 0;
 #pragma unroll
   for (int p = 0; p < NC; p++) {
-    const bool cod = sh.mode[p] == HUFF || sh.mode[p] == GROUP;
+    const bool cod = sh.mode[p] == HUFF || sh.mode[p] == GROUP || sh.mode[p] == TANS;
     codedm |= int(cod) << p;
     ncc += int(cod);
     rawm |= int(sh.mode[p] == RAW) << p;
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
     const int ci = ln / spw, sj = wv * spw + ln % spw;
     if (ci < ncc && sj < nseg) {
       const int pc = nth_coded(ci);
-      if (spec && pc == 0 && sj == tid) sbits0 = sh.mode[0] == HUFF ? sbh0 : sbg0;
+      if (spec && pc == 0 && sj == tid && sh.mode[0] != TANS) sbits0 = sh.mode[0] == HUFF ? sbh0 : sbg0;
       else sbits0 = ldg2(in + sh.seg_off[pc] + 2 * sj);
     }
   }
@@ -300,6 +314,25 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       const uint32_t *gl = a.group_lut + size_t(sh.aux[p]) * kLutSize;
       for (int i = tid; i < kLutSize; i += DEC_NT) sh.lut[DecShared<DT>::SMALL1 ? 0 : p][i] = ldg4(gl + i);
       if (tid < A) sh.len[p][tid] = ldg1(a.group_len + sh.aux[p] * 256 + tid);
+    } else if (mode == TANS) {
+      // the counts: the mask's present symbols take the stored values in
+      // symbol order, each at least 1; the table needs their sum to be 2^11
+      auto &T = sh.u.tq;
+      const uint8_t *mk = in + sh.tq_off;
+      const bool pres = tid < A && ((ldg1(mk + (tid >> 3)) >> (tid & 7)) & 1);
+      const uint64_t m = __ballot(pres);
+      if (ln == 0) T.wc[wv] = __popcll(m);
+      __syncthreads();
+      uint32_t idx = uint32_t(__popcll(m & lanemask_lt()));
+      for (int w = 0; w < wv; w++) idx += uint32_t(T.wc[w]);
+      const uint32_t qv = pres ? ldg2(mk + A / 8 + 2 * idx) : 0u;
+      if (tid < A) T.q[tid] = qv;
+      const int zero = __syncthreads_or(pres && qv == 0);
+      const bool ok = tans_tables<DEC_NT>(T.q, A, T.tb, sh.lut[0], nullptr, nullptr);
+      if (zero || !ok) {
+        if (tid == 0) atomicOr(&a.ctl[0], kErrCorrupt);
+        return;
+      }
     }
   }
   __syncthreads();
@@ -336,8 +369,9 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   auto cfield = [&](int p) -> uint64_t { return 0x0101010101010101ull * uint64_t(sh.aux[p]); };
 
   int bad = 0;
-  auto path = [&](auto spw_c, auto rawf_c, auto allc_c, auto rawm_c, auto constm_c) {
+  auto path = [&](auto spw_c, auto rawf_c, auto allc_c, auto rawm_c, auto constm_c, auto tans_c) {
     constexpr int SPW = decltype(spw_c)::value;   // lanes per coded stream per wave
+    constexpr bool TANS0 = decltype(tans_c)::value; // the first stream is tANS-coded
     constexpr bool RAWF = decltype(rawf_c)::value; // some stream is stored raw
     constexpr bool ALLC = decltype(allc_c)::value; // every stream is coded
     // RAWM != 0: stream p is raw if bit p of RAWM is set, constant if bit p
@@ -444,6 +478,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         nb = 32 - int(b0 & 31);
       }
       int ov = 0;         // symbols of the next strip decoded early (staged words 8, 9)
+      uint32_t tx = 0;    // tANS: the lane's state minus 2^11
       uint64_t cur = 0;   // staged bytes not yet stored whole: those of the word at a, then the next
       // Raw bits and raw-stream fields merged by this lane in round r: the
       // same loads every round (an empty vector reads element 0 and is
@@ -500,7 +535,60 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           nsec++;
           pend = false;
         }
-        if (lim > 0) {
+        if (TANS0 && p == 0 && lim > 0) {
+          // tANS: one table step per symbol.  The segment opens with the
+          // encoder's final state (11 bits); each step reads the state's
+          // entry (symbol, bit count, base of the next state) and adds the
+          // next bits to the base.  The window takes a word whenever fewer
+          // than 22 bits remain (two steps need at most 22), so, as for the
+          // Huffman lanes, a round reads at most 12 words.  Symbols are staged
+          // four to a word at bytes 0..lim of the lane's staging area.
+          const uint32_t abase = uint32_t(tid * STB);
+          uint32_t *const stw = reinterpret_cast<uint32_t *>(sh.u.stage);
+          pre = rp[__builtin_amdgcn_ubfe(wpos, 0, 5) * DEC_NT];
+          auto refill = [&](int below) {
+            const bool need = nb < below;
+            W |= uint64_t(need ? pre : 0u) << (nb + 2);
+            nb += need ? 32 : 0;
+            wpos += need ? 1u : 0u;
+            pre = rp[__builtin_amdgcn_ubfe(wpos, 0, 5) * DEC_NT];
+          };
+          if (r == 0) {
+            refill(kTansLog);
+            tx = (uint32_t(W) >> 2) & (kTansStates - 1);
+            W >>= kTansLog;
+            nb -= kTansLog;
+          }
+          auto tstep = [&]() -> uint32_t {
+            const uint32_t e = lut[tx];
+            const uint32_t kb = (e >> 8) & 15u;
+            tx = (e >> 12) + ((uint32_t(W) >> 2) & ((1u << kb) - 1u));
+            W >>= kb;
+            nb -= int(kb);
+            return e & 0xFFu;
+          };
+          uint32_t word = 0;
+          for (int i = 0; i < lim; i += 2) {
+            refill(22);
+            word |= tstep() << (8 * (i & 3));
+            if (i + 1 < lim) word |= tstep() << (8 * ((i + 1) & 3));
+            if ((i & 3) == 2 || i + 2 >= lim) {
+              stw[(abase + uint32_t(i & ~3)) >> 2] = word;
+              word = 0;
+            }
+          }
+          if (last) {
+            // exact end: the stored bit length used up, back in state 2^11
+            const uint64_t bpos = uint64_t(wpos - adj) * 32 - uint32_t(nb);
+            if (bpos != uint64_t(b0) + sbits || tx != 0) bad = 1;
+          } else if (((wpos + 11) >> 4) >= nsec && nsec <= slast) {
+            ps0 = grp(4 * nsec);
+            ps1 = grp(4 * nsec + 1);
+            ps2 = grp(4 * nsec + 2);
+            ps3 = grp(4 * nsec + 3);
+            pend = true;
+          }
+        } else if (lim > 0) {
           // Each lookup appends its (up to three) symbols, one byte each, to
           // the lane's staged bytes: they join the pending bytes of the
           // current word in cur, which is stored whole and aligned (single
@@ -698,27 +786,32 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   using I2 = std::integral_constant<int, 2>;
   using I12 = std::integral_constant<int, 12>;
   using I14 = std::integral_constant<int, 14>;
-  if (ncc == NC) {
-    if constexpr (NC == 1) path(I64{}, F{}, T{}, I0{}, I0{});
-    else if constexpr (NC == 2) path(I32{}, F{}, T{}, I0{}, I0{});
-    else path(I16{}, F{}, T{}, I0{}, I0{});
-  } else if constexpr (NC == 1) {
-    if (anyraw) path(I64{}, T{}, F{}, I0{}, I0{}); else path(I64{}, F{}, F{}, I0{}, I0{});
-  } else if constexpr (NC == 2) {
-    // usual FP8 weights: E4 coded, M3 raw
-    if (ncc == 1 && rawm == 2) path(I64{}, T{}, F{}, I2{}, I0{});
-    else if (anyraw) path(I64{}, T{}, F{}, I0{}, I0{});
-    else path(I64{}, F{}, F{}, I0{}, I0{});
-  } else {
-    // usual FP32 weights: exponent coded, the three fraction bytes raw, or
-    // the low two constant (values that are rounded BF16).  Any other mix
-    // takes 16 lanes per stream, whatever ncc is: few vectors per lane keep
-    // the registers of this rare case small.
-    if (ncc == 1 && rawm == 14) path(I64{}, T{}, F{}, I14{}, I0{});
-    else if (ncc == 1 && rawm == 2 && constm == 12) path(I64{}, T{}, F{}, I2{}, I12{});
-    else if (anyraw) path(I16{}, T{}, F{}, I0{}, I0{});
-    else path(I16{}, F{}, F{}, I0{}, I0{});
-  }
+  // the same layouts with the first stream tANS-coded or not
+  auto dispatch = [&](auto tc) {
+    if (ncc == NC) {
+      if constexpr (NC == 1) path(I64{}, F{}, T{}, I0{}, I0{}, tc);
+      else if constexpr (NC == 2) path(I32{}, F{}, T{}, I0{}, I0{}, tc);
+      else path(I16{}, F{}, T{}, I0{}, I0{}, tc);
+    } else if constexpr (NC == 1) {
+      if (anyraw) path(I64{}, T{}, F{}, I0{}, I0{}, tc); else path(I64{}, F{}, F{}, I0{}, I0{}, tc);
+    } else if constexpr (NC == 2) {
+      // usual FP8 weights: E4 coded, M3 raw
+      if (ncc == 1 && rawm == 2) path(I64{}, T{}, F{}, I2{}, I0{}, tc);
+      else if (anyraw) path(I64{}, T{}, F{}, I0{}, I0{}, tc);
+      else path(I64{}, F{}, F{}, I0{}, I0{}, tc);
+    } else {
+      // usual FP32 weights: exponent coded, the three fraction bytes raw, or
+      // the low two constant (values that are rounded BF16).  Any other mix
+      // takes 16 lanes per stream, whatever ncc is: few vectors per lane keep
+      // the registers of this rare case small.
+      if (ncc == 1 && rawm == 14) path(I64{}, T{}, F{}, I14{}, I0{}, tc);
+      else if (ncc == 1 && rawm == 2 && constm == 12) path(I64{}, T{}, F{}, I2{}, I12{}, tc);
+      else if (anyraw) path(I16{}, T{}, F{}, I0{}, I0{}, tc);
+      else path(I16{}, F{}, F{}, I0{}, I0{}, tc);
+    }
+  };
+  if (sh.mode[0] == TANS) dispatch(T{});
+  else dispatch(F{});
   if (bad) atomicOr(&a.ctl[0], kErrCorrupt);
 }
 

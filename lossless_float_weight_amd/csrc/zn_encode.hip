@@ -36,8 +36,10 @@ constexpr int PACK_NT = 256, PACK_NW = PACK_NT / 64;
 //   u64 bits[4] (payload bits per coded stream), u32 sec_off[4] (offset of
 //   each stream's section in the record), u8 mode[4], u8 aux[4], pad to 64,
 //   then u32 enc[ncoded][256] (bit-reversed code | length << 16) for the
-//   streams coded with a Huffman or group code.
-__host__ __device__ constexpr uint64_t plan_stride(int dt) { return 64 + 1024ull * ncoded(dt); }
+//   streams coded with a Huffman or group code, or the normalised counts of
+//   a tANS-coded stream; then (tANS) the u16 bit length of each segment of
+//   the first stream.
+__host__ __device__ constexpr uint64_t plan_fixed(int dt) { return 64 + 1024ull * ncoded(dt); }
 
 template <int DT, int P>
 __device__ __forceinline__ uint32_t field(uint32_t w) {
@@ -113,14 +115,112 @@ __device__ __forceinline__ uint32_t mant4(uint32_t x) {
   }
 }
 
+// LDS of a tANS encoder: table construction, then the state of each
+// (symbol, rank) and each symbol's step constants.
+template <int NT>
+struct TansEnc {
+  TansBuild<NT> tb;
+  uint16_t est[kTansStates];
+  uint32_t esym[256];
+};
+
+// Encodes segment j of the first coded stream of a chunk of n elements at
+// src with tANS, backwards: its strips j + r*nseg (32 elements each) from the
+// last to the first, each from its last element.  emit(v, nb) receives each
+// symbol's bits in that order.  Returns the final state minus 2^11.  The next
+// strip's 16-byte vectors load while the current one is encoded.
+template <int DT, class Emit>
+__device__ __forceinline__ uint32_t tans_encode_segment(const uint8_t *src, uint32_t n, bool aligned, int nseg,
+                                                        int j, const uint32_t *esym, const uint16_t *est,
+                                                        Emit &&emit) {
+  constexpr int ES = esize(DT), VE = 16 / ES, NQ = 32 * ES / 16;
+  const uint32_t nstrips = (n + 31) / 32;
+  uint32_t X = kTansStates;
+  auto load = [&](uint32_t q, u32x4 (&v)[NQ]) {
+    const uint32_t eb = q * 32;
+    if (aligned && eb + 32 <= n) {
+#pragma unroll
+      for (int i = 0; i < NQ; i++) v[i] = ldg16(src + uint64_t(eb) * ES + 16 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NQ; i++) v[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 32; e++) {
+        const uint32_t w = eb + e < n ? load_elem<DT>(src + uint64_t(eb + e) * ES) : 0u;
+        const int b = e * ES;
+        v[b >> 4][(b >> 2) & 3] |= w << ((b & 3) * 8);
+      }
+    }
+  };
+  if (uint32_t(j) >= nstrips) return 0;   // not reached: a stream has no more segments than strips
+  const uint32_t ql = uint32_t(j) + (nstrips - 1 - uint32_t(j)) / uint32_t(nseg) * uint32_t(nseg);
+  u32x4 cur[NQ], nxt[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; i++) nxt[i] = u32x4{0, 0, 0, 0};
+  load(ql, cur);
+  for (int64_t q = ql; q >= j; q -= nseg) {
+    if (q - nseg >= j) load(uint32_t(q - nseg), nxt);
+    const uint32_t eb = uint32_t(q) * 32;
+    const uint32_t lim = n - eb < 32 ? n - eb : 32u;
+#pragma unroll
+    for (int e = 31; e >= 0; e--) {
+      if (uint32_t(e) < lim) {
+        const u32x4 c4 = cur[e / VE];
+        const uint32_t s = field<DT, 0>(vec_elem<DT>(make_uint4(c4[0], c4[1], c4[2], c4[3]), e % VE));
+        uint32_t v;
+        const uint32_t nb = tans_enc_step(X, esym[s], est, v);
+        emit(v, nb);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; i++) cur[i] = nxt[i];
+  }
+  return X - kTansStates;
+}
+
+// Writes one segment's bits [b0, b1) of a payload backwards, as tANS emits
+// them: acc holds words T-1 (low half) and T (high half), and word T goes out
+// once the bits reach below word T-1.  Words the segment shares with its
+// neighbours (or with the end of the payload) were cleared beforehand and
+// take an atomic OR; the others a plain store.
+struct BackWriter {
+  uint32_t *pw;
+  int32_t b0, b1, cur, T;
+  uint64_t acc;
+  __device__ BackWriter(uint32_t *p, int32_t lo, int32_t hi)
+      : pw(p), b0(lo), b1(hi), cur(hi), T((hi - 1) >> 5), acc(0) {}
+  __device__ __forceinline__ void word(int32_t w, uint32_t x) {
+    const bool shared = (w == (b0 >> 5) && (b0 & 31)) || (w == ((b1 - 1) >> 5) && (b1 & 31));
+    if (shared) atomicOr(pw + w, x);
+    else stg4(pw + w, x);
+  }
+  __device__ __forceinline__ void put(uint32_t v, uint32_t nb) {
+    const int32_t pos = cur - int32_t(nb);
+    if (pos < 32 * (T - 1)) {
+      word(T, uint32_t(acc >> 32));
+      acc <<= 32;
+      T--;
+    }
+    acc |= uint64_t(v) << ((pos - 32 * (T - 1)) & 63);   // nb = 0 ORs nothing
+    cur = pos;
+  }
+  __device__ __forceinline__ void finish() {
+    word(T, uint32_t(acc >> 32));
+    if ((b0 >> 5) == T - 1) word(T - 1, uint32_t(acc));
+  }
+};
+
 template <int DT>
 struct PackShared {
   static constexpr int NC = ncoded(DT);
   static constexpr int G = pack_g(DT);
   // words of one tile at the longest codes, plus slack for the group ORs
   static constexpr int STAGE = (PACK_NW * G * segsyms(DT) * kMaxLen + 31) / 32 + 4;
-  uint32_t enc[NC][256];
-  uint32_t stage[2][STAGE];      // alternate tiles use alternate buffers
+  uint32_t enc[NC][256];         // tANS: the first stream's normalised counts
+  union {
+    uint32_t stage[2][STAGE];    // alternate tiles use alternate buffers
+    TansEnc<PACK_NT> tans;       // a tANS stream's tables (no tiles meanwhile)
+  } su;
   uint32_t wtot[2][PACK_NW];
   // 1-byte elements: one tile's words of a raw stream (32 strips per segment,
   // up to 4 words per strip), written from the coded stream's tiles
@@ -149,7 +249,7 @@ struct EncShared {
   static constexpr bool PACK16 = DT == BF16;
   static constexpr int PRIVW = PACK16 ? APRIV * COLS / 2 : APRIV * COLS;
   uint32_t hist[NC][256];
-  uint32_t enc[NC][256];
+  uint32_t enc[NC][256];   // tANS: the first stream's normalised counts
   uint8_t len[NC][256];
   unsigned long long bits[NC];
   unsigned long long sec_off[NC + 1];
@@ -157,7 +257,7 @@ struct EncShared {
   unsigned long long rsum[NW];
   int icnt[NW];
   int cnt[4][kMaxLen + 1];
-  int need_block;
+  int need_block, need_tans, tans_d;
   union {
     uint32_t priv[PRIVW];
     struct {
@@ -165,6 +265,7 @@ struct EncShared {
       uint64_t hw[256];
     } cb;
     WaveCB wcb;
+    TansEnc<NT> tans;
   } u;
 };
 
@@ -210,8 +311,11 @@ __device__ __forceinline__ void count(EncShared<DT> &sh, int p, uint32_t b, int 
 
 // Steps 1 and 2 for chunk c: raw planes stored, histograms, and per coded
 // stream the mode, code and section offset in sh.  Returns the record size.
-template <int DT>
-__device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT> &sh, uint32_t c) {
+// TC: the exponent stream takes the tANS coder (chunks with their own
+// counts; no group tables), its segments' bit lengths going to segbits.
+template <int DT, bool TC>
+__device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT> &sh, uint32_t c,
+                                                  uint8_t *segbits) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int COLS = EncShared<DT>::COLS;
@@ -433,13 +537,18 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
         mq[q] = __ballot(hq[q] != 0);
         d += __popcll(mq[q]);
       }
-      int mode = RAW, aux = 0, need_block = 0;
+      int mode = RAW, aux = 0, need_block = 0, need_tans = 0;
       uint64_t bits = 0;
       if (d == 1) {
         mode = CONST;
 #pragma unroll
         for (int q = 3; q >= 0; q--)
           if (mq[q]) aux = 64 * q + __ffsll((long long)mq[q]) - 1;
+      } else if (TC && p == 0) {
+        // tANS: the counts here; the size needs every segment encoded (below)
+        const int dd = wave_tans_normalize(sh.hist[0], A, n, sh.enc[0]);
+        if (ln == 0) sh.tans_d = dd;
+        need_tans = 1;
       } else {
         bool escape = true;
         if (p == 0 && a.group_map) {
@@ -510,9 +619,31 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
         sh.aux[p] = aux;
         sh.bits[p] = bits;
         sh.need_block = need_block;
+        sh.need_tans = need_tans;
       }
     }
     __syncthreads();
+    if constexpr (TC) {
+      if (sh.need_tans) {
+        // one thread per segment encodes it backwards to count its bits
+        auto &T = sh.u.tans;
+        tans_tables<ENC_NT>(sh.enc[0], A, T.tb, nullptr, T.est, T.esym);
+        unsigned long long acc = 0;
+        for (int j = tid; j < nseg; j += ENC_NT) {
+          uint32_t nbits = kTansLog;   // the final state, then the symbols' bits
+          tans_encode_segment<DT>(src, n, aligned, nseg, j, T.esym, T.est,
+                                  [&](uint32_t, uint32_t nb) { nbits += nb; });
+          stg2(segbits + 2ull * j, nbits);
+          acc += nbits;
+        }
+        const unsigned long long bits = block_sum<DT>(sh, acc);
+        if (tid == 0) {
+          sh.mode[p] = section_bytes(TANS, k, n, nseg, bits, sh.tans_d) < raw ? TANS : RAW;
+          sh.bits[p] = bits;
+        }
+        __syncthreads();
+      }
+    }
     if (sh.need_block) {
       const uint32_t h = tid < A ? sh.hist[p][tid] : 0;
       if (tid < A) sh.u.cb.hw[tid] = h;
@@ -534,13 +665,13 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
       if (mode == RAW) sh.bits[p] = uint64_t(n) * k;
       sh.sec_off[p] = rec;
     }
-    rec += section_bytes(mode, k, n, nseg, mode == RAW ? 0 : sh.bits[p]);
+    rec += section_bytes(mode, k, n, nseg, mode == RAW ? 0 : sh.bits[p], mode == TANS ? sh.tans_d : 0);
     __syncthreads();
   }
   return rec;
 }
 
-template <int DT>
+template <int DT, bool TC>
 // BF16: at most 7 waves' worth of registers per SIMD, so that every chunk of a
 // large workload is resident at once (the scalar registers would otherwise
 // allow 6 workgroups per CU; the extra ones spill to vector-register lanes,
@@ -550,10 +681,11 @@ __global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT =
   __shared__ EncShared<DT> sh;
   const int tid = threadIdx.x;
   const uint32_t c = blockIdx.x;
-  const uint64_t rec = analyze_chunk<DT>(a, sh, c);
+  uint8_t *plan = a.plans + uint64_t(c) * a.plan_stride;
+  const uint64_t rec = analyze_chunk<DT, TC>(a, sh, c, plan + plan_fixed(DT));
 
-  // the plan: sizes and offsets, then the code words of coded streams
-  uint8_t *plan = a.plans + uint64_t(c) * plan_stride(DT);
+  // the plan: sizes and offsets, then the code words of coded streams (the
+  // counts of a tANS-coded one)
   if (tid == 0) a.sizes[c] = rec;
   if (tid < NC) {
     stg8(plan + 8 * tid, u32x2{uint32_t(sh.bits[tid]), uint32_t(sh.bits[tid] >> 32)});
@@ -563,20 +695,117 @@ __global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT =
   }
   for (int p = 0; p < NC; p++) {
     const int A = 1 << kbits(DT, p), mode = sh.mode[p];
-    if ((mode == HUFF || mode == GROUP) && tid < A) stg4(plan + 64 + 1024 * p + 4 * tid, sh.enc[p][tid]);
+    if ((mode == HUFF || mode == GROUP || mode == TANS) && tid < A)
+      stg4(plan + 64 + 1024 * p + 4 * tid, sh.enc[p][tid]);
   }
+}
+
+// The section of a tANS-coded first stream at sec: head (mode, segment
+// count, payload bytes), the presence mask and the counts of the present
+// symbols, the segment bit lengths (from the plan), then the payload, each
+// segment encoded backwards by one thread at the offset the scan of the
+// lengths gives it.  q: the counts (LDS); wtot: LDS scratch.
+template <int DT>
+__device__ void pack_tans(const uint8_t *src, uint32_t n, bool aligned, int nseg, uint8_t *sec, const uint32_t *q,
+                          int A, int k, uint64_t bits, const uint8_t *segbits, TansEnc<PACK_NT> &T,
+                          uint32_t (*wtot)[PACK_NW]) {
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  int d = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int s = ln + 64 * j;
+    d += __popcll(__ballot(s < A && q[s] != 0));
+  }
+  const uint64_t qoff = 8 + A / 8, soff = qoff + 2ull * d, head = head_bytes_of(TANS, k, nseg, d);
+  const uint64_t pay = payload_bytes_of(TANS, k, n, bits);
+  if (tid == 0) {
+    *reinterpret_cast<uint32_t *>(sec) = uint32_t(TANS) | (uint32_t(nseg) << 16);
+    *reinterpret_cast<uint32_t *>(sec + 4) = uint32_t(pay);
+  }
+  if (tid < A / 8) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int b = 0; b < 8; b++) m |= uint32_t(q[8 * tid + b] != 0) << b;
+    sec[8 + tid] = uint8_t(m);
+  }
+  if (wv == 0) {   // the counts of the present symbols, in symbol order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) cnt += uint32_t(4 * ln + j < A && q[4 * ln + j] != 0);
+    uint32_t idx = wave_incl_scan(cnt) - cnt;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int s = 4 * ln + j;
+      if (s < A && q[s] != 0) {
+        *reinterpret_cast<uint16_t *>(sec + qoff + 2 * idx) = uint16_t(q[s]);
+        idx++;
+      }
+    }
+  }
+  for (int j = tid; j < nseg; j += PACK_NT)
+    *reinterpret_cast<uint16_t *>(sec + soff + 2 * j) = uint16_t(ldg2(segbits + 2 * j));
+  for (uint64_t i = soff + 2ull * nseg + tid; i < head; i += PACK_NT) sec[i] = 0;
+  tans_tables<PACK_NT>(q, A, T.tb, nullptr, T.est, T.esym);
+  // segment bit offsets: a scan over rows of PACK_NT segments (a chunk of at
+  // most 1 MiB has at most 1024 segments per stream)
+  constexpr int MAXR = 1024 / PACK_NT;
+  uint32_t *pw = reinterpret_cast<uint32_t *>(sec + head);
+  int32_t lo[MAXR], hi[MAXR];
+  uint32_t carry = 0;
+#pragma unroll
+  for (int r = 0; r < MAXR; r++) {
+    const int j = r * PACK_NT + tid;
+    const uint32_t sb = j < nseg ? ldg2(segbits + 2 * j) : 0u;
+    const uint32_t incl = wave_incl_scan(sb);
+    if (ln == 63) wtot[0][wv] = incl;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < PACK_NW; w++) {
+      const uint32_t x = wtot[0][w];
+      before += w < wv ? x : 0u;
+      tot += x;
+    }
+    __syncthreads();
+    lo[r] = int32_t(carry + before + incl - sb);
+    hi[r] = lo[r] + int32_t(sb);
+    carry += tot;
+  }
+  // clear the words a segment shares with another (or with the payload's end)
+  // and the payload's zero pad, then let every thread's atomic ORs follow
+#pragma unroll
+  for (int r = 0; r < MAXR; r++) {
+    if (r * PACK_NT + tid >= nseg) continue;
+    if (lo[r] & 31) stg4(pw + (lo[r] >> 5), 0u);
+    if (hi[r] & 31) stg4(pw + ((hi[r] - 1) >> 5), 0u);
+  }
+  for (uint64_t i = (uint64_t(carry) + 31) / 32 + tid; i < align16(pay) / 4; i += PACK_NT) stg4(pw + i, 0u);
+  __threadfence();
+  __syncthreads();
+#pragma unroll 1
+  for (int r = 0; r < MAXR; r++) {
+    const int j = r * PACK_NT + tid;
+    if (j >= nseg) continue;
+    BackWriter wr(pw, lo[r], hi[r]);
+    const uint32_t st = tans_encode_segment<DT>(src, n, aligned, nseg, j, T.esym, T.est,
+                                                [&](uint32_t v, uint32_t nb) { wr.put(v, nb); });
+    wr.put(st, kTansLog);
+    wr.finish();
+  }
+  __syncthreads();
 }
 
 // The record of chunk c at recp: stream heads, raw streams, coded payloads.
 // The choice per stream (mode, aux, payload bits, section offset) and the
 // code words come from LDS; stage and wtot are LDS scratch of this function.
-template <int DT>
+template <int DT, bool TC>
 __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *const *in_ptrs, uint32_t c,
                                            uint8_t *const recp, const uint32_t (*enc)[256], const int *pmode,
                                            const int *paux, const unsigned long long *pbits,
                                            const unsigned long long *psec,
                                            uint32_t (*stage_all)[PackShared<DT>::STAGE],
-                                           uint32_t (*wtot)[PACK_NW], uint32_t *rawt) {
+                                           uint32_t (*wtot)[PACK_NW], uint32_t *rawt,
+                                           const uint8_t *segbits, TansEnc<PACK_NT> *tans) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
@@ -685,6 +914,15 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   // -------------------------------------------------------- the record
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k, mode = pmode[p];
+    if constexpr (TC) {
+      if (mode == TANS) {
+        pack_tans<DT>(src, n, aligned, nseg, recp + psec[p], enc[p], A, k, pbits[p], segbits, *tans, wtot);
+        // the tables took the tile buffers: clear them for the streams after
+        for (int i = tid; i < 2 * STAGE; i += ENC_NT) stage_all[i / STAGE][i % STAGE] = 0;
+        __syncthreads();
+        continue;
+      }
+    }
     const uint64_t bits = pbits[p];
     uint8_t *sec = recp + psec[p];
     const uint64_t head = head_bytes_of(mode, k, nseg);
@@ -946,19 +1184,19 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
 
 
 // One workgroup per chunk: the record at its directory offset.
-template <int DT>
+template <int DT, bool TC>
 __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   constexpr int NC = ncoded(DT);
   __shared__ PackShared<DT> sh;
   const int tid = threadIdx.x;
   if (a.ctl[0]) return;  // the container did not fit
   const uint32_t c = blockIdx.x;
-  const uint8_t *plan = a.plans + uint64_t(c) * plan_stride(DT);
+  const uint8_t *plan = a.plans + uint64_t(c) * a.plan_stride;
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
     if (tid < A)
       sh.enc[p][tid] = mode == RAW ? uint32_t(tid) | (uint32_t(k) << 16)
-                     : (mode == HUFF || mode == GROUP) ? ldg4(plan + 64 + 1024 * p + 4 * tid) : 0u;
+                     : (mode == HUFF || mode == GROUP || mode == TANS) ? ldg4(plan + 64 + 1024 * p + 4 * tid) : 0u;
   }
   if (tid < NC) {
     sh.mode[tid] = plan[48 + tid];
@@ -967,8 +1205,8 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     sh.sec_off[tid] = *reinterpret_cast<const uint32_t *>(plan + 32 + 4 * tid);
   }
   const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
-  pack_chunk<DT>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off, sh.stage,
-                 sh.wtot, sh.rawt);
+  pack_chunk<DT, TC>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off,
+                     sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), &sh.su.tans);
 }
 
 // One workgroup: exclusive scan of the record sizes into the directory, then
@@ -1025,25 +1263,48 @@ __global__ __launch_bounds__(1024) void k_finish(FinishArgs a) {
   if (fits && tid < 4) stg4(a.out + end + 4 * tid, 0);
 }
 
-uint64_t plan_bytes(int dtype) { return plan_stride(dtype); }
+uint64_t plan_bytes(int dtype, uint32_t chunk_elems) {
+  const uint64_t maxseg = (uint64_t(chunk_elems) + segsyms(dtype) - 1) / segsyms(dtype);
+  return align16(plan_fixed(dtype) + 2 * maxseg);
+}
 
 hipError_t launch_analyze(int dtype, const EncArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.L.n_chunks == 0) return hipSuccess;
   const dim3 grid(a.L.n_chunks), block(enc_nt(dtype));
-  if (dtype == BF16) hipExtLaunchKernelGGL(k_analyze<BF16>, grid, block, 0, s, e0, e1, 0, a);
-  else if (dtype == FP32) hipExtLaunchKernelGGL(k_analyze<FP32>, grid, block, 0, s, e0, e1, 0, a);
-  else if (dtype == FP8) hipExtLaunchKernelGGL(k_analyze<FP8>, grid, block, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL(k_analyze<FP4X2>, grid, block, 0, s, e0, e1, 0, a);
+  const bool tc = a.coder == CODER_TANS;
+  if (dtype == BF16) {
+    if (tc) hipExtLaunchKernelGGL((k_analyze<BF16, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_analyze<BF16, false>), grid, block, 0, s, e0, e1, 0, a);
+  } else if (dtype == FP32) {
+    if (tc) hipExtLaunchKernelGGL((k_analyze<FP32, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_analyze<FP32, false>), grid, block, 0, s, e0, e1, 0, a);
+  } else if (dtype == FP8) {
+    if (tc) hipExtLaunchKernelGGL((k_analyze<FP8, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_analyze<FP8, false>), grid, block, 0, s, e0, e1, 0, a);
+  } else {
+    if (tc) hipExtLaunchKernelGGL((k_analyze<FP4X2, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_analyze<FP4X2, false>), grid, block, 0, s, e0, e1, 0, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.L.n_chunks == 0) return hipSuccess;
   const dim3 grid(a.L.n_chunks), block(PACK_NT);
-  if (dtype == BF16) hipExtLaunchKernelGGL(k_pack<BF16>, grid, block, 0, s, e0, e1, 0, a);
-  else if (dtype == FP32) hipExtLaunchKernelGGL(k_pack<FP32>, grid, block, 0, s, e0, e1, 0, a);
-  else if (dtype == FP8) hipExtLaunchKernelGGL(k_pack<FP8>, grid, block, 0, s, e0, e1, 0, a);
-  else hipExtLaunchKernelGGL(k_pack<FP4X2>, grid, block, 0, s, e0, e1, 0, a);
+  const bool tc = a.coder == CODER_TANS;
+  if (dtype == BF16) {
+    if (tc) hipExtLaunchKernelGGL((k_pack<BF16, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_pack<BF16, false>), grid, block, 0, s, e0, e1, 0, a);
+  } else if (dtype == FP32) {
+    if (tc) hipExtLaunchKernelGGL((k_pack<FP32, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_pack<FP32, false>), grid, block, 0, s, e0, e1, 0, a);
+  } else if (dtype == FP8) {
+    if (tc) hipExtLaunchKernelGGL((k_pack<FP8, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_pack<FP8, false>), grid, block, 0, s, e0, e1, 0, a);
+  } else {
+    if (tc) hipExtLaunchKernelGGL((k_pack<FP4X2, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((k_pack<FP4X2, false>), grid, block, 0, s, e0, e1, 0, a);
+  }
   return hipGetLastError();
 }
 

@@ -16,16 +16,20 @@ struct EncArgs {
   const uint32_t *group_enc;       // [K][256] bit-reversed code | len << 16
   const uint8_t *group_len;        // [K][256]
   uint8_t *out;                    // container (the raw planes are written here)
-  uint8_t *plans;                  // [n_chunks][plan_bytes(dtype)] code choice and code words
+  uint8_t *plans;                  // [n_chunks][plan_stride] code choice and code words
+  uint64_t plan_stride;            // plan_bytes(dtype, chunk_elems)
   unsigned long long *sizes;       // [n_chunks] record bytes
+  int coder;                       // Coder of the exponent stream (TANS: no group tables)
 };
 // Packs every record at its directory offset (after k_finish).
 struct PackArgs {
   DevLayout L;
   const uint8_t *const *in_ptrs;
   const uint8_t *plans;
+  uint64_t plan_stride;
   uint8_t *out;
   const uint32_t *ctl;             // [0] non-zero: the container did not fit, write nothing
+  int coder;
 };
 
 // Offsets of the records (exclusive scan of their sizes), the directory, the
@@ -72,7 +76,8 @@ constexpr uint64_t kCtlBytes = 256;
 // have nothing to store (their content is meaningless).
 constexpr uint64_t kSinkOff = 128;
 
-uint64_t plan_bytes(int dtype);
+// bytes of one chunk's plan (compress scratch) for chunks of chunk_elems elements
+uint64_t plan_bytes(int dtype, uint32_t chunk_elems);
 // e0, e1 (optional): events that take the start and end times of the
 // launch, attached to its dispatch (no marker joins the stream); left as they
 // were when there is nothing to launch.

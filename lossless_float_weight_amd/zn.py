@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzn.so")
 
 BF16, FP32, FP8_E4M3, FP4X2_E2M1 = 0, 1, 2, 3
+CODER_HUFFMAN, CODER_TANS = 0, 1
 # FP4 E2M1 pairs travel as uint8 tensors (two values per byte, low nibble first)
 TORCH_DTYPE = {BF16: torch.bfloat16, FP32: torch.float32, FP8_E4M3: torch.float8_e4m3fn,
                FP4X2_E2M1: torch.uint8}
@@ -54,6 +55,7 @@ def lib() -> C.CDLL:
         L.zn_compress_bound.argtypes = [P, PU64]
         L.zn_scratch_bytes.argtypes = [P, PU64]
         L.zn_compress.argtypes = [P, P, P, U64, PU64, P, U64, P]
+        L.zn_compress2.argtypes = [P, I, P, P, U64, PU64, P, U64, P]
         L.zn_decompress.argtypes = [P, P, U64, P, P, U64, I, P]
         L.zn_decompress_noalloc.argtypes = [P, P, U64, P, P, I, P]
         L.zn_tableset_save.argtypes = [P, P, U64, PU64]
@@ -279,6 +281,14 @@ def compress(ts: Tableset, tensors: Sequence[torch.Tensor], out: torch.Tensor | 
              sync: bool = True, stream=None):
     """zn_compress.  Returns the container (a view of `out`) when sync, else
     `out` itself (size at byte 56 once the stream has run)."""
+    return compress2(ts, CODER_HUFFMAN, tensors, out, scratch, ptrs, sync, stream)
+
+
+def compress2(ts: Tableset, coder: int, tensors: Sequence[torch.Tensor], out: torch.Tensor | None = None,
+              scratch: torch.Tensor | None = None, ptrs: torch.Tensor | None = None,
+              sync: bool = True, stream=None):
+    """zn_compress2: compress with the exponent stream's coder chosen
+    (CODER_HUFFMAN or CODER_TANS)."""
     _check_tensors(ts, tensors, "compress", exact=True)
     dev = tensors[0].device
     tmp = []
@@ -296,9 +306,9 @@ def compress(ts: Tableset, tensors: Sequence[torch.Tensor], out: torch.Tensor | 
     if not sync:
         _keep_alive(stream, *tmp)
     nb = C.c_uint64()
-    _check(lib().zn_compress(ts.handle, C.c_void_p(ptrs.data_ptr()), C.c_void_p(out.data_ptr()),
-                             out.numel(), C.byref(nb) if sync else None,
-                             C.c_void_p(scratch.data_ptr()), scratch.numel(), _stream(stream)),
+    _check(lib().zn_compress2(ts.handle, int(coder), C.c_void_p(ptrs.data_ptr()), C.c_void_p(out.data_ptr()),
+                              out.numel(), C.byref(nb) if sync else None,
+                              C.c_void_p(scratch.data_ptr()), scratch.numel(), _stream(stream)),
            "compress")
     return out[: nb.value] if sync else out
 

@@ -41,6 +41,7 @@ def test_status_strings_and_argument_errors_need_no_gpu():
     assert lib.zn_setup(0, None, n, 1, 1000, 0, None, ctypes.byref(out)) == -1   # bad chunk size
     assert lib.zn_setup(7, None, n, 1, 262144, 0, None, ctypes.byref(out)) == -1  # bad dtype
     assert lib.zn_compress(None, None, None, 0, None, None, 0, None) == -1
+    assert lib.zn_compress2(None, 1, None, None, 0, None, None, 0, None) == -1
     assert lib.zn_setup_transfer(None, None, n, 1, None, ctypes.byref(out)) == -1      # no source
 
 
