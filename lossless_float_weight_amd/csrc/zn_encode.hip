@@ -22,6 +22,8 @@
 //   streams, from those tiles where their words allow, else in a pass of
 //   their own.
 // No chunk ever waits for another, and no record is copied after packing.
+#include <type_traits>
+
 #include "zn_internal.h"
 
 namespace zn {
@@ -127,12 +129,17 @@ struct TansEnc {
 // Encodes segment j of the first coded stream of a chunk of n elements at
 // src with tANS, backwards: its strips j + r*nseg (32 elements each) from the
 // last to the first, each from its last element.  emit(v, nb) receives each
-// symbol's bits in that order.  Returns the final state minus 2^11.  The next
-// strip's 16-byte vectors load while the current one is encoded.
-template <int DT, class Emit>
+// symbol's bits in that order.  Returns the final state minus 2^11.
+// Per strip: the strip's 32 symbols are taken out of its loaded vectors
+// (held in registers from then on), then hook() runs (the packer stores
+// what the previous strip completed), then the next strip's vectors are
+// loaded, then the symbols are encoded.  No global store comes between a
+// load and the wait for it: the one counter of outstanding vector memory
+// operations would otherwise make that wait drain the stores too.
+template <int DT, class Emit, class Hook>
 __device__ __forceinline__ uint32_t tans_encode_segment(const uint8_t *src, uint32_t n, bool aligned, int nseg,
                                                         int j, const uint32_t *esym, const uint16_t *est,
-                                                        Emit &&emit) {
+                                                        Emit &&emit, Hook &&hook) {
   constexpr int ES = esize(DT), VE = 16 / ES, NQ = 32 * ES / 16;
   const uint32_t nstrips = (n + 31) / 32;
   uint32_t X = kTansStates;
@@ -154,45 +161,91 @@ __device__ __forceinline__ uint32_t tans_encode_segment(const uint8_t *src, uint
   };
   if (uint32_t(j) >= nstrips) return 0;   // not reached: a stream has no more segments than strips
   const uint32_t ql = uint32_t(j) + (nstrips - 1 - uint32_t(j)) / uint32_t(nseg) * uint32_t(nseg);
-  u32x4 cur[NQ], nxt[NQ];
-#pragma unroll
-  for (int i = 0; i < NQ; i++) nxt[i] = u32x4{0, 0, 0, 0};
-  load(ql, cur);
+  u32x4 raw[NQ];
+  load(ql, raw);
   for (int64_t q = ql; q >= j; q -= nseg) {
-    if (q - nseg >= j) load(uint32_t(q - nseg), nxt);
+    // the strip's symbols, four to a register (every field is at most 8 bits)
+    uint32_t sy[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int e = 4 * k + i;
+        const u32x4 c4 = raw[e / VE];
+        x |= field<DT, 0>(vec_elem<DT>(make_uint4(c4[0], c4[1], c4[2], c4[3]), e % VE)) << (8 * i);
+      }
+      sy[k] = x;
+      asm volatile("" : "+v"(sy[k]));   // taken here, before the hook's stores and the next loads
+    }
+    hook();
+    if (q - nseg >= j) load(uint32_t(q - nseg), raw);
     const uint32_t eb = uint32_t(q) * 32;
     const uint32_t lim = n - eb < 32 ? n - eb : 32u;
+    // each symbol's step constants are read one step ahead, so that a step
+    // waits for one LDS read (the next state), not two
+    auto symb = [&](int e) { return (sy[e >> 2] >> (8 * (e & 3))) & 0xFFu; };
+    uint32_t info = esym[symb(31)];
 #pragma unroll
     for (int e = 31; e >= 0; e--) {
+      const uint32_t next = e > 0 ? esym[symb(e > 0 ? e - 1 : 0)] : 0u;
       if (uint32_t(e) < lim) {
-        const u32x4 c4 = cur[e / VE];
-        const uint32_t s = field<DT, 0>(vec_elem<DT>(make_uint4(c4[0], c4[1], c4[2], c4[3]), e % VE));
         uint32_t v;
-        const uint32_t nb = tans_enc_step(X, esym[s], est, v);
+        const uint32_t nb = tans_enc_step(X, info, est, v);
         emit(v, nb);
       }
+      info = next;
     }
-#pragma unroll
-    for (int i = 0; i < NQ; i++) cur[i] = nxt[i];
   }
   return X - kTansStates;
 }
 
 // Writes one segment's bits [b0, b1) of a payload backwards, as tANS emits
-// them: acc holds words T-1 (low half) and T (high half), and word T goes out
-// once the bits reach below word T-1.  Words the segment shares with its
-// neighbours (or with the end of the payload) were cleared beforehand and
-// take an atomic OR; the others a plain store.
-struct BackWriter {
-  uint32_t *pw;
-  int32_t b0, b1, cur, T;
+// them: acc holds words T-1 (low half) and T (high half), and word T is done
+// once the bits reach below word T-1.  Done words go to the lane's 16-word
+// ring in LDS (word w at w mod 16); store() writes the 4-word blocks whose
+// words are all done, a whole aligned block as one 16-byte store: every lane
+// of a wave writes a segment of its own, so word stores would leave lines
+// partly written in the L2.  The words the segment shares with its
+// neighbours (its first and last, when not word-aligned) are ORed
+// atomically at the end into words cleared beforehand.  A strip adds at
+// most 11 words (32 symbols of at most 11 bits) to at most 3 not yet stored,
+// so the ring never wraps onto a word not yet stored.
+struct RingWriter {
+  uint32_t *pw, *lb;
+  int32_t b0, b1, cur, T, fw, lw, ofw, olw, wl, pend;
+  uint32_t topw, botw;
   uint64_t acc;
-  __device__ BackWriter(uint32_t *p, int32_t lo, int32_t hi)
-      : pw(p), b0(lo), b1(hi), cur(hi), T((hi - 1) >> 5), acc(0) {}
+  __device__ RingWriter(uint32_t *p, uint32_t *ring, int32_t lo, int32_t hi)
+      : pw(p), lb(ring), b0(lo), b1(hi), cur(hi), T((hi - 1) >> 5), fw(lo >> 5), lw((hi - 1) >> 5),
+        topw(0), botw(0), acc(0) {
+    ofw = fw + ((lo & 31) != 0);   // the words this segment alone holds: [ofw, olw]
+    olw = lw - ((hi & 31) != 0);
+    wl = olw + 1;                  // lowest word done so far
+    pend = olw >> 2;               // highest block not yet stored
+  }
   __device__ __forceinline__ void word(int32_t w, uint32_t x) {
-    const bool shared = (w == (b0 >> 5) && (b0 & 31)) || (w == ((b1 - 1) >> 5) && (b1 & 31));
-    if (shared) atomicOr(pw + w, x);
-    else stg4(pw + w, x);
+    if (w == lw && (b1 & 31)) topw = x;
+    else if (w == fw && (b0 & 31)) botw = x;
+    else {
+      lb[w & 15] = x;
+      wl = w;
+    }
+  }
+  __device__ __forceinline__ void block(int32_t B) {
+    const int32_t w0 = 4 * B;
+    if (w0 >= ofw && w0 + 3 <= olw) {
+      stg16(pw + w0, *reinterpret_cast<const u32x4 *>(lb + (w0 & 15)));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        if (w0 + k >= ofw && w0 + k <= olw) stg4(pw + w0 + k, lb[(w0 + k) & 15]);
+    }
+  }
+  // the blocks whose owned words are all done
+  __device__ __forceinline__ void store() {
+    const int32_t lowb = (wl + 3) >> 2;
+    for (; pend >= lowb; pend--) block(pend);
   }
   __device__ __forceinline__ void put(uint32_t v, uint32_t nb) {
     const int32_t pos = cur - int32_t(nb);
@@ -204,13 +257,25 @@ struct BackWriter {
     acc |= uint64_t(v) << ((pos - 32 * (T - 1)) & 63);   // nb = 0 ORs nothing
     cur = pos;
   }
+  // after the final state: the last words, every block left, the shared words
   __device__ __forceinline__ void finish() {
     word(T, uint32_t(acc >> 32));
-    if ((b0 >> 5) == T - 1) word(T - 1, uint32_t(acc));
+    if (fw == T - 1) word(T - 1, uint32_t(acc));
+    for (; pend >= (ofw >> 2); pend--) block(pend);
+    if (b1 & 31)
+      __hip_atomic_fetch_or((ZN_GLOBAL uint32_t *)(pw + lw), topw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((b0 & 31) && !(fw == lw && (b1 & 31)))
+      __hip_atomic_fetch_or((ZN_GLOBAL uint32_t *)(pw + fw), botw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 };
 
-template <int DT>
+// LDS of the tANS packing: the encoder tables and each lane's word ring.
+struct TansPack {
+  TansEnc<PACK_NT> e;
+  alignas(16) uint32_t ring[PACK_NT][16];
+};
+
+template <int DT, bool TC = false>
 struct PackShared {
   static constexpr int NC = ncoded(DT);
   static constexpr int G = pack_g(DT);
@@ -219,7 +284,9 @@ struct PackShared {
   uint32_t enc[NC][256];         // tANS: the first stream's normalised counts
   union {
     uint32_t stage[2][STAGE];    // alternate tiles use alternate buffers
-    TansEnc<PACK_NT> tans;       // a tANS stream's tables (no tiles meanwhile)
+    // a tANS stream's tables and write buffers (no tiles meanwhile); only
+    // the kernels that pack tANS hold them
+    std::conditional_t<TC, TansPack, uint32_t> tans;
   } su;
   uint32_t wtot[2][PACK_NW];
   // 1-byte elements: one tile's words of a raw stream (32 strips per segment,
@@ -632,7 +699,7 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
         for (int j = tid; j < nseg; j += ENC_NT) {
           uint32_t nbits = kTansLog;   // the final state, then the symbols' bits
           tans_encode_segment<DT>(src, n, aligned, nseg, j, T.esym, T.est,
-                                  [&](uint32_t, uint32_t nb) { nbits += nb; });
+                                  [&](uint32_t, uint32_t nb) { nbits += nb; }, [] {});
           stg2(segbits + 2ull * j, nbits);
           acc += nbits;
         }
@@ -707,8 +774,9 @@ __global__ __launch_bounds__(enc_nt(DT)) __attribute__((amdgpu_waves_per_eu(DT =
 // lengths gives it.  q: the counts (LDS); wtot: LDS scratch.
 template <int DT>
 __device__ void pack_tans(const uint8_t *src, uint32_t n, bool aligned, int nseg, uint8_t *sec, const uint32_t *q,
-                          int A, int k, uint64_t bits, const uint8_t *segbits, TansEnc<PACK_NT> &T,
+                          int A, int k, uint64_t bits, const uint8_t *segbits, TansPack &TP,
                           uint32_t (*wtot)[PACK_NW]) {
+  TansEnc<PACK_NT> &T = TP.e;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
   int d = 0;
 #pragma unroll
@@ -772,7 +840,10 @@ __device__ void pack_tans(const uint8_t *src, uint32_t n, bool aligned, int nseg
     carry += tot;
   }
   // clear the words a segment shares with another (or with the payload's end)
-  // and the payload's zero pad, then let every thread's atomic ORs follow
+  // and the payload's zero pad, then let every thread's atomic ORs follow.
+  // The barrier's workgroup-scope fence is enough: the stores are complete
+  // in this XCD's L2 when it passes, and the atomics run there (an
+  // agent-scope fence would write the L2 back to memory)
 #pragma unroll
   for (int r = 0; r < MAXR; r++) {
     if (r * PACK_NT + tid >= nseg) continue;
@@ -780,15 +851,15 @@ __device__ void pack_tans(const uint8_t *src, uint32_t n, bool aligned, int nseg
     if (hi[r] & 31) stg4(pw + ((hi[r] - 1) >> 5), 0u);
   }
   for (uint64_t i = (uint64_t(carry) + 31) / 32 + tid; i < align16(pay) / 4; i += PACK_NT) stg4(pw + i, 0u);
-  __threadfence();
   __syncthreads();
 #pragma unroll 1
   for (int r = 0; r < MAXR; r++) {
     const int j = r * PACK_NT + tid;
     if (j >= nseg) continue;
-    BackWriter wr(pw, lo[r], hi[r]);
+    RingWriter wr(pw, TP.ring[tid], lo[r], hi[r]);
     const uint32_t st = tans_encode_segment<DT>(src, n, aligned, nseg, j, T.esym, T.est,
-                                                [&](uint32_t v, uint32_t nb) { wr.put(v, nb); });
+                                                [&](uint32_t v, uint32_t nb) { wr.put(v, nb); },
+                                                [&] { wr.store(); });
     wr.put(st, kTansLog);
     wr.finish();
   }
@@ -805,7 +876,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
                                            const unsigned long long *psec,
                                            uint32_t (*stage_all)[PackShared<DT>::STAGE],
                                            uint32_t (*wtot)[PACK_NW], uint32_t *rawt,
-                                           const uint8_t *segbits, TansEnc<PACK_NT> *tans) {
+                                           const uint8_t *segbits, TansPack *tans) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
@@ -1183,11 +1254,17 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
 }
 
 
+template <int DT, bool TC>
+__device__ __forceinline__ TansPack *tans_of(PackShared<DT, TC> &sh) {
+  if constexpr (TC) return &sh.su.tans;
+  else return nullptr;
+}
+
 // One workgroup per chunk: the record at its directory offset.
 template <int DT, bool TC>
 __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   constexpr int NC = ncoded(DT);
-  __shared__ PackShared<DT> sh;
+  __shared__ PackShared<DT, TC> sh;
   const int tid = threadIdx.x;
   if (a.ctl[0]) return;  // the container did not fit
   const uint32_t c = blockIdx.x;
@@ -1206,7 +1283,7 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   }
   const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
   pack_chunk<DT, TC>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off,
-                     sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), &sh.su.tans);
+                     sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), tans_of(sh));
 }
 
 // One workgroup: exclusive scan of the record sizes into the directory, then
