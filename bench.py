@@ -258,7 +258,12 @@ def main():
 
     torch.cuda.set_device(0)
     coder = zn.CODER_TANS if args.coder == "tans" else zn.CODER_HUFFMAN
+
+    def progress(msg):   # phases of the run, on stderr (the JSON line is the only stdout)
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
+
     base = make_tensors(args.workload)
+    progress(f"{args.workload}: {len(base)} tensors made")
     unc = sum(t.numel() * t.element_size() for t in base)
     extra = {}
     if args.workload == "model":
@@ -306,6 +311,7 @@ def main():
             "blob": torch.empty(bound, dtype=torch.uint8, device="cuda"),
             "cscr": zn.new_scratch(ts), "dscr": torch.empty(256, dtype=torch.uint8, device="cuda"),
         })
+    progress("plan ready, buffers allocated")
     # first pass: container size (needed to hand decompress its input length)
     s0 = sets[0]
     blob = zn.compress2(ts, coder, s0["ins"], out=s0["blob"], scratch=s0["cscr"], ptrs=s0["in_ptrs"])
@@ -338,6 +344,7 @@ def main():
         for k in everything:
             zn.debug_kernel_events(k, None, None)
 
+    progress(f"container {nbytes} bytes; timing")
     for i in range(args.warmup):
         step(sets[i % R])
     torch.cuda.synchronize()
@@ -454,6 +461,7 @@ def main():
         del pblob, pscr
     line.update(extra)
     if not args.no_cpu_baseline:
+        progress("GPU timing done; CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(base, coder=coder)
     print(json.dumps(line), flush=True)
 
