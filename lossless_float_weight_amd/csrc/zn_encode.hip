@@ -1267,7 +1267,9 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   __shared__ PackShared<DT, TC> sh;
   const int tid = threadIdx.x;
   if (a.ctl[0]) return;  // the container did not fit
-  const uint32_t c = blockIdx.x;
+  // chunks in the reverse of the analysis order: the last chunks analysed
+  // are the likeliest still in the 256 MB Infinity Cache
+  const uint32_t c = a.L.n_chunks - 1 - blockIdx.x;
   const uint8_t *plan = a.plans + uint64_t(c) * a.plan_stride;
   for (int p = 0; p < NC; p++) {
     const int k = kbits(DT, p), A = 1 << k, mode = plan[48 + p];
