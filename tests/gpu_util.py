@@ -46,9 +46,10 @@ def record_bounds(blob: np.ndarray):
 
 def field_modes(blob: np.ndarray, n_fields: int, kbits):
     """Per chunk, the tuple of its streams' modes (0 raw, 1 constant, 2 Huffman,
-    3 group) read from the records (format: 8-byte stream head, code lengths
-    as nibbles when Huffman, u16 segment bit lengths when coded, then the
-    16-byte aligned payload)."""
+    3 group, 4 tANS) read from the records (format: 8-byte stream head, code
+    lengths as nibbles when Huffman, a presence mask and the present symbols'
+    u16 counts when tANS, u16 segment bit lengths when coded, then the 16-byte
+    aligned payload)."""
     _, n_chunks, dirv = record_bounds(blob)
     out = []
     for c in range(n_chunks):
@@ -58,6 +59,10 @@ def field_modes(blob: np.ndarray, n_fields: int, kbits):
             pay = int(np.frombuffer(blob[pos + 4:pos + 8].tobytes(), np.uint32)[0])
             mode, nseg = h0 & 0xFF, h0 >> 16
             head = 8 + ((1 << kbits[p]) // 2 if mode == 2 else 0) + (2 * nseg if mode in (2, 3) else 0)
+            if mode == 4:
+                A = 1 << kbits[p]
+                d = sum(bin(int(v)).count("1") for v in blob[pos + 8:pos + 8 + A // 8])
+                head = 8 + A // 8 + 2 * d + 2 * nseg
             pos += ((head + 15) & ~15) + ((pay + 15) & ~15)
             modes.append(mode)
         out.append(tuple(modes))

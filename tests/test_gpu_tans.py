@@ -14,7 +14,8 @@ import torch
 
 from lossless_float_weight_amd import workloads as W
 from lossless_float_weight_amd import zn
-from tests.gpu_util import assert_roundtrip, first_difference, oracle_compress_async, to_np
+from tests.gpu_util import assert_roundtrip, field_modes, first_difference, to_np
+from tests.test_gpu_parity import _fp32_mixes, _fp4_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -205,3 +206,38 @@ def test_block_full_size_whole_container(oracle):
             print(f"  oracle still running at {time.time() - t0:.0f} s", flush=True)
     print(f"  oracle container {o.size} bytes at {time.time() - t0:.0f} s", flush=True)
     assert g.size == o.size and np.array_equal(g, o), first_difference(g, o)
+
+
+def test_every_decode_path_with_tans_lanes(oracle):
+    # tANS exponent lanes next to Huffman lanes of the other streams in the
+    # same wave (FP32 16 lanes per stream, FP8 and FP4 32), and next to raw
+    # and constant streams
+    ts32 = [t.cuda() for t in _fp32_mixes()] + [W.gaussian(4096, 0.0, 0.02, torch.float32, "cuda", 9, 0)]
+    _, g = _check(oracle, ts32, 16384, "FP32 field-mode mixes")
+    m32 = set(field_modes(g, 4, [8, 8, 8, 8]))
+    assert any(m[0] == 4 and m.count(2) == 3 for m in m32), m32
+    assert any(m[0] == 4 and 0 in m[1:] for m in m32), m32
+    gen = torch.Generator(device="cpu").manual_seed(8)
+    n = 4096
+    both = torch.randint(0, 6, (n,), generator=gen).to(torch.uint8) * 9
+    e4 = W.fp8_blockscaled(n, device="cpu")[0][1].view(torch.uint8)
+    ts8 = [x.view(torch.float8_e4m3fn).cuda() for x in (both, e4)]
+    _, g = _check(oracle, ts8, 4096, "FP8 field-mode mixes")
+    m8 = set(field_modes(g, 2, [4, 3]))
+    assert (4, 2) in m8 and (4, 0) in m8, m8
+    sk = lambda: torch.randint(0, 8, (n,), generator=gen).clamp(max=4) // 2        # noqa: E731
+    few = lambda: (torch.randint(0, 8, (n,), generator=gen) == 0).to(torch.int64)  # noqa: E731
+    bit = lambda: torch.randint(0, 2, (n,), generator=gen)                          # noqa: E731
+    nib = lambda e, m, s: 8 * s + 2 * e + m                                         # noqa: E731
+    ts4 = [_fp4_bytes(nib(sk(), few(), bit()), nib(sk(), few(), bit())).cuda(),
+           _fp4_bytes(nib(sk(), bit(), bit()), nib(sk(), bit(), bit())).cuda()]
+    _, g = _check(oracle, ts4, 4096, "FP4 field-mode mixes")
+    m4 = set(field_modes(g, 2, [4, 2]))
+    assert (4, 2) in m4 and (4, 0) in m4, m4
+
+
+def test_empty_tensors(oracle):
+    x = W.single_bf16(1000, device="cuda")[0][1]
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    _check(oracle, [e, x, e], 4096, "BF16 with empty tensors")
+    _check(oracle, [e], 4096, "one empty BF16 tensor")
