@@ -18,9 +18,9 @@ def _gpu():
     zn.lib()
 
 
-def _case(tensors, chunk_bytes, n_groups=0):
+def _case(tensors, chunk_bytes, n_groups=0, coder=zn.CODER_HUFFMAN):
     ts = zn.setup(tensors, chunk_bytes=chunk_bytes, n_groups=n_groups)
-    blob = zn.compress(ts, tensors)
+    blob = zn.compress2(ts, coder, tensors)
     ref = zn.decompress(ts, blob)
     outs = [torch.full_like(r, 0) for r in ref]
     ptrs = torch.tensor([o.data_ptr() for o in outs], dtype=torch.int64, device="cuda")
@@ -30,11 +30,13 @@ def _case(tensors, chunk_bytes, n_groups=0):
 
 
 def test_noalloc_equals_decompress_twice_then_smaller():
-    print("case: no-alloc decompression, BF16 block then a smaller FP8 and BF16 tensor", flush=True)
+    print("case: no-alloc decompression, BF16 block then smaller FP8 and BF16 tensors (Huffman, groups, tANS)",
+          flush=True)
     big = _case([t for _, t in W.block_bf16("cuda", seed=2, scale=8)], 262144)
     small8 = _case([W.fp8_blockscaled(70001, device="cuda")[0][1]], 16384)
     small = _case([W.single_bf16(5000, device="cuda")[0][1]], 8192, n_groups=2)
-    for ts, blob, ref, outs, ptrs, status in (big, small8, small):
+    tans = _case([W.single_bf16(3000, device="cuda")[0][1]], 4096, coder=zn.CODER_TANS)
+    for ts, blob, ref, outs, ptrs, status in (big, small8, small, tans):
         for sync in (True, False):
             for o in outs:
                 o.zero_()
