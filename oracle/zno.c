@@ -110,6 +110,27 @@
  *      presence mask of A bits (bit s of byte s/8), u16 q[s] of each present
  *      symbol in increasing order, u16 bit length per segment, pad 16,
  *      payload (4*ceil(bits/32) bytes, segments bit-contiguous), pad 16.
+ * R9 Packed exponent pairs ("NeuralZip", Abstract: recurring exponent tuples
+ *    represented by packed exponents, chosen by the setup, for a further
+ *    moderate gain).  Ours, for BF16 setups with groups when asked for:
+ *    - pair positions: in each 32-value strip of a chunk's exponent stream,
+ *      values 2i and 2i+1 (a strip of odd length ends with a lone value);
+ *    - after the grouping, per group: F = the (up to) 16 values of largest
+ *      pooled count (ties to the smaller value; present values only), rank
+ *      = position in F; over the group's chunks, a pair position (x, y)
+ *      with x, y in F counts for token 256 + 16*rank(x) + rank(y), every
+ *      other value for its single token x; token lengths by the R7 rule
+ *      over the 512 token counts; the group packs iff the tokens' pooled
+ *      bits are fewer than the singles' under its single table (strict);
+ *    - a chunk of a packing group coded with its group code: per pair
+ *      position the pair token when x, y in F and the token has a code
+ *      word, else the two singles; lone values singles; a single without a
+ *      code word makes the chunk an escape (own table, no pairs).  Canonical
+ *      codes over the 512 tokens, first bit first as always;
+ *    - decoding reads tokens in segment order, a pair token giving its two
+ *      values; the segment's tokens must give exactly its value count;
+ *    - the tableset (format version 2) stores per group the packing flag,
+ *      F and the token lengths; a transfer keeps the source's.
  * ---------------------------------------------------------------------------
  */
 #include "zno.h"
@@ -317,9 +338,9 @@ static void sort_leaves(uint64_t *w, int *sym, int d) {
 /* Code lengths for a histogram; returns the number of distinct symbols d.
  * d < 2 leaves every length 0 (the stream is constant or empty). */
 int zno_code_lengths(const uint64_t *h, int A, int L, uint8_t *len) {
-  uint64_t w[256];
-  int sym[256], d = 0;
-  if (A < 2 || A > 256) return ZNO_ERR_ARG;
+  uint64_t w[512];
+  int sym[512], d = 0;
+  if (A < 2 || A > 512) return ZNO_ERR_ARG;
   memset(len, 0, (size_t)A);
   for (int s = 0; s < A; s++)
     if (h[s]) {
@@ -337,9 +358,9 @@ int zno_code_lengths(const uint64_t *h, int A, int L, uint8_t *len) {
  * symbol gets the smallest absent symbol as a zero-weight partner so the
  * table is a complete code; an empty histogram gives an empty table. */
 int zno_group_lengths(const uint64_t *h, int A, int L, uint8_t *len) {
-  uint64_t w[256];
-  int sym[256], d = 0;
-  if (A < 2 || A > 256) return ZNO_ERR_ARG;
+  uint64_t w[512];
+  int sym[512], d = 0;
+  if (A < 2 || A > 512) return ZNO_ERR_ARG;
   memset(len, 0, (size_t)A);
   for (int s = 0; s < A; s++)
     if (h[s]) {
@@ -597,12 +618,39 @@ static uint64_t nchunks_of(int dt, uint64_t n, uint32_t cb) {
   return (n + ce - 1) / ce;
 }
 
+/* The pair code of one group: F's ranks and the token lengths. */
+typedef struct {
+  int nF;
+  uint8_t F[16];
+  uint8_t rank[256]; /* rank in F, 0xFF when not in F */
+  const uint8_t *tlen;
+} pair_code;
+/* The tokens of the symbols [a, b) of one strip (R9); returns their number. */
+static int strip_tokens(const uint8_t *sym, uint64_t a, uint64_t b, const pair_code *pc, uint16_t *tok) {
+  int m = 0;
+  for (uint64_t i = a; i < b; i += 2) {
+    if (i + 1 < b) {
+      int rx = pc->rank[sym[i]], ry = pc->rank[sym[i + 1]];
+      if (rx < pc->nF && ry < pc->nF && pc->tlen[256 + 16 * rx + ry]) {
+        tok[m++] = (uint16_t)(256 + 16 * rx + ry);
+        continue;
+      }
+      tok[m++] = sym[i];
+      tok[m++] = sym[i + 1];
+    } else {
+      tok[m++] = sym[i];
+    }
+  }
+  return m;
+}
+
 /* Plans one coded stream of one chunk: histogram, mode and code lengths. */
 typedef struct {
   int mode, aux, nseg, d;
   uint8_t len[256];
   uint32_t q[256];  /* TANS: normalised counts */
   uint64_t bits;
+  const pair_code *pc; /* GROUP with a packing group (R9) */
 } stream_plan;
 
 /* The symbols of segment j of a stream of n symbols, in decoding order
@@ -615,7 +663,7 @@ static uint64_t segment_symbols(const uint8_t *sym, uint64_t n, int nseg, int j,
 }
 
 static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8_t *group_len,
-                       int group_id, int coder, stream_plan *pl, int *escape) {
+                       int group_id, int coder, const pair_code *pc, stream_plan *pl, int *escape) {
   uint64_t h[256] = {0};
   int A = 1 << k, d = 0, last = 0;
   for (uint64_t i = 0; i < n; i++) h[sym[i]]++;
@@ -625,6 +673,7 @@ static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8
       last = s;
     }
   memset(pl->len, 0, sizeof pl->len);
+  pl->pc = NULL;
   pl->d = d;
   pl->nseg = (int)((n + (uint64_t)S - 1) / (uint64_t)S);
   pl->bits = 0;
@@ -638,9 +687,21 @@ static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8
   if (group_len) {
     int covered = 1;
     uint64_t bits = 0;
-    for (int s = 0; s < A; s++) {
-      if (h[s] && !group_len[s]) covered = 0;
-      bits += h[s] * group_len[s];
+    if (pc) {
+      /* R9: the strips' tokens under the group's pair code */
+      uint16_t tok[STRIP];
+      for (uint64_t a = 0; a < n; a += STRIP) {
+        int m = strip_tokens(sym, a, a + STRIP < n ? a + STRIP : n, pc, tok);
+        for (int i = 0; i < m; i++) {
+          if (!pc->tlen[tok[i]]) covered = 0;
+          bits += pc->tlen[tok[i]];
+        }
+      }
+    } else {
+      for (int s = 0; s < A; s++) {
+        if (h[s] && !group_len[s]) covered = 0;
+        bits += h[s] * group_len[s];
+      }
     }
     if (covered) {
       uint64_t gs = section_bytes(ZNO_GROUP, k, n, pl->nseg, bits);
@@ -648,6 +709,7 @@ static int plan_stream(const uint8_t *sym, uint64_t n, int k, int S, const uint8
         pl->mode = ZNO_GROUP;
         pl->aux = group_id;
         memcpy(pl->len, group_len, (size_t)A);
+        pl->pc = pc;
         pl->bits = bits;
       } else {
         pl->mode = ZNO_RAW;
@@ -714,7 +776,20 @@ static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k
     q += A / 2;
   }
   bitw bw = {out + head, 0};
-  if (pl->mode == ZNO_HUFF || pl->mode == ZNO_GROUP) {
+  if (pl->mode == ZNO_GROUP && pl->pc) {
+    /* R9: tokens, canonical codes over the 512 tokens */
+    uint32_t code[512];
+    uint16_t tok[STRIP];
+    zno_canonical_codes(pl->pc->tlen, 512, MAXLEN, code);
+    for (int j = 0; j < pl->nseg; j++) {
+      uint64_t b0 = bw.pos;
+      for (uint64_t q0 = (uint64_t)j * STRIP; q0 < n; q0 += (uint64_t)pl->nseg * STRIP) {
+        int m = strip_tokens(sym, q0, q0 + STRIP < n ? q0 + STRIP : n, pl->pc, tok);
+        for (int i = 0; i < m; i++) put_code(&bw, code[tok[i]], pl->pc->tlen[tok[i]]);
+      }
+      put_u16(q + 2 * j, (uint32_t)(bw.pos - b0));
+    }
+  } else if (pl->mode == ZNO_HUFF || pl->mode == ZNO_GROUP) {
     uint32_t code[256];
     zno_canonical_codes(pl->len, A, MAXLEN, code);
     for (int j = 0; j < pl->nseg; j++) {
@@ -753,8 +828,8 @@ static uint64_t write_stream(uint8_t *out, const uint8_t *sym, uint64_t n, int k
 
 /* Encodes the record of one chunk of n elements; the record is zero-padded. */
 static int encode_record(int dt, const uint8_t *chunk, uint64_t n, const uint8_t *group_len,
-                         int group_id, int coder, uint8_t *rec, uint64_t cap, uint64_t *rec_bytes,
-                         int *escape, zno_stats *st) {
+                         int group_id, int coder, const pair_code *pc, uint8_t *rec, uint64_t cap,
+                         uint64_t *rec_bytes, int *escape, zno_stats *st) {
   int nc = ncoded(dt), S = segsyms(dt);
   uint8_t *sym = (uint8_t *)malloc((size_t)n * 4 + 1);
   if (!sym) return ZNO_ERR_NOMEM;
@@ -769,7 +844,7 @@ static int encode_record(int dt, const uint8_t *chunk, uint64_t n, const uint8_t
   if (escape) *escape = 0;
   for (int p = 0; p < nc; p++) {
     int rc = plan_stream(sym + (uint64_t)p * n, n, kbits(dt, p), S, p == 0 ? group_len : NULL,
-                         group_id, p == 0 ? coder : ZNO_CODER_HUFFMAN, &pl[p], escape);
+                         group_id, p == 0 ? coder : ZNO_CODER_HUFFMAN, p == 0 ? pc : NULL, &pl[p], escape);
     if (rc < 0) {
       free(sym);
       return rc;
@@ -800,7 +875,7 @@ int zno_encode_chunk2(int dt, const void *chunk, uint64_t n, const uint8_t *grou
                       int coder, void *rec, uint64_t cap, uint64_t *rec_bytes, int *escape) {
   if (!valid_dtype(dt) || !rec_bytes || n == 0) return ZNO_ERR_ARG;
   if (coder != ZNO_CODER_HUFFMAN && (coder != ZNO_CODER_TANS || group_len)) return ZNO_ERR_ARG;
-  return encode_record(dt, (const uint8_t *)chunk, n, group_len, group_id, coder, (uint8_t *)rec, cap,
+  return encode_record(dt, (const uint8_t *)chunk, n, group_len, group_id, coder, NULL, (uint8_t *)rec, cap,
                        rec_bytes, escape, NULL);
 }
 int zno_encode_chunk(int dt, const void *chunk, uint64_t n, const uint8_t *group_len, int group_id,
@@ -821,16 +896,35 @@ struct zno_tableset {
   uint8_t *map;        /* [n_chunks] group of each chunk */
   uint64_t cost[ROUNDS + 1];
   uint64_t hash;
+  /* R9: packed exponent pairs (pairs = 1 when the setup was asked for them) */
+  int pairs;
+  uint8_t *packed;      /* [K] */
+  uint8_t *nF;          /* [K] */
+  uint8_t (*F)[16];     /* [K] the values of the pairs, by rank */
+  uint8_t (*tlen)[512]; /* [K] token lengths: singles 0..255, pairs 256.. */
 };
 
+static void pair_code_of(const zno_tableset *ts, int g, pair_code *pc) {
+  pc->nF = ts->nF[g];
+  memcpy(pc->F, ts->F[g], 16);
+  memset(pc->rank, 0xFF, 256);
+  for (int i = 0; i < pc->nF; i++) pc->rank[pc->F[i]] = (uint8_t)i;
+  pc->tlen = ts->tlen[g];
+}
+
+
+/* per group of a version-2 tableset: packing flag, |F|, F[16], 512 token
+   lengths two per byte (even token in the low nibble) */
+#define TS_PAIR_BYTES 274
 static uint64_t ts_serial_bytes(const zno_tableset *ts) {
   int A = 1 << kbits(ts->dtype, 0);
-  return 24 + 8 * (uint64_t)ts->n_tensors + (uint64_t)ts->K * (A / 2) + ts->n_chunks;
+  return 24 + 8 * (uint64_t)ts->n_tensors + (uint64_t)ts->K * (A / 2) + ts->n_chunks +
+         (ts->pairs ? (uint64_t)ts->K * TS_PAIR_BYTES : 0);
 }
 static void ts_serialise(const zno_tableset *ts, uint8_t *b) {
   int A = 1 << kbits(ts->dtype, 0);
   put_u32(b, TS_MAGIC);
-  put_u16(b + 4, VERSION);
+  put_u16(b + 4, ts->pairs ? 2 : VERSION);
   b[6] = (uint8_t)ts->dtype;
   b[7] = (uint8_t)ts->K;
   put_u32(b + 8, ts->chunk_bytes);
@@ -842,6 +936,14 @@ static void ts_serialise(const zno_tableset *ts, uint8_t *b) {
   for (int g = 0; g < ts->K; g++)
     for (int s = 0; s < A; s += 2) *q++ = (uint8_t)(ts->len[g][s] | (ts->len[g][s + 1] << 4));
   memcpy(q, ts->map, ts->n_chunks);
+  q += ts->n_chunks;
+  for (int g = 0; ts->pairs && g < ts->K; g++) {
+    *q++ = ts->packed[g];
+    *q++ = ts->nF[g];
+    memcpy(q, ts->F[g], 16);
+    q += 16;
+    for (int t = 0; t < 512; t += 2) *q++ = (uint8_t)(ts->tlen[g][t] | (ts->tlen[g][t + 1] << 4));
+  }
 }
 /* FNV-1a, 64-bit (Fowler, Noll, Vo). */
 static uint64_t fnv1a64(const uint8_t *b, uint64_t n) {
@@ -867,6 +969,10 @@ void zno_tableset_free(zno_tableset *ts) {
   free(ts->n_elems);
   free(ts->len);
   free(ts->map);
+  free(ts->packed);
+  free(ts->nF);
+  free(ts->F);
+  free(ts->tlen);
   free(ts);
 }
 
@@ -881,7 +987,11 @@ static zno_tableset *ts_alloc(int dt, int K, uint32_t cb, int T, uint32_t M) {
   ts->n_elems = (uint64_t *)calloc((size_t)T + 1, 8);
   ts->len = (uint8_t(*)[256])calloc((size_t)K + 1, 256);
   ts->map = (uint8_t *)calloc((size_t)M + 1, 1);
-  if (!ts->n_elems || !ts->len || !ts->map) {
+  ts->packed = (uint8_t *)calloc((size_t)K + 1, 1);
+  ts->nF = (uint8_t *)calloc((size_t)K + 1, 1);
+  ts->F = (uint8_t(*)[16])calloc((size_t)K + 1, 16);
+  ts->tlen = (uint8_t(*)[512])calloc((size_t)K + 1, 512);
+  if (!ts->n_elems || !ts->len || !ts->map || !ts->packed || !ts->nF || !ts->F || !ts->tlen) {
     zno_tableset_free(ts);
     return NULL;
   }
@@ -956,9 +1066,91 @@ static int cmp_keyed(const void *a, const void *b) {
   return x->c < y->c ? -1 : x->c > y->c;
 }
 
+/* R9: every group's pair code, from the final assignment (hist: the chunks'
+ * exponent histograms). */
+static int setup_pairs(zno_tableset *ts, const uint32_t *hist, const void *const *tensors,
+                       const uint64_t *n_elems, int T) {
+  const int K = ts->K, dt = ts->dtype;
+  const uint32_t M = ts->n_chunks;
+  const uint64_t ce = chunk_elems(dt, ts->chunk_bytes);
+  uint64_t *H = (uint64_t *)calloc((size_t)K * 256, 8), *Tk = (uint64_t *)calloc((size_t)K * 512, 8);
+  uint8_t *sym = (uint8_t *)malloc((size_t)ce);
+  pair_code *pc = (pair_code *)calloc((size_t)K, sizeof(pair_code));
+  if (!H || !Tk || !sym || !pc) {
+    free(H), free(Tk), free(sym), free(pc);
+    return ZNO_ERR_NOMEM;
+  }
+  for (uint32_t c = 0; c < M; c++)
+    for (int s = 0; s < 256; s++) H[(uint64_t)ts->map[c] * 256 + s] += hist[(uint64_t)c * 256 + s];
+  /* F: the values of largest pooled count, ties to the smaller value */
+  for (int g = 0; g < K; g++) {
+    uint8_t taken[256] = {0};
+    int nF = 0;
+    for (; nF < 16; nF++) {
+      int best = -1;
+      for (int s = 0; s < 256; s++)
+        if (!taken[s] && H[(uint64_t)g * 256 + s] && (best < 0 || H[(uint64_t)g * 256 + s] > H[(uint64_t)g * 256 + best]))
+          best = s;
+      if (best < 0) break;
+      taken[best] = 1;
+      ts->F[g][nF] = (uint8_t)best;
+    }
+    ts->nF[g] = (uint8_t)nF;
+    pair_code_of(ts, g, &pc[g]);
+  }
+  /* token counts over the group's chunks */
+  uint32_t c = 0;
+  for (int t = 0; t < T; t++) {
+    const uint8_t *b = (const uint8_t *)tensors[t];
+    for (uint64_t i0 = 0; i0 < n_elems[t]; i0 += ce, c++) {
+      const uint64_t n = n_elems[t] - i0 < ce ? n_elems[t] - i0 : ce;
+      const int g = ts->map[c];
+      for (uint64_t i = 0; i < n; i++) {
+        uint8_t s4[4];
+        uint32_t raw;
+        split_one(dt, load_elem(dt, b, i0 + i), s4, &raw);
+        sym[i] = s4[0];
+      }
+      uint64_t *tk = Tk + (uint64_t)g * 512;
+      for (uint64_t a = 0; a < n; a += STRIP) {
+        const uint64_t e = a + STRIP < n ? a + STRIP : n;
+        for (uint64_t i = a; i < e; i += 2) {
+          const int rx = pc[g].rank[sym[i]], ry = i + 1 < e ? pc[g].rank[sym[i + 1]] : 0xFF;
+          if (i + 1 < e && rx < pc[g].nF && ry < pc[g].nF) {
+            tk[256 + 16 * rx + ry]++;
+          } else {
+            tk[sym[i]]++;
+            if (i + 1 < e) tk[sym[i + 1]]++;
+          }
+        }
+      }
+    }
+  }
+  int rc = ZNO_OK;
+  for (int g = 0; g < K && rc == ZNO_OK; g++) {
+    rc = zno_group_lengths(Tk + (uint64_t)g * 512, 512, MAXLEN, ts->tlen[g]);
+    if (rc < 0) break;
+    rc = ZNO_OK;
+    uint64_t bt = 0, bs = 0;
+    for (int t = 0; t < 512; t++) bt += Tk[(uint64_t)g * 512 + t] * ts->tlen[g][t];
+    for (int s = 0; s < 256; s++) bs += H[(uint64_t)g * 256 + s] * ts->len[g][s];
+    ts->packed[g] = bt < bs;
+  }
+  ts->pairs = 1;
+  free(H), free(Tk), free(sym), free(pc);
+  return rc;
+}
+
 int zno_setup(int dt, const void *const *tensors, const uint64_t *n_elems, int T, uint32_t cb,
               int K, zno_tableset **out) {
+  return zno_setup2(dt, tensors, n_elems, T, cb, K, 0, out);
+}
+
+int zno_setup2(int dt, const void *const *tensors, const uint64_t *n_elems, int T, uint32_t cb,
+               int K, int flags, zno_tableset **out) {
   if (!out || !valid_dtype(dt) || !valid_chunk(cb) || T < 1 || K < 0 || K > 255) return ZNO_ERR_ARG;
+  if ((flags & ~ZNO_SETUP_PAIRS) || ((flags & ZNO_SETUP_PAIRS) && (dt != ZNO_BF16 || K < 1)))
+    return ZNO_ERR_ARG;
   uint32_t M = 0;
   for (int t = 0; t < T; t++) M += (uint32_t)nchunks_of(dt, n_elems[t], cb);
   zno_tableset *ts = ts_alloc(dt, K, cb, T, M);
@@ -1022,6 +1214,8 @@ int zno_setup(int dt, const void *const *tensors, const uint64_t *n_elems, int T
   /* (4) final tables from the final assignment */
   if (rc == ZNO_OK) rc = tables_from_assignment(hist, M, A, K, ts->map, ts->len);
   if (rc == ZNO_OK) ts->cost[ROUNDS] = total_cost(hist, M, A, ts->map, ts->len);
+  /* (5) R9: pair codes */
+  if (rc == ZNO_OK && (flags & ZNO_SETUP_PAIRS)) rc = setup_pairs(ts, hist, tensors, n_elems, T);
   free(hist), free(cn), free(keys);
   if (rc == ZNO_OK) rc = ts_rehash(ts);
   if (rc < 0) {
@@ -1059,6 +1253,11 @@ int zno_setup_transfer(const zno_tableset *src, const void *const *tensors, cons
   memcpy(ts->n_elems, n_elems, 8 * (size_t)T);
   memcpy(ts->len, src->len, (size_t)K * 256);
   memcpy(ts->cost, src->cost, sizeof ts->cost);
+  ts->pairs = src->pairs;
+  memcpy(ts->packed, src->packed, (size_t)K);
+  memcpy(ts->nF, src->nF, (size_t)K);
+  memcpy(ts->F, src->F, (size_t)K * 16);
+  memcpy(ts->tlen, src->tlen, (size_t)K * 512);
   uint32_t *hist = (uint32_t *)calloc((size_t)M * A + 1, 4);
   uint64_t *cn = (uint64_t *)calloc((size_t)M + 1, 8);
   if (!hist || !cn) {
@@ -1110,6 +1309,14 @@ int zno_tableset_cost_history(const zno_tableset *ts, uint64_t *cost) {
   memcpy(cost, ts->cost, sizeof ts->cost);
   return ZNO_OK;
 }
+int zno_tableset_pairs(const zno_tableset *ts, int g, int *packed, int *nF, uint8_t *F, uint8_t *tlen) {
+  if (!ts || g < 0 || g >= ts->K) return ZNO_ERR_ARG;
+  if (packed) *packed = ts->pairs ? ts->packed[g] : 0;
+  if (nF) *nF = ts->pairs ? ts->nF[g] : 0;
+  if (F) memcpy(F, ts->F[g], 16);
+  if (tlen) memcpy(tlen, ts->tlen[g], 512);
+  return ts->pairs;
+}
 int zno_tableset_save(const zno_tableset *ts, void *buf, uint64_t cap, uint64_t *len) {
   if (!ts || !len) return ZNO_ERR_ARG;
   *len = ts_serial_bytes(ts);
@@ -1120,14 +1327,17 @@ int zno_tableset_save(const zno_tableset *ts, void *buf, uint64_t cap, uint64_t 
 }
 int zno_tableset_load(const void *buf, uint64_t len, zno_tableset **out) {
   const uint8_t *b = (const uint8_t *)buf;
-  if (!b || !out || len < 24 || get_u32(b) != TS_MAGIC || get_u16(b + 4) != VERSION ||
-      get_u32(b + 20) != MAXLEN)
-    return ZNO_ERR_CORRUPT;
+  if (!b || !out || len < 24 || get_u32(b) != TS_MAGIC || get_u32(b + 20) != MAXLEN) return ZNO_ERR_CORRUPT;
+  /* version 2: with the pair codes of R9 (BF16 with groups only) */
+  const int ver = (int)get_u16(b + 4);
   int dt = b[6], K = b[7], T = (int)get_u32(b + 12);
   uint32_t cb = get_u32(b + 8), M = get_u32(b + 16);
-  if (!valid_dtype(dt) || !valid_chunk(cb) || T < 1) return ZNO_ERR_CORRUPT;
+  if ((ver != VERSION && ver != 2) || !valid_dtype(dt) || !valid_chunk(cb) || T < 1) return ZNO_ERR_CORRUPT;
+  const int pairs = ver == 2;
+  if (pairs && (dt != ZNO_BF16 || K < 1)) return ZNO_ERR_CORRUPT;
   int A = 1 << kbits(dt, 0);
-  if (len != 24 + 8 * (uint64_t)T + (uint64_t)K * (A / 2) + M) return ZNO_ERR_CORRUPT;
+  if (len != 24 + 8 * (uint64_t)T + (uint64_t)K * (A / 2) + M + (pairs ? (uint64_t)K * TS_PAIR_BYTES : 0))
+    return ZNO_ERR_CORRUPT;
   zno_tableset *ts = ts_alloc(dt, K, cb, T, M);
   if (!ts) return ZNO_ERR_NOMEM;
   const uint8_t *q = b + 24;
@@ -1142,7 +1352,41 @@ int zno_tableset_load(const void *buf, uint64_t len, zno_tableset **out) {
       ts->len[g][s + 1] = *q >> 4;
     }
   memcpy(ts->map, q, M);
+  q += M;
   int bad = msum != M;
+  ts->pairs = pairs;
+  for (int g = 0; pairs && g < K; g++) {
+    ts->packed[g] = q[0];
+    ts->nF[g] = q[1];
+    memcpy(ts->F[g], q + 2, 16);
+    for (int t = 0; t < 512; t += 2) {
+      ts->tlen[g][t] = q[18 + t / 2] & 15;
+      ts->tlen[g][t + 1] = q[18 + t / 2] >> 4;
+    }
+    q += TS_PAIR_BYTES;
+    /* a flag, at most 16 distinct values of F (zero past |F|), lengths within
+       the limit, no pair token past |F|, and a packing group's token code
+       complete (Kraft equality) */
+    const int nF = ts->nF[g];
+    bad |= ts->packed[g] > 1 || nF > 16;
+    uint8_t seen[256] = {0};
+    for (int i = 0; i < 16 && !bad; i++) {
+      if (i < nF) bad |= seen[ts->F[g][i]]++ != 0;
+      else bad |= ts->F[g][i] != 0;
+    }
+    uint64_t kraft = 0;
+    int d = 0;
+    for (int t = 0; t < 512 && !bad; t++) {
+      const int l = ts->tlen[g][t];
+      bad |= l > MAXLEN;
+      if (t >= 256 && (((t - 256) >> 4) >= nF || ((t - 256) & 15) >= nF)) bad |= l != 0;
+      if (l && l <= MAXLEN) {
+        kraft += (uint64_t)1 << (MAXLEN - l);
+        d++;
+      }
+    }
+    if (ts->packed[g] && !bad) bad = d < 2 || kraft != ((uint64_t)1 << MAXLEN);
+  }
   /* a plan without groups stores its map as zero bytes; with groups each
      byte names one of the K groups */
   for (uint32_t c = 0; c < M && !bad; c++) bad = K ? ts->map[c] >= K : ts->map[c] != 0;
@@ -1278,8 +1522,11 @@ int zno_compress2(int dt, const void *const *tensors, const uint64_t *n, int T, 
         rc = ZNO_ERR_CAPACITY;
         break;
       }
+      pair_code pcg;
+      const int packed = grouped && ts->pairs && ts->packed[g];
+      if (packed) pair_code_of(ts, g, &pcg);
       rc = encode_record(dt, b + i0 * (uint64_t)esize(dt), m, grouped ? ts->len[g] : NULL, g, coder,
-                         out + pos, cap - pos, &sz, &esc, st);
+                         packed ? &pcg : NULL, out + pos, cap - pos, &sz, &esc, st);
       if (rc < 0) break;
       if (st) st->escapes += (uint64_t)esc;
       pos += sz;
@@ -1317,6 +1564,82 @@ int zno_header(const void *inv, uint64_t in_bytes, int *dt, int *T, uint64_t *nt
   if (total) *total = get_u64(in + 56);
   if (hash) *hash = get_u64(in + 32);
   return ZNO_OK;
+}
+
+/* R9: the tokens of a GROUP section whose group packs pairs; q: the segment
+ * lengths.  Returns the section size, or a negative status. */
+static int64_t decode_pairs(const uint8_t *q, const uint8_t *payload, uint64_t pay, uint64_t head,
+                            uint64_t n, int nseg, const zno_tableset *ts, int g, uint8_t *sym) {
+  const uint8_t *tlen = ts->tlen[g];
+  uint64_t kraft = 0;
+  int count[17] = {0}, d = 0;
+  for (int t = 0; t < 512; t++) {
+    if (tlen[t] > MAXLEN) return ZNO_ERR_CORRUPT;
+    if (tlen[t]) {
+      kraft += (uint64_t)1 << (MAXLEN - tlen[t]);
+      count[tlen[t]]++;
+      d++;
+    }
+  }
+  if (d < 2 || kraft != ((uint64_t)1 << MAXLEN)) return ZNO_ERR_CORRUPT;
+  int sorted[512], offs[17], first[17], o = 0;
+  uint32_t code = 0;
+  for (int l = 1; l <= MAXLEN; l++) {
+    offs[l] = o;
+    o += count[l];
+  }
+  {
+    int fill[17];
+    memcpy(fill, offs, sizeof fill);
+    for (int t = 0; t < 512; t++)
+      if (tlen[t]) sorted[fill[tlen[t]]++] = t;
+  }
+  for (int l = 1; l <= MAXLEN; l++) {
+    code = (code + (uint32_t)count[l - 1]) << 1;
+    first[l] = (int)code;
+  }
+  uint64_t total_bits = 0;
+  for (int j = 0; j < nseg; j++) total_bits += get_u16(q + 2 * j);
+  if (pay != 4 * ((total_bits + 31) / 32)) return ZNO_ERR_CORRUPT;
+  uint64_t seg_start = 0;
+  for (int j = 0; j < nseg; j++) {
+    uint64_t sb = get_u16(q + 2 * j);
+    bitr br = {payload, seg_start, seg_start + sb};
+    /* the segment's positions: strips j, j + nseg, ...; a pair fills two */
+    uint64_t i = (uint64_t)j * STRIP;
+    int half = 0;   /* 1: the next position takes a pair's second value */
+    uint8_t second = 0;
+    while (i < n) {
+      if (half) {
+        sym[i] = second;
+        half = 0;
+      } else {
+        int c = 0, found = -1;
+        for (int l = 1; l <= MAXLEN; l++) {
+          unsigned bit;
+          if (get_bit(&br, &bit)) return ZNO_ERR_CORRUPT;
+          c = (c << 1) | (int)bit;
+          if (c >= first[l] && c - first[l] < count[l]) {
+            found = sorted[offs[l] + c - first[l]];
+            break;
+          }
+        }
+        if (found < 0) return ZNO_ERR_CORRUPT;
+        if (found < 256) {
+          sym[i] = (uint8_t)found;
+        } else {
+          sym[i] = ts->F[g][(found - 256) >> 4];
+          second = ts->F[g][(found - 256) & 15];
+          half = 1;
+        }
+      }
+      i = ((i + 1) % STRIP) ? i + 1 : i + 1 + (uint64_t)(nseg - 1) * STRIP;
+    }
+    if (half) return ZNO_ERR_CORRUPT;             /* a pair past the segment's last value */
+    if (br.pos != br.end) return ZNO_ERR_CORRUPT; /* segment length must be exact */
+    seg_start += sb;
+  }
+  return (int64_t)(head + align16(pay));
 }
 
 /* Decodes one stream section of n symbols at sec (within [sec, lim)).
@@ -1426,6 +1749,7 @@ static int64_t decode_stream(const uint8_t *sec, const uint8_t *lim, uint64_t n,
   } else {
     if (!allow_group) return ZNO_ERR_CORRUPT;
     if (!ts || ts->K == 0 || aux >= ts->K) return ZNO_ERR_TABLESET;
+    if (ts->pairs && ts->packed[aux]) return decode_pairs(q, payload, pay, head, n, nseg, ts, aux, sym);
     memcpy(len, ts->len[aux], (size_t)A);
   }
   /* the lengths must form a complete prefix code (Kraft equality) */

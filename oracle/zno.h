@@ -98,6 +98,11 @@ int zno_encode_chunk2(int dtype, const void *chunk, uint64_t n, const uint8_t *g
 /* ---- NeuralZip-style setup ---- */
 int zno_setup(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,
               uint32_t chunk_bytes, int n_groups, zno_tableset **out);
+/* zno_setup with flags: ZNO_SETUP_PAIRS adds the packed exponent pairs of
+ * R9 (BF16 with groups only; ZNO_ERR_ARG otherwise). */
+enum { ZNO_SETUP_PAIRS = 1 };
+int zno_setup2(int dtype, const void *const *tensors, const uint64_t *n_elems, int n_tensors,
+               uint32_t chunk_bytes, int n_groups, int flags, zno_tableset **out);
 /* The source's group codes for other tensors of its dtype and chunk size;
  * each chunk to the group code of least coded size (content, not position). */
 int zno_setup_transfer(const zno_tableset *src, const void *const *tensors, const uint64_t *n_elems,
@@ -107,6 +112,9 @@ int zno_tableset_info(const zno_tableset *ts, int *n_groups, uint32_t *n_chunks,
 int zno_tableset_lengths(const zno_tableset *ts, int g, uint8_t *len /* alphabet */);
 int zno_tableset_map(const zno_tableset *ts, uint8_t *map /* n_chunks */);
 int zno_tableset_cost_history(const zno_tableset *ts, uint64_t *cost /* rounds+1 */);
+/* R9: group g's packing flag, |F|, F[16] and its 512 token lengths; returns
+ * 1 if the setup has pair codes, 0 if not. */
+int zno_tableset_pairs(const zno_tableset *ts, int g, int *packed, int *nF, uint8_t *F, uint8_t *tlen);
 int zno_tableset_save(const zno_tableset *ts, void *buf, uint64_t cap, uint64_t *len);
 int zno_tableset_load(const void *buf, uint64_t len, zno_tableset **out);
 

@@ -82,6 +82,8 @@ def lib():
         L.zno_decompress.argtypes = [P, U64, P, C.POINTER(P), PU64, I]
         L.zno_encode_chunk.argtypes = [I, P, U64, P, I, P, U64, PU64, C.POINTER(I)]
         L.zno_setup.argtypes = [I, C.POINTER(P), PU64, I, U32, I, C.POINTER(P)]
+        L.zno_setup2.argtypes = [I, C.POINTER(P), PU64, I, U32, I, I, C.POINTER(P)]
+        L.zno_tableset_pairs.argtypes = [P, I, C.POINTER(I), C.POINTER(I), P, P]
         L.zno_setup_transfer.argtypes = [P, C.POINTER(P), PU64, I, C.POINTER(P)]
         L.zno_tableset_free.argtypes = [P]
         L.zno_tableset_info.argtypes = [P, C.POINTER(I), C.POINTER(U32), PU64]
@@ -296,6 +298,18 @@ class Tableset:
         _check(lib().zno_tableset_lengths(self.handle, g, _ptr(out)), "lengths")
         return out
 
+    def pairs(self, g: int):
+        """R9: (packed, F as a list, token lengths[512]) of group g, or None
+        when the setup has no pair codes."""
+        packed, nf = C.c_int(), C.c_int()
+        F = np.zeros(16, np.uint8)
+        tl = np.zeros(512, np.uint8)
+        rc = lib().zno_tableset_pairs(self.handle, g, C.byref(packed), C.byref(nf), _ptr(F), _ptr(tl))
+        _check(rc if rc < 0 else 0, "pairs")
+        if rc == 0:
+            return None
+        return bool(packed.value), F[: nf.value].tolist(), tl
+
     def group_map(self) -> np.ndarray:
         out = np.zeros(self.info()[1], np.uint8)
         _check(lib().zno_tableset_map(self.handle, _ptr(out)), "map")
@@ -321,14 +335,17 @@ class Tableset:
         return cls(h, int(buf[6]))
 
 
-def setup(dtype: int, tensors, chunk_bytes: int = 262144, n_groups: int = 16) -> Tableset:
+SETUP_PAIRS = 1
+
+
+def setup(dtype: int, tensors, chunk_bytes: int = 262144, n_groups: int = 16, pairs: bool = False) -> Tableset:
     if isinstance(tensors, np.ndarray):
         tensors = [tensors]
     arrs = [np.ascontiguousarray(t, ELEM_DTYPE[dtype]).ravel() for t in tensors]
     ptrs = (C.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
     h = C.c_void_p()
-    _check(lib().zno_setup(dtype, ptrs, _u64arr([a.size for a in arrs]), len(arrs), chunk_bytes,
-                           n_groups, C.byref(h)), "setup")
+    _check(lib().zno_setup2(dtype, ptrs, _u64arr([a.size for a in arrs]), len(arrs), chunk_bytes,
+                            n_groups, SETUP_PAIRS if pairs else 0, C.byref(h)), "setup")
     return Tableset(h, dtype)
 
 

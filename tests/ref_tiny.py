@@ -363,8 +363,69 @@ def encode_stream_tans(syms, k, S):
     return bytes(out)
 
 
+# ------------------------------------------------- packed exponent pairs ----
+# Restated from the codec's reading of NeuralZip's packed exponents: in each
+# 32-value strip, values 2i and 2i+1 are a pair position; a group's pair code
+# has F (its 16 most common values, most common first, ties to the smaller
+# value), tokens 0..255 for single values and 256 + 16*rank(x) + rank(y) for
+# a pair of values of F, and one length per token.
+def pair_F(pooled):
+    order = sorted((s for s in range(256) if pooled[s]), key=lambda s: (-pooled[s], s))
+    return order[:16]
+
+
+def strip_tokens(vals, F, tlen):
+    rank = {v: i for i, v in enumerate(F)}
+    toks, i = [], 0
+    while i < len(vals):
+        if i + 1 < len(vals):
+            x, y = vals[i], vals[i + 1]
+            if x in rank and y in rank and tlen[256 + 16 * rank[x] + rank[y]]:
+                toks.append(256 + 16 * rank[x] + rank[y])
+            else:
+                toks += [x, y]
+            i += 2
+        else:
+            toks.append(vals[i])
+            i += 1
+    return toks
+
+
+def pair_setup(chunks, gmap, K, single_lens):
+    """chunks: the exponent list of every chunk; gmap: group of each chunk;
+    single_lens: each group's single-value lengths.  Returns per group
+    (packs, F, token lengths)."""
+    out = []
+    for g in range(K):
+        pooled = [0] * 256
+        for c, ex in enumerate(chunks):
+            if gmap[c] == g:
+                for v in ex:
+                    pooled[v] += 1
+        F = pair_F(pooled)
+        rank = {v: i for i, v in enumerate(F)}
+        counts = [0] * 512
+        for c, ex in enumerate(chunks):
+            if gmap[c] != g:
+                continue
+            for a in range(0, len(ex), 32):
+                st = ex[a:a + 32]
+                for i in range(0, len(st), 2):
+                    if i + 1 < len(st) and st[i] in rank and st[i + 1] in rank:
+                        counts[256 + 16 * rank[st[i]] + rank[st[i + 1]]] += 1
+                    else:
+                        for v in st[i:i + 2]:
+                            counts[v] += 1
+        tlen = group_lengths(counts)
+        tok_bits = sum(c * l for c, l in zip(counts, tlen))
+        single_bits = sum(pooled[s] * single_lens[g][s] for s in range(256))
+        out.append((tok_bits < single_bits, F, tlen))
+    return out
+
+
 def encode_stream(syms, k, S, group=None, force_raw=False):
-    """One stream section; group = (lengths, id) to try GROUP mode."""
+    """One stream section; group = (lengths, id) or (lengths, id, (F, token
+    lengths)) to try GROUP mode (with pair tokens)."""
     n = len(syms)
     A = 1 << k
     h = [0] * A
@@ -379,7 +440,29 @@ def encode_stream(syms, k, S, group=None, force_raw=False):
         raw_size = rh + a16(rp)
         mode, aux, lens = RAW, 0, None
         tried = False
-        if group is not None:
+        if group is not None and len(group) == 3:
+            gl, gid, (F, tlen) = group
+            toks = [t for a in range(0, n, 32) for t in strip_tokens(syms[a:a + 32], F, tlen)]
+            if all(tlen[t] > 0 for t in toks):
+                tried = True
+                bits = sum(tlen[t] for t in toks)
+                gh, gp = section(GROUP, k, n, nseg, bits)
+                if gh + a16(gp) >= raw_size:
+                    return encode_stream(syms, k, S, None, force_raw=True)
+                out = bytearray(gh + a16(gp))
+                struct.pack_into("<BBHI", out, 0, GROUP, gid, nseg, gp)
+                codes = canonical(tlen)
+                bw = Bits()
+                for j in range(nseg):
+                    b0 = bw.n
+                    for a in range(j * 32, n, nseg * 32):
+                        for t in strip_tokens(syms[a:a + 32], F, tlen):
+                            bw.code(codes[t], tlen[t])
+                    struct.pack_into("<H", out, 8 + 2 * j, bw.n - b0)
+                if gp:
+                    out[gh:gh + gp] = bw.tobytes(gp)
+                return bytes(out)
+        elif group is not None:
             gl, gid = group
             if all(gl[s] > 0 for s in present):
                 tried = True
@@ -419,7 +502,8 @@ def encode_stream(syms, k, S, group=None, force_raw=False):
 
 
 def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0, tans=False):
-    """tensors: lists of ints (bit patterns); groups: (lengths per group, map);
+    """tensors: lists of ints (bit patterns); groups: (lengths per group, map)
+    or (lengths per group, map, pair codes per group as pair_setup gives);
     tans: the exponent stream with the tANS coder."""
     T = len(tensors)
     ce = chunk_bytes // ESIZE[dt]
@@ -446,7 +530,10 @@ def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0, tans=Fals
             for p in range(NCODED[dt]):
                 grp = None
                 if groups is not None and p == 0:
-                    grp = (groups[0][groups[1][c]], groups[1][c])
+                    g = groups[1][c]
+                    grp = (groups[0][g], g)
+                    if len(groups) == 3 and groups[2][g][0]:
+                        grp = (groups[0][g], g, (groups[2][g][1], groups[2][g][2]))
                 if tans and p == 0:
                     rec += encode_stream_tans(planes[p], kbits(dt, p), SEG[dt])
                 else:
@@ -477,8 +564,9 @@ def encode_container(dt, tensors, chunk_bytes, groups=None, ts_hash=0, tans=Fals
     return bytes(out)
 
 
-def decode_container(blob, group_lengths_table=None):
-    """Parses and decodes a container; returns the list of tensors (ints)."""
+def decode_container(blob, group_lengths_table=None, pair_codes=None):
+    """Parses and decodes a container; returns the list of tensors (ints).
+    pair_codes: per group (packs, F, token lengths), as pair_setup gives."""
     (magic, ver, dt, flags, T, cb, ntot, M, S, L, nc, h, off_dir, off_rec,
      total) = struct.unpack_from("<IHBBIIQIHBBQQQQ", blob, 0)
     assert magic == 0x31464E5A and ver == 1 and L == MAX_LEN
@@ -531,6 +619,35 @@ def decode_container(blob, group_lengths_table=None):
                         q += A // 2
                     else:
                         lens = list(group_lengths_table[aux])
+                        if pair_codes is not None and pair_codes[aux][0]:
+                            _, F, tlen = pair_codes[aux]
+                            seg_bits = [struct.unpack_from("<H", blob, q + 2 * j)[0] for j in range(nseg)]
+                            head = a16(q + 2 * nseg - pos)
+                            codes = canonical(tlen)
+                            table = {(tlen[t], codes[t]): t for t in range(512) if tlen[t]}
+                            v = int.from_bytes(blob[pos + head:pos + head + pay], "little")
+                            bitpos, syms = 0, [None] * m
+                            for j in range(nseg):
+                                end = bitpos + seg_bits[j]
+                                order = list(segment_order(m, nseg, j))
+                                got = []
+                                while len(got) < len(order):
+                                    code, l = 0, 0
+                                    while True:
+                                        code = (code << 1) | ((v >> bitpos) & 1)
+                                        bitpos += 1
+                                        l += 1
+                                        if (l, code) in table:
+                                            t = table[(l, code)]
+                                            break
+                                        assert l < MAX_LEN
+                                    got += [t] if t < 256 else [F[(t - 256) >> 4], F[(t - 256) & 15]]
+                                assert len(got) == len(order) and bitpos == end
+                                for i, val in zip(order, got):
+                                    syms[i] = val
+                            planes.append(syms)
+                            pos += head + a16(pay)
+                            continue
                     seg_bits = [struct.unpack_from("<H", blob, q + 2 * j)[0] for j in range(nseg)]
                     head = a16(q + 2 * nseg - pos)
                     codes = canonical(lens)
