@@ -92,6 +92,24 @@ zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t 
                    int n_tensors, uint32_t chunk_bytes, int n_groups, hipStream_t stream,
                    zn_tableset **out);
 
+/* zn_setup2 -- zn_setup with flags.  ZN_SETUP_PAIRS: packed exponent pairs
+ * ("NeuralZip: Reusable Setup for Fast Lossless Compression", Abstract:
+ * recurring exponent tuples represented by packed exponents, chosen by the
+ * setup).  After the grouping, each group's 16 most common exponent values
+ * (F) are found, the group's tokens are counted on the GPU -- in every
+ * 32-value strip of a chunk's exponents, values 2i and 2i+1 both in F make
+ * one pair token, every other value a single token -- each group gets an
+ * optimal code (lengths <= 11) over its 512 tokens, and it packs when that
+ * code takes fewer bits than its single-value code on its own chunks.
+ * zn_compress then codes a packing group's chunks with tokens, and
+ * zn_decompress reads them.  BF16 with n_groups >= 1 only (ZN_ERR_ARG
+ * otherwise, and for unknown flags).  The saved tableset is format version 2.
+ * Everything else as zn_setup. */
+enum { ZN_SETUP_PAIRS = 1 };
+zn_status zn_setup2(zn_dtype dtype, const void *const *d_tensors, const uint64_t *n_elems,
+                    int n_tensors, uint32_t chunk_bytes, int n_groups, int flags, hipStream_t stream,
+                    zn_tableset **out);
+
 /* zn_setup_transfer -- a setup reused on other tensors of the same dtype and
  * chunk size, such as another architecture of the same kind ("NeuralZip: Reusable
  * Setup for Fast Lossless Compression", Abstract).  The new plan keeps src's
@@ -228,6 +246,12 @@ zn_status zn_tableset_save(const zn_tableset *ts, void *h_buf, uint64_t cap, uin
 zn_status zn_tableset_load(const void *h_buf, uint64_t len, zn_tableset **out);
 /* Group g's code lengths (alphabet of the exponent stream) and the chunk map. */
 zn_status zn_tableset_lengths(const zn_tableset *ts, int g, uint8_t *h_len);
+/* Group g's packed-pair code (host outputs, any may be NULL): has_pairs = 1
+ * if the setup was made with ZN_SETUP_PAIRS; packed = 1 if the group packs;
+ * n_values = |F|; h_values[16] = F by rank (zero past |F|); h_token_len[512]
+ * = token code lengths (singles 0..255, pair 256 + 16*rank(x) + rank(y)). */
+zn_status zn_tableset_pairs(const zn_tableset *ts, int g, int *has_pairs, int *packed, int *n_values,
+                            uint8_t *h_values, uint8_t *h_token_len);
 zn_status zn_tableset_map(const zn_tableset *ts, uint8_t *h_map);
 /* Setup objective (total coded exponent bits) before each of the 8 Lloyd
  * rounds and after the last one: h_cost[9]. */

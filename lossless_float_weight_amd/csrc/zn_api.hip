@@ -37,12 +37,20 @@ struct zn_tableset {
   std::vector<uint8_t> len;            // [K][256] group code lengths
   std::vector<uint8_t> map;            // [n_chunks] group of each chunk
   std::vector<unsigned long long> cost;  // objective per setup round (diagnostic)
+  // packed exponent pairs (pairs = 1 when the setup was asked for them):
+  // per group the packing flag, |F|, F[16] and the 512 token lengths
+  int pairs = 0;
+  std::vector<uint8_t> packed, nF, F, tlen;
   // device copies
   uint64_t *d_n = nullptr, *d_raw = nullptr;
   uint32_t *d_chunk0 = nullptr;
   uint8_t *d_hdr = nullptr;
   uint8_t *d_map = nullptr, *d_len = nullptr;
   uint32_t *d_enc = nullptr, *d_lut = nullptr;
+  // for packing groups: len/enc/lut hold the token code's singles and its
+  // one-token decode table; penc the pair tokens' codes, rank F's ranks
+  uint8_t *d_packed = nullptr, *d_rank = nullptr;
+  uint32_t *d_penc = nullptr;
   int device = 0;
 };
 
@@ -78,13 +86,17 @@ DevLayout dev_layout(const zn_tableset *ts) {
 
 int alphabet0(int dt) { return 1 << kbits(dt, 0); }
 
+// per group of a version-2 tableset (with pairs): packing flag, |F|, F[16],
+// the 512 token lengths two per byte (even token in the low nibble)
+constexpr int kTsPairBytes = 274;
 uint64_t serial_bytes(const zn_tableset *ts) {
-  return 24 + 8ull * ts->T + uint64_t(ts->K) * (alphabet0(ts->dtype) / 2) + ts->n_chunks;
+  return 24 + 8ull * ts->T + uint64_t(ts->K) * (alphabet0(ts->dtype) / 2) + ts->n_chunks +
+         (ts->pairs ? uint64_t(ts->K) * kTsPairBytes : 0);
 }
 void serialise(const zn_tableset *ts, uint8_t *b) {
   const int A = alphabet0(ts->dtype);
   put_u32(b, kTsMagic);
-  put_u16(b + 4, kVersion);
+  put_u16(b + 4, ts->pairs ? 2 : kVersion);
   b[6] = uint8_t(ts->dtype);
   b[7] = uint8_t(ts->K);
   put_u32(b + 8, ts->chunk_bytes);
@@ -96,6 +108,14 @@ void serialise(const zn_tableset *ts, uint8_t *b) {
   for (int g = 0; g < ts->K; g++)
     for (int s = 0; s < A; s += 2) *q++ = uint8_t(ts->len[g * 256 + s] | (ts->len[g * 256 + s + 1] << 4));
   if (ts->n_chunks) memcpy(q, ts->map.data(), ts->n_chunks);
+  q += ts->n_chunks;
+  for (int g = 0; ts->pairs && g < ts->K; g++) {
+    *q++ = ts->packed[g];
+    *q++ = ts->nF[g];
+    memcpy(q, ts->F.data() + 16 * g, 16);
+    q += 16;
+    for (int t = 0; t < 512; t += 2) *q++ = uint8_t(ts->tlen[512 * g + t] | (ts->tlen[512 * g + t + 1] << 4));
+  }
 }
 uint64_t fnv1a64(const uint8_t *b, uint64_t n) {
   uint64_t h = 14695981039346656037ull;
@@ -115,10 +135,15 @@ void free_device(zn_tableset *ts) {
   (void)hipFree(ts->d_len);
   (void)hipFree(ts->d_enc);
   (void)hipFree(ts->d_lut);
+  (void)hipFree(ts->d_packed);
+  (void)hipFree(ts->d_rank);
+  (void)hipFree(ts->d_penc);
   ts->d_n = ts->d_raw = nullptr;
   ts->d_chunk0 = nullptr;
   ts->d_hdr = ts->d_map = ts->d_len = nullptr;
   ts->d_enc = ts->d_lut = nullptr;
+  ts->d_packed = ts->d_rank = nullptr;
+  ts->d_penc = nullptr;
 }
 
 // Host layout of the container for the plan's tensors.
@@ -191,6 +216,12 @@ zn_status finish_plan(zn_tableset *ts) {
   return ZN_OK;
 }
 
+struct DevBufU8 {
+  uint8_t *p = nullptr;
+  ~DevBufU8() { (void)hipFree(p); }
+  hipError_t alloc(size_t n) { return hipMalloc(&p, n ? n : 1); }
+};
+
 // Device group tables (encode codes, decode tables) from host lengths and map.
 zn_status upload_groups(zn_tableset *ts, hipStream_t s) {
   const int K = ts->K;
@@ -204,10 +235,32 @@ zn_status upload_groups(zn_tableset *ts, hipStream_t s) {
   if (ts->n_chunks)
     HIPCHK(hipMemcpyAsync(ts->d_map, ts->map.data(), ts->n_chunks, hipMemcpyHostToDevice, s));
   HIPCHK(hipMemcpyAsync(ts->d_len, ts->len.data(), 256ull * K, hipMemcpyHostToDevice, s));
+  // packing flags (all zero without pairs) and F's ranks, for the kernels
+  std::vector<uint8_t> pk(K, 0), rank(256ull * K, 0xFF);
+  for (int g = 0; ts->pairs && g < K; g++) {
+    pk[g] = ts->packed[g];
+    for (int i = 0; i < ts->nF[g]; i++) rank[256ull * g + ts->F[16 * g + i]] = uint8_t(i);
+  }
+  if (!ts->d_packed) {
+    HIPCHK(hipMalloc(&ts->d_packed, K));
+    HIPCHK(hipMalloc(&ts->d_rank, 256ull * K));
+    HIPCHK(hipMalloc(&ts->d_penc, 4ull * 256 * K));
+  }
+  HIPCHK(hipMemcpyAsync(ts->d_packed, pk.data(), K, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(ts->d_rank, rank.data(), 256ull * K, hipMemcpyHostToDevice, s));
+  DevBufU8 tl, fv;
   uint32_t *ctl = nullptr;
   HIPCHK(hipMalloc(&ctl, 4));
   HIPCHK(hipMemsetAsync(ctl, 0, 4, s));
   hipError_t e = launch_group_tables(ts->d_len, K, alphabet0(ts->dtype), ts->d_enc, ts->d_lut, ctl, s);
+  if (e == hipSuccess && ts->pairs) {
+    e = tl.alloc(512ull * K);
+    if (e == hipSuccess) e = fv.alloc(16ull * K);
+    if (e == hipSuccess) e = hipMemcpyAsync(tl.p, ts->tlen.data(), 512ull * K, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(fv.p, ts->F.data(), 16ull * K, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = launch_pair_tables(tl.p, fv.p, ts->d_packed, K, ts->d_len, ts->d_enc, ts->d_penc, ts->d_lut, ctl, s);
+  }
   uint32_t flag = 0;
   if (e == hipSuccess) e = hipMemcpyAsync(&flag, ctl, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -273,6 +326,26 @@ zn_status run_grouping(zn_tableset *ts, const void *const *d_tensors, hipStream_
   HIPCHK(hipMemcpyAsync(ts->cost.data(), cost.p, 8ull * (kRounds + 1), hipMemcpyDeviceToHost, s));
   HIPCHK(hipMemcpyAsync(ts->len.data(), len.p, 256ull * K, hipMemcpyDeviceToHost, s));
   HIPCHK(hipMemcpyAsync(ts->map.data(), map.p, M, hipMemcpyDeviceToHost, s));
+  if (ts->pairs) {
+    // packed exponent pairs from the final assignment: pooled holds the final
+    // groups' histograms (the last round measures only) and len their codes
+    DevBuf<unsigned long long> tok;
+    DevBuf<uint8_t> F, nF, rank, tlen, packed;
+    if (tok.alloc(512ull * K) || F.alloc(16ull * K) || nF.alloc(K) || rank.alloc(256ull * K) ||
+        tlen.alloc(512ull * K) || packed.alloc(K))
+      return ZN_ERR_NOMEM;
+    HIPCHK(hipMemsetAsync(tok.p, 0, 8 * 512ull * K, s));
+    HIPCHK(launch_pairs(L, ptrs.p, map.p, pooled.p, len.p, K, F.p, nF.p, rank.p, tok.p, tlen.p, packed.p, s));
+    ts->F.assign(16ull * K, 0);
+    ts->nF.assign(K, 0);
+    ts->tlen.assign(512ull * K, 0);
+    ts->packed.assign(K, 0);
+    HIPCHK(hipMemcpyAsync(ts->F.data(), F.p, 16ull * K, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(ts->nF.data(), nF.p, K, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(ts->tlen.data(), tlen.p, 512ull * K, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(ts->packed.data(), packed.p, K, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+  }
   HIPCHK(hipStreamSynchronize(s));
   return ZN_OK;
 }
@@ -329,13 +402,28 @@ void zn_tableset_free(zn_tableset *ts) {
 zn_status zn_setup(zn_dtype dtype, const void *const *d_tensors, const uint64_t *n_elems,
                    int n_tensors, uint32_t chunk_bytes, int n_groups, hipStream_t stream,
                    zn_tableset **out) {
+  return zn_setup2(dtype, d_tensors, n_elems, n_tensors, chunk_bytes, n_groups, 0, stream, out);
+}
+
+zn_status zn_setup2(zn_dtype dtype, const void *const *d_tensors, const uint64_t *n_elems,
+                    int n_tensors, uint32_t chunk_bytes, int n_groups, int flags, hipStream_t stream,
+                    zn_tableset **out) {
   if (!out || n_groups < 0 || n_groups > 255) return ZN_ERR_ARG;
   *out = nullptr;
+  if ((flags & ~ZN_SETUP_PAIRS) || ((flags & ZN_SETUP_PAIRS) && (dtype != ZN_BF16 || n_groups < 1)))
+    return ZN_ERR_ARG;
   zn_tableset *ts = new (std::nothrow) zn_tableset;
   if (!ts) return ZN_ERR_NOMEM;
   zn_status st = make_plan(ts, dtype, n_elems, n_tensors, chunk_bytes);
   ts->K = n_groups;
+  ts->pairs = (flags & ZN_SETUP_PAIRS) ? 1 : 0;
   ts->len.assign(256ull * n_groups, 0);  // group tables are serialised with the plan
+  if (ts->pairs) {                       // and so are the pair codes
+    ts->packed.assign(n_groups, 0);
+    ts->nF.assign(n_groups, 0);
+    ts->F.assign(16ull * n_groups, 0);
+    ts->tlen.assign(512ull * n_groups, 0);
+  }
   if (st == ZN_OK && n_groups > 0) {
     if (!d_tensors) st = ZN_ERR_ARG;
     for (int t = 0; st == ZN_OK && t < n_tensors; t++)
@@ -366,6 +454,11 @@ zn_status zn_setup_transfer(const zn_tableset *src, const void *const *d_tensors
     ts->K = src->K;
     ts->len = src->len;    // the source's codes, unchanged
     ts->cost = src->cost;  // and the history of their fit
+    ts->pairs = src->pairs;  // with their pair codes
+    ts->packed = src->packed;
+    ts->nF = src->nF;
+    ts->F = src->F;
+    ts->tlen = src->tlen;
     for (int t = 0; t < n_tensors; t++)
       if (n_elems[t] && !d_tensors[t]) st = ZN_ERR_ARG;
   }
@@ -501,6 +594,9 @@ zn_status zn_compress2(const zn_tableset *ts, int coder, const void *const *d_in
   a.group_map = ts->K ? ts->d_map : nullptr;
   a.group_enc = ts->d_enc;
   a.group_len = ts->d_len;
+  a.group_packed = ts->K ? ts->d_packed : nullptr;
+  a.group_rank = ts->d_rank;
+  a.group_penc = ts->d_penc;
   a.out = static_cast<uint8_t *>(d_out);
   a.plans = scr + plans_offset(ts);
   a.plan_stride = plan_bytes(ts->dtype, ts->chunk_elems);
@@ -520,6 +616,11 @@ zn_status zn_compress2(const zn_tableset *ts, int coder, const void *const *d_in
   PackArgs pk;
   pk.L = a.L;
   pk.in_ptrs = a.in_ptrs;
+  pk.group_packed = a.group_packed;
+  pk.group_rank = a.group_rank;
+  pk.group_penc = a.group_penc;
+  pk.pairs = 0;
+  for (int g = 0; ts->pairs && g < ts->K; g++) pk.pairs |= ts->packed[g];
   pk.plans = a.plans;
   pk.plan_stride = a.plan_stride;
   pk.out = a.out;
@@ -570,6 +671,7 @@ zn_status decompress_with(const zn_tableset *ts, const void *d_in, uint64_t in_b
   a.out_ptrs = reinterpret_cast<uint8_t *const *>(d_out_ptrs);
   a.group_lut = ts->d_lut;
   a.group_len = ts->d_len;
+  a.group_packed = ts->K ? ts->d_packed : nullptr;
   a.K = ts->K;
   a.ctl = ctl;
   HIPCHK(launch_decode(ts->dtype, a, stream, g_ev_before[KDecode], g_ev_after[KDecode]));
@@ -648,13 +750,18 @@ zn_status zn_tableset_load(const void *h_buf, uint64_t len, zn_tableset **out) {
   const uint8_t *b = static_cast<const uint8_t *>(h_buf);
   if (!b || !out) return ZN_ERR_ARG;
   *out = nullptr;
-  if (len < 24 || get_u32(b) != kTsMagic || get_u16(b + 4) != kVersion || get_u32(b + 20) != kMaxLen)
-    return ZN_ERR_CORRUPT;
+  if (len < 24 || get_u32(b) != kTsMagic || get_u32(b + 20) != kMaxLen) return ZN_ERR_CORRUPT;
+  // version 2: with the pair codes of packed exponent pairs (BF16 with groups)
+  const int ver = int(get_u16(b + 4));
   const int dt = b[6], K = b[7], T = int(get_u32(b + 12));
   const uint32_t cb = get_u32(b + 8), M = get_u32(b + 16);
-  if (!valid_dtype(dt) || !valid_chunk(cb) || T < 1 || uint64_t(T) > len / 8) return ZN_ERR_CORRUPT;
+  if ((ver != kVersion && ver != 2) || !valid_dtype(dt) || !valid_chunk(cb) || T < 1 || uint64_t(T) > len / 8)
+    return ZN_ERR_CORRUPT;
+  const int pairs = ver == 2;
+  if (pairs && (dt != BF16 || K < 1)) return ZN_ERR_CORRUPT;
   const int A = alphabet0(dt);
-  if (len != 24 + 8ull * T + uint64_t(K) * (A / 2) + M) return ZN_ERR_CORRUPT;
+  if (len != 24 + 8ull * T + uint64_t(K) * (A / 2) + M + (pairs ? uint64_t(K) * kTsPairBytes : 0))
+    return ZN_ERR_CORRUPT;
   std::vector<uint64_t> n(T);
   for (int t = 0; t < T; t++) n[t] = get_u64(b + 24 + 8 * t);
   zn_tableset *ts = new (std::nothrow) zn_tableset;
@@ -672,10 +779,44 @@ zn_status zn_tableset_load(const void *h_buf, uint64_t len, zn_tableset **out) {
         if ((*q & 15) > kMaxLen || (*q >> 4) > kMaxLen) st = ZN_ERR_CORRUPT;
       }
     if (M) memcpy(ts->map.data(), q, M);
+    q += M;
     // a plan without groups stores its map as zero bytes; with groups each
     // byte names one of the K groups
     for (uint32_t c = 0; c < M && st == ZN_OK; c++)
       if (K ? ts->map[c] >= K : ts->map[c] != 0) st = ZN_ERR_CORRUPT;
+    ts->pairs = pairs;
+    if (pairs) {
+      ts->packed.assign(K, 0);
+      ts->nF.assign(K, 0);
+      ts->F.assign(16ull * K, 0);
+      ts->tlen.assign(512ull * K, 0);
+    }
+    for (int g = 0; pairs && g < K && st == ZN_OK; g++, q += kTsPairBytes) {
+      // a flag, at most 16 distinct values of F (zero past |F|), lengths
+      // within the limit, no pair token past |F|, and a packing group's
+      // token code complete (Kraft equality, two tokens at least)
+      const int nf = q[1];
+      ts->packed[g] = q[0];
+      ts->nF[g] = q[1];
+      memcpy(ts->F.data() + 16 * g, q + 2, 16);
+      if (q[0] > 1 || nf > 16) st = ZN_ERR_CORRUPT;
+      uint8_t seen[256] = {0};
+      for (int i = 0; i < 16 && st == ZN_OK; i++)
+        if (i < nf ? seen[q[2 + i]]++ != 0 : q[2 + i] != 0) st = ZN_ERR_CORRUPT;
+      uint64_t kraft = 0;
+      int d = 0;
+      for (int t = 0; t < 512 && st == ZN_OK; t++) {
+        const int l = (q[18 + t / 2] >> (4 * (t & 1))) & 15;
+        ts->tlen[512ull * g + t] = uint8_t(l);
+        if (l > kMaxLen) st = ZN_ERR_CORRUPT;
+        if (t >= 256 && (((t - 256) >> 4) >= nf || ((t - 256) & 15) >= nf) && l) st = ZN_ERR_CORRUPT;
+        if (l && l <= kMaxLen) {
+          kraft += 1ull << (kMaxLen - l);
+          d++;
+        }
+      }
+      if (st == ZN_OK && q[0] && (d < 2 || kraft != (1ull << kMaxLen))) st = ZN_ERR_CORRUPT;
+    }
   }
   if (st == ZN_ERR_ARG) st = ZN_ERR_CORRUPT;
   if (st == ZN_OK) st = finish_plan(ts);
@@ -691,6 +832,23 @@ zn_status zn_tableset_load(const void *h_buf, uint64_t len, zn_tableset **out) {
 zn_status zn_tableset_lengths(const zn_tableset *ts, int g, uint8_t *h_len) {
   if (!ts || !h_len || g < 0 || g >= ts->K) return ZN_ERR_ARG;
   memcpy(h_len, ts->len.data() + 256ull * g, size_t(alphabet0(ts->dtype)));
+  return ZN_OK;
+}
+
+zn_status zn_tableset_pairs(const zn_tableset *ts, int g, int *has_pairs, int *packed, int *n_values,
+                            uint8_t *h_values, uint8_t *h_token_len) {
+  if (!ts || g < 0 || g >= ts->K) return ZN_ERR_ARG;
+  if (has_pairs) *has_pairs = ts->pairs;
+  if (packed) *packed = ts->pairs ? ts->packed[g] : 0;
+  if (n_values) *n_values = ts->pairs ? ts->nF[g] : 0;
+  if (h_values) {
+    memset(h_values, 0, 16);
+    if (ts->pairs) memcpy(h_values, ts->F.data() + 16 * g, 16);
+  }
+  if (h_token_len) {
+    memset(h_token_len, 0, 512);
+    if (ts->pairs) memcpy(h_token_len, ts->tlen.data() + 512ull * g, 512);
+  }
   return ZN_OK;
 }
 

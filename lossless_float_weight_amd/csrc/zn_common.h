@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace zn {
 
 constexpr int kMaxLen = 11;           // longest code word, bits
@@ -156,17 +158,21 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v) {
 }
 
 // ------------------------------------------------------- package-merge ----
-// Shared memory of one code construction (about 18 KB).
-struct PMShared {
-  uint64_t w[2][512];               // item weights of the previous/current list
-  uint64_t leaf_w[256];             // leaves sorted by (count, symbol)
-  uint8_t leafcl[kMaxLen][256];     // packages ahead of sorted leaf i in list j
-  uint8_t leaf_sym[256];
-  uint8_t tmp_sym[256];
+// Shared memory of one code construction over at most AM symbols (about
+// 18 KB for 256, 33 KB for 512).
+template <int AM>
+struct PMSharedA {
+  using Sym = std::conditional_t<(AM > 256), uint16_t, uint8_t>;
+  uint64_t w[2][2 * AM];            // item weights of the previous/current list
+  uint64_t leaf_w[AM];              // leaves sorted by (count, symbol)
+  Sym leafcl[kMaxLen][AM];          // packages ahead of sorted leaf i in list j
+  Sym leaf_sym[AM];
+  Sym tmp_sym[AM];
   int c[kMaxLen];                   // leaves among the selected prefix of list j
   int d;
-  int wave_cnt[4];
+  int wave_cnt[AM / 64];
 };
+using PMShared = PMSharedA<256>;
 // present symbols in symbol order, before sorting (shares w[1], which is
 // written only from the first merge on)
 #define PM_TMP_W(S) ((S).w[1])
@@ -182,23 +188,28 @@ struct PMShared {
 // Returns d, the number of symbols with non-zero weight (after the group
 // rule, which adds the smallest absent symbol with weight 0 when d == 1).
 // len[0..A) is written for every symbol (0 when absent).
-template <int NT>
-__device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rule, uint8_t *len) {
-  static_assert(NT >= 256, "code construction needs at least 256 threads");
+template <int NT, int AM = 256>
+__device__ int pm_lengths(PMSharedA<AM> &S, const uint64_t *hw, int A, bool group_rule, uint8_t *len) {
+  static_assert(NT >= AM, "code construction needs a thread per symbol");
+  using Sym = typename PMSharedA<AM>::Sym;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
   const bool nz = tid < A && hw[tid] != 0;
   const uint64_t m = __ballot(nz);
-  if (ln == 0 && wv < 4) S.wave_cnt[wv] = __popcll(m);
+  if (ln == 0 && wv < AM / 64) S.wave_cnt[wv] = __popcll(m);
   if (tid < A) len[tid] = 0;
   __syncthreads();
   if (nz) {
     int base = 0;
     for (int q = 0; q < wv; q++) base += S.wave_cnt[q];
     const int idx = base + __popcll(m & lanemask_lt());
-    S.tmp_sym[idx] = uint8_t(tid);
+    S.tmp_sym[idx] = Sym(tid);
     PM_TMP_W(S)[idx] = hw[tid];
   }
-  if (tid == 0) S.d = S.wave_cnt[0] + S.wave_cnt[1] + S.wave_cnt[2] + S.wave_cnt[3];
+  if (tid == 0) {
+    int d = 0;
+    for (int q = 0; q < AM / 64; q++) d += S.wave_cnt[q];
+    S.d = d;
+  }
   __syncthreads();
   int d = S.d;
   if (group_rule && d == 1) {
@@ -221,7 +232,7 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
       r += (wj < w) || (wj == w && S.tmp_sym[j] < s);
     }
     S.leaf_w[r] = w;
-    S.leaf_sym[r] = uint8_t(s);
+    S.leaf_sym[r] = Sym(s);
     S.w[0][r] = w;
     S.leafcl[0][r] = 0;
   }
@@ -240,7 +251,7 @@ __device__ int pm_lengths(PMShared &S, const uint64_t *hw, int A, bool group_rul
           if (prev[2 * mid] + prev[2 * mid + 1] < wi) lo = mid + 1; else hi = mid;
         }
         cur[q + lo] = wi;
-        S.leafcl[j][q] = uint8_t(lo);
+        S.leafcl[j][q] = Sym(lo);
       } else {      // package k: after every leaf not heavier than it
         const int k = q - d;
         const uint64_t p = prev[2 * k] + prev[2 * k + 1];

@@ -61,6 +61,7 @@ struct DecShared {
   int mode[NC], aux[NC];
   unsigned long long pay_off[NC], seg_off[NC];
   unsigned long long tq_off;      // a tANS first stream: its presence mask
+  int gpacked;                    // the first stream's group codes packed pairs
   uint32_t pay[NC];
   uint32_t wtot[DEC_NT / 64][NC];   // [wave][coded stream index]
   int bad;
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
   // ------------------------------------------------- 1. walk the record
   if (tid == 0) {
     int bad = 0, tsbad = 0;
+    sh.gpacked = 0;
     if (r0 < a.L.off_records || r1 < r0 || r1 + 16 > a.in_bytes || (r0 & 15)) bad = 1;
     uint64_t pos = r0;
     for (int p = 0; p < NC && !bad; p++) {
@@ -223,6 +225,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       if (mode == GROUP && (p != 0 || !grouped || pay == 0 || (pay & 3))) bad = 1;
       if (mode == GROUP && !bad && aux >= a.K) tsbad = 1;
       if (mode == GROUP && !bad && !tsbad && ldg4(a.group_lut + size_t(aux) * kLutSize) == 0) bad = 1;
+      if (mode == GROUP && !bad && !tsbad) sh.gpacked = a.group_packed ? ldg1(a.group_packed + aux) : 0;
       if (tsbad) break;
       sh.mode[p] = mode;
       sh.aux[p] = aux;
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           pre = rp[__builtin_amdgcn_ubfe(wpos, 0, 5) * DEC_NT];
           const uint8_t *lutb = reinterpret_cast<const uint8_t *>(lut);
           uint32_t *const stw = reinterpret_cast<uint32_t *>(sh.u.stage);   // abase is a multiple of 8
-          auto step = [&]() {
+          auto step = [&]() -> uint32_t {
             const uint32_t e = *reinterpret_cast<const uint32_t *>(lutb + (uint32_t(W) & wmask));
             cur |= uint64_t(e >> 8) << ((a & 3) * 8);   // unused symbol bytes of an entry are zero
             stw[a >> 2] = uint32_t(cur);
@@ -622,7 +625,12 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             a = an;
             W >>= (e & 63);
             nbk -= e & 0xFF;
+            return e;
           };
+          // packed pairs take one token per table entry: the staging place
+          // after the first lookup of the last pair, and the second's entry,
+          // tell the exact end of the segment
+          uint32_t a1 = a, e2 = 0;
           while (a < alim) {
             const uint32_t t = nbk + (a << 6);   // nb + 2
             const bool need = t < 32;
@@ -631,7 +639,8 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             wpos += need ? 1u : 0u;
             pre = rp[__builtin_amdgcn_ubfe(wpos, 0, 5) * DEC_NT];
             step();
-            step();
+            a1 = a;
+            e2 = step();
           }
           stw[a >> 2] = uint32_t(cur);   // the last, partial word
           const int pos = int(a - abase);
@@ -640,9 +649,19 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
           if (last) {
             // exact end: the segment must use exactly its stored bit length
             uint64_t bpos = uint64_t(wpos - adj) * 32 - uint32_t(nb);
-            for (int x = 0; x < ov; x++) {
-              const int bb = lim + x;
-              bpos -= sh.len[p][sb[bb]];
+            if (p == 0 && sh.gpacked) {
+              // tokens of packed pairs: past the end may lie only the whole
+              // token of the last lookup, after a first lookup that ended
+              // exactly there (a pair across the end is not a valid stream)
+              if (ov > 0) {
+                if (a1 == alim && uint32_t(ov) == ((e2 >> 6) & 3)) bpos -= e2 & 63;
+                else bad = 1;
+              }
+            } else {
+              for (int x = 0; x < ov; x++) {
+                const int bb = lim + x;
+                bpos -= sh.len[p][sb[bb]];
+              }
             }
             if (bpos != uint64_t(b0) + sbits) bad = 1;
             ov = 0;

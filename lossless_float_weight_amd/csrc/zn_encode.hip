@@ -289,6 +289,11 @@ struct PackShared {
     std::conditional_t<TC, TansPack, uint32_t> tans;
   } su;
   uint32_t wtot[2][PACK_NW];
+  // BF16 chunks of a group that packs exponent pairs: the pair tokens' codes
+  // and F's ranks
+  static constexpr int PA = DT == BF16 ? 256 : 1;
+  uint32_t penc[PA];
+  uint8_t prk[PA];
   // 1-byte elements: one tile's words of a raw stream (32 strips per segment,
   // up to 4 words per strip), written from the coded stream's tiles
   static constexpr bool RSTAGE = DT == FP8 || DT == FP4X2;
@@ -413,11 +418,30 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
       const int g = ldg1(a.group_map + c);
       const uint32_t ef = (load_elem<DT>(src) >> 7) & 0xFF;   // the chunk's first exponent
       unsigned long long *tbl = reinterpret_cast<unsigned long long *>(sh.u.priv);
+      // a group that packs exponent pairs ("NeuralZip", Abstract: recurring
+      // tuples as packed exponents): each aligned pair of values of its F
+      // with a pair code costs that code's length instead of the two
+      // singles' (tbl then holds the token code's single lengths)
+      const bool packed = a.group_packed && ldg1(a.group_packed + g);
+      uint8_t *rk = reinterpret_cast<uint8_t *>(sh.u.priv + 512);        // F's ranks
+      uint8_t *plen = reinterpret_cast<uint8_t *>(sh.u.priv + 576);      // pair code lengths
       if (tid < 256) {
         const uint32_t l = ldg1(a.group_len + g * 256 + tid);
         tbl[tid] = l | (uint64_t(l == 0) << 16) | (uint64_t(uint32_t(tid) == ef) << 32);
+        if (packed) {
+          rk[tid] = uint8_t(ldg1(a.group_rank + g * 256 + tid));
+          plen[tid] = uint8_t(ldg4(a.group_penc + g * 256 + tid) >> 16);
+        }
       }
       __syncthreads();
+      // one aligned pair's entry: the pair code's length (bits 0-15) with
+      // the two values' "equals the first" counts, or the two singles
+      auto pair_cost = [&](uint32_t x, uint32_t y) -> unsigned long long {
+        const unsigned long long sxy = tbl[x] + tbl[y];
+        const uint32_t rx = rk[x], ry = rk[y];
+        const uint32_t pl = (rx | ry) < 16 ? plen[16 * rx + ry] : 0u;
+        return pl ? (sxy & ~0xFFFFFFFFull) | pl : sxy;
+      };
       unsigned long long acc = 0;
       constexpr int B0 = 4;  // 16-byte loads in flight per thread
       for (uint32_t v0 = tid; v0 < nvec; v0 += B0 * ENC_NT) {
@@ -433,20 +457,39 @@ __device__ __forceinline__ uint64_t analyze_chunk(const EncArgs &a, EncShared<DT
           if (v >= nvec) break;
           const uint4 q = make_uint4(qs[b][0], qs[b][1], qs[b][2], qs[b][3]);
           uint32_t lo = 0, hi = 0;
+          if (packed) {   // a vector holds 4 aligned pairs
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              acc += pair_cost((vec_elem<DT>(q, 2 * j) >> 7) & 0xFF, (vec_elem<DT>(q, 2 * j + 1) >> 7) & 0xFF);
+          }
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const uint32_t w0 = vec_elem<DT>(q, i), w1 = vec_elem<DT>(q, i + 4);
-            acc += tbl[(w0 >> 7) & 0xFF] + tbl[(w1 >> 7) & 0xFF];
+            if (!packed) acc += tbl[(w0 >> 7) & 0xFF] + tbl[(w1 >> 7) & 0xFF];
             lo |= (((w0 >> 8) & 0x80) | (w0 & 0x7F)) << (8 * i);
             hi |= (((w1 >> 8) & 0x80) | (w1 & 0x7F)) << (8 * i);
           }
           stg8(rawp + e0 + uint64_t(v) * 8, u32x2{lo, hi});
         }
       }
-      for (uint32_t i = nvec * VE + tid; i < n; i += ENC_NT) {  // ragged tail or unaligned input
-        const uint32_t w = load_elem<DT>(src + uint64_t(i) * ES);
-        acc += tbl[(w >> 7) & 0xFF];
-        stg1(rawp + e0 + i, ((w >> 8) & 0x80) | (w & 0x7F));
+      if (packed) {   // ragged tail or unaligned input: pairs from even positions
+        for (uint32_t i = nvec * VE + 2 * tid; i < n; i += 2 * ENC_NT) {
+          const uint32_t w = load_elem<DT>(src + uint64_t(i) * ES);
+          stg1(rawp + e0 + i, ((w >> 8) & 0x80) | (w & 0x7F));
+          if (i + 1 < n) {
+            const uint32_t w1 = load_elem<DT>(src + uint64_t(i + 1) * ES);
+            stg1(rawp + e0 + i + 1, ((w1 >> 8) & 0x80) | (w1 & 0x7F));
+            acc += pair_cost((w >> 7) & 0xFF, (w1 >> 7) & 0xFF);
+          } else {
+            acc += tbl[(w >> 7) & 0xFF];   // a lone last value
+          }
+        }
+      } else {
+        for (uint32_t i = nvec * VE + tid; i < n; i += ENC_NT) {  // ragged tail or unaligned input
+          const uint32_t w = load_elem<DT>(src + uint64_t(i) * ES);
+          acc += tbl[(w >> 7) & 0xFF];
+          stg1(rawp + e0 + i, ((w >> 8) & 0x80) | (w & 0x7F));
+        }
       }
       const unsigned long long bits = block_sum<DT>(sh, acc & 0xFFFFu);
       const unsigned long long nmiss = block_sum<DT>(sh, (acc >> 16) & 0xFFFFu);
@@ -869,14 +912,16 @@ __device__ void pack_tans(const uint8_t *src, uint32_t n, bool aligned, int nseg
 // The record of chunk c at recp: stream heads, raw streams, coded payloads.
 // The choice per stream (mode, aux, payload bits, section offset) and the
 // code words come from LDS; stage and wtot are LDS scratch of this function.
-template <int DT, bool TC>
+// PK: some group codes packed exponent pairs (BF16 only)
+template <int DT, bool TC, bool PK = false>
 __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *const *in_ptrs, uint32_t c,
                                            uint8_t *const recp, const uint32_t (*enc)[256], const int *pmode,
                                            const int *paux, const unsigned long long *pbits,
                                            const unsigned long long *psec,
                                            uint32_t (*stage_all)[PackShared<DT>::STAGE],
                                            uint32_t (*wtot)[PACK_NW], uint32_t *rawt,
-                                           const uint8_t *segbits, TansPack *tans) {
+                                           const uint8_t *segbits, TansPack *tans,
+                                           const uint32_t *penc, const uint8_t *prk, bool packed) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
@@ -1128,13 +1173,36 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
 #pragma unroll
         for (int g8 = 0; g8 < NG; g8++) {
           uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+          bool pairs = false;
+          if constexpr (DT == BF16 && GE % 2 == 0 && PK) pairs = packed && p == 0;
+          if (pairs) {
+            // aligned pairs (a run starts at an even place of its strip): a
+            // pair of values of F with a pair code is one token, its second
+            // slot empty; otherwise two singles (a value past the chunk's end
+            // none, a lone last value a single)
 #pragma unroll
-          for (int i = 0; i < GE; i++) {
-            const int e = g8 * GE + i;
-            const uint32_t ce = enc[p][field_rt<DT>(w[e], p)];
-            const uint32_t c = uint32_t(e) < lim ? ce : 0u;
-            v[i] = c & 0xFFFF;
-            l[i] = c >> 16;
+            for (int j = 0; j < GE / 2; j++) {
+              const int e = g8 * GE + 2 * j;
+              const uint32_t x = field_rt<DT>(w[e], 0), y = field_rt<DT>(w[e + 1], 0);
+              const uint32_t rx = prk[x], ry = prk[y];
+              const uint32_t pc = (rx | ry) < 16 ? penc[16 * rx + ry] : 0u;
+              const bool tok = uint32_t(e + 1) < lim && (pc >> 16) != 0;
+              const uint32_t c0 = tok ? pc : uint32_t(e) < lim ? enc[0][x] : 0u;
+              const uint32_t c1 = tok ? 0u : uint32_t(e + 1) < lim ? enc[0][y] : 0u;
+              v[2 * j] = c0 & 0xFFFF;
+              l[2 * j] = c0 >> 16;
+              v[2 * j + 1] = c1 & 0xFFFF;
+              l[2 * j + 1] = c1 >> 16;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < GE; i++) {
+              const int e = g8 * GE + i;
+              const uint32_t ce = enc[p][field_rt<DT>(w[e], p)];
+              const uint32_t c = uint32_t(e) < lim ? ce : 0u;
+              v[i] = c & 0xFFFF;
+              l[i] = c >> 16;
+            }
           }
           const uint32_t c01 = v[0] | (v[1] << l[0]), l01 = l[0] + l[1];
           const uint32_t c23 = v[2] | (v[3] << l[2]), l23 = l[2] + l[3];
@@ -1261,7 +1329,7 @@ __device__ __forceinline__ TansPack *tans_of(PackShared<DT, TC> &sh) {
 }
 
 // One workgroup per chunk: the record at its directory offset.
-template <int DT, bool TC>
+template <int DT, bool TC, bool PK = false>
 __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   constexpr int NC = ncoded(DT);
   __shared__ PackShared<DT, TC> sh;
@@ -1277,6 +1345,15 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
       sh.enc[p][tid] = mode == RAW ? uint32_t(tid) | (uint32_t(k) << 16)
                      : (mode == HUFF || mode == GROUP || mode == TANS) ? ldg4(plan + 64 + 1024 * p + 4 * tid) : 0u;
   }
+  bool packed = false;
+  if constexpr (DT == BF16 && PK) {
+    const int g = plan[52];
+    packed = plan[48] == GROUP && a.group_packed && ldg1(a.group_packed + g);
+    if (packed) {
+      sh.penc[tid] = ldg4(a.group_penc + g * 256 + tid);
+      sh.prk[tid] = uint8_t(ldg1(a.group_rank + g * 256 + tid));
+    }
+  }
   if (tid < NC) {
     sh.mode[tid] = plan[48 + tid];
     sh.aux[tid] = plan[52 + tid];
@@ -1284,8 +1361,8 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
     sh.sec_off[tid] = *reinterpret_cast<const uint32_t *>(plan + 32 + 4 * tid);
   }
   const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
-  pack_chunk<DT, TC>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off,
-                     sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), tans_of(sh));
+  pack_chunk<DT, TC, PK>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off,
+                     sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), tans_of(sh), sh.penc, sh.prk, packed);
 }
 
 // One workgroup: exclusive scan of the record sizes into the directory, then
@@ -1373,6 +1450,7 @@ hipError_t launch_pack(int dtype, const PackArgs &a, hipStream_t s, hipEvent_t e
   const bool tc = a.coder == CODER_TANS;
   if (dtype == BF16) {
     if (tc) hipExtLaunchKernelGGL((k_pack<BF16, true>), grid, block, 0, s, e0, e1, 0, a);
+    else if (a.pairs) hipExtLaunchKernelGGL((k_pack<BF16, false, true>), grid, block, 0, s, e0, e1, 0, a);
     else hipExtLaunchKernelGGL((k_pack<BF16, false>), grid, block, 0, s, e0, e1, 0, a);
   } else if (dtype == FP32) {
     if (tc) hipExtLaunchKernelGGL((k_pack<FP32, true>), grid, block, 0, s, e0, e1, 0, a);

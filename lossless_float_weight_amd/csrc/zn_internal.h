@@ -15,6 +15,9 @@ struct EncArgs {
   const uint8_t *group_map;        // [n_chunks] or nullptr
   const uint32_t *group_enc;       // [K][256] bit-reversed code | len << 16
   const uint8_t *group_len;        // [K][256]
+  const uint8_t *group_packed;     // [K] 1: the group codes packed exponent pairs (BF16)
+  const uint8_t *group_rank;       // [K][256] rank of a value in the group's F, or 0xFF
+  const uint32_t *group_penc;      // [K][256] pair token codes, as group_enc
   uint8_t *out;                    // container (the raw planes are written here)
   uint8_t *plans;                  // [n_chunks][plan_stride] code choice and code words
   uint64_t plan_stride;            // plan_bytes(dtype, chunk_elems)
@@ -25,6 +28,10 @@ struct EncArgs {
 struct PackArgs {
   DevLayout L;
   const uint8_t *const *in_ptrs;
+  const uint8_t *group_packed;     // as in EncArgs
+  const uint8_t *group_rank;
+  const uint32_t *group_penc;
+  int pairs;                       // some group packs exponent pairs
   const uint8_t *plans;
   uint64_t plan_stride;
   uint8_t *out;
@@ -52,6 +59,7 @@ struct DecArgs {
   uint8_t *const *out_ptrs;        // [T] device pointers
   const uint32_t *group_lut;       // [K][2048]
   const uint8_t *group_len;        // [K][256]
+  const uint8_t *group_packed;     // [K] 1: one token per table entry (packed pairs)
   int K;
   uint32_t *ctl;                   // [0] error bits
 };
@@ -105,5 +113,15 @@ hipError_t launch_assign(const uint32_t *hist, int stride_words, int A, uint32_t
                          int K, int reassign, uint8_t *map, unsigned long long *cost, hipStream_t s);
 hipError_t launch_keys(const uint32_t *hist, int stride_words, int A, const DevLayout &L,
                        unsigned long long *keys, hipStream_t s);
+// packed exponent pairs (BF16): F, ranks, token counts and lengths, packing flags
+hipError_t launch_pairs(const DevLayout &L, const uint8_t *const *in_ptrs, const uint8_t *map,
+                        const unsigned long long *pooled /* [K][256] */, const uint8_t *len /* [K][256] */,
+                        int K, uint8_t *F /* [K][16] */, uint8_t *nF /* [K] */, uint8_t *rank /* [K][256] */,
+                        unsigned long long *tok /* [K][512], zeroed */, uint8_t *tlen /* [K][512] */,
+                        uint8_t *packed /* [K] */, hipStream_t s);
+// a packing group's tables: len/enc take the single tokens, penc the pairs,
+// lut the one-token decode table; non-packing groups are left alone
+hipError_t launch_pair_tables(const uint8_t *tlen, const uint8_t *F, const uint8_t *packed, int K, uint8_t *len,
+                              uint32_t *enc, uint32_t *penc, uint32_t *lut, uint32_t *ctl, hipStream_t s);
 
 }  // namespace zn

@@ -11,6 +11,14 @@
 //   k_lengths      optimal lengths (<= 11) of a histogram, one per workgroup
 //   k_group_tables encode table and decode table of each group
 //   k_assign       each chunk to the group code of least coded size
+// and, for packed exponent pairs ("NeuralZip", Abstract: recurring exponent
+// tuples represented by packed exponents, chosen by the setup):
+//   k_pair_F       each group's 16 most common values (F) and their ranks
+//   k_pair_tokens  each group's token counts: pairs of values of F at the
+//                  aligned positions of each 32-value strip, singles otherwise
+//   k_token_lengths optimal lengths (<= 11) over the 512 tokens of a group
+//   k_pair_decide  a group packs when its tokens take fewer pooled bits
+//   k_pair_tables  encode tables and a one-token decode table of a packing group
 #include "zn_internal.h"
 
 namespace zn {
@@ -308,6 +316,195 @@ __global__ __launch_bounds__(256) void k_assign(const uint32_t *hist, int stride
   if (ln == 0) wsum[tid >> 6] = wave_cost;
   __syncthreads();
   if (tid == 0) atomicAdd(cost, wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+}
+
+// ------------------------------------------------ packed exponent pairs ----
+// F of group g: the values of largest pooled count (ties to the smaller
+// value), at most 16, present values only; rank[g][v] = v's place in F or
+// 0xFF.  One workgroup per group.
+__global__ __launch_bounds__(256) void k_pair_F(const unsigned long long *pooled, uint8_t *F, uint8_t *nF,
+                                                uint8_t *rank) {
+  __shared__ unsigned long long h[256];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  const unsigned long long mine = pooled[uint64_t(g) * 256 + tid];
+  h[tid] = mine;
+  __syncthreads();
+  int r = 0;   // values ahead of this one in (count descending, value ascending) order
+  for (int s = 0; s < 256; s++) {
+    const unsigned long long o = h[s];
+    r += (o > mine) || (o == mine && s < tid);
+  }
+  const int present = __syncthreads_count(mine != 0);
+  const int n = present < 16 ? present : 16;
+  const bool in = mine != 0 && r < 16;
+  rank[uint64_t(g) * 256 + tid] = in ? uint8_t(r) : uint8_t(0xFF);
+  if (in) F[g * 16 + r] = uint8_t(tid);
+  if (tid >= n && tid < 16) F[g * 16 + tid] = 0;
+  if (tid == 0) nF[g] = uint8_t(n);
+}
+
+// Token counts of the groups: one workgroup per chunk, LDS bins in 4 lane
+// columns, then one global add per non-zero bin.  Token 256 + 16 rank(x) +
+// rank(y) for an aligned pair of values of F (a 16-byte vector holds 4
+// aligned pairs), the single token of each other value.
+__global__ __launch_bounds__(256) void k_pair_tokens(DevLayout L, const uint8_t *const *in_ptrs,
+                                                     const uint8_t *map, const uint8_t *rank,
+                                                     unsigned long long *tok) {
+  __shared__ uint32_t bins[4][512];
+  __shared__ uint8_t rk[256];
+  const int tid = threadIdx.x, col = tid & 3;
+  const uint32_t c = blockIdx.x;
+  const int g = ldg1(map + c);
+  rk[tid] = ldg1(rank + uint64_t(g) * 256 + tid);
+  for (int i = tid; i < 4 * 512; i += 256) bins[i >> 9][i & 511] = 0;
+  __syncthreads();
+  const int t = find_tensor(L, c);
+  const uint64_t e0 = uint64_t(c - L.t_chunk0[t]) * L.chunk_elems;
+  const uint64_t rem = L.t_n[t] - e0;
+  const uint32_t n = uint32_t(rem < L.chunk_elems ? rem : L.chunk_elems);
+  const uint8_t *src = in_ptrs[t] + e0 * 2;
+  const bool aligned = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  const uint32_t nvec = aligned ? n / 8 : 0;
+  auto pair = [&](uint32_t x, uint32_t y) {
+    const uint32_t rx = rk[x], ry = rk[y];
+    if ((rx | ry) < 16) {
+      atomicAdd(&bins[col][256 + 16 * rx + ry], 1u);
+    } else {
+      atomicAdd(&bins[col][x], 1u);
+      atomicAdd(&bins[col][y], 1u);
+    }
+  };
+  for (uint32_t v = tid; v < nvec; v += 256) {
+    const u32x4 q = ldg16(src + 16ull * v);
+#pragma unroll
+    for (int i = 0; i < 4; i++) pair((q[i] >> 7) & 0xFF, (q[i] >> 23) & 0xFF);
+  }
+  for (uint32_t i = nvec * 8 + 2 * tid; i < n; i += 512) {   // the tail, pairs from even positions
+    const uint32_t x = (ldg2(src + 2ull * i) >> 7) & 0xFF;
+    if (i + 1 < n) pair(x, (ldg2(src + 2ull * i + 2) >> 7) & 0xFF);
+    else atomicAdd(&bins[col][x], 1u);   // a lone last value
+  }
+  __syncthreads();
+  for (int i = tid; i < 512; i += 256) {
+    const uint32_t v = bins[0][i] + bins[1][i] + bins[2][i] + bins[3][i];
+    if (v) atomicAdd(tok + uint64_t(g) * 512 + i, (unsigned long long)v);
+  }
+}
+
+// Lengths over a group's 512 token counts (the group rule for one token).
+__global__ __launch_bounds__(512) void k_token_lengths(const unsigned long long *tok, uint8_t *tlen) {
+  __shared__ PMSharedA<512> pm;
+  __shared__ uint64_t w[512];
+  __shared__ uint8_t l[512];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  w[tid] = tok[uint64_t(g) * 512 + tid];
+  __syncthreads();
+  pm_lengths<512, 512>(pm, w, 512, true, l);
+  __syncthreads();
+  tlen[uint64_t(g) * 512 + tid] = l[tid];
+}
+
+// A group packs when its pooled token bits are fewer than its pooled single
+// bits under its single-value code.
+__global__ __launch_bounds__(256) void k_pair_decide(const unsigned long long *tok, const uint8_t *tlen,
+                                                     const unsigned long long *pooled, const uint8_t *len,
+                                                     uint8_t *packed) {
+  __shared__ unsigned long long sb[4], ss[4];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  const uint64_t o = uint64_t(g) * 512;
+  unsigned long long bt = tok[o + tid] * tlen[o + tid] + tok[o + 256 + tid] * tlen[o + 256 + tid];
+  unsigned long long bs = pooled[uint64_t(g) * 256 + tid] * len[uint64_t(g) * 256 + tid];
+  bt = wave_sum64(bt);
+  bs = wave_sum64(bs);
+  if ((tid & 63) == 0) {
+    sb[tid >> 6] = bt;
+    ss[tid >> 6] = bs;
+  }
+  __syncthreads();
+  if (tid == 0) packed[g] = (sb[0] + sb[1] + sb[2] + sb[3]) < (ss[0] + ss[1] + ss[2] + ss[3]) ? 1 : 0;
+}
+
+// Tables of a packing group: canonical codes over the 512 tokens (singles
+// into enc and the single lengths into len, pairs into penc), and the decode
+// table with one token per entry: the window's bits used | values (1 or 2)
+// << 6 | the values, first in bits 8..15.  A token code that is not complete
+// is a tableset error.  One workgroup of 512 per group.
+__global__ __launch_bounds__(512) void k_pair_tables(const uint8_t *tlen, const uint8_t *F, const uint8_t *packed,
+                                                     uint8_t *len, uint32_t *enc, uint32_t *penc, uint32_t *lut,
+                                                     uint32_t *ctl) {
+  __shared__ int cnt[8][kMaxLen + 1];
+  __shared__ uint32_t lt[kLutSize];
+  __shared__ uint8_t f[16];
+  const int tid = threadIdx.x, g = blockIdx.x, wv = tid >> 6, ln = tid & 63;
+  if (!packed[g]) return;
+  const int l = tlen[uint64_t(g) * 512 + tid];
+  if (tid < 16) f[tid] = F[g * 16 + tid];
+  for (int i = tid; i < kLutSize; i += 512) lt[i] = 0;
+  int rank = 0;
+  for (int b = 1; b <= kMaxLen; b++) {
+    const uint64_t m = __ballot(l == b);
+    if (l == b) rank = __popcll(m & lanemask_lt());
+    if (ln == 0) cnt[wv][b] = __popcll(m);
+  }
+  const int kr = __syncthreads_count(l != 0) >= 2;
+  int kraft_part = l ? 1 << (kMaxLen - l) : 0;
+  const int full = kr ? 1 : 0;
+  uint32_t e = 0;
+  if (l) {
+    uint32_t code = 0;
+    for (int b = 1; b <= l; b++) {
+      int prevc = 0;
+      if (b > 1)
+        for (int q = 0; q < 8; q++) prevc += cnt[q][b - 1];
+      code = (code + prevc) << 1;
+    }
+    for (int q = 0; q < wv; q++) code += cnt[q][l];
+    code += rank;
+    e = (__builtin_bitreverse32(code) >> (32 - l)) | (uint32_t(l) << 16);
+  }
+  if (tid < 256) {
+    enc[g * 256 + tid] = e;
+    len[g * 256 + tid] = uint8_t(l);
+  } else {
+    penc[g * 256 + tid - 256] = e;
+  }
+  // Kraft equality over the tokens
+  __shared__ int ksum;
+  if (tid == 0) ksum = 0;
+  __syncthreads();
+  kraft_part = wave_sum(kraft_part);
+  if (ln == 0) atomicAdd(&ksum, kraft_part);
+  __syncthreads();
+  if (!full || ksum != kLutSize) {
+    if (tid == 0) atomicOr(ctl, kErrTableset);
+    return;
+  }
+  if (l) {
+    const uint32_t vals = tid < 256 ? uint32_t(tid) : uint32_t(f[(tid - 256) >> 4]) | (uint32_t(f[(tid - 256) & 15]) << 8);
+    const uint32_t ent = uint32_t(l) | ((tid < 256 ? 1u : 2u) << 6) | (vals << 8);
+    const uint32_t rev = e & 0xFFFFu;
+    for (uint32_t k = 0; k < (1u << (kMaxLen - l)); k++) lt[rev | (k << l)] = ent;
+  }
+  __syncthreads();
+  for (int i = tid; i < kLutSize; i += 512) lut[uint64_t(g) * kLutSize + i] = lt[i];
+}
+
+hipError_t launch_pairs(const DevLayout &L, const uint8_t *const *in_ptrs, const uint8_t *map,
+                        const unsigned long long *pooled, const uint8_t *len, int K, uint8_t *F, uint8_t *nF,
+                        uint8_t *rank, unsigned long long *tok, uint8_t *tlen, uint8_t *packed, hipStream_t s) {
+  if (K <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pair_F, dim3(K), dim3(256), 0, s, pooled, F, nF, rank);
+  if (L.n_chunks) hipLaunchKernelGGL(k_pair_tokens, dim3(L.n_chunks), dim3(256), 0, s, L, in_ptrs, map, rank, tok);
+  hipLaunchKernelGGL(k_token_lengths, dim3(K), dim3(512), 0, s, tok, tlen);
+  hipLaunchKernelGGL(k_pair_decide, dim3(K), dim3(256), 0, s, tok, tlen, pooled, len, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_tables(const uint8_t *tlen, const uint8_t *F, const uint8_t *packed, int K, uint8_t *len,
+                              uint32_t *enc, uint32_t *penc, uint32_t *lut, uint32_t *ctl, hipStream_t s) {
+  if (K <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pair_tables, dim3(K), dim3(512), 0, s, tlen, F, packed, len, enc, penc, lut, ctl);
+  return hipGetLastError();
 }
 
 hipError_t launch_hist_all(int dtype, const DevLayout &L, const uint8_t *const *in_ptrs,

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libzn.so")
 
 BF16, FP32, FP8_E4M3, FP4X2_E2M1 = 0, 1, 2, 3
 CODER_HUFFMAN, CODER_TANS = 0, 1
+SETUP_PAIRS = 1
 # FP4 E2M1 pairs travel as uint8 tensors (two values per byte, low nibble first)
 TORCH_DTYPE = {BF16: torch.bfloat16, FP32: torch.float32, FP8_E4M3: torch.float8_e4m3fn,
                FP4X2_E2M1: torch.uint8}
@@ -46,6 +47,8 @@ def lib() -> C.CDLL:
         P, U64, I, U32 = C.c_void_p, C.c_uint64, C.c_int, C.c_uint32
         PU64 = C.POINTER(C.c_uint64)
         L.zn_setup.argtypes = [I, C.POINTER(P), PU64, I, U32, I, P, C.POINTER(P)]
+        L.zn_setup2.argtypes = [I, C.POINTER(P), PU64, I, U32, I, I, P, C.POINTER(P)]
+        L.zn_tableset_pairs.argtypes = [P, I, C.POINTER(I), C.POINTER(I), C.POINTER(I), P, P]
         L.zn_setup_transfer.argtypes = [P, C.POINTER(P), PU64, I, P, C.POINTER(P)]
         L.zn_plan_from_container.argtypes = [P, U64, P, C.POINTER(P)]
         L.zn_header_info.argtypes = [P, U64, C.POINTER(I), C.POINTER(I), PU64, C.POINTER(U32),
@@ -147,6 +150,18 @@ class Tableset:
         _check(lib().zn_tableset_lengths(self.handle, g, buf), "tableset_lengths")
         return list(buf)
 
+    def pairs(self, g: int):
+        """Group g's packed-pair code: (packs, F as a list, token lengths as a
+        list of 512), or None when the setup has no pair codes."""
+        has, packed, nf = C.c_int(), C.c_int(), C.c_int()
+        F = (C.c_uint8 * 16)()
+        tl = (C.c_uint8 * 512)()
+        _check(lib().zn_tableset_pairs(self.handle, g, C.byref(has), C.byref(packed), C.byref(nf), F, tl),
+               "tableset_pairs")
+        if not has.value:
+            return None
+        return bool(packed.value), list(F)[: nf.value], list(tl)
+
     def group_map(self) -> list:
         buf = (C.c_uint8 * max(1, self.info()["n_chunks"]))()
         _check(lib().zn_tableset_map(self.handle, buf), "tableset_map")
@@ -173,9 +188,10 @@ class Tableset:
 
 
 def setup(tensors: Sequence[torch.Tensor] | None = None, *, dtype=None, n_elems=None,
-          chunk_bytes: int = 262144, n_groups: int = 0, stream=None) -> Tableset:
-    """zn_setup: a plan for these tensor sizes; with n_groups > 0 the chunks of
-    `tensors` are grouped and share code tables."""
+          chunk_bytes: int = 262144, n_groups: int = 0, pairs: bool = False, stream=None) -> Tableset:
+    """zn_setup (zn_setup2 with pairs): a plan for these tensor sizes; with
+    n_groups > 0 the chunks of `tensors` are grouped and share code tables;
+    pairs adds packed exponent pairs (BF16)."""
     if tensors is not None:
         tensors = [t.contiguous() for t in tensors]
         dtype = ZN_DTYPE[tensors[0].dtype]
@@ -185,8 +201,8 @@ def setup(tensors: Sequence[torch.Tensor] | None = None, *, dtype=None, n_elems=
         ptrs = None
         dtype = ZN_DTYPE.get(dtype, dtype)
     h = C.c_void_p()
-    _check(lib().zn_setup(int(dtype), ptrs, _u64(n_elems), len(n_elems), chunk_bytes, n_groups,
-                          _stream(stream), C.byref(h)), "setup")
+    _check(lib().zn_setup2(int(dtype), ptrs, _u64(n_elems), len(n_elems), chunk_bytes, n_groups,
+                           SETUP_PAIRS if pairs else 0, _stream(stream), C.byref(h)), "setup")
     return Tableset(h)
 
 

@@ -130,3 +130,40 @@ def test_header_info_equals_oracle_header_needs_no_gpu(oracle):
     assert _header_info(lib, blobs[0][:63].tobytes())[0] == -1      # too short: argument error
     lib.zn_header_info.argtypes = [ctypes.c_void_p, ctypes.c_uint64] + [ctypes.c_void_p] * 7
     assert lib.zn_header_info(None, 64, *([None] * 7)) == -1
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libzn.so not built")
+def test_pair_setup_arguments_and_bad_v2_tablesets_need_no_gpu(oracle):
+    # zn_setup2's flags are checked before any HIP call; a version-2 saved
+    # plan (with packed-pair codes) is validated as the oracle validates it
+    import numpy as np
+    lib = ctypes.CDLL(LIB)
+    out = ctypes.c_void_p()
+    n = (ctypes.c_uint64 * 1)(100000)
+    I = ctypes.c_int
+    lib.zn_setup2.argtypes = [I, ctypes.c_void_p, ctypes.c_void_p, I, ctypes.c_uint32, I, I, ctypes.c_void_p,
+                              ctypes.c_void_p]
+    assert lib.zn_setup2(1, None, n, 1, 262144, 4, 1, None, ctypes.byref(out)) == -1   # pairs on FP32
+    assert lib.zn_setup2(0, None, n, 1, 262144, 0, 1, None, ctypes.byref(out)) == -1   # pairs without groups
+    assert lib.zn_setup2(0, None, n, 1, 262144, 4, 2, None, ctypes.byref(out)) == -1   # unknown flag
+    rng = np.random.default_rng(1)
+    e = 120 + np.minimum(rng.geometric(0.45, 30000), 8)
+    e[1::2] = e[0::2]
+    x = ((e << 7) | rng.integers(0, 128, e.size)).astype(np.uint16)
+    ts = oracle.setup(oracle.BF16, [x], 4096, 2, pairs=True)
+    good = ts.save()
+    g = next(i for i in range(2) if ts.pairs(i)[0])
+    rec = 24 + 8 + 2 * 128 + ts.info()[1] + 274 * g
+    muts = [(rec, 2), (rec + 1, 17), (rec + 3, good[rec + 2]), (rec + 18, 0xCC), (rec + 18 + 200, 0x11)]
+    for pos, val in muts:
+        bad = bytearray(good)
+        bad[pos] = val
+        try:
+            oracle.Tableset.load(bytes(bad))
+            want = 0
+        except oracle.OracleError as err:
+            want = err.code
+        b = ctypes.create_string_buffer(bytes(bad), len(bad))
+        got = lib.zn_tableset_load(b, len(bad), ctypes.byref(out))
+        if want != 0:
+            assert got == want == -2, (pos, val, got, want)
