@@ -239,9 +239,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--coder", default="huffman", choices=("huffman", "tans"),
                     help="exponent coder (tans: tabled ANS, plans without groups)")
+    ap.add_argument("--pairs", action="store_true",
+                    help="packed exponent pairs in the grouped setup (model and transfer workloads)")
     args = ap.parse_args()
     if args.coder == "tans" and args.workload in ("model", "transfer"):
         raise SystemExit("--coder tans takes a workload without group tables")
+    if args.pairs and args.workload not in ("model", "transfer"):
+        raise SystemExit("--pairs takes a workload with group tables (model, transfer)")
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this codec's path runs on a single MI355X and shards "
               f"by chunk ranges with no exchange during decode; --gpus {args.gpus} is not run.",
@@ -275,9 +279,11 @@ def main():
         for _ in range(4):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            ts = zn.setup(base, chunk_bytes=CHUNK_BYTES, n_groups=16)
+            ts = zn.setup(base, chunk_bytes=CHUNK_BYTES, n_groups=16, pairs=args.pairs)
             torch.cuda.synchronize()
             times.append((time.perf_counter() - t0) * 1e3)
+        # with pairs: the same grouping without them, for the ratio they gain
+        ts_np = zn.setup(base, chunk_bytes=CHUNK_BYTES, n_groups=16) if args.pairs else None
         extra["setup_first_ms"] = round(times[0], 2)
         extra["setup_ms"] = round(sorted(times[1:])[1], 2)
         extra["setup_GBps"] = round(unc / (extra["setup_ms"] * 1e-3) / 1e9, 1)
@@ -287,17 +293,21 @@ def main():
     elif args.workload == "transfer":
         # the source setup on one architecture, reused on another by content
         src_tensors = make_tensors("block")
-        src = zn.setup(src_tensors, chunk_bytes=CHUNK_BYTES, n_groups=16)
+        src = zn.setup(src_tensors, chunk_bytes=CHUNK_BYTES, n_groups=16, pairs=args.pairs)
+        src_np = zn.setup(src_tensors, chunk_bytes=CHUNK_BYTES, n_groups=16) if args.pairs else None
         del src_tensors
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ts = zn.setup_transfer(src, base)
         torch.cuda.synchronize()
         extra["transfer_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        ts_np = zn.setup_transfer(src_np, base) if args.pairs else None
         gm = ts.group_map()
         extra["groups_used"] = len(set(gm))
     else:
         ts = zn.setup(base, chunk_bytes=CHUNK_BYTES)
+    if args.pairs:
+        extra["groups_packed"] = sum(ts.pairs(g)[0] for g in range(16))
     bound = zn.compress_bound(ts)
     R = max(1, args.rotate if args.workload != "model" else 1)
     sets = []
@@ -404,7 +414,8 @@ def main():
         avg = sum(kern_ms[k]) / len(kern_ms[k])
         gbps = algo[k] / (avg * 1e-3) / 1e9
         rl[k] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(k, args.workload + ("" if args.coder == "huffman" else "_tans")),
+                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(k, args.workload + ("" if args.coder == "huffman" else "_tans")
+                                                          + ("_pairs" if args.pairs else "")),
                  "kernel": f"k_{k}", "avg_ms": round(avg, 4), "algorithmic_bytes": algo[k],
                  "timed_in": "timed region" if k == dominant else f"breakdown pass ({nb_steps} steps)"}
     ms_step = total_ms / args.steps
@@ -422,7 +433,8 @@ def main():
         "vs_baseline": (round(value / BASELINE_VALUE, 4) if BASELINE_VALUE else None),
         "dtype": "u32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload], "coder": args.coder, "uncompressed_bytes": unc,
+        "config": {"workload": WORKLOADS[args.workload], "coder": args.coder, "pairs": args.pairs,
+                   "uncompressed_bytes": unc,
                    "container_bytes": nbytes, "chunk_bytes": CHUNK_BYTES, "tensors": len(base)},
         "decompress_GBps": round(unc / (med(dec_ms) * 1e-3) / 1e9, 2),
         "compress_GBps": round(unc / (med(comp_ms) * 1e-3) / 1e9, 2),
@@ -454,6 +466,12 @@ def main():
         stop_timing()
         per_chunk_ms = med([d[comp_first][0].elapsed_time(d[comp_last][1]) for d in pe])
         pbytes = int(pblob[56:64].cpu().numpy().view("<u8")[0])
+        if ts_np is not None:
+            del pblob, pscr
+            npb = zn.compress(ts_np, base, ptrs=ptrs).numel()
+            pblob = pscr = None
+            extra.update({"ratio_without_pairs": round(npb / unc, 5),
+                          "pairs_gain": round(1 - nbytes / npb, 6)})
         extra.update({"post_setup_compress_ms": round(med(comp_ms), 3),
                       "per_chunk_table_compress_ms": round(per_chunk_ms, 3),
                       "post_setup_speedup": round(per_chunk_ms / med(comp_ms), 3),
