@@ -208,6 +208,33 @@ def test_block_full_size_whole_container(oracle):
     assert g.size == o.size and np.array_equal(g, o), first_difference(g, o)
 
 
+def test_fp8_full_size_whole_container(oracle):
+    # the 2^30-value block-scaled FP8 tensor: both coded streams may take tANS
+    # lanes beside raw ones; the oracle works on the host meanwhile
+    print("case: tANS FP8 E4M3 2^30, whole-container parity", flush=True)
+    import time
+    t0 = time.time()
+    tensors = [W.fp8_blockscaled(1 << 30, device="cuda")[0][1]]
+    arrs = [to_np(t) for t in tensors]
+    import concurrent.futures as cf
+    ex = cf.ThreadPoolExecutor(1)
+    fut = ex.submit(oracle.compress, oracle.FP8_E4M3, arrs, 262144, None, False, oracle.CODER_TANS)
+    ex.shutdown(wait=False)
+    ts, blob = _tans(tensors, 262144)
+    g = blob.cpu().numpy()
+    print(f"  GPU container {g.size} bytes at {time.time() - t0:.0f} s", flush=True)
+    assert_roundtrip(ts, blob, tensors)
+    del blob
+    while True:
+        try:
+            o = fut.result(timeout=30)
+            break
+        except cf.TimeoutError:
+            print(f"  oracle still running at {time.time() - t0:.0f} s", flush=True)
+    print(f"  oracle container {o.size} bytes at {time.time() - t0:.0f} s", flush=True)
+    assert g.size == o.size and np.array_equal(g, o), first_difference(g, o)
+
+
 def test_every_decode_path_with_tans_lanes(oracle):
     # tANS exponent lanes next to Huffman lanes of the other streams in the
     # same wave (FP32 16 lanes per stream, FP8 and FP4 32), and next to raw
