@@ -231,15 +231,13 @@ __global__ __launch_bounds__(256) void k_group_tables(const uint8_t *len, int A,
 // Each chunk to the group code of least coded size (ties to the smaller id;
 // a chunk that every code lacks a symbol for keeps its group), and cost[0] +=
 // its coded size under its current group (all ones if that code lacks one of
-// its symbols).  The K code-length tables wait in LDS; one wave per chunk at a
-// time.  Lane l holds the counts of symbols l, l+64, l+128, l+192; for 16
-// groups at once it forms the partial sums sum_s h[s]*len_g[s], plus 2^40 per
-// present symbol without a code word (every true sum is below 2^40), and a
-// butterfly over the lanes halves the set of groups a lane carries at each
-// of its first four steps (17 exchanges instead of 16 full reductions):
-// afterwards lane l holds the total of group 8*b5 + 4*b4 + 2*b3 + b2, bi the
-// bits of l.
-constexpr unsigned long long kMissUnit = 1ull << 40;
+// its symbols).  One lane per chunk: for 16 groups at a time the lane sums
+// h[s] * len_g[s] over the symbols, the 16 lengths at symbol s being one
+// 16-byte LDS read that every lane shares (symbol-major table), so a term
+// costs a byte extract and a multiply-add and no lane exchange is needed.
+// The sums fit 32 bits (a chunk holds at most 2^20 elements, a length is at
+// most 11).  A code lacks one of the chunk's symbols when the chunk's
+// present-symbol mask meets the complement of the code's mask.
 __device__ __forceinline__ unsigned long long shx64(unsigned long long v, int m) {
   const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(v)), m, 64));
   const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(v >> 32)), m, 64));
@@ -248,72 +246,85 @@ __device__ __forceinline__ unsigned long long shx64(unsigned long long v, int m)
 __global__ __launch_bounds__(256) void k_assign(const uint32_t *hist, int stride, int A, uint32_t M,
                                                 const uint8_t *len, int K, int reassign, uint8_t *map,
                                                 unsigned long long *cost) {
-  extern __shared__ uint8_t lsh[];   // [K][256] code lengths
+  __shared__ alignas(16) uint8_t lb[256][16];   // lengths of 16 groups at each symbol
+  __shared__ uint32_t cmask[16][8];             // bit s: symbol s has a code word
+  __shared__ unsigned long long wsum[4];
   const int tid = threadIdx.x, ln = tid & 63;
-  for (int i = tid; i < K * 256; i += 256) lsh[i] = len[i];
-  __syncthreads();
-  const uint32_t nw = gridDim.x * 4;
-  unsigned long long wave_cost = 0;   // this wave's chunks, added to cost[0] once per workgroup
-  for (uint32_t c = blockIdx.x * 4 + (tid >> 6); c < M; c += nw) {
-    uint32_t h[4];
+  const uint32_t c = blockIdx.x * 256u + uint32_t(tid);
+  const bool live = c < M;
+  const uint32_t *hc = hist + uint64_t(live ? c : 0u) * uint32_t(stride);
+  const int cur = live ? int(ldg1(map + c)) : 0;
+  uint32_t pres[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // symbols present in the chunk
+  unsigned long long best = ~0ull, here = ~0ull;
+  int bg = cur;
+  auto block16 = [&](int s0, uint32_t (&h)[16]) {   // counts of symbols [s0, s0 + 16)
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const int s = ln + 64 * q;
-      h[q] = s < A ? ldg4(hist + uint64_t(c) * stride + s) : 0u;
+      const u32x4 v = live ? ldg16(hc + s0 + 4 * q) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; j++) h[4 * q + j] = v[j];
     }
-    const int cur = ldg1(map + c);
-    unsigned long long best = ~0ull, here = ~0ull;
-    int bg = cur;
-    for (int gb = 0; gb < K; gb += 16) {
-      unsigned long long v[16];
+  };
+  for (int gb = 0; gb < K; gb += 16) {
+    __syncthreads();   // the previous batch's tables are no longer read
+    for (int i = tid; i < 256 * 16; i += 256) {
+      const int sy = i >> 4, g = gb + (i & 15);
+      lb[sy][i & 15] = g < K && sy < A ? len[g * 256 + sy] : 0;
+    }
+    if (tid < 128) {
+      const int g = gb + (tid >> 3), w = tid & 7;
+      uint32_t m = 0;
+      if (g < K)
+        for (int j = 0; j < 32; j++) m |= uint32_t(32 * w + j < A && len[g * 256 + 32 * w + j] != 0) << j;
+      cmask[tid >> 3][w] = m;
+    }
+    __syncthreads();
+    uint32_t x[16];
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int g = gb + i;
-        unsigned long long x = 0;
-        if (g < K) {
+    for (int i = 0; i < 16; i++) x[i] = 0;
+    // counts loaded one block of 16 symbols ahead
+    uint32_t hn[16];
+    block16(0, hn);
+    for (int s0 = 0; s0 < A; s0 += 16) {
+      uint32_t h[16];
 #pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const int s = ln + 64 * q;
-            const uint32_t l = s < A ? lsh[g * 256 + s] : 0u;
-            x += uint64_t(h[q]) * l + (h[q] && !l ? kMissUnit : 0ull);
-          }
-        }
-        v[i] = x;
+      for (int j = 0; j < 16; j++) h[j] = hn[j];
+      if (s0 + 16 < A) block16(s0 + 16, hn);
+      if (gb == 0) {
+        uint32_t pm = 0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) pm |= uint32_t(h[j] != 0) << j;
+        pres[s0 >> 5] |= pm << (s0 & 16);
       }
 #pragma unroll
-      for (int half = 8, m = 32; half >= 1; half >>= 1, m >>= 1) {
-        const bool up = (ln & m) != 0;
+      for (int j = 0; j < 16; j++) {
+        const uint4 lq = *reinterpret_cast<const uint4 *>(&lb[s0 + j][0]);
+        const uint32_t lw[4] = {lq.x, lq.y, lq.z, lq.w};
 #pragma unroll
-        for (int i = 0; i < half; i++) {
-          const unsigned long long keep = up ? v[half + i] : v[i];
-          const unsigned long long send = up ? v[i] : v[half + i];
-          v[i] = keep + shx64(send, m);
-        }
-      }
-      unsigned long long t = v[0];
-      t += shx64(t, 2);
-      t += shx64(t, 1);
-      // group gb + i is in the lanes whose bits 5..2 are i's bits 3..0
-#pragma unroll
-      for (int i = 0; i < 16 && gb + i < K; i++) {
-        const int lane = ((i & 8) ? 32 : 0) | ((i & 4) ? 16 : 0) | ((i & 2) ? 8 : 0) | ((i & 1) ? 4 : 0);
-        const unsigned long long tot = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(t >> 32)), lane))) << 32) |
-                                       uint32_t(__builtin_amdgcn_readlane(int(uint32_t(t)), lane));
-        const unsigned long long x = tot >= kMissUnit ? ~0ull : tot;
-        if (gb + i == cur) here = x;
-        if (x < best) {
-          best = x;
-          bg = gb + i;
-        }
+        for (int i = 0; i < 16; i++) x[i] += h[j] * ((lw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
       }
     }
-    if (ln == 0 && reassign) map[c] = uint8_t(bg);
-    wave_cost += here;   // modulo 2^64, as one atomic add per chunk would be
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      if (gb + i >= K) break;
+      uint32_t miss = 0;
+#pragma unroll
+      for (int w = 0; w < 8; w++) miss |= pres[w] & ~cmask[i][w];
+      const unsigned long long tot = miss ? ~0ull : uint64_t(x[i]);
+      if (gb + i == cur) here = tot;
+      if (tot < best) {
+        best = tot;
+        bg = gb + i;
+      }
+    }
   }
-  // one atomic per workgroup: a single counter taking one add per chunk
-  // serialises tens of thousands of them
-  __shared__ unsigned long long wsum[4];
-  if (ln == 0) wsum[tid >> 6] = wave_cost;
+  if (live && reassign) map[c] = uint8_t(bg);
+  // modulo 2^64, as one atomic add per chunk would be; one atomic per
+  // workgroup, since a single counter taking one add per chunk serialises
+  // tens of thousands of them
+  unsigned long long v = live ? here : 0ull;
+  for (int m = 32; m >= 1; m >>= 1) v += shx64(v, m);
+  if (ln == 0) wsum[tid >> 6] = v;
   __syncthreads();
   if (tid == 0) atomicAdd(cost, wsum[0] + wsum[1] + wsum[2] + wsum[3]);
 }
@@ -564,9 +575,8 @@ hipError_t launch_group_tables(const uint8_t *len, int K, int A, uint32_t *enc, 
 hipError_t launch_assign(const uint32_t *hist, int stride, int A, uint32_t M, const uint8_t *len,
                          int K, int reassign, uint8_t *map, unsigned long long *cost, hipStream_t s) {
   if (!M || K <= 0) return hipSuccess;
-  const uint32_t blocks = (M + 3) / 4 < 2048 ? (M + 3) / 4 : 2048;
-  hipLaunchKernelGGL(k_assign, dim3(blocks), dim3(256), size_t(K) * 256, s, hist, stride, A, M, len, K,
-                     reassign, map, cost);
+  hipLaunchKernelGGL(k_assign, dim3((M + 255) / 256), dim3(256), 0, s, hist, stride, A, M, len, K, reassign,
+                     map, cost);
   return hipGetLastError();
 }
 
