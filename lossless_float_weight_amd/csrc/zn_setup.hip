@@ -153,22 +153,42 @@ __global__ void k_keys(const uint32_t *hist, int stride, int A, DevLayout L, uns
 // kPoolSlice chunks and adds each chunk's histogram to its group's row in
 // LDS (thread s owns symbol s, so no two threads share a counter), for up to
 // kPoolGroups groups at a time; the rows then go to pooled[g] with one
-// atomic add per non-zero counter.  A slice's counts fit 32 bits: at most
-// 4096 chunks of at most 2^19 elements.
+// atomic add per non-zero counter.  A slice's counts fit 32 bits: it holds
+// at most max(36, M / 2048 + 1) chunks and at most 4096, so its elements are
+// fewer than 36 * 2^20, or than 1/2048 of the input plus one chunk, or (with
+// more than 8M chunks, which device memory bounds to under 36 KiB each) than
+// 4096 * 2^16.
 constexpr int kPoolGroups = 32;
 constexpr uint32_t kPoolSlice = 4096;
 __global__ __launch_bounds__(256) void k_pool(const uint32_t *hist, int stride, int A, uint32_t M,
                                               const uint8_t *map, int K, unsigned long long *pooled) {
   __shared__ uint32_t acc[kPoolGroups][256];
+  __shared__ uint8_t gm[kPoolSlice];   // the slice's groups, read once
   const int tid = threadIdx.x;
   const uint32_t per = (M + gridDim.x - 1) / gridDim.x;
   const uint32_t c0 = blockIdx.x * per, c1 = c0 + per < M ? c0 + per : M;
+  const uint32_t nc = c1 > c0 ? c1 - c0 : 0u;
+  for (uint32_t i = tid; i < nc; i += 256) gm[i] = uint8_t(ldg1(map + c0 + i));
+  const uint32_t *hp = hist + uint64_t(c0) * uint32_t(stride) + tid;
   for (int gb = 0; gb < K; gb += kPoolGroups) {
     for (int g = 0; g < kPoolGroups; g++) acc[g][tid] = 0;
     __syncthreads();
-    for (uint32_t c = c0; c < c1; c++) {
-      const int g = int(ldg1(map + c)) - gb;   // the same for every thread
-      if (g >= 0 && g < kPoolGroups && tid < A) acc[g][tid] += ldg4(hist + uint64_t(c) * stride + tid);
+    // eight rows in flight at a time; a row's group is the same for every
+    // thread
+    uint32_t i = 0;
+    for (; i + 8 <= nc; i += 8) {
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) h[j] = tid < A ? ldg4(hp + uint64_t(i + j) * uint32_t(stride)) : 0u;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int g = int(gm[i + j]) - gb;
+        if (g >= 0 && g < kPoolGroups) acc[g][tid] += h[j];
+      }
+    }
+    for (; i < nc; i++) {
+      const int g = int(gm[i]) - gb;
+      if (g >= 0 && g < kPoolGroups && tid < A) acc[g][tid] += ldg4(hp + uint64_t(i) * uint32_t(stride));
     }
     __syncthreads();
     for (int g = 0; g < kPoolGroups && gb + g < K; g++)
