@@ -451,6 +451,12 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
       uint32_t wpos = 0, nsec = 0, pre = 0;         // next word to read, next sector to fetch
       uint32_t slast = 0;                           // last sector holding bits of the segment
       u32x4 ps0 = {0, 0, 0, 0}, ps1 = ps0, ps2 = ps0, ps3 = ps0;
+      // The segment's last sector, when it is not among the first two: it is
+      // the next segment's first, which the neighbouring lane loads now, so it
+      // is loaded now as well (one read of the line) and held until needed,
+      // rather than read again from memory at the segment's end.
+      u32x4 hl0 = ps0, hl1 = ps0, hl2 = ps0, hl3 = ps0;
+      bool hold = false;
       bool pend = false;
       // 16-byte group gi of the window; groups past the payload read its last one
       auto grp = [&](uint32_t gi) { return ldg16(pay64 + 16ull * (gi < glast ? gi : glast)); };
@@ -473,8 +479,20 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
         const uint32_t s1 = s0 + 1 <= slast ? s0 + 1 : s0;
         const u32x4 a0 = grp(4 * s0), a1 = grp(4 * s0 + 1), a2 = grp(4 * s0 + 2), a3 = grp(4 * s0 + 3);
         const u32x4 a4 = grp(4 * s1), a5 = grp(4 * s1 + 1), a6 = grp(4 * s1 + 2), a7 = grp(4 * s1 + 3);
+        hold = slast > s0 + 1;
+        if (hold) {
+          hl0 = grp(4 * slast);
+          hl1 = grp(4 * slast + 1);
+          hl2 = grp(4 * slast + 2);
+          hl3 = grp(4 * slast + 3);
+        }
         put_sector(s0, a0, a1, a2, a3);
         put_sector(s0 + 1, a4, a5, a6, a7);
+        // the held sector's loads complete here, with the first two, so no
+        // wait inside the rounds is for them
+        asm volatile("" ::"v"(hl0[0]), "v"(hl0[1]), "v"(hl0[2]), "v"(hl0[3]), "v"(hl1[0]), "v"(hl1[1]),
+                     "v"(hl1[2]), "v"(hl1[3]), "v"(hl2[0]), "v"(hl2[1]), "v"(hl2[2]), "v"(hl2[3]),
+                     "v"(hl3[0]), "v"(hl3[1]), "v"(hl3[2]), "v"(hl3[3]));
         nsec = s0 + 2;
         W = uint64_t(rp[(w0 & (RING - 1)) * DEC_NT] >> (b0 & 31)) << 2;
         wpos = w0 + 1;
@@ -585,10 +603,17 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             const uint64_t bpos = uint64_t(wpos - adj) * 32 - uint32_t(nb);
             if (bpos != uint64_t(b0) + sbits || tx != 0) bad = 1;
           } else if (((wpos + 11) >> 4) >= nsec && nsec <= slast) {
-            ps0 = grp(4 * nsec);
-            ps1 = grp(4 * nsec + 1);
-            ps2 = grp(4 * nsec + 2);
-            ps3 = grp(4 * nsec + 3);
+            if (hold && nsec == slast) {
+              ps0 = hl0;
+              ps1 = hl1;
+              ps2 = hl2;
+              ps3 = hl3;
+            } else {
+              ps0 = grp(4 * nsec);
+              ps1 = grp(4 * nsec + 1);
+              ps2 = grp(4 * nsec + 2);
+              ps3 = grp(4 * nsec + 3);
+            }
             pend = true;
           }
         } else if (lim > 0) {
@@ -672,10 +697,17 @@ __global__ __launch_bounds__(DEC_NT) void k_decode(DecArgs a) {
             // only while it holds fewer than 30, so at most 12 words
             // [wpos, wpos + 12): at most one sector past those in the ring,
             // whose slot held a sector before wpos's.
-            ps0 = grp(4 * nsec);
-            ps1 = grp(4 * nsec + 1);
-            ps2 = grp(4 * nsec + 2);
-            ps3 = grp(4 * nsec + 3);
+            if (hold && nsec == slast) {
+              ps0 = hl0;
+              ps1 = hl1;
+              ps2 = hl2;
+              ps3 = hl3;
+            } else {
+              ps0 = grp(4 * nsec);
+              ps1 = grp(4 * nsec + 1);
+              ps2 = grp(4 * nsec + 2);
+              ps3 = grp(4 * nsec + 3);
+            }
             pend = true;
           }
         }
