@@ -135,3 +135,33 @@ def test_model_scaled_with_pairs(oracle):
     n_packed = sum(ts.pairs(i)[0] for i in range(16))
     print(f"  {n_packed} of 16 groups pack; container {g.size} bytes with pairs, {pb} without "
           f"({1 - g.size / pb:+.5f})", flush=True)
+
+
+def test_empty_tensors_and_more_groups_than_chunks(oracle):
+    # zero-element tensors beside others, and K larger than the chunk count
+    # (empty groups: no F, never packing)
+    cases = [([_paired(20001, 31), _paired(0, 32), _paired(5, 33)], 16384, 8, "empty tensor, K > chunks"),
+             ([_paired(3, 34)], 4096, 4, "one chunk of 3 values")]
+    for tensors, cb, K, label in cases:
+        ts, ots, g = _check(oracle, tensors, cb, K, label)
+        n_chunks = ts.info()["n_chunks"]
+        used = set(ts.group_map())
+        for i in range(K):
+            if i not in used:
+                packed, F, tl = ts.pairs(i)
+                assert not packed and F == [] and not any(tl), i
+        assert n_chunks < K
+
+
+def test_all_empty_plan_with_pairs(oracle):
+    print("case: pairs, every tensor empty", flush=True)
+    tensors = [_paired(0, 41), _paired(0, 42)]
+    ts = zn.setup(tensors, chunk_bytes=8192, n_groups=2, pairs=True)
+    ots = oracle.setup(oracle.BF16, [to_np(t) for t in tensors], 8192, 2, pairs=True)
+    _same_setup(ts, ots, 2)
+    blob = zn.compress(ts, tensors)
+    torch.cuda.synchronize()
+    o = oracle.compress(oracle.BF16, [to_np(t) for t in tensors], 8192, ots)
+    assert np.array_equal(blob.cpu().numpy(), o)
+    outs = zn.decompress(ts, blob)
+    assert all(x.numel() == 0 for x in outs)
