@@ -42,7 +42,7 @@ def lib() -> C.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ZnError(-1, f"libzn.so not built at {LIB_PATH} (run __graft_entry__.build())")
+            raise ZnError(-1, f"libzn.so not built at {LIB_PATH} (run python lossless_float_weight_amd/build.py)")
         L = C.CDLL(LIB_PATH)
         P, U64, I, U32 = C.c_void_p, C.c_uint64, C.c_int, C.c_uint32
         PU64 = C.POINTER(C.c_uint64)
