@@ -435,9 +435,10 @@ def test_fp4_full_size(oracle):
 @pytest.mark.slow
 def test_config5_full_model_grouped(oracle):
     """Full 8B-shaped model + KV cache (290 tensors, 9.65e9 BF16 values):
-    the K = 16 setup on the GPU equals the oracle's on the same data; the
-    perturbed copy compressed with that setup unchanged is byte-identical to
-    the oracle's container and round-trips exactly."""
+    the K = 16 setup on the GPU equals the oracle's on the same data, also
+    with packed exponent pairs; the perturbed copy compressed with that setup
+    unchanged is byte-identical to the oracle's container and round-trips
+    exactly."""
     import time
     t0 = time.time()
     print("case: full model 290 tensors, K=16 setup, perturbed reuse", flush=True)
@@ -455,7 +456,20 @@ def test_config5_full_model_grouped(oracle):
         assert ts.lengths(g) == ots.lengths(g).tolist()
     assert ts.hash == ots.hash and ts.save() == ots.save()
     assert ts.cost_history() == [int(v) for v in ots.cost_history()]
-    del arrs
+    # the same setup with packed exponent pairs: the grouping is the same, and
+    # F, the token code lengths, the packing flags and the saved bytes (format
+    # version 2) equal the oracle's
+    tsp = zn.setup(tensors, chunk_bytes=262144, n_groups=16, pairs=True)
+    torch.cuda.synchronize()
+    otsp = oracle.setup(oracle.BF16, arrs, 262144, 16, pairs=True)
+    print(f"  setups with pairs done at {time.time() - t0:.0f} s", flush=True)
+    assert tsp.group_map() == ts.group_map()
+    for g in range(16):
+        packed, F, tl = tsp.pairs(g)
+        opk, oF, otl = otsp.pairs(g)
+        assert packed == opk and F == oF and tl == otl.tolist(), g
+    assert tsp.hash == otsp.hash and tsp.save() == otsp.save()
+    del arrs, tsp, otsp
     pert = [t for _, t in W.perturbed_model(named, seed=5)]
     del named, tensors
     _whole_container_parity(oracle, oracle.BF16, pert, 262144, ts, ots, label="perturbed model")
