@@ -239,6 +239,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--coder", default="huffman", choices=("huffman", "tans"),
                     help="exponent coder (tans: tabled ANS, plans without groups)")
+    ap.add_argument("--no-comparison", action="store_true",
+                    help="model and transfer workloads: skip the compression with per-chunk tables that the "
+                         "line compares against (for counter runs, whose kernel means it would mix in)")
     ap.add_argument("--pairs", action="store_true",
                     help="packed exponent pairs in the grouped setup (model and transfer workloads)")
     args = ap.parse_args()
@@ -447,7 +450,7 @@ def main():
                      if k not in ("avg_ms", "algorithmic_bytes", "timed_in")},
         "kernels": rl,
     }
-    if args.workload in ("model", "transfer"):
+    if args.workload in ("model", "transfer") and not args.no_comparison:
         # the same compression with per-chunk tables (no setup), for the
         # post-setup speed-up the reusable setup is about
         plain = zn.setup(base, chunk_bytes=CHUNK_BYTES)
