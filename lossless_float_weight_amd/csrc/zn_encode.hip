@@ -1373,8 +1373,18 @@ __global__ __launch_bounds__(1024) void k_finish(FinishArgs a) {
   const uint32_t M = a.L.n_chunks;
   const uint32_t per = (M + 1023) / 1024;
   const uint32_t c0 = tid * per, c1 = c0 + per < M ? c0 + per : M;
+  // a thread's sizes eight loads at a time (a large model gives each thread
+  // dozens; one dependent load per size would make the scan a latency chain)
   unsigned long long s = 0;
-  for (uint32_t c = c0; c < c1; c++) s += a.sizes[c];
+  uint32_t c = c0;
+  for (; c + 8 <= c1; c += 8) {
+    unsigned long long v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = a.sizes[c + i];
+#pragma unroll
+    for (int i = 0; i < 8; i++) s += v[i];
+  }
+  for (; c < c1; c++) s += a.sizes[c];
   // block exclusive scan of the per-thread sums
   unsigned long long incl = s;
   for (int o = 1; o < 64; o <<= 1) {
@@ -1392,7 +1402,17 @@ __global__ __launch_bounds__(1024) void k_finish(FinishArgs a) {
   uint64_t *dir = reinterpret_cast<uint64_t *>(a.out + a.L.off_dir);
   const uint64_t end = a.L.off_records + total;
   const bool fits = end + 16 <= a.cap;
-  for (uint32_t c = c0; c < c1; c++) {
+  for (c = c0; c + 8 <= c1; c += 8) {
+    unsigned long long v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = a.sizes[c + i];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      stg8(dir + c + i, u32x2{uint32_t(off), uint32_t(off >> 32)});
+      off += v[i];
+    }
+  }
+  for (; c < c1; c++) {
     stg8(dir + c, u32x2{uint32_t(off), uint32_t(off >> 32)});
     off += a.sizes[c];
   }
