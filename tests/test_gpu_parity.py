@@ -474,3 +474,27 @@ def test_config5_full_model_grouped(oracle):
     del named, tensors
     _whole_container_parity(oracle, oracle.BF16, pert, 262144, ts, ots, label="perturbed model")
     print(f"  done at {time.time() - t0:.0f} s", flush=True)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_thousands_of_small_tensors(oracle, dt):
+    # a state dict of many small tensors (biases, norms, some empty): the
+    # tensor table, each chunk's tensor lookup and the per-tensor raw planes
+    print(f"case: {dt} 3000 small tensors", flush=True)
+    rng = np.random.default_rng(17)
+    sizes = [int(v) for v in rng.integers(0, 5000, 3000)]
+    sizes[::97] = [0] * len(sizes[::97])
+    if dt == "bf16":
+        tensors = [W.gaussian(max(n, 1), 0.0, 0.02, torch.bfloat16, "cuda", i, 3)[:n] for i, n in enumerate(sizes)]
+        odt = oracle.BF16
+    else:
+        tensors = [(torch.arange(n, dtype=torch.int64) * (i + 3) % 256).to(torch.uint8)
+                   .view(torch.float8_e4m3fn).cuda() for i, n in enumerate(sizes)]
+        odt = oracle.FP8_E4M3
+    for cb in (4096, 16384):
+        _check_equal(oracle, odt, tensors, cb)
+    if dt == "bf16":
+        ts = zn.setup(tensors, chunk_bytes=4096, n_groups=4)
+        ots = oracle.setup(oracle.BF16, [to_np(t) for t in tensors], 4096, 4)
+        assert ts.group_map() == ots.group_map().tolist() and ts.save() == ots.save()
+        _check_equal(oracle, odt, tensors, 4096, ts, ots)
