@@ -93,9 +93,14 @@ def _stream(stream) -> C.c_void_p:
     return C.c_void_p(s.cuda_stream)
 
 
-def _ptr_array(tensors: Sequence[torch.Tensor], device) -> torch.Tensor:
-    """Device array of the tensors' data pointers (the ABI's d_*_ptrs)."""
-    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+def _ptr_array(tensors: Sequence[torch.Tensor], device, stream=None) -> torch.Tensor:
+    """Device array of the tensors' data pointers (the ABI's d_*_ptrs), its
+    copy ordered on the stream the call runs on."""
+    vals = torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64)
+    if stream is None:
+        return vals.to(device)
+    with torch.cuda.stream(stream):
+        return vals.to(device)
 
 
 def _u64(vals):
@@ -314,7 +319,7 @@ def compress2(ts: Tableset, coder: int, tensors: Sequence[torch.Tensor], out: to
         scratch = new_scratch(ts, dev)
         tmp.append(scratch)
     if ptrs is None:
-        ptrs = _ptr_array(tensors, dev)
+        ptrs = _ptr_array(tensors, dev, stream)
         tmp.append(ptrs)
     for name, b in (("out", out), ("scratch", scratch)):
         if b.device != dev or not b.is_contiguous() or b.dtype != torch.uint8:
@@ -347,7 +352,7 @@ def decompress(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Tensor] | 
         scratch = torch.empty(256, dtype=torch.uint8, device=blob.device)
         tmp.append(scratch)
     if ptrs is None:
-        ptrs = _ptr_array(outs, blob.device)
+        ptrs = _ptr_array(outs, blob.device, stream)
         tmp.append(ptrs)
     if not sync:
         _keep_alive(stream, *tmp)

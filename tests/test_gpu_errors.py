@@ -287,3 +287,40 @@ def test_binding_refuses_mismatched_tensors():
         zn.decompress(ts, blob, outs=[torch.empty(9999, dtype=torch.bfloat16, device="cuda")])
     with pytest.raises(zn.ZnError):
         zn.decompress(ts, blob, outs=[torch.empty(10000, dtype=torch.float16, device="cuda")])
+
+
+def test_two_streams_overlapping_calls():
+    # two plans on two streams (default priority): both compressions run at
+    # once, each decompression follows its compression on the other stream by
+    # an event; containers equal the ones made alone, outputs equal inputs
+    print("case: overlapping calls on two streams", flush=True)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    xa = [t for _, t in W.block_bf16("cuda", seed=2, scale=8)]
+    xb = [W.fp8_blockscaled(1 << 20, device="cuda")[0][1]]
+    tsa = zn.setup(xa, chunk_bytes=262144)
+    tsb = zn.setup(xb, chunk_bytes=65536)
+    ref_a = zn.compress(tsa, xa).cpu()
+    ref_b = zn.compress(tsb, xb).cpu()
+    outa = torch.empty(zn.compress_bound(tsa), dtype=torch.uint8, device="cuda")
+    outb = torch.empty(zn.compress_bound(tsb), dtype=torch.uint8, device="cuda")
+    ya = [torch.empty_like(t) for t in xa]
+    yb = [torch.empty_like(t) for t in xb]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        outa.fill_(0xEE)
+        outb.fill_(0xEE)
+        torch.cuda.synchronize()
+        zn.compress(tsa, xa, out=outa, sync=False, stream=s1)
+        zn.compress(tsb, xb, out=outb, sync=False, stream=s2)
+        ea, eb = torch.cuda.Event(), torch.cuda.Event()
+        ea.record(s1)
+        eb.record(s2)
+        s2.wait_event(ea)
+        s1.wait_event(eb)
+        zn.decompress(tsa, outa[: ref_a.numel()], outs=ya, sync=False, stream=s2)
+        zn.decompress(tsb, outb[: ref_b.numel()], outs=yb, sync=False, stream=s1)
+        torch.cuda.synchronize()
+        assert torch.equal(outa[: ref_a.numel()].cpu(), ref_a), rep
+        assert torch.equal(outb[: ref_b.numel()].cpu(), ref_b), rep
+        for x, y in zip(xa + xb, ya + yb):
+            assert torch.equal(W.bits(x).reshape(-1), W.bits(y).reshape(-1)), rep
