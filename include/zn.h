@@ -28,6 +28,10 @@
  *     caller's stream in stream order and need d_scratch of at least
  *     zn_scratch_bytes() bytes (16-byte aligned).  Concurrent calls on one
  *     tableset need distinct scratch buffers.
+ *   - A tableset's device memory lives on the device that was current when
+ *     the tableset was made.  Every call that launches work with it needs
+ *     that device current (ZN_ERR_ARG otherwise); zn_tableset_free may be
+ *     called with any device current.
  *   - Inputs are read-only; outputs must not overlap inputs.  Tensor data
  *     pointers should be 16-byte aligned (unaligned ones take a slow path).
  *   - Calls return a zn_status and never throw.  HIP failures map to

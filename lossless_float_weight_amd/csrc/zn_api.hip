@@ -51,7 +51,9 @@ struct zn_tableset {
   // one-token decode table; penc the pair tokens' codes, rank F's ranks
   uint8_t *d_packed = nullptr, *d_rank = nullptr;
   uint32_t *d_penc = nullptr;
-  int device = 0;
+  // the device that was current when the device copies were made: they live
+  // there, so every launch with this tableset needs that device current
+  int device = -1;
 };
 
 namespace {
@@ -126,7 +128,19 @@ uint64_t fnv1a64(const uint8_t *b, uint64_t n) {
   return h;
 }
 
+// The current device is the tableset's own (a tableset that never reached
+// its device copies has none, and every call that launches refuses it).
+bool on_device(const zn_tableset *ts) {
+  int dev = -1;
+  return ts->device >= 0 && hipGetDevice(&dev) == hipSuccess && dev == ts->device;
+}
+
+// Frees on the device that holds the memory, then makes the caller's device
+// current again.
 void free_device(zn_tableset *ts) {
+  int cur = -1;
+  const bool sw = ts->device >= 0 && hipGetDevice(&cur) == hipSuccess && cur != ts->device &&
+                  hipSetDevice(ts->device) == hipSuccess;
   (void)hipFree(ts->d_n);
   (void)hipFree(ts->d_raw);
   (void)hipFree(ts->d_chunk0);
@@ -144,6 +158,7 @@ void free_device(zn_tableset *ts) {
   ts->d_enc = ts->d_lut = nullptr;
   ts->d_packed = ts->d_rank = nullptr;
   ts->d_penc = nullptr;
+  if (sw) (void)hipSetDevice(cur);
 }
 
 // Host layout of the container for the plan's tensors.
@@ -204,6 +219,7 @@ zn_status finish_plan(zn_tableset *ts) {
     put_u64(h + 72 + 16 * t, ts->raw[t]);
   }
   if (!ts->d_n) {
+    HIPCHK(hipGetDevice(&ts->device));
     HIPCHK(hipMalloc(&ts->d_n, 8ull * ts->T));
     HIPCHK(hipMalloc(&ts->d_raw, 8ull * ts->T));
     HIPCHK(hipMalloc(&ts->d_chunk0, 4ull * (ts->T + 1)));
@@ -446,7 +462,7 @@ zn_status zn_setup_transfer(const zn_tableset *src, const void *const *d_tensors
                             zn_tableset **out) {
   if (!out) return ZN_ERR_ARG;
   *out = nullptr;
-  if (!src || src->K < 1 || !d_tensors || !n_elems || n_tensors < 1) return ZN_ERR_ARG;
+  if (!src || src->K < 1 || !d_tensors || !n_elems || n_tensors < 1 || !on_device(src)) return ZN_ERR_ARG;
   zn_tableset *ts = new (std::nothrow) zn_tableset;
   if (!ts) return ZN_ERR_NOMEM;
   zn_status st = make_plan(ts, src->dtype, n_elems, n_tensors, src->chunk_bytes);
@@ -578,7 +594,7 @@ zn_status zn_compress(const zn_tableset *ts, const void *const *d_in_ptrs, void 
 zn_status zn_compress2(const zn_tableset *ts, int coder, const void *const *d_in_ptrs, void *d_out,
                        uint64_t out_cap, uint64_t *out_bytes, void *d_scratch,
                        uint64_t scratch_bytes, hipStream_t stream) {
-  if (!ts || (!d_in_ptrs && ts->n_chunks) || !d_out || !d_scratch) return ZN_ERR_ARG;
+  if (!ts || (!d_in_ptrs && ts->n_chunks) || !d_out || !d_scratch || !on_device(ts)) return ZN_ERR_ARG;
   if (coder != ZN_CODER_HUFFMAN && (coder != ZN_CODER_TANS || ts->K > 0)) return ZN_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_scratch) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15))
     return ZN_ERR_ARG;
@@ -713,7 +729,7 @@ extern "C" {
 zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
                         void *const *d_out_ptrs, void *d_scratch, uint64_t scratch_bytes, int sync,
                         hipStream_t stream) {
-  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks) || !d_scratch) return ZN_ERR_ARG;
+  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks) || !d_scratch || !on_device(ts)) return ZN_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_scratch) & 15) || (reinterpret_cast<uintptr_t>(d_in) & 15))
     return ZN_ERR_ARG;
   if (scratch_bytes < kCtlBytes) return ZN_ERR_CAPACITY;
@@ -723,7 +739,7 @@ zn_status zn_decompress(const zn_tableset *ts, const void *d_in, uint64_t in_byt
 zn_status zn_decompress_noalloc(const zn_tableset *ts, const void *d_in, uint64_t in_bytes,
                                 void *const *d_out_ptrs, uint32_t *d_status, int sync,
                                 hipStream_t stream) {
-  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks)) return ZN_ERR_ARG;
+  if (!ts || !d_in || (!d_out_ptrs && ts->n_chunks) || !on_device(ts)) return ZN_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(d_in) & 15) return ZN_ERR_ARG;
   void *ctl = nullptr;
   zn_status st = noalloc_scratch(&ctl);
@@ -866,7 +882,7 @@ zn_status zn_tableset_cost_history(const zn_tableset *ts, uint64_t *h_cost) {
 
 zn_status zn_debug_histograms(const zn_tableset *ts, const void *const *d_in_ptrs, uint32_t *d_hist,
                               hipStream_t stream) {
-  if (!ts || !d_in_ptrs || !d_hist) return ZN_ERR_ARG;
+  if (!ts || !d_in_ptrs || !d_hist || !on_device(ts)) return ZN_ERR_ARG;
   HIPCHK(launch_hist_all(ts->dtype, dev_layout(ts), reinterpret_cast<const uint8_t *const *>(d_in_ptrs),
                          d_hist, stream));
   return ZN_OK;

@@ -206,8 +206,10 @@ def setup(tensors: Sequence[torch.Tensor] | None = None, *, dtype=None, n_elems=
         ptrs = None
         dtype = ZN_DTYPE.get(dtype, dtype)
     h = C.c_void_p()
-    _check(lib().zn_setup2(int(dtype), ptrs, _u64(n_elems), len(n_elems), chunk_bytes, n_groups,
-                           SETUP_PAIRS if pairs else 0, _stream(stream), C.byref(h)), "setup")
+    # the tableset lives on the tensors' device (else on the current one)
+    with torch.cuda.device(tensors[0].device if tensors else None):
+        _check(lib().zn_setup2(int(dtype), ptrs, _u64(n_elems), len(n_elems), chunk_bytes, n_groups,
+                               SETUP_PAIRS if pairs else 0, _stream(stream), C.byref(h)), "setup")
     return Tableset(h)
 
 
@@ -221,15 +223,17 @@ def setup_transfer(src: Tableset, tensors: Sequence[torch.Tensor], stream=None) 
     tensors = [t.contiguous() for t in tensors]
     ptrs = (C.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
     h = C.c_void_p()
-    _check(lib().zn_setup_transfer(src.handle, ptrs, _u64([t.numel() for t in tensors]), len(tensors),
-                                   _stream(stream), C.byref(h)), "setup_transfer")
+    with torch.cuda.device(tensors[0].device):
+        _check(lib().zn_setup_transfer(src.handle, ptrs, _u64([t.numel() for t in tensors]), len(tensors),
+                                       _stream(stream), C.byref(h)), "setup_transfer")
     return Tableset(h)
 
 
 def plan_from_container(blob: torch.Tensor, stream=None) -> Tableset:
     h = C.c_void_p()
-    _check(lib().zn_plan_from_container(C.c_void_p(blob.data_ptr()), blob.numel(), _stream(stream),
-                                        C.byref(h)), "plan_from_container")
+    with torch.cuda.device(blob.device):
+        _check(lib().zn_plan_from_container(C.c_void_p(blob.data_ptr()), blob.numel(), _stream(stream),
+                                            C.byref(h)), "plan_from_container")
     return Tableset(h)
 
 
@@ -327,10 +331,11 @@ def compress2(ts: Tableset, coder: int, tensors: Sequence[torch.Tensor], out: to
     if not sync:
         _keep_alive(stream, *tmp)
     nb = C.c_uint64()
-    _check(lib().zn_compress2(ts.handle, int(coder), C.c_void_p(ptrs.data_ptr()), C.c_void_p(out.data_ptr()),
-                              out.numel(), C.byref(nb) if sync else None,
-                              C.c_void_p(scratch.data_ptr()), scratch.numel(), _stream(stream)),
-           "compress")
+    with torch.cuda.device(dev):   # the tableset must live on the tensors' device
+        _check(lib().zn_compress2(ts.handle, int(coder), C.c_void_p(ptrs.data_ptr()),
+                                  C.c_void_p(out.data_ptr()), out.numel(), C.byref(nb) if sync else None,
+                                  C.c_void_p(scratch.data_ptr()), scratch.numel(), _stream(stream)),
+               "compress")
     return out[: nb.value] if sync else out
 
 
@@ -356,9 +361,10 @@ def decompress(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Tensor] | 
         tmp.append(ptrs)
     if not sync:
         _keep_alive(stream, *tmp)
-    _check(lib().zn_decompress(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
-                               C.c_void_p(ptrs.data_ptr()), C.c_void_p(scratch.data_ptr()),
-                               scratch.numel(), 1 if sync else 0, _stream(stream)), "decompress")
+    with torch.cuda.device(blob.device):
+        _check(lib().zn_decompress(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
+                                   C.c_void_p(ptrs.data_ptr()), C.c_void_p(scratch.data_ptr()),
+                                   scratch.numel(), 1 if sync else 0, _stream(stream)), "decompress")
     return outs
 
 
@@ -375,10 +381,11 @@ def decompress_noalloc(ts: Tableset, blob: torch.Tensor, outs: Sequence[torch.Te
         raise ZnError(-1, "decompress_noalloc: ptrs must be the outputs' int64 device pointers")
     if status is not None and (status.device != blob.device or status.dtype != torch.int32):
         raise ZnError(-1, "decompress_noalloc: status must be an int32 tensor on the container's device")
-    _check(lib().zn_decompress_noalloc(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
-                                       C.c_void_p(ptrs.data_ptr()),
-                                       C.c_void_p(status.data_ptr()) if status is not None else None,
-                                       1 if sync else 0, _stream(stream)), "decompress_noalloc")
+    with torch.cuda.device(blob.device):
+        _check(lib().zn_decompress_noalloc(ts.handle, C.c_void_p(blob.data_ptr()), blob.numel(),
+                                           C.c_void_p(ptrs.data_ptr()),
+                                           C.c_void_p(status.data_ptr()) if status is not None else None,
+                                           1 if sync else 0, _stream(stream)), "decompress_noalloc")
     return outs
 
 
