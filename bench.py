@@ -18,7 +18,9 @@ gives the compress / decompress split); `traffic` is
 the HBM bytes per launch from committed rocprofv3 counter runs
 (profiles/traffic_*.txt), reported only while the kernel sources are the
 ones those counters were taken on.  The CPU oracle's rate on a bounded
-sample of the same workload is reported beside it.
+sample of the same workload is reported beside it, and the GPU's container
+of that sample (per-chunk tables, the timed coder) is compared with the
+oracle's byte for byte (`cpu_baseline.container_equals_gpu`).
 
 --copy-calibration runs a plain device-to-device copy of the workload's
 size instead (the calibration kernel for the HBM byte counters).
@@ -167,6 +169,18 @@ def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16, coder: in
     assert all(np.array_equal(x, y) for x, y in zip(sample, outs))
     one = nbytes / (t2 - t0)
 
+    # the GPU's container of the same sample (its own plan, per-chunk tables,
+    # the timed coder), compared with the oracle's byte for byte
+    import torch
+
+    from lossless_float_weight_amd import zn
+    gsamp = [t.reshape(-1)[: s.size] for t, s in zip(tensors, sample)]
+    gblob = zn.compress2(zn.setup(gsamp, chunk_bytes=CHUNK_BYTES), coder, gsamp).cpu().numpy()
+    torch.cuda.synchronize()
+    identical = bool(gblob.size == blob.size and np.array_equal(gblob, blob))
+    digest = hashlib.sha256(blob.tobytes()).hexdigest()[:16]
+    del gsamp, gblob
+
     # the same sample over P processes, each a run of whole chunks, each
     # repeated so that it works about a second
     P = max(1, min(max_procs, os.cpu_count() or 1))
@@ -201,6 +215,7 @@ def cpu_baseline(tensors, budget_s: float = 20.0, max_procs: int = 16, coder: in
     wall = max(t for t, _ in res)
     many = flat.nbytes * reps / wall
     return {"value": round(many / 1e9, 4), "unit": "GB/s", "cores": len(spans), "kind": "oracle",
+            "container_equals_gpu": identical, "container_sha256_16": digest,
             "sample": f"{len(sample)} leading tensor(s) of the workload, {nbytes} bytes: one thread "
                       f"{one / 1e9:.4f} GB/s (compress {nbytes / (t1 - t0) / 1e9:.4f} + decompress "
                       f"{nbytes / (t2 - t1) / 1e9:.4f}); {len(spans)} processes on runs of whole "

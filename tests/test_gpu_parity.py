@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    zn.lib()  # a missing library is an error on a GPU machine, not a skip
+    zn.lib()  # a missing library is an error wherever a GPU is present, not a skip
 
 
 def _check_equal(oracle, dt, tensors, chunk_bytes, ts=None, ots=None):
