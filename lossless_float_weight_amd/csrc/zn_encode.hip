@@ -74,6 +74,15 @@ __device__ __forceinline__ uint32_t field_rt(uint32_t w, int p) {
   return p == 0 ? field<DT, 0>(w) : field<DT, 1>(w);
 }
 
+// The first stream's field of each of a word's four 1-byte elements, in
+// that element's byte.
+template <int DT>
+__device__ __forceinline__ uint32_t field0_4(uint32_t x) {
+  static_assert(DT == FP8 || DT == FP4X2, "1-byte elements");
+  if constexpr (DT == FP4X2) return ((x >> 1) & 0x03030303u) | ((x >> 3) & 0x0C0C0C0Cu);
+  return (x >> 3) & 0x0F0F0F0Fu;
+}
+
 // element i of a 16-byte vector
 template <int DT>
 __device__ __forceinline__ uint32_t vec_elem(const uint4 &q, int i) {
@@ -294,6 +303,12 @@ struct PackShared {
   static constexpr int PA = DT == BF16 ? 256 : 1;
   uint32_t penc[PA];
   uint8_t prk[PA];
+  // 1-byte elements: the first stream's codes joined for two consecutive
+  // symbols x, y at entry x + 16 y (rows 0..15), the single code of x at
+  // 256 + x and nothing at 272..287 (for a run's elements past the chunk's
+  // end); the code word in bits 0..21, its bit count in bits 27..31
+  static constexpr int P2 = DT == FP8 || DT == FP4X2 ? 288 : 1;
+  uint32_t enc2[P2];
   // 1-byte elements: one tile's words of a raw stream (32 strips per segment,
   // up to 4 words per strip), written from the coded stream's tiles
   static constexpr bool RSTAGE = DT == FP8 || DT == FP4X2;
@@ -910,7 +925,8 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
                                            uint32_t (*stage_all)[PackShared<DT>::STAGE],
                                            uint32_t (*wtot)[PACK_NW], uint32_t *rawt,
                                            const uint8_t *segbits, TansPack *tans,
-                                           const uint32_t *penc, const uint8_t *prk, bool packed) {
+                                           const uint32_t *penc, const uint8_t *prk, bool packed,
+                                           const uint32_t *enc2) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
@@ -1098,18 +1114,29 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
       for (int g = 0; g < G; g++) {
         const uint32_t eb = neb[g];
         const bool vec = aligned && eb + EPT <= n;
-        uint32_t w[EPT];
-        if (vec) {
+        if (!vec) {
+          // a run off 16-byte alignment or reaching past the chunk's end: its
+          // elements one at a time (zero past the end), placed in the vectors
+          // as the 16-byte loads place them, so everything below reads the
+          // vectors
 #pragma unroll
           for (int j = 0; j < NV; j++) {
-            const uint4 q = make_uint4(nq[g][j][0], nq[g][j][1], nq[g][j][2], nq[g][j][3]);
+            u32x4 q = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
+            for (int i = 0; i < VE; i++) {
+              const uint32_t e = eb + uint32_t(j * VE + i);
+              const uint32_t x = e < n ? load_elem<DT>(src + uint64_t(e) * ES) : 0u;
+              q[(i * ES) >> 2] |= x << (8 * ((i * ES) & 3));
+            }
+            nq[g][j] = q;
           }
-        } else {
+        }
+        uint32_t w[EPT];
 #pragma unroll
-          for (int i = 0; i < EPT; i++)
-            w[i] = eb + i < n ? load_elem<DT>(src + uint64_t(eb + i) * ES) : 0;
+        for (int j = 0; j < NV; j++) {
+          const uint4 q = make_uint4(nq[g][j][0], nq[g][j][1], nq[g][j][2], nq[g][j][3]);
+#pragma unroll
+          for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
         }
         nb[g] = 0;
         // elements of this lane's run inside the chunk: the code of every
@@ -1143,8 +1170,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
           uint64_t bq = 0;
 #pragma unroll
           for (int j = 0; j < 4; j++) {
-            const uint32_t x = vec ? nq[g][0][j]
-                                   : w[4 * j] | (w[4 * j + 1] << 8) | (w[4 * j + 2] << 16) | (w[4 * j + 3] << 24);
+            const uint32_t x = nq[g][0][j];
             bq |= uint64_t(mant4<DT>(x)) << (4 * KM * j);
           }
           const int at = ((ln >> 1) * NWG + wv * G + g) * 2 * KM + (ln & 1) * KM;   // 16-bit words
@@ -1161,6 +1187,46 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         }
 #pragma unroll
         for (int g8 = 0; g8 < NG; g8++) {
+          if constexpr ((DT == FP8 || DT == FP4X2) && GE == 8) if (p == 0) {
+            // 1-byte elements, first stream: one lookup per two symbols gives
+            // their codes joined (the first code's bits, then the second's),
+            // the same bits as two single lookups.  Only a run that reaches
+            // past the chunk's end takes singles and empties; every other
+            // lane skips that branch.
+            // elements 8 g8 .. 8 g8 + 7 of the run are words 2 g8, 2 g8 + 1 of
+            // its vector; each word's four fields, a byte each, give the
+            // indices of its two pairs
+            uint32_t ix[4];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+              const uint32_t f = field0_4<DT>(nq[g][0][2 * g8 + h]);
+              const uint32_t u = f | (f >> 4);     // bytes 0 and 2: x | y << 4
+              ix[2 * h] = u & 0xFFu;
+              ix[2 * h + 1] = (u >> 16) & 0xFFu;
+            }
+            if (lim < uint32_t(EPT)) {
+#pragma unroll
+              for (int j = 0; j < 4; j++) {
+                const uint32_t e = uint32_t(g8 * GE + 2 * j);
+                ix[j] = e + 1 < lim ? ix[j] : e < lim ? 256u + (ix[j] & 15u) : 272u;
+              }
+            }
+            uint32_t pv[4], pl[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              const uint32_t c = enc2[ix[j]];
+              pv[j] = c & 0x3FFFFFu;
+              pl[j] = c >> 27;
+            }
+            const uint64_t q0 = uint64_t(pv[0]) | (uint64_t(pv[1]) << pl[0]);
+            const uint64_t q1 = uint64_t(pv[2]) | (uint64_t(pv[3]) << pl[2]);
+            const uint32_t L0 = pl[0] + pl[1], L1 = pl[2] + pl[3];
+            glo[g][g8] = q0 | (q1 << L0);
+            ghi[g][g8] = L0 ? uint32_t(q1 >> (64 - L0)) : 0u;
+            gb[g][g8] = L0 + L1;
+            nb[g] += gb[g][g8];
+            continue;
+          }
           uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l[8] = {0, 0, 0, 0, 0, 0, 0, 0};
           bool pairs = false;
           if constexpr (DT == BF16 && GE % 2 == 0 && PK) pairs = packed && p == 0;
@@ -1343,6 +1409,16 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
       sh.prk[tid] = uint8_t(ldg1(a.group_rank + g * 256 + tid));
     }
   }
+  if constexpr (DT == FP8 || DT == FP4X2) {
+    // the first stream's joined pair codes, from its single codes
+    __syncthreads();
+    for (int i = tid; i < 288; i += PACK_NT) {
+      const uint32_t cx = sh.enc[0][i & 15], row = uint32_t(i) >> 4;
+      const uint32_t cy = row < 16 ? sh.enc[0][row] : 0u;
+      const uint32_t lx = cx >> 16, ly = row < 16 ? cy >> 16 : 0u;
+      sh.enc2[i] = row < 17 ? ((cx & 0xFFFFu) | ((cy & 0xFFFFu) << lx)) | ((lx + ly) << 27) : 0u;
+    }
+  }
   if (tid < NC) {
     sh.mode[tid] = plan[48 + tid];
     sh.aux[tid] = plan[52 + tid];
@@ -1351,7 +1427,8 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   }
   const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
   pack_chunk<DT, TC, PK>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off,
-                     sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), tans_of(sh), sh.penc, sh.prk, packed);
+                     sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), tans_of(sh), sh.penc, sh.prk, packed,
+                     sh.enc2);
 }
 
 // One workgroup: exclusive scan of the record sizes into the directory, then
