@@ -309,10 +309,18 @@ struct PackShared {
   // end); the code word in bits 0..21, its bit count in bits 27..31
   static constexpr int P2 = DT == FP8 || DT == FP4X2 ? 288 : 1;
   uint32_t enc2[P2];
-  // 1-byte elements: one tile's words of a raw stream (32 strips per segment,
-  // up to 4 words per strip), written from the coded stream's tiles
-  static constexpr bool RSTAGE = DT == FP8 || DT == FP4X2;
-  uint32_t rawt[RSTAGE ? 32 * PACK_NW * G * 4 : 1];
+  // 1-byte elements: the raw mantissa stream's words of a group of RT
+  // consecutive tiles (32 strips per segment, kbits words per strip),
+  // written from the coded stream's tiles and stored after the group's last
+  // tile as one run per strip row (192 bytes for FP8, 256 for FP4 pairs):
+  // the per-tile runs are 48 and 32 bytes, parts of lines that the L2 then
+  // writes back before the next tiles fill them.  Longer groups make the
+  // stores a burst that the next tile's loads wait behind (measured: FP8
+  // packs fastest at 4 tiles, FP4 pairs at 8).  A chunk whose first stream
+  // is tANS-coded never takes this path, so the tANS kernels hold no buffer.
+  static constexpr bool RSTAGE = (DT == FP8 || DT == FP4X2) && !TC;
+  static constexpr int RT = DT == FP8 ? 4 : 8;
+  uint32_t rawt[RSTAGE ? 32 * RT * PACK_NW * G * kbits(DT, 1) : 1];
   unsigned long long bits[NC], sec_off[NC];
   int mode[NC], aux[NC];
 };
@@ -957,7 +965,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
   // stores (one row per strip row of the tile's segments).
   // Otherwise (and when no stream is coded) they take one pass of their own
   // here, in element order.
-  constexpr bool RSTAGE = PackShared<DT>::RSTAGE;
+  constexpr bool RSTAGE = PackShared<DT, TC>::RSTAGE;
   constexpr int NWG = NW * G;            // segments per tile
   uint32_t rawmask = 0, tilemask = 0, lmask = 0;
   int firstcoded = -1;
@@ -1173,7 +1181,8 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
             const uint32_t x = nq[g][0][j];
             bq |= uint64_t(mant4<DT>(x)) << (4 * KM * j);
           }
-          const int at = ((ln >> 1) * NWG + wv * G + g) * 2 * KM + (ln & 1) * KM;   // 16-bit words
+          constexpr int RT = PackShared<DT, TC>::RT;
+          const int at = ((ln >> 1) * (RT * NWG) + (T % RT) * NWG + wv * G + g) * 2 * KM + (ln & 1) * KM;   // 16-bit words
           uint16_t *rt = reinterpret_cast<uint16_t *>(rawt);
           if constexpr (KM == 2) {
             rawt[at >> 1] = uint32_t(bq);
@@ -1323,26 +1332,29 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         }
         base += segtot[g];
       }
-      if (RSTAGE && p == 0 && lmask) {
-        // the tile's mantissa words: strip row r holds kq words of each of the
-        // tile's segments, at word kq*(r*nseg + T*NWG) of the stream
-        {
-          constexpr int q = 1, kq = kbits(DT, 1);
-          const int segs = nseg - T * NWG < NWG ? nseg - T * NWG : NWG;   // segments in this tile
-          const uint32_t rw = uint32_t(segs) * kq;                        // words per row
-          uint32_t *const dst = reinterpret_cast<uint32_t *>(pwr[q]) + uint32_t(kq * NWG) * uint32_t(T);
-          if (segs == NWG && (nseg * kq) % 4 == 0 && (reinterpret_cast<uintptr_t>(pwr[q]) & 15) == 0) {
-            // NWG*kq words per row, a multiple of 4, 16-byte aligned
-            const int per = NWG * kq / 4;
+      if constexpr (RSTAGE) if (p == 0 && lmask) {
+        // after a group's last tile and the last tile: the group's mantissa
+        // words; strip row r holds kq words of each of its segments, at word
+        // kq*(r*nseg + T0*NWG) of the stream
+        constexpr int RT = PackShared<DT, TC>::RT, q = 1, kq = kbits(DT, 1);
+        constexpr int RWS = RT * NWG * kq;                 // words per row of the buffer
+        if (T % RT == RT - 1 || T == ntiles - 1) {
+          const int T0 = T - T % RT;                       // the group's first tile
+          const int segs = (nseg < (T + 1) * NWG ? nseg : (T + 1) * NWG) - T0 * NWG;
+          uint32_t *const dst = reinterpret_cast<uint32_t *>(pwr[q]) + uint32_t(kq * NWG) * uint32_t(T0);
+          if (segs == RT * NWG && (nseg * kq) % 4 == 0 && (reinterpret_cast<uintptr_t>(pwr[q]) & 15) == 0) {
+            // RWS words per row, a multiple of 4, 16-byte aligned
+            constexpr int per = RWS / 4;
             for (int i = tid; i < 32 * per; i += ENC_NT) {
               const int r = i / per, v = i % per;
-              const uint32_t *sv = rawt + r * NWG * kq + 4 * v;
+              const uint32_t *sv = rawt + r * RWS + 4 * v;
               stg16(dst + uint64_t(kq) * uint32_t(r) * uint32_t(nseg) + 4 * v, u32x4{sv[0], sv[1], sv[2], sv[3]});
             }
           } else {
+            const uint32_t rw = uint32_t(segs) * kq;       // words per row
             for (uint32_t i = tid; i < 32 * rw; i += ENC_NT) {
               const uint32_t r = i / rw, v = i % rw;
-              stg4(dst + uint64_t(kq) * r * uint32_t(nseg) + v, rawt[r * NWG * kq + v]);
+              stg4(dst + uint64_t(kq) * r * uint32_t(nseg) + v, rawt[r * RWS + v]);
             }
           }
         }
