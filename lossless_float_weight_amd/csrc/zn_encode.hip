@@ -1122,29 +1122,37 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
       for (int g = 0; g < G; g++) {
         const uint32_t eb = neb[g];
         const bool vec = aligned && eb + EPT <= n;
-        if (!vec) {
-          // a run off 16-byte alignment or reaching past the chunk's end: its
-          // elements one at a time (zero past the end), placed in the vectors
-          // as the 16-byte loads place them, so everything below reads the
-          // vectors
-#pragma unroll
-          for (int j = 0; j < NV; j++) {
+        uint32_t w[EPT];
+        if constexpr (DT == FP8 || DT == FP4X2) {
+          static_assert(NV == 1 && VE == EPT && ES == 1, "a run of 1-byte elements is one 16-byte vector");
+          if (!vec) {
+            // a run off 16-byte alignment or reaching past the chunk's end:
+            // its elements one at a time (zero past the end), placed in the
+            // vector as the 16-byte load places them, so everything below
+            // reads the vector
             u32x4 q = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < VE; i++) {
-              const uint32_t e = eb + uint32_t(j * VE + i);
-              const uint32_t x = e < n ? load_elem<DT>(src + uint64_t(e) * ES) : 0u;
-              q[(i * ES) >> 2] |= x << (8 * ((i * ES) & 3));
+              const uint32_t e = eb + uint32_t(i);
+              const uint32_t x = e < n ? load_elem<DT>(src + uint64_t(e)) : 0u;
+              q[i >> 2] |= x << (8 * (i & 3));
             }
-            nq[g][j] = q;
+            nq[g][0] = q;
           }
-        }
-        uint32_t w[EPT];
+          const uint4 q = make_uint4(nq[g][0][0], nq[g][0][1], nq[g][0][2], nq[g][0][3]);
 #pragma unroll
-        for (int j = 0; j < NV; j++) {
-          const uint4 q = make_uint4(nq[g][j][0], nq[g][j][1], nq[g][j][2], nq[g][j][3]);
+          for (int i = 0; i < VE; i++) w[i] = vec_elem<DT>(q, i);
+        } else if (vec) {
 #pragma unroll
-          for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
+          for (int j = 0; j < NV; j++) {
+            const uint4 q = make_uint4(nq[g][j][0], nq[g][j][1], nq[g][j][2], nq[g][j][3]);
+#pragma unroll
+            for (int i = 0; i < VE; i++) w[j * VE + i] = vec_elem<DT>(q, i);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPT; i++)
+            w[i] = eb + i < n ? load_elem<DT>(src + uint64_t(eb + i) * ES) : 0;
         }
         nb[g] = 0;
         // elements of this lane's run inside the chunk: the code of every
