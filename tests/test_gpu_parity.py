@@ -142,12 +142,14 @@ def test_fp8_ragged_every_pattern(oracle, n):
 @pytest.mark.parametrize("dt", ["fp8", "fp4"])
 def test_1byte_mantissa_raw_whole_segments(oracle, dt):
     # chunks of whole 1024-element segments, exponent coded and mantissa raw:
-    # the mantissa words are written from the exponent's tiles, as 16-byte
-    # rows (segment count a multiple of 4) or word by word (the rest)
+    # the mantissa words are written from the exponent's tiles, held for a
+    # group of tiles (4 of 4 segments for FP8, 8 for FP4 pairs) and stored as
+    # 16-byte rows (a whole group) or word by word (a group cut short by the
+    # chunk's end); 21 and 40 segments give whole groups followed by a short one
     print(f"case: {dt} whole segments, mantissa raw", flush=True)
     odt = oracle.FP8_E4M3 if dt == "fp8" else oracle.FP4X2_E2M1
     seen = set()
-    for k in (1, 3, 5, 6, 259):
+    for k in (1, 3, 5, 6, 21, 40, 259):
         x = (W.fp8_blockscaled(1024 * k + 1, device="cuda")[0][1] if dt == "fp8"
              else W.fp4_blockscaled(1024 * k + 1, device="cuda")[0][1])
         # aligned, and one byte off 16-byte alignment (the tiles then load bytes)
