@@ -309,18 +309,23 @@ struct PackShared {
   // end); the code word in bits 0..21, its bit count in bits 27..31
   static constexpr int P2 = DT == FP8 || DT == FP4X2 ? 288 : 1;
   uint32_t enc2[P2];
-  // 1-byte elements: the raw mantissa stream's words of a group of RT
-  // consecutive tiles (32 strips per segment, kbits words per strip),
-  // written from the coded stream's tiles and stored after the group's last
-  // tile as one run per strip row (192 bytes for FP8, 256 for FP4 pairs):
-  // the per-tile runs are 48 and 32 bytes, parts of lines that the L2 then
-  // writes back before the next tiles fill them.  Longer groups make the
-  // stores a burst that the next tile's loads wait behind (measured: FP8
-  // packs fastest at 4 tiles, FP4 pairs at 8).  A chunk whose first stream
-  // is tANS-coded never takes this path, so the tANS kernels hold no buffer.
+  // 1-byte elements: the raw mantissa stream's words (32 strips per
+  // segment, kbits words per strip), written from the coded stream's tiles
+  // into a ring per strip row.  After each group of RT tiles a row stores
+  // the whole 128-byte lines it now holds and keeps the rest (under a line)
+  // for the next group, so no store leaves a line part-written (the per-tile
+  // runs are 48 bytes for FP8 and 32 for FP4 pairs, parts of lines that the
+  // L2 wrote back before the next tiles filled them).  The ring holds a
+  // group and the rest before it (RW >= GW + 28); it is a whole number of
+  // strips and of 16-byte vectors, and small enough to keep six workgroups
+  // per CU.  A chunk whose first stream is tANS-coded never takes this path,
+  // so the tANS kernels hold no ring.
   static constexpr bool RSTAGE = (DT == FP8 || DT == FP4X2) && !TC;
-  static constexpr int RT = DT == FP8 ? 4 : 8;
-  uint32_t rawt[RSTAGE ? 32 * RT * PACK_NW * G * kbits(DT, 1) : 1];
+  static constexpr int RT = 4;
+  static constexpr int GW = RT * PACK_NW * G * kbits(DT, 1);      // a group's words per row
+  static constexpr int RW = DT == FP8 ? 84 : 64;                  // ring words per row
+  static_assert(!RSTAGE || (RW >= GW + 28 && RW % kbits(DT, 1) == 0 && RW % 4 == 0), "ring size");
+  uint32_t rawt[RSTAGE ? 32 * RW : 1];
   unsigned long long bits[NC], sec_off[NC];
   int mode[NC], aux[NC];
 };
@@ -1189,8 +1194,10 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
             const uint32_t x = nq[g][0][j];
             bq |= uint64_t(mant4<DT>(x)) << (4 * KM * j);
           }
-          constexpr int RT = PackShared<DT, TC>::RT;
-          const int at = ((ln >> 1) * (RT * NWG) + (T % RT) * NWG + wv * G + g) * 2 * KM + (ln & 1) * KM;   // 16-bit words
+          // the strip of segment s sits at word KM * s of its row, modulo the ring
+          constexpr int RW = PackShared<DT, TC>::RW;
+          const int s = T * NWG + wv * G + g;
+          const int at = (ln >> 1) * (2 * RW) + (s % (RW / KM)) * 2 * KM + (ln & 1) * KM;   // 16-bit words
           uint16_t *rt = reinterpret_cast<uint16_t *>(rawt);
           if constexpr (KM == 2) {
             rawt[at >> 1] = uint32_t(bq);
@@ -1341,29 +1348,35 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
         base += segtot[g];
       }
       if constexpr (RSTAGE) if (p == 0 && lmask) {
-        // after a group's last tile and the last tile: the group's mantissa
-        // words; strip row r holds kq words of each of its segments, at word
-        // kq*(r*nseg + T0*NWG) of the stream
-        constexpr int RT = PackShared<DT, TC>::RT, q = 1, kq = kbits(DT, 1);
-        constexpr int RWS = RT * NWG * kq;                 // words per row of the buffer
-        if (T % RT == RT - 1 || T == ntiles - 1) {
-          const int T0 = T - T % RT;                       // the group's first tile
-          const int segs = (nseg < (T + 1) * NWG ? nseg : (T + 1) * NWG) - T0 * NWG;
-          uint32_t *const dst = reinterpret_cast<uint32_t *>(pwr[q]) + uint32_t(kq * NWG) * uint32_t(T0);
-          if (segs == RT * NWG && (nseg * kq) % 4 == 0 && (reinterpret_cast<uintptr_t>(pwr[q]) & 15) == 0) {
-            // RWS words per row, a multiple of 4, 16-byte aligned
-            constexpr int per = RWS / 4;
-            for (int i = tid; i < 32 * per; i += ENC_NT) {
-              const int r = i / per, v = i % per;
-              const uint32_t *sv = rawt + r * RWS + 4 * v;
-              stg16(dst + uint64_t(kq) * uint32_t(r) * uint32_t(nseg) + 4 * v, u32x4{sv[0], sv[1], sv[2], sv[3]});
+        // after a group's last tile and the chunk's last tile: 8 threads per
+        // strip row store the row's words from the last store's end up to
+        // the last line boundary the group reaches (to the row's end after
+        // the last tile); row r's words start at word kq*r*nseg of the stream
+        constexpr int RT = PackShared<DT, TC>::RT, RW = PackShared<DT, TC>::RW, q = 1, kq = kbits(DT, 1);
+        constexpr int GW = PackShared<DT, TC>::GW;          // a group's words per row
+        const bool last = T == ntiles - 1;
+        if (T % RT == RT - 1 || last) {
+          const uint32_t gi = uint32_t(T / RT), r = uint32_t(tid >> 3), k = uint32_t(tid & 7);
+          const uint32_t rowlen = uint32_t(kq) * uint32_t(nseg);
+          uint32_t *const dst = reinterpret_cast<uint32_t *>(pwr[q]) + rowlen * r;
+          const uint32_t *ring = rawt + r * RW;
+          if ((rowlen & 3) == 0 && (reinterpret_cast<uintptr_t>(pwr[q]) & 15) == 0) {
+            // rows start 16-byte aligned; phi: the row start's word within its line
+            const uint32_t phi = uint32_t(reinterpret_cast<uintptr_t>(dst) >> 2) & 31u;
+            auto bound = [&](uint32_t e) {   // the last line boundary at or before word e of the row
+              const uint32_t b = (e + phi) & ~31u;
+              return b >= phi ? b - phi : 0u;
+            };
+            const uint32_t f0 = gi == 0 ? 0u : bound(GW * gi);
+            const uint32_t f1 = last ? rowlen : bound(GW * (gi + 1));
+            for (uint32_t x = f0 + 4 * k; x < f1; x += 32) {
+              const uint32_t *sv = ring + x % RW;
+              stg16(dst + x, u32x4{sv[0], sv[1], sv[2], sv[3]});
             }
           } else {
-            const uint32_t rw = uint32_t(segs) * kq;       // words per row
-            for (uint32_t i = tid; i < 32 * rw; i += ENC_NT) {
-              const uint32_t r = i / rw, v = i % rw;
-              stg4(dst + uint64_t(kq) * r * uint32_t(nseg) + v, rawt[r * RWS + v]);
-            }
+            // rows off 16-byte alignment: the group's own words, one at a time
+            const uint32_t e = last ? rowlen : GW * (gi + 1);
+            for (uint32_t x = GW * gi + k; x < e; x += 8) stg4(dst + x, ring[x % RW]);
           }
         }
       }
