@@ -326,6 +326,12 @@ struct PackShared {
   static constexpr int RW = DT == FP8 ? 84 : 64;                  // ring words per row
   static_assert(!RSTAGE || (RW >= GW + 28 && RW % kbits(DT, 1) == 0 && RW % 4 == 0), "ring size");
   uint32_t rawt[RSTAGE ? 32 * RW : 1];
+  // FP32: the same for the raw fraction-byte streams written from the first
+  // coded stream's tiles (up to three streams, 8 strip rows each, 64 words
+  // of a row per tile, stored after every tile), in chunks of whole segments
+  static constexpr bool FRING = DT == FP32 && !TC;
+  static constexpr int FW = 128;                                  // ring words per row (a power of two)
+  uint32_t fring[FRING ? 3 * 8 * FW : 1];
   unsigned long long bits[NC], sec_off[NC];
   int mode[NC], aux[NC];
 };
@@ -939,7 +945,7 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
                                            uint32_t (*wtot)[PACK_NW], uint32_t *rawt,
                                            const uint8_t *segbits, TansPack *tans,
                                            const uint32_t *penc, const uint8_t *prk, bool packed,
-                                           const uint32_t *enc2) {
+                                           const uint32_t *enc2, uint32_t *rawf) {
   constexpr int NC = ncoded(DT), ES = esize(DT), S = segsyms(DT);
   constexpr int VE = 16 / ES;          // elements per 16-byte vector
   constexpr int EPT = S / 64;          // elements per thread per tile (a wave = a segment)
@@ -1112,6 +1118,9 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
       }
     };
     issue(0);
+    // FP32 in chunks of whole segments: the raw streams written from these
+    // tiles go through the rings
+    const bool fring = PackShared<DT, TC>::FRING && p == firstcoded && tilemask && n % S == 0;
     for (int T = 0; T < ntiles; T++) {
       const int buf = T & 1;
       uint32_t *stage = stage_all[buf];
@@ -1178,6 +1187,17 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
               bq |= uint64_t(f) << ((e * kq) & 63);
             }
             const uint32_t nwq = uint32_t((uint64_t(n) * kq + 31) / 32), w0 = eb * kq / 32;
+            if constexpr (PackShared<DT, TC>::FRING) {
+              if (fring) {
+                // word 8J + ln%8 of strip row ln/8, modulo the ring
+                static_assert(EPT * 8 == 32 && S == 256, "one word per lane run, 8 strip rows per segment");
+                constexpr int FW = PackShared<DT, TC>::FW;
+                const int J = (T * NW + wv) * G + g;
+                const int qi = __popc(tilemask & ((1u << q) - 1u));
+                if (lim > 0) rawf[(qi * 8 + (ln >> 3)) * FW + (8 * J + (ln & 7)) % FW] = uint32_t(bq);
+                continue;
+              }
+            }
 #pragma unroll
             for (int x = 0; x < 2; x++)
               if (x * 32 < EPT * kq && lim > 0 && w0 + x < nwq) stg4(pwr[q] + 4ull * (w0 + x), uint32_t(bq >> (32 * x)));
@@ -1380,6 +1400,45 @@ __device__ __forceinline__ void pack_chunk(const DevLayout &L, const uint8_t *co
           }
         }
       }
+      if constexpr (PackShared<DT, TC>::FRING) if (fring) {
+        // after every tile: 8 threads per (raw stream, strip row) store the
+        // row's whole lines up to the last line boundary the tile reaches
+        // (to the row's end after the last tile); row r of a stream starts
+        // at word 8*r*nseg
+        constexpr int FW = PackShared<DT, TC>::FW, GW = 8 * NWG;
+        const uint32_t pr = uint32_t(tid >> 3), k = uint32_t(tid & 7);
+        const uint32_t nraw = uint32_t(__popc(tilemask));
+        if (pr < 8 * nraw) {
+          const uint32_t qi = pr >> 3, r = pr & 7;
+          int q = 0;
+#pragma unroll
+          for (int z = 0, cnt = 0; z < NC; z++) {
+            const bool in = (tilemask >> z) & 1;
+            q = in && uint32_t(cnt) == qi ? z : q;
+            cnt += int(in);
+          }
+          const bool last = T == ntiles - 1;
+          const uint32_t rowlen = 8u * uint32_t(nseg);
+          uint32_t *const dst = reinterpret_cast<uint32_t *>(pwr[q]) + rowlen * r;
+          const uint32_t *ring = rawf + pr * FW;
+          if ((reinterpret_cast<uintptr_t>(pwr[q]) & 15) == 0) {
+            const uint32_t phi = uint32_t(reinterpret_cast<uintptr_t>(dst) >> 2) & 31u;
+            auto bound = [&](uint32_t e) {   // the last line boundary at or before word e of the row
+              const uint32_t b = (e + phi) & ~31u;
+              return b >= phi ? b - phi : 0u;
+            };
+            const uint32_t f0 = T == 0 ? 0u : bound(GW * uint32_t(T));
+            const uint32_t f1 = last ? rowlen : bound(GW * uint32_t(T + 1));
+            for (uint32_t x = f0 + 4 * k; x < f1; x += 32) {
+              const uint32_t *sv = ring + x % FW;
+              stg16(dst + x, u32x4{sv[0], sv[1], sv[2], sv[3]});
+            }
+          } else {
+            const uint32_t e = last ? rowlen : GW * uint32_t(T + 1);
+            for (uint32_t x = GW * uint32_t(T) + k; x < e; x += 8) stg4(dst + x, ring[x % FW]);
+          }
+        }
+      }
       __syncthreads();
       // store the whole words and clear them for the tile after next; the
       // partial last word moves to word 0 of the next tile's (clear) buffer
@@ -1461,7 +1520,7 @@ __global__ __launch_bounds__(PACK_NT) void k_pack(PackArgs a) {
   const uint64_t *dir = reinterpret_cast<const uint64_t *>(a.out + a.L.off_dir);
   pack_chunk<DT, TC, PK>(a.L, a.in_ptrs, c, a.out + dir[c], sh.enc, sh.mode, sh.aux, sh.bits, sh.sec_off,
                      sh.su.stage, sh.wtot, sh.rawt, plan + plan_fixed(DT), tans_of(sh), sh.penc, sh.prk, packed,
-                     sh.enc2);
+                     sh.enc2, sh.fring);
 }
 
 // One workgroup: exclusive scan of the record sizes into the directory, then
