@@ -19,8 +19,8 @@
 //   at its directory offset: stream heads, then each coded payload in tiles
 //   of whole segments (one or two per wave) -- a wave scan of bit counts, code
 //   words ORed into an LDS tile, whole words stored coalesced -- and the raw
-//   streams, from those tiles where their words allow, else in a pass of
-//   their own.
+//   streams, from those tiles where their words allow (through rings per
+//   strip row that store whole 128-byte lines), else in a pass of their own.
 // No chunk ever waits for another, and no record is copied after packing.
 #include <type_traits>
 
